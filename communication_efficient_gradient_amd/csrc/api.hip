@@ -1,0 +1,213 @@
+// api.hip — the C ABI declared in include/gq.h: argument validation on the
+// host, then dispatch to the kernel launchers.  No allocation, no global
+// state, no device synchronization.
+#include "gq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "common.hpp"
+
+namespace {
+
+constexpr int64_t kMaxN = int64_t(1) << 38;  // beyond any single HBM stack
+
+int ceil_log2(int v) {
+  int b = 0;
+  while ((1 << b) < v) ++b;
+  return b;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+// Validates a descriptor and fills the launch parameters.
+int check_desc(const gq_desc* d, gq::LaunchDesc* L) {
+  if (d == nullptr) return GQ_EINVAL;
+  const int b = d->bucket;
+  if (b < 64 || b > 32768 || (b & (b - 1)) != 0) return GQ_EINVAL;
+  if (d->flags & ~GQ_FLAG_CLIP) return GQ_EINVAL;
+  L->scheme = d->scheme;
+  L->d = b;
+  L->s = d->s;
+  L->L = d->levels;
+  L->flags = d->flags;
+  L->clip_sigma = d->clip_sigma;
+  switch (d->scheme) {
+    case GQ_UNIFORM: {
+      if (d->s < 1 || d->s > 127) return GQ_EUNSUPPORTED;
+      const int w = ceil_log2(2 * d->s + 1);
+      L->bits = w <= 4 ? w : 8;
+      L->k = 1;
+      break;
+    }
+    case GQ_BIN_SIGN:
+    case GQ_BIN_OPT:
+      L->bits = 1;
+      L->k = 2;
+      break;
+    case GQ_ORQ:
+      if (d->levels < 2 || d->levels > 16) return GQ_EUNSUPPORTED;
+      L->bits = ceil_log2(d->levels);
+      L->k = d->levels;
+      break;
+    default:
+      return GQ_EUNSUPPORTED;
+  }
+  if (d->flags & GQ_FLAG_CLIP) {
+    if (d->scheme != GQ_ORQ) return GQ_EUNSUPPORTED;
+    if (!(d->clip_sigma > 0.f) || !std::isfinite(d->clip_sigma)) return GQ_EINVAL;
+  }
+  return GQ_OK;
+}
+
+int64_t code_bytes_of(const gq::LaunchDesc& L, int64_t n) { return (n * L.bits + 7) / 8; }
+int64_t meta_floats_of(const gq::LaunchDesc& L, int64_t n) {
+  return ((n + L.d - 1) / L.d) * L.k;
+}
+
+int launch_status(int hip_rc) { return hip_rc == 0 ? GQ_OK : GQ_ELAUNCH; }
+
+bool is_sort_scheme(const gq::LaunchDesc& L) {
+  return L.scheme == GQ_BIN_OPT || L.scheme == GQ_ORQ;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gq_version(void) { return (1 << 16) | 0; }
+
+const char* gq_strerror(int status) {
+  switch (status) {
+    case GQ_OK:
+      return "success";
+    case GQ_EINVAL:
+      return "invalid argument (null or misaligned pointer, bad size, bad descriptor, overlapping buffers)";
+    case GQ_EUNSUPPORTED:
+      return "unsupported scheme parameters";
+    case GQ_ELAUNCH:
+      return "kernel launch failed";
+    case GQ_ETOOMANY:
+      return "too many payloads (W > GQ_MAX_PAYLOADS)";
+    default:
+      return "unknown status";
+  }
+}
+
+int gq_code_bits(const gq_desc* desc, int32_t* bits) {
+  gq::LaunchDesc L;
+  const int rc = check_desc(desc, &L);
+  if (rc) return rc;
+  if (bits == nullptr) return GQ_EINVAL;
+  *bits = L.bits;
+  return GQ_OK;
+}
+
+int gq_payload_size(const gq_desc* desc, int64_t n, int64_t* code_bytes,
+                    int64_t* code_capacity, int64_t* meta_floats) {
+  gq::LaunchDesc L;
+  const int rc = check_desc(desc, &L);
+  if (rc) return rc;
+  if (n < 1 || n > kMaxN) return GQ_EINVAL;
+  const int64_t cb = code_bytes_of(L, n);
+  if (code_bytes) *code_bytes = cb;
+  if (code_capacity) *code_capacity = (cb + 15) / 16 * 16;
+  if (meta_floats) *meta_floats = meta_floats_of(L, n);
+  return GQ_OK;
+}
+
+int gq_select_levels(const gq_desc* desc, int64_t n, const float* g,
+                     const float* e, float* meta, void* stream) {
+  gq::LaunchDesc L;
+  int rc = check_desc(desc, &L);
+  if (rc) return rc;
+  if (n < 1 || n > kMaxN || !g || !meta) return GQ_EINVAL;
+  if (!aligned16(g) || !aligned16(meta) || (e && !aligned16(e))) return GQ_EINVAL;
+  if (overlap(meta, 4 * meta_floats_of(L, n), g, 4 * n) ||
+      (e && overlap(meta, 4 * meta_floats_of(L, n), e, 4 * n)))
+    return GQ_EINVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* ew = const_cast<float*>(e);  // read-only when codes == nullptr
+  if (is_sort_scheme(L))
+    return launch_status(gq::launch_sort_quant(L, n, g, ew, 0, 0, nullptr, meta,
+                                               0, st));
+  return launch_status(gq::launch_stream_quant(L, n, g, ew, 0, 0, nullptr, meta,
+                                               0, st));
+}
+
+int gq_quantize(const gq_desc* desc, int64_t n, const float* g, float* e,
+                uint64_t seed, uint32_t step, uint8_t* codes, float* meta,
+                void* stream) {
+  gq::LaunchDesc L;
+  int rc = check_desc(desc, &L);
+  if (rc) return rc;
+  if (n < 1 || n > kMaxN || !g || !codes || !meta) return GQ_EINVAL;
+  if (!aligned16(g) || !aligned16(codes) || !aligned16(meta) || (e && !aligned16(e)))
+    return GQ_EINVAL;
+  const int64_t cb = code_bytes_of(L, n);
+  const int64_t cap = (cb + 15) / 16 * 16;
+  const int64_t mb = 4 * meta_floats_of(L, n);
+  if (e && (overlap(e, 4 * n, g, 4 * n) || overlap(e, 4 * n, codes, cap) ||
+            overlap(e, 4 * n, meta, mb)))
+    return GQ_EINVAL;
+  if (overlap(codes, cap, g, 4 * n) || overlap(meta, mb, g, 4 * n) ||
+      overlap(codes, cap, meta, mb))
+    return GQ_EINVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (is_sort_scheme(L))
+    return launch_status(
+        gq::launch_sort_quant(L, n, g, e, seed, step, codes, meta, cb, st));
+  return launch_status(
+      gq::launch_stream_quant(L, n, g, e, seed, step, codes, meta, cb, st));
+}
+
+int gq_error_feedback(const gq_desc* desc, int64_t n, const float* g, float* e,
+                      const uint8_t* codes, const float* meta, void* stream) {
+  gq::LaunchDesc L;
+  int rc = check_desc(desc, &L);
+  if (rc) return rc;
+  if (n < 1 || n > kMaxN || !g || !e || !codes || !meta) return GQ_EINVAL;
+  if (!aligned16(g) || !aligned16(e) || !aligned16(codes) || !aligned16(meta))
+    return GQ_EINVAL;
+  const int64_t cb = code_bytes_of(L, n);
+  if (overlap(e, 4 * n, g, 4 * n) || overlap(e, 4 * n, codes, cb) ||
+      overlap(e, 4 * n, meta, 4 * meta_floats_of(L, n)))
+    return GQ_EINVAL;
+  return launch_status(gq::launch_error_feedback(
+      L, n, g, e, codes, meta, cb, static_cast<hipStream_t>(stream)));
+}
+
+int gq_dequantize_accumulate(const gq_desc* desc, int64_t n, int32_t W,
+                             const uint8_t* const* codes,
+                             const float* const* meta, float alpha, float beta,
+                             float* out, void* stream) {
+  gq::LaunchDesc L;
+  int rc = check_desc(desc, &L);
+  if (rc) return rc;
+  if (W > GQ_MAX_PAYLOADS) return GQ_ETOOMANY;
+  if (n < 1 || n > kMaxN || W < 1 || !codes || !meta || !out) return GQ_EINVAL;
+  if (!aligned16(out) || !std::isfinite(alpha) || !std::isfinite(beta))
+    return GQ_EINVAL;
+  const int64_t cb = code_bytes_of(L, n);
+  const int64_t mb = 4 * meta_floats_of(L, n);
+  gq::PayloadPtrs pp{};
+  for (int w = 0; w < W; ++w) {
+    if (!codes[w] || !meta[w] || !aligned16(codes[w]) || !aligned16(meta[w]))
+      return GQ_EINVAL;
+    if (overlap(out, 4 * n, codes[w], cb) || overlap(out, 4 * n, meta[w], mb))
+      return GQ_EINVAL;
+    pp.codes[w] = codes[w];
+    pp.meta[w] = meta[w];
+  }
+  return launch_status(gq::launch_deq_acc(L, n, W, pp, alpha, beta, out, cb,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

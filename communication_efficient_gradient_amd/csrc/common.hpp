@@ -1,0 +1,213 @@
+// common.hpp — device helpers shared by libgq's kernels (gfx950, wave64).
+//
+// Philox4x32-10, group reductions over 16..64 lanes (DPP/bpermute via
+// __shfl_xor) and across waves (LDS), fp64 TwoSum accumulation, and the
+// OR-combine that turns per-lane code fields into LSB-first stream words.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gq {
+
+enum Scheme { UNIFORM = 0, BIN_SIGN = 1, BIN_OPT = 2, ORQ = 3 };
+
+constexpr int kMaxPayloads = 16;
+
+// --------------------------------------------------------------- Philox --
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of the
+// 4x32 S-box, multipliers 0xD2511F53 / 0xCD9E8D57, key bumped by the Weyl
+// constants 0x9E3779B9 / 0xBB67AE85 after each round.  Key = seed,
+// counter = (i/4 lo, i/4 hi, step, 0): the four output words serve elements
+// 4c .. 4c+3.  The pages ask only for rounding that is random and unbiased
+// ("Gradient Quantization" glossary, Stochastic Quantization bullet); a
+// counter-based generator makes the draw for element i a pure function of
+// (seed, i, step), independent of the launch shape.
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t k0, uint32_t k1,
+                                               uint32_t c0, uint32_t c1,
+                                               uint32_t c2, uint32_t c3) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t m0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t m1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(m1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(m0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)m1;
+    c3 = (uint32_t)m0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return make_uint4(c0, c1, c2, c3);
+}
+
+// Uniform in [0, 1) from the top 24 bits of a word (exact in binary32).
+__device__ __forceinline__ float u24(uint32_t w) {
+  return (float)(w >> 8) * 0x1p-24f;
+}
+
+// ------------------------------------------------------- group reductions --
+// Reductions over aligned groups of G lanes inside one wave (G <= 64).
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, G));
+  return v;
+}
+
+template <int G>
+__device__ __forceinline__ int group_sum_i(int v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, G);
+  return v;
+}
+
+template <int K>
+__device__ __forceinline__ uint32_t group_or(uint32_t v) {
+#pragma unroll
+  for (int o = K / 2; o > 0; o >>= 1) v |= __shfl_xor(v, o, K);
+  return v;
+}
+
+// fp64 sum with a running error term (Knuth TwoSum, branch-free).  The
+// result s + c is the exact sum up to O(n u^2) relative error, so means
+// rounded to fp32 agree with any other near-exact summation order.
+struct Sum2 {
+  double s, c;
+};
+
+__device__ __forceinline__ void two_sum_add(Sum2& a, double x) {
+  const double t = a.s + x;
+  const double bp = t - a.s;
+  const double err = (a.s - (t - bp)) + (x - bp);
+  a.s = t;
+  a.c += err;
+}
+
+__device__ __forceinline__ Sum2 two_sum_merge(Sum2 a, Sum2 b) {
+  Sum2 r = a;
+  two_sum_add(r, b.s);
+  r.c += b.c;
+  return r;
+}
+
+template <int G>
+__device__ __forceinline__ Sum2 group_sum2(Sum2 v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) {
+    Sum2 w;
+    w.s = __shfl_xor(v.s, o, G);
+    w.c = __shfl_xor(v.c, o, G);
+    v = two_sum_merge(v, w);
+  }
+  return v;
+}
+
+// ------------------------------------------------------------- packing --
+// Pack four codes of BITS bits (already masked) into one 4*BITS-bit field,
+// element 0 in the lowest bits.
+template <int BITS>
+__device__ __forceinline__ uint32_t field4(uint32_t c0, uint32_t c1,
+                                           uint32_t c2, uint32_t c3) {
+  return c0 | (c1 << BITS) | (c2 << (2 * BITS)) | (c3 << (3 * BITS));
+}
+
+// Load the float4 at element index i (a multiple of 4) with a guarded tail.
+__device__ __forceinline__ float4 load4(const float* __restrict__ a, int64_t i,
+                                        int64_t n) {
+  if (i + 3 < n) return *reinterpret_cast<const float4*>(a + i);
+  float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (i + 0 < n) r.x = a[i + 0];
+  if (i + 1 < n) r.y = a[i + 1];
+  if (i + 2 < n) r.z = a[i + 2];
+  return r;
+}
+
+__device__ __forceinline__ void store4(float* __restrict__ a, int64_t i,
+                                       int64_t n, float4 v) {
+  if (i + 3 < n) {
+    *reinterpret_cast<float4*>(a + i) = v;
+    return;
+  }
+  if (i + 0 < n) a[i + 0] = v.x;
+  if (i + 1 < n) a[i + 1] = v.y;
+  if (i + 2 < n) a[i + 2] = v.z;
+}
+
+__device__ __forceinline__ float comp(const float4& v, int k) {
+  return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+
+// Store this lane's 4*BITS-bit field into the LSB-first stream.  The field
+// of lane t covers elements idx .. idx+3; K consecutive lanes together fill
+// whole 32-bit words (K = 8/BITS), or three words for BITS = 3.  Words that
+// start at or past code_bytes are skipped (the buffer holds code_bytes
+// rounded up to 16).
+template <int BITS, int G>
+__device__ __forceinline__ void store_field(uint8_t* __restrict__ codes,
+                                            int64_t idx, int lane,
+                                            uint32_t field,
+                                            int64_t code_bytes) {
+  if constexpr (BITS == 3) {
+    const int q = lane & 7;
+    const int off = 12 * q;
+    const uint64_t x = (uint64_t)field << (off & 31);
+    const int wi = off >> 5;
+    uint32_t w0 = wi == 0 ? (uint32_t)x : 0u;
+    uint32_t w1 = wi == 1 ? (uint32_t)x : (wi == 0 ? (uint32_t)(x >> 32) : 0u);
+    uint32_t w2 = wi == 2 ? (uint32_t)x : (wi == 1 ? (uint32_t)(x >> 32) : 0u);
+    w0 = group_or<8>(w0);
+    w1 = group_or<8>(w1);
+    w2 = group_or<8>(w2);
+    if (q < 3) {
+      const int64_t byte = ((idx - 4 * q) >> 5) * 12 + 4 * q;
+      if (byte < code_bytes) {
+        const uint32_t w = q == 0 ? w0 : (q == 1 ? w1 : w2);
+        *reinterpret_cast<uint32_t*>(codes + byte) = w;
+      }
+    }
+  } else {
+    constexpr int K = 8 / BITS;
+    const int q = lane & (K - 1);
+    uint32_t w = field << (4 * BITS * q);
+    w = group_or<K>(w);
+    if (q == 0) {
+      const int64_t byte = (idx * BITS) >> 3;
+      if (byte < code_bytes) *reinterpret_cast<uint32_t*>(codes + byte) = w;
+    }
+  }
+}
+
+}  // namespace gq
+
+// ----------------------------------------------------- host launchers --
+// Implemented in the kernel translation units; called by the C ABI after
+// validation.  Each returns 0 or a hipError_t value.
+namespace gq {
+
+struct LaunchDesc {
+  int scheme, d, s, L, flags, bits, k;
+  float clip_sigma;
+};
+
+struct PayloadPtrs {
+  const uint8_t* codes[kMaxPayloads];
+  const float* meta[kMaxPayloads];
+};
+
+// quantize (codes != nullptr) or levels only (codes == nullptr, e read-only)
+int launch_stream_quant(const LaunchDesc& L, int64_t n, const float* g,
+                        float* e, uint64_t seed, uint32_t step, uint8_t* codes,
+                        float* meta, int64_t code_bytes, hipStream_t st);
+int launch_sort_quant(const LaunchDesc& L, int64_t n, const float* g, float* e,
+                      uint64_t seed, uint32_t step, uint8_t* codes, float* meta,
+                      int64_t code_bytes, hipStream_t st);
+int launch_deq_acc(const LaunchDesc& L, int64_t n, int W, const PayloadPtrs& pp,
+                   float alpha, float beta, float* out, int64_t code_bytes,
+                   hipStream_t st);
+int launch_error_feedback(const LaunchDesc& L, int64_t n, const float* g,
+                          float* e, const uint8_t* codes, const float* meta,
+                          int64_t code_bytes, hipStream_t st);
+
+}  // namespace gq

@@ -1,0 +1,635 @@
+// sort_quant.hip — quantizers whose levels need the bucket sorted:
+//   BIN_OPT  the two-level split that minimises squared error (BinGrad-b),
+//   ORQ      greedy multi-level selection minimising the random-rounding
+//            variance, with optional clipping, then random rounding.
+// ("Optimal Gradient Quantization Condition" review, §Proposed method.)
+//
+// One workgroup per bucket, T threads, E = d/T elements per thread.
+//   1. load p = g (+ e) in element order (thread t: elements t + T*m);
+//   2. (ORQ + clip) clip to +-clip_sigma * RMS;
+//   3. bitonic sort of the bucket in LDS (absent tail slots hold +inf);
+//   4. thread t then owns the sorted run [t*E, t*E + E) and the block runs
+//      fp64 (segmented) prefix / suffix scans over it:
+//        BIN_OPT  F(k) = P_k^2/k + Q_k^2/(n-k) for every split between
+//                 distinct values, block argmax (smallest k on equality);
+//        ORQ      L-2 greedy steps; each evaluates, for every distinct
+//                 interior value c of every interval (a, b),
+//                 G(c) = (b-c) * sum_{a<y<=c}(y-a) + (c-a) * sum_{c<y<b}(b-y)
+//                 from segmented scans (all terms >= 0: no cancellation),
+//                 and inserts the block argmax (smallest c on equality);
+//   5. back in element order: codes, packing, residual.
+// The bucket is read from HBM once; everything after the load is on-chip.
+#include "common.hpp"
+
+namespace gq {
+namespace {
+
+template <int D>
+struct SortCfg {
+  static constexpr int T = D <= 256 ? 64 : (D / 4 <= 1024 ? D / 4 : 1024);
+  static constexpr int E = D / T;
+  static constexpr int NW = T / 64;
+};
+
+// ------------------------------------------------------ block primitives --
+// Block max of a float (all threads get the result).
+template <int T>
+__device__ __forceinline__ float block_maxf(float v, float* red) {
+  v = group_max<64>(v);
+  if constexpr (T > 64) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    v = red[0];
+#pragma unroll
+    for (int w = 1; w < T / 64; ++w) v = fmaxf(v, red[w]);
+  }
+  return v;
+}
+
+template <int T>
+__device__ __forceinline__ Sum2 block_sum2(Sum2 v, double* red) {
+  v = group_sum2<64>(v);
+  if constexpr (T > 64) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) {
+      red[2 * wave] = v.s;
+      red[2 * wave + 1] = v.c;
+    }
+    __syncthreads();
+    v = Sum2{red[0], red[1]};
+#pragma unroll
+    for (int w = 1; w < T / 64; ++w) v = two_sum_merge(v, Sum2{red[2 * w], red[2 * w + 1]});
+  }
+  return v;
+}
+
+// Block argmax of (value, key): larger value wins, equal values -> smaller
+// key.  Returns the winning key (all threads).  Threads without a candidate
+// pass value = -1 (all real values are >= 0).
+template <int T>
+__device__ __forceinline__ int block_argmax(double v, int key, double* redv,
+                                            int* redk, double* best_out) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const double v2 = __shfl_xor(v, o, 64);
+    const int k2 = __shfl_xor(key, o, 64);
+    if (v2 > v || (v2 == v && k2 < key)) {
+      v = v2;
+      key = k2;
+    }
+  }
+  if constexpr (T > 64) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) {
+      redv[wave] = v;
+      redk[wave] = key;
+    }
+    __syncthreads();
+    v = redv[0];
+    key = redk[0];
+#pragma unroll
+    for (int w = 1; w < T / 64; ++w) {
+      const double v2 = redv[w];
+      const int k2 = redk[w];
+      if (v2 > v || (v2 == v && k2 < key)) {
+        v = v2;
+        key = k2;
+      }
+    }
+  }
+  *best_out = v;
+  return key;
+}
+
+// Carry for a block-wide segmented scan over per-thread aggregates (f, s):
+// f = the thread's run contains a segment boundary, s = the sum that flows
+// on to the next thread.  Combining an earlier aggregate a with a later b
+// gives (a.f | b.f, b.f ? b.s : a.s + b.s).  Returns, for each thread, the
+// combination of all threads before it (REV = false) or after it
+// (REV = true); identity (0, 0).
+template <int T, bool REV>
+__device__ __forceinline__ double block_seg_carry(bool f, double s,
+                                                  double* red_s, int* red_f) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int fi = f ? 1 : 0;
+  // inclusive scan within the wave, in lane order (or reverse lane order)
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double s2 = REV ? __shfl_down(s, o, 64) : __shfl_up(s, o, 64);
+    const int f2 = REV ? __shfl_down(fi, o, 64) : __shfl_up(fi, o, 64);
+    const bool valid = REV ? (lane + o < 64) : (lane >= o);
+    if (valid) {
+      if (!fi) s = s2 + s;
+      fi |= f2;
+    }
+  }
+  // exclusive: the inclusive value of the neighbouring lane
+  double ex_s = REV ? __shfl_down(s, 1, 64) : __shfl_up(s, 1, 64);
+  int ex_f = REV ? __shfl_down(fi, 1, 64) : __shfl_up(fi, 1, 64);
+  if (REV ? lane == 63 : lane == 0) {
+    ex_s = 0.0;
+    ex_f = 0;
+  }
+  if constexpr (T > 64) {
+    constexpr int NW = T / 64;
+    __syncthreads();
+    if (REV ? lane == 0 : lane == 63) {
+      red_s[wave] = s;
+      red_f[wave] = fi;
+    }
+    __syncthreads();
+    // carry from the waves before this one (in scan order)
+    double cs = 0.0;
+    if (!REV) {
+      for (int w = 0; w < wave; ++w) {
+        if (!red_f[w]) cs = cs + red_s[w]; else cs = red_s[w];
+      }
+    } else {
+      for (int w = NW - 1; w > wave; --w) {
+        if (!red_f[w]) cs = cs + red_s[w]; else cs = red_s[w];
+      }
+    }
+    // combine wave carry (earlier) with the lane-exclusive value (later)
+    if (!ex_f) ex_s = cs + ex_s;
+  }
+  return ex_s;
+}
+
+// Bitonic sort of D floats in LDS by T threads (ascending).
+template <int D, int T>
+__device__ __forceinline__ void bitonic_sort(float* s) {
+  for (int k = 2; k <= D; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      __syncthreads();
+#pragma unroll 4
+      for (int i = threadIdx.x; i < D / 2; i += T) {
+        const int lo = 2 * j * (i / j) + (i % j);
+        const int hi = lo + j;
+        const bool up = (lo & k) == 0;
+        const float a = s[lo], b = s[hi];
+        if ((a > b) == up) {
+          s[lo] = b;
+          s[hi] = a;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// ----------------------------------------------------- element-order I/O --
+// Codes of one element per lane, lanes in element order: K lanes with
+// K*BITS = 32 fill one word; for BITS = 3, 32 lanes fill three words.
+template <int BITS>
+__device__ __forceinline__ void store_code1(uint8_t* __restrict__ codes,
+                                            int64_t i, uint32_t c,
+                                            int64_t code_bytes) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (BITS == 3) {
+    const int q = lane & 31;
+    const int off = 3 * q;
+    const uint64_t x = (uint64_t)c << (off & 31);
+    const int wi = off >> 5;
+    uint32_t w0 = wi == 0 ? (uint32_t)x : 0u;
+    uint32_t w1 = wi == 1 ? (uint32_t)x : (wi == 0 ? (uint32_t)(x >> 32) : 0u);
+    uint32_t w2 = wi == 2 ? (uint32_t)x : (wi == 1 ? (uint32_t)(x >> 32) : 0u);
+    w0 = group_or<32>(w0);
+    w1 = group_or<32>(w1);
+    w2 = group_or<32>(w2);
+    if (q < 3) {
+      const int64_t byte = ((i - q) >> 5) * 12 + 4 * q;
+      if (byte < code_bytes) {
+        const uint32_t w = q == 0 ? w0 : (q == 1 ? w1 : w2);
+        *reinterpret_cast<uint32_t*>(codes + byte) = w;
+      }
+    }
+  } else {
+    constexpr int K = 32 / BITS;
+    const int q = lane & (K - 1);
+    uint32_t w = c << (BITS * q);
+    w = group_or<K>(w);
+    if (q == 0) {
+      const int64_t byte = (i * BITS) >> 3;
+      if (byte < code_bytes) *reinterpret_cast<uint32_t*>(codes + byte) = w;
+    }
+  }
+}
+
+struct SortShared {
+  double red_d[2 * 16];
+  double red_v[16];
+  int red_i[16];
+  int red_k[16];
+  float lev[16];
+  float thr;
+};
+
+template <int SCHEME, int BITS, int D>
+__global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
+    int64_t n, const float* __restrict__ g, float* __restrict__ e,
+    uint32_t k0, uint32_t k1, uint32_t step, int L, int clip, float clip_sigma,
+    uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes) {
+  constexpr int T = SortCfg<D>::T;
+  constexpr int E = SortCfg<D>::E;
+  __shared__ float sorted[D];
+  __shared__ SortShared sh;
+
+  const int tid = threadIdx.x;
+  const int64_t bucket = blockIdx.x;
+  const int64_t base = bucket * D;
+  const int nj = (int)((n - base) < D ? (n - base) : D);
+
+  // ---- 1. load p = g (+ e), element order t + T*m ----------------------
+  float p[E];
+#pragma unroll
+  for (int m = 0; m < E; ++m) {
+    const int64_t i = base + tid + T * m;
+    float x = 0.f;
+    if (tid + T * m < nj) {
+      x = g[i];
+      if (e != nullptr) x = x + e[i];
+    }
+    p[m] = x;
+  }
+
+  // ---- 2. clip (ORQ) -----------------------------------------------------
+  float pc[E];
+#pragma unroll
+  for (int m = 0; m < E; ++m) pc[m] = p[m];
+  if (SCHEME == ORQ && clip) {
+    Sum2 sq{0.0, 0.0};
+#pragma unroll
+    for (int m = 0; m < E; ++m)
+      if (tid + T * m < nj) two_sum_add(sq, (double)p[m] * (double)p[m]);
+    sq = block_sum2<T>(sq, sh.red_d);
+    const double sigma = sqrt((sq.s + sq.c) / (double)nj);
+    const float C = (float)((double)clip_sigma * sigma);
+#pragma unroll
+    for (int m = 0; m < E; ++m) pc[m] = fminf(fmaxf(p[m], -C), C);
+  }
+
+  // ---- 3. sort (canonical +0, +inf padding) -----------------------------
+#pragma unroll
+  for (int m = 0; m < E; ++m) {
+    const int pos = tid + T * m;
+    sorted[pos] = pos < nj ? (pc[m] == 0.f ? 0.f : pc[m]) : __builtin_inff();
+  }
+  bitonic_sort<D, T>(sorted);
+
+  // sorted run of this thread
+  const int r0 = tid * E;
+  const float y_next_run = (r0 + E < D) ? sorted[r0 + E] : __builtin_inff();
+  const float y_prev_run = r0 > 0 ? sorted[r0 - 1] : -__builtin_inff();
+
+  float lvl_a = 0.f, lvl_b = 0.f;  // BIN levels
+  float thr = 0.f;
+  bool no_split = false;
+
+  if constexpr (SCHEME == BIN_OPT) {
+    // ---- 4a. best split -------------------------------------------------
+    double tot = 0.0;
+#pragma unroll
+    for (int m = 0; m < E; ++m)
+      if (r0 + m < nj) tot = tot + (double)sorted[r0 + m];
+    // prefix before this run, suffix after it (plain fp64 scans)
+    const double pre = block_seg_carry<T, false>(false, tot, sh.red_d, sh.red_i);
+    const double suf = block_seg_carry<T, true>(false, tot, sh.red_d, sh.red_i);
+    double best = -1.0;
+    int bestk = 0x7fffffff;
+    // Q for each split: the suffix sum after each position of the run.
+    double Qrun[E];
+    {
+      double acc = suf;
+#pragma unroll
+      for (int m = E - 1; m >= 0; --m) {
+        Qrun[m] = acc;  // sum of positions > r0 + m
+        if (r0 + m < nj) acc = acc + (double)sorted[r0 + m];
+      }
+    }
+    double P = pre;
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+      const int pos = r0 + m;
+      if (pos < nj) P = P + (double)sorted[pos];
+      const int k = pos + 1;  // split: positions < k below
+      if (k < nj) {
+        const float yk = (m + 1 < E) ? sorted[pos + 1] : y_next_run;
+        if (sorted[pos] < yk) {
+          const double F = P * P / (double)k + Qrun[m] * Qrun[m] / (double)(nj - k);
+          if (F > best) {
+            best = F;
+            bestk = k;
+          }
+        }
+      }
+    }
+    double bestF;
+    const int kstar = block_argmax<T>(best, bestk, sh.red_v, sh.red_k, &bestF);
+    if (bestF < 0.0) {
+      no_split = true;
+      thr = sorted[0];
+      lvl_a = lvl_b = sorted[0];
+    } else {
+      thr = sorted[kstar];
+      // levels: means of the two sides, near-exact fp64 sums
+      Sum2 lo{0.0, 0.0}, hi{0.0, 0.0};
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        if (tid + T * m < nj) {
+          if (p[m] >= thr) two_sum_add(hi, (double)p[m]);
+          else two_sum_add(lo, (double)p[m]);
+        }
+      }
+      lo = block_sum2<T>(lo, sh.red_d);
+      hi = block_sum2<T>(hi, sh.red_d);
+      lvl_a = (float)((lo.s + lo.c) / (double)kstar);
+      lvl_b = (float)((hi.s + hi.c) / (double)(nj - kstar));
+    }
+    if (tid == 0) {
+      meta[2 * bucket + 0] = lvl_a;
+      meta[2 * bucket + 1] = lvl_b;
+    }
+  } else {
+    // ---- 4b. ORQ greedy levels -------------------------------------------
+    const float ymin = sorted[0], ymax = sorted[nj - 1];
+    if (tid == 0) {
+      sh.lev[0] = ymin;
+      sh.lev[1] = ymax;
+    }
+    int cnt = 2;
+    if (ymin == ymax) {
+      if (tid < L) sh.lev[tid] = ymin;
+      cnt = L;
+    }
+    __syncthreads();
+    while (cnt < L) {
+      // segment of each sorted value: last level <= y
+      float lv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) lv[j] = j < cnt ? sh.lev[j] : __builtin_inff();
+      int seg[E];
+      float a_of[E], b_of[E];
+      bool head[E], tail[E];
+      double va[E], vb[E];
+      int seg_prev = -1;
+      {
+        // segment of the value just before this run
+        int sp = -1;
+        if (r0 > 0) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (lv[j] <= y_prev_run) sp = j;
+        }
+        seg_prev = sp;
+      }
+      int seg_next = -1;
+      {
+        int sn = -1;
+        if (r0 + E < nj) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (lv[j] <= y_next_run) sn = j;
+        }
+        seg_next = sn;
+      }
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        const float y = sorted[r0 + m];
+        int sj = 0;
+        float a = lv[0], b = lv[0];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if (lv[j] <= y) {
+            sj = j;
+            a = lv[j];
+            b = (j + 1 < 16 && j + 1 < cnt) ? lv[j + 1 < 16 ? j + 1 : 15] : lv[j];
+          }
+        }
+        seg[m] = sj;
+        a_of[m] = a;
+        b_of[m] = b;
+        const bool real = r0 + m < nj;
+        va[m] = real ? (double)y - (double)a_of[m] : 0.0;
+        vb[m] = real ? (double)b_of[m] - (double)y : 0.0;
+      }
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        head[m] = (m == 0) ? (seg_prev != seg[0]) : (seg[m] != seg[m - 1]);
+        tail[m] = (m == E - 1) ? (seg_next != seg[E - 1]) : (seg[m] != seg[m + 1]);
+      }
+      // forward aggregate for A (sum over the run's last segment piece)
+      bool fa = false;
+      double sa = 0.0;
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        if (head[m]) {
+          fa = true;
+          sa = va[m];
+        } else {
+          sa = sa + va[m];
+        }
+      }
+      // reverse aggregate for B (sum over the run's first segment piece)
+      bool fb = false;
+      double sb = 0.0;
+#pragma unroll
+      for (int m = E - 1; m >= 0; --m) {
+        if (tail[m]) {
+          fb = true;
+          sb = vb[m];
+        } else {
+          sb = sb + vb[m];
+        }
+      }
+      const double ca = block_seg_carry<T, false>(fa, sa, sh.red_d, sh.red_i);
+      const double cb = block_seg_carry<T, true>(fb, sb, sh.red_d, sh.red_i);
+      // B: exclusive suffix within the segment
+      double B[E];
+      {
+        double run = cb;
+#pragma unroll
+        for (int m = E - 1; m >= 0; --m) {
+          if (tail[m]) {
+            B[m] = 0.0;
+            run = vb[m];
+          } else {
+            B[m] = run;
+            run = run + vb[m];
+          }
+        }
+      }
+      double best = -1.0;
+      int bestk = 0x7fffffff;
+      {
+        double A = ca;
+#pragma unroll
+        for (int m = 0; m < E; ++m) {
+          A = head[m] ? va[m] : A + va[m];
+          const int pos = r0 + m;
+          const float y = sorted[pos];
+          const float ynext = (m + 1 < E) ? sorted[pos + 1] : y_next_run;
+          const bool cand = pos < nj && seg[m] + 1 < cnt && y > a_of[m] &&
+                            (pos + 1 >= nj || ynext != y);
+          if (cand) {
+            const double c = (double)y;
+            const double G = ((double)b_of[m] - c) * A + (c - (double)a_of[m]) * B[m];
+            if (G > best) {
+              best = G;
+              bestk = pos;
+            }
+          }
+        }
+      }
+      double bestG;
+      const int kstar = block_argmax<T>(best, bestk, sh.red_v, sh.red_k, &bestG);
+      __syncthreads();
+      if (bestG < 0.0) {
+        // fewer distinct values than levels: repeat the maximum
+        if (tid == 0)
+          for (int j = cnt; j < L; ++j) sh.lev[j] = ymax;
+        cnt = L;
+      } else {
+        if (tid == 0) {
+          const float c = sorted[kstar];
+          int pos = cnt;
+          while (pos > 0 && sh.lev[pos - 1] > c) {
+            sh.lev[pos] = sh.lev[pos - 1];
+            --pos;
+          }
+          sh.lev[pos] = c;
+        }
+        ++cnt;
+      }
+      __syncthreads();
+    }
+    if (tid < L) meta[bucket * L + tid] = sh.lev[tid];
+  }
+
+  if (codes == nullptr) return;  // levels only
+
+  // ---- 5. codes, packing, residual (element order) ----------------------
+  float lv[16];
+  if constexpr (SCHEME == ORQ) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) lv[j] = j < L ? sh.lev[j] : __builtin_inff();
+  }
+#pragma unroll
+  for (int m = 0; m < E; ++m) {
+    const int pos = tid + T * m;
+    const int64_t i = base + pos;
+    const bool real = pos < nj;
+    uint32_t c = 0u;
+    float xh = 0.f;
+    if constexpr (SCHEME == BIN_OPT) {
+      c = (!no_split && pc[m] >= thr) ? 1u : 0u;
+      xh = c ? lvl_b : lvl_a;
+    } else {
+      const float x = pc[m];
+      int first_eq = -1, below = 0;
+#pragma unroll
+      for (int j = 15; j >= 0; --j)
+        if (j < L && lv[j] == x) first_eq = j;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j < L && lv[j] < x) below = j;
+      if (first_eq >= 0) {
+        c = (uint32_t)first_eq;
+      } else {
+        // random rounding between lv[below] and lv[below + 1]
+        const uint64_t ctr = (uint64_t)i >> 2;
+        const uint4 w = philox4x32_10(k0, k1, (uint32_t)ctr,
+                                      (uint32_t)(ctr >> 32), step, 0u);
+        const int sub = (int)(i & 3);
+        const uint32_t word = sub == 0 ? w.x : sub == 1 ? w.y : sub == 2 ? w.z : w.w;
+        float lo = lv[0], hi = lv[1];
+#pragma unroll
+        for (int j = 0; j < 15; ++j)
+          if (j == below) {
+            lo = lv[j];
+            hi = lv[j + 1];
+          }
+        const float q = (x - lo) / (hi - lo);
+        c = (uint32_t)(below + (u24(word) < q ? 1 : 0));
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if ((uint32_t)j == c) xh = lv[j];
+    }
+    if (!real) c = 0u;
+    store_code1<BITS>(codes, i, c, code_bytes);
+    if (e != nullptr && real) e[i] = p[m] - xh;
+  }
+}
+
+template <int SCHEME, int BITS, int D>
+int launch_sort_one(int64_t n, const float* g, float* e, uint64_t seed,
+                    uint32_t step, int L, int clip, float clip_sigma,
+                    uint8_t* codes, float* meta, int64_t code_bytes,
+                    hipStream_t st) {
+  const int64_t nb = (n + D - 1) / D;
+  hipLaunchKernelGGL((k_sort_quant<SCHEME, BITS, D>), dim3((uint32_t)nb),
+                     dim3(SortCfg<D>::T), 0, st, n, g, e, (uint32_t)seed,
+                     (uint32_t)(seed >> 32), step, L, clip, clip_sigma, codes,
+                     meta, code_bytes);
+  return (int)hipGetLastError();
+}
+
+template <int SCHEME, int BITS>
+int sort_dispatch_d(int d, int64_t n, const float* g, float* e, uint64_t seed,
+                    uint32_t step, int L, int clip, float clip_sigma,
+                    uint8_t* codes, float* meta, int64_t code_bytes,
+                    hipStream_t st) {
+#define GQ_SCASE(D_)                                                        \
+  case D_:                                                                  \
+    return launch_sort_one<SCHEME, BITS, D_>(n, g, e, seed, step, L, clip,  \
+                                             clip_sigma, codes, meta,       \
+                                             code_bytes, st);
+  switch (d) {
+    GQ_SCASE(64)
+    GQ_SCASE(128)
+    GQ_SCASE(256)
+    GQ_SCASE(512)
+    GQ_SCASE(1024)
+    GQ_SCASE(2048)
+    GQ_SCASE(4096)
+    GQ_SCASE(8192)
+    GQ_SCASE(16384)
+    GQ_SCASE(32768)
+    default:
+      return (int)hipErrorInvalidValue;
+  }
+#undef GQ_SCASE
+}
+
+}  // namespace
+
+int launch_sort_quant(const LaunchDesc& L, int64_t n, const float* g, float* e,
+                      uint64_t seed, uint32_t step, uint8_t* codes, float* meta,
+                      int64_t code_bytes, hipStream_t st) {
+  const int clip = (L.flags & 1) ? 1 : 0;
+  if (L.scheme == BIN_OPT)
+    return sort_dispatch_d<BIN_OPT, 1>(L.d, n, g, e, seed, step, 2, 0, 0.f,
+                                       codes, meta, code_bytes, st);
+  switch (L.bits) {
+    case 1:
+      return sort_dispatch_d<ORQ, 1>(L.d, n, g, e, seed, step, L.L, clip,
+                                     L.clip_sigma, codes, meta, code_bytes, st);
+    case 2:
+      return sort_dispatch_d<ORQ, 2>(L.d, n, g, e, seed, step, L.L, clip,
+                                     L.clip_sigma, codes, meta, code_bytes, st);
+    case 3:
+      return sort_dispatch_d<ORQ, 3>(L.d, n, g, e, seed, step, L.L, clip,
+                                     L.clip_sigma, codes, meta, code_bytes, st);
+    case 4:
+      return sort_dispatch_d<ORQ, 4>(L.d, n, g, e, seed, step, L.L, clip,
+                                     L.clip_sigma, codes, meta, code_bytes, st);
+    default:
+      return (int)hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gq

@@ -1,0 +1,283 @@
+// stream_quant.hip — one-pass quantizers whose per-bucket levels come from a
+// reduction: max-abs uniform (QSGD / ternary / INT8) and the sign split.
+//
+// One HBM pass per bucket: 128-bit loads of g (and e), p = g + e kept in
+// registers, a group reduction for the bucket's levels, then Philox rounding,
+// packing and the residual store, all from registers.
+//
+// Work mapping (d = 4 * G * V):  a group of G lanes owns one bucket; lane t
+// holds the float4s t, t+G, ..., t+(V-1)G of it, so every load instruction
+// of the group reads G consecutive 16-byte vectors.  G <= 64 groups live
+// inside one wave (256-thread blocks hold 256/G buckets); G > 64 spans G/64
+// waves of one block and reduces through LDS.
+#include "common.hpp"
+
+namespace gq {
+namespace {
+
+template <int G>
+struct BlockCfg {
+  static constexpr int kThreads = G <= 64 ? 256 : G;
+  static constexpr int kGroups = kThreads / G;
+  static constexpr int kWaves = kThreads / 64;
+};
+
+// Reduce across the G/64 waves of a bucket (G > 64) through LDS.
+template <int G>
+__device__ __forceinline__ float bucket_max(float v, float* red) {
+  if constexpr (G <= 64) {
+    return group_max<G>(v);
+  } else {
+    v = group_max<64>(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float m = red[0];
+#pragma unroll
+    for (int w = 1; w < G / 64; ++w) m = fmaxf(m, red[w]);
+    return m;
+  }
+}
+
+template <int G>
+__device__ __forceinline__ void bucket_side_sums(Sum2& neg, Sum2& pos, int& nn,
+                                                 int& np, double* redd,
+                                                 int* redi) {
+  neg = group_sum2<(G <= 64 ? G : 64)>(neg);
+  pos = group_sum2<(G <= 64 ? G : 64)>(pos);
+  nn = group_sum_i<(G <= 64 ? G : 64)>(nn);
+  np = group_sum_i<(G <= 64 ? G : 64)>(np);
+  if constexpr (G > 64) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int NW = G / 64;
+    if (lane == 0) {
+      redd[4 * wave + 0] = neg.s;
+      redd[4 * wave + 1] = neg.c;
+      redd[4 * wave + 2] = pos.s;
+      redd[4 * wave + 3] = pos.c;
+      redi[2 * wave + 0] = nn;
+      redi[2 * wave + 1] = np;
+    }
+    __syncthreads();
+    neg = Sum2{redd[0], redd[1]};
+    pos = Sum2{redd[2], redd[3]};
+    nn = redi[0];
+    np = redi[1];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      neg = two_sum_merge(neg, Sum2{redd[4 * w + 0], redd[4 * w + 1]});
+      pos = two_sum_merge(pos, Sum2{redd[4 * w + 2], redd[4 * w + 3]});
+      nn += redi[2 * w + 0];
+      np += redi[2 * w + 1];
+    }
+  }
+}
+
+template <int SCHEME, int BITS, int G, int V>
+__global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
+    int64_t n, int64_t nb, const float* __restrict__ g, float* __restrict__ e,
+    uint32_t k0, uint32_t k1, uint32_t step, int s, uint8_t* __restrict__ codes,
+    float* __restrict__ meta, int64_t code_bytes) {
+  constexpr int D = 4 * G * V;
+  constexpr int NW = G > 64 ? G / 64 : 1;
+  __shared__ float red_f[NW];
+  __shared__ double red_d[4 * NW];
+  __shared__ int red_i[2 * NW];
+
+  const int lane = threadIdx.x % G;
+  const int64_t bucket =
+      (int64_t)blockIdx.x * BlockCfg<G>::kGroups + threadIdx.x / G;
+  if (bucket >= nb) return;  // whole groups leave together
+  const int64_t base = bucket * D;
+
+  // ---- load p = g (+ e) ------------------------------------------------
+  float4 p[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int64_t i = base + 4 * (lane + G * v);
+    float4 x = load4(g, i, n);
+    if (e != nullptr) {
+      const float4 r = load4(e, i, n);
+      x.x = x.x + r.x;
+      x.y = x.y + r.y;
+      x.z = x.z + r.z;
+      x.w = x.w + r.w;
+    }
+    p[v] = x;
+  }
+
+  // ---- per-bucket levels ----------------------------------------------
+  // UNIFORM: M = max |p| (absent tail elements load as 0, which never
+  // raises a max-abs).  BIN_SIGN: side means over the real elements.
+  float lvl0 = 0.f, lvl1 = 0.f;
+  if constexpr (SCHEME == UNIFORM) {
+    float m = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(p[v].x), fabsf(p[v].y)),
+                         fmaxf(fabsf(p[v].z), fabsf(p[v].w))));
+    lvl0 = bucket_max<G>(m, red_f);
+  } else {
+    Sum2 neg{0.0, 0.0}, pos{0.0, 0.0};
+    int nn = 0, np = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int64_t i = base + 4 * (lane + G * v);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (i + k < n) {
+          const float x = comp(p[v], k);
+          if (x >= 0.f) {
+            two_sum_add(pos, (double)x);
+            ++np;
+          } else {
+            two_sum_add(neg, (double)x);
+            ++nn;
+          }
+        }
+      }
+    }
+    bucket_side_sums<G>(neg, pos, nn, np, red_d, red_i);
+    lvl0 = nn ? (float)((neg.s + neg.c) / (double)nn) : 0.f;
+    lvl1 = np ? (float)((pos.s + pos.c) / (double)np) : 0.f;
+  }
+
+  if (lane == 0) {
+    if constexpr (SCHEME == UNIFORM) {
+      meta[bucket] = lvl0;
+    } else {
+      meta[2 * bucket + 0] = lvl0;
+      meta[2 * bucket + 1] = lvl1;
+    }
+  }
+  if (codes == nullptr) return;  // levels only
+
+  // ---- round, pack, residual ---------------------------------------------
+  const float M = lvl0;
+  const float sf = (float)s;
+  // A bucket whose max-abs is below 2^-96 is scaled by 2^96 first (exact)
+  // so that s / M stays finite; for all other buckets the factor is 1.
+  const float up = M < 0x1p-96f ? 0x1p96f : 1.0f;
+  const float inv = M > 0.f ? sf / (M * up) : 0.f;
+  const float delta = M / sf;
+
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int64_t i = base + 4 * (lane + G * v);
+    uint32_t c[4];
+    float4 xh;
+    if constexpr (SCHEME == UNIFORM) {
+      const uint64_t ctr = (uint64_t)i >> 2;
+      const uint4 w = philox4x32_10(k0, k1, (uint32_t)ctr,
+                                    (uint32_t)(ctr >> 32), step, 0u);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float x = comp(p[v], k);
+        const float r = fminf((fabsf(x) * up) * inv, sf);
+        const float l = floorf(r);
+        const float q = r - l;
+        const int mag = (int)l + (u24(ws[k]) < q ? 1 : 0);
+        const int ci = x < 0.f ? -mag : mag;
+        c[k] = (uint32_t)ci & ((1u << BITS) - 1u);
+        const float xk = (float)ci * delta;
+        if (k == 0) xh.x = xk;
+        if (k == 1) xh.y = xk;
+        if (k == 2) xh.z = xk;
+        if (k == 3) xh.w = xk;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float x = comp(p[v], k);
+        c[k] = x >= 0.f ? 1u : 0u;
+        const float xk = c[k] ? lvl1 : lvl0;
+        if (k == 0) xh.x = xk;
+        if (k == 1) xh.y = xk;
+        if (k == 2) xh.z = xk;
+        if (k == 3) xh.w = xk;
+      }
+    }
+    // absent tail elements pack as 0
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (i + k >= n) c[k] = 0u;
+    store_field<BITS, G>(codes, i, lane, field4<BITS>(c[0], c[1], c[2], c[3]),
+                         code_bytes);
+    if (e != nullptr && i < n) {
+      float4 r;
+      r.x = p[v].x - xh.x;
+      r.y = p[v].y - xh.y;
+      r.z = p[v].z - xh.z;
+      r.w = p[v].w - xh.w;
+      store4(e, i, n, r);
+    }
+  }
+}
+
+template <int SCHEME, int BITS, int G, int V>
+int launch_one(int64_t n, const float* g, float* e, uint64_t seed,
+               uint32_t step, int s, uint8_t* codes, float* meta,
+               int64_t code_bytes, hipStream_t st) {
+  constexpr int D = 4 * G * V;
+  const int64_t nb = (n + D - 1) / D;
+  const int64_t blocks = (nb + BlockCfg<G>::kGroups - 1) / BlockCfg<G>::kGroups;
+  hipLaunchKernelGGL((k_stream_quant<SCHEME, BITS, G, V>), dim3((uint32_t)blocks),
+                     dim3(BlockCfg<G>::kThreads), 0, st, n, nb, g, e,
+                     (uint32_t)seed, (uint32_t)(seed >> 32), step, s, codes,
+                     meta, code_bytes);
+  return (int)hipGetLastError();
+}
+
+template <int SCHEME, int BITS>
+int dispatch_d(int d, int64_t n, const float* g, float* e, uint64_t seed,
+               uint32_t step, int s, uint8_t* codes, float* meta,
+               int64_t code_bytes, hipStream_t st) {
+#define GQ_CASE(D_, G_, V_)                                                  \
+  case D_:                                                                   \
+    return launch_one<SCHEME, BITS, G_, V_>(n, g, e, seed, step, s, codes,   \
+                                            meta, code_bytes, st);
+  switch (d) {
+    GQ_CASE(64, 16, 1)
+    GQ_CASE(128, 32, 1)
+    GQ_CASE(256, 64, 1)
+    GQ_CASE(512, 64, 2)
+    GQ_CASE(1024, 64, 4)
+    GQ_CASE(2048, 64, 8)
+    GQ_CASE(4096, 128, 8)
+    GQ_CASE(8192, 256, 8)
+    GQ_CASE(16384, 512, 8)
+    GQ_CASE(32768, 1024, 8)
+    default:
+      return (int)hipErrorInvalidValue;
+  }
+#undef GQ_CASE
+}
+
+}  // namespace
+
+int launch_stream_quant(const LaunchDesc& L, int64_t n, const float* g,
+                        float* e, uint64_t seed, uint32_t step, uint8_t* codes,
+                        float* meta, int64_t code_bytes, hipStream_t st) {
+  if (L.scheme == BIN_SIGN)
+    return dispatch_d<BIN_SIGN, 1>(L.d, n, g, e, seed, step, L.s, codes, meta,
+                                   code_bytes, st);
+  switch (L.bits) {
+    case 2:
+      return dispatch_d<UNIFORM, 2>(L.d, n, g, e, seed, step, L.s, codes, meta,
+                                    code_bytes, st);
+    case 3:
+      return dispatch_d<UNIFORM, 3>(L.d, n, g, e, seed, step, L.s, codes, meta,
+                                    code_bytes, st);
+    case 4:
+      return dispatch_d<UNIFORM, 4>(L.d, n, g, e, seed, step, L.s, codes, meta,
+                                    code_bytes, st);
+    case 8:
+      return dispatch_d<UNIFORM, 8>(L.d, n, g, e, seed, step, L.s, codes, meta,
+                                    code_bytes, st);
+    default:
+      return (int)hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gq

@@ -1,0 +1,145 @@
+/*
+ * gq.h — C ABI of libgq: bucketed stochastic gradient quantization with
+ * error feedback, for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the compress / decompress / aggregate steps of
+ * data-parallel gradient exchange ("gradient quantization for
+ * communication" glossary, §How Gradient Quantization Works: quantize before
+ * transmission, dequantize on receipt, then average) together with the
+ * error-feedback loop ("Gradient Quantization" glossary, error-feedback
+ * paragraph: keep the quantization residual and add it to the next
+ * gradient).  One GPU; no collectives.
+ *
+ * Layout shared by every call
+ *   - A gradient is a flat fp32 array of n >= 1 elements.  Bucket j holds
+ *     elements [j*d, min(n, (j+1)*d)); the last bucket may be partial and its
+ *     statistics use only its real elements ("Optimal Gradient Quantization
+ *     Condition" review, §Proposed method: fixed-size buckets, d = 512).
+ *   - Codes form one LSB-first bitstream: element i owns stream bits
+ *     [b*i, b*i + b), stream bit t is bit (t mod 8) of byte t/8, code bit 0
+ *     first.  Bytes past the last element's bits are written as zero.
+ *   - meta is fp32 [nb][k]:  k = 1 (GQ_UNIFORM: the bucket's max-abs M),
+ *     2 (GQ_BIN_*: lower level a, upper level b), L (GQ_ORQ: ascending levels).
+ *
+ * Conventions
+ *   - All pointers to arrays are DEVICE pointers (except the two pointer
+ *     arrays of gq_dequantize_accumulate, which live in host memory and hold
+ *     device pointers).  Every device array must be 16-byte aligned.
+ *   - The caller owns every buffer; libgq allocates no device memory and
+ *     keeps no state between calls, so calls on different streams may run
+ *     concurrently as long as their buffers do not overlap.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously; nothing synchronizes the device.
+ *   - Argument errors are detected on the host before any launch and
+ *     returned; a failed launch returns GQ_ELAUNCH.
+ *   - Inputs must be finite; NaN/Inf inputs give unspecified outputs but
+ *     never out-of-bounds accesses.
+ *   - Outputs are a pure function of (inputs, desc, seed, step): they do not
+ *     depend on launch configuration or on other calls.
+ */
+#ifndef GQ_H
+#define GQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Schemes.
+ * GQ_UNIFORM  max-abs scaled uniform levels, s per sign, random rounding:
+ *             QSGD (s = 4: 4-bit), ternary / TernGrad (s = 1: 2-bit),
+ *             INT8 (s = 127).  ("Gradient Quantization" glossary: core
+ *             mechanism, Stochastic Quantization bullet, QSGD and ternary
+ *             paragraphs.)
+ * GQ_BIN_SIGN two levels split at zero, each the mean of its side; 1-bit
+ *             (the sign path: ternary/binary paragraph, SignSGD).
+ * GQ_BIN_OPT  two levels minimising the bucket's squared error (BinGrad-b:
+ *             "Optimal Gradient Quantization Condition" review, §Proposed
+ *             method); deterministic, 1-bit.
+ * GQ_ORQ      L levels picked greedily to minimise the summed random-
+ *             rounding variance sum (b-x)(x-a), random rounding between
+ *             adjacent levels (ORQ, same section); optional clip. */
+typedef enum {
+  GQ_UNIFORM = 0,
+  GQ_BIN_SIGN = 1,
+  GQ_BIN_OPT = 2,
+  GQ_ORQ = 3
+} gq_scheme;
+
+/* GQ_ORQ only: clip every value of a bucket to +-clip_sigma * RMS(bucket)
+ * before selecting levels and rounding (same section: clipping). */
+enum { GQ_FLAG_CLIP = 1 };
+
+typedef struct {
+  int32_t scheme;     /* gq_scheme                                          */
+  int32_t bucket;     /* d: power of two, 64 <= d <= 32768                  */
+  int32_t s;          /* GQ_UNIFORM: levels per sign, 1..127                 */
+  int32_t levels;     /* GQ_ORQ: L total levels incl. min and max, 2..16     */
+  int32_t flags;      /* GQ_FLAG_* (others must be 0)                       */
+  float clip_sigma;   /* with GQ_FLAG_CLIP: > 0                             */
+} gq_desc;
+
+enum {
+  GQ_OK = 0,
+  GQ_EINVAL = -1,       /* null/misaligned pointer, bad size or descriptor  */
+  GQ_EUNSUPPORTED = -2, /* well-formed but unsupported (scheme, s, L, flag) */
+  GQ_ELAUNCH = -3,      /* a kernel launch failed (hipGetLastError)         */
+  GQ_ETOOMANY = -4      /* W > GQ_MAX_PAYLOADS                               */
+};
+
+#define GQ_MAX_PAYLOADS 16
+
+/* Bits per code: GQ_UNIFORM ceil(log2(2s+1)) rounded up to 2, 3, 4 or 8
+ * (two's complement); GQ_BIN_* 1 (1 = upper level); GQ_ORQ ceil(log2 L)
+ * (unsigned level index).  Host-only; never touches the GPU. */
+int gq_code_bits(const gq_desc* desc, int32_t* bits);
+
+/* Payload sizes for n elements: code_bytes = ceil(n*bits/8); code_capacity
+ * = code_bytes rounded up to a multiple of 16 (the size a codes buffer
+ * written by gq_quantize must have); meta_floats = ceil(n/d) * k.
+ * Any output pointer may be NULL.  Host-only. */
+int gq_payload_size(const gq_desc* desc, int64_t n, int64_t* code_bytes,
+                    int64_t* code_capacity, int64_t* meta_floats);
+
+/* Per-bucket levels of p = g (+ e when e != NULL) into meta, exactly as
+ * gq_quantize would compute them; nothing else is written. */
+int gq_select_levels(const gq_desc* desc, int64_t n, const float* g,
+                     const float* e, float* meta, void* stream);
+
+/* Quantize n elements: p = g (+ e), levels per bucket, random rounding
+ * (round up iff u < q, u from Philox4x32-10 with key = seed and counter =
+ * (i/4, step); element i uses word i mod 4, u = (word >> 8) * 2^-24), pack.
+ * With e != NULL, e is read and then overwritten in place with the residual
+ * p - dequant(code) (unclipped p).  codes: code_capacity bytes.  e must not
+ * overlap g, codes or meta. */
+int gq_quantize(const gq_desc* desc, int64_t n, const float* g, float* e,
+                uint64_t seed, uint32_t step, uint8_t* codes, float* meta,
+                void* stream);
+
+/* Standalone residual update: e <- fl(fl(g + e) - dequant(codes, meta));
+ * bitwise equal to the residual gq_quantize writes for the same payload. */
+int gq_error_feedback(const gq_desc* desc, int64_t n, const float* g, float* e,
+                      const uint8_t* codes, const float* meta, void* stream);
+
+/* Aggregate W payloads (1 <= W <= GQ_MAX_PAYLOADS), each quantized with the
+ * same desc over the same n:  out <- beta*out + alpha * sum_w dequant_w.
+ * codes[w] / meta[w] are device pointers held in HOST arrays of length W.
+ * beta == 0 means out is write-only (never read).  Accumulation is fp32;
+ * W = 1, alpha = 1, beta = 0 reproduces dequant exactly.  out must not
+ * overlap any payload. */
+int gq_dequantize_accumulate(const gq_desc* desc, int64_t n, int32_t W,
+                             const uint8_t* const* codes,
+                             const float* const* meta, float alpha, float beta,
+                             float* out, void* stream);
+
+/* Static description of a status code. */
+const char* gq_strerror(int status);
+
+/* Library version, (major << 16) | minor. */
+int gq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GQ_H */
