@@ -1,0 +1,474 @@
+#!/usr/bin/env python3
+"""Throughput of bucketed stochastic gradient quantization with error feedback
+on one MI355X.
+
+A step of the headline workload is one error-feedback step of ternary
+(TernGrad-style, s = 1, 2-bit) quantization over a 25.6M-element fp32 gradient
+made of 160 Laplace "layers", bucket d = 512: p = g + e, per-bucket max-abs
+scale, Philox random rounding, packing, residual write-back (one fused kernel),
+then the receiving side's unpack + dequantize + accumulate (W = 1).  Five
+seeded gradients are resident in HBM and cycled, and the residual is carried
+from step to step.
+
+Printed: ONE JSON line with the whole-job throughput (GB/s of fp32 gradient
+through quantize + dequantize), the roofline of the dominant kernel (the fused
+quantizer) from HIP events on the launch stream, the CPU oracle timed on the
+host as a baseline, and one entry per other kernel/workload (QSGD latency,
+ORQ-5/9, BinGrad-b / sign over the bucket sweep, INT8 + EF for 8 workers and
+their W = 8 aggregation).
+
+    python bench.py [--steps K] [--warmup W] [--suite main|all]
+    python bench.py --counters          # short run for rocprofv3 --pmc
+    python bench.py --ingest DIR        # turn two --pmc runs into traffic
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("GB/s of fp32 gradient quantized+packed (and dequant+accumulated); "
+          "% HBM peak")
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+VALU_PEAK_TOPS = 157.3         # fp32 vector, published (256 CU x 2.4 GHz)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+_CSRC = "communication_efficient_gradient_amd/csrc/"
+# the sources (and build flags) each measured kernel is compiled from
+KERNEL_SOURCES = {
+    "k_stream_quant": [_CSRC + "common.hpp", _CSRC + "stream_quant.hip",
+                       "communication_efficient_gradient_amd/build.py"],
+    "k_deq_acc": [_CSRC + "common.hpp", _CSRC + "deq.hip",
+                  "communication_efficient_gradient_amd/build.py"],
+}
+COPY_BYTES = 1 << 29           # known-size copy for counter calibration
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------- algorithmic bytes --
+def quant_bytes(bits: int, k: int, d: int, n: int, ef: bool) -> int:
+    """HBM bytes a quantize launch must move: g (+ e in, e out), codes, meta."""
+    nb = (n + d - 1) // d
+    return 4 * n + (8 * n if ef else 0) + (n * bits + 7) // 8 + 4 * k * nb
+
+
+def deq_bytes(bits: int, k: int, d: int, n: int, W: int, beta: float) -> int:
+    """HBM bytes of dequantize-accumulate: W payloads, out (+ out read)."""
+    nb = (n + d - 1) // d
+    per = (n * bits + 7) // 8 + 4 * k * nb
+    return W * per + 4 * n + (4 * n if beta != 0.0 else 0)
+
+
+# ------------------------------------------------------------- GPU timing --
+def load_traffic(key: str, kernel: str):
+    """HBM bytes per launch from the rocprofv3 counter runs, if they were
+    taken on the current sources of `kernel` (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = t.get(key)
+    if not ent or ent.get("source_digest") != source_digest(kernel):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+# --------------------------------------------------------------- workloads --
+class Main:
+    """Ternary + error feedback over the 25.6M-element layered gradient,
+    then dequantize (W = 1), cycling the five seeded steps."""
+
+    SEED = 2
+    KEY = "ternary_ef_d512_n25.6M"
+
+    def __init__(self, torch, gq, WL, stream):
+        self.torch, self.gq, self.stream = torch, gq, stream
+        self.n = WL.TERNARY_N
+        t0 = time.time()
+        self.host = [WL.ternary_gradient(t) for t in range(WL.TERNARY_STEPS)]
+        log(f"main: generated {len(self.host)} x {self.n} in {time.time() - t0:.1f}s")
+        self.G = [torch.from_numpy(h).cuda() for h in self.host]
+        self.E = torch.zeros(self.n, dtype=torch.float32, device="cuda")
+        self.desc = gq.desc(gq.GQ_UNIFORM, 512, s=1)
+        self.codes, self.meta = gq.alloc_payload(self.desc, self.n)
+        self.out = torch.empty(self.n, dtype=torch.float32, device="cuda")
+        self.bits = gq.gq_code_bits(self.desc)
+        self.q = [gq.PreparedQuantize(self.desc, G, self.E, self.codes,
+                                      self.meta, stream) for G in self.G]
+        self.dq = gq.PreparedDequantizeAccumulate(
+            self.desc, self.n, [self.codes], [self.meta], 1.0, 0.0, self.out,
+            stream)
+
+    def quantize(self, t: int):
+        self.q[t % len(self.q)](self.SEED, t)
+
+    def step(self, t: int):
+        self.quantize(t)
+        self.dq()
+
+    def qbytes(self):
+        return quant_bytes(self.bits, 1, 512, self.n, True)
+
+    def dbytes(self):
+        return deq_bytes(self.bits, 1, 512, self.n, 1, 0.0)
+
+
+def cpu_baseline(main: Main, min_wall: float = 1.0):
+    """The oracle on the host, on the headline workload: consecutive error-
+    feedback steps (quantize with the carried residual, then dequantize),
+    repeated until at least `min_wall` seconds have passed."""
+    import numpy as np
+
+    import oracle as O
+
+    od = O.Desc(O.UNIFORM, 512, s=1)
+    e = np.zeros(main.n, dtype=np.float32)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        g = main.host[steps % len(main.host)]
+        c, m, e, _ = O.quantize(od, g, e, seed=Main.SEED, step=steps)
+        O.dequantize_accumulate(od, g.size, [c], [m], 1.0, 0.0)
+        steps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_wall:
+            break
+    th = O.threads()
+    return {"value": round(4 * main.n * steps / dt / 1e9, 4), "unit": "GB/s",
+            "cores": th, "kind": "oracle",
+            "sample": (f"{steps} error-feedback step(s) of the headline "
+                       f"workload ({main.n} elements each): quantize + "
+                       f"dequantize, {dt:.2f} s wall on {th} OpenMP threads "
+                       f"({dt * th:.1f} thread-seconds)")}
+
+
+def time_back_to_back(torch, stream, launch, reps: int, warm: int = 3) -> float:
+    """Average duration of `reps` launches issued back to back, bracketed by
+    one pair of HIP events on the launch stream."""
+    for i in range(warm):
+        launch(i)
+    ev = torch.cuda.Event
+    a, b = ev(enable_timing=True), ev(enable_timing=True)
+    a.record(stream)
+    for i in range(reps):
+        launch(warm + i)
+    b.record(stream)
+    b.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def copy_reference(torch, stream, nbytes: int = 1 << 30) -> dict:
+    """A plain read-once / write-once pass of known size (torch's negation,
+    128-bit vectorised): what a streaming kernel reaches on this GPU."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    src.normal_()
+    dst = torch.empty_like(src)
+    ms = time_back_to_back(torch, stream,
+                           lambda i: torch.neg(src, out=dst), 20)
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": f"reference copy (read {nbytes >> 20} MiB + write)",
+            "ms": round(ms, 5), "moved_GBps": round(gbs, 2),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
+
+
+def entry(name, ms, nbytes, n, bound="hbm", extra=None):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    r = {"kernel": name, "ms": round(ms, 5),
+         "elements_per_s": round(n / (ms * 1e-3)),
+         "logical_GBps": round(4 * n / (ms * 1e-3) / 1e9, 2),
+         "moved_GBps": round(gbs, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+         "bound": bound}
+    if extra:
+        r.update(extra)
+    return r
+
+
+def suite(torch, gq, WL, stream, reps: int):
+    """Every other workload's kernels, each timed back to back."""
+    out = []
+    tb = lambda f, r=reps: time_back_to_back(torch, stream, f, r)  # noqa: E731
+
+    # QSGD s=4, 65,536 elements: cache-resident, latency-bound.
+    g = torch.from_numpy(WL.qsgd_gradient()).cuda()
+    d = gq.desc(gq.GQ_UNIFORM, 512, s=4)
+    c, m = gq.alloc_payload(d, g.numel())
+    o = torch.empty_like(g)
+    q = gq.PreparedQuantize(d, g, None, c, m, stream)
+    ms = tb(lambda i: q(0, 0))
+    out.append(entry("quantize qsgd s=4 d=512 n=65536", ms,
+                     quant_bytes(4, 1, 512, g.numel(), False), g.numel(),
+                     bound="latency"))
+    dq = gq.PreparedDequantizeAccumulate(d, g.numel(), [c], [m], 1.0, 0.0, o,
+                                         stream)
+    ms = tb(lambda i: dq())
+    out.append(entry("dequantize qsgd W=1 n=65536", ms,
+                     deq_bytes(4, 1, 512, g.numel(), 1, 0.0), g.numel(),
+                     bound="latency"))
+    del g, c, m, o, q, dq
+
+    # ORQ-5 / ORQ-9 on 100M elements, clip off / on.
+    t0 = time.time()
+    g = torch.from_numpy(WL.orq_gradient()).cuda()
+    log(f"suite: orq input in {time.time() - t0:.1f}s")
+    n = g.numel()
+    for L in (5, 9):
+        for clip in (0, 1):
+            d = gq.desc(gq.GQ_ORQ, 512, levels=L, flags=clip, clip_sigma=3.0)
+            c, m = gq.alloc_payload(d, n)
+            bits = gq.gq_code_bits(d)
+            q = gq.PreparedQuantize(d, g, None, c, m, stream)
+            ms = tb(lambda i: q(3, 0), max(3, reps // 2))
+            out.append(entry(f"quantize orq L={L} clip={clip} d=512 n={n}", ms,
+                             quant_bytes(bits, L, 512, n, False), n,
+                             bound="alu"))
+            del c, m, q
+    del g
+
+    # BinGrad-b (optimal two-level) and the sign split with error feedback,
+    # 1B elements, over the bucket sweep.
+    t0 = time.time()
+    g = torch.from_numpy(WL.bingrad_gradient()).cuda()
+    log(f"suite: bingrad input in {time.time() - t0:.1f}s")
+    n = g.numel()
+    e = torch.zeros_like(g)
+    for scheme, nm in ((gq.GQ_BIN_OPT, "bin_opt"), (gq.GQ_BIN_SIGN, "bin_sign")):
+        for dd in (128, 512, 2048, 8192, 32768):
+            d = gq.desc(scheme, dd)
+            c, m = gq.alloc_payload(d, n)
+            e.zero_()
+            q = gq.PreparedQuantize(d, g, e, c, m, stream)
+            ms = tb(lambda i: q(0, i), max(3, reps // 2))
+            out.append(entry(f"quantize {nm}+ef d={dd} n={n}", ms,
+                             quant_bytes(1, 2, dd, n, True), n))
+            del c, m, q
+    del g, e
+
+    # INT8 + EF for 8 workers of 256M each, then the W = 8 average.
+    W, n = WL.WORKERS_W, WL.WORKERS_N
+    d = gq.desc(gq.GQ_UNIFORM, 512, s=127)
+    Gs, Es, Cs, Ms = [], [], [], []
+    t0 = time.time()
+    for w in range(1, W + 1):
+        Gs.append(torch.from_numpy(WL.worker_gradient(w)).cuda())
+        Es.append(torch.zeros(n, dtype=torch.float32, device="cuda"))
+        c, m = gq.alloc_payload(d, n)
+        Cs.append(c)
+        Ms.append(m)
+    log(f"suite: worker inputs in {time.time() - t0:.1f}s")
+    qs = [gq.PreparedQuantize(d, Gs[w], Es[w], Cs[w], Ms[w], stream)
+          for w in range(W)]
+    ms = tb(lambda i: qs[i % W](i % W + 1, 0), 2 * W)
+    out.append(entry(f"quantize int8+ef d=512 n={n} (per worker)", ms,
+                     quant_bytes(8, 1, 512, n, True), n))
+    avg = torch.empty(n, dtype=torch.float32, device="cuda")
+    dq = gq.PreparedDequantizeAccumulate(d, n, Cs, Ms, 1.0 / W, 0.0, avg,
+                                         stream)
+    ms = tb(lambda i: dq())
+    out.append(entry(f"dequantize_accumulate int8 W={W} n={n}", ms,
+                     deq_bytes(8, 1, 512, n, W, 0.0), n * W))
+    del Gs, Es, Cs, Ms, avg, qs, dq
+    return out
+
+
+# ------------------------------------------------------- counter ingestion --
+def ingest(dirs):
+    """Combine two rocprofv3 --pmc runs of `bench.py --counters` (one with
+    FETCH_SIZE, one with WRITE_SIZE; rocpd databases) into
+    profiles/traffic.json.  Each counter is scaled by what it reads for the
+    known-size negation pass in the same run (COPY_BYTES read, COPY_BYTES
+    written), and each kernel's value is the median over its dispatches."""
+    import sqlite3
+
+    vals = {}
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
+            con = sqlite3.connect(path)
+            for name, cn, v in con.execute(
+                    "select kernel_name, counter_name, value "
+                    "from counters_collection"):
+                vals.setdefault((cn, name), []).append(float(v))
+            con.close()
+
+    def med(cn, pred):
+        for (c, name), v in vals.items():
+            if c == cn and pred(name):
+                v = sorted(v)
+                return name, v[len(v) // 2]
+        raise KeyError(f"{cn}: kernel not found in the counter runs")
+
+    is_copy = lambda k: "neg_kernel" in k  # noqa: E731
+    f_scale = COPY_BYTES / (med("FETCH_SIZE", is_copy)[1] * 1024.0)
+    w_scale = COPY_BYTES / (med("WRITE_SIZE", is_copy)[1] * 1024.0)
+    res = {"_calibration": {
+        "copy_bytes": COPY_BYTES, "fetch_scale": round(f_scale, 5),
+        "write_scale": round(w_scale, 5),
+        "note": ("counters are KiB per dispatch; traffic = FETCH_SIZE*1024*"
+                 "fetch_scale + WRITE_SIZE*1024*write_scale")}}
+    for key, tag in ((Main.KEY, "k_stream_quant"),
+                     (Main.KEY + ":dequantize", "k_deq_acc")):
+        kname, f = med("FETCH_SIZE", lambda k, t=tag: t in k)
+        _, w = med("WRITE_SIZE", lambda k, t=tag: t in k)
+        res[key] = {"kernel": kname, "source_digest": source_digest(tag),
+                    "fetch_kib": f, "write_kib": w,
+                    "bytes_per_launch": round(f * 1024 * f_scale +
+                                              w * 1024 * w_scale)}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(res, indent=1))
+
+
+# -------------------------------------------------------------------- main --
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--suite", choices=("main", "all"), default="all")
+    ap.add_argument("--reps", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="short run for rocprofv3 --pmc: main steps + a copy")
+    ap.add_argument("--ingest", nargs="+", metavar="DIR")
+    args = ap.parse_args()
+
+    if args.ingest:
+        ingest(args.ingest)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the quantize / dequantize path "
+              "runs on a single device with no collectives; --gpus must be 1.",
+              file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from communication_efficient_gradient_amd import gq
+    from communication_efficient_gradient_amd import workloads as WL
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    mw = Main(torch, gq, WL, stream)
+    if args.counters:
+        for t in range(4):
+            mw.step(t)
+        # calibration: one plain elementwise pass (read COPY_BYTES, write
+        # COPY_BYTES); torch's negation kernel is the only one of its kind here
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log("counters run done")
+        return 0
+
+    # ---- the timed region: K whole steps --------------------------------
+    for t in range(args.warmup):
+        mw.step(t)
+    torch.cuda.synchronize()
+    ev0, ev1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for t in range(args.warmup, args.warmup + args.steps):
+        mw.step(t)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    gpu_ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # ---- per-kernel durations: each kernel back to back ------------------
+    reps = max(20, min(args.steps, 200))
+    q_ms = time_back_to_back(torch, stream, mw.quantize, reps)
+    d_ms = time_back_to_back(torch, stream, lambda i: mw.dq(), reps)
+    n = mw.n
+    qb = mw.qbytes()
+    achieved = qb / (q_ms * 1e-3) / 1e9
+    traffic = load_traffic(Main.KEY, "k_stream_quant")
+    log(f"main: {ms_step * 1e3:.1f} us/step wall ({gpu_ms_step * 1e3:.1f} us "
+        f"GPU), quantize {q_ms * 1e3:.1f} us ({achieved:.0f} GB/s), "
+        f"dequantize {d_ms * 1e3:.1f} us")
+
+    kernels = [
+        entry("quantize ternary+ef d=512 n=25.6M (headline)", q_ms, qb, n),
+        entry("dequantize ternary W=1 n=25.6M (headline)", d_ms,
+              mw.dbytes(), n),
+    ]
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(mw)
+        log(f"cpu baseline: {cpu}")
+    if args.suite == "all":
+        del mw.q, mw.G
+        torch.cuda.empty_cache()
+        kernels.append(copy_reference(torch, stream))
+        kernels += suite(torch, gq, WL, stream, args.reps)
+
+    line = {
+        "metric": METRIC,
+        "value": round(4 * n / (ms_step * 1e-3) / 1e9, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": ("ternary (s=1, 2-bit) + error feedback, 25.6M fp32 "
+                         "elements in 160 Laplace layers, d=512, Philox "
+                         "rounding; quantize + dequantize per step"),
+            "elements": n, "bucket": 512, "code_bits": 2,
+            "hbm_bytes_per_step": qb + mw.dbytes(),
+            "gpu_ms_per_step": round(gpu_ms_step, 5),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_stream_quant (ternary, error feedback, d=512)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": qb,
+            "avg_launch_us": round(q_ms * 1e3, 3),
+        },
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

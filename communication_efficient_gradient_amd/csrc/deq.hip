@@ -4,76 +4,63 @@
 // standalone residual update of error feedback ("Gradient Quantization"
 // glossary, error-feedback paragraph).
 //
-// Output-stationary: each thread owns 16 consecutive output elements (all in
-// one bucket, since d >= 64 is a multiple of 16).  Per payload it reads the
-// 2*BITS code bytes of those elements with one load, the bucket's meta row,
-// decodes 16 codes and adds them into two fp32 accumulators (even and odd
-// payloads), so a sum of W terms is at most ceil(W/2)+1 additions deep.
+// Output-stationary and lane-contiguous: a thread owns kV float4 groups of
+// the output, group f covering elements 4f .. 4f+3 (one bucket, since d is a
+// multiple of 4), and neighbouring lanes own neighbouring groups, so every
+// 128-bit store and load of a wave covers 1 KiB of consecutive memory.  The
+// codes of a group are 4*BITS consecutive stream bits: one byte load (1, 2
+// bits), two (3 bits), a 16-bit (4 bits) or a 32-bit (8 bits) load, again
+// consecutive across lanes.  Payloads are summed in fp32 into two
+// accumulators (even and odd payloads), so a sum of W terms is at most
+// ceil(W/2)+1 additions deep.
 #include "common.hpp"
 
 namespace gq {
 namespace {
 
-constexpr int kElems = 16;   // elements per thread
 constexpr int kThreads = 256;
+constexpr int kV = 4;                       // float4 groups per thread
+constexpr int kGroupsPerBlock = kThreads * kV;
 
-// Code bytes of the thread's 16 elements: 2*BITS bytes at 2*BITS*t.  The
-// full path uses one aligned load; the last thread of a partial payload
-// reads byte by byte up to code_bytes.
+// The 4*BITS code bits of group f (elements 4f..4f+3), element 4f in the
+// lowest bits.  `full` groups lie wholly inside the stream; the last,
+// partial group reads byte by byte up to code_bytes.
 template <int BITS>
-__device__ __forceinline__ void load_chunk(const uint8_t* __restrict__ c,
-                                           int64_t t, bool full,
-                                           int64_t code_bytes, uint32_t w[4]) {
-  const int64_t off = (int64_t)2 * BITS * t;
-  w[0] = w[1] = w[2] = w[3] = 0u;
+__device__ __forceinline__ uint32_t load_codes4(const uint8_t* __restrict__ c,
+                                                int64_t f, bool full,
+                                                int64_t code_bytes) {
+  const int64_t bit0 = (int64_t)4 * BITS * f;
+  const int64_t byte0 = bit0 >> 3;
+  const int sh = (int)(bit0 & 7);
   if (full) {
-    if constexpr (BITS == 8) {
-      const uint4 v = *reinterpret_cast<const uint4*>(c + off);
-      w[0] = v.x;
-      w[1] = v.y;
-      w[2] = v.z;
-      w[3] = v.w;
-    } else if constexpr (BITS == 4) {
-      const uint2 v = *reinterpret_cast<const uint2*>(c + off);
-      w[0] = v.x;
-      w[1] = v.y;
-    } else if constexpr (BITS == 2) {
-      w[0] = *reinterpret_cast<const uint32_t*>(c + off);
-    } else if constexpr (BITS == 1) {
-      w[0] = *reinterpret_cast<const uint16_t*>(c + off);
-    } else {  // 3 bits: 6 bytes, 2-byte aligned
-      const uint16_t* h = reinterpret_cast<const uint16_t*>(c + off);
-      w[0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-      w[1] = (uint32_t)h[2];
-    }
-  } else {
-    for (int b = 0; b < 2 * BITS; ++b)
-      if (off + b < code_bytes) w[b >> 2] |= (uint32_t)c[off + b] << (8 * (b & 3));
+    if constexpr (BITS == 1) return ((uint32_t)c[byte0] >> sh) & 0xFu;
+    if constexpr (BITS == 2) return (uint32_t)c[byte0];
+    if constexpr (BITS == 3)
+      return (((uint32_t)c[byte0] | ((uint32_t)c[byte0 + 1] << 8)) >> sh) & 0xFFFu;
+    if constexpr (BITS == 4) return (uint32_t)*reinterpret_cast<const uint16_t*>(c + byte0);
+    if constexpr (BITS == 8) return *reinterpret_cast<const uint32_t*>(c + byte0);
   }
+  // bytes a group can touch: its 4*BITS bits start at bit 0 or 4 of a byte
+  uint32_t w = 0u;
+  constexpr int kBytes = BITS == 8 ? 4 : (4 * BITS + 4 + 7) / 8;
+#pragma unroll
+  for (int b = 0; b < kBytes; ++b)
+    if (byte0 + b < code_bytes) w |= (uint32_t)c[byte0 + b] << (8 * b);
+  w >>= sh;
+  return BITS == 8 ? w : (w & ((1u << (4 * BITS)) - 1u));
 }
 
-template <int BITS>
-__device__ __forceinline__ uint32_t code_at(const uint32_t w[4], int k) {
-  const int o = BITS * k;
-  if constexpr (BITS == 3) {
-    const uint64_t x = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
-    return (uint32_t)(x >> o) & 7u;
-  } else {
-    return (w[o >> 5] >> (o & 31)) & ((1u << BITS) - 1u);
-  }
-}
-
-// Dequantized value of the 16 codes of one payload.
+// Dequantized values of one group of one payload.
 template <int SCHEME, int BITS>
-__device__ __forceinline__ void dequant16(const uint32_t w[4],
-                                          const float* __restrict__ meta,
-                                          int64_t bucket, int s, int L,
-                                          float x[kElems]) {
+__device__ __forceinline__ float4 dequant4(uint32_t w,
+                                           const float* __restrict__ meta,
+                                           int64_t bucket, int s, int L) {
+  float x[4];
   if constexpr (SCHEME == UNIFORM) {
     const float delta = meta[bucket] / (float)s;
 #pragma unroll
-    for (int k = 0; k < kElems; ++k) {
-      const uint32_t u = code_at<BITS>(w, k);
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t u = (w >> (BITS * k)) & ((1u << BITS) - 1u);
       const uint32_t m = 1u << (BITS - 1);
       const int ci = (int)((u ^ m) - m);  // sign-extend
       x[k] = (float)ci * delta;
@@ -81,83 +68,89 @@ __device__ __forceinline__ void dequant16(const uint32_t w[4],
   } else if constexpr (SCHEME == BIN_SIGN || SCHEME == BIN_OPT) {
     const float a = meta[2 * bucket + 0], b = meta[2 * bucket + 1];
 #pragma unroll
-    for (int k = 0; k < kElems; ++k) x[k] = code_at<BITS>(w, k) ? b : a;
+    for (int k = 0; k < 4; ++k) x[k] = ((w >> k) & 1u) ? b : a;
   } else {
     // codes past the level table (never written by the quantizer) are
     // clamped so that no read leaves the bucket's meta row
     const float* lv = meta + bucket * L;
     const uint32_t top = (uint32_t)(L - 1);
 #pragma unroll
-    for (int k = 0; k < kElems; ++k) {
-      const uint32_t c = code_at<BITS>(w, k);
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t c = (w >> (BITS * k)) & ((1u << BITS) - 1u);
       x[k] = lv[c < top ? c : top];
     }
   }
+  return make_float4(x[0], x[1], x[2], x[3]);
+}
+
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
 template <int SCHEME, int BITS>
 __global__ __launch_bounds__(kThreads) void k_deq_acc(
     int64_t n, int d, int s, int L, int W, PayloadPtrs pp, float alpha,
     float beta, float* __restrict__ out, int64_t code_bytes) {
-  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t i0 = t * kElems;
-  if (i0 >= n) return;
-  const bool full = i0 + kElems <= n;
-  const int64_t bucket = i0 / d;
+  const int64_t ngroups = (n + 3) >> 2;
+  const int64_t f0 = (int64_t)blockIdx.x * kGroupsPerBlock + threadIdx.x;
 
-  float acc0[kElems], acc1[kElems];
-  {
-    uint32_t w[4];
-    load_chunk<BITS>(pp.codes[0], t, full, code_bytes, w);
-    dequant16<SCHEME, BITS>(w, pp.meta[0], bucket, s, L, acc0);
-  }
-  if (W > 1) {
-    uint32_t w[4];
-    load_chunk<BITS>(pp.codes[1], t, full, code_bytes, w);
-    dequant16<SCHEME, BITS>(w, pp.meta[1], bucket, s, L, acc1);
-  }
-  for (int p = 2; p < W; ++p) {
-    uint32_t w[4];
-    float x[kElems];
-    load_chunk<BITS>(pp.codes[p], t, full, code_bytes, w);
-    dequant16<SCHEME, BITS>(w, pp.meta[p], bucket, s, L, x);
-    if (p & 1) {
+  float4 acc0[kV], acc1[kV];
 #pragma unroll
-      for (int k = 0; k < kElems; ++k) acc1[k] = acc1[k] + x[k];
-    } else {
+  for (int v = 0; v < kV; ++v) {
+    acc0[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+    acc1[v] = acc0[v];
+  }
+  for (int p = 0; p < W; ++p) {
+    const uint8_t* __restrict__ c = pp.codes[p];
+    const float* __restrict__ m = pp.meta[p];
+    float4 x[kV];
 #pragma unroll
-      for (int k = 0; k < kElems; ++k) acc0[k] = acc0[k] + x[k];
+    for (int v = 0; v < kV; ++v) {
+      const int64_t f = f0 + (int64_t)kThreads * v;
+      if (f < ngroups) {
+        const bool full = 4 * f + 4 <= n;
+        x[v] = dequant4<SCHEME, BITS>(load_codes4<BITS>(c, f, full, code_bytes),
+                                      m, (4 * f) / d, s, L);
+      } else {
+        x[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    // payload 0 and 1 initialise the two accumulators (x + 0 == x exactly
+    // for every finite x except -0, which becomes +0; p == 0 copies so a
+    // single payload is reproduced bit for bit)
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+      if (p == 0) acc0[v] = x[v];
+      else if (p == 1) acc1[v] = x[v];
+      else if (p & 1) acc1[v] = add4(acc1[v], x[v]);
+      else acc0[v] = add4(acc0[v], x[v]);
     }
   }
-  if (W > 1) {
 #pragma unroll
-    for (int k = 0; k < kElems; ++k) acc0[k] = acc0[k] + acc1[k];
-  }
-
-  float* o = out + i0;
-  if (full) {
-#pragma unroll
-    for (int q = 0; q < kElems / 4; ++q) {
-      float4 r;
-      r.x = alpha * acc0[4 * q + 0];
-      r.y = alpha * acc0[4 * q + 1];
-      r.z = alpha * acc0[4 * q + 2];
-      r.w = alpha * acc0[4 * q + 3];
+  for (int v = 0; v < kV; ++v) {
+    const int64_t f = f0 + (int64_t)kThreads * v;
+    if (f >= ngroups) continue;
+    float4 a = W > 1 ? add4(acc0[v], acc1[v]) : acc0[v];
+    float4 r = make_float4(alpha * a.x, alpha * a.y, alpha * a.z, alpha * a.w);
+    float* o = out + 4 * f;
+    if (4 * f + 4 <= n) {
       if (beta != 0.f) {
-        const float4 old = reinterpret_cast<const float4*>(o)[q];
+        const float4 old = *reinterpret_cast<const float4*>(o);
         r.x = r.x + beta * old.x;
         r.y = r.y + beta * old.y;
         r.z = r.z + beta * old.z;
         r.w = r.w + beta * old.w;
       }
-      reinterpret_cast<float4*>(o)[q] = r;
-    }
-  } else {
-    for (int k = 0; k < kElems; ++k) {
-      if (i0 + k < n) {
-        float r = alpha * acc0[k];
-        if (beta != 0.f) r = r + beta * o[k];
-        o[k] = r;
+      *reinterpret_cast<float4*>(o) = r;
+    } else {
+      const int rem = (int)(n - 4 * f);
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        if (k < rem) {
+          float rk = comp(r, k);
+          if (beta != 0.f) rk = rk + beta * o[k];
+          o[k] = rk;
+        }
       }
     }
   }
@@ -168,39 +161,37 @@ __global__ __launch_bounds__(kThreads) void k_error_feedback(
     int64_t n, int d, int s, int L, const float* __restrict__ g,
     float* __restrict__ e, const uint8_t* __restrict__ codes,
     const float* __restrict__ meta, int64_t code_bytes) {
-  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t i0 = t * kElems;
-  if (i0 >= n) return;
-  const bool full = i0 + kElems <= n;
-  uint32_t w[4];
-  float x[kElems];
-  load_chunk<BITS>(codes, t, full, code_bytes, w);
-  dequant16<SCHEME, BITS>(w, meta, i0 / d, s, L, x);
-  if (full) {
+  const int64_t ngroups = (n + 3) >> 2;
+  const int64_t f0 = (int64_t)blockIdx.x * kGroupsPerBlock + threadIdx.x;
 #pragma unroll
-    for (int q = 0; q < kElems / 4; ++q) {
-      const float4 gv = reinterpret_cast<const float4*>(g + i0)[q];
-      const float4 ev = reinterpret_cast<const float4*>(e + i0)[q];
-      float4 r;
-      r.x = (gv.x + ev.x) - x[4 * q + 0];
-      r.y = (gv.y + ev.y) - x[4 * q + 1];
-      r.z = (gv.z + ev.z) - x[4 * q + 2];
-      r.w = (gv.w + ev.w) - x[4 * q + 3];
-      reinterpret_cast<float4*>(e + i0)[q] = r;
-    }
-  } else {
-    for (int k = 0; k < kElems; ++k)
-      if (i0 + k < n) e[i0 + k] = (g[i0 + k] + e[i0 + k]) - x[k];
+  for (int v = 0; v < kV; ++v) {
+    const int64_t f = f0 + (int64_t)kThreads * v;
+    if (f >= ngroups) continue;
+    const int64_t i = 4 * f;
+    const bool full = i + 4 <= n;
+    const float4 x = dequant4<SCHEME, BITS>(
+        load_codes4<BITS>(codes, f, full, code_bytes), meta, i / d, s, L);
+    const float4 gv = load4(g, i, n);
+    const float4 ev = load4(e, i, n);
+    float4 r;
+    r.x = (gv.x + ev.x) - x.x;
+    r.y = (gv.y + ev.y) - x.y;
+    r.z = (gv.z + ev.z) - x.z;
+    r.w = (gv.w + ev.w) - x.w;
+    store4(e, i, n, r);
   }
+}
+
+int64_t blocks_for(int64_t n) {
+  const int64_t ngroups = (n + 3) >> 2;
+  return (ngroups + kGroupsPerBlock - 1) / kGroupsPerBlock;
 }
 
 template <int SCHEME, int BITS>
 int deq_one(const LaunchDesc& L, int64_t n, int W, const PayloadPtrs& pp,
             float alpha, float beta, float* out, int64_t code_bytes,
             hipStream_t st) {
-  const int64_t threads = (n + kElems - 1) / kElems;
-  const int64_t blocks = (threads + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL((k_deq_acc<SCHEME, BITS>), dim3((uint32_t)blocks),
+  hipLaunchKernelGGL((k_deq_acc<SCHEME, BITS>), dim3((uint32_t)blocks_for(n)),
                      dim3(kThreads), 0, st, n, L.d, L.s, L.L, W, pp, alpha,
                      beta, out, code_bytes);
   return (int)hipGetLastError();
@@ -210,11 +201,9 @@ template <int SCHEME, int BITS>
 int ef_one(const LaunchDesc& L, int64_t n, const float* g, float* e,
            const uint8_t* codes, const float* meta, int64_t code_bytes,
            hipStream_t st) {
-  const int64_t threads = (n + kElems - 1) / kElems;
-  const int64_t blocks = (threads + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL((k_error_feedback<SCHEME, BITS>), dim3((uint32_t)blocks),
-                     dim3(kThreads), 0, st, n, L.d, L.s, L.L, g, e, codes, meta,
-                     code_bytes);
+  hipLaunchKernelGGL((k_error_feedback<SCHEME, BITS>),
+                     dim3((uint32_t)blocks_for(n)), dim3(kThreads), 0, st, n,
+                     L.d, L.s, L.L, g, e, codes, meta, code_bytes);
   return (int)hipGetLastError();
 }
 

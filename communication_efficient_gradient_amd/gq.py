@@ -207,3 +207,51 @@ def gq_dequantize_accumulate(d: gq_desc, n: int,
     _check(_lib.gq_dequantize_accumulate(
         C.byref(d), n, W, cp, mp, alpha, beta, _ptr(out, torch.float32, "out"),
         _stream(stream, out)), "gq_dequantize_accumulate")
+
+
+# ---------------------------------------------------------------------------
+# Prepared calls: validate and marshal the arguments once, then re-issue the
+# same launch with only (seed, step) changing.  For launch loops where the
+# per-call Python checks above would otherwise dominate a ~10 us kernel.
+class PreparedQuantize:
+    def __init__(self, d: gq_desc, g: torch.Tensor, e: torch.Tensor | None,
+                 codes: torch.Tensor, meta: torch.Tensor, stream=None):
+        if e is not None and e.numel() != g.numel():
+            raise ValueError("e must have g's size")
+        _, cap, mf = gq_payload_size(d, g.numel())
+        _need(codes, cap, "codes")
+        _need(meta, mf, "meta")
+        self._keep = (d, g, e, codes, meta)
+        self._args = (C.byref(d), g.numel(), _ptr(g, torch.float32, "g"),
+                      _ptr(e, torch.float32, "e"))
+        self._tail = (_ptr(codes, torch.uint8, "codes"),
+                      _ptr(meta, torch.float32, "meta"), _stream(stream, g))
+
+    def __call__(self, seed: int, step: int) -> None:
+        _check(_lib.gq_quantize(*self._args, seed, step, *self._tail),
+               "gq_quantize")
+
+
+class PreparedDequantizeAccumulate:
+    def __init__(self, d: gq_desc, n: int, codes: Sequence[torch.Tensor],
+                 meta: Sequence[torch.Tensor], alpha: float, beta: float,
+                 out: torch.Tensor, stream=None):
+        W = len(codes)
+        if len(meta) != W or not 1 <= W <= GQ_MAX_PAYLOADS:
+            raise ValueError("need 1..GQ_MAX_PAYLOADS (codes, meta) pairs")
+        if out.numel() < n:
+            raise ValueError("out is smaller than n")
+        cb, _, mf = gq_payload_size(d, n)
+        for c, m in zip(codes, meta):
+            _need(c, cb, "codes")
+            _need(m, mf, "meta")
+        self._keep = (d, list(codes), list(meta), out)
+        cp = (C.c_void_p * W)(*[_ptr(c, torch.uint8, "codes") for c in codes])
+        mp = (C.c_void_p * W)(*[_ptr(m, torch.float32, "meta") for m in meta])
+        self._ptrs = (cp, mp)
+        self._args = (C.byref(d), n, W, cp, mp, alpha, beta,
+                      _ptr(out, torch.float32, "out"), _stream(stream, out))
+
+    def __call__(self) -> None:
+        _check(_lib.gq_dequantize_accumulate(*self._args),
+               "gq_dequantize_accumulate")
