@@ -179,6 +179,50 @@ __device__ __forceinline__ void store_field(uint8_t* __restrict__ codes,
   }
 }
 
+// Store the codes of VEC consecutive elements (idx .. idx+VEC-1, idx a
+// multiple of VEC) held by this lane as one VEC*BITS-bit field, element idx
+// in the lowest bits.  The lanes of a wave must hold consecutive VEC-element
+// chunks (lane t chunk c0 + t): K = 32/(VEC*BITS) neighbouring lanes OR their
+// fields into one 32-bit stream word, and for BITS = 3 the 32/VEC lanes that
+// cover 32 elements build three words.  Words that start at or past
+// code_bytes are skipped (the buffer holds code_bytes rounded up to 16).
+template <int BITS, int VEC>
+__device__ __forceinline__ void store_chunk(uint8_t* __restrict__ codes,
+                                            int64_t idx, int lane,
+                                            uint32_t field, int64_t code_bytes) {
+  constexpr int FB = VEC * BITS;
+  if constexpr (BITS == 3) {
+    constexpr int Q = 32 / VEC;
+    const int q = lane & (Q - 1);
+    const int off = FB * q;
+    const uint64_t x = (uint64_t)field << (off & 31);
+    const int wi = off >> 5;
+    uint32_t w0 = wi == 0 ? (uint32_t)x : 0u;
+    uint32_t w1 = wi == 1 ? (uint32_t)x : (wi == 0 ? (uint32_t)(x >> 32) : 0u);
+    uint32_t w2 = wi == 2 ? (uint32_t)x : (wi == 1 ? (uint32_t)(x >> 32) : 0u);
+    w0 = group_or<Q>(w0);
+    w1 = group_or<Q>(w1);
+    w2 = group_or<Q>(w2);
+    if (q < 3) {
+      const int64_t first = idx - (int64_t)VEC * q;
+      const int64_t byte = (first >> 5) * 12 + 4 * q;
+      if (byte < code_bytes) {
+        const uint32_t w = q == 0 ? w0 : (q == 1 ? w1 : w2);
+        *reinterpret_cast<uint32_t*>(codes + byte) = w;
+      }
+    }
+  } else {
+    constexpr int K = 32 / FB;
+    const int q = lane & (K - 1);
+    uint32_t w = K > 1 ? field << (FB * q) : field;
+    w = group_or<K>(w);
+    if (q == 0) {
+      const int64_t byte = (idx * BITS) >> 3;
+      if (byte < code_bytes) *reinterpret_cast<uint32_t*>(codes + byte) = w;
+    }
+  }
+}
+
 }  // namespace gq
 
 // ----------------------------------------------------- host launchers --

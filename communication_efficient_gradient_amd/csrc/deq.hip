@@ -100,30 +100,54 @@ __global__ __launch_bounds__(kThreads) void k_deq_acc(
     acc0[v] = make_float4(0.f, 0.f, 0.f, 0.f);
     acc1[v] = acc0[v];
   }
-  for (int p = 0; p < W; ++p) {
-    const uint8_t* __restrict__ c = pp.codes[p];
-    const float* __restrict__ m = pp.meta[p];
-    float4 x[kV];
+  // Payloads two at a time: both payloads' code and meta loads are issued
+  // before any arithmetic, so a wave keeps 2*kV loads in flight.  Payload
+  // 0 and 1 initialise the two accumulators (a copy, so a single payload is
+  // reproduced bit for bit), later even / odd payloads add into them.
+  int p = 0;
+  for (; p + 2 <= W; p += 2) {
+    uint32_t w0[kV], w1[kV];
+    const uint8_t* __restrict__ c0 = pp.codes[p];
+    const uint8_t* __restrict__ c1 = pp.codes[p + 1];
 #pragma unroll
     for (int v = 0; v < kV; ++v) {
       const int64_t f = f0 + (int64_t)kThreads * v;
-      if (f < ngroups) {
-        const bool full = 4 * f + 4 <= n;
-        x[v] = dequant4<SCHEME, BITS>(load_codes4<BITS>(c, f, full, code_bytes),
-                                      m, (4 * f) / d, s, L);
-      } else {
-        x[v] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      const bool ok = f < ngroups;
+      const bool full = 4 * f + 4 <= n;
+      w0[v] = ok ? load_codes4<BITS>(c0, f, full, code_bytes) : 0u;
+      w1[v] = ok ? load_codes4<BITS>(c1, f, full, code_bytes) : 0u;
     }
-    // payload 0 and 1 initialise the two accumulators (x + 0 == x exactly
-    // for every finite x except -0, which becomes +0; p == 0 copies so a
-    // single payload is reproduced bit for bit)
 #pragma unroll
     for (int v = 0; v < kV; ++v) {
-      if (p == 0) acc0[v] = x[v];
-      else if (p == 1) acc1[v] = x[v];
-      else if (p & 1) acc1[v] = add4(acc1[v], x[v]);
-      else acc0[v] = add4(acc0[v], x[v]);
+      const int64_t f = f0 + (int64_t)kThreads * v;
+      if (f >= ngroups) continue;
+      const int64_t b = (4 * f) / d;
+      const float4 x0 = dequant4<SCHEME, BITS>(w0[v], pp.meta[p], b, s, L);
+      const float4 x1 = dequant4<SCHEME, BITS>(w1[v], pp.meta[p + 1], b, s, L);
+      if (p == 0) {
+        acc0[v] = x0;
+        acc1[v] = x1;
+      } else {
+        acc0[v] = add4(acc0[v], x0);
+        acc1[v] = add4(acc1[v], x1);
+      }
+    }
+  }
+  if (p < W) {  // odd W: the last payload is even-numbered
+    const uint8_t* __restrict__ c0 = pp.codes[p];
+    uint32_t w0[kV];
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+      const int64_t f = f0 + (int64_t)kThreads * v;
+      w0[v] = f < ngroups ? load_codes4<BITS>(c0, f, 4 * f + 4 <= n, code_bytes)
+                          : 0u;
+    }
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+      const int64_t f = f0 + (int64_t)kThreads * v;
+      if (f >= ngroups) continue;
+      const float4 x0 = dequant4<SCHEME, BITS>(w0[v], pp.meta[p], (4 * f) / d, s, L);
+      acc0[v] = p == 0 ? x0 : add4(acc0[v], x0);
     }
   }
 #pragma unroll

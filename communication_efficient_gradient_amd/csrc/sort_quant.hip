@@ -565,16 +565,446 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
   }
 }
 
+// ------------------------------------------------- one wave per bucket --
+// d <= 512: a wavefront owns a bucket and keeps it in registers, E = d/64
+// values per lane, kWaveBuckets buckets per workgroup.  Element order (I/O):
+// lane t holds elements VEC*(t + 64*q) + c, q < E/VEC, c < VEC, so each load
+// instruction of the wave reads 64*VEC consecutive floats.  Sorted order:
+// lane t holds sorted positions t*E .. t*E+E-1.  The bitonic network runs in
+// registers (partners in the same lane: compare-exchange; partners j/E
+// lanes away: __shfl_xor), so the sort needs no LDS and no barrier.  The
+// selection steps are those of the workgroup kernel above, with wave-wide
+// scans and argmax.
+constexpr int kWaveBuckets = 4;
+
+template <int E>
+__device__ __forceinline__ void wave_bitonic(float (&y)[E], int lane) {
+  constexpr int N = 64 * E;
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= E) {
+        const int lj = j / E;
+        const bool lower = (lane & lj) == 0;
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          const bool up = ((lane * E + r) & k) == 0;
+          const float o = __shfl_xor(y[r], lj, 64);
+          y[r] = (lower == up) ? fminf(y[r], o) : fmaxf(y[r], o);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          if (r & j) continue;
+          const bool up = ((lane * E + r) & k) == 0;
+          const float a = y[r], b = y[r | j];
+          const float lo = fminf(a, b), hi = fmaxf(a, b);
+          y[r] = up ? lo : hi;
+          y[r | j] = up ? hi : lo;
+        }
+      }
+    }
+  }
+}
+
+// Sorted value at wave-uniform position pos.
+template <int E>
+__device__ __forceinline__ float wave_at(const float (&y)[E], int pos) {
+  float v = y[0];
+#pragma unroll
+  for (int r = 1; r < E; ++r)
+    if ((pos % E) == r) v = y[r];
+  return __shfl(v, pos / E, 64);
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_vec(const float* __restrict__ a,
+                                         int64_t i, int64_t n, float (&x)[VEC]) {
+  if constexpr (VEC == 4) {
+    const float4 v = load4(a, i, n);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  } else {
+    if (i + VEC <= n) {
+      if constexpr (VEC == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(a + i);
+        x[0] = v.x; x[1] = v.y;
+      } else {
+        x[0] = a[i];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) x[c] = (i + c < n) ? a[i + c] : 0.f;
+    }
+  }
+}
+
+template <int VEC>
+__device__ __forceinline__ void store_vec(float* __restrict__ a, int64_t i,
+                                          int64_t n, const float (&x)[VEC]) {
+  if constexpr (VEC == 4) {
+    store4(a, i, n, make_float4(x[0], x[1], x[2], x[3]));
+  } else {
+    if (i + VEC <= n) {
+      if constexpr (VEC == 2) *reinterpret_cast<float2*>(a + i) = make_float2(x[0], x[1]);
+      else a[i] = x[0];
+    } else {
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) if (i + c < n) a[i + c] = x[c];
+    }
+  }
+}
+
+template <int SCHEME, int BITS, int D>
+__global__ __launch_bounds__(64 * kWaveBuckets) void k_wave_sort_quant(
+    int64_t n, int64_t nb, const float* __restrict__ g, float* __restrict__ e,
+    uint32_t k0, uint32_t k1, uint32_t step, int L, int clip, float clip_sigma,
+    uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes) {
+  constexpr int E = D / 64;
+  constexpr int VEC = E < 4 ? E : 4;
+  constexpr int NQ = E / VEC;
+  const int lane = threadIdx.x & 63;
+  const int64_t bucket = (int64_t)blockIdx.x * kWaveBuckets + (threadIdx.x >> 6);
+  if (bucket >= nb) return;  // whole waves leave together
+  const int64_t base = bucket * D;
+  const int nj = (int)((n - base) < D ? (n - base) : D);
+
+  // ---- 1. load p = g (+ e), element order --------------------------------
+  float p[E];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int64_t i = base + (int64_t)VEC * (lane + 64 * q);
+    float x[VEC];
+    load_vec<VEC>(g, i, n, x);
+    if (e != nullptr) {
+      float r[VEC];
+      load_vec<VEC>(e, i, n, r);
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) x[c] = x[c] + r[c];
+    }
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) p[VEC * q + c] = x[c];
+  }
+  auto epos = [&](int m) { return VEC * (lane + 64 * (m / VEC)) + (m % VEC); };
+
+  // ---- 2. clip (ORQ) -----------------------------------------------------
+  float pc[E];
+#pragma unroll
+  for (int m = 0; m < E; ++m) pc[m] = p[m];
+  if (SCHEME == ORQ && clip) {
+    Sum2 sq{0.0, 0.0};
+#pragma unroll
+    for (int m = 0; m < E; ++m)
+      if (epos(m) < nj) two_sum_add(sq, (double)p[m] * (double)p[m]);
+    sq = group_sum2<64>(sq);
+    const double sigma = sqrt((sq.s + sq.c) / (double)nj);
+    const float C = (float)((double)clip_sigma * sigma);
+#pragma unroll
+    for (int m = 0; m < E; ++m) pc[m] = fminf(fmaxf(p[m], -C), C);
+  }
+
+  // ---- 3. sort in registers (canonical +0, +inf padding) -----------------
+  float y[E];
+#pragma unroll
+  for (int m = 0; m < E; ++m)
+    y[m] = epos(m) < nj ? (pc[m] == 0.f ? 0.f : pc[m]) : __builtin_inff();
+  wave_bitonic<E>(y, lane);
+
+  const int r0 = lane * E;
+  float y_next_run = __shfl_down(y[0], 1, 64);
+  if (lane == 63) y_next_run = __builtin_inff();
+  float y_prev_run = __shfl_up(y[E - 1], 1, 64);
+  if (lane == 0) y_prev_run = -__builtin_inff();
+
+  float lvl_a = 0.f, lvl_b = 0.f, thr = 0.f;
+  bool no_split = false;
+  float lv[16];
+
+  if constexpr (SCHEME == BIN_OPT) {
+    // ---- 4a. best split -------------------------------------------------
+    double tot = 0.0;
+#pragma unroll
+    for (int m = 0; m < E; ++m)
+      if (r0 + m < nj) tot = tot + (double)y[m];
+    const double pre = block_seg_carry<64, false>(false, tot, nullptr, nullptr);
+    const double suf = block_seg_carry<64, true>(false, tot, nullptr, nullptr);
+    double Qrun[E];
+    {
+      double acc = suf;
+#pragma unroll
+      for (int m = E - 1; m >= 0; --m) {
+        Qrun[m] = acc;
+        if (r0 + m < nj) acc = acc + (double)y[m];
+      }
+    }
+    double best = -1.0;
+    int bestk = 0x7fffffff;
+    double P = pre;
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+      const int pos = r0 + m;
+      if (pos < nj) P = P + (double)y[m];
+      const int k = pos + 1;
+      if (k < nj) {
+        const float yk = (m + 1 < E) ? y[m + 1] : y_next_run;
+        if (y[m] < yk) {
+          const double F = P * P / (double)k + Qrun[m] * Qrun[m] / (double)(nj - k);
+          if (F > best) {
+            best = F;
+            bestk = k;
+          }
+        }
+      }
+    }
+    double bestF;
+    const int kstar = block_argmax<64>(best, bestk, nullptr, nullptr, &bestF);
+    if (bestF < 0.0) {
+      no_split = true;
+      thr = wave_at<E>(y, 0);
+      lvl_a = lvl_b = thr;
+    } else {
+      thr = wave_at<E>(y, kstar);
+      Sum2 lo{0.0, 0.0}, hi{0.0, 0.0};
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        const int pos = r0 + m;
+        if (pos < kstar) two_sum_add(lo, (double)y[m]);
+        else if (pos < nj) two_sum_add(hi, (double)y[m]);
+      }
+      lo = group_sum2<64>(lo);
+      hi = group_sum2<64>(hi);
+      lvl_a = (float)((lo.s + lo.c) / (double)kstar);
+      lvl_b = (float)((hi.s + hi.c) / (double)(nj - kstar));
+    }
+    if (lane == 0) {
+      meta[2 * bucket + 0] = lvl_a;
+      meta[2 * bucket + 1] = lvl_b;
+    }
+  } else {
+    // ---- 4b. ORQ greedy levels (lv[j] = +inf past the current count) ------
+    const float ymin = wave_at<E>(y, 0), ymax = wave_at<E>(y, nj - 1);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) lv[j] = __builtin_inff();
+    lv[0] = ymin;
+    lv[1] = ymax;
+    int cnt = 2;
+    if (ymin == ymax) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) lv[j] = j < L ? ymin : __builtin_inff();
+      cnt = L;
+    }
+    while (cnt < L) {
+      int seg[E];
+      float a_of[E], b_of[E];
+      bool head[E], tail[E];
+      double va[E], vb[E];
+      int seg_prev = -1, seg_next = -1;
+      if (r0 > 0) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (lv[j] <= y_prev_run) seg_prev = j;
+      }
+      if (r0 + E < nj) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (lv[j] <= y_next_run) seg_next = j;
+      }
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        const float yv = y[m];
+        int sj = 0;
+        float a = lv[0], b = lv[0];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if (lv[j] <= yv) {
+            sj = j;
+            a = lv[j];
+            b = (j + 1 < 16 && j + 1 < cnt) ? lv[j + 1 < 16 ? j + 1 : 15] : lv[j];
+          }
+        }
+        seg[m] = sj;
+        a_of[m] = a;
+        b_of[m] = b;
+        const bool real = r0 + m < nj;
+        va[m] = real ? (double)yv - (double)a : 0.0;
+        vb[m] = real ? (double)b - (double)yv : 0.0;
+      }
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        head[m] = (m == 0) ? (seg_prev != seg[0]) : (seg[m] != seg[m - 1]);
+        tail[m] = (m == E - 1) ? (seg_next != seg[E - 1]) : (seg[m] != seg[m + 1]);
+      }
+      bool fa = false, fb = false;
+      double sa = 0.0, sb = 0.0;
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        if (head[m]) {
+          fa = true;
+          sa = va[m];
+        } else {
+          sa = sa + va[m];
+        }
+      }
+#pragma unroll
+      for (int m = E - 1; m >= 0; --m) {
+        if (tail[m]) {
+          fb = true;
+          sb = vb[m];
+        } else {
+          sb = sb + vb[m];
+        }
+      }
+      const double ca = block_seg_carry<64, false>(fa, sa, nullptr, nullptr);
+      const double cb = block_seg_carry<64, true>(fb, sb, nullptr, nullptr);
+      double B[E];
+      {
+        double run = cb;
+#pragma unroll
+        for (int m = E - 1; m >= 0; --m) {
+          if (tail[m]) {
+            B[m] = 0.0;
+            run = vb[m];
+          } else {
+            B[m] = run;
+            run = run + vb[m];
+          }
+        }
+      }
+      double best = -1.0;
+      int bestk = 0x7fffffff;
+      {
+        double A = ca;
+#pragma unroll
+        for (int m = 0; m < E; ++m) {
+          A = head[m] ? va[m] : A + va[m];
+          const int pos = r0 + m;
+          const float yv = y[m];
+          const float ynext = (m + 1 < E) ? y[m + 1] : y_next_run;
+          const bool cand = pos < nj && seg[m] + 1 < cnt && yv > a_of[m] &&
+                            (pos + 1 >= nj || ynext != yv);
+          if (cand) {
+            const double c = (double)yv;
+            const double G = ((double)b_of[m] - c) * A + (c - (double)a_of[m]) * B[m];
+            if (G > best) {
+              best = G;
+              bestk = pos;
+            }
+          }
+        }
+      }
+      double bestG;
+      const int kstar = block_argmax<64>(best, bestk, nullptr, nullptr, &bestG);
+      if (bestG < 0.0) {
+        // fewer distinct values than levels: repeat the maximum
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (j >= cnt && j < L) lv[j] = ymax;
+        cnt = L;
+      } else {
+        // insert c after every level <= c (levels stay ascending)
+        const float c = wave_at<E>(y, kstar);
+        int ins = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) ins += (lv[j] <= c) ? 1 : 0;
+        float nl[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          nl[j] = j < ins ? lv[j] : (j == ins ? c : lv[j > 0 ? j - 1 : 0]);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) lv[j] = nl[j];
+        ++cnt;
+      }
+    }
+    float mine = lv[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j)
+      if (lane == j) mine = lv[j];
+    if (lane < L) meta[bucket * L + lane] = mine;
+  }
+
+  if (codes == nullptr) return;  // levels only
+
+  // ---- 5. codes, packing, residual (element order) ----------------------
+  if constexpr (SCHEME == ORQ) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j >= L) lv[j] = __builtin_inff();
+  }
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int64_t i0 = base + (int64_t)VEC * (lane + 64 * q);
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (SCHEME == ORQ) {
+      const uint64_t ctr = (uint64_t)i0 >> 2;
+      w = philox4x32_10(k0, k1, (uint32_t)ctr, (uint32_t)(ctr >> 32), step, 0u);
+    }
+    uint32_t field = 0u;
+    float r[VEC];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) {
+      const int m = VEC * q + c;
+      const int64_t i = i0 + c;
+      const bool real = i < n;
+      uint32_t code = 0u;
+      float xh = 0.f;
+      if constexpr (SCHEME == BIN_OPT) {
+        code = (!no_split && pc[m] >= thr) ? 1u : 0u;
+        xh = code ? lvl_b : lvl_a;
+      } else {
+        const float x = pc[m];
+        int first_eq = -1, below = 0;
+#pragma unroll
+        for (int j = 15; j >= 0; --j)
+          if (j < L && lv[j] == x) first_eq = j;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (j < L && lv[j] < x) below = j;
+        if (first_eq >= 0) {
+          code = (uint32_t)first_eq;
+        } else {
+          const int sub = (int)(i & 3);
+          const uint32_t word = sub == 0 ? w.x : sub == 1 ? w.y : sub == 2 ? w.z : w.w;
+          float lo = lv[0], hi = lv[1];
+#pragma unroll
+          for (int j = 0; j < 15; ++j)
+            if (j == below) {
+              lo = lv[j];
+              hi = lv[j + 1];
+            }
+          const float qf = (x - lo) / (hi - lo);
+          code = (uint32_t)(below + (u24(word) < qf ? 1 : 0));
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if ((uint32_t)j == code) xh = lv[j];
+      }
+      if (!real) code = 0u;
+      field |= code << (BITS * c);
+      r[c] = p[m] - xh;
+    }
+    store_chunk<BITS, VEC>(codes, i0, lane, field, code_bytes);
+    if (e != nullptr && i0 < n) store_vec<VEC>(e, i0, n, r);
+  }
+}
+
 template <int SCHEME, int BITS, int D>
 int launch_sort_one(int64_t n, const float* g, float* e, uint64_t seed,
                     uint32_t step, int L, int clip, float clip_sigma,
                     uint8_t* codes, float* meta, int64_t code_bytes,
                     hipStream_t st) {
   const int64_t nb = (n + D - 1) / D;
-  hipLaunchKernelGGL((k_sort_quant<SCHEME, BITS, D>), dim3((uint32_t)nb),
-                     dim3(SortCfg<D>::T), 0, st, n, g, e, (uint32_t)seed,
-                     (uint32_t)(seed >> 32), step, L, clip, clip_sigma, codes,
-                     meta, code_bytes);
+  if constexpr (D <= 512) {
+    const int64_t blocks = (nb + kWaveBuckets - 1) / kWaveBuckets;
+    hipLaunchKernelGGL((k_wave_sort_quant<SCHEME, BITS, D>), dim3((uint32_t)blocks),
+                       dim3(64 * kWaveBuckets), 0, st, n, nb, g, e,
+                       (uint32_t)seed, (uint32_t)(seed >> 32), step, L, clip,
+                       clip_sigma, codes, meta, code_bytes);
+  } else {
+    hipLaunchKernelGGL((k_sort_quant<SCHEME, BITS, D>), dim3((uint32_t)nb),
+                       dim3(SortCfg<D>::T), 0, st, n, g, e, (uint32_t)seed,
+                       (uint32_t)(seed >> 32), step, L, clip, clip_sigma, codes,
+                       meta, code_bytes);
+  }
   return (int)hipGetLastError();
 }
 

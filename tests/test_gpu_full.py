@@ -1,0 +1,226 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration
+bench.py times (one gq_quantize / gq_dequantize_accumulate call over the
+whole gradient).
+
+The HIP library runs on the full gradient; the CPU oracle recomputes runs of
+consecutive buckets (always the first and the partial last one) from the
+same seeded inputs, with the same global element index for the random
+counter, and the two are compared element by element on those runs.  The
+ternary workload is small enough to be compared whole, over its five
+error-feedback steps.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from communication_efficient_gradient_amd import workloads as WL
+from tests.parity import (bucket_mask, compare_codes, compare_meta,
+                          compare_values, sample_runs, say)
+
+pytestmark = pytest.mark.gpu
+
+RUNS, RUN_LEN = 12, 16
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from communication_efficient_gradient_amd import gq
+    return gq, torch
+
+
+def gdesc(gq, d: O.Desc):
+    return gq.desc(d.scheme, d.d, d.s, d.L, d.flags, d.clip_sigma)
+
+
+def byte_range(d: O.Desc, lo: int, hi: int):
+    """Code bytes of elements [lo, hi) (lo is a bucket start)."""
+    return lo * d.bits // 8, (hi * d.bits + 7) // 8
+
+
+def check_runs(d: O.Desc, n, g_host, e_old_host, gpu_codes, gpu_meta,
+               gpu_e_new, seed, step, runs):
+    """Compare sampled bucket runs; returns {run start: oracle tie flags}.
+
+    g_host / e_old_host are callables (lo, hi) -> fp32 host arrays;
+    gpu_* are device tensors of the whole payload / residual."""
+    nb = d.nb(n)
+    exact = d.scheme in (O.UNIFORM, O.BIN_SIGN)
+    ties = 0
+    for j0 in runs:
+        j1 = min(nb, j0 + RUN_LEN)
+        lo, hi = j0 * d.d, min(n, j1 * d.d)
+        g = g_host(lo, hi)
+        e = None if e_old_host is None else e_old_host(lo, hi)
+        rc, rm, re_, tie = O.quantize(d, g, e, seed=seed, step=step, i0=lo)
+        b0, b1 = byte_range(d, lo, hi)
+        gc = gpu_codes[b0:b1].cpu().numpy()
+        gm = gpu_meta[j0 * d.k: j1 * d.k].cpu().numpy().reshape(-1, d.k)
+        bad = compare_codes(d, hi - lo, gc, rc, tie, exact=exact)
+        ties += int(tie.sum())
+        if d.scheme == O.UNIFORM:
+            compare_meta(d, gm, rm, exact=True)
+        else:
+            compare_meta(d, gm, rm, skip=bad)
+        if e is not None:
+            ge = gpu_e_new[lo:hi].cpu().numpy()
+            p = (g + e).astype(np.float64)
+            m = bucket_mask(d, hi - lo, bad)
+            scale = np.maximum(np.abs(p), np.abs(p - re_))
+            compare_values(ge[m], re_[m], scale[m],
+                           exact=(d.scheme == O.UNIFORM),
+                           extra=1e-5 * np.abs(p - re_)[m])
+    return ties
+
+
+def test_qsgd_whole(dev):
+    gq, torch = dev
+    d = O.Desc(O.UNIFORM, 512, s=4)
+    g = WL.qsgd_gradient()
+    n = g.size
+    say(f"qsgd n={n}")
+    G = torch.from_numpy(g).cuda()
+    codes, meta = gq.alloc_payload(gdesc(gq, d), n)
+    out = torch.empty(n, device="cuda")
+    gq.gq_quantize(gdesc(gq, d), G, None, 0, 0, codes, meta)
+    gq.gq_dequantize_accumulate(gdesc(gq, d), n, [codes], [meta], 1.0, 0.0, out)
+    torch.cuda.synchronize()
+    rc, rm, _, _ = O.quantize(d, g, None, seed=0, step=0)
+    compare_codes(d, n, codes.cpu().numpy(), rc)
+    compare_meta(d, meta.cpu().numpy().reshape(-1, 1), rm, exact=True)
+    xr = O.dequantize(d, n, rc, rm)
+    compare_values(out.cpu().numpy(), xr, np.abs(xr), exact=True)
+
+
+def test_ternary_ef_five_steps_whole(dev):
+    """All 25.6M elements, five steps; both sides carry their own residual
+    (uniform residuals are bit-exact, so nothing can drift apart)."""
+    gq, torch = dev
+    d = O.Desc(O.UNIFORM, 512, s=1)
+    n = WL.TERNARY_N
+    E = torch.zeros(n, device="cuda")
+    e_ref = np.zeros(n, dtype=np.float32)
+    codes, meta = gq.alloc_payload(gdesc(gq, d), n)
+    out = torch.empty(n, device="cuda")
+    for t in range(WL.TERNARY_STEPS):
+        say(f"ternary step {t}")
+        g = WL.ternary_gradient(t)
+        gq.gq_quantize(gdesc(gq, d), torch.from_numpy(g).cuda(), E, 2, t,
+                       codes, meta)
+        gq.gq_dequantize_accumulate(gdesc(gq, d), n, [codes], [meta], 1.0,
+                                    0.0, out)
+        torch.cuda.synchronize()
+        rc, rm, e_ref, _ = O.quantize(d, g, e_ref, seed=2, step=t)
+        compare_codes(d, n, codes.cpu().numpy(), rc)
+        compare_meta(d, meta.cpu().numpy().reshape(-1, 1), rm, exact=True)
+        assert np.array_equal(E.cpu().numpy().view(np.uint32),
+                              e_ref.view(np.uint32)), f"residual, step {t}"
+        xr = O.dequantize(d, n, rc, rm)
+        assert np.array_equal(out.cpu().numpy().view(np.uint32),
+                              xr.view(np.uint32)), f"dequantized, step {t}"
+
+
+@pytest.mark.parametrize("L,clip", [(5, 0), (5, 1), (9, 0), (9, 1)])
+def test_orq_100m_sampled(dev, L, clip):
+    gq, torch = dev
+    d = O.Desc(O.ORQ, 512, L=L, flags=clip, clip_sigma=3.0)
+    n = WL.ORQ_N
+    say(f"orq L={L} clip={clip} n={n}")
+    g = WL.orq_gradient()
+    G = torch.from_numpy(g).cuda()
+    codes, meta = gq.alloc_payload(gdesc(gq, d), n)
+    gq.gq_quantize(gdesc(gq, d), G, None, 3, 0, codes, meta)
+    torch.cuda.synchronize()
+    runs = sample_runs(d.nb(n), RUNS, RUN_LEN, seed=L + 10 * clip)
+    check_runs(d, n, lambda lo, hi: g[lo:hi], None, codes, meta, None, 3, 0,
+               runs)
+    # every code names a level of its bucket, on the whole payload
+    v = O.unpack(d.bits, n, codes.cpu().numpy())
+    assert int(v.max()) < L
+
+
+@pytest.mark.parametrize("bucket", [128, 512, 2048, 8192, 32768])
+@pytest.mark.parametrize("scheme", [O.BIN_OPT, O.BIN_SIGN])
+def test_bingrad_1b_two_steps_sampled(dev, bucket, scheme):
+    """1B elements, two error-feedback steps on the same gradient.  For the
+    sorted scheme the oracle's step 1 starts from the GPU's step-0 residual
+    (checked within tolerance first), so ulp-level level differences cannot
+    cascade."""
+    gq, torch = dev
+    d = O.Desc(scheme, bucket)
+    n = WL.BINGRAD_N
+    say(f"bingrad scheme={scheme} d={bucket} n={n}")
+    g = _bingrad_host()
+    G = torch.from_numpy(g).cuda()
+    E = torch.zeros(n, device="cuda")
+    codes, meta = gq.alloc_payload(gdesc(gq, d), n)
+    runs = sample_runs(d.nb(n), RUNS, RUN_LEN, seed=bucket + scheme)
+    e_prev = None
+    for step in (0, 1):
+        gq.gq_quantize(gdesc(gq, d), G, E, 0, step, codes, meta)
+        torch.cuda.synchronize()
+        if step == 0:
+            e_old = lambda lo, hi: np.zeros(hi - lo, dtype=np.float32)  # noqa: E731
+        else:
+            e_old = lambda lo, hi: e_prev[(lo, hi)]  # noqa: E731
+        check_runs(d, n, lambda lo, hi: g[lo:hi], e_old, codes, meta, E, 0,
+                   step, runs)
+        nb = d.nb(n)
+        e_prev = {}
+        for j0 in runs:
+            lo, hi = j0 * bucket, min(n, min(nb, j0 + RUN_LEN) * bucket)
+            e_prev[(lo, hi)] = E[lo:hi].cpu().numpy()
+    del G, E, codes, meta
+    torch.cuda.empty_cache()
+
+
+_BINGRAD = {}
+
+
+def _bingrad_host():
+    if "g" not in _BINGRAD:
+        _BINGRAD["g"] = WL.bingrad_gradient()
+    return _BINGRAD["g"]
+
+
+def test_eight_workers_int8_ef_and_average(dev):
+    """8 x 256M INT8 + EF quantizations, then the W = 8 average over all
+    256M outputs, compared on sampled bucket runs."""
+    gq, torch = dev
+    d = O.Desc(O.UNIFORM, 512, s=127)
+    W, n = WL.WORKERS_W, WL.WORKERS_N
+    runs = sample_runs(d.nb(n), RUNS, RUN_LEN, seed=5)
+    spans = [(j0 * 512, min(n, (j0 + RUN_LEN) * 512)) for j0 in runs]
+    codes_l, meta_l, ref_codes, ref_meta = [], [], [], []
+    for w in range(1, W + 1):
+        say(f"worker {w}")
+        g = WL.worker_gradient(w)
+        G = torch.from_numpy(g).cuda()
+        E = torch.zeros(n, device="cuda")
+        c, m = gq.alloc_payload(gdesc(gq, d), n)
+        gq.gq_quantize(gdesc(gq, d), G, E, w, 0, c, m)
+        torch.cuda.synchronize()
+        check_runs(d, n, lambda lo, hi: g[lo:hi],
+                   lambda lo, hi: np.zeros(hi - lo, dtype=np.float32),
+                   c, m, E, w, 0, runs)
+        codes_l.append(c)
+        meta_l.append(m)
+        ref_codes.append([c[lo:hi].cpu().numpy() for lo, hi in spans])
+        ref_meta.append([m[lo // 512: (hi + 511) // 512].cpu().numpy()
+                         for lo, hi in spans])
+        del G, E, g
+    out = torch.full((n,), float("nan"), device="cuda")
+    gq.gq_dequantize_accumulate(gdesc(gq, d), n, codes_l, meta_l, 1.0 / W, 0.0,
+                                out)
+    torch.cuda.synchronize()
+    for s, (lo, hi) in enumerate(spans):
+        cl = [ref_codes[w][s] for w in range(W)]
+        ml = [ref_meta[w][s] for w in range(W)]
+        ref = O.dequantize_accumulate(d, hi - lo, cl, ml, 1.0 / W, 0.0)
+        xs = [np.abs(O.dequantize(d, hi - lo, c, m).astype(np.float64))
+              for c, m in zip(cl, ml)]
+        got = out[lo:hi].cpu().numpy()
+        compare_values(got, ref, np.sum(xs, axis=0) / W)
+    assert not torch.isnan(out).any().item()
