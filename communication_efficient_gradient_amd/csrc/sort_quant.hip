@@ -565,21 +565,59 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
   }
 }
 
-// ------------------------------------------------- one wave per bucket --
-// d <= 512: a wavefront owns a bucket and keeps it in registers, E = d/64
-// values per lane, kWaveBuckets buckets per workgroup.  Element order (I/O):
-// lane t holds elements VEC*(t + 64*q) + c, q < E/VEC, c < VEC, so each load
-// instruction of the wave reads 64*VEC consecutive floats.  Sorted order:
-// lane t holds sorted positions t*E .. t*E+E-1.  The bitonic network runs in
-// registers (partners in the same lane: compare-exchange; partners j/E
-// lanes away: __shfl_xor), so the sort needs no LDS and no barrier.  The
-// selection steps are those of the workgroup kernel above, with wave-wide
-// scans and argmax.
-constexpr int kWaveBuckets = 4;
+// ------------------------------------------- one lane group per bucket --
+// d <= 512: a group of G = d/8 lanes of one wavefront owns a bucket and keeps
+// it in registers, E = 8 values per lane; a 256-thread workgroup holds 256/G
+// buckets.  Element order (I/O): group lane t holds elements 4*(t + G*q) + c,
+// q < 2, c < 4, so each 128-bit load of a group reads 4*G consecutive
+// floats.  Sorted order: group lane t holds sorted positions 8t .. 8t+7.  The
+// bitonic network runs in registers (partners in the same lane: compare-
+// exchange; partners j/8 lanes away: __shfl_xor within the group), so the
+// sort needs no LDS and no barrier.  The selection steps are those of the
+// workgroup kernel above, with group-wide scans and argmax.
+constexpr int kGroupThreads = 256;
 
-template <int E>
+// Exclusive segmented scan over the G lanes of a group (see block_seg_carry):
+// returns the combination of the aggregates (f, s) of the lanes before this
+// one (REV = false) or after it (REV = true).
+template <int G, bool REV>
+__device__ __forceinline__ double group_seg_carry(bool f, double s, int gl) {
+  int fi = f ? 1 : 0;
+#pragma unroll
+  for (int o = 1; o < G; o <<= 1) {
+    const double s2 = REV ? __shfl_down(s, o, G) : __shfl_up(s, o, G);
+    const int f2 = REV ? __shfl_down(fi, o, G) : __shfl_up(fi, o, G);
+    const bool valid = REV ? (gl + o < G) : (gl >= o);
+    if (valid) {
+      if (!fi) s = s2 + s;
+      fi |= f2;
+    }
+  }
+  double ex = REV ? __shfl_down(s, 1, G) : __shfl_up(s, 1, G);
+  if (REV ? gl == G - 1 : gl == 0) ex = 0.0;
+  return ex;
+}
+
+// Group argmax of (value, key): larger value wins, equal values -> smaller
+// key; every lane of the group gets the winner.
+template <int G>
+__device__ __forceinline__ int group_argmax(double v, int key, double* best_out) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) {
+    const double v2 = __shfl_xor(v, o, G);
+    const int k2 = __shfl_xor(key, o, G);
+    if (v2 > v || (v2 == v && k2 < key)) {
+      v = v2;
+      key = k2;
+    }
+  }
+  *best_out = v;
+  return key;
+}
+
+template <int E, int G>
 __device__ __forceinline__ void wave_bitonic(float (&y)[E], int lane) {
-  constexpr int N = 64 * E;
+  constexpr int N = G * E;
 #pragma unroll
   for (int k = 2; k <= N; k <<= 1) {
 #pragma unroll
@@ -590,7 +628,7 @@ __device__ __forceinline__ void wave_bitonic(float (&y)[E], int lane) {
 #pragma unroll
         for (int r = 0; r < E; ++r) {
           const bool up = ((lane * E + r) & k) == 0;
-          const float o = __shfl_xor(y[r], lj, 64);
+          const float o = __shfl_xor(y[r], lj, G);
           y[r] = (lower == up) ? fminf(y[r], o) : fmaxf(y[r], o);
         }
       } else {
@@ -608,14 +646,14 @@ __device__ __forceinline__ void wave_bitonic(float (&y)[E], int lane) {
   }
 }
 
-// Sorted value at wave-uniform position pos.
-template <int E>
+// Sorted value at group-uniform position pos.
+template <int E, int G>
 __device__ __forceinline__ float wave_at(const float (&y)[E], int pos) {
   float v = y[0];
 #pragma unroll
   for (int r = 1; r < E; ++r)
     if ((pos % E) == r) v = y[r];
-  return __shfl(v, pos / E, 64);
+  return __shfl(v, pos / E, G);
 }
 
 template <int VEC>
@@ -656,16 +694,18 @@ __device__ __forceinline__ void store_vec(float* __restrict__ a, int64_t i,
 }
 
 template <int SCHEME, int BITS, int D>
-__global__ __launch_bounds__(64 * kWaveBuckets) void k_wave_sort_quant(
+__global__ __launch_bounds__(kGroupThreads) void k_wave_sort_quant(
     int64_t n, int64_t nb, const float* __restrict__ g, float* __restrict__ e,
     uint32_t k0, uint32_t k1, uint32_t step, int L, int clip, float clip_sigma,
     uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes) {
-  constexpr int E = D / 64;
-  constexpr int VEC = E < 4 ? E : 4;
+  constexpr int E = 8;
+  constexpr int G = D / E;
+  constexpr int VEC = 4;
   constexpr int NQ = E / VEC;
-  const int lane = threadIdx.x & 63;
-  const int64_t bucket = (int64_t)blockIdx.x * kWaveBuckets + (threadIdx.x >> 6);
-  if (bucket >= nb) return;  // whole waves leave together
+  const int lane = threadIdx.x % G;  // lane within the bucket's group
+  const int64_t bucket =
+      (int64_t)blockIdx.x * (kGroupThreads / G) + threadIdx.x / G;
+  if (bucket >= nb) return;  // whole groups leave together
   const int64_t base = bucket * D;
   const int nj = (int)((n - base) < D ? (n - base) : D);
 
@@ -673,7 +713,7 @@ __global__ __launch_bounds__(64 * kWaveBuckets) void k_wave_sort_quant(
   float p[E];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
-    const int64_t i = base + (int64_t)VEC * (lane + 64 * q);
+    const int64_t i = base + (int64_t)VEC * (lane + G * q);
     float x[VEC];
     load_vec<VEC>(g, i, n, x);
     if (e != nullptr) {
@@ -685,36 +725,35 @@ __global__ __launch_bounds__(64 * kWaveBuckets) void k_wave_sort_quant(
 #pragma unroll
     for (int c = 0; c < VEC; ++c) p[VEC * q + c] = x[c];
   }
-  auto epos = [&](int m) { return VEC * (lane + 64 * (m / VEC)) + (m % VEC); };
+  auto epos = [&](int m) { return VEC * (lane + G * (m / VEC)) + (m % VEC); };
 
   // ---- 2. clip (ORQ) -----------------------------------------------------
-  float pc[E];
-#pragma unroll
-  for (int m = 0; m < E; ++m) pc[m] = p[m];
+  float C = __builtin_inff();
   if (SCHEME == ORQ && clip) {
     Sum2 sq{0.0, 0.0};
 #pragma unroll
     for (int m = 0; m < E; ++m)
       if (epos(m) < nj) two_sum_add(sq, (double)p[m] * (double)p[m]);
-    sq = group_sum2<64>(sq);
+    sq = group_sum2<G>(sq);
     const double sigma = sqrt((sq.s + sq.c) / (double)nj);
-    const float C = (float)((double)clip_sigma * sigma);
-#pragma unroll
-    for (int m = 0; m < E; ++m) pc[m] = fminf(fmaxf(p[m], -C), C);
+    C = (float)((double)clip_sigma * sigma);
   }
+  auto clipped = [&](float x) {
+    return (SCHEME == ORQ && clip) ? fminf(fmaxf(x, -C), C) : x;
+  };
 
   // ---- 3. sort in registers (canonical +0, +inf padding) -----------------
   float y[E];
 #pragma unroll
-  for (int m = 0; m < E; ++m)
-    y[m] = epos(m) < nj ? (pc[m] == 0.f ? 0.f : pc[m]) : __builtin_inff();
-  wave_bitonic<E>(y, lane);
+  for (int m = 0; m < E; ++m) {
+    const float x = clipped(p[m]);
+    y[m] = epos(m) < nj ? (x == 0.f ? 0.f : x) : __builtin_inff();
+  }
+  wave_bitonic<E, G>(y, lane);
 
   const int r0 = lane * E;
-  float y_next_run = __shfl_down(y[0], 1, 64);
-  if (lane == 63) y_next_run = __builtin_inff();
-  float y_prev_run = __shfl_up(y[E - 1], 1, 64);
-  if (lane == 0) y_prev_run = -__builtin_inff();
+  float y_next_run = __shfl_down(y[0], 1, G);
+  if (lane == G - 1) y_next_run = __builtin_inff();
 
   float lvl_a = 0.f, lvl_b = 0.f, thr = 0.f;
   bool no_split = false;
@@ -726,8 +765,8 @@ __global__ __launch_bounds__(64 * kWaveBuckets) void k_wave_sort_quant(
 #pragma unroll
     for (int m = 0; m < E; ++m)
       if (r0 + m < nj) tot = tot + (double)y[m];
-    const double pre = block_seg_carry<64, false>(false, tot, nullptr, nullptr);
-    const double suf = block_seg_carry<64, true>(false, tot, nullptr, nullptr);
+    const double pre = group_seg_carry<G, false>(false, tot, lane);
+    const double suf = group_seg_carry<G, true>(false, tot, lane);
     double Qrun[E];
     {
       double acc = suf;
@@ -757,13 +796,13 @@ __global__ __launch_bounds__(64 * kWaveBuckets) void k_wave_sort_quant(
       }
     }
     double bestF;
-    const int kstar = block_argmax<64>(best, bestk, nullptr, nullptr, &bestF);
+    const int kstar = group_argmax<G>(best, bestk, &bestF);
     if (bestF < 0.0) {
       no_split = true;
-      thr = wave_at<E>(y, 0);
+      thr = wave_at<E, G>(y, 0);
       lvl_a = lvl_b = thr;
     } else {
-      thr = wave_at<E>(y, kstar);
+      thr = wave_at<E, G>(y, kstar);
       Sum2 lo{0.0, 0.0}, hi{0.0, 0.0};
 #pragma unroll
       for (int m = 0; m < E; ++m) {
@@ -771,8 +810,8 @@ __global__ __launch_bounds__(64 * kWaveBuckets) void k_wave_sort_quant(
         if (pos < kstar) two_sum_add(lo, (double)y[m]);
         else if (pos < nj) two_sum_add(hi, (double)y[m]);
       }
-      lo = group_sum2<64>(lo);
-      hi = group_sum2<64>(hi);
+      lo = group_sum2<G>(lo);
+      hi = group_sum2<G>(hi);
       lvl_a = (float)((lo.s + lo.c) / (double)kstar);
       lvl_b = (float)((hi.s + hi.c) / (double)(nj - kstar));
     }
@@ -782,7 +821,10 @@ __global__ __launch_bounds__(64 * kWaveBuckets) void k_wave_sort_quant(
     }
   } else {
     // ---- 4b. ORQ greedy levels (lv[j] = +inf past the current count) ------
-    const float ymin = wave_at<E>(y, 0), ymax = wave_at<E>(y, nj - 1);
+    // Each sorted value keeps its segment (index of the last level <= y)
+    // and the segment's end points (a, b); inserting c into (a0, b0) moves
+    // every y >= c one segment up and splits (a0, b0) into (a0, c), (c, b0).
+    const float ymin = wave_at<E, G>(y, 0), ymax = wave_at<E, G>(y, nj - 1);
 #pragma unroll
     for (int j = 0; j < 16; ++j) lv[j] = __builtin_inff();
     lv[0] = ymin;
@@ -793,90 +835,75 @@ __global__ __launch_bounds__(64 * kWaveBuckets) void k_wave_sort_quant(
       for (int j = 0; j < 16; ++j) lv[j] = j < L ? ymin : __builtin_inff();
       cnt = L;
     }
+    int seg[E];
+    float a_of[E], b_of[E];
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+      const bool top = y[m] >= ymax;
+      seg[m] = top ? 1 : 0;
+      a_of[m] = top ? ymax : ymin;
+      b_of[m] = ymax;
+    }
     while (cnt < L) {
-      int seg[E];
-      float a_of[E], b_of[E];
-      bool head[E], tail[E];
-      double va[E], vb[E];
-      int seg_prev = -1, seg_next = -1;
-      if (r0 > 0) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (lv[j] <= y_prev_run) seg_prev = j;
-      }
-      if (r0 + E < nj) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (lv[j] <= y_next_run) seg_next = j;
-      }
-#pragma unroll
-      for (int m = 0; m < E; ++m) {
-        const float yv = y[m];
-        int sj = 0;
-        float a = lv[0], b = lv[0];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          if (lv[j] <= yv) {
-            sj = j;
-            a = lv[j];
-            b = (j + 1 < 16 && j + 1 < cnt) ? lv[j + 1 < 16 ? j + 1 : 15] : lv[j];
-          }
-        }
-        seg[m] = sj;
-        a_of[m] = a;
-        b_of[m] = b;
-        const bool real = r0 + m < nj;
-        va[m] = real ? (double)yv - (double)a : 0.0;
-        vb[m] = real ? (double)b - (double)yv : 0.0;
-      }
-#pragma unroll
-      for (int m = 0; m < E; ++m) {
-        head[m] = (m == 0) ? (seg_prev != seg[0]) : (seg[m] != seg[m - 1]);
-        tail[m] = (m == E - 1) ? (seg_next != seg[E - 1]) : (seg[m] != seg[m + 1]);
-      }
+      int seg_prev = __shfl_up(seg[E - 1], 1, G);
+      if (lane == 0) seg_prev = -1;
+      int seg_next = __shfl_down(seg[0], 1, G);
+      if (lane == G - 1 || r0 + E >= nj) seg_next = -1;
+      // (y - a) and (b - y) of real values, 0 for the +inf padding
+      auto va = [&](int m) {
+        return r0 + m < nj ? (double)y[m] - (double)a_of[m] : 0.0;
+      };
+      auto vb = [&](int m) {
+        return r0 + m < nj ? (double)b_of[m] - (double)y[m] : 0.0;
+      };
+      auto head = [&](int m) {
+        return m == 0 ? seg_prev != seg[0] : seg[m] != seg[m - 1];
+      };
+      auto tail = [&](int m) {
+        return m == E - 1 ? seg_next != seg[E - 1] : seg[m] != seg[m + 1];
+      };
       bool fa = false, fb = false;
       double sa = 0.0, sb = 0.0;
 #pragma unroll
       for (int m = 0; m < E; ++m) {
-        if (head[m]) {
+        if (head(m)) {
           fa = true;
-          sa = va[m];
+          sa = va(m);
         } else {
-          sa = sa + va[m];
+          sa = sa + va(m);
         }
       }
 #pragma unroll
       for (int m = E - 1; m >= 0; --m) {
-        if (tail[m]) {
+        if (tail(m)) {
           fb = true;
-          sb = vb[m];
+          sb = vb(m);
         } else {
-          sb = sb + vb[m];
+          sb = sb + vb(m);
         }
       }
-      const double ca = block_seg_carry<64, false>(fa, sa, nullptr, nullptr);
-      const double cb = block_seg_carry<64, true>(fb, sb, nullptr, nullptr);
-      double B[E];
-      {
-        double run = cb;
-#pragma unroll
-        for (int m = E - 1; m >= 0; --m) {
-          if (tail[m]) {
-            B[m] = 0.0;
-            run = vb[m];
-          } else {
-            B[m] = run;
-            run = run + vb[m];
-          }
-        }
-      }
+      const double ca = group_seg_carry<G, false>(fa, sa, lane);
+      const double cb = group_seg_carry<G, true>(fb, sb, lane);
       double best = -1.0;
       int bestk = 0x7fffffff;
       {
+        // Bv[m]: sum of (b - y) over the values after m in m's segment
+        double Bv[E];
+        double run = cb;
+#pragma unroll
+        for (int m = E - 1; m >= 0; --m) {
+          if (tail(m)) {
+            Bv[m] = 0.0;
+            run = vb(m);
+          } else {
+            Bv[m] = run;
+            run = run + vb(m);
+          }
+        }
         double A = ca;
 #pragma unroll
         for (int m = 0; m < E; ++m) {
-          A = head[m] ? va[m] : A + va[m];
+          A = head(m) ? va(m) : A + va(m);
           const int pos = r0 + m;
           const float yv = y[m];
           const float ynext = (m + 1 < E) ? y[m + 1] : y_next_run;
@@ -884,16 +911,16 @@ __global__ __launch_bounds__(64 * kWaveBuckets) void k_wave_sort_quant(
                             (pos + 1 >= nj || ynext != yv);
           if (cand) {
             const double c = (double)yv;
-            const double G = ((double)b_of[m] - c) * A + (c - (double)a_of[m]) * B[m];
-            if (G > best) {
-              best = G;
+            const double Gv = ((double)b_of[m] - c) * A + (c - (double)a_of[m]) * Bv[m];
+            if (Gv > best) {
+              best = Gv;
               bestk = pos;
             }
           }
         }
       }
       double bestG;
-      const int kstar = block_argmax<64>(best, bestk, nullptr, nullptr, &bestG);
+      const int kstar = group_argmax<G>(best, bestk, &bestG);
       if (bestG < 0.0) {
         // fewer distinct values than levels: repeat the maximum
 #pragma unroll
@@ -902,7 +929,7 @@ __global__ __launch_bounds__(64 * kWaveBuckets) void k_wave_sort_quant(
         cnt = L;
       } else {
         // insert c after every level <= c (levels stay ascending)
-        const float c = wave_at<E>(y, kstar);
+        const float c = wave_at<E, G>(y, kstar);
         int ins = 0;
 #pragma unroll
         for (int j = 0; j < 16; ++j) ins += (lv[j] <= c) ? 1 : 0;
@@ -912,14 +939,22 @@ __global__ __launch_bounds__(64 * kWaveBuckets) void k_wave_sort_quant(
           nl[j] = j < ins ? lv[j] : (j == ins ? c : lv[j > 0 ? j - 1 : 0]);
 #pragma unroll
         for (int j = 0; j < 16; ++j) lv[j] = nl[j];
+#pragma unroll
+        for (int m = 0; m < E; ++m) {
+          const bool split = seg[m] == ins - 1;
+          const bool up = y[m] >= c;
+          if (split) {
+            if (up) a_of[m] = c;
+            else b_of[m] = c;
+          }
+          seg[m] += up ? 1 : 0;
+        }
         ++cnt;
       }
     }
-    float mine = lv[0];
 #pragma unroll
-    for (int j = 1; j < 16; ++j)
-      if (lane == j) mine = lv[j];
-    if (lane < L) meta[bucket * L + lane] = mine;
+    for (int j = 0; j < 16; ++j)
+      if (j % G == lane && j < L) meta[bucket * L + j] = lv[j];
   }
 
   if (codes == nullptr) return;  // levels only
@@ -930,9 +965,27 @@ __global__ __launch_bounds__(64 * kWaveBuckets) void k_wave_sort_quant(
     for (int j = 0; j < 16; ++j)
       if (j >= L) lv[j] = __builtin_inff();
   }
+  // ORQ reads its bucket again here (from cache in practice) rather than
+  // holding p through the level search: fewer live registers, more waves.
+  if constexpr (SCHEME == ORQ) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int64_t i = base + (int64_t)VEC * (lane + G * q);
+      float x[VEC];
+      load_vec<VEC>(g, i, n, x);
+      if (e != nullptr) {
+        float r[VEC];
+        load_vec<VEC>(e, i, n, r);
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) x[c] = x[c] + r[c];
+      }
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) p[VEC * q + c] = x[c];
+    }
+  }
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
-    const int64_t i0 = base + (int64_t)VEC * (lane + 64 * q);
+    const int64_t i0 = base + (int64_t)VEC * (lane + G * q);
     uint4 w = make_uint4(0u, 0u, 0u, 0u);
     if constexpr (SCHEME == ORQ) {
       const uint64_t ctr = (uint64_t)i0 >> 2;
@@ -948,10 +1001,10 @@ __global__ __launch_bounds__(64 * kWaveBuckets) void k_wave_sort_quant(
       uint32_t code = 0u;
       float xh = 0.f;
       if constexpr (SCHEME == BIN_OPT) {
-        code = (!no_split && pc[m] >= thr) ? 1u : 0u;
+        code = (!no_split && p[m] >= thr) ? 1u : 0u;
         xh = code ? lvl_b : lvl_a;
       } else {
-        const float x = pc[m];
+        const float x = clipped(p[m]);
         int first_eq = -1, below = 0;
 #pragma unroll
         for (int j = 15; j >= 0; --j)
@@ -994,9 +1047,10 @@ int launch_sort_one(int64_t n, const float* g, float* e, uint64_t seed,
                     hipStream_t st) {
   const int64_t nb = (n + D - 1) / D;
   if constexpr (D <= 512) {
-    const int64_t blocks = (nb + kWaveBuckets - 1) / kWaveBuckets;
+    constexpr int per_block = kGroupThreads / (D / 8);
+    const int64_t blocks = (nb + per_block - 1) / per_block;
     hipLaunchKernelGGL((k_wave_sort_quant<SCHEME, BITS, D>), dim3((uint32_t)blocks),
-                       dim3(64 * kWaveBuckets), 0, st, n, nb, g, e,
+                       dim3(kGroupThreads), 0, st, n, nb, g, e,
                        (uint32_t)seed, (uint32_t)(seed >> 32), step, L, clip,
                        clip_sigma, codes, meta, code_bytes);
   } else {
