@@ -1,7 +1,7 @@
 // common.hpp — device helpers shared by libgq's kernels (gfx950, wave64).
 //
 // Philox4x32-10, group reductions over 16..64 lanes (DPP/bpermute via
-// __shfl_xor) and across waves (LDS), fp64 TwoSum accumulation, and the
+// DPP and lane swaps) and across waves (LDS), fp64 TwoSum accumulation, and the
 // OR-combine that turns per-lane code fields into LSB-first stream words.
 #pragma once
 
@@ -47,27 +47,78 @@ __device__ __forceinline__ float u24(uint32_t w) {
   return (float)(w >> 8) * 0x1p-24f;
 }
 
+// ------------------------------------------------------- lane exchange --
+// Value of lane (lane ^ o) for o = 1..32, without the LDS crossbar: DPP
+// quad permutes for 1 and 2, a quad reversal followed by a half-row mirror
+// for 4 (l ^ 3 ^ 7), a row rotation by 8 for 8, and gfx950's row / half-wave
+// swaps for 16 and 32 (each lane then picks the half that came from its
+// partner).  o must be a compile-time constant after unrolling; other
+// values fall back to __shfl_xor.
+__device__ __forceinline__ uint32_t xshfl(uint32_t v, int o) {
+  switch (o) {
+    case 1:
+      return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+    case 2:
+      return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+    case 4:
+      return (uint32_t)__builtin_amdgcn_mov_dpp(
+          __builtin_amdgcn_mov_dpp((int)v, 0x1B, 0xF, 0xF, false), 0x141, 0xF,
+          0xF, false);
+    case 8:
+      return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
+    case 16: {
+      const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      return (threadIdx.x & 16) ? (uint32_t)r[0] : (uint32_t)r[1];
+    }
+    case 32: {
+      const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      return (threadIdx.x & 32) ? (uint32_t)r[0] : (uint32_t)r[1];
+    }
+    default:
+      return (uint32_t)__shfl_xor((int)v, o, 64);
+  }
+}
+
+__device__ __forceinline__ float xshfl(float v, int o) {
+  return __uint_as_float(xshfl(__float_as_uint(v), o));
+}
+
+__device__ __forceinline__ int xshfl(int v, int o) {
+  return (int)xshfl((uint32_t)v, o);
+}
+
+__device__ __forceinline__ double xshfl(double v, int o) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = xshfl((uint32_t)b, o), hi = xshfl((uint32_t)(b >> 32), o);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 // ------------------------------------------------------- group reductions --
-// Reductions over aligned groups of G lanes inside one wave (G <= 64).
+// Butterfly reductions over aligned groups of G lanes inside one wave
+// (G <= 64): exchange distances G/2, G/4, ..., 1, unrolled at compile time.
+template <int G, typename V, typename Op>
+__device__ __forceinline__ V group_reduce(V v, Op op) {
+  if constexpr (G > 1) {
+    v = op(v, xshfl(v, G / 2));
+    return group_reduce<G / 2>(v, op);
+  } else {
+    return v;
+  }
+}
+
 template <int G>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int o = G / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, G));
-  return v;
+  return group_reduce<G>(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 template <int G>
 __device__ __forceinline__ int group_sum_i(int v) {
-#pragma unroll
-  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, G);
-  return v;
+  return group_reduce<G>(v, [](int a, int b) { return a + b; });
 }
 
 template <int K>
 __device__ __forceinline__ uint32_t group_or(uint32_t v) {
-#pragma unroll
-  for (int o = K / 2; o > 0; o >>= 1) v |= __shfl_xor(v, o, K);
-  return v;
+  return group_reduce<K>(v, [](uint32_t a, uint32_t b) { return a | b; });
 }
 
 // fp64 sum with a running error term (Knuth TwoSum, branch-free).  The
@@ -94,14 +145,14 @@ __device__ __forceinline__ Sum2 two_sum_merge(Sum2 a, Sum2 b) {
 
 template <int G>
 __device__ __forceinline__ Sum2 group_sum2(Sum2 v) {
-#pragma unroll
-  for (int o = G / 2; o > 0; o >>= 1) {
+  if constexpr (G > 1) {
     Sum2 w;
-    w.s = __shfl_xor(v.s, o, G);
-    w.c = __shfl_xor(v.c, o, G);
-    v = two_sum_merge(v, w);
+    w.s = xshfl(v.s, G / 2);
+    w.c = xshfl(v.c, G / 2);
+    return group_sum2<G / 2>(two_sum_merge(v, w));
+  } else {
+    return v;
   }
-  return v;
 }
 
 // ------------------------------------------------------------- packing --

@@ -7,7 +7,9 @@
 // Output-stationary and lane-contiguous: a thread owns kV float4 groups of
 // the output, group f covering elements 4f .. 4f+3 (one bucket, since d is a
 // multiple of 4), and neighbouring lanes own neighbouring groups, so every
-// 128-bit store and load of a wave covers 1 KiB of consecutive memory.  The
+// 128-bit store and load of a wave covers 1 KiB of consecutive memory.  For
+// the uniform scheme the per-bucket step M/s is divided out once per
+// (payload, bucket) of a block and read from LDS.  The
 // codes of a group are 4*BITS consecutive stream bits: one byte load (1, 2
 // bits), two (3 bits), a 16-bit (4 bits) or a 32-bit (8 bits) load, again
 // consecutive across lanes.  Payloads are summed in fp32 into two
@@ -87,72 +89,105 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) {
   return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
-template <int SCHEME, int BITS>
+template <int SCHEME, int BITS, int NB>
 __global__ __launch_bounds__(kThreads) void k_deq_acc(
     int64_t n, int d, int s, int L, int W, PayloadPtrs pp, float alpha,
     float beta, float* __restrict__ out, int64_t code_bytes) {
+  // The block's tile is kGroupsPerBlock consecutive groups; pass v of the
+  // block covers the kThreads groups [tile + kThreads v, tile + kThreads
+  // (v + 1)), thread t taking group tile + kThreads v + t.
   const int64_t ngroups = (n + 3) >> 2;
-  const int64_t f0 = (int64_t)blockIdx.x * kGroupsPerBlock + threadIdx.x;
+  const int64_t tile = (int64_t)blockIdx.x * kGroupsPerBlock;
+  const int64_t f0 = tile + threadIdx.x;
+  constexpr int kStride = kThreads;  // groups between a thread's v and v+1
 
+  // Code loads of NB payloads at once (NB = 1, 2 or 4), all issued before
+  // any use.
+  constexpr bool TABLE = NB == 4;
+  uint32_t cw[NB][kV];
+  auto load_batch = [&](int p0) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int p = p0 + j;
+#pragma unroll
+      for (int v = 0; v < kV; ++v) {
+        const int64_t f = f0 + kStride * v;
+        cw[j][v] = (p < W && f < ngroups)
+                       ? load_codes4<BITS>(pp.codes[p < W ? p : 0], f,
+                                           4 * f + 4 <= n, code_bytes)
+                       : 0u;
+      }
+    }
+  };
+  load_batch(0);
+
+  // Uniform scheme with TABLE (NB = 4, W >= 3): the step M/s of every (payload,
+  // bucket) the tile touches, one correctly rounded division each, shared
+  // through LDS (built while the first code loads are in flight).  For one
+  // or two payloads each group divides for itself: the barrier would cost
+  // more than the divisions it saves.
+  __shared__ float delta_tab[TABLE ? kMaxPayloads * (kGroupsPerBlock * 4 / 64 + 1) : 1];
+  const int64_t b0 = (4 * tile) / d;
+  int nbk = 0;
+  if constexpr (SCHEME == UNIFORM && TABLE) {
+    const int64_t last = (4 * (tile + kGroupsPerBlock) - 1) / d;
+    const int64_t nb = (n + d - 1) / d;
+    nbk = (int)(last - b0 + 1);
+    for (int t = threadIdx.x; t < W * nbk; t += kThreads) {
+      const int p = t / nbk, j = t % nbk;
+      const int64_t bucket = b0 + j;
+      delta_tab[t] = bucket < nb ? pp.meta[p][bucket] / (float)s : 0.f;
+    }
+    __syncthreads();
+  }
+  auto deq = [&](uint32_t w, int p, int64_t f) -> float4 {
+    const int64_t bucket = (4 * f) / d;
+    if constexpr (SCHEME == UNIFORM) {
+      const float delta = TABLE ? delta_tab[p * nbk + (int)(bucket - b0)]
+                                : pp.meta[p][bucket] / (float)s;
+      float x[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t u = (w >> (BITS * k)) & ((1u << BITS) - 1u);
+        const uint32_t m = 1u << (BITS - 1);
+        x[k] = (float)(int)((u ^ m) - m) * delta;  // sign-extended code
+      }
+      return make_float4(x[0], x[1], x[2], x[3]);
+    } else {
+      return dequant4<SCHEME, BITS>(w, pp.meta[p], bucket, s, L);
+    }
+  };
+
+  // Payloads 0 and 1 initialise the two accumulators (a copy, so a single
+  // payload is reproduced bit for bit); later even / odd payloads add into
+  // acc0 / acc1 in payload order.
   float4 acc0[kV], acc1[kV];
 #pragma unroll
   for (int v = 0; v < kV; ++v) {
     acc0[v] = make_float4(0.f, 0.f, 0.f, 0.f);
     acc1[v] = acc0[v];
   }
-  // Payloads two at a time: both payloads' code and meta loads are issued
-  // before any arithmetic, so a wave keeps 2*kV loads in flight.  Payload
-  // 0 and 1 initialise the two accumulators (a copy, so a single payload is
-  // reproduced bit for bit), later even / odd payloads add into them.
-  int p = 0;
-  for (; p + 2 <= W; p += 2) {
-    uint32_t w0[kV], w1[kV];
-    const uint8_t* __restrict__ c0 = pp.codes[p];
-    const uint8_t* __restrict__ c1 = pp.codes[p + 1];
+  for (int p0 = 0; p0 < W; p0 += NB) {
+    if (p0 > 0) load_batch(p0);
 #pragma unroll
-    for (int v = 0; v < kV; ++v) {
-      const int64_t f = f0 + (int64_t)kThreads * v;
-      const bool ok = f < ngroups;
-      const bool full = 4 * f + 4 <= n;
-      w0[v] = ok ? load_codes4<BITS>(c0, f, full, code_bytes) : 0u;
-      w1[v] = ok ? load_codes4<BITS>(c1, f, full, code_bytes) : 0u;
-    }
+    for (int j = 0; j < NB; ++j) {
+      const int p = p0 + j;
+      if (p >= W) break;
 #pragma unroll
-    for (int v = 0; v < kV; ++v) {
-      const int64_t f = f0 + (int64_t)kThreads * v;
-      if (f >= ngroups) continue;
-      const int64_t b = (4 * f) / d;
-      const float4 x0 = dequant4<SCHEME, BITS>(w0[v], pp.meta[p], b, s, L);
-      const float4 x1 = dequant4<SCHEME, BITS>(w1[v], pp.meta[p + 1], b, s, L);
-      if (p == 0) {
-        acc0[v] = x0;
-        acc1[v] = x1;
-      } else {
-        acc0[v] = add4(acc0[v], x0);
-        acc1[v] = add4(acc1[v], x1);
+      for (int v = 0; v < kV; ++v) {
+        const int64_t f = f0 + kStride * v;
+        if (f >= ngroups) continue;
+        const float4 x = deq(cw[j][v], p, f);
+        if (p == 0) acc0[v] = x;
+        else if (p == 1) acc1[v] = x;
+        else if (p & 1) acc1[v] = add4(acc1[v], x);
+        else acc0[v] = add4(acc0[v], x);
       }
-    }
-  }
-  if (p < W) {  // odd W: the last payload is even-numbered
-    const uint8_t* __restrict__ c0 = pp.codes[p];
-    uint32_t w0[kV];
-#pragma unroll
-    for (int v = 0; v < kV; ++v) {
-      const int64_t f = f0 + (int64_t)kThreads * v;
-      w0[v] = f < ngroups ? load_codes4<BITS>(c0, f, 4 * f + 4 <= n, code_bytes)
-                          : 0u;
-    }
-#pragma unroll
-    for (int v = 0; v < kV; ++v) {
-      const int64_t f = f0 + (int64_t)kThreads * v;
-      if (f >= ngroups) continue;
-      const float4 x0 = dequant4<SCHEME, BITS>(w0[v], pp.meta[p], (4 * f) / d, s, L);
-      acc0[v] = p == 0 ? x0 : add4(acc0[v], x0);
     }
   }
 #pragma unroll
   for (int v = 0; v < kV; ++v) {
-    const int64_t f = f0 + (int64_t)kThreads * v;
+    const int64_t f = f0 + kStride * v;
     if (f >= ngroups) continue;
     float4 a = W > 1 ? add4(acc0[v], acc1[v]) : acc0[v];
     float4 r = make_float4(alpha * a.x, alpha * a.y, alpha * a.z, alpha * a.w);
@@ -215,9 +250,16 @@ template <int SCHEME, int BITS>
 int deq_one(const LaunchDesc& L, int64_t n, int W, const PayloadPtrs& pp,
             float alpha, float beta, float* out, int64_t code_bytes,
             hipStream_t st) {
-  hipLaunchKernelGGL((k_deq_acc<SCHEME, BITS>), dim3((uint32_t)blocks_for(n)),
-                     dim3(kThreads), 0, st, n, L.d, L.s, L.L, W, pp, alpha,
-                     beta, out, code_bytes);
+  const dim3 grid((uint32_t)blocks_for(n)), block(kThreads);
+  if (W == 1)
+    hipLaunchKernelGGL((k_deq_acc<SCHEME, BITS, 1>), grid, block, 0, st, n,
+                       L.d, L.s, L.L, W, pp, alpha, beta, out, code_bytes);
+  else if (W == 2)
+    hipLaunchKernelGGL((k_deq_acc<SCHEME, BITS, 2>), grid, block, 0, st, n,
+                       L.d, L.s, L.L, W, pp, alpha, beta, out, code_bytes);
+  else
+    hipLaunchKernelGGL((k_deq_acc<SCHEME, BITS, 4>), grid, block, 0, st, n,
+                       L.d, L.s, L.L, W, pp, alpha, beta, out, code_bytes);
   return (int)hipGetLastError();
 }
 

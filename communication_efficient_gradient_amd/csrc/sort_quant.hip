@@ -26,8 +26,8 @@ namespace {
 
 template <int D>
 struct SortCfg {
-  static constexpr int T = D <= 256 ? 64 : (D / 4 <= 1024 ? D / 4 : 1024);
-  static constexpr int E = D / T;
+  static constexpr int E = D <= 8192 ? 8 : D / 1024;  // values per thread
+  static constexpr int T = D / E;                      // 128 .. 1024 threads
   static constexpr int NW = T / 64;
 };
 
@@ -60,7 +60,7 @@ __device__ __forceinline__ Sum2 block_sum2(Sum2 v, double* red) {
     }
     __syncthreads();
     v = Sum2{red[0], red[1]};
-#pragma unroll
+#pragma unroll 1
     for (int w = 1; w < T / 64; ++w) v = two_sum_merge(v, Sum2{red[2 * w], red[2 * w + 1]});
   }
   return v;
@@ -74,8 +74,8 @@ __device__ __forceinline__ int block_argmax(double v, int key, double* redv,
                                             int* redk, double* best_out) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    const double v2 = __shfl_xor(v, o, 64);
-    const int k2 = __shfl_xor(key, o, 64);
+    const double v2 = xshfl(v, o);
+    const int k2 = xshfl(key, o);
     if (v2 > v || (v2 == v && k2 < key)) {
       v = v2;
       key = k2;
@@ -91,7 +91,7 @@ __device__ __forceinline__ int block_argmax(double v, int key, double* redv,
     __syncthreads();
     v = redv[0];
     key = redk[0];
-#pragma unroll
+#pragma unroll 1
     for (int w = 1; w < T / 64; ++w) {
       const double v2 = redv[w];
       const int k2 = redk[w];
@@ -159,64 +159,69 @@ __device__ __forceinline__ double block_seg_carry(bool f, double s,
   return ex_s;
 }
 
-// Bitonic sort of D floats in LDS by T threads (ascending).
-template <int D, int T>
-__device__ __forceinline__ void bitonic_sort(float* s) {
-  for (int k = 2; k <= D; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      __syncthreads();
-#pragma unroll 4
-      for (int i = threadIdx.x; i < D / 2; i += T) {
-        const int lo = 2 * j * (i / j) + (i % j);
-        const int hi = lo + j;
-        const bool up = (lo & k) == 0;
-        const float a = s[lo], b = s[hi];
-        if ((a > b) == up) {
-          s[lo] = b;
-          s[hi] = a;
-        }
-      }
+// One bitonic stage (merge size K, partner distance J), unrolled at compile
+// time.
+template <int E, int T, int K, int J>
+__device__ __forceinline__ void hb_stage(float (&y)[E], float* lds, int tid,
+                                         int lane) {
+  if constexpr (J < E) {
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      if (r & J) continue;
+      const bool up = ((tid * E + r) & K) == 0;
+      const float a = y[r], b = y[r | J];
+      const float lo = fminf(a, b), hi = fmaxf(a, b);
+      y[r] = up ? lo : hi;
+      y[r | J] = up ? hi : lo;
     }
-  }
-  __syncthreads();
-}
-
-// ----------------------------------------------------- element-order I/O --
-// Codes of one element per lane, lanes in element order: K lanes with
-// K*BITS = 32 fill one word; for BITS = 3, 32 lanes fill three words.
-template <int BITS>
-__device__ __forceinline__ void store_code1(uint8_t* __restrict__ codes,
-                                            int64_t i, uint32_t c,
-                                            int64_t code_bytes) {
-  const int lane = threadIdx.x & 63;
-  if constexpr (BITS == 3) {
-    const int q = lane & 31;
-    const int off = 3 * q;
-    const uint64_t x = (uint64_t)c << (off & 31);
-    const int wi = off >> 5;
-    uint32_t w0 = wi == 0 ? (uint32_t)x : 0u;
-    uint32_t w1 = wi == 1 ? (uint32_t)x : (wi == 0 ? (uint32_t)(x >> 32) : 0u);
-    uint32_t w2 = wi == 2 ? (uint32_t)x : (wi == 1 ? (uint32_t)(x >> 32) : 0u);
-    w0 = group_or<32>(w0);
-    w1 = group_or<32>(w1);
-    w2 = group_or<32>(w2);
-    if (q < 3) {
-      const int64_t byte = ((i - q) >> 5) * 12 + 4 * q;
-      if (byte < code_bytes) {
-        const uint32_t w = q == 0 ? w0 : (q == 1 ? w1 : w2);
-        *reinterpret_cast<uint32_t*>(codes + byte) = w;
-      }
+  } else if constexpr (J < 64 * E) {
+    constexpr int LJ = J / E;
+    const bool lower = (lane & LJ) == 0;
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      const bool up = ((tid * E + r) & K) == 0;
+      const float o = xshfl(y[r], LJ);
+      y[r] = (lower == up) ? fminf(y[r], o) : fmaxf(y[r], o);
     }
   } else {
-    constexpr int K = 32 / BITS;
-    const int q = lane & (K - 1);
-    uint32_t w = c << (BITS * q);
-    w = group_or<K>(w);
-    if (q == 0) {
-      const int64_t byte = (i * BITS) >> 3;
-      if (byte < code_bytes) *reinterpret_cast<uint32_t*>(codes + byte) = w;
+    float4* l4 = reinterpret_cast<float4*>(lds);
+#pragma unroll
+    for (int r = 0; r < E; r += 4)
+      l4[(tid * E + r) / 4] = make_float4(y[r], y[r + 1], y[r + 2], y[r + 3]);
+    __syncthreads();
+    const int pbase = (tid * E) ^ J;  // partner positions pbase + r
+    const bool lower = ((tid * E) & J) == 0;
+#pragma unroll
+    for (int r = 0; r < E; r += 4) {
+      const float4 o = l4[(pbase + r) / 4];
+      const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bool up = ((tid * E + r + c) & K) == 0;
+        y[r + c] = (lower == up) ? fminf(y[r + c], ov[c]) : fmaxf(y[r + c], ov[c]);
+      }
     }
+    __syncthreads();
   }
+  if constexpr (J > 1) hb_stage<E, T, K, J / 2>(y, lds, tid, lane);
+}
+
+template <int E, int T, int K>
+__device__ __forceinline__ void hb_merge(float (&y)[E], float* lds, int tid,
+                                         int lane) {
+  hb_stage<E, T, K, K / 2>(y, lds, tid, lane);
+  if constexpr (K < T * E) hb_merge<E, T, 2 * K>(y, lds, tid, lane);
+}
+
+// Bitonic sort of T*E floats held E per thread (thread t: positions
+// t*E .. t*E+E-1, ascending at the end).  Stages whose partner is in the
+// same thread are register compare-exchanges, partners up to 63 lanes away
+// are reached with lane exchanges (DPP / lane swaps), and only the stages
+// that cross waves go
+// through LDS (lds: T*E floats), two barriers each.
+template <int E, int T>
+__device__ __forceinline__ void hybrid_bitonic(float (&y)[E], float* lds) {
+  hb_merge<E, T, 2>(y, lds, threadIdx.x, threadIdx.x & 63);
 }
 
 struct SortShared {
@@ -243,42 +248,58 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
   const int64_t base = bucket * D;
   const int nj = (int)((n - base) < D ? (n - base) : D);
 
-  // ---- 1. load p = g (+ e), element order t + T*m ----------------------
+  // ---- 1. load p = g (+ e); element order: thread t holds the float4s
+  //         t, t + T, ... of the bucket -------------------------------------
+  constexpr int NQ = E / 4;
   float p[E];
 #pragma unroll
-  for (int m = 0; m < E; ++m) {
-    const int64_t i = base + tid + T * m;
-    float x = 0.f;
-    if (tid + T * m < nj) {
-      x = g[i];
-      if (e != nullptr) x = x + e[i];
+  for (int q = 0; q < NQ; ++q) {
+    const int64_t i = base + 4 * (tid + (int64_t)T * q);
+    float4 x = load4(g, i, n);
+    if (e != nullptr) {
+      const float4 r = load4(e, i, n);
+      x.x = x.x + r.x;
+      x.y = x.y + r.y;
+      x.z = x.z + r.z;
+      x.w = x.w + r.w;
     }
-    p[m] = x;
+    p[4 * q + 0] = x.x;
+    p[4 * q + 1] = x.y;
+    p[4 * q + 2] = x.z;
+    p[4 * q + 3] = x.w;
   }
+  auto epos = [&](int m) { return 4 * (tid + T * (m / 4)) + (m % 4); };
 
   // ---- 2. clip (ORQ) -----------------------------------------------------
-  float pc[E];
-#pragma unroll
-  for (int m = 0; m < E; ++m) pc[m] = p[m];
+  float C = __builtin_inff();
   if (SCHEME == ORQ && clip) {
     Sum2 sq{0.0, 0.0};
 #pragma unroll
     for (int m = 0; m < E; ++m)
-      if (tid + T * m < nj) two_sum_add(sq, (double)p[m] * (double)p[m]);
+      if (epos(m) < nj) two_sum_add(sq, (double)p[m] * (double)p[m]);
     sq = block_sum2<T>(sq, sh.red_d);
     const double sigma = sqrt((sq.s + sq.c) / (double)nj);
-    const float C = (float)((double)clip_sigma * sigma);
-#pragma unroll
-    for (int m = 0; m < E; ++m) pc[m] = fminf(fmaxf(p[m], -C), C);
+    C = (float)((double)clip_sigma * sigma);
   }
+  auto clipped = [&](float x) {
+    return (SCHEME == ORQ && clip) ? fminf(fmaxf(x, -C), C) : x;
+  };
 
-  // ---- 3. sort (canonical +0, +inf padding) -----------------------------
+  // ---- 3. sort (canonical +0, +inf padding), then publish it in LDS ------
+  {
+    float y[E];
 #pragma unroll
-  for (int m = 0; m < E; ++m) {
-    const int pos = tid + T * m;
-    sorted[pos] = pos < nj ? (pc[m] == 0.f ? 0.f : pc[m]) : __builtin_inff();
+    for (int m = 0; m < E; ++m) {
+      const float x = clipped(p[m]);
+      y[m] = epos(m) < nj ? (x == 0.f ? 0.f : x) : __builtin_inff();
+    }
+    hybrid_bitonic<E, T>(y, sorted);
+    float4* l4 = reinterpret_cast<float4*>(sorted);
+#pragma unroll
+    for (int r = 0; r < E; r += 4)
+      l4[(tid * E + r) / 4] = make_float4(y[r], y[r + 1], y[r + 2], y[r + 3]);
+    __syncthreads();
   }
-  bitonic_sort<D, T>(sorted);
 
   // sorted run of this thread
   const int r0 = tid * E;
@@ -339,10 +360,9 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
       Sum2 lo{0.0, 0.0}, hi{0.0, 0.0};
 #pragma unroll
       for (int m = 0; m < E; ++m) {
-        if (tid + T * m < nj) {
-          if (p[m] >= thr) two_sum_add(hi, (double)p[m]);
-          else two_sum_add(lo, (double)p[m]);
-        }
+        const int pos = r0 + m;
+        if (pos < kstar) two_sum_add(lo, (double)sorted[pos]);
+        else if (pos < nj) two_sum_add(hi, (double)sorted[pos]);
       }
       lo = block_sum2<T>(lo, sh.red_d);
       hi = block_sum2<T>(hi, sh.red_d);
@@ -511,57 +531,72 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
 
   if (codes == nullptr) return;  // levels only
 
-  // ---- 5. codes, packing, residual (element order) ----------------------
+  // ---- 5. codes, packing, residual (element order, bucket read again) ----
   float lv[16];
   if constexpr (SCHEME == ORQ) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) lv[j] = j < L ? sh.lev[j] : __builtin_inff();
   }
+  const int lane = tid & 63;
 #pragma unroll
-  for (int m = 0; m < E; ++m) {
-    const int pos = tid + T * m;
-    const int64_t i = base + pos;
-    const bool real = pos < nj;
-    uint32_t c = 0u;
-    float xh = 0.f;
-    if constexpr (SCHEME == BIN_OPT) {
-      c = (!no_split && pc[m] >= thr) ? 1u : 0u;
-      xh = c ? lvl_b : lvl_a;
-    } else {
-      const float x = pc[m];
-      int first_eq = -1, below = 0;
-#pragma unroll
-      for (int j = 15; j >= 0; --j)
-        if (j < L && lv[j] == x) first_eq = j;
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (j < L && lv[j] < x) below = j;
-      if (first_eq >= 0) {
-        c = (uint32_t)first_eq;
-      } else {
-        // random rounding between lv[below] and lv[below + 1]
-        const uint64_t ctr = (uint64_t)i >> 2;
-        const uint4 w = philox4x32_10(k0, k1, (uint32_t)ctr,
-                                      (uint32_t)(ctr >> 32), step, 0u);
-        const int sub = (int)(i & 3);
-        const uint32_t word = sub == 0 ? w.x : sub == 1 ? w.y : sub == 2 ? w.z : w.w;
-        float lo = lv[0], hi = lv[1];
-#pragma unroll
-        for (int j = 0; j < 15; ++j)
-          if (j == below) {
-            lo = lv[j];
-            hi = lv[j + 1];
-          }
-        const float q = (x - lo) / (hi - lo);
-        c = (uint32_t)(below + (u24(word) < q ? 1 : 0));
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if ((uint32_t)j == c) xh = lv[j];
+  for (int q = 0; q < NQ; ++q) {
+    const int64_t i0 = base + 4 * (tid + (int64_t)T * q);
+    float4 pv = load4(g, i0, n);
+    if (e != nullptr) {
+      const float4 r = load4(e, i0, n);
+      pv.x = pv.x + r.x;
+      pv.y = pv.y + r.y;
+      pv.z = pv.z + r.z;
+      pv.w = pv.w + r.w;
     }
-    if (!real) c = 0u;
-    store_code1<BITS>(codes, i, c, code_bytes);
-    if (e != nullptr && real) e[i] = p[m] - xh;
+    const float px[4] = {pv.x, pv.y, pv.z, pv.w};
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (SCHEME == ORQ) {
+      const uint64_t ctr = (uint64_t)i0 >> 2;
+      w = philox4x32_10(k0, k1, (uint32_t)ctr, (uint32_t)(ctr >> 32), step, 0u);
+    }
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    uint32_t field = 0u;
+    float rr[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t code = 0u;
+      float xh = 0.f;
+      if constexpr (SCHEME == BIN_OPT) {
+        code = (!no_split && px[c] >= thr) ? 1u : 0u;
+        xh = code ? lvl_b : lvl_a;
+      } else {
+        const float x = clipped(px[c]);
+        int first_eq = -1, below = 0;
+#pragma unroll
+        for (int j = 15; j >= 0; --j)
+          if (j < L && lv[j] == x) first_eq = j;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (j < L && lv[j] < x) below = j;
+        if (first_eq >= 0) {
+          code = (uint32_t)first_eq;
+        } else {
+          float lo = lv[0], hi = lv[1];
+#pragma unroll
+          for (int j = 0; j < 15; ++j)
+            if (j == below) {
+              lo = lv[j];
+              hi = lv[j + 1];
+            }
+          const float qf = (x - lo) / (hi - lo);
+          code = (uint32_t)(below + (u24(ws[c]) < qf ? 1 : 0));
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if ((uint32_t)j == code) xh = lv[j];
+      }
+      if (i0 + c >= n) code = 0u;
+      field |= code << (BITS * c);
+      rr[c] = px[c] - xh;
+    }
+    store_chunk<BITS, 4>(codes, i0, lane, field, code_bytes);
+    if (e != nullptr && i0 < n) store4(e, i0, n, make_float4(rr[0], rr[1], rr[2], rr[3]));
   }
 }
 
@@ -572,7 +607,7 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
 // q < 2, c < 4, so each 128-bit load of a group reads 4*G consecutive
 // floats.  Sorted order: group lane t holds sorted positions 8t .. 8t+7.  The
 // bitonic network runs in registers (partners in the same lane: compare-
-// exchange; partners j/8 lanes away: __shfl_xor within the group), so the
+// exchange; partners j/8 lanes away: DPP / lane swaps in the group), so the
 // sort needs no LDS and no barrier.  The selection steps are those of the
 // workgroup kernel above, with group-wide scans and argmax.
 constexpr int kGroupThreads = 256;
@@ -604,8 +639,8 @@ template <int G>
 __device__ __forceinline__ int group_argmax(double v, int key, double* best_out) {
 #pragma unroll
   for (int o = G / 2; o > 0; o >>= 1) {
-    const double v2 = __shfl_xor(v, o, G);
-    const int k2 = __shfl_xor(key, o, G);
+    const double v2 = xshfl(v, o);
+    const int k2 = xshfl(key, o);
     if (v2 > v || (v2 == v && k2 < key)) {
       v = v2;
       key = k2;
@@ -628,7 +663,7 @@ __device__ __forceinline__ void wave_bitonic(float (&y)[E], int lane) {
 #pragma unroll
         for (int r = 0; r < E; ++r) {
           const bool up = ((lane * E + r) & k) == 0;
-          const float o = __shfl_xor(y[r], lj, G);
+          const float o = xshfl(y[r], lj);
           y[r] = (lower == up) ? fminf(y[r], o) : fmaxf(y[r], o);
         }
       } else {

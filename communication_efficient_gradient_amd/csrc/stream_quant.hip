@@ -63,7 +63,9 @@ __device__ __forceinline__ void bucket_side_sums(Sum2& neg, Sum2& pos, int& nn,
     pos = Sum2{redd[2], redd[3]};
     nn = redi[0];
     np = redi[1];
-#pragma unroll
+    // sequential over the waves: unrolling would hoist every partial into
+    // registers at once
+#pragma unroll 1
     for (int w = 1; w < NW; ++w) {
       neg = two_sum_merge(neg, Sum2{redd[4 * w + 0], redd[4 * w + 1]});
       pos = two_sum_merge(pos, Sum2{redd[4 * w + 2], redd[4 * w + 3]});
@@ -118,25 +120,27 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
                          fmaxf(fabsf(p[v].z), fabsf(p[v].w))));
     lvl0 = bucket_max<G>(m, red_f);
   } else {
-    Sum2 neg{0.0, 0.0}, pos{0.0, 0.0};
+    // Each lane sums its own values of one sign in plain fp64 (no
+    // cancellation: relative error < 4V * 2^-53); lanes then merge their
+    // sums with TwoSum.
+    double sn = 0.0, sp = 0.0;
     int nn = 0, np = 0;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       const int64_t i = base + 4 * (lane + G * v);
+      const int nreal = i + 4 <= n ? 4 : (i < n ? (int)(n - i) : 0);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        if (i + k < n) {
-          const float x = comp(p[v], k);
-          if (x >= 0.f) {
-            two_sum_add(pos, (double)x);
-            ++np;
-          } else {
-            two_sum_add(neg, (double)x);
-            ++nn;
-          }
-        }
+        const float x = comp(p[v], k);
+        const bool real = k < nreal;
+        const bool up = x >= 0.f;
+        sp += (real && up) ? (double)x : 0.0;
+        sn += (real && !up) ? (double)x : 0.0;
+        np += (real && up) ? 1 : 0;
+        nn += (real && !up) ? 1 : 0;
       }
     }
+    Sum2 neg{sn, 0.0}, pos{sp, 0.0};
     bucket_side_sums<G>(neg, pos, nn, np, red_d, red_i);
     lvl0 = nn ? (float)((neg.s + neg.c) / (double)nn) : 0.f;
     lvl1 = np ? (float)((pos.s + pos.c) / (double)np) : 0.f;
@@ -199,9 +203,10 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
       }
     }
     // absent tail elements pack as 0
+    const int nreal = i + 4 <= n ? 4 : (i < n ? (int)(n - i) : 0);
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      if (i + k >= n) c[k] = 0u;
+      if (k >= nreal) c[k] = 0u;
     store_field<BITS, G>(codes, i, lane, field4<BITS>(c[0], c[1], c[2], c[3]),
                          code_bytes);
     if (e != nullptr && i < n) {
