@@ -202,12 +202,27 @@ def entry(name, ms, nbytes, n, bound="hbm", extra=None):
     return r
 
 
-def suite(torch, gq, WL, stream, reps: int):
-    """Every other workload's kernels, each timed back to back."""
+def suite(torch, gq, WL, stream, reps: int, only: str | None = None):
+    """Every other workload's kernels, each timed back to back (only the
+    workloads whose name contains `only`: qsgd, orq, bingrad, workers)."""
     out = []
     tb = lambda f, r=reps: time_back_to_back(torch, stream, f, r)  # noqa: E731
+    want = lambda name: only is None or only in name  # noqa: E731
 
-    # QSGD s=4, 65,536 elements: cache-resident, latency-bound.
+    if want("qsgd"):
+        out += suite_qsgd(torch, gq, WL, stream, tb)
+    if want("orq"):
+        out += suite_orq(torch, gq, WL, stream, tb, reps)
+    if want("bingrad"):
+        out += suite_bingrad(torch, gq, WL, stream, tb, reps)
+    if want("workers"):
+        out += suite_workers(torch, gq, WL, stream, tb)
+    return out
+
+
+def suite_qsgd(torch, gq, WL, stream, tb):
+    """QSGD s=4, 65,536 elements: cache-resident, latency-bound."""
+    out = []
     g = torch.from_numpy(WL.qsgd_gradient()).cuda()
     d = gq.desc(gq.GQ_UNIFORM, 512, s=4)
     c, m = gq.alloc_payload(d, g.numel())
@@ -223,9 +238,12 @@ def suite(torch, gq, WL, stream, reps: int):
     out.append(entry("dequantize qsgd W=1 n=65536", ms,
                      deq_bytes(4, 1, 512, g.numel(), 1, 0.0), g.numel(),
                      bound="latency"))
-    del g, c, m, o, q, dq
+    return out
 
-    # ORQ-5 / ORQ-9 on 100M elements, clip off / on.
+
+def suite_orq(torch, gq, WL, stream, tb, reps):
+    """ORQ-5 / ORQ-9 on 100M elements, clip off / on."""
+    out = []
     t0 = time.time()
     g = torch.from_numpy(WL.orq_gradient()).cuda()
     log(f"suite: orq input in {time.time() - t0:.1f}s")
@@ -241,10 +259,13 @@ def suite(torch, gq, WL, stream, reps: int):
                              quant_bytes(bits, L, 512, n, False), n,
                              bound="alu"))
             del c, m, q
-    del g
+    return out
 
-    # BinGrad-b (optimal two-level) and the sign split with error feedback,
-    # 1B elements, over the bucket sweep.
+
+def suite_bingrad(torch, gq, WL, stream, tb, reps):
+    """BinGrad-b (optimal two-level) and the sign split with error feedback,
+    1B elements, over the bucket sweep."""
+    out = []
     t0 = time.time()
     g = torch.from_numpy(WL.bingrad_gradient()).cuda()
     log(f"suite: bingrad input in {time.time() - t0:.1f}s")
@@ -260,9 +281,12 @@ def suite(torch, gq, WL, stream, reps: int):
             out.append(entry(f"quantize {nm}+ef d={dd} n={n}", ms,
                              quant_bytes(1, 2, dd, n, True), n))
             del c, m, q
-    del g, e
+    return out
 
-    # INT8 + EF for 8 workers of 256M each, then the W = 8 average.
+
+def suite_workers(torch, gq, WL, stream, tb):
+    """INT8 + EF for 8 workers of 256M each, then the W = 8 average."""
+    out = []
     W, n = WL.WORKERS_W, WL.WORKERS_N
     d = gq.desc(gq.GQ_UNIFORM, 512, s=127)
     Gs, Es, Cs, Ms = [], [], [], []
@@ -285,7 +309,6 @@ def suite(torch, gq, WL, stream, reps: int):
     ms = tb(lambda i: dq())
     out.append(entry(f"dequantize_accumulate int8 W={W} n={n}", ms,
                      deq_bytes(8, 1, 512, n, W, 0.0), n * W))
-    del Gs, Es, Cs, Ms, avg, qs, dq
     return out
 
 
@@ -346,6 +369,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--suite", choices=("main", "all"), default="all")
     ap.add_argument("--reps", type=int, default=20)
+    ap.add_argument("--only", choices=("qsgd", "orq", "bingrad", "workers"),
+                    help="time only this workload's kernels after the headline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--counters", action="store_true",
                     help="short run for rocprofv3 --pmc: main steps + a copy")
@@ -429,7 +454,7 @@ def main() -> int:
         del mw.q, mw.G
         torch.cuda.empty_cache()
         kernels.append(copy_reference(torch, stream))
-        kernels += suite(torch, gq, WL, stream, args.reps)
+        kernels += suite(torch, gq, WL, stream, args.reps, args.only)
 
     line = {
         "metric": METRIC,

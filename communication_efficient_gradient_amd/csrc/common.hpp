@@ -48,14 +48,40 @@ __device__ __forceinline__ float u24(uint32_t w) {
 }
 
 // ------------------------------------------------------- lane exchange --
-// Value of lane (lane ^ o) for o = 1..32, without the LDS crossbar: DPP
-// quad permutes for 1 and 2, a quad reversal followed by a half-row mirror
-// for 4 (l ^ 3 ^ 7), a row rotation by 8 for 8, and gfx950's row / half-wave
-// swaps for 16 and 32 (each lane then picks the half that came from its
-// partner).  o must be a compile-time constant after unrolling; other
-// values fall back to __shfl_xor.
+// Value of lane (lane ^ o) for o = 1, 2, 4, .., 32 and for the mirror masks
+// 3, 7, 15, 31, 63, without the LDS crossbar: DPP quad permutes for 1, 2
+// and 3 (quad reversal), the half-row mirror for 7, the row mirror for 15,
+// a quad reversal then a half-row mirror for 4 (l ^ 3 ^ 7), a row rotation
+// by 8 for 8, and gfx950's row / half-wave swaps for 16 and 32 (each lane
+// then picks the half that came from its partner); 31 and 63 compose a
+// mirror with the swaps.  o must be a compile-time constant after
+// unrolling; other values fall back to __shfl_xor.
+__device__ __forceinline__ uint32_t xshfl(uint32_t v, int o);
+
+__device__ __forceinline__ uint32_t xshfl_swap16(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return (threadIdx.x & 16) ? (uint32_t)r[0] : (uint32_t)r[1];
+}
+
+__device__ __forceinline__ uint32_t xshfl_swap32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (threadIdx.x & 32) ? (uint32_t)r[0] : (uint32_t)r[1];
+}
+
 __device__ __forceinline__ uint32_t xshfl(uint32_t v, int o) {
   switch (o) {
+    case 3:
+      return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x1B, 0xF, 0xF, false);
+    case 7:
+      return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);
+    case 15:
+      return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);
+    case 31:
+      return xshfl_swap16(
+          (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));
+    case 63:
+      return xshfl_swap32(xshfl_swap16(
+          (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false)));
     case 1:
       return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
     case 2:
@@ -66,14 +92,10 @@ __device__ __forceinline__ uint32_t xshfl(uint32_t v, int o) {
           0xF, false);
     case 8:
       return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
-    case 16: {
-      const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-      return (threadIdx.x & 16) ? (uint32_t)r[0] : (uint32_t)r[1];
-    }
-    case 32: {
-      const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-      return (threadIdx.x & 32) ? (uint32_t)r[0] : (uint32_t)r[1];
-    }
+    case 16:
+      return xshfl_swap16(v);
+    case 32:
+      return xshfl_swap32(v);
     default:
       return (uint32_t)__shfl_xor((int)v, o, 64);
   }

@@ -159,69 +159,90 @@ __device__ __forceinline__ double block_seg_carry(bool f, double s,
   return ex_s;
 }
 
-// One bitonic stage (merge size K, partner distance J), unrolled at compile
-// time.
-template <int E, int T, int K, int J>
-__device__ __forceinline__ void hb_stage(float (&y)[E], float* lds, int tid,
+// Bitonic sort in "flip" form (every comparator ascending): merge level K
+// first compares position i with i ^ (K-1) (the mirror image inside its
+// K-block), then with i ^ J for J = K/4, ..., 1; the smaller value always
+// goes to the lower position.  Values are held E per thread in blocked
+// order (thread t: positions t*E .. t*E+E-1).  Partners in the same thread
+// are register compare-exchanges; partners up to 63 lanes away come through
+// lane exchanges (DPP, lane swaps); partners in another wave go through LDS
+// (lds: the T*E values, two barriers per stage).  Everything is unrolled at
+// compile time.
+
+// stage with partner i ^ MASK; MASK = K-1 (mirror) or J (power of two)
+template <int E, int MASK, bool MIRROR>
+__device__ __forceinline__ void fb_stage(float (&y)[E], float* lds, int tid,
                                          int lane) {
-  if constexpr (J < E) {
+  constexpr int TOP = MIRROR ? (MASK + 1) / 2 : MASK;  // bit deciding lower
+  if constexpr (MASK < E) {
+    // partners inside the thread
 #pragma unroll
     for (int r = 0; r < E; ++r) {
-      if (r & J) continue;
-      const bool up = ((tid * E + r) & K) == 0;
-      const float a = y[r], b = y[r | J];
-      const float lo = fminf(a, b), hi = fmaxf(a, b);
-      y[r] = up ? lo : hi;
-      y[r | J] = up ? hi : lo;
-    }
-  } else if constexpr (J < 64 * E) {
-    constexpr int LJ = J / E;
-    const bool lower = (lane & LJ) == 0;
-#pragma unroll
-    for (int r = 0; r < E; ++r) {
-      const bool up = ((tid * E + r) & K) == 0;
-      const float o = xshfl(y[r], LJ);
-      y[r] = (lower == up) ? fminf(y[r], o) : fmaxf(y[r], o);
+      const int r2 = r ^ MASK;
+      if (r2 <= r) continue;
+      const float a = y[r], b = y[r2];
+      y[r] = fminf(a, b);
+      y[r2] = fmaxf(a, b);
     }
   } else {
-    float4* l4 = reinterpret_cast<float4*>(lds);
+    // partner thread t ^ LM; register r pairs with r (power of two) or with
+    // E-1-r (mirror)
+    constexpr int LM = MASK / E;
+    const bool lower = (tid & (TOP / E)) == 0;
+    float o[E];
+    if constexpr (LM < 64) {
 #pragma unroll
-    for (int r = 0; r < E; r += 4)
-      l4[(tid * E + r) / 4] = make_float4(y[r], y[r + 1], y[r + 2], y[r + 3]);
-    __syncthreads();
-    const int pbase = (tid * E) ^ J;  // partner positions pbase + r
-    const bool lower = ((tid * E) & J) == 0;
+      for (int r = 0; r < E; ++r) o[r] = xshfl(y[MIRROR ? E - 1 - r : r], LM);
+    } else {
+      float4* l4 = reinterpret_cast<float4*>(lds);
 #pragma unroll
-    for (int r = 0; r < E; r += 4) {
-      const float4 o = l4[(pbase + r) / 4];
-      const float ov[4] = {o.x, o.y, o.z, o.w};
+      for (int r = 0; r < E; r += 4)
+        l4[(tid * E + r) / 4] = make_float4(y[r], y[r + 1], y[r + 2], y[r + 3]);
+      __syncthreads();
+      const int pt = tid ^ LM;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bool up = ((tid * E + r + c) & K) == 0;
-        y[r + c] = (lower == up) ? fminf(y[r + c], ov[c]) : fmaxf(y[r + c], ov[c]);
+      for (int r = 0; r < E; r += 4) {
+        const float4 v = l4[(pt * E + r) / 4];
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (MIRROR) o[E - 1 - (r + c)] = vv[c];
+          else o[r + c] = vv[c];
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
+    (void)lane;
+#pragma unroll
+    for (int r = 0; r < E; ++r)
+      y[r] = lower ? fminf(y[r], o[r]) : fmaxf(y[r], o[r]);
   }
-  if constexpr (J > 1) hb_stage<E, T, K, J / 2>(y, lds, tid, lane);
 }
 
-template <int E, int T, int K>
-__device__ __forceinline__ void hb_merge(float (&y)[E], float* lds, int tid,
-                                         int lane) {
-  hb_stage<E, T, K, K / 2>(y, lds, tid, lane);
-  if constexpr (K < T * E) hb_merge<E, T, 2 * K>(y, lds, tid, lane);
+template <int E, int K, int J>
+__device__ __forceinline__ void fb_halves(float (&y)[E], float* lds, int tid,
+                                          int lane) {
+  if constexpr (J >= 1) {
+    fb_stage<E, J, false>(y, lds, tid, lane);
+    fb_halves<E, K, J / 2>(y, lds, tid, lane);
+  }
 }
 
-// Bitonic sort of T*E floats held E per thread (thread t: positions
-// t*E .. t*E+E-1, ascending at the end).  Stages whose partner is in the
-// same thread are register compare-exchanges, partners up to 63 lanes away
-// are reached with lane exchanges (DPP / lane swaps), and only the stages
-// that cross waves go
-// through LDS (lds: T*E floats), two barriers each.
-template <int E, int T>
-__device__ __forceinline__ void hybrid_bitonic(float (&y)[E], float* lds) {
-  hb_merge<E, T, 2>(y, lds, threadIdx.x, threadIdx.x & 63);
+template <int E, int N, int K>
+__device__ __forceinline__ void fb_levels(float (&y)[E], float* lds, int tid,
+                                          int lane) {
+  fb_stage<E, K - 1, true>(y, lds, tid, lane);
+  fb_halves<E, K, K / 4>(y, lds, tid, lane);
+  if constexpr (K < N) fb_levels<E, N, 2 * K>(y, lds, tid, lane);
+}
+
+// Sort N = T*E values (T threads of a workgroup, or the lanes of one group
+// when N <= 64*E and lds is unused) ascending in blocked order.  `tid` is
+// the thread's index among the N/E participants.
+template <int E, int N>
+__device__ __forceinline__ void flip_bitonic(float (&y)[E], float* lds,
+                                             int tid) {
+  fb_levels<E, N, 2>(y, lds, tid, tid & 63);
 }
 
 struct SortShared {
@@ -293,7 +314,7 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
       const float x = clipped(p[m]);
       y[m] = epos(m) < nj ? (x == 0.f ? 0.f : x) : __builtin_inff();
     }
-    hybrid_bitonic<E, T>(y, sorted);
+    flip_bitonic<E, D>(y, sorted, tid);
     float4* l4 = reinterpret_cast<float4*>(sorted);
 #pragma unroll
     for (int r = 0; r < E; r += 4)
@@ -650,37 +671,6 @@ __device__ __forceinline__ int group_argmax(double v, int key, double* best_out)
   return key;
 }
 
-template <int E, int G>
-__device__ __forceinline__ void wave_bitonic(float (&y)[E], int lane) {
-  constexpr int N = G * E;
-#pragma unroll
-  for (int k = 2; k <= N; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j >= E) {
-        const int lj = j / E;
-        const bool lower = (lane & lj) == 0;
-#pragma unroll
-        for (int r = 0; r < E; ++r) {
-          const bool up = ((lane * E + r) & k) == 0;
-          const float o = xshfl(y[r], lj);
-          y[r] = (lower == up) ? fminf(y[r], o) : fmaxf(y[r], o);
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < E; ++r) {
-          if (r & j) continue;
-          const bool up = ((lane * E + r) & k) == 0;
-          const float a = y[r], b = y[r | j];
-          const float lo = fminf(a, b), hi = fmaxf(a, b);
-          y[r] = up ? lo : hi;
-          y[r | j] = up ? hi : lo;
-        }
-      }
-    }
-  }
-}
-
 // Sorted value at group-uniform position pos.
 template <int E, int G>
 __device__ __forceinline__ float wave_at(const float (&y)[E], int pos) {
@@ -784,7 +774,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_wave_sort_quant(
     const float x = clipped(p[m]);
     y[m] = epos(m) < nj ? (x == 0.f ? 0.f : x) : __builtin_inff();
   }
-  wave_bitonic<E, G>(y, lane);
+  flip_bitonic<E, D>(y, nullptr, lane);
 
   const int r0 = lane * E;
   float y_next_run = __shfl_down(y[0], 1, G);
