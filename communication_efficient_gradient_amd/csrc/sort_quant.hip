@@ -801,17 +801,46 @@ __global__ __launch_bounds__(kGroupThreads) void k_wave_sort_quant(
         if (r0 + m < nj) acc = acc + (double)y[m];
       }
     }
+    // F(k) = P^2/k + Q^2/(n-k) at every split between distinct values: first
+    // in fp32 (a screen), then exactly in fp64 only where the screen is
+    // within 1e-5 of its maximum (two fp64 divisions per split otherwise).  The screen's error (< 1e-6 relative,
+    // both terms >= 0, values scaled by a power of two so |P|, |Q| <= d)
+    // keeps the exact maximum and every exact tie among the candidates.
+    const float amax = fmaxf(fabsf(wave_at<E, G>(y, 0)), fabsf(wave_at<E, G>(y, nj - 1)));
+    int ex = 0;
+    frexpf(amax, &ex);
+    const double sc = ldexp(1.0, -ex);
+    auto screen_at = [&](int m, double P) -> float {
+      const int pos = r0 + m;
+      const int k = pos + 1;
+      const float yk = (m + 1 < E) ? y[m + 1] : y_next_run;
+      if (k >= nj || !(y[m] < yk)) return -1.f;
+      const float p32 = (float)(P * sc), q32 = (float)(Qrun[m] * sc);
+      return p32 * p32 * __builtin_amdgcn_rcpf((float)k) +
+             q32 * q32 * __builtin_amdgcn_rcpf((float)(nj - k));
+    };
+    float Fa[E];
+    float fmax32 = -1.f;
+    {
+      double P = pre;
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        if (r0 + m < nj) P = P + (double)y[m];
+        Fa[m] = screen_at(m, P);
+        fmax32 = fmaxf(fmax32, Fa[m]);
+      }
+    }
+    fmax32 = group_max<G>(fmax32);
+    const float screen = fmax32 * (1.0f - 1e-5f);
     double best = -1.0;
     int bestk = 0x7fffffff;
-    double P = pre;
+    {
+      double P = pre;
 #pragma unroll
-    for (int m = 0; m < E; ++m) {
-      const int pos = r0 + m;
-      if (pos < nj) P = P + (double)y[m];
-      const int k = pos + 1;
-      if (k < nj) {
-        const float yk = (m + 1 < E) ? y[m + 1] : y_next_run;
-        if (y[m] < yk) {
+      for (int m = 0; m < E; ++m) {
+        if (r0 + m < nj) P = P + (double)y[m];
+        if (Fa[m] >= 0.f && Fa[m] >= screen) {
+          const int k = r0 + m + 1;
           const double F = P * P / (double)k + Qrun[m] * Qrun[m] / (double)(nj - k);
           if (F > best) {
             best = F;
