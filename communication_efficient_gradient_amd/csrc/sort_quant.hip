@@ -633,6 +633,15 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
 // workgroup kernel above, with group-wide scans and argmax.
 constexpr int kGroupThreads = 256;
 
+// Values per lane and lanes per bucket.  8 values per lane keeps these
+// kernels near 100-140 VGPRs; 16 per lane (fewer lanes per bucket, so
+// cheaper scans and reductions) measured slower at half the occupancy.
+template <int D>
+struct WaveCfg {
+  static constexpr int E = 8;
+  static constexpr int G = D / E;
+};
+
 // Exclusive segmented scan over the G lanes of a group (see block_seg_carry):
 // returns the combination of the aggregates (f, s) of the lanes before this
 // one (REV = false) or after it (REV = true).
@@ -723,8 +732,8 @@ __global__ __launch_bounds__(kGroupThreads) void k_wave_sort_quant(
     int64_t n, int64_t nb, const float* __restrict__ g, float* __restrict__ e,
     uint32_t k0, uint32_t k1, uint32_t step, int L, int clip, float clip_sigma,
     uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes) {
-  constexpr int E = 8;
-  constexpr int G = D / E;
+  constexpr int E = WaveCfg<D>::E;
+  constexpr int G = WaveCfg<D>::G;
   constexpr int VEC = 4;
   constexpr int NQ = E / VEC;
   const int lane = threadIdx.x % G;  // lane within the bucket's group
@@ -1101,7 +1110,7 @@ int launch_sort_one(int64_t n, const float* g, float* e, uint64_t seed,
                     hipStream_t st) {
   const int64_t nb = (n + D - 1) / D;
   if constexpr (D <= 512) {
-    constexpr int per_block = kGroupThreads / (D / 8);
+    constexpr int per_block = kGroupThreads / WaveCfg<D>::G;
     const int64_t blocks = (nb + per_block - 1) / per_block;
     hipLaunchKernelGGL((k_wave_sort_quant<SCHEME, BITS, D>), dim3((uint32_t)blocks),
                        dim3(kGroupThreads), 0, st, n, nb, g, e,
