@@ -190,6 +190,29 @@ def copy_reference(torch, stream, nbytes: int = 1 << 30) -> dict:
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
 
 
+def oracle_rate(host_g, desc_kw, ef: bool, seed: int = 0, budget: float = 0.5,
+                max_n: int = 1 << 22):
+    """The CPU oracle's quantize throughput (GB/s of fp32 input) on a prefix
+    of the same input: whole buckets, growing until `budget` seconds."""
+    import numpy as np
+
+    import oracle as O
+
+    od = O.Desc(**desc_kw)
+    n = min(host_g.size, 1 << 16)
+    n -= n % od.d if n > od.d else 0
+    while True:
+        g = host_g[:n]
+        e = np.zeros(n, dtype=np.float32) if ef else None
+        t0 = time.perf_counter()
+        O.quantize(od, g, e, seed=seed, step=0)
+        dt = time.perf_counter() - t0
+        if dt >= budget or n >= min(max_n, host_g.size):
+            return {"oracle_GBps": round(4 * n / dt / 1e9, 4),
+                    "oracle_elements": n, "oracle_threads": O.threads()}
+        n = min(4 * n, max_n, host_g.size)
+
+
 def entry(name, ms, nbytes, n, bound="hbm", extra=None):
     gbs = nbytes / (ms * 1e-3) / 1e9
     r = {"kernel": name, "ms": round(ms, 5),
@@ -245,7 +268,8 @@ def suite_orq(torch, gq, WL, stream, tb, reps):
     """ORQ-5 / ORQ-9 on 100M elements, clip off / on."""
     out = []
     t0 = time.time()
-    g = torch.from_numpy(WL.orq_gradient()).cuda()
+    host = WL.orq_gradient()
+    g = torch.from_numpy(host).cuda()
     log(f"suite: orq input in {time.time() - t0:.1f}s")
     n = g.numel()
     for L in (5, 9):
@@ -257,7 +281,9 @@ def suite_orq(torch, gq, WL, stream, tb, reps):
             ms = tb(lambda i: q(3, 0), max(3, reps // 2))
             out.append(entry(f"quantize orq L={L} clip={clip} d=512 n={n}", ms,
                              quant_bytes(bits, L, 512, n, False), n,
-                             bound="alu"))
+                             bound="alu", extra=oracle_rate(
+                                 host, dict(scheme=3, d=512, L=L, flags=clip,
+                                            clip_sigma=3.0), False, seed=3)))
             del c, m, q
     return out
 
@@ -267,7 +293,8 @@ def suite_bingrad(torch, gq, WL, stream, tb, reps):
     1B elements, over the bucket sweep."""
     out = []
     t0 = time.time()
-    g = torch.from_numpy(WL.bingrad_gradient()).cuda()
+    host = WL.bingrad_gradient()
+    g = torch.from_numpy(host).cuda()
     log(f"suite: bingrad input in {time.time() - t0:.1f}s")
     n = g.numel()
     e = torch.zeros_like(g)
@@ -279,7 +306,9 @@ def suite_bingrad(torch, gq, WL, stream, tb, reps):
             q = gq.PreparedQuantize(d, g, e, c, m, stream)
             ms = tb(lambda i: q(0, i), max(3, reps // 2))
             out.append(entry(f"quantize {nm}+ef d={dd} n={n}", ms,
-                             quant_bytes(1, 2, dd, n, True), n))
+                             quant_bytes(1, 2, dd, n, True), n,
+                             extra=oracle_rate(host, dict(scheme=scheme, d=dd),
+                                               True)))
             del c, m, q
     return out
 
@@ -291,8 +320,13 @@ def suite_workers(torch, gq, WL, stream, tb):
     d = gq.desc(gq.GQ_UNIFORM, 512, s=127)
     Gs, Es, Cs, Ms = [], [], [], []
     t0 = time.time()
+    host1 = None
     for w in range(1, W + 1):
-        Gs.append(torch.from_numpy(WL.worker_gradient(w)).cuda())
+        h = WL.worker_gradient(w)
+        if w == 1:
+            host1 = h[: 1 << 22].copy()
+        Gs.append(torch.from_numpy(h).cuda())
+        del h
         Es.append(torch.zeros(n, dtype=torch.float32, device="cuda"))
         c, m = gq.alloc_payload(d, n)
         Cs.append(c)
@@ -302,7 +336,9 @@ def suite_workers(torch, gq, WL, stream, tb):
           for w in range(W)]
     ms = tb(lambda i: qs[i % W](i % W + 1, 0), 2 * W)
     out.append(entry(f"quantize int8+ef d=512 n={n} (per worker)", ms,
-                     quant_bytes(8, 1, 512, n, True), n))
+                     quant_bytes(8, 1, 512, n, True), n,
+                     extra=oracle_rate(host1, dict(scheme=0, d=512, s=127),
+                                       True, seed=1)))
     avg = torch.empty(n, dtype=torch.float32, device="cuda")
     dq = gq.PreparedDequantizeAccumulate(d, n, Cs, Ms, 1.0 / W, 0.0, avg,
                                          stream)

@@ -16,6 +16,8 @@ Parity status of each routine (what pins it is in ``tests/test_oracle_*``):
     quantize (orq)        brute-force best insertion per greedy step, global
                           optimum for L=3, grid search, variance chain
     pack / unpack         numpy.packbits (1 bit), int8 bytes (8 bit)
+    dense pack / unpack   Python big-integer base-A arithmetic, field widths
+                          from exact integer powers, round trips
     dequantize_accumulate exact rational sums (fractions) on small inputs
 """
 from __future__ import annotations
@@ -30,6 +32,7 @@ from . import build as _build
 
 UNIFORM, BIN_SIGN, BIN_OPT, ORQ = 0, 1, 2, 3
 FLAG_CLIP = 1
+FLAG_DENSE = 2
 
 _lib = None
 
@@ -52,12 +55,18 @@ def lib():
                                      i64, cfp, fp, u64, u32, u8p, fp, u8p]
         L.gqref_select_levels.argtypes = [i32, i32, i32, i32, i32, C.c_float,
                                           i64, i64, cfp, cfp, fp, u8p]
-        L.gqref_dequantize.argtypes = [i32, i32, i32, i32, i64, u8p, cfp, fp]
-        L.gqref_error_feedback.argtypes = [i32, i32, i32, i32, i64, cfp, fp,
-                                           u8p, cfp]
+        L.gqref_dequantize.argtypes = [i32, i32, i32, i32, i32, i64, u8p, cfp,
+                                       fp]
+        L.gqref_error_feedback.argtypes = [i32, i32, i32, i32, i32, i64, cfp,
+                                           fp, u8p, cfp]
         L.gqref_dequantize_accumulate.argtypes = [
-            i32, i32, i32, i32, i64, i32, C.POINTER(C.c_void_p),
+            i32, i32, i32, i32, i32, i64, i32, C.POINTER(C.c_void_p),
             C.POINTER(C.c_void_p), C.c_float, C.c_float, fp]
+        L.gqref_dense_width.argtypes = [i32]
+        L.gqref_pack_dense.argtypes = [i32, i64, C.c_void_p, u8p]
+        L.gqref_pack_dense.restype = None
+        L.gqref_unpack_dense.argtypes = [i32, i64, u8p, C.c_void_p]
+        L.gqref_unpack_dense.restype = None
         L.gqref_pack.argtypes = [i32, i64, C.c_void_p, u8p]
         L.gqref_pack.restype = None
         L.gqref_unpack.argtypes = [i32, i64, u8p, C.c_void_p]
@@ -86,10 +95,27 @@ class Desc:
     def k(self) -> int:
         return lib().gqref_meta_per_bucket(self.scheme, self.L)
 
+    @property
+    def dense(self) -> bool:
+        return bool(self.flags & FLAG_DENSE)
+
+    @property
+    def alphabet(self) -> int:
+        """Number of distinct codes: 2s+1, L or 2."""
+        return 2 * self.s + 1 if self.scheme == UNIFORM else (
+            self.L if self.scheme == ORQ else 2)
+
+    @property
+    def field_bits(self) -> int:
+        """Dense packing: bits of one 8-code field."""
+        return dense_width(self.alphabet)
+
     def nb(self, n: int) -> int:
         return (n + self.d - 1) // self.d
 
     def code_bytes(self, n: int) -> int:
+        if self.dense:
+            return (((n + 7) // 8) * self.field_bits + 7) // 8
         return (n * self.bits + 7) // 8
 
 
@@ -156,8 +182,9 @@ def dequantize(desc: Desc, n: int, codes, meta):
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     meta = _f32(meta)
     out = np.empty(n, dtype=np.float32)
-    rc = lib().gqref_dequantize(desc.scheme, desc.d, desc.s, desc.L, n,
-                                _ptr(codes), _ptr(meta), _ptr(out))
+    rc = lib().gqref_dequantize(desc.scheme, desc.d, desc.s, desc.L,
+                                desc.flags, n, _ptr(codes), _ptr(meta),
+                                _ptr(out))
     if rc:
         raise ValueError("oracle dequantize: invalid arguments")
     return out
@@ -169,8 +196,8 @@ def error_feedback(desc: Desc, g, e, codes, meta):
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     meta = _f32(meta)
     rc = lib().gqref_error_feedback(desc.scheme, desc.d, desc.s, desc.L,
-                                    g.size, _ptr(g), _ptr(e), _ptr(codes),
-                                    _ptr(meta))
+                                    desc.flags, g.size, _ptr(g), _ptr(e),
+                                    _ptr(codes), _ptr(meta))
     if rc:
         raise ValueError("oracle error_feedback: invalid arguments")
     return e
@@ -185,8 +212,8 @@ def dequantize_accumulate(desc: Desc, n: int, codes_list, meta_list,
     cp = (C.c_void_p * W)(*[c.ctypes.data for c in cl])
     mp = (C.c_void_p * W)(*[m.ctypes.data for m in ml])
     rc = lib().gqref_dequantize_accumulate(desc.scheme, desc.d, desc.s, desc.L,
-                                           n, W, cp, mp, alpha, beta,
-                                           _ptr(out))
+                                           desc.flags, n, W, cp, mp, alpha,
+                                           beta, _ptr(out))
     if rc:
         raise ValueError("oracle dequantize_accumulate: invalid arguments")
     return out
@@ -206,8 +233,30 @@ def unpack(bits: int, n: int, codes) -> np.ndarray:
     return out
 
 
+def dense_width(A: int) -> int:
+    return lib().gqref_dense_width(A)
+
+
+def pack_dense(A: int, digits) -> np.ndarray:
+    v = np.ascontiguousarray(digits, dtype=np.uint32)
+    out = np.zeros((((v.size + 7) // 8) * dense_width(A) + 7) // 8, dtype=np.uint8)
+    lib().gqref_pack_dense(A, v.size, _ptr(v), _ptr(out))
+    return out
+
+
+def unpack_dense(A: int, n: int, codes) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(n, dtype=np.uint32)
+    lib().gqref_unpack_dense(A, n, _ptr(c), _ptr(out))
+    return out
+
+
 def signed_codes(desc: Desc, n: int, codes) -> np.ndarray:
-    """Codes as integers (two's complement decoded for the uniform scheme)."""
+    """Codes as integers: -s..s for the uniform scheme (two's complement or
+    dense digits decoded), level index otherwise."""
+    if desc.dense:
+        v = unpack_dense(desc.alphabet, n, codes).astype(np.int64)
+        return v - desc.s if desc.scheme == UNIFORM else v
     v = unpack(desc.bits, n, codes).astype(np.int64)
     if desc.scheme == UNIFORM:
         m = 1 << (desc.bits - 1)

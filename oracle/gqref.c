@@ -99,6 +99,67 @@ void gqref_unpack(int bits, int64_t n, const uint8_t *codes, uint32_t *vals) {
   for (int64_t i = 0; i < n; ++i) vals[i] = get_code(codes, i, bits);
 }
 
+/* ------------------------------------------------------ dense packing --
+ * An alphabet of A symbols (A <= 16) that is not a power of two wastes
+ * bits in a fixed-width field.  Dense packing groups 8 consecutive codes
+ * into one base-A integer V = sum_t digit(8g + t) * A^t (the first code is
+ * the least significant digit; digits of absent elements are 0) and writes
+ * V as a field of W = ceil(log2(A^8)) bits: field g occupies stream bits
+ * [W*g, W*g + W), least significant bit first, in the same LSB-first
+ * bitstream as fixed-width codes. */
+int gqref_dense_width(int A) {
+  if (A < 2 || A > 16) return -1;
+  uint64_t p = 1;
+  for (int i = 0; i < 8; ++i) p *= (uint64_t)A;
+  int w = 0;
+  while (((uint64_t)1 << w) < p) ++w;
+  return w;
+}
+
+static void put_bits(uint8_t *codes, int64_t bit0, int w, uint64_t v) {
+  for (int t = 0; t < w; ++t) {
+    int64_t pos = bit0 + t;
+    if ((v >> t) & 1u) codes[pos / 8] |= (uint8_t)(1u << (pos % 8));
+  }
+}
+
+static uint64_t get_bits(const uint8_t *codes, int64_t bit0, int w) {
+  uint64_t v = 0;
+  for (int t = 0; t < w; ++t) {
+    int64_t pos = bit0 + t;
+    v |= (uint64_t)((codes[pos / 8] >> (pos % 8)) & 1u) << t;
+  }
+  return v;
+}
+
+/* Encode digits[0 .. n) (each < A) as dense fields starting at field 0. */
+void gqref_pack_dense(int A, int64_t n, const uint32_t *digits, uint8_t *codes) {
+  int w = gqref_dense_width(A);
+  int64_t groups = (n + 7) / 8;
+  memset(codes, 0, (size_t)((groups * w + 7) / 8));
+  for (int64_t g = 0; g < groups; ++g) {
+    uint64_t v = 0, place = 1;
+    for (int t = 0; t < 8; ++t) {
+      int64_t i = 8 * g + t;
+      if (i < n) v += (uint64_t)digits[i] * place;
+      place *= (uint64_t)A;
+    }
+    put_bits(codes, g * w, w, v);
+  }
+}
+
+/* Digit of element i of a dense stream. */
+static uint32_t dense_digit(const uint8_t *codes, int A, int w, int64_t i) {
+  uint64_t v = get_bits(codes, (i / 8) * w, w);
+  for (int64_t t = 0; t < i % 8; ++t) v /= (uint64_t)A;
+  return (uint32_t)(v % (uint64_t)A);
+}
+
+void gqref_unpack_dense(int A, int64_t n, const uint8_t *codes, uint32_t *digits) {
+  int w = gqref_dense_width(A);
+  for (int64_t i = 0; i < n; ++i) digits[i] = dense_digit(codes, A, w, i);
+}
+
 /* ---------------------------------------------------- compensated sums -- */
 typedef struct {
   double s, c;
@@ -379,6 +440,7 @@ static void orq_greedy(const float *y, int64_t nj, int L, float *lev,
 typedef struct {
   int scheme, d, s, L, flags, bits, k;
   float clip_sigma;
+  int dense, A, w; /* dense packing: alphabet size and field width */
 } params;
 
 /* Select the bucket's levels from its effective values p; for ORQ also
@@ -415,27 +477,38 @@ static void select_bucket(const params *pr, const float *p, int64_t nj,
   }
 }
 
-/* Level value for a code, given the bucket's meta row. */
-static float dequant_one(const params *pr, uint32_t code, const float *meta) {
+/* Level value for a code value c (signed integer -s..s for the uniform
+ * scheme, level index otherwise), given the bucket's meta row. */
+static float dequant_one(const params *pr, int32_t c, const float *meta) {
   switch (pr->scheme) {
     case UNIFORM: {
       /* step = M / s; xhat = c * step, each rounded once. */
       float delta = meta[0] / (float)pr->s;
-      return (float)sext(code, pr->bits) * delta;
+      return (float)c * delta;
     }
     case BIN_SIGN:
     case BIN_OPT:
-      return code ? meta[1] : meta[0];
+      return c ? meta[1] : meta[0];
     default:
-      return meta[code];
+      return meta[c];
   }
+}
+
+/* Code value of element i of a payload (fixed-width or dense). */
+static int32_t read_code(const params *pr, const uint8_t *codes, int64_t i) {
+  if (pr->dense) {
+    int32_t digit = (int32_t)dense_digit(codes, pr->A, pr->w, i);
+    return pr->scheme == UNIFORM ? digit - pr->s : digit;
+  }
+  uint32_t raw = get_code(codes, i, pr->bits);
+  return pr->scheme == UNIFORM ? sext(raw, pr->bits) : (int32_t)raw;
 }
 
 /* Code for one element: random rounding between the two adjacent levels
  * ("Gradient Quantization" glossary, Stochastic Quantization bullet: a value
  * a fraction q of the way from the lower to the upper level rounds up with
  * probability q).  Rounds up iff u < q. */
-static uint32_t code_uniform(const params *pr, float p, float M, float u) {
+static int32_t code_uniform(const params *pr, float p, float M, float u) {
   if (M == 0.0f || p == 0.0f) return 0;
   /* A bucket whose max-abs is tiny is scaled up by 2^96 first (exact), so
    * s/M stays finite; for every normal-range bucket the factor is 1. */
@@ -446,8 +519,7 @@ static uint32_t code_uniform(const params *pr, float p, float M, float u) {
   float l = floorf(r);
   float q = r - l;
   int32_t mag = (int32_t)l + (u < q ? 1 : 0);
-  int32_t c = (p < 0.0f) ? -mag : mag;
-  return (uint32_t)c & ((1u << pr->bits) - 1u);
+  return (p < 0.0f) ? -mag : mag;
 }
 
 static uint32_t code_orq(const params *pr, float pcl, const float *lev,
@@ -470,6 +542,7 @@ static void quantize_bucket(const params *pr, int64_t gi, const float *g,
                             uint8_t *tie) {
   float *p = (float *)malloc((size_t)nj * sizeof(float));
   float *pc = (float *)malloc((size_t)nj * sizeof(float));
+  int32_t *cv = (int32_t *)malloc((size_t)nj * sizeof(int32_t));
   /* Error feedback: add the carried residual before quantizing ("Gradient
    * Quantization" glossary, error-feedback paragraph). */
   for (int64_t t = 0; t < nj; ++t) p[t] = e ? g[t] + e[t] : g[t];
@@ -477,27 +550,44 @@ static void quantize_bucket(const params *pr, int64_t gi, const float *g,
   int no_split = 0;
   select_bucket(pr, p, nj, meta, tie, pc, &thr, &no_split);
   for (int64_t t = 0; t < nj; ++t) {
-    uint32_t c;
+    int32_t c;
     switch (pr->scheme) {
       case UNIFORM:
         c = code_uniform(pr, p[t], meta[0], uniform_u(seed, step, gi + t));
         break;
       case BIN_SIGN:
-        c = p[t] >= 0.0f ? 1u : 0u;
+        c = p[t] >= 0.0f ? 1 : 0;
         break;
       case BIN_OPT:
-        c = no_split ? 0u : (p[t] >= thr ? 1u : 0u);
+        c = no_split ? 0 : (p[t] >= thr ? 1 : 0);
         break;
       default:
-        c = code_orq(pr, pc[t], meta, uniform_u(seed, step, gi + t));
+        c = (int32_t)code_orq(pr, pc[t], meta, uniform_u(seed, step, gi + t));
         break;
     }
-    put_code(codes, li + t, pr->bits, c);
+    cv[t] = c;
+    if (!pr->dense) put_code(codes, li + t, pr->bits, (uint32_t)c & ((1u << pr->bits) - 1u));
     /* Residual with the unclipped value, so a clipped excess is carried. */
     if (e) e[t] = p[t] - dequant_one(pr, c, meta);
   }
+  if (pr->dense) {
+    /* the bucket starts at a multiple of d (a multiple of 8) in the stream,
+     * so its fields are whole; a partial last group pads with digit 0 */
+    for (int64_t g0 = 0; g0 < nj; g0 += 8) {
+      uint64_t v = 0, place = 1;
+      for (int t = 0; t < 8; ++t) {
+        if (g0 + t < nj) {
+          int32_t digit = pr->scheme == UNIFORM ? cv[g0 + t] + pr->s : cv[g0 + t];
+          v += (uint64_t)digit * place;
+        }
+        place *= (uint64_t)pr->A;
+      }
+      put_bits(codes, ((li + g0) / 8) * pr->w, pr->w, v);
+    }
+  }
   free(p);
   free(pc);
+  free(cv);
 }
 
 static int make_params(params *pr, int scheme, int d, int s, int L, int flags,
@@ -510,7 +600,18 @@ static int make_params(params *pr, int scheme, int d, int s, int L, int flags,
   pr->clip_sigma = clip_sigma;
   pr->bits = gqref_bits(scheme, s, L);
   pr->k = gqref_meta_per_bucket(scheme, L);
-  return (pr->bits < 0 || pr->k < 0) ? -1 : 0;
+  if (pr->bits < 0 || pr->k < 0) return -1;
+  pr->dense = (flags & 2) ? 1 : 0;
+  pr->A = scheme == UNIFORM ? 2 * s + 1 : (scheme == ORQ ? L : 2);
+  pr->w = pr->dense ? gqref_dense_width(pr->A) : 0;
+  if (pr->dense && pr->w < 0) return -1;
+  return 0;
+}
+
+/* Bytes of the code stream for n elements. */
+static int64_t stream_bytes(const params *pr, int64_t n) {
+  if (pr->dense) return (((n + 7) / 8) * pr->w + 7) / 8;
+  return (n * pr->bits + 7) / 8;
 }
 
 int gqref_quantize(int scheme, int d, int s, int L, int flags, float clip_sigma,
@@ -523,7 +624,7 @@ int gqref_quantize(int scheme, int d, int s, int L, int flags, float clip_sigma,
     return -1;
   if (!g || !codes || !meta) return -1;
   int64_t nb = (n + d - 1) / d;
-  memset(codes, 0, (size_t)((n * pr.bits + 7) / 8));
+  memset(codes, 0, (size_t)stream_bytes(&pr, n));
 #pragma omp parallel for schedule(static)
   for (int64_t j = 0; j < nb; ++j) {
     int64_t lo = j * d, nj = (n - lo < d) ? n - lo : d;
@@ -557,44 +658,44 @@ int gqref_select_levels(int scheme, int d, int s, int L, int flags,
   return 0;
 }
 
-int gqref_dequantize(int scheme, int d, int s, int L, int64_t n,
+int gqref_dequantize(int scheme, int d, int s, int L, int flags, int64_t n,
                      const uint8_t *codes, const float *meta, float *xhat) {
   params pr;
-  if (check(scheme, d, s, L, 0, n) || make_params(&pr, scheme, d, s, L, 0, 0.f))
+  if (check(scheme, d, s, L, 0, n) || make_params(&pr, scheme, d, s, L, flags, 0.f))
     return -1;
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i)
-    xhat[i] = dequant_one(&pr, get_code(codes, i, pr.bits), meta + (i / d) * pr.k);
+    xhat[i] = dequant_one(&pr, read_code(&pr, codes, i), meta + (i / d) * pr.k);
   return 0;
 }
 
-int gqref_error_feedback(int scheme, int d, int s, int L, int64_t n,
+int gqref_error_feedback(int scheme, int d, int s, int L, int flags, int64_t n,
                          const float *g, float *e, const uint8_t *codes,
                          const float *meta) {
   params pr;
-  if (check(scheme, d, s, L, 0, n) || make_params(&pr, scheme, d, s, L, 0, 0.f))
+  if (check(scheme, d, s, L, 0, n) || make_params(&pr, scheme, d, s, L, flags, 0.f))
     return -1;
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) {
     float p = g[i] + e[i];
-    e[i] = p - dequant_one(&pr, get_code(codes, i, pr.bits), meta + (i / d) * pr.k);
+    e[i] = p - dequant_one(&pr, read_code(&pr, codes, i), meta + (i / d) * pr.k);
   }
   return 0;
 }
 
-int gqref_dequantize_accumulate(int scheme, int d, int s, int L, int64_t n,
-                                int W, const uint8_t *const *codes,
+int gqref_dequantize_accumulate(int scheme, int d, int s, int L, int flags,
+                                int64_t n, int W, const uint8_t *const *codes,
                                 const float *const *meta, float alpha,
                                 float beta, float *out) {
   params pr;
-  if (check(scheme, d, s, L, 0, n) || make_params(&pr, scheme, d, s, L, 0, 0.f))
+  if (check(scheme, d, s, L, 0, n) || make_params(&pr, scheme, d, s, L, flags, 0.f))
     return -1;
   if (W < 1) return -1;
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) {
     nsum acc = {0, 0};
     for (int w = 0; w < W; ++w)
-      nadd(&acc, (double)dequant_one(&pr, get_code(codes[w], i, pr.bits),
+      nadd(&acc, (double)dequant_one(&pr, read_code(&pr, codes[w], i),
                                      meta[w] + (i / d) * pr.k));
     double v = (double)alpha * nval(&acc);
     if (beta != 0.0f) v += (double)beta * (double)out[i];

@@ -23,7 +23,8 @@
  * the bucket that starts at i0.
  *
  * Scheme numbers: 0 uniform (QSGD / ternary / INT8), 1 two-level sign split,
- * 2 two-level optimal split (BinGrad-b), 3 ORQ.  flags bit 0 = clip.
+ * 2 two-level optimal split (BinGrad-b), 3 ORQ.  flags bit 0 = clip, bit 1 =
+ * dense packing (digits: c + s for the uniform scheme, the code otherwise).
  *
  * Return value: 0 on success, -1 on an invalid argument.
  */
@@ -48,7 +49,8 @@ int gqref_meta_per_bucket(int scheme, int L);
 
 /* Quantize: p = g (+ e), per-bucket levels, random rounding, packing;
  * with e != NULL the residual p - dequant(code) is written back into e.
- * codes: ceil(n*bits/8) bytes (fully written, pad bits zero).
+ * codes: ceil(n*bits/8) bytes, or ceil(ceil(n/8)*W/8) with dense packing
+ * (fully written, pad bits zero).
  * meta: nb * k floats.  tie: nb bytes or NULL (near-tie record). */
 int gqref_quantize(int scheme, int d, int s, int L, int flags, float clip_sigma,
                    int64_t i0, int64_t n, const float *g, float *e,
@@ -61,21 +63,29 @@ int gqref_select_levels(int scheme, int d, int s, int L, int flags,
                         const float *g, const float *e, float *meta,
                         uint8_t *tie);
 
-/* xhat[i] = level value that code i stands for. */
-int gqref_dequantize(int scheme, int d, int s, int L, int64_t n,
+/* xhat[i] = level value that code i stands for (flags: the payload's flags,
+ * bit 1 = dense packing). */
+int gqref_dequantize(int scheme, int d, int s, int L, int flags, int64_t n,
                      const uint8_t *codes, const float *meta, float *xhat);
 
 /* e <- fl(fl(g + e) - xhat). */
-int gqref_error_feedback(int scheme, int d, int s, int L, int64_t n,
+int gqref_error_feedback(int scheme, int d, int s, int L, int flags, int64_t n,
                          const float *g, float *e,
                          const uint8_t *codes, const float *meta);
 
 /* out <- fl32(beta*out + alpha*sum_w xhat_w), evaluated in binary64 and
  * rounded once; beta == 0 means out is not read. */
-int gqref_dequantize_accumulate(int scheme, int d, int s, int L, int64_t n,
-                                int W, const uint8_t *const *codes,
+int gqref_dequantize_accumulate(int scheme, int d, int s, int L, int flags,
+                                int64_t n, int W, const uint8_t *const *codes,
                                 const float *const *meta, float alpha,
                                 float beta, float *out);
+
+/* Dense packing (flags bit 1): groups of 8 codes as one base-A integer,
+ * first code least significant, in fields of gqref_dense_width(A) =
+ * ceil(log2(A^8)) bits of the LSB-first stream; A <= 16. */
+int gqref_dense_width(int A);
+void gqref_pack_dense(int A, int64_t n, const uint32_t *digits, uint8_t *codes);
+void gqref_unpack_dense(int A, int64_t n, const uint8_t *codes, uint32_t *digits);
 
 /* Raw bitstream access, element i of a stream with `bits` bits per code. */
 void gqref_pack(int bits, int64_t n, const uint32_t *vals, uint8_t *codes);
