@@ -227,7 +227,8 @@ def entry(name, ms, nbytes, n, bound="hbm", extra=None):
 
 def suite(torch, gq, WL, stream, reps: int, only: str | None = None):
     """Every other workload's kernels, each timed back to back (only the
-    workloads whose name contains `only`: qsgd, orq, bingrad, workers)."""
+    workloads whose name contains `only`: qsgd, orq, bingrad, workers,
+    dense)."""
     out = []
     tb = lambda f, r=reps: time_back_to_back(torch, stream, f, r)  # noqa: E731
     want = lambda name: only is None or only in name  # noqa: E731
@@ -240,6 +241,58 @@ def suite(torch, gq, WL, stream, reps: int, only: str | None = None):
         out += suite_bingrad(torch, gq, WL, stream, tb, reps)
     if want("workers"):
         out += suite_workers(torch, gq, WL, stream, tb)
+    if want("dense"):
+        out += suite_dense(torch, gq, WL, stream, tb, reps)
+    return out
+
+
+def suite_dense(torch, gq, WL, stream, tb, reps):
+    """Dense packing (8 codes per base-A field): ternary + EF on the 25.6M
+    layered gradient and its dequantize, ORQ-3 / ORQ-9 on 100M."""
+    out = []
+    D = gq.GQ_FLAG_DENSE
+
+    def ratio(d, n):
+        cb, _, mf = gq.gq_payload_size(d, n)
+        return {"compression_vs_fp32": round(4 * n / (cb + 4 * mf), 3),
+                "code_bytes": cb}
+
+    host = WL.ternary_gradient(0)
+    g = torch.from_numpy(host).cuda()
+    n = g.numel()
+    e = torch.zeros_like(g)
+    d = gq.desc(gq.GQ_UNIFORM, 512, s=1, flags=D)
+    c, m = gq.alloc_payload(d, n)
+    q = gq.PreparedQuantize(d, g, e, c, m, stream)
+    ms = tb(lambda i: q(2, i))
+    cb = ratio(d, n)
+    out.append(entry(f"quantize ternary+ef dense d=512 n={n}", ms,
+                     12 * n + cb["code_bytes"] + 4 * ((n + 511) // 512), n,
+                     extra={**cb, **oracle_rate(host, dict(scheme=0, d=512, s=1,
+                                                           flags=2), True, seed=2)}))
+    o = torch.empty_like(g)
+    dq = gq.PreparedDequantizeAccumulate(d, n, [c], [m], 1.0, 0.0, o, stream)
+    ms = tb(lambda i: dq())
+    out.append(entry(f"dequantize ternary dense W=1 n={n}", ms,
+                     cb["code_bytes"] + 4 * ((n + 511) // 512) + 4 * n, n))
+    del g, e, c, m, q, o, dq, host
+
+    host = WL.orq_gradient()
+    g = torch.from_numpy(host).cuda()
+    n = g.numel()
+    for L in (3, 9):
+        d = gq.desc(gq.GQ_ORQ, 512, levels=L, flags=D)
+        c, m = gq.alloc_payload(d, n)
+        q = gq.PreparedQuantize(d, g, None, c, m, stream)
+        ms = tb(lambda i: q(3, 0), max(3, reps // 2))
+        cb = ratio(d, n)
+        out.append(entry(f"quantize orq L={L} dense d=512 n={n}", ms,
+                         4 * n + cb["code_bytes"] + 4 * L * ((n + 511) // 512),
+                         n, bound="alu",
+                         extra={**cb, **oracle_rate(host, dict(scheme=3, d=512,
+                                                               L=L, flags=2),
+                                                    False, seed=3)}))
+        del c, m, q
     return out
 
 
@@ -405,7 +458,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--suite", choices=("main", "all"), default="all")
     ap.add_argument("--reps", type=int, default=20)
-    ap.add_argument("--only", choices=("qsgd", "orq", "bingrad", "workers"),
+    ap.add_argument("--only", choices=("qsgd", "orq", "bingrad", "workers",
+                                       "dense"),
                     help="time only this workload's kernels after the headline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--counters", action="store_true",

@@ -32,7 +32,7 @@ int check_desc(const gq_desc* d, gq::LaunchDesc* L) {
   if (d == nullptr) return GQ_EINVAL;
   const int b = d->bucket;
   if (b < 64 || b > 32768 || (b & (b - 1)) != 0) return GQ_EINVAL;
-  if (d->flags & ~GQ_FLAG_CLIP) return GQ_EINVAL;
+  if (d->flags & ~(GQ_FLAG_CLIP | GQ_FLAG_DENSE)) return GQ_EINVAL;
   L->scheme = d->scheme;
   L->d = b;
   L->s = d->s;
@@ -64,10 +64,33 @@ int check_desc(const gq_desc* d, gq::LaunchDesc* L) {
     if (d->scheme != GQ_ORQ) return GQ_EUNSUPPORTED;
     if (!(d->clip_sigma > 0.f) || !std::isfinite(d->clip_sigma)) return GQ_EINVAL;
   }
+  L->dense = 0;
+  L->A = L->W = 0;
+  L->A4 = 0;
+  if (d->flags & GQ_FLAG_DENSE) {
+    const int A = d->scheme == GQ_UNIFORM ? 2 * d->s + 1
+                                          : (d->scheme == GQ_ORQ ? d->levels : 2);
+    if (A > 16) return GQ_EUNSUPPORTED;
+    if ((A & (A - 1)) != 0) {  // not a power of two: a different layout
+      if (d->scheme == GQ_ORQ && b < 512) return GQ_EUNSUPPORTED;
+      uint64_t p = 1;
+      for (int i = 0; i < 8; ++i) p *= (uint64_t)A;
+      int w = 0;
+      while (((uint64_t)1 << w) < p) ++w;
+      L->dense = 1;
+      L->A = A;
+      L->W = w;
+      L->A4 = (uint32_t)(A * A * A * A);
+      L->bits = w;  // reported by gq_code_bits as the 8-code field width
+    }
+  }
   return GQ_OK;
 }
 
-int64_t code_bytes_of(const gq::LaunchDesc& L, int64_t n) { return (n * L.bits + 7) / 8; }
+int64_t code_bytes_of(const gq::LaunchDesc& L, int64_t n) {
+  if (L.dense) return (((n + 7) / 8) * L.W + 7) / 8;
+  return (n * L.bits + 7) / 8;
+}
 int64_t meta_floats_of(const gq::LaunchDesc& L, int64_t n) {
   return ((n + L.d - 1) / L.d) * L.k;
 }

@@ -296,6 +296,79 @@ __device__ __forceinline__ void store_chunk(uint8_t* __restrict__ codes,
   }
 }
 
+// ------------------------------------------------------- dense packing --
+// The 64 lanes of a wave hold the 256 consecutive elements chunk0 ..
+// chunk0+255 (chunk0 a multiple of 256), lane l the elements chunk0 + 4l ..
+// +3, given as u = d0 + A d1 + A^2 d2 + A^3 d3 (d0 for the first element).
+// Lanes 2f and 2f+1 form field f = u_2f + A^4 u_2f+1 (< A^8 <= 2^32); the
+// chunk's 32 fields of W bits (13 <= W <= 32) fill exactly W stream words,
+// words c*W .. c*W + W-1 for chunk c, and lane L < W assembles word L from
+// the (at most four) fields that overlap it.  All 64 lanes must take part.
+// Words that start at or past code_bytes are skipped.
+__device__ __forceinline__ void store_dense_chunk(uint8_t* __restrict__ codes,
+                                                  int64_t chunk0, uint32_t u,
+                                                  uint32_t A4, int W,
+                                                  int64_t code_bytes) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t V = u + A4 * xshfl(u, 1);  // meaningful on even lanes
+  const int L = lane < W ? lane : 0;
+  const int f0 = (32 * L) / W;
+  uint32_t word = 0u;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int f = f0 + r;
+    const uint32_t vf = (uint32_t)__shfl((int)V, 2 * (f < 32 ? f : 31), 64);
+    const int off = W * f - 32 * L;  // bit of field f inside word L
+    if (f < 32 && off < 32) word |= off >= 0 ? (vf << off) : (vf >> (-off));
+  }
+  if (lane < W) {
+    const int64_t byte = (chunk0 >> 8) * 4 * (int64_t)W + 4 * lane;
+    if (byte < code_bytes) *reinterpret_cast<uint32_t*>(codes + byte) = word;
+  }
+}
+
+// v / q for v < 2^32 and 2 <= q <= 2^16, with rq = 1.0 / q: the fp64
+// product is within 2^-20 of the exact quotient, whose fractional part is a
+// multiple of 1/q >= 2^-16, so truncation is exact; the two integer checks
+// make that independent of the rounding of rq.
+__device__ __forceinline__ uint32_t udiv_small(uint32_t v, uint32_t q, double rq) {
+  uint32_t t = (uint32_t)((double)v * rq);
+  if ((uint64_t)t * q > v) --t;
+  else if ((uint64_t)(t + 1) * q <= v) ++t;
+  return t;
+}
+
+// The four digits (element 4f .. 4f+3) of float4 group f of a dense stream,
+// digit k in bits 8k .. 8k+7.  `full` groups have both stream words they
+// can touch inside code_bytes; otherwise bytes are read one by one.
+__device__ __forceinline__ uint32_t load_dense4(const uint8_t* __restrict__ c,
+                                                int64_t f, int W, uint32_t A,
+                                                uint32_t A4, double rA,
+                                                double rA4, int64_t code_bytes) {
+  const int64_t bit0 = (int64_t)W * (f >> 1);
+  const int64_t wi = bit0 >> 5;
+  uint64_t x;
+  if (4 * wi + 8 <= code_bytes) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(c);
+    x = (uint64_t)w[wi] | ((uint64_t)w[wi + 1] << 32);
+  } else {
+    x = 0;
+    for (int b = 0; b < 8; ++b)
+      if (4 * wi + b < code_bytes) x |= (uint64_t)c[4 * wi + b] << (8 * b);
+  }
+  uint32_t v = (uint32_t)(x >> (bit0 & 31));
+  if (W < 32) v &= (1u << W) - 1u;
+  if (f & 1) v = udiv_small(v, A4, rA4);
+  uint32_t out = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t q = udiv_small(v, A, rA);
+    out |= (v - q * A) << (8 * k);
+    v = q;
+  }
+  return out;
+}
+
 }  // namespace gq
 
 // ----------------------------------------------------- host launchers --
@@ -306,6 +379,10 @@ namespace gq {
 struct LaunchDesc {
   int scheme, d, s, L, flags, bits, k;
   float clip_sigma;
+  // dense packing (when it differs from the fixed-width layout): alphabet
+  // size A, A^4, and the field width W of 8 codes; dense = 0 otherwise
+  int dense, A, W;
+  uint32_t A4;
 };
 
 struct PayloadPtrs {

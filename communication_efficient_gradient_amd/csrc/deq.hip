@@ -52,6 +52,45 @@ __device__ __forceinline__ uint32_t load_codes4(const uint8_t* __restrict__ c,
   return BITS == 8 ? w : (w & ((1u << (4 * BITS)) - 1u));
 }
 
+// Dense packing (BITS = 0): field width, alphabet size, A^4 and their
+// reciprocals for the digit split.
+struct DenseCfg {
+  int W;
+  uint32_t A, A4;
+  double rA, rA4;
+};
+
+// The codes of group f: BITS-bit fields (element 4f in the low bits) or,
+// dense, four 8-bit digits (digit k in bits 8k .. 8k+7).
+template <int BITS>
+__device__ __forceinline__ uint32_t load_group(const uint8_t* __restrict__ c,
+                                               int64_t f, bool full,
+                                               int64_t code_bytes,
+                                               const DenseCfg& dc) {
+  if constexpr (BITS == 0)
+    return load_dense4(c, f, dc.W, dc.A, dc.A4, dc.rA, dc.rA4, code_bytes);
+  else
+    return load_codes4<BITS>(c, f, full, code_bytes);
+}
+
+// Code value k of a loaded group: the signed integer -s..s for the uniform
+// scheme (two's complement, or dense digit - s), the level index otherwise.
+template <int SCHEME, int BITS>
+__device__ __forceinline__ int code_value(uint32_t w, int k, int s) {
+  if constexpr (BITS == 0) {
+    const int digit = (int)((w >> (8 * k)) & 0xFFu);
+    return SCHEME == UNIFORM ? digit - s : digit;
+  } else {
+    const uint32_t u = (w >> (BITS * k)) & ((1u << BITS) - 1u);
+    if constexpr (SCHEME == UNIFORM) {
+      const uint32_t m = 1u << (BITS - 1);
+      return (int)((u ^ m) - m);  // sign-extend
+    } else {
+      return (int)u;
+    }
+  }
+}
+
 // Dequantized values of one group of one payload.
 template <int SCHEME, int BITS>
 __device__ __forceinline__ float4 dequant4(uint32_t w,
@@ -61,12 +100,7 @@ __device__ __forceinline__ float4 dequant4(uint32_t w,
   if constexpr (SCHEME == UNIFORM) {
     const float delta = meta[bucket] / (float)s;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t u = (w >> (BITS * k)) & ((1u << BITS) - 1u);
-      const uint32_t m = 1u << (BITS - 1);
-      const int ci = (int)((u ^ m) - m);  // sign-extend
-      x[k] = (float)ci * delta;
-    }
+    for (int k = 0; k < 4; ++k) x[k] = (float)code_value<SCHEME, BITS>(w, k, s) * delta;
   } else if constexpr (SCHEME == BIN_SIGN || SCHEME == BIN_OPT) {
     const float a = meta[2 * bucket + 0], b = meta[2 * bucket + 1];
 #pragma unroll
@@ -78,7 +112,7 @@ __device__ __forceinline__ float4 dequant4(uint32_t w,
     const uint32_t top = (uint32_t)(L - 1);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t c = (w >> (BITS * k)) & ((1u << BITS) - 1u);
+      const uint32_t c = (uint32_t)code_value<SCHEME, BITS>(w, k, s);
       x[k] = lv[c < top ? c : top];
     }
   }
@@ -92,7 +126,7 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) {
 template <int SCHEME, int BITS, int NB>
 __global__ __launch_bounds__(kThreads) void k_deq_acc(
     int64_t n, int d, int s, int L, int W, PayloadPtrs pp, float alpha,
-    float beta, float* __restrict__ out, int64_t code_bytes) {
+    float beta, float* __restrict__ out, int64_t code_bytes, DenseCfg dc) {
   // The block's tile is kGroupsPerBlock consecutive groups; pass v of the
   // block covers the kThreads groups [tile + kThreads v, tile + kThreads
   // (v + 1)), thread t taking group tile + kThreads v + t.
@@ -113,8 +147,8 @@ __global__ __launch_bounds__(kThreads) void k_deq_acc(
       for (int v = 0; v < kV; ++v) {
         const int64_t f = f0 + kStride * v;
         cw[j][v] = (p < W && f < ngroups)
-                       ? load_codes4<BITS>(pp.codes[p < W ? p : 0], f,
-                                           4 * f + 4 <= n, code_bytes)
+                       ? load_group<BITS>(pp.codes[p < W ? p : 0], f,
+                                          4 * f + 4 <= n, code_bytes, dc)
                        : 0u;
       }
     }
@@ -147,11 +181,8 @@ __global__ __launch_bounds__(kThreads) void k_deq_acc(
                                 : pp.meta[p][bucket] / (float)s;
       float x[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t u = (w >> (BITS * k)) & ((1u << BITS) - 1u);
-        const uint32_t m = 1u << (BITS - 1);
-        x[k] = (float)(int)((u ^ m) - m) * delta;  // sign-extended code
-      }
+      for (int k = 0; k < 4; ++k)
+        x[k] = (float)code_value<SCHEME, BITS>(w, k, s) * delta;
       return make_float4(x[0], x[1], x[2], x[3]);
     } else {
       return dequant4<SCHEME, BITS>(w, pp.meta[p], bucket, s, L);
@@ -219,7 +250,7 @@ template <int SCHEME, int BITS>
 __global__ __launch_bounds__(kThreads) void k_error_feedback(
     int64_t n, int d, int s, int L, const float* __restrict__ g,
     float* __restrict__ e, const uint8_t* __restrict__ codes,
-    const float* __restrict__ meta, int64_t code_bytes) {
+    const float* __restrict__ meta, int64_t code_bytes, DenseCfg dc) {
   const int64_t ngroups = (n + 3) >> 2;
   const int64_t f0 = (int64_t)blockIdx.x * kGroupsPerBlock + threadIdx.x;
 #pragma unroll
@@ -229,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void k_error_feedback(
     const int64_t i = 4 * f;
     const bool full = i + 4 <= n;
     const float4 x = dequant4<SCHEME, BITS>(
-        load_codes4<BITS>(codes, f, full, code_bytes), meta, i / d, s, L);
+        load_group<BITS>(codes, f, full, code_bytes, dc), meta, i / d, s, L);
     const float4 gv = load4(g, i, n);
     const float4 ev = load4(e, i, n);
     float4 r;
@@ -246,20 +277,30 @@ int64_t blocks_for(int64_t n) {
   return (ngroups + kGroupsPerBlock - 1) / kGroupsPerBlock;
 }
 
+DenseCfg dense_cfg(const LaunchDesc& L) {
+  DenseCfg dc{L.W, (uint32_t)L.A, L.A4, 0.0, 0.0};
+  if (L.dense) {
+    dc.rA = 1.0 / (double)L.A;
+    dc.rA4 = 1.0 / (double)L.A4;
+  }
+  return dc;
+}
+
 template <int SCHEME, int BITS>
 int deq_one(const LaunchDesc& L, int64_t n, int W, const PayloadPtrs& pp,
             float alpha, float beta, float* out, int64_t code_bytes,
             hipStream_t st) {
   const dim3 grid((uint32_t)blocks_for(n)), block(kThreads);
+  const DenseCfg dc = dense_cfg(L);
   if (W == 1)
     hipLaunchKernelGGL((k_deq_acc<SCHEME, BITS, 1>), grid, block, 0, st, n,
-                       L.d, L.s, L.L, W, pp, alpha, beta, out, code_bytes);
+                       L.d, L.s, L.L, W, pp, alpha, beta, out, code_bytes, dc);
   else if (W == 2)
     hipLaunchKernelGGL((k_deq_acc<SCHEME, BITS, 2>), grid, block, 0, st, n,
-                       L.d, L.s, L.L, W, pp, alpha, beta, out, code_bytes);
+                       L.d, L.s, L.L, W, pp, alpha, beta, out, code_bytes, dc);
   else
     hipLaunchKernelGGL((k_deq_acc<SCHEME, BITS, 4>), grid, block, 0, st, n,
-                       L.d, L.s, L.L, W, pp, alpha, beta, out, code_bytes);
+                       L.d, L.s, L.L, W, pp, alpha, beta, out, code_bytes, dc);
   return (int)hipGetLastError();
 }
 
@@ -269,12 +310,19 @@ int ef_one(const LaunchDesc& L, int64_t n, const float* g, float* e,
            hipStream_t st) {
   hipLaunchKernelGGL((k_error_feedback<SCHEME, BITS>),
                      dim3((uint32_t)blocks_for(n)), dim3(kThreads), 0, st, n,
-                     L.d, L.s, L.L, g, e, codes, meta, code_bytes);
+                     L.d, L.s, L.L, g, e, codes, meta, code_bytes,
+                     dense_cfg(L));
   return (int)hipGetLastError();
 }
 
-// Calls F<SCHEME, BITS>(args...) for the descriptor's (scheme, bits).
+// Calls F<SCHEME, BITS>(args...) for the descriptor's (scheme, bits);
+// BITS = 0 for dense packing.
 #define GQ_DISPATCH(FN, ...)                                        \
+  if (L.dense) {                                                    \
+    if (L.scheme == UNIFORM) return FN<UNIFORM, 0>(__VA_ARGS__);    \
+    if (L.scheme == ORQ) return FN<ORQ, 0>(__VA_ARGS__);            \
+    return (int)hipErrorInvalidValue;                               \
+  }                                                                 \
   switch (L.scheme) {                                               \
     case UNIFORM:                                                   \
       switch (L.bits) {                                             \

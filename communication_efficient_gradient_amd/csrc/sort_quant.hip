@@ -258,7 +258,8 @@ template <int SCHEME, int BITS, int D>
 __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
     int64_t n, const float* __restrict__ g, float* __restrict__ e,
     uint32_t k0, uint32_t k1, uint32_t step, int L, int clip, float clip_sigma,
-    uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes) {
+    uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes,
+    uint32_t A4, int W) {
   constexpr int T = SortCfg<D>::T;
   constexpr int E = SortCfg<D>::E;
   __shared__ float sorted[D];
@@ -577,7 +578,9 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
       w = philox4x32_10(k0, k1, (uint32_t)ctr, (uint32_t)(ctr >> 32), step, 0u);
     }
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-    uint32_t field = 0u;
+    uint32_t field = 0u;  // BITS-bit codes, or (dense) base-L digits
+    const uint32_t dplace[4] = {1u, (uint32_t)L, (uint32_t)(L * L),
+                                (uint32_t)(L * L * L)};
     float rr[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -613,10 +616,14 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
           if ((uint32_t)j == code) xh = lv[j];
       }
       if (i0 + c >= n) code = 0u;
-      field |= code << (BITS * c);
+      if constexpr (BITS == 0) field += code * dplace[c];
+      else field |= code << (BITS * c);
       rr[c] = px[c] - xh;
     }
-    store_chunk<BITS, 4>(codes, i0, lane, field, code_bytes);
+    if constexpr (BITS == 0)
+      store_dense_chunk(codes, i0 - 4 * lane, field, A4, W, code_bytes);
+    else
+      store_chunk<BITS, 4>(codes, i0, lane, field, code_bytes);
     if (e != nullptr && i0 < n) store4(e, i0, n, make_float4(rr[0], rr[1], rr[2], rr[3]));
   }
 }
@@ -731,7 +738,8 @@ template <int SCHEME, int BITS, int D>
 __global__ __launch_bounds__(kGroupThreads) void k_wave_sort_quant(
     int64_t n, int64_t nb, const float* __restrict__ g, float* __restrict__ e,
     uint32_t k0, uint32_t k1, uint32_t step, int L, int clip, float clip_sigma,
-    uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes) {
+    uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes,
+    uint32_t A4, int W) {
   constexpr int E = WaveCfg<D>::E;
   constexpr int G = WaveCfg<D>::G;
   constexpr int VEC = 4;
@@ -1054,7 +1062,9 @@ __global__ __launch_bounds__(kGroupThreads) void k_wave_sort_quant(
       const uint64_t ctr = (uint64_t)i0 >> 2;
       w = philox4x32_10(k0, k1, (uint32_t)ctr, (uint32_t)(ctr >> 32), step, 0u);
     }
-    uint32_t field = 0u;
+    uint32_t field = 0u;  // BITS-bit codes, or (dense) base-L digits
+    const uint32_t dplace[4] = {1u, (uint32_t)L, (uint32_t)(L * L),
+                                (uint32_t)(L * L * L)};
     float r[VEC];
 #pragma unroll
     for (int c = 0; c < VEC; ++c) {
@@ -1095,10 +1105,18 @@ __global__ __launch_bounds__(kGroupThreads) void k_wave_sort_quant(
           if ((uint32_t)j == code) xh = lv[j];
       }
       if (!real) code = 0u;
-      field |= code << (BITS * c);
+      if constexpr (BITS == 0) field += code * dplace[c];
+      else field |= code << (BITS * c);
       r[c] = p[m] - xh;
     }
-    store_chunk<BITS, VEC>(codes, i0, lane, field, code_bytes);
+    if constexpr (BITS == 0) {
+      // dense ORQ runs with d >= 512 only, so here a bucket is one wave
+      if constexpr (G == 64)
+        store_dense_chunk(codes, i0 - 4 * (threadIdx.x & 63), field, A4, W,
+                          code_bytes);
+    } else {
+      store_chunk<BITS, VEC>(codes, i0, lane, field, code_bytes);
+    }
     if (e != nullptr && i0 < n) store_vec<VEC>(e, i0, n, r);
   }
 }
@@ -1107,20 +1125,21 @@ template <int SCHEME, int BITS, int D>
 int launch_sort_one(int64_t n, const float* g, float* e, uint64_t seed,
                     uint32_t step, int L, int clip, float clip_sigma,
                     uint8_t* codes, float* meta, int64_t code_bytes,
-                    hipStream_t st) {
+                    uint32_t A4, int W, hipStream_t st) {
   const int64_t nb = (n + D - 1) / D;
+  if (BITS == 0 && D < 512) return (int)hipErrorInvalidValue;  // dense: d >= 512
   if constexpr (D <= 512) {
     constexpr int per_block = kGroupThreads / WaveCfg<D>::G;
     const int64_t blocks = (nb + per_block - 1) / per_block;
     hipLaunchKernelGGL((k_wave_sort_quant<SCHEME, BITS, D>), dim3((uint32_t)blocks),
                        dim3(kGroupThreads), 0, st, n, nb, g, e,
                        (uint32_t)seed, (uint32_t)(seed >> 32), step, L, clip,
-                       clip_sigma, codes, meta, code_bytes);
+                       clip_sigma, codes, meta, code_bytes, A4, W);
   } else {
     hipLaunchKernelGGL((k_sort_quant<SCHEME, BITS, D>), dim3((uint32_t)nb),
                        dim3(SortCfg<D>::T), 0, st, n, g, e, (uint32_t)seed,
                        (uint32_t)(seed >> 32), step, L, clip, clip_sigma, codes,
-                       meta, code_bytes);
+                       meta, code_bytes, A4, W);
   }
   return (int)hipGetLastError();
 }
@@ -1129,12 +1148,12 @@ template <int SCHEME, int BITS>
 int sort_dispatch_d(int d, int64_t n, const float* g, float* e, uint64_t seed,
                     uint32_t step, int L, int clip, float clip_sigma,
                     uint8_t* codes, float* meta, int64_t code_bytes,
-                    hipStream_t st) {
+                    uint32_t A4, int W, hipStream_t st) {
 #define GQ_SCASE(D_)                                                        \
   case D_:                                                                  \
     return launch_sort_one<SCHEME, BITS, D_>(n, g, e, seed, step, L, clip,  \
                                              clip_sigma, codes, meta,       \
-                                             code_bytes, st);
+                                             code_bytes, A4, W, st);
   switch (d) {
     GQ_SCASE(64)
     GQ_SCASE(128)
@@ -1160,23 +1179,25 @@ int launch_sort_quant(const LaunchDesc& L, int64_t n, const float* g, float* e,
   const int clip = (L.flags & 1) ? 1 : 0;
   if (L.scheme == BIN_OPT)
     return sort_dispatch_d<BIN_OPT, 1>(L.d, n, g, e, seed, step, 2, 0, 0.f,
-                                       codes, meta, code_bytes, st);
+                                       codes, meta, code_bytes, 0u, 0, st);
+#define GQ_ORQ(BITS)                                                          \
+  sort_dispatch_d<ORQ, BITS>(L.d, n, g, e, seed, step, L.L, clip,            \
+                             L.clip_sigma, codes, meta, code_bytes, L.A4, L.W, \
+                             st)
+  if (L.dense) return GQ_ORQ(0);
   switch (L.bits) {
     case 1:
-      return sort_dispatch_d<ORQ, 1>(L.d, n, g, e, seed, step, L.L, clip,
-                                     L.clip_sigma, codes, meta, code_bytes, st);
+      return GQ_ORQ(1);
     case 2:
-      return sort_dispatch_d<ORQ, 2>(L.d, n, g, e, seed, step, L.L, clip,
-                                     L.clip_sigma, codes, meta, code_bytes, st);
+      return GQ_ORQ(2);
     case 3:
-      return sort_dispatch_d<ORQ, 3>(L.d, n, g, e, seed, step, L.L, clip,
-                                     L.clip_sigma, codes, meta, code_bytes, st);
+      return GQ_ORQ(3);
     case 4:
-      return sort_dispatch_d<ORQ, 4>(L.d, n, g, e, seed, step, L.L, clip,
-                                     L.clip_sigma, codes, meta, code_bytes, st);
+      return GQ_ORQ(4);
     default:
       return (int)hipErrorInvalidValue;
   }
+#undef GQ_ORQ
 }
 
 }  // namespace gq

@@ -80,12 +80,18 @@ __device__ __forceinline__ void bucket_side_sums(double& sn, double& sp, int& nn
   }
 }
 
+// BITS = 0 selects dense packing (uniform scheme, A = 2s+1 <= 15 symbols):
+// see store_dense_chunk.  Every wave then holds aligned 256-element chunks
+// (per v, the wave's 64 lanes cover 256 consecutive elements), and groups
+// past the last bucket stay to the end: all their loads and stores are
+// bounds-checked, and the field assembly needs all 64 lanes.
 template <int SCHEME, int BITS, int G, int V>
 __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
     int64_t n, int64_t nb, const float* __restrict__ g, float* __restrict__ e,
     uint32_t k0, uint32_t k1, uint32_t step, int s, uint8_t* __restrict__ codes,
-    float* __restrict__ meta, int64_t code_bytes) {
+    float* __restrict__ meta, int64_t code_bytes, uint32_t A4, int W) {
   constexpr int D = 4 * G * V;
+  constexpr bool DENSE = BITS == 0;
   constexpr int NW = G > 64 ? G / 64 : 1;
   __shared__ float red_f[NW];
   __shared__ double red_d[2 * NW];
@@ -94,7 +100,7 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
   const int lane = threadIdx.x % G;
   const int64_t bucket =
       (int64_t)blockIdx.x * BlockCfg<G>::kGroups + threadIdx.x / G;
-  if (bucket >= nb) return;  // whole groups leave together
+  if (!DENSE && bucket >= nb) return;  // whole groups leave together
   const int64_t base = bucket * D;
 
   // ---- load p = g (+ e) ------------------------------------------------
@@ -149,7 +155,7 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
     lvl1 = np ? (float)(sp / (double)np) : 0.f;
   }
 
-  if (lane == 0) {
+  if (lane == 0 && bucket < nb) {
     if constexpr (SCHEME == UNIFORM) {
       meta[bucket] = lvl0;
     } else {
@@ -172,6 +178,7 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
   for (int v = 0; v < V; ++v) {
     const int64_t i = base + 4 * (lane + G * v);
     uint32_t c[4];
+    int sc[4] = {0, 0, 0, 0};  // signed codes (dense digits are sc + s)
     float4 xh;
     if constexpr (SCHEME == UNIFORM) {
       const uint64_t ctr = (uint64_t)i >> 2;
@@ -186,7 +193,8 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
         const float q = r - l;
         const int mag = (int)l + (u24(ws[k]) < q ? 1 : 0);
         const int ci = x < 0.f ? -mag : mag;
-        c[k] = (uint32_t)ci & ((1u << BITS) - 1u);
+        sc[k] = ci;
+        c[k] = DENSE ? 0u : ((uint32_t)ci & ((1u << BITS) - 1u));
         const float xk = (float)ci * delta;
         if (k == 0) xh.x = xk;
         if (k == 1) xh.y = xk;
@@ -210,8 +218,17 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       if (k >= nreal) c[k] = 0u;
-    store_field<BITS, G>(codes, i, lane, field4<BITS>(c[0], c[1], c[2], c[3]),
-                         code_bytes);
+    if constexpr (DENSE) {
+      const uint32_t A = 2u * (uint32_t)s + 1u;
+      uint32_t u = 0u;
+#pragma unroll
+      for (int k = 3; k >= 0; --k)
+        u = u * A + (k < nreal ? (uint32_t)(sc[k] + s) : 0u);
+      store_dense_chunk(codes, i - 4 * (threadIdx.x & 63), u, A4, W, code_bytes);
+    } else {
+      store_field<BITS, G>(codes, i, lane, field4<BITS>(c[0], c[1], c[2], c[3]),
+                           code_bytes);
+    }
     if (e != nullptr && i < n) {
       float4 r;
       r.x = p[v].x - xh.x;
@@ -226,25 +243,25 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
 template <int SCHEME, int BITS, int G, int V>
 int launch_one(int64_t n, const float* g, float* e, uint64_t seed,
                uint32_t step, int s, uint8_t* codes, float* meta,
-               int64_t code_bytes, hipStream_t st) {
+               int64_t code_bytes, uint32_t A4, int W, hipStream_t st) {
   constexpr int D = 4 * G * V;
   const int64_t nb = (n + D - 1) / D;
   const int64_t blocks = (nb + BlockCfg<G>::kGroups - 1) / BlockCfg<G>::kGroups;
   hipLaunchKernelGGL((k_stream_quant<SCHEME, BITS, G, V>), dim3((uint32_t)blocks),
                      dim3(BlockCfg<G>::kThreads), 0, st, n, nb, g, e,
                      (uint32_t)seed, (uint32_t)(seed >> 32), step, s, codes,
-                     meta, code_bytes);
+                     meta, code_bytes, A4, W);
   return (int)hipGetLastError();
 }
 
 template <int SCHEME, int BITS>
 int dispatch_d(int d, int64_t n, const float* g, float* e, uint64_t seed,
                uint32_t step, int s, uint8_t* codes, float* meta,
-               int64_t code_bytes, hipStream_t st) {
+               int64_t code_bytes, uint32_t A4, int W, hipStream_t st) {
 #define GQ_CASE(D_, G_, V_)                                                  \
   case D_:                                                                   \
     return launch_one<SCHEME, BITS, G_, V_>(n, g, e, seed, step, s, codes,   \
-                                            meta, code_bytes, st);
+                                            meta, code_bytes, A4, W, st);
   switch (d) {
     GQ_CASE(64, 16, 1)
     GQ_CASE(128, 32, 1)
@@ -267,25 +284,24 @@ int dispatch_d(int d, int64_t n, const float* g, float* e, uint64_t seed,
 int launch_stream_quant(const LaunchDesc& L, int64_t n, const float* g,
                         float* e, uint64_t seed, uint32_t step, uint8_t* codes,
                         float* meta, int64_t code_bytes, hipStream_t st) {
-  if (L.scheme == BIN_SIGN)
-    return dispatch_d<BIN_SIGN, 1>(L.d, n, g, e, seed, step, L.s, codes, meta,
-                                   code_bytes, st);
+#define GQ_D(SCHEME, BITS)                                                    \
+  dispatch_d<SCHEME, BITS>(L.d, n, g, e, seed, step, L.s, codes, meta,        \
+                           code_bytes, L.A4, L.W, st)
+  if (L.scheme == BIN_SIGN) return GQ_D(BIN_SIGN, 1);
+  if (L.dense) return GQ_D(UNIFORM, 0);
   switch (L.bits) {
     case 2:
-      return dispatch_d<UNIFORM, 2>(L.d, n, g, e, seed, step, L.s, codes, meta,
-                                    code_bytes, st);
+      return GQ_D(UNIFORM, 2);
     case 3:
-      return dispatch_d<UNIFORM, 3>(L.d, n, g, e, seed, step, L.s, codes, meta,
-                                    code_bytes, st);
+      return GQ_D(UNIFORM, 3);
     case 4:
-      return dispatch_d<UNIFORM, 4>(L.d, n, g, e, seed, step, L.s, codes, meta,
-                                    code_bytes, st);
+      return GQ_D(UNIFORM, 4);
     case 8:
-      return dispatch_d<UNIFORM, 8>(L.d, n, g, e, seed, step, L.s, codes, meta,
-                                    code_bytes, st);
+      return GQ_D(UNIFORM, 8);
     default:
       return (int)hipErrorInvalidValue;
   }
+#undef GQ_D
 }
 
 }  // namespace gq

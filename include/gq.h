@@ -18,6 +18,14 @@
  *   - Codes form one LSB-first bitstream: element i owns stream bits
  *     [b*i, b*i + b), stream bit t is bit (t mod 8) of byte t/8, code bit 0
  *     first.  Bytes past the last element's bits are written as zero.
+ *   - With GQ_FLAG_DENSE the stream holds fields of W bits instead: eight
+ *     consecutive codes form one base-A integer (A = 2s+1 symbols for
+ *     GQ_UNIFORM, digit c + s; A = L for GQ_ORQ, digit = level index), the
+ *     first code least significant, absent codes of a partial group 0, and
+ *     field g occupies stream bits [W*g, W*g + W), W = ceil(log2 A^8)
+ *     (ternary 13 bits per 8 codes, nine levels 26): the compression the
+ *     paper review quotes for ORQ-3 / ORQ-9 (20.2 / 10.1 x, the entropy
+ *     limit 32/log2 A) is reached to within 2.5 %.
  *   - meta is fp32 [nb][k]:  k = 1 (GQ_UNIFORM: the bucket's max-abs M),
  *     2 (GQ_BIN_*: lower level a, upper level b), L (GQ_ORQ: ascending levels).
  *
@@ -67,16 +75,22 @@ typedef enum {
   GQ_ORQ = 3
 } gq_scheme;
 
-/* GQ_ORQ only: clip every value of a bucket to +-clip_sigma * RMS(bucket)
- * before selecting levels and rounding (same section: clipping). */
-enum { GQ_FLAG_CLIP = 1 };
+/* GQ_FLAG_CLIP (GQ_ORQ only): clip every value of a bucket to
+ * +-clip_sigma * RMS(bucket) before selecting levels and rounding (same
+ * section: clipping).
+ * GQ_FLAG_DENSE: dense packing of the codes (see the layout above): for
+ * GQ_UNIFORM with s <= 7 and for GQ_ORQ with d >= 512 (GQ_EUNSUPPORTED
+ * otherwise).  For the two-level schemes and ORQ with L a power of two the
+ * dense layout is the fixed-width layout, and the flag changes nothing.
+ * Every call that reads or writes a payload must be given the same flag. */
+enum { GQ_FLAG_CLIP = 1, GQ_FLAG_DENSE = 2 };
 
 typedef struct {
   int32_t scheme;     /* gq_scheme                                          */
   int32_t bucket;     /* d: power of two, 64 <= d <= 32768                  */
   int32_t s;          /* GQ_UNIFORM: levels per sign, 1..127                 */
   int32_t levels;     /* GQ_ORQ: L total levels incl. min and max, 2..16     */
-  int32_t flags;      /* GQ_FLAG_* (others must be 0)                       */
+  int32_t flags;      /* GQ_FLAG_* bits (others must be 0)                  */
   float clip_sigma;   /* with GQ_FLAG_CLIP: > 0                             */
 } gq_desc;
 
@@ -92,10 +106,13 @@ enum {
 
 /* Bits per code: GQ_UNIFORM ceil(log2(2s+1)) rounded up to 2, 3, 4 or 8
  * (two's complement); GQ_BIN_* 1 (1 = upper level); GQ_ORQ ceil(log2 L)
- * (unsigned level index).  Host-only; never touches the GPU. */
+ * (unsigned level index).  With GQ_FLAG_DENSE (where it changes the
+ * layout): the width W of one 8-code field.  Host-only; never touches the
+ * GPU. */
 int gq_code_bits(const gq_desc* desc, int32_t* bits);
 
-/* Payload sizes for n elements: code_bytes = ceil(n*bits/8); code_capacity
+/* Payload sizes for n elements: code_bytes = ceil(n*bits/8) (dense:
+ * ceil(ceil(n/8)*W/8)); code_capacity
  * = code_bytes rounded up to a multiple of 16 (the size a codes buffer
  * written by gq_quantize must have); meta_floats = ceil(n/d) * k.
  * Any output pointer may be NULL.  Host-only. */

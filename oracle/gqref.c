@@ -96,6 +96,7 @@ void gqref_pack(int bits, int64_t n, const uint32_t *vals, uint8_t *codes) {
 }
 
 void gqref_unpack(int bits, int64_t n, const uint8_t *codes, uint32_t *vals) {
+#pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) vals[i] = get_code(codes, i, bits);
 }
 
@@ -157,6 +158,7 @@ static uint32_t dense_digit(const uint8_t *codes, int A, int w, int64_t i) {
 
 void gqref_unpack_dense(int A, int64_t n, const uint8_t *codes, uint32_t *digits) {
   int w = gqref_dense_width(A);
+#pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) digits[i] = dense_digit(codes, A, w, i);
 }
 

@@ -29,6 +29,8 @@ def say(*a):
 
 
 def bucket_code_bytes(desc: O.Desc) -> int:
+    if desc.dense:
+        return (desc.d // 8) * desc.field_bits // 8
     return desc.d * desc.bits // 8
 
 

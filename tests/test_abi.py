@@ -64,7 +64,8 @@ def test_payload_sizes(gq):
     (dict(bucket=63), -1), (dict(bucket=96), -1), (dict(bucket=65536), -1),
     (dict(bucket=32), -1), (dict(s=0), -2), (dict(s=128), -2),
     (dict(scheme=3, levels=1), -2), (dict(scheme=3, levels=17), -2),
-    (dict(scheme=7), -2), (dict(flags=2), -1), (dict(flags=1), -2),
+    (dict(scheme=7), -2), (dict(flags=4), -1), (dict(flags=1), -2),
+    (dict(s=8, flags=2), -2), (dict(scheme=3, bucket=256, flags=2), -2),
     (dict(scheme=3, flags=1, clip_sigma=0.0), -1),
     (dict(scheme=3, flags=1, clip_sigma=float("inf")), -1)])
 def test_bad_descriptors(gq, kw, status):
@@ -94,3 +95,34 @@ def test_validation_before_launch(gq):
     assert L.gq_dequantize_accumulate(C.byref(d), 100, 2, cp, mp, 1.0, 0.0, fake * 2, None) == -1
     assert L.gq_payload_size(C.byref(d), 0, None, None, None) == -1
     assert L.gq_code_bits(None, None) == -1
+
+
+def test_dense_flag_rules_and_sizes(gq):
+    import oracle as O
+    D = gq.GQ_FLAG_DENSE
+    # alphabets above 16 symbols, and ORQ below d = 512, are not supported
+    with pytest.raises(gq.GQError) as ex:
+        gq.gq_payload_size(gq.desc(gq.GQ_UNIFORM, 512, s=8, flags=D), 100)
+    assert ex.value.status == gq.GQ_EUNSUPPORTED
+    with pytest.raises(gq.GQError) as ex:
+        gq.gq_payload_size(gq.desc(gq.GQ_ORQ, 256, levels=9, flags=D), 100)
+    assert ex.value.status == gq.GQ_EUNSUPPORTED
+    with pytest.raises(gq.GQError) as ex:
+        gq.gq_payload_size(gq.desc(gq.GQ_UNIFORM, 512, s=1, flags=4), 100)
+    assert ex.value.status == gq.GQ_EINVAL
+    # sizes agree with the oracle's dense layout
+    for scheme, d, s, L in [(0, 64, 1, 5), (0, 512, 4, 5), (0, 4096, 7, 5),
+                            (3, 512, 4, 3), (3, 1024, 4, 9), (3, 32768, 4, 13)]:
+        od = O.Desc(scheme, d, s, L, flags=O.FLAG_DENSE)
+        for n in (1, 8, 9, 255, 256, 257, 100_000_000):
+            cb, cap, mf = gq.gq_payload_size(gq.desc(scheme, d, s, L, flags=D), n)
+            assert cb == od.code_bytes(n) and cap % 16 == 0 and cap >= cb
+            assert mf == od.nb(n) * od.k
+    # field widths: 13 bits per 8 ternary codes, 26 per 8 nine-level codes
+    assert gq.gq_code_bits(gq.desc(gq.GQ_UNIFORM, 512, s=1, flags=D)) == 13
+    assert gq.gq_code_bits(gq.desc(gq.GQ_ORQ, 512, levels=9, flags=D)) == 26
+    # power-of-two alphabets keep the fixed-width layout
+    for scheme, L in [(gq.GQ_BIN_OPT, 5), (gq.GQ_BIN_SIGN, 5), (gq.GQ_ORQ, 8)]:
+        a = gq.gq_payload_size(gq.desc(scheme, 128, levels=L, flags=D), 1000)
+        b = gq.gq_payload_size(gq.desc(scheme, 128, levels=L), 1000)
+        assert a == b

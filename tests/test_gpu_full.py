@@ -36,7 +36,11 @@ def gdesc(gq, d: O.Desc):
 
 
 def byte_range(d: O.Desc, lo: int, hi: int):
-    """Code bytes of elements [lo, hi) (lo is a bucket start)."""
+    """Code bytes of elements [lo, hi) (lo is a bucket start, and with dense
+    packing a multiple of 512, so the run starts on a byte)."""
+    if d.dense:
+        w = d.field_bits
+        return (lo // 8) * w // 8, (((hi + 7) // 8) * w + 7) // 8
     return lo * d.bits // 8, (hi * d.bits + 7) // 8
 
 
@@ -94,11 +98,12 @@ def test_qsgd_whole(dev):
     compare_values(out.cpu().numpy(), xr, np.abs(xr), exact=True)
 
 
-def test_ternary_ef_five_steps_whole(dev):
+@pytest.mark.parametrize("flags", [0, O.FLAG_DENSE])
+def test_ternary_ef_five_steps_whole(dev, flags):
     """All 25.6M elements, five steps; both sides carry their own residual
     (uniform residuals are bit-exact, so nothing can drift apart)."""
     gq, torch = dev
-    d = O.Desc(O.UNIFORM, 512, s=1)
+    d = O.Desc(O.UNIFORM, 512, s=1, flags=flags)
     n = WL.TERNARY_N
     E = torch.zeros(n, device="cuda")
     e_ref = np.zeros(n, dtype=np.float32)
@@ -122,7 +127,8 @@ def test_ternary_ef_five_steps_whole(dev):
                               xr.view(np.uint32)), f"dequantized, step {t}"
 
 
-@pytest.mark.parametrize("L,clip", [(5, 0), (5, 1), (9, 0), (9, 1)])
+@pytest.mark.parametrize("L,clip", [(5, 0), (5, 1), (9, 0), (9, 1),
+                                    (3, O.FLAG_DENSE), (9, O.FLAG_DENSE)])
 def test_orq_100m_sampled(dev, L, clip):
     gq, torch = dev
     d = O.Desc(O.ORQ, 512, L=L, flags=clip, clip_sigma=3.0)
@@ -137,7 +143,10 @@ def test_orq_100m_sampled(dev, L, clip):
     check_runs(d, n, lambda lo, hi: g[lo:hi], None, codes, meta, None, 3, 0,
                runs)
     # every code names a level of its bucket, on the whole payload
-    v = O.unpack(d.bits, n, codes.cpu().numpy())
+    if d.dense:
+        v = O.unpack_dense(L, n, codes.cpu().numpy())
+    else:
+        v = O.unpack(d.bits, n, codes.cpu().numpy())
     assert int(v.max()) < L
 
 
