@@ -327,24 +327,47 @@ __device__ __forceinline__ void store_dense_chunk(uint8_t* __restrict__ codes,
   }
 }
 
-// v / q for v < 2^32 and 2 <= q <= 2^16, with rq = 1.0 / q: the fp64
-// product is within 2^-20 of the exact quotient, whose fractional part is a
-// multiple of 1/q >= 2^-16, so truncation is exact; the two integer checks
-// make that independent of the rounding of rq.
-__device__ __forceinline__ uint32_t udiv_small(uint32_t v, uint32_t q, double rq) {
-  uint32_t t = (uint32_t)((double)v * rq);
-  if ((uint64_t)t * q > v) --t;
-  else if ((uint64_t)(t + 1) * q <= v) ++t;
-  return t;
+// Four 4-bit digits (first in the low nibble) as one base-A number,
+// first digit least significant.
+__device__ __forceinline__ uint32_t nibbles_to_base(uint32_t nib, uint32_t A) {
+  uint32_t u = (nib >> 12) & 0xFu;
+  u = __umul24(u, A) + ((nib >> 8) & 0xFu);
+  u = __umul24(u, A) + ((nib >> 4) & 0xFu);
+  return __umul24(u, A) + (nib & 0xFu);
 }
 
+// Digit split of a dense field without integer division.  For an integer
+// v and divisor q, floor(v / q) = floor((v + 1/2) / q), and the fractional
+// part of (v + 1/2) / q lies in [1/(2q), 1 - 1/(2q)].  The product
+// (v + 1/2) * fl(1/q), evaluated as one fused multiply-add, is within a
+// relative 2^-(p-1) of that quotient (p = 53 or 24 bits), so truncating it
+// is exact whenever quotient * 2^-(p-1) < 1/(2q):
+//   * fp64, v < 2^32, q = A^4 <= 2^16: error < 2^-20 against a margin of
+//     at least 2^-17;
+//   * fp32, v < 2^16, q = A <= 16: error < 2^-8 against at least 2^-5.
+// rq = fl(1/q) and hq = rq / 2 (exact) come from the host.
+__device__ __forceinline__ uint32_t div_field(uint32_t v, double rq, double hq) {
+  return (uint32_t)__fma_rn((double)v, rq, hq);
+}
+__device__ __forceinline__ uint32_t div_digit(uint32_t v, float rq, float hq) {
+  return (uint32_t)__fmaf_rn((float)v, rq, hq);
+}
+
+// Reciprocals for the digit split of a dense stream with alphabet A.
+struct DenseRecip {
+  double rA4, hA4;  // fl(1/A^4) and half of it
+  float rA, hA;     // fl(1/A) and half of it
+};
+
 // The four digits (element 4f .. 4f+3) of float4 group f of a dense stream,
-// digit k in bits 8k .. 8k+7.  `full` groups have both stream words they
-// can touch inside code_bytes; otherwise bytes are read one by one.
+// digit k in bits 8k .. 8k+7.  Group f is the low (f even) or high (f odd)
+// base-A^4 half of field f/2.  Groups whose two stream words lie inside
+// code_bytes load them whole; otherwise bytes are read one by one.
 __device__ __forceinline__ uint32_t load_dense4(const uint8_t* __restrict__ c,
                                                 int64_t f, int W, uint32_t A,
-                                                uint32_t A4, double rA,
-                                                double rA4, int64_t code_bytes) {
+                                                uint32_t A4,
+                                                const DenseRecip& r,
+                                                int64_t code_bytes) {
   const int64_t bit0 = (int64_t)W * (f >> 1);
   const int64_t wi = bit0 >> 5;
   uint64_t x;
@@ -358,15 +381,16 @@ __device__ __forceinline__ uint32_t load_dense4(const uint8_t* __restrict__ c,
   }
   uint32_t v = (uint32_t)(x >> (bit0 & 31));
   if (W < 32) v &= (1u << W) - 1u;
-  if (f & 1) v = udiv_small(v, A4, rA4);
+  const uint32_t hi = div_field(v, r.rA4, r.hA4);  // < A^4 <= 2^16
+  v = (f & 1) ? hi : v - __umul24(hi, A4);
   uint32_t out = 0;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t q = udiv_small(v, A, rA);
-    out |= (v - q * A) << (8 * k);
+  for (int k = 0; k < 3; ++k) {
+    const uint32_t q = div_digit(v, r.rA, r.hA);
+    out |= (v - __umul24(q, A)) << (8 * k);
     v = q;
   }
-  return out;
+  return out | (v << 24);
 }
 
 }  // namespace gq

@@ -21,7 +21,7 @@ namespace gq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kV = 4;                       // float4 groups per thread
+constexpr int kV = 2;                       // float4 groups per thread
 constexpr int kGroupsPerBlock = kThreads * kV;
 
 // The 4*BITS code bits of group f (elements 4f..4f+3), element 4f in the
@@ -52,12 +52,12 @@ __device__ __forceinline__ uint32_t load_codes4(const uint8_t* __restrict__ c,
   return BITS == 8 ? w : (w & ((1u << (4 * BITS)) - 1u));
 }
 
-// Dense packing (BITS = 0): field width, alphabet size, A^4 and their
+// Dense packing (BITS = 0): field width, alphabet size, A^4 and the
 // reciprocals for the digit split.
 struct DenseCfg {
   int W;
   uint32_t A, A4;
-  double rA, rA4;
+  DenseRecip r;
 };
 
 // The codes of group f: BITS-bit fields (element 4f in the low bits) or,
@@ -68,7 +68,7 @@ __device__ __forceinline__ uint32_t load_group(const uint8_t* __restrict__ c,
                                                int64_t code_bytes,
                                                const DenseCfg& dc) {
   if constexpr (BITS == 0)
-    return load_dense4(c, f, dc.W, dc.A, dc.A4, dc.rA, dc.rA4, code_bytes);
+    return load_dense4(c, f, dc.W, dc.A, dc.A4, dc.r, code_bytes);
   else
     return load_codes4<BITS>(c, f, full, code_bytes);
 }
@@ -125,7 +125,7 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) {
 
 template <int SCHEME, int BITS, int NB>
 __global__ __launch_bounds__(kThreads) void k_deq_acc(
-    int64_t n, int d, int s, int L, int W, PayloadPtrs pp, float alpha,
+    int64_t n, int dsh, int s, int L, int W, PayloadPtrs pp, float alpha,
     float beta, float* __restrict__ out, int64_t code_bytes, DenseCfg dc) {
   // The block's tile is kGroupsPerBlock consecutive groups; pass v of the
   // block covers the kThreads groups [tile + kThreads v, tile + kThreads
@@ -161,11 +161,11 @@ __global__ __launch_bounds__(kThreads) void k_deq_acc(
   // or two payloads each group divides for itself: the barrier would cost
   // more than the divisions it saves.
   __shared__ float delta_tab[TABLE ? kMaxPayloads * (kGroupsPerBlock * 4 / 64 + 1) : 1];
-  const int64_t b0 = (4 * tile) / d;
+  const int64_t b0 = (4 * tile) >> dsh;
   int nbk = 0;
   if constexpr (SCHEME == UNIFORM && TABLE) {
-    const int64_t last = (4 * (tile + kGroupsPerBlock) - 1) / d;
-    const int64_t nb = (n + d - 1) / d;
+    const int64_t last = (4 * (tile + kGroupsPerBlock) - 1) >> dsh;
+    const int64_t nb = (n + ((int64_t)1 << dsh) - 1) >> dsh;
     nbk = (int)(last - b0 + 1);
     for (int t = threadIdx.x; t < W * nbk; t += kThreads) {
       const int p = t / nbk, j = t % nbk;
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void k_deq_acc(
     __syncthreads();
   }
   auto deq = [&](uint32_t w, int p, int64_t f) -> float4 {
-    const int64_t bucket = (4 * f) / d;
+    const int64_t bucket = (4 * f) >> dsh;
     if constexpr (SCHEME == UNIFORM) {
       const float delta = TABLE ? delta_tab[p * nbk + (int)(bucket - b0)]
                                 : pp.meta[p][bucket] / (float)s;
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void k_deq_acc(
 
 template <int SCHEME, int BITS>
 __global__ __launch_bounds__(kThreads) void k_error_feedback(
-    int64_t n, int d, int s, int L, const float* __restrict__ g,
+    int64_t n, int dsh, int s, int L, const float* __restrict__ g,
     float* __restrict__ e, const uint8_t* __restrict__ codes,
     const float* __restrict__ meta, int64_t code_bytes, DenseCfg dc) {
   const int64_t ngroups = (n + 3) >> 2;
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void k_error_feedback(
     const int64_t i = 4 * f;
     const bool full = i + 4 <= n;
     const float4 x = dequant4<SCHEME, BITS>(
-        load_group<BITS>(codes, f, full, code_bytes, dc), meta, i / d, s, L);
+        load_group<BITS>(codes, f, full, code_bytes, dc), meta, i >> dsh, s, L);
     const float4 gv = load4(g, i, n);
     const float4 ev = load4(e, i, n);
     float4 r;
@@ -278,13 +278,18 @@ int64_t blocks_for(int64_t n) {
 }
 
 DenseCfg dense_cfg(const LaunchDesc& L) {
-  DenseCfg dc{L.W, (uint32_t)L.A, L.A4, 0.0, 0.0};
+  DenseCfg dc{L.W, (uint32_t)L.A, L.A4, {0.0, 0.0, 0.f, 0.f}};
   if (L.dense) {
-    dc.rA = 1.0 / (double)L.A;
-    dc.rA4 = 1.0 / (double)L.A4;
+    dc.r.rA4 = 1.0 / (double)L.A4;
+    dc.r.hA4 = 0.5 * dc.r.rA4;
+    dc.r.rA = 1.0f / (float)L.A;
+    dc.r.hA = 0.5f * dc.r.rA;
   }
   return dc;
 }
+
+// log2 of the bucket size (a power of two)
+int dshift(const LaunchDesc& L) { return __builtin_ctz((unsigned)L.d); }
 
 template <int SCHEME, int BITS>
 int deq_one(const LaunchDesc& L, int64_t n, int W, const PayloadPtrs& pp,
@@ -294,13 +299,13 @@ int deq_one(const LaunchDesc& L, int64_t n, int W, const PayloadPtrs& pp,
   const DenseCfg dc = dense_cfg(L);
   if (W == 1)
     hipLaunchKernelGGL((k_deq_acc<SCHEME, BITS, 1>), grid, block, 0, st, n,
-                       L.d, L.s, L.L, W, pp, alpha, beta, out, code_bytes, dc);
+                       dshift(L), L.s, L.L, W, pp, alpha, beta, out, code_bytes, dc);
   else if (W == 2)
     hipLaunchKernelGGL((k_deq_acc<SCHEME, BITS, 2>), grid, block, 0, st, n,
-                       L.d, L.s, L.L, W, pp, alpha, beta, out, code_bytes, dc);
+                       dshift(L), L.s, L.L, W, pp, alpha, beta, out, code_bytes, dc);
   else
     hipLaunchKernelGGL((k_deq_acc<SCHEME, BITS, 4>), grid, block, 0, st, n,
-                       L.d, L.s, L.L, W, pp, alpha, beta, out, code_bytes, dc);
+                       dshift(L), L.s, L.L, W, pp, alpha, beta, out, code_bytes, dc);
   return (int)hipGetLastError();
 }
 
@@ -310,7 +315,7 @@ int ef_one(const LaunchDesc& L, int64_t n, const float* g, float* e,
            hipStream_t st) {
   hipLaunchKernelGGL((k_error_feedback<SCHEME, BITS>),
                      dim3((uint32_t)blocks_for(n)), dim3(kThreads), 0, st, n,
-                     L.d, L.s, L.L, g, e, codes, meta, code_bytes,
+                     dshift(L), L.s, L.L, g, e, codes, meta, code_bytes,
                      dense_cfg(L));
   return (int)hipGetLastError();
 }

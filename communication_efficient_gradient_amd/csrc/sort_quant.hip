@@ -578,9 +578,9 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
       w = philox4x32_10(k0, k1, (uint32_t)ctr, (uint32_t)(ctr >> 32), step, 0u);
     }
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-    uint32_t field = 0u;  // BITS-bit codes, or (dense) base-L digits
-    const uint32_t dplace[4] = {1u, (uint32_t)L, (uint32_t)(L * L),
-                                (uint32_t)(L * L * L)};
+    // BITS-bit codes, or (dense) 4-bit digits turned into one base-L
+    // number at the store
+    uint32_t field = 0u;
     float rr[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -616,12 +616,12 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
           if ((uint32_t)j == code) xh = lv[j];
       }
       if (i0 + c >= n) code = 0u;
-      if constexpr (BITS == 0) field += code * dplace[c];
-      else field |= code << (BITS * c);
+      field |= code << ((BITS == 0 ? 4 : BITS) * c);
       rr[c] = px[c] - xh;
     }
     if constexpr (BITS == 0)
-      store_dense_chunk(codes, i0 - 4 * lane, field, A4, W, code_bytes);
+      store_dense_chunk(codes, i0 - 4 * lane, nibbles_to_base(field, L), A4, W,
+                        code_bytes);
     else
       store_chunk<BITS, 4>(codes, i0, lane, field, code_bytes);
     if (e != nullptr && i0 < n) store4(e, i0, n, make_float4(rr[0], rr[1], rr[2], rr[3]));
@@ -735,7 +735,8 @@ __device__ __forceinline__ void store_vec(float* __restrict__ a, int64_t i,
 }
 
 template <int SCHEME, int BITS, int D>
-__global__ __launch_bounds__(kGroupThreads) void k_wave_sort_quant(
+__global__ __launch_bounds__(kGroupThreads)
+void k_wave_sort_quant(
     int64_t n, int64_t nb, const float* __restrict__ g, float* __restrict__ e,
     uint32_t k0, uint32_t k1, uint32_t step, int L, int clip, float clip_sigma,
     uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes,
@@ -1054,6 +1055,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_wave_sort_quant(
       for (int c = 0; c < VEC; ++c) p[VEC * q + c] = x[c];
     }
   }
+  uint32_t dfield[BITS == 0 ? NQ : 1];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int64_t i0 = base + (int64_t)VEC * (lane + G * q);
@@ -1062,9 +1064,9 @@ __global__ __launch_bounds__(kGroupThreads) void k_wave_sort_quant(
       const uint64_t ctr = (uint64_t)i0 >> 2;
       w = philox4x32_10(k0, k1, (uint32_t)ctr, (uint32_t)(ctr >> 32), step, 0u);
     }
-    uint32_t field = 0u;  // BITS-bit codes, or (dense) base-L digits
-    const uint32_t dplace[4] = {1u, (uint32_t)L, (uint32_t)(L * L),
-                                (uint32_t)(L * L * L)};
+    // BITS-bit codes, or (dense) 4-bit digits turned into one base-L
+    // number at the store
+    uint32_t field = 0u;
     float r[VEC];
 #pragma unroll
     for (int c = 0; c < VEC; ++c) {
@@ -1105,19 +1107,20 @@ __global__ __launch_bounds__(kGroupThreads) void k_wave_sort_quant(
           if ((uint32_t)j == code) xh = lv[j];
       }
       if (!real) code = 0u;
-      if constexpr (BITS == 0) field += code * dplace[c];
-      else field |= code << (BITS * c);
+      field |= code << ((BITS == 0 ? 4 : BITS) * c);
       r[c] = p[m] - xh;
     }
-    if constexpr (BITS == 0) {
-      // dense ORQ runs with d >= 512 only, so here a bucket is one wave
-      if constexpr (G == 64)
-        store_dense_chunk(codes, i0 - 4 * (threadIdx.x & 63), field, A4, W,
-                          code_bytes);
-    } else {
-      store_chunk<BITS, VEC>(codes, i0, lane, field, code_bytes);
-    }
+    if constexpr (BITS == 0) dfield[q] = field;
+    else store_chunk<BITS, VEC>(codes, i0, lane, field, code_bytes);
     if (e != nullptr && i0 < n) store_vec<VEC>(e, i0, n, r);
+  }
+  // Dense fields are stored once the values and levels are dead.  Dense ORQ
+  // runs with d >= 512 only, so here a bucket is one wave.
+  if constexpr (BITS == 0 && G == 64) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      store_dense_chunk(codes, base + (int64_t)VEC * G * q,
+                        nibbles_to_base(dfield[q], L), A4, W, code_bytes);
   }
 }
 

@@ -223,7 +223,7 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
       uint32_t u = 0u;
 #pragma unroll
       for (int k = 3; k >= 0; --k)
-        u = u * A + (k < nreal ? (uint32_t)(sc[k] + s) : 0u);
+        u = __umul24(u, A) + (k < nreal ? (uint32_t)(sc[k] + s) : 0u);
       store_dense_chunk(codes, i - 4 * (threadIdx.x & 63), u, A4, W, code_bytes);
     } else {
       store_field<BITS, G>(codes, i, lane, field4<BITS>(c[0], c[1], c[2], c[3]),
