@@ -228,7 +228,7 @@ def entry(name, ms, nbytes, n, bound="hbm", extra=None):
 def suite(torch, gq, WL, stream, reps: int, only: str | None = None):
     """Every other workload's kernels, each timed back to back (only the
     workloads whose name contains `only`: qsgd, orq, bingrad, workers,
-    dense)."""
+    dense, nearest)."""
     out = []
     tb = lambda f, r=reps: time_back_to_back(torch, stream, f, r)  # noqa: E731
     want = lambda name: only is None or only in name  # noqa: E731
@@ -243,6 +243,35 @@ def suite(torch, gq, WL, stream, reps: int, only: str | None = None):
         out += suite_workers(torch, gq, WL, stream, tb)
     if want("dense"):
         out += suite_dense(torch, gq, WL, stream, tb, reps)
+    if want("nearest"):
+        out += suite_nearest(torch, gq, WL, stream, tb, reps)
+    return out
+
+
+def suite_nearest(torch, gq, WL, stream, tb, reps):
+    """Deterministic rounding to the nearest level: ternary + EF on the
+    25.6M layered gradient, ORQ-9 on 100M."""
+    out = []
+    N = gq.GQ_FLAG_NEAREST
+    host = WL.ternary_gradient(0)
+    g = torch.from_numpy(host).cuda()
+    n = g.numel()
+    e = torch.zeros_like(g)
+    d = gq.desc(gq.GQ_UNIFORM, 512, s=1, flags=N)
+    c, m = gq.alloc_payload(d, n)
+    q = gq.PreparedQuantize(d, g, e, c, m, stream)
+    ms = tb(lambda i: q(2, i))
+    out.append(entry(f"quantize ternary+ef nearest d=512 n={n}", ms,
+                     quant_bytes(2, 1, 512, n, True), n))
+    del g, e, c, m, q, host
+    g = torch.from_numpy(WL.orq_gradient()).cuda()
+    n = g.numel()
+    d = gq.desc(gq.GQ_ORQ, 512, levels=9, flags=N)
+    c, m = gq.alloc_payload(d, n)
+    q = gq.PreparedQuantize(d, g, None, c, m, stream)
+    ms = tb(lambda i: q(3, 0), max(3, reps // 2))
+    out.append(entry(f"quantize orq L=9 nearest d=512 n={n}", ms,
+                     quant_bytes(4, 9, 512, n, False), n, bound="alu"))
     return out
 
 
@@ -459,7 +488,7 @@ def main() -> int:
     ap.add_argument("--suite", choices=("main", "all"), default="all")
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--only", choices=("qsgd", "orq", "bingrad", "workers",
-                                       "dense"),
+                                       "dense", "nearest"),
                     help="time only this workload's kernels after the headline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--counters", action="store_true",

@@ -32,7 +32,7 @@ int check_desc(const gq_desc* d, gq::LaunchDesc* L) {
   if (d == nullptr) return GQ_EINVAL;
   const int b = d->bucket;
   if (b < 64 || b > 32768 || (b & (b - 1)) != 0) return GQ_EINVAL;
-  if (d->flags & ~(GQ_FLAG_CLIP | GQ_FLAG_DENSE)) return GQ_EINVAL;
+  if (d->flags & ~(GQ_FLAG_CLIP | GQ_FLAG_DENSE | GQ_FLAG_NEAREST)) return GQ_EINVAL;
   L->scheme = d->scheme;
   L->d = b;
   L->s = d->s;
@@ -64,6 +64,8 @@ int check_desc(const gq_desc* d, gq::LaunchDesc* L) {
     if (d->scheme != GQ_ORQ) return GQ_EUNSUPPORTED;
     if (!(d->clip_sigma > 0.f) || !std::isfinite(d->clip_sigma)) return GQ_EINVAL;
   }
+  if ((d->flags & GQ_FLAG_NEAREST) && d->scheme != GQ_UNIFORM && d->scheme != GQ_ORQ)
+    return GQ_EUNSUPPORTED;
   L->dense = 0;
   L->A = L->W = 0;
   L->A4 = 0;

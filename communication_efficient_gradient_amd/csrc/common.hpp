@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gq.h"
+
 namespace gq {
 
 enum Scheme { UNIFORM = 0, BIN_SIGN = 1, BIN_OPT = 2, ORQ = 3 };
@@ -46,6 +48,10 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t k0, uint32_t k1,
 __device__ __forceinline__ float u24(uint32_t w) {
   return (float)(w >> 8) * 0x1p-24f;
 }
+
+// A word whose u is exactly 1/2 (deterministic rounding to the nearest level:
+// up iff q > 1/2).
+constexpr uint32_t kHalfWord = 0x80000000u;
 
 // ------------------------------------------------------- lane exchange --
 // Value of lane (lane ^ o) for o = 1, 2, 4, .., 32 and for the mirror masks

@@ -257,7 +257,7 @@ struct SortShared {
 template <int SCHEME, int BITS, int D>
 __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
     int64_t n, const float* __restrict__ g, float* __restrict__ e,
-    uint32_t k0, uint32_t k1, uint32_t step, int L, int clip, float clip_sigma,
+    uint32_t k0, uint32_t k1, uint32_t step, int L, int flags, float clip_sigma,
     uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes,
     uint32_t A4, int W) {
   constexpr int T = SortCfg<D>::T;
@@ -293,6 +293,7 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
   auto epos = [&](int m) { return 4 * (tid + T * (m / 4)) + (m % 4); };
 
   // ---- 2. clip (ORQ) -----------------------------------------------------
+  const bool clip = (flags & GQ_FLAG_CLIP) != 0;
   float C = __builtin_inff();
   if (SCHEME == ORQ && clip) {
     Sum2 sq{0.0, 0.0};
@@ -574,8 +575,13 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
     const float px[4] = {pv.x, pv.y, pv.z, pv.w};
     uint4 w = make_uint4(0u, 0u, 0u, 0u);
     if constexpr (SCHEME == ORQ) {
-      const uint64_t ctr = (uint64_t)i0 >> 2;
-      w = philox4x32_10(k0, k1, (uint32_t)ctr, (uint32_t)(ctr >> 32), step, 0u);
+      // random words, or (nearest) words whose u is exactly 1/2: the value
+      // then rounds up iff q > 1/2
+      w = make_uint4(kHalfWord, kHalfWord, kHalfWord, kHalfWord);
+      if (!(flags & GQ_FLAG_NEAREST)) {
+        const uint64_t ctr = (uint64_t)i0 >> 2;
+        w = philox4x32_10(k0, k1, (uint32_t)ctr, (uint32_t)(ctr >> 32), step, 0u);
+      }
     }
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
     // BITS-bit codes, or (dense) 4-bit digits turned into one base-L
@@ -738,7 +744,7 @@ template <int SCHEME, int BITS, int D>
 __global__ __launch_bounds__(kGroupThreads)
 void k_wave_sort_quant(
     int64_t n, int64_t nb, const float* __restrict__ g, float* __restrict__ e,
-    uint32_t k0, uint32_t k1, uint32_t step, int L, int clip, float clip_sigma,
+    uint32_t k0, uint32_t k1, uint32_t step, int L, int flags, float clip_sigma,
     uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes,
     uint32_t A4, int W) {
   constexpr int E = WaveCfg<D>::E;
@@ -771,6 +777,7 @@ void k_wave_sort_quant(
   auto epos = [&](int m) { return VEC * (lane + G * (m / VEC)) + (m % VEC); };
 
   // ---- 2. clip (ORQ) -----------------------------------------------------
+  const bool clip = (flags & GQ_FLAG_CLIP) != 0;
   float C = __builtin_inff();
   if (SCHEME == ORQ && clip) {
     Sum2 sq{0.0, 0.0};
@@ -1061,8 +1068,13 @@ void k_wave_sort_quant(
     const int64_t i0 = base + (int64_t)VEC * (lane + G * q);
     uint4 w = make_uint4(0u, 0u, 0u, 0u);
     if constexpr (SCHEME == ORQ) {
-      const uint64_t ctr = (uint64_t)i0 >> 2;
-      w = philox4x32_10(k0, k1, (uint32_t)ctr, (uint32_t)(ctr >> 32), step, 0u);
+      // random words, or (nearest) words whose u is exactly 1/2: the value
+      // then rounds up iff q > 1/2
+      w = make_uint4(kHalfWord, kHalfWord, kHalfWord, kHalfWord);
+      if (!(flags & GQ_FLAG_NEAREST)) {
+        const uint64_t ctr = (uint64_t)i0 >> 2;
+        w = philox4x32_10(k0, k1, (uint32_t)ctr, (uint32_t)(ctr >> 32), step, 0u);
+      }
     }
     // BITS-bit codes, or (dense) 4-bit digits turned into one base-L
     // number at the store
@@ -1126,7 +1138,7 @@ void k_wave_sort_quant(
 
 template <int SCHEME, int BITS, int D>
 int launch_sort_one(int64_t n, const float* g, float* e, uint64_t seed,
-                    uint32_t step, int L, int clip, float clip_sigma,
+                    uint32_t step, int L, int flags, float clip_sigma,
                     uint8_t* codes, float* meta, int64_t code_bytes,
                     uint32_t A4, int W, hipStream_t st) {
   const int64_t nb = (n + D - 1) / D;
@@ -1136,12 +1148,12 @@ int launch_sort_one(int64_t n, const float* g, float* e, uint64_t seed,
     const int64_t blocks = (nb + per_block - 1) / per_block;
     hipLaunchKernelGGL((k_wave_sort_quant<SCHEME, BITS, D>), dim3((uint32_t)blocks),
                        dim3(kGroupThreads), 0, st, n, nb, g, e,
-                       (uint32_t)seed, (uint32_t)(seed >> 32), step, L, clip,
+                       (uint32_t)seed, (uint32_t)(seed >> 32), step, L, flags,
                        clip_sigma, codes, meta, code_bytes, A4, W);
   } else {
     hipLaunchKernelGGL((k_sort_quant<SCHEME, BITS, D>), dim3((uint32_t)nb),
                        dim3(SortCfg<D>::T), 0, st, n, g, e, (uint32_t)seed,
-                       (uint32_t)(seed >> 32), step, L, clip, clip_sigma, codes,
+                       (uint32_t)(seed >> 32), step, L, flags, clip_sigma, codes,
                        meta, code_bytes, A4, W);
   }
   return (int)hipGetLastError();
@@ -1149,12 +1161,12 @@ int launch_sort_one(int64_t n, const float* g, float* e, uint64_t seed,
 
 template <int SCHEME, int BITS>
 int sort_dispatch_d(int d, int64_t n, const float* g, float* e, uint64_t seed,
-                    uint32_t step, int L, int clip, float clip_sigma,
+                    uint32_t step, int L, int flags, float clip_sigma,
                     uint8_t* codes, float* meta, int64_t code_bytes,
                     uint32_t A4, int W, hipStream_t st) {
 #define GQ_SCASE(D_)                                                        \
   case D_:                                                                  \
-    return launch_sort_one<SCHEME, BITS, D_>(n, g, e, seed, step, L, clip,  \
+    return launch_sort_one<SCHEME, BITS, D_>(n, g, e, seed, step, L, flags, \
                                              clip_sigma, codes, meta,       \
                                              code_bytes, A4, W, st);
   switch (d) {
@@ -1179,12 +1191,12 @@ int sort_dispatch_d(int d, int64_t n, const float* g, float* e, uint64_t seed,
 int launch_sort_quant(const LaunchDesc& L, int64_t n, const float* g, float* e,
                       uint64_t seed, uint32_t step, uint8_t* codes, float* meta,
                       int64_t code_bytes, hipStream_t st) {
-  const int clip = (L.flags & 1) ? 1 : 0;
+  const int flags = L.flags & (GQ_FLAG_CLIP | GQ_FLAG_NEAREST);
   if (L.scheme == BIN_OPT)
     return sort_dispatch_d<BIN_OPT, 1>(L.d, n, g, e, seed, step, 2, 0, 0.f,
                                        codes, meta, code_bytes, 0u, 0, st);
 #define GQ_ORQ(BITS)                                                          \
-  sort_dispatch_d<ORQ, BITS>(L.d, n, g, e, seed, step, L.L, clip,            \
+  sort_dispatch_d<ORQ, BITS>(L.d, n, g, e, seed, step, L.L, flags,            \
                              L.clip_sigma, codes, meta, code_bytes, L.A4, L.W, \
                              st)
   if (L.dense) return GQ_ORQ(0);

@@ -88,8 +88,9 @@ __device__ __forceinline__ void bucket_side_sums(double& sn, double& sp, int& nn
 template <int SCHEME, int BITS, int G, int V>
 __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
     int64_t n, int64_t nb, const float* __restrict__ g, float* __restrict__ e,
-    uint32_t k0, uint32_t k1, uint32_t step, int s, uint8_t* __restrict__ codes,
-    float* __restrict__ meta, int64_t code_bytes, uint32_t A4, int W) {
+    uint32_t k0, uint32_t k1, uint32_t step, int s, int nearest,
+    uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes,
+    uint32_t A4, int W) {
   constexpr int D = 4 * G * V;
   constexpr bool DENSE = BITS == 0;
   constexpr int NW = G > 64 ? G / 64 : 1;
@@ -181,9 +182,13 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
     int sc[4] = {0, 0, 0, 0};  // signed codes (dense digits are sc + s)
     float4 xh;
     if constexpr (SCHEME == UNIFORM) {
-      const uint64_t ctr = (uint64_t)i >> 2;
-      const uint4 w = philox4x32_10(k0, k1, (uint32_t)ctr,
-                                    (uint32_t)(ctr >> 32), step, 0u);
+      // random words, or (nearest) words whose u is exactly 1/2, so that the
+      // value rounds up iff q > 1/2
+      uint4 w = make_uint4(kHalfWord, kHalfWord, kHalfWord, kHalfWord);
+      if (!nearest) {
+        const uint64_t ctr = (uint64_t)i >> 2;
+        w = philox4x32_10(k0, k1, (uint32_t)ctr, (uint32_t)(ctr >> 32), step, 0u);
+      }
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -242,26 +247,27 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
 
 template <int SCHEME, int BITS, int G, int V>
 int launch_one(int64_t n, const float* g, float* e, uint64_t seed,
-               uint32_t step, int s, uint8_t* codes, float* meta,
+               uint32_t step, int s, int nearest, uint8_t* codes, float* meta,
                int64_t code_bytes, uint32_t A4, int W, hipStream_t st) {
   constexpr int D = 4 * G * V;
   const int64_t nb = (n + D - 1) / D;
   const int64_t blocks = (nb + BlockCfg<G>::kGroups - 1) / BlockCfg<G>::kGroups;
   hipLaunchKernelGGL((k_stream_quant<SCHEME, BITS, G, V>), dim3((uint32_t)blocks),
                      dim3(BlockCfg<G>::kThreads), 0, st, n, nb, g, e,
-                     (uint32_t)seed, (uint32_t)(seed >> 32), step, s, codes,
-                     meta, code_bytes, A4, W);
+                     (uint32_t)seed, (uint32_t)(seed >> 32), step, s, nearest,
+                     codes, meta, code_bytes, A4, W);
   return (int)hipGetLastError();
 }
 
 template <int SCHEME, int BITS>
 int dispatch_d(int d, int64_t n, const float* g, float* e, uint64_t seed,
-               uint32_t step, int s, uint8_t* codes, float* meta,
+               uint32_t step, int s, int nearest, uint8_t* codes, float* meta,
                int64_t code_bytes, uint32_t A4, int W, hipStream_t st) {
 #define GQ_CASE(D_, G_, V_)                                                  \
   case D_:                                                                   \
-    return launch_one<SCHEME, BITS, G_, V_>(n, g, e, seed, step, s, codes,   \
-                                            meta, code_bytes, A4, W, st);
+    return launch_one<SCHEME, BITS, G_, V_>(n, g, e, seed, step, s, nearest, \
+                                            codes, meta, code_bytes, A4, W,  \
+                                            st);
   switch (d) {
     GQ_CASE(64, 16, 1)
     GQ_CASE(128, 32, 1)
@@ -285,7 +291,8 @@ int launch_stream_quant(const LaunchDesc& L, int64_t n, const float* g,
                         float* e, uint64_t seed, uint32_t step, uint8_t* codes,
                         float* meta, int64_t code_bytes, hipStream_t st) {
 #define GQ_D(SCHEME, BITS)                                                    \
-  dispatch_d<SCHEME, BITS>(L.d, n, g, e, seed, step, L.s, codes, meta,        \
+  dispatch_d<SCHEME, BITS>(L.d, n, g, e, seed, step, L.s,                     \
+                           (L.flags & GQ_FLAG_NEAREST) ? 1 : 0, codes, meta,  \
                            code_bytes, L.A4, L.W, st)
   if (L.scheme == BIN_SIGN) return GQ_D(BIN_SIGN, 1);
   if (L.dense) return GQ_D(UNIFORM, 0);

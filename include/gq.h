@@ -82,8 +82,17 @@ typedef enum {
  * GQ_UNIFORM with s <= 7 and for GQ_ORQ with d >= 512 (GQ_EUNSUPPORTED
  * otherwise).  For the two-level schemes and ORQ with L a power of two the
  * dense layout is the fixed-width layout, and the flag changes nothing.
- * Every call that reads or writes a payload must be given the same flag. */
-enum { GQ_FLAG_CLIP = 1, GQ_FLAG_DENSE = 2 };
+ * Every call that reads or writes a payload must be given the same flag.
+ * GQ_FLAG_NEAREST (GQ_UNIFORM and GQ_ORQ): deterministic rounding to the
+ * nearest level instead of random rounding ("Gradient Quantization"
+ * glossary, Deterministic Quantization bullet): with q the value's
+ * fractional position between its two adjacent levels, it rounds up iff
+ * q > 1/2 (a value exactly halfway takes the lower level, i.e. the smaller
+ * magnitude for GQ_UNIFORM).  This is the random rule with u = 1/2 for every
+ * element; seed and step are ignored.  The two-level schemes are already
+ * deterministic and return GQ_EUNSUPPORTED for it.  Payloads are read the
+ * same way with or without the flag. */
+enum { GQ_FLAG_CLIP = 1, GQ_FLAG_DENSE = 2, GQ_FLAG_NEAREST = 4 };
 
 typedef struct {
   int32_t scheme;     /* gq_scheme                                          */
@@ -126,7 +135,8 @@ int gq_select_levels(const gq_desc* desc, int64_t n, const float* g,
 
 /* Quantize n elements: p = g (+ e), levels per bucket, random rounding
  * (round up iff u < q, u from Philox4x32-10 with key = seed and counter =
- * (i/4, step); element i uses word i mod 4, u = (word >> 8) * 2^-24), pack.
+ * (i/4, step); element i uses word i mod 4, u = (word >> 8) * 2^-24; with
+ * GQ_FLAG_NEAREST u = 1/2), pack.
  * With e != NULL, e is read and then overwritten in place with the residual
  * p - dequant(code) (unclipped p).  codes: code_capacity bytes.  e must not
  * overlap g, codes or meta. */

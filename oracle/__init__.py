@@ -33,6 +33,7 @@ from . import build as _build
 UNIFORM, BIN_SIGN, BIN_OPT, ORQ = 0, 1, 2, 3
 FLAG_CLIP = 1
 FLAG_DENSE = 2
+FLAG_NEAREST = 4
 
 _lib = None
 

@@ -443,6 +443,7 @@ typedef struct {
   int scheme, d, s, L, flags, bits, k;
   float clip_sigma;
   int dense, A, w; /* dense packing: alphabet size and field width */
+  int nearest;     /* deterministic rounding to the nearest level */
 } params;
 
 /* Select the bucket's levels from its effective values p; for ORQ also
@@ -506,6 +507,16 @@ static int32_t read_code(const params *pr, const uint8_t *codes, int64_t i) {
   return pr->scheme == UNIFORM ? sext(raw, pr->bits) : (int32_t)raw;
 }
 
+/* Whether a value a fraction q of the way from its lower to its upper level
+ * takes the upper one.  Random rounding: iff u < q, so with probability q
+ * ("Gradient Quantization" glossary, Stochastic Quantization bullet).
+ * Deterministic rounding (flags bit 2; same glossary, Deterministic
+ * Quantization bullet: the nearest level): iff q > 1/2, an exact tie going
+ * to the lower level. */
+static int round_up(const params *pr, float q, float u) {
+  return pr->nearest ? q > 0.5f : u < q;
+}
+
 /* Code for one element: random rounding between the two adjacent levels
  * ("Gradient Quantization" glossary, Stochastic Quantization bullet: a value
  * a fraction q of the way from the lower to the upper level rounds up with
@@ -520,7 +531,7 @@ static int32_t code_uniform(const params *pr, float p, float M, float u) {
   if (r > (float)pr->s) r = (float)pr->s;
   float l = floorf(r);
   float q = r - l;
-  int32_t mag = (int32_t)l + (u < q ? 1 : 0);
+  int32_t mag = (int32_t)l + (round_up(pr, q, u) ? 1 : 0);
   return (p < 0.0f) ? -mag : mag;
 }
 
@@ -535,7 +546,7 @@ static uint32_t code_orq(const params *pr, float pcl, const float *lev,
   float num = pcl - lev[j];
   float den = lev[j + 1] - lev[j];
   float q = num / den;
-  return (uint32_t)(j + (u < q ? 1 : 0));
+  return (uint32_t)(j + (round_up(pr, q, u) ? 1 : 0));
 }
 
 static void quantize_bucket(const params *pr, int64_t gi, const float *g,
@@ -555,7 +566,8 @@ static void quantize_bucket(const params *pr, int64_t gi, const float *g,
     int32_t c;
     switch (pr->scheme) {
       case UNIFORM:
-        c = code_uniform(pr, p[t], meta[0], uniform_u(seed, step, gi + t));
+        c = code_uniform(pr, p[t], meta[0],
+                         pr->nearest ? 0.0f : uniform_u(seed, step, gi + t));
         break;
       case BIN_SIGN:
         c = p[t] >= 0.0f ? 1 : 0;
@@ -564,7 +576,8 @@ static void quantize_bucket(const params *pr, int64_t gi, const float *g,
         c = no_split ? 0 : (p[t] >= thr ? 1 : 0);
         break;
       default:
-        c = (int32_t)code_orq(pr, pc[t], meta, uniform_u(seed, step, gi + t));
+        c = (int32_t)code_orq(pr, pc[t], meta,
+                              pr->nearest ? 0.0f : uniform_u(seed, step, gi + t));
         break;
     }
     cv[t] = c;
@@ -604,6 +617,8 @@ static int make_params(params *pr, int scheme, int d, int s, int L, int flags,
   pr->k = gqref_meta_per_bucket(scheme, L);
   if (pr->bits < 0 || pr->k < 0) return -1;
   pr->dense = (flags & 2) ? 1 : 0;
+  pr->nearest = (flags & 4) ? 1 : 0;
+  if (pr->nearest && scheme != UNIFORM && scheme != ORQ) return -1;
   pr->A = scheme == UNIFORM ? 2 * s + 1 : (scheme == ORQ ? L : 2);
   pr->w = pr->dense ? gqref_dense_width(pr->A) : 0;
   if (pr->dense && pr->w < 0) return -1;

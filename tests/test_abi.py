@@ -64,7 +64,8 @@ def test_payload_sizes(gq):
     (dict(bucket=63), -1), (dict(bucket=96), -1), (dict(bucket=65536), -1),
     (dict(bucket=32), -1), (dict(s=0), -2), (dict(s=128), -2),
     (dict(scheme=3, levels=1), -2), (dict(scheme=3, levels=17), -2),
-    (dict(scheme=7), -2), (dict(flags=4), -1), (dict(flags=1), -2),
+    (dict(scheme=7), -2), (dict(flags=8), -1), (dict(flags=1), -2),
+    (dict(scheme=1, flags=4), -2), (dict(scheme=2, flags=4), -2),
     (dict(s=8, flags=2), -2), (dict(scheme=3, bucket=256, flags=2), -2),
     (dict(scheme=3, flags=1, clip_sigma=0.0), -1),
     (dict(scheme=3, flags=1, clip_sigma=float("inf")), -1)])
@@ -108,7 +109,7 @@ def test_dense_flag_rules_and_sizes(gq):
         gq.gq_payload_size(gq.desc(gq.GQ_ORQ, 256, levels=9, flags=D), 100)
     assert ex.value.status == gq.GQ_EUNSUPPORTED
     with pytest.raises(gq.GQError) as ex:
-        gq.gq_payload_size(gq.desc(gq.GQ_UNIFORM, 512, s=1, flags=4), 100)
+        gq.gq_payload_size(gq.desc(gq.GQ_UNIFORM, 512, s=1, flags=8), 100)
     assert ex.value.status == gq.GQ_EINVAL
     # sizes agree with the oracle's dense layout
     for scheme, d, s, L in [(0, 64, 1, 5), (0, 512, 4, 5), (0, 4096, 7, 5),
@@ -126,3 +127,23 @@ def test_dense_flag_rules_and_sizes(gq):
         a = gq.gq_payload_size(gq.desc(scheme, 128, levels=L, flags=D), 1000)
         b = gq.gq_payload_size(gq.desc(scheme, 128, levels=L), 1000)
         assert a == b
+
+
+def test_nearest_flag_rules(gq):
+    """Deterministic rounding: uniform and ORQ only, with any other flag;
+    it never changes the payload layout."""
+    N = gq.GQ_FLAG_NEAREST
+    assert N == 4
+    for scheme, d, s, L, f in [(0, 512, 1, 5, 0), (0, 64, 127, 5, 0),
+                               (0, 512, 4, 5, gq.GQ_FLAG_DENSE),
+                               (3, 512, 4, 9, gq.GQ_FLAG_CLIP),
+                               (3, 1024, 4, 5, gq.GQ_FLAG_DENSE)]:
+        a = gq.gq_payload_size(gq.desc(scheme, d, s, L, flags=f | N), 12345)
+        b = gq.gq_payload_size(gq.desc(scheme, d, s, L, flags=f), 12345)
+        assert a == b
+        assert gq.gq_code_bits(gq.desc(scheme, d, s, L, flags=f | N)) == \
+            gq.gq_code_bits(gq.desc(scheme, d, s, L, flags=f))
+    for scheme in (gq.GQ_BIN_SIGN, gq.GQ_BIN_OPT):
+        with pytest.raises(gq.GQError) as ex:
+            gq.gq_payload_size(gq.desc(scheme, 512, flags=N), 100)
+        assert ex.value.status == gq.GQ_EUNSUPPORTED

@@ -68,7 +68,7 @@ def check_quantize(dev, d: O.Desc, g, e, seed=1, step=0):
     bad = compare_codes(d, n, gc, rc, tie, exact=exact)
     if d.scheme == O.UNIFORM:
         compare_meta(d, gm, rm, exact=True)
-    elif d.scheme == O.ORQ and not d.flags:
+    elif d.scheme == O.ORQ and not d.flags & O.FLAG_CLIP:
         compare_meta(d, gm, rm, skip=bad, exact=False)
         keep = np.ones(rm.shape[0], bool)
         keep[bad] = False
