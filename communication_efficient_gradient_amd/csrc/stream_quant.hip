@@ -105,19 +105,59 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
   const int64_t base = bucket * D;
 
   // ---- load p = g (+ e) ------------------------------------------------
-  float4 p[V];
+  // Random words for the uniform scheme, or (nearest) words whose u is
+  // exactly 1/2, so that a value rounds up iff q > 1/2.  They depend on the
+  // element index only and are drawn while the loads are in flight.
+  uint4 wr[SCHEME == UNIFORM ? V : 1];
+  auto draw = [&]() {
+    if constexpr (SCHEME == UNIFORM) {
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int64_t i = base + 4 * (lane + G * v);
-    float4 x = load4(g, i, n);
-    if (e != nullptr) {
-      const float4 r = load4(e, i, n);
-      x.x = x.x + r.x;
-      x.y = x.y + r.y;
-      x.z = x.z + r.z;
-      x.w = x.w + r.w;
+      for (int v = 0; v < V; ++v) {
+        wr[v] = make_uint4(kHalfWord, kHalfWord, kHalfWord, kHalfWord);
+        if (!nearest && codes != nullptr) {
+          const uint64_t ctr = (uint64_t)(base + 4 * (lane + G * v)) >> 2;
+          wr[v] = philox4x32_10(k0, k1, (uint32_t)ctr, (uint32_t)(ctr >> 32),
+                                step, 0u);
+        }
+      }
     }
-    p[v] = x;
+  };
+  float4 p[V], r[V];
+  auto add_residual = [&]() {
+    if (e != nullptr) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        p[v].x = p[v].x + r[v].x;
+        p[v].y = p[v].y + r[v].y;
+        p[v].z = p[v].z + r[v].z;
+        p[v].w = p[v].w + r[v].w;
+      }
+    }
+  };
+  // A bucket wholly inside the gradient (every bucket but possibly the
+  // last; the test is uniform over the group) loads with plain 128-bit
+  // loads, all issued before any use; the last bucket checks each element.
+  const bool whole = base + D <= n;
+  if (whole) {
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      p[v] = *reinterpret_cast<const float4*>(g + base + 4 * (lane + G * v));
+    if (e != nullptr) {
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        r[v] = *reinterpret_cast<const float4*>(e + base + 4 * (lane + G * v));
+    }
+    draw();
+    add_residual();
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int64_t i = base + 4 * (lane + G * v);
+      p[v] = load4(g, i, n);
+      if (e != nullptr) r[v] = load4(e, i, n);
+    }
+    draw();
+    add_residual();
   }
 
   // ---- per-bucket levels ----------------------------------------------
@@ -182,14 +222,7 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
     int sc[4] = {0, 0, 0, 0};  // signed codes (dense digits are sc + s)
     float4 xh;
     if constexpr (SCHEME == UNIFORM) {
-      // random words, or (nearest) words whose u is exactly 1/2, so that the
-      // value rounds up iff q > 1/2
-      uint4 w = make_uint4(kHalfWord, kHalfWord, kHalfWord, kHalfWord);
-      if (!nearest) {
-        const uint64_t ctr = (uint64_t)i >> 2;
-        w = philox4x32_10(k0, k1, (uint32_t)ctr, (uint32_t)(ctr >> 32), step, 0u);
-      }
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      const uint32_t ws[4] = {wr[v].x, wr[v].y, wr[v].z, wr[v].w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float x = comp(p[v], k);
@@ -240,7 +273,8 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
       r.y = p[v].y - xh.y;
       r.z = p[v].z - xh.z;
       r.w = p[v].w - xh.w;
-      store4(e, i, n, r);
+      if (whole) *reinterpret_cast<float4*>(e + i) = r;
+      else store4(e, i, n, r);
     }
   }
 }
