@@ -136,9 +136,14 @@ __global__ __launch_bounds__(kThreads) void k_deq_acc(
   constexpr int kStride = kThreads;  // groups between a thread's v and v+1
 
   // Code loads of NB payloads at once (NB = 1, 2 or 4), all issued before
-  // any use.
+  // any use, together with the loads of the bucket's scale (uniform scheme
+  // without the LDS table) or two levels (two-level schemes), which do not
+  // depend on the codes.  ORQ levels are looked up by code afterwards.
   constexpr bool TABLE = NB == 4;
+  constexpr int MK = SCHEME == UNIFORM ? (TABLE ? 0 : 1)
+                                       : (SCHEME == ORQ ? 0 : 2);
   uint32_t cw[NB][kV];
+  float mv[NB][kV][MK > 0 ? MK : 1];
   auto load_batch = [&](int p0) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
@@ -146,10 +151,15 @@ __global__ __launch_bounds__(kThreads) void k_deq_acc(
 #pragma unroll
       for (int v = 0; v < kV; ++v) {
         const int64_t f = f0 + kStride * v;
-        cw[j][v] = (p < W && f < ngroups)
-                       ? load_group<BITS>(pp.codes[p < W ? p : 0], f,
-                                          4 * f + 4 <= n, code_bytes, dc)
-                       : 0u;
+        const bool live = p < W && f < ngroups;
+        cw[j][v] = live ? load_group<BITS>(pp.codes[p < W ? p : 0], f,
+                                           4 * f + 4 <= n, code_bytes, dc)
+                        : 0u;
+        if constexpr (MK > 0) {
+          const float* m = pp.meta[p < W ? p : 0] + MK * ((4 * f) >> dsh);
+#pragma unroll
+          for (int t = 0; t < MK; ++t) mv[j][v][t] = live ? m[t] : 0.f;
+        }
       }
     }
   };
@@ -174,19 +184,24 @@ __global__ __launch_bounds__(kThreads) void k_deq_acc(
     }
     __syncthreads();
   }
-  auto deq = [&](uint32_t w, int p, int64_t f) -> float4 {
+  auto deq = [&](int j, int v, int p, int64_t f) -> float4 {
+    const uint32_t w = cw[j][v];
     const int64_t bucket = (4 * f) >> dsh;
+    float x[4];
     if constexpr (SCHEME == UNIFORM) {
-      const float delta = TABLE ? delta_tab[p * nbk + (int)(bucket - b0)]
-                                : pp.meta[p][bucket] / (float)s;
-      float x[4];
+      float delta;
+      if constexpr (TABLE) delta = delta_tab[p * nbk + (int)(bucket - b0)];
+      else delta = mv[j][v][0] / (float)s;
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         x[k] = (float)code_value<SCHEME, BITS>(w, k, s) * delta;
-      return make_float4(x[0], x[1], x[2], x[3]);
+    } else if constexpr (SCHEME == BIN_SIGN || SCHEME == BIN_OPT) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[k] = ((w >> k) & 1u) ? mv[j][v][1] : mv[j][v][0];
     } else {
       return dequant4<SCHEME, BITS>(w, pp.meta[p], bucket, s, L);
     }
+    return make_float4(x[0], x[1], x[2], x[3]);
   };
 
   // Payloads 0 and 1 initialise the two accumulators (a copy, so a single
@@ -208,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void k_deq_acc(
       for (int v = 0; v < kV; ++v) {
         const int64_t f = f0 + kStride * v;
         if (f >= ngroups) continue;
-        const float4 x = deq(cw[j][v], p, f);
+        const float4 x = deq(j, v, p, f);
         if (p == 0) acc0[v] = x;
         else if (p == 1) acc1[v] = x;
         else if (p & 1) acc1[v] = add4(acc1[v], x);
