@@ -14,7 +14,8 @@
 // bits), two (3 bits), a 16-bit (4 bits) or a 32-bit (8 bits) load, again
 // consecutive across lanes.  Payloads are summed in fp32 into two
 // accumulators (even and odd payloads), so a sum of W terms is at most
-// ceil(W/2)+1 additions deep.
+// ceil(W/2)+1 additions deep.  The fp32 streams (aggregate, gradient,
+// residual) use nontemporal 128-bit accesses.
 #include "common.hpp"
 
 namespace gq {
@@ -240,13 +241,13 @@ __global__ __launch_bounds__(kThreads) void k_deq_acc(
     float* o = out + 4 * f;
     if (4 * f + 4 <= n) {
       if (beta != 0.f) {
-        const float4 old = *reinterpret_cast<const float4*>(o);
+        const float4 old = load4_nt(o);
         r.x = r.x + beta * old.x;
         r.y = r.y + beta * old.y;
         r.z = r.z + beta * old.z;
         r.w = r.w + beta * old.w;
       }
-      *reinterpret_cast<float4*>(o) = r;
+      store4_nt(o, r);
     } else {
       const int rem = (int)(n - 4 * f);
 #pragma unroll
@@ -276,14 +277,15 @@ __global__ __launch_bounds__(kThreads) void k_error_feedback(
     const bool full = i + 4 <= n;
     const float4 x = dequant4<SCHEME, BITS>(
         load_group<BITS>(codes, f, full, code_bytes, dc), meta, i >> dsh, s, L);
-    const float4 gv = load4(g, i, n);
-    const float4 ev = load4(e, i, n);
+    const float4 gv = full ? load4_nt(g + i) : load4(g, i, n);
+    const float4 ev = full ? load4_nt(e + i) : load4(e, i, n);
     float4 r;
     r.x = (gv.x + ev.x) - x.x;
     r.y = (gv.y + ev.y) - x.y;
     r.z = (gv.z + ev.z) - x.z;
     r.w = (gv.w + ev.w) - x.w;
-    store4(e, i, n, r);
+    if (full) store4_nt(e + i, r);
+    else store4(e, i, n, r);
   }
 }
 

@@ -10,6 +10,8 @@
 // of the group reads G consecutive 16-byte vectors.  G <= 64 groups live
 // inside one wave (256-thread blocks hold 256/G buckets); G > 64 spans G/64
 // waves of one block and reduces through LDS.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace gq {
@@ -135,17 +137,18 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
     }
   };
   // A bucket wholly inside the gradient (every bucket but possibly the
-  // last; the test is uniform over the group) loads with plain 128-bit
-  // loads, all issued before any use; the last bucket checks each element.
+  // last; the test is uniform over the group) loads with 128-bit
+  // nontemporal loads, all issued before any use; the last bucket checks
+  // each element.
   const bool whole = base + D <= n;
   if (whole) {
 #pragma unroll
     for (int v = 0; v < V; ++v)
-      p[v] = *reinterpret_cast<const float4*>(g + base + 4 * (lane + G * v));
+      p[v] = load4_nt(g + base + 4 * (lane + G * v));
     if (e != nullptr) {
 #pragma unroll
       for (int v = 0; v < V; ++v)
-        r[v] = *reinterpret_cast<const float4*>(e + base + 4 * (lane + G * v));
+        r[v] = load4_nt(e + base + 4 * (lane + G * v));
     }
     draw();
     add_residual();
@@ -215,68 +218,76 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
   const float inv = M > 0.f ? sf / (M * up) : 0.f;
   const float delta = M / sf;
 
+  // The rounding pass, specialised on whether the bucket is scaled (the
+  // factor 1 multiplies exactly, so the common case skips it).
+  auto code_pass = [&](auto scaled_tag) {
+    constexpr bool SCALED = decltype(scaled_tag)::value;
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int64_t i = base + 4 * (lane + G * v);
-    uint32_t c[4];
-    int sc[4] = {0, 0, 0, 0};  // signed codes (dense digits are sc + s)
-    float4 xh;
-    if constexpr (SCHEME == UNIFORM) {
-      const uint32_t ws[4] = {wr[v].x, wr[v].y, wr[v].z, wr[v].w};
+    for (int v = 0; v < V; ++v) {
+      const int64_t i = base + 4 * (lane + G * v);
+      uint32_t c[4];
+      int sc[4] = {0, 0, 0, 0};  // signed codes (dense digits are sc + s)
+      float4 xh;
+      if constexpr (SCHEME == UNIFORM) {
+        const uint32_t ws[4] = {wr[v].x, wr[v].y, wr[v].z, wr[v].w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float x = comp(p[v], k);
-        const float r = fminf((fabsf(x) * up) * inv, sf);
-        const float l = floorf(r);
-        const float q = r - l;
-        const int mag = (int)l + (u24(ws[k]) < q ? 1 : 0);
-        const int ci = x < 0.f ? -mag : mag;
-        sc[k] = ci;
-        c[k] = DENSE ? 0u : ((uint32_t)ci & ((1u << BITS) - 1u));
-        const float xk = (float)ci * delta;
-        if (k == 0) xh.x = xk;
-        if (k == 1) xh.y = xk;
-        if (k == 2) xh.z = xk;
-        if (k == 3) xh.w = xk;
+        for (int k = 0; k < 4; ++k) {
+          const float x = comp(p[v], k);
+          const float ax = SCALED ? fabsf(x) * up : fabsf(x);
+          const float r = fminf(ax * inv, sf);
+          const float l = floorf(r);
+          const float q = r - l;
+          const int mag = (int)l + (u24(ws[k]) < q ? 1 : 0);
+          const int ci = x < 0.f ? -mag : mag;
+          sc[k] = ci;
+          c[k] = DENSE ? 0u : ((uint32_t)ci & ((1u << BITS) - 1u));
+          const float xk = (float)ci * delta;
+          if (k == 0) xh.x = xk;
+          if (k == 1) xh.y = xk;
+          if (k == 2) xh.z = xk;
+          if (k == 3) xh.w = xk;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float x = comp(p[v], k);
+          c[k] = x >= 0.f ? 1u : 0u;
+          const float xk = c[k] ? lvl1 : lvl0;
+          if (k == 0) xh.x = xk;
+          if (k == 1) xh.y = xk;
+          if (k == 2) xh.z = xk;
+          if (k == 3) xh.w = xk;
+        }
       }
-    } else {
+      // absent tail elements pack as 0
+      const int nreal = i + 4 <= n ? 4 : (i < n ? (int)(n - i) : 0);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float x = comp(p[v], k);
-        c[k] = x >= 0.f ? 1u : 0u;
-        const float xk = c[k] ? lvl1 : lvl0;
-        if (k == 0) xh.x = xk;
-        if (k == 1) xh.y = xk;
-        if (k == 2) xh.z = xk;
-        if (k == 3) xh.w = xk;
+      for (int k = 0; k < 4; ++k)
+        if (k >= nreal) c[k] = 0u;
+      if constexpr (DENSE) {
+        const uint32_t A = 2u * (uint32_t)s + 1u;
+        uint32_t u = 0u;
+#pragma unroll
+        for (int k = 3; k >= 0; --k)
+          u = __umul24(u, A) + (k < nreal ? (uint32_t)(sc[k] + s) : 0u);
+        store_dense_chunk(codes, i - 4 * (threadIdx.x & 63), u, A4, W, code_bytes);
+      } else {
+        store_field<BITS, G>(codes, i, lane, field4<BITS>(c[0], c[1], c[2], c[3]),
+                             code_bytes);
+      }
+      if (e != nullptr && i < n) {
+        float4 r;
+        r.x = p[v].x - xh.x;
+        r.y = p[v].y - xh.y;
+        r.z = p[v].z - xh.z;
+        r.w = p[v].w - xh.w;
+        if (whole) store4_nt(e + i, r);
+        else store4(e, i, n, r);
       }
     }
-    // absent tail elements pack as 0
-    const int nreal = i + 4 <= n ? 4 : (i < n ? (int)(n - i) : 0);
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (k >= nreal) c[k] = 0u;
-    if constexpr (DENSE) {
-      const uint32_t A = 2u * (uint32_t)s + 1u;
-      uint32_t u = 0u;
-#pragma unroll
-      for (int k = 3; k >= 0; --k)
-        u = __umul24(u, A) + (k < nreal ? (uint32_t)(sc[k] + s) : 0u);
-      store_dense_chunk(codes, i - 4 * (threadIdx.x & 63), u, A4, W, code_bytes);
-    } else {
-      store_field<BITS, G>(codes, i, lane, field4<BITS>(c[0], c[1], c[2], c[3]),
-                           code_bytes);
-    }
-    if (e != nullptr && i < n) {
-      float4 r;
-      r.x = p[v].x - xh.x;
-      r.y = p[v].y - xh.y;
-      r.z = p[v].z - xh.z;
-      r.w = p[v].w - xh.w;
-      if (whole) *reinterpret_cast<float4*>(e + i) = r;
-      else store4(e, i, n, r);
-    }
-  }
+  };
+  if (up == 1.0f) code_pass(std::false_type{});
+  else code_pass(std::true_type{});
 }
 
 template <int SCHEME, int BITS, int G, int V>
