@@ -63,6 +63,11 @@ def lib():
         L.gqref_dequantize_accumulate.argtypes = [
             i32, i32, i32, i32, i32, i64, i32, C.POINTER(C.c_void_p),
             C.POINTER(C.c_void_p), C.c_float, C.c_float, fp]
+        L.gqref_quantize_layers.argtypes = [i32, i32, i64, i32, C.c_void_p,
+                                            cfp, fp, u64, u32, u8p, fp]
+        L.gqref_dequantize_accumulate_layers.argtypes = [
+            i32, i32, i64, i32, C.c_void_p, i32, C.POINTER(C.c_void_p),
+            C.POINTER(C.c_void_p), C.c_float, C.c_float, fp]
         L.gqref_dense_width.argtypes = [i32]
         L.gqref_pack_dense.argtypes = [i32, i64, C.c_void_p, u8p]
         L.gqref_pack_dense.restype = None
@@ -217,6 +222,51 @@ def dequantize_accumulate(desc: Desc, n: int, codes_list, meta_list,
                                            beta, _ptr(out))
     if rc:
         raise ValueError("oracle dequantize_accumulate: invalid arguments")
+    return out
+
+
+def _offsets(offsets, n: int) -> np.ndarray:
+    off = np.ascontiguousarray(offsets, dtype=np.int64)
+    if off.ndim != 1 or off.size < 2:
+        raise ValueError("layer offsets: need nl + 1 >= 2 entries")
+    return off
+
+
+def quantize_layers(desc: Desc, offsets, g, e=None, seed: int = 0,
+                    step: int = 0):
+    """Per-layer scale (TernGrad): layer l = g[off[l]:off[l+1]] is one bucket
+    of the uniform scheme.  Returns (codes u8, meta f32[nl], e_new or None).
+    desc.d is not used."""
+    g = _f32(g)
+    n = g.size
+    off = _offsets(offsets, n)
+    nl = off.size - 1
+    e_new = None if e is None else _f32(e).copy()
+    codes = np.zeros(desc.code_bytes(n), dtype=np.uint8)
+    meta = np.zeros(nl, dtype=np.float32)
+    rc = lib().gqref_quantize_layers(desc.s, desc.flags, n, nl, _ptr(off),
+                                     _ptr(g), _ptr(e_new), seed, step,
+                                     _ptr(codes), _ptr(meta))
+    if rc:
+        raise ValueError("oracle quantize_layers: invalid arguments")
+    return codes, meta, e_new
+
+
+def dequantize_accumulate_layers(desc: Desc, offsets, n: int, codes_list,
+                                 meta_list, alpha: float = 1.0,
+                                 beta: float = 0.0, out=None):
+    off = _offsets(offsets, n)
+    W = len(codes_list)
+    cl = [np.ascontiguousarray(c, dtype=np.uint8) for c in codes_list]
+    ml = [_f32(m) for m in meta_list]
+    out = np.zeros(n, dtype=np.float32) if out is None else _f32(out).copy()
+    cp = (C.c_void_p * W)(*[c.ctypes.data for c in cl])
+    mp = (C.c_void_p * W)(*[m.ctypes.data for m in ml])
+    rc = lib().gqref_dequantize_accumulate_layers(
+        desc.s, desc.flags, n, off.size - 1, _ptr(off), W, cp, mp, alpha,
+        beta, _ptr(out))
+    if rc:
+        raise ValueError("oracle dequantize_accumulate_layers: invalid arguments")
     return out
 
 

@@ -721,6 +721,98 @@ int gqref_dequantize_accumulate(int scheme, int d, int s, int L, int flags,
   return 0;
 }
 
+/* ------------------------------------------------------ per-layer scale --
+ * TernGrad's layout ("Gradient Quantization" glossary, ternary paragraph:
+ * one scaling factor per layer): the flat gradient is the concatenation of
+ * nl layers, layer l = elements [off[l], off[l+1]), and each layer is one
+ * bucket of the uniform scheme, whatever its size or offset.  The random
+ * counter is the element's index in the flat gradient and the codes form
+ * the same flat stream as the bucketed layout (dense: 8-code fields by flat
+ * index, so a field may hold codes of two layers).  meta[l] = the layer's
+ * max-abs (0 for an empty layer). */
+static int check_layers(int s, int flags, int64_t n, int nl,
+                        const int64_t *off) {
+  if (n < 1 || nl < 1 || !off) return -1;
+  if (gqref_bits(UNIFORM, s, 2) < 0) return -1;
+  if (flags & 1) return -1; /* clipping is an ORQ option */
+  if (off[0] != 0 || off[nl] != n) return -1;
+  for (int l = 0; l < nl; ++l)
+    if (off[l + 1] < off[l]) return -1;
+  return 0;
+}
+
+int gqref_quantize_layers(int s, int flags, int64_t n, int nl,
+                          const int64_t *off, const float *g, float *e,
+                          uint64_t seed, uint32_t step, uint8_t *codes,
+                          float *meta) {
+  params pr;
+  if (check_layers(s, flags, n, nl, off) ||
+      make_params(&pr, UNIFORM, 64, s, 2, flags, 0.f))
+    return -1;
+  if (!g || !codes || !meta) return -1;
+  int32_t *cv = (int32_t *)malloc((size_t)n * sizeof(int32_t));
+  if (!cv) return -1;
+#pragma omp parallel for schedule(dynamic)
+  for (int l = 0; l < nl; ++l) {
+    int64_t lo = off[l], hi = off[l + 1];
+    /* error feedback: p = g + e, then the layer's max-abs */
+    float M = 0.0f;
+    for (int64_t i = lo; i < hi; ++i) {
+      float p = e ? g[i] + e[i] : g[i];
+      if (fabsf(p) > M) M = fabsf(p);
+    }
+    meta[l] = M;
+    for (int64_t i = lo; i < hi; ++i) {
+      float p = e ? g[i] + e[i] : g[i];
+      int32_t c = code_uniform(&pr, p, M, pr.nearest ? 0.0f : uniform_u(seed, step, i));
+      cv[i] = c;
+      if (e) e[i] = p - dequant_one(&pr, c, meta + l);
+    }
+  }
+  /* pack the flat stream (sequentially: fields may straddle layers) */
+  memset(codes, 0, (size_t)stream_bytes(&pr, n));
+  if (pr.dense) {
+    for (int64_t g0 = 0; g0 < n; g0 += 8) {
+      uint64_t v = 0, place = 1;
+      for (int t = 0; t < 8; ++t) {
+        if (g0 + t < n) v += (uint64_t)(cv[g0 + t] + pr.s) * place;
+        place *= (uint64_t)pr.A;
+      }
+      put_bits(codes, (g0 / 8) * pr.w, pr.w, v);
+    }
+  } else {
+    for (int64_t i = 0; i < n; ++i)
+      put_code(codes, i, pr.bits, (uint32_t)cv[i] & ((1u << pr.bits) - 1u));
+  }
+  free(cv);
+  return 0;
+}
+
+int gqref_dequantize_accumulate_layers(int s, int flags, int64_t n, int nl,
+                                       const int64_t *off, int W,
+                                       const uint8_t *const *codes,
+                                       const float *const *meta, float alpha,
+                                       float beta, float *out) {
+  params pr;
+  if (check_layers(s, flags, n, nl, off) ||
+      make_params(&pr, UNIFORM, 64, s, 2, flags, 0.f))
+    return -1;
+  if (W < 1) return -1;
+#pragma omp parallel for schedule(dynamic)
+  for (int l = 0; l < nl; ++l) {
+    for (int64_t i = off[l]; i < off[l + 1]; ++i) {
+      nsum acc = {0, 0};
+      for (int w = 0; w < W; ++w)
+        nadd(&acc, (double)dequant_one(&pr, read_code(&pr, codes[w], i),
+                                       meta[w] + l));
+      double v = (double)alpha * nval(&acc);
+      if (beta != 0.0f) v += (double)beta * (double)out[i];
+      out[i] = (float)v;
+    }
+  }
+  return 0;
+}
+
 void gqref_set_threads(int t) {
   if (t > 0) omp_set_num_threads(t);
 }

@@ -81,6 +81,21 @@ int gqref_dequantize_accumulate(int scheme, int d, int s, int L, int flags,
                                 const float *const *meta, float alpha,
                                 float beta, float *out);
 
+/* Per-layer scale (TernGrad): the uniform scheme with layer l = elements
+ * [off[l], off[l+1]) of the flat gradient as one bucket (off[0] = 0,
+ * off[nl] = n, non-decreasing; empty layers allowed).  meta: nl floats
+ * (each layer's max-abs).  flags: dense (bit 1) and nearest (bit 2); codes
+ * as in gqref_quantize for the flat index. */
+int gqref_quantize_layers(int s, int flags, int64_t n, int nl,
+                          const int64_t *off, const float *g, float *e,
+                          uint64_t seed, uint32_t step, uint8_t *codes,
+                          float *meta);
+int gqref_dequantize_accumulate_layers(int s, int flags, int64_t n, int nl,
+                                       const int64_t *off, int W,
+                                       const uint8_t *const *codes,
+                                       const float *const *meta, float alpha,
+                                       float beta, float *out);
+
 /* Dense packing (flags bit 1): groups of 8 codes as one base-A integer,
  * first code least significant, in fields of gqref_dense_width(A) =
  * ceil(log2(A^8)) bits of the LSB-first stream; A <= 16. */
