@@ -247,7 +247,7 @@ def entry(name, ms, nbytes, n, bound="hbm", extra=None):
 def suite(torch, gq, WL, stream, reps: int, only: str | None = None):
     """Every other workload's kernels, each timed back to back (only the
     workloads whose name contains `only`: qsgd, orq, bingrad, workers,
-    dense, nearest)."""
+    dense, nearest, layers)."""
     out = []
     tb = lambda f, r=reps: time_back_to_back(torch, stream, f, r)  # noqa: E731
     want = lambda name: only is None or only in name  # noqa: E731
@@ -264,6 +264,37 @@ def suite(torch, gq, WL, stream, reps: int, only: str | None = None):
         out += suite_dense(torch, gq, WL, stream, tb, reps)
     if want("nearest"):
         out += suite_nearest(torch, gq, WL, stream, tb, reps)
+    if want("layers"):
+        out += suite_layers(torch, gq, WL, stream, tb)
+    return out
+
+
+def suite_layers(torch, gq, WL, stream, tb):
+    """Per-layer scale (TernGrad): ternary + EF on the 25.6M gradient with
+    one scale for each of its 160 layers, and its dequantize.  The quantizer
+    makes two passes (layer maxima, then rounding): 8 + 12 bytes per element
+    plus codes and scales."""
+    import numpy as np
+    out = []
+    sizes, _ = WL.ternary_layout()
+    off = torch.from_numpy(np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)).cuda()
+    nl = len(sizes)
+    G = [torch.from_numpy(WL.ternary_gradient(t)).cuda() for t in range(2)]
+    n = G[0].numel()
+    E = [torch.zeros(n, dtype=torch.float32, device="cuda") for _ in range(2)]
+    d = gq.desc(gq.GQ_UNIFORM, 512, s=1)
+    _, cap, _ = gq.gq_payload_size(d, n)
+    C = [torch.empty(cap, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    M = [torch.empty(nl, dtype=torch.float32, device="cuda") for _ in range(2)]
+    O_ = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(2)]
+    ms = tb(lambda i: gq.gq_quantize_layers(d, off, G[i % 2], E[i % 2], 2, i,
+                                            C[i % 2], M[i % 2], stream))
+    out.append(entry(f"quantize ternary+ef per-layer scale ({nl} layers) n={n}",
+                     ms, 20 * n + (2 * n + 7) // 8 + 4 * nl, n))
+    ms = tb(lambda i: gq.gq_dequantize_accumulate_layers(
+        d, n, off, [C[i % 2]], [M[i % 2]], 1.0, 0.0, O_[i % 2], stream))
+    out.append(entry(f"dequantize ternary per-layer scale W=1 n={n}", ms,
+                     (2 * n + 7) // 8 + 4 * nl + 4 * n, n))
     return out
 
 
@@ -507,7 +538,7 @@ def main() -> int:
     ap.add_argument("--suite", choices=("main", "all"), default="all")
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--only", choices=("qsgd", "orq", "bingrad", "workers",
-                                       "dense", "nearest"),
+                                       "dense", "nearest", "layers"),
                     help="time only this workload's kernels after the headline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--counters", action="store_true",

@@ -235,4 +235,65 @@ int gq_dequantize_accumulate(const gq_desc* desc, int64_t n, int32_t W,
                                           static_cast<hipStream_t>(stream)));
 }
 
+int gq_quantize_layers(const gq_desc* desc, int64_t n, int32_t nl,
+                       const int64_t* layer_offsets, const float* g, float* e,
+                       uint64_t seed, uint32_t step, uint8_t* codes,
+                       float* meta, void* stream) {
+  gq::LaunchDesc L;
+  int rc = check_desc(desc, &L);
+  if (rc) return rc;
+  if (L.scheme != GQ_UNIFORM) return GQ_EUNSUPPORTED;
+  if (n < 1 || n > kMaxN || nl < 1 || !layer_offsets || !g || !codes || !meta)
+    return GQ_EINVAL;
+  if (!aligned16(g) || !aligned16(codes) || !aligned16(meta) ||
+      (e && !aligned16(e)) || reinterpret_cast<uintptr_t>(layer_offsets) % 8)
+    return GQ_EINVAL;
+  const int64_t cb = code_bytes_of(L, n);
+  const int64_t cap = (cb + 15) / 16 * 16;
+  const int64_t mb = 4 * (int64_t)nl, ob = 8 * ((int64_t)nl + 1);
+  if (e && (overlap(e, 4 * n, g, 4 * n) || overlap(e, 4 * n, codes, cap) ||
+            overlap(e, 4 * n, meta, mb) || overlap(e, 4 * n, layer_offsets, ob)))
+    return GQ_EINVAL;
+  if (overlap(codes, cap, g, 4 * n) || overlap(meta, mb, g, 4 * n) ||
+      overlap(codes, cap, meta, mb) || overlap(codes, cap, layer_offsets, ob) ||
+      overlap(meta, mb, layer_offsets, ob))
+    return GQ_EINVAL;
+  return launch_status(gq::launch_layer_quant(L, n, nl, layer_offsets, g, e,
+                                              seed, step, codes, meta, cb,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int gq_dequantize_accumulate_layers(const gq_desc* desc, int64_t n, int32_t nl,
+                                    const int64_t* layer_offsets, int32_t W,
+                                    const uint8_t* const* codes,
+                                    const float* const* meta, float alpha,
+                                    float beta, float* out, void* stream) {
+  gq::LaunchDesc L;
+  int rc = check_desc(desc, &L);
+  if (rc) return rc;
+  if (L.scheme != GQ_UNIFORM) return GQ_EUNSUPPORTED;
+  if (W > GQ_MAX_PAYLOADS) return GQ_ETOOMANY;
+  if (n < 1 || n > kMaxN || nl < 1 || W < 1 || !layer_offsets || !codes ||
+      !meta || !out)
+    return GQ_EINVAL;
+  if (!aligned16(out) || reinterpret_cast<uintptr_t>(layer_offsets) % 8 ||
+      !std::isfinite(alpha) || !std::isfinite(beta))
+    return GQ_EINVAL;
+  const int64_t cb = code_bytes_of(L, n);
+  const int64_t mb = 4 * (int64_t)nl, ob = 8 * ((int64_t)nl + 1);
+  if (overlap(out, 4 * n, layer_offsets, ob)) return GQ_EINVAL;
+  gq::PayloadPtrs pp{};
+  for (int w = 0; w < W; ++w) {
+    if (!codes[w] || !meta[w] || !aligned16(codes[w]) || !aligned16(meta[w]))
+      return GQ_EINVAL;
+    if (overlap(out, 4 * n, codes[w], cb) || overlap(out, 4 * n, meta[w], mb))
+      return GQ_EINVAL;
+    pp.codes[w] = codes[w];
+    pp.meta[w] = meta[w];
+  }
+  return launch_status(gq::launch_layer_deq(L, n, nl, layer_offsets, W, pp,
+                                            alpha, beta, out, cb,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

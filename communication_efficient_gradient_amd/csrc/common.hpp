@@ -54,6 +54,24 @@ __device__ __forceinline__ float u24(uint32_t w) {
 // up iff q > 1/2).
 constexpr uint32_t kHalfWord = 0x80000000u;
 
+// Signed code of x on the uniform grid of a bucket with max-abs M and s
+// levels per sign ("Gradient Quantization" glossary: max-abs scaling, the
+// Stochastic Quantization bullet): r = min(|x| * inv, s) with inv = s / M,
+// l = floor(r), q = r - l (exact), magnitude l + [u < q], u from word w.  A
+// bucket with M < 2^-96 is scaled by up = 2^96 first (inv = s / (M * up));
+// SCALED = false is the common case up = 1, whose multiply is exact and
+// skipped.
+template <bool SCALED>
+__device__ __forceinline__ int uniform_code(float x, float up, float inv,
+                                            float sf, uint32_t w) {
+  const float ax = SCALED ? fabsf(x) * up : fabsf(x);
+  const float r = fminf(ax * inv, sf);
+  const float l = floorf(r);
+  const float q = r - l;
+  const int mag = (int)l + (u24(w) < q ? 1 : 0);
+  return x < 0.f ? -mag : mag;
+}
+
 // ------------------------------------------------------- lane exchange --
 // Value of lane (lane ^ o) for o = 1, 2, 4, .., 32 and for the mirror masks
 // 3, 7, 15, 31, 63, without the LDS crossbar: DPP quad permutes for 1, 2
@@ -414,6 +432,122 @@ __device__ __forceinline__ uint32_t load_dense4(const uint8_t* __restrict__ c,
   return out | (v << 24);
 }
 
+// ---------------------------------------------------------- layers --
+// Per-layer scale (TernGrad): the flat gradient is the concatenation of nl
+// layers, layer l = elements [off[l], off[l+1]).  Kernels that walk it in
+// tiles find the layers meeting a tile once per block.  With nl <
+// kOffCache the block first copies off into LDS (one load per thread,
+// issued before the tile's data loads, so the search waits for it alone);
+// otherwise one wave searches off in global memory.  The layer starts
+// inside the tile (at most kMaxStarts) are then kept in LDS; a tile met by
+// more layers looks each element up.  Every layer index is clamped to
+// [0, nl), so any contents of off give in-bounds accesses.
+constexpr int kMaxStarts = 32;     // layer starts inside one tile kept in LDS
+constexpr int kOffCache = 1024;    // offsets copied to LDS when nl < this
+constexpr int kOffPerThread = kOffCache / 256;
+
+// Layer holding flat element x: the largest l in [0, nl) with off[l] <= x
+// (empty layers are passed over); off may be global or LDS memory.
+__device__ __forceinline__ int layer_of(const int64_t* __restrict__ off,
+                                        int nl, int64_t x) {
+  int lo = 0, hi = nl;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (off[mid] <= x) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// The same, found by the 64 lanes of one wave together in global memory
+// (every lane returns it): each round reads 64 evenly spaced offsets of the
+// remaining range and keeps the stretch after the last one <= x.
+__device__ __forceinline__ int layer_of_wave(const int64_t* __restrict__ off,
+                                             int nl, int64_t x) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = nl;  // the layer lies in [lo, hi)
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) >> 6;
+    const int idx = lo + lane * step;
+    const bool ok = idx < hi && off[idx] <= x;
+    const uint64_t m = __ballot(ok);
+    const int last = m ? 63 - __clzll((long long)m) : 0;
+    lo += last * step;
+    hi = lo + step < hi ? lo + step : hi;
+  }
+  return lo;
+}
+
+// The layers of a tile: lf holds its first element; starts[k] =
+// off[lf + 1 + k] for the ns layers that start inside it, or ns = -1 when
+// there are more than kMaxStarts.  offc: off[0..nl] when nl < kOffCache.
+struct TileLayers {
+  int lf, ns;
+  int64_t starts[kMaxStarts];
+  int64_t offc[kOffCache];
+};
+
+// Step 1 (before the tile's data loads): this thread's share of off.
+__device__ __forceinline__ void prefetch_offsets(int64_t (&o)[kOffPerThread],
+                                                 const int64_t* __restrict__ off,
+                                                 int nl) {
+#pragma unroll
+  for (int j = 0; j < kOffPerThread; ++j) {
+    const int idx = threadIdx.x + 256 * j;
+    o[j] = (nl < kOffCache && idx <= nl) ? off[idx] : 0;
+  }
+}
+
+// Step 2: the tile [t0, t1).  Blocks of 256 threads; every thread calls it.
+__device__ void find_tile_layers(TileLayers& T, const int64_t (&o)[kOffPerThread],
+                                 const int64_t* __restrict__ off, int nl,
+                                 int64_t t0, int64_t t1) {
+  __shared__ int ends[2];
+  if (nl < kOffCache) {
+#pragma unroll
+    for (int j = 0; j < kOffPerThread; ++j) {
+      const int idx = threadIdx.x + 256 * j;
+      if (idx <= nl) T.offc[idx] = o[j];
+    }
+    __syncthreads();
+    if (threadIdx.x < 2) ends[threadIdx.x] = layer_of(T.offc, nl, threadIdx.x ? t1 - 1 : t0);
+  } else {
+    const int wave = threadIdx.x >> 6;
+    if (wave < 2) {
+      const int l = layer_of_wave(off, nl, wave == 0 ? t0 : t1 - 1);
+      if ((threadIdx.x & 63) == 0) ends[wave] = l;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int lf = ends[0], ll = ends[1];
+    T.lf = lf;
+    T.ns = (ll < lf || ll - lf > kMaxStarts) ? -1 : ll - lf;
+  }
+  __syncthreads();
+  const int ns = T.ns;
+  if (ns > 0 && (int)threadIdx.x < ns)
+    T.starts[threadIdx.x] = nl < kOffCache ? T.offc[T.lf + 1 + threadIdx.x]
+                                           : off[T.lf + 1 + threadIdx.x];
+  __syncthreads();
+}
+
+// Layer of flat element i of the tile.
+__device__ __forceinline__ int elem_layer(const TileLayers& T,
+                                          const int64_t* __restrict__ off,
+                                          int nl, int64_t i) {
+  const int ns = T.ns;
+  if (ns == 0) return T.lf;
+  if (ns < 0) return layer_of(nl < kOffCache ? T.offc : off, nl, i);
+  int lo = 0, hi = ns;  // count of starts <= i
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (T.starts[mid] <= i) lo = mid + 1;
+    else hi = mid;
+  }
+  return T.lf + lo;
+}
+
 }  // namespace gq
 
 // ----------------------------------------------------- host launchers --
@@ -448,5 +582,15 @@ int launch_deq_acc(const LaunchDesc& L, int64_t n, int W, const PayloadPtrs& pp,
 int launch_error_feedback(const LaunchDesc& L, int64_t n, const float* g,
                           float* e, const uint8_t* codes, const float* meta,
                           int64_t code_bytes, hipStream_t st);
+// per-layer scale (uniform scheme): max-abs pass then rounding pass
+// (codes == nullptr: the max-abs pass only)
+int launch_layer_quant(const LaunchDesc& L, int64_t n, int nl,
+                       const int64_t* off, const float* g, float* e,
+                       uint64_t seed, uint32_t step, uint8_t* codes,
+                       float* meta, int64_t code_bytes, hipStream_t st);
+int launch_layer_deq(const LaunchDesc& L, int64_t n, int nl,
+                     const int64_t* off, int W, const PayloadPtrs& pp,
+                     float alpha, float beta, float* out, int64_t code_bytes,
+                     hipStream_t st);
 
 }  // namespace gq

@@ -289,6 +289,128 @@ __global__ __launch_bounds__(kThreads) void k_error_feedback(
   }
 }
 
+// Per-layer scale (TernGrad, "Gradient Quantization" glossary, ternary
+// paragraph): the uniform scheme with layer l = elements [off[l], off[l+1])
+// as one bucket.  Same tiles and accumulation order as k_deq_acc; the step
+// of each element is that of its layer, M / s, divided once per (payload,
+// layer) of the tile into LDS (per element for a tile met by more than
+// kMaxStarts layers).
+static_assert(kThreads == 256, "find_tile_layers expects blocks of 256 threads");
+
+template <int BITS, int NB>
+__global__ __launch_bounds__(kThreads) void k_layer_deq(
+    int64_t n, int nl, const int64_t* __restrict__ off, int s, int W,
+    PayloadPtrs pp, float alpha, float beta, float* __restrict__ out,
+    int64_t code_bytes, DenseCfg dc) {
+  __shared__ TileLayers T;
+  __shared__ float dtab[kMaxPayloads][kMaxStarts + 1];
+  const int64_t ngroups = (n + 3) >> 2;
+  const int64_t tile = (int64_t)blockIdx.x * kGroupsPerBlock;
+  const int64_t f0 = tile + threadIdx.x;
+  const int64_t t0 = 4 * tile;
+  const int64_t t1 = t0 + 4 * (int64_t)kGroupsPerBlock < n ? t0 + 4 * (int64_t)kGroupsPerBlock : n;
+  int64_t o[kOffPerThread];
+  prefetch_offsets(o, off, nl);
+  // the first batch of code loads goes out before the layer search
+  uint32_t cw[NB][kV];
+  auto load_batch = [&](int p0) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int p = p0 + j;
+#pragma unroll
+      for (int v = 0; v < kV; ++v) {
+        const int64_t f = f0 + (int64_t)kThreads * v;
+        cw[j][v] = (p < W && f < ngroups)
+                       ? load_group<BITS>(pp.codes[p < W ? p : 0], f,
+                                          4 * f + 4 <= n, code_bytes, dc)
+                       : 0u;
+      }
+    }
+  };
+  load_batch(0);
+  find_tile_layers(T, o, off, nl, t0, t1);
+  const int ns = T.ns;
+  const int nent = ns >= 0 ? ns + 1 : 0;
+  for (int t = threadIdx.x; t < W * nent; t += kThreads)
+    dtab[t / nent][t % nent] = pp.meta[t / nent][T.lf + t % nent] / (float)s;
+  __syncthreads();
+
+  // layer of each element (ns != 0): its LDS column, or (ns < 0) the layer
+  int li[kV][4];
+#pragma unroll
+  for (int v = 0; v < kV; ++v) {
+    const int64_t i = 4 * (f0 + (int64_t)kThreads * v);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      li[v][k] = 0;
+      if (ns != 0) {
+        const int l = elem_layer(T, off, nl, i + k < n ? i + k : n - 1);
+        li[v][k] = ns > 0 ? l - T.lf : l;
+      }
+    }
+  }
+  float4 acc0[kV], acc1[kV];
+#pragma unroll
+  for (int v = 0; v < kV; ++v) {
+    acc0[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+    acc1[v] = acc0[v];
+  }
+  for (int p0 = 0; p0 < W; p0 += NB) {
+    if (p0 > 0) load_batch(p0);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int p = p0 + j;
+      if (p >= W) break;
+#pragma unroll
+      for (int v = 0; v < kV; ++v) {
+        const int64_t f = f0 + (int64_t)kThreads * v;
+        if (f >= ngroups) continue;
+        float x[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float delta = ns == 0 ? dtab[p][0]
+                              : (ns > 0 ? dtab[p][li[v][k]]
+                                        : pp.meta[p][li[v][k]] / (float)s);
+          x[k] = (float)code_value<UNIFORM, BITS>(cw[j][v], k, s) * delta;
+        }
+        const float4 xv = make_float4(x[0], x[1], x[2], x[3]);
+        if (p == 0) acc0[v] = xv;
+        else if (p == 1) acc1[v] = xv;
+        else if (p & 1) acc1[v] = add4(acc1[v], xv);
+        else acc0[v] = add4(acc0[v], xv);
+      }
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < kV; ++v) {
+    const int64_t f = f0 + (int64_t)kThreads * v;
+    if (f >= ngroups) continue;
+    float4 a = W > 1 ? add4(acc0[v], acc1[v]) : acc0[v];
+    float4 r = make_float4(alpha * a.x, alpha * a.y, alpha * a.z, alpha * a.w);
+    float* o = out + 4 * f;
+    if (4 * f + 4 <= n) {
+      if (beta != 0.f) {
+        const float4 old = load4_nt(o);
+        r.x = r.x + beta * old.x;
+        r.y = r.y + beta * old.y;
+        r.z = r.z + beta * old.z;
+        r.w = r.w + beta * old.w;
+      }
+      store4_nt(o, r);
+    } else {
+      const int rem = (int)(n - 4 * f);
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        if (k < rem) {
+          float rk = comp(r, k);
+          if (beta != 0.f) rk = rk + beta * o[k];
+          o[k] = rk;
+        }
+      }
+    }
+  }
+}
+
 int64_t blocks_for(int64_t n) {
   const int64_t ngroups = (n + 3) >> 2;
   return (ngroups + kGroupsPerBlock - 1) / kGroupsPerBlock;
@@ -369,6 +491,24 @@ int ef_one(const LaunchDesc& L, int64_t n, const float* g, float* e,
       return (int)hipErrorInvalidValue;                             \
   }
 
+template <int BITS>
+int layer_deq_one(const LaunchDesc& L, int64_t n, int nl, const int64_t* off,
+                  int W, const PayloadPtrs& pp, float alpha, float beta,
+                  float* out, int64_t code_bytes, hipStream_t st) {
+  const dim3 grid((uint32_t)blocks_for(n)), block(kThreads);
+  const DenseCfg dc = dense_cfg(L);
+  if (W == 1)
+    hipLaunchKernelGGL((k_layer_deq<BITS, 1>), grid, block, 0, st, n, nl, off,
+                       L.s, W, pp, alpha, beta, out, code_bytes, dc);
+  else if (W == 2)
+    hipLaunchKernelGGL((k_layer_deq<BITS, 2>), grid, block, 0, st, n, nl, off,
+                       L.s, W, pp, alpha, beta, out, code_bytes, dc);
+  else
+    hipLaunchKernelGGL((k_layer_deq<BITS, 4>), grid, block, 0, st, n, nl, off,
+                       L.s, W, pp, alpha, beta, out, code_bytes, dc);
+  return (int)hipGetLastError();
+}
+
 }  // namespace
 
 int launch_deq_acc(const LaunchDesc& L, int64_t n, int W, const PayloadPtrs& pp,
@@ -381,6 +521,25 @@ int launch_error_feedback(const LaunchDesc& L, int64_t n, const float* g,
                           float* e, const uint8_t* codes, const float* meta,
                           int64_t code_bytes, hipStream_t st) {
   GQ_DISPATCH(ef_one, L, n, g, e, codes, meta, code_bytes, st)
+}
+
+}  // namespace gq
+
+namespace gq {
+
+int launch_layer_deq(const LaunchDesc& L, int64_t n, int nl,
+                     const int64_t* off, int W, const PayloadPtrs& pp,
+                     float alpha, float beta, float* out, int64_t code_bytes,
+                     hipStream_t st) {
+  if (L.scheme != UNIFORM) return (int)hipErrorInvalidValue;
+  if (L.dense) return layer_deq_one<0>(L, n, nl, off, W, pp, alpha, beta, out, code_bytes, st);
+  switch (L.bits) {
+    case 2: return layer_deq_one<2>(L, n, nl, off, W, pp, alpha, beta, out, code_bytes, st);
+    case 3: return layer_deq_one<3>(L, n, nl, off, W, pp, alpha, beta, out, code_bytes, st);
+    case 4: return layer_deq_one<4>(L, n, nl, off, W, pp, alpha, beta, out, code_bytes, st);
+    case 8: return layer_deq_one<8>(L, n, nl, off, W, pp, alpha, beta, out, code_bytes, st);
+    default: return (int)hipErrorInvalidValue;
+  }
 }
 
 }  // namespace gq

@@ -232,13 +232,7 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
         const uint32_t ws[4] = {wr[v].x, wr[v].y, wr[v].z, wr[v].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const float x = comp(p[v], k);
-          const float ax = SCALED ? fabsf(x) * up : fabsf(x);
-          const float r = fminf(ax * inv, sf);
-          const float l = floorf(r);
-          const float q = r - l;
-          const int mag = (int)l + (u24(ws[k]) < q ? 1 : 0);
-          const int ci = x < 0.f ? -mag : mag;
+          const int ci = uniform_code<SCALED>(comp(p[v], k), up, inv, sf, ws[k]);
           sc[k] = ci;
           c[k] = DENSE ? 0u : ((uint32_t)ci & ((1u << BITS) - 1u));
           const float xk = (float)ci * delta;

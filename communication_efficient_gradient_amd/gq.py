@@ -26,6 +26,7 @@ GQ_MAX_PAYLOADS = 16
 
 SYMBOLS = ("gq_code_bits", "gq_payload_size", "gq_select_levels",
            "gq_quantize", "gq_error_feedback", "gq_dequantize_accumulate",
+           "gq_quantize_layers", "gq_dequantize_accumulate_layers",
            "gq_strerror", "gq_version")
 
 
@@ -64,6 +65,11 @@ def _load():
     lib.gq_dequantize_accumulate.argtypes = [D, i64, i32, C.POINTER(P),
                                              C.POINTER(P), C.c_float,
                                              C.c_float, P, P]
+    lib.gq_quantize_layers.argtypes = [D, i64, i32, P, P, P, C.c_uint64,
+                                       C.c_uint32, P, P, P]
+    lib.gq_dequantize_accumulate_layers.argtypes = [
+        D, i64, i32, P, i32, C.POINTER(P), C.POINTER(P), C.c_float, C.c_float,
+        P, P]
     lib.gq_strerror.argtypes = [C.c_int]
     lib.gq_strerror.restype = C.c_char_p
     lib.gq_version.argtypes = []
@@ -209,6 +215,58 @@ def gq_dequantize_accumulate(d: gq_desc, n: int,
     _check(_lib.gq_dequantize_accumulate(
         C.byref(d), n, W, cp, mp, alpha, beta, _ptr(out, torch.float32, "out"),
         _stream(stream, out)), "gq_dequantize_accumulate")
+
+
+def _offsets(off: torch.Tensor) -> int:
+    if off.dim() != 1 or off.numel() < 2:
+        raise ValueError("layer_offsets: a 1-D tensor of nl + 1 >= 2 entries")
+    return _ptr(off, torch.int64, "layer_offsets")
+
+
+def gq_quantize_layers(d: gq_desc, layer_offsets: torch.Tensor,
+                       g: torch.Tensor, e: torch.Tensor | None, seed: int,
+                       step: int, codes: torch.Tensor, meta: torch.Tensor,
+                       stream=None) -> None:
+    """Per-layer scale: layer_offsets is an int64 device tensor of nl + 1
+    flat offsets; meta receives nl floats."""
+    if e is not None and e.numel() != g.numel():
+        raise ValueError("e must have g's size")
+    op = _offsets(layer_offsets)
+    nl = layer_offsets.numel() - 1
+    _, cap, _ = gq_payload_size(d, g.numel())
+    _need(codes, cap, "codes")
+    _need(meta, nl, "meta")
+    _check(_lib.gq_quantize_layers(
+        C.byref(d), g.numel(), nl, op, _ptr(g, torch.float32, "g"),
+        _ptr(e, torch.float32, "e"), seed, step,
+        _ptr(codes, torch.uint8, "codes"), _ptr(meta, torch.float32, "meta"),
+        _stream(stream, g)), "gq_quantize_layers")
+
+
+def gq_dequantize_accumulate_layers(d: gq_desc, n: int,
+                                    layer_offsets: torch.Tensor,
+                                    codes: Sequence[torch.Tensor],
+                                    meta: Sequence[torch.Tensor],
+                                    alpha: float, beta: float,
+                                    out: torch.Tensor, stream=None) -> None:
+    W = len(codes)
+    if len(meta) != W:
+        raise ValueError("codes and meta must have the same length")
+    if out.numel() < n:
+        raise ValueError("out is smaller than n")
+    op = _offsets(layer_offsets)
+    nl = layer_offsets.numel() - 1
+    if 1 <= W <= GQ_MAX_PAYLOADS:
+        cb, _, _ = gq_payload_size(d, n)
+        for c, m in zip(codes, meta):
+            _need(c, cb, "codes")
+            _need(m, nl, "meta")
+    cp = (C.c_void_p * max(W, 1))(*[_ptr(c, torch.uint8, "codes") for c in codes])
+    mp = (C.c_void_p * max(W, 1))(*[_ptr(m, torch.float32, "meta") for m in meta])
+    _check(_lib.gq_dequantize_accumulate_layers(
+        C.byref(d), n, nl, op, W, cp, mp, alpha, beta,
+        _ptr(out, torch.float32, "out"), _stream(stream, out)),
+        "gq_dequantize_accumulate_layers")
 
 
 # ---------------------------------------------------------------------------

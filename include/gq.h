@@ -160,6 +160,36 @@ int gq_dequantize_accumulate(const gq_desc* desc, int64_t n, int32_t W,
                              const float* const* meta, float alpha, float beta,
                              float* out, void* stream);
 
+/* Per-layer scale ("Gradient Quantization" glossary, ternary paragraph:
+ * TernGrad keeps one scaling factor per layer).  The gradient is the
+ * concatenation of nl >= 1 layers: layer l = elements
+ * [layer_offsets[l], layer_offsets[l+1]) of the flat array, with
+ * layer_offsets a DEVICE array of nl + 1 int64 values, 8-byte aligned,
+ * layer_offsets[0] = 0, layer_offsets[nl] = n, non-decreasing (empty layers
+ * allowed).  Each layer is one bucket of GQ_UNIFORM whatever its size:
+ * meta holds nl floats, meta[l] = max |p| over layer l (0 if empty), and
+ * every code is rounded on its own layer's grid exactly as in gq_quantize.
+ * Codes, Philox counter (the flat element index) and dense layout are
+ * those of gq_quantize for the flat array.  desc->scheme must be
+ * GQ_UNIFORM (GQ_EUNSUPPORTED otherwise; GQ_FLAG_DENSE and GQ_FLAG_NEAREST
+ * apply, desc->bucket is not used but must be valid).  The offsets are not
+ * read on the host: other contents give unspecified outputs but never
+ * out-of-bounds accesses.  Two passes over g (and e): the layer maxima
+ * first (meta is zeroed by the call), then rounding, packing and the
+ * residual.  meta, codes and e must not overlap layer_offsets or g. */
+int gq_quantize_layers(const gq_desc* desc, int64_t n, int32_t nl,
+                       const int64_t* layer_offsets, const float* g, float* e,
+                       uint64_t seed, uint32_t step, uint8_t* codes,
+                       float* meta, void* stream);
+
+/* gq_dequantize_accumulate for payloads written by gq_quantize_layers with
+ * the same desc, n and layer layout (meta[w] holds nl floats). */
+int gq_dequantize_accumulate_layers(const gq_desc* desc, int64_t n, int32_t nl,
+                                    const int64_t* layer_offsets, int32_t W,
+                                    const uint8_t* const* codes,
+                                    const float* const* meta, float alpha,
+                                    float beta, float* out, void* stream);
+
 /* Static description of a status code. */
 const char* gq_strerror(int status);
 

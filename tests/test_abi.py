@@ -147,3 +147,34 @@ def test_nearest_flag_rules(gq):
         with pytest.raises(gq.GQError) as ex:
             gq.gq_payload_size(gq.desc(scheme, 512, flags=N), 100)
         assert ex.value.status == gq.GQ_EUNSUPPORTED
+
+
+def test_layer_entry_points_validate_before_launch(gq):
+    """Per-layer scale: argument errors are found on the host (the offsets
+    array itself is device memory and is not read there)."""
+    L = gq.lib()
+    P = C.c_void_p
+    fake = 1 << 20          # aligned, never dereferenced: validation fails first
+    d = gq.desc(gq.GQ_UNIFORM, 512, 1)
+    q = L.gq_quantize_layers
+    assert q(C.byref(gq.desc(gq.GQ_ORQ, 512, levels=5)), 100, 2, fake, fake * 2,
+             None, 0, 0, fake * 3, fake * 4, None) == gq.GQ_EUNSUPPORTED
+    assert q(C.byref(gq.desc(gq.GQ_BIN_SIGN, 512)), 100, 2, fake, fake * 2,
+             None, 0, 0, fake * 3, fake * 4, None) == gq.GQ_EUNSUPPORTED
+    assert q(C.byref(d), 100, 0, fake, fake * 2, None, 0, 0, fake * 3,
+             fake * 4, None) == gq.GQ_EINVAL                    # nl < 1
+    assert q(C.byref(d), 100, 2, None, fake * 2, None, 0, 0, fake * 3,
+             fake * 4, None) == gq.GQ_EINVAL                    # no offsets
+    assert q(C.byref(d), 100, 2, fake + 4, fake * 2, None, 0, 0, fake * 3,
+             fake * 4, None) == gq.GQ_EINVAL                    # misaligned
+    assert q(C.byref(d), 100, 2, fake * 4, fake * 2, None, 0, 0, fake * 3,
+             fake * 4, None) == gq.GQ_EINVAL                    # overlaps meta
+    cp = (P * 17)(*([fake * 2] * 17))
+    mp = (P * 17)(*([fake * 3] * 17))
+    dq = L.gq_dequantize_accumulate_layers
+    assert dq(C.byref(d), 100, 2, fake, 17, cp, mp, 1.0, 0.0, fake * 4,
+              None) == gq.GQ_ETOOMANY
+    assert dq(C.byref(d), 100, 2, fake, 0, cp, mp, 1.0, 0.0, fake * 4,
+              None) == gq.GQ_EINVAL
+    assert dq(C.byref(gq.desc(gq.GQ_ORQ, 512, levels=3)), 100, 2, fake, 1, cp,
+              mp, 1.0, 0.0, fake * 4, None) == gq.GQ_EUNSUPPORTED
