@@ -34,6 +34,7 @@ UNIFORM, BIN_SIGN, BIN_OPT, ORQ = 0, 1, 2, 3
 FLAG_CLIP = 1
 FLAG_DENSE = 2
 FLAG_NEAREST = 4
+FLAG_BISECT = 8
 
 _lib = None
 

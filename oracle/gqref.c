@@ -438,6 +438,99 @@ static void orq_greedy(const float *y, int64_t nj, int L, float *lev,
   free(B);
 }
 
+/* ORQ levels by recursive bisection, the other reading of the greedy
+ * selection that also yields the 3 / 5 / 9 levels of the review's
+ * experiments (2^k + 1): rounds in which every interval between adjacent
+ * levels receives its own best level c (the G(c) above, restricted to that
+ * interval) at once.  When a full round would pass L levels, only the
+ * round's candidates with the largest G are inserted (ties: smaller c).
+ * Starts, degenerate buckets and the fill with max are as in orq_greedy.
+ * The near-tie record covers the best and second-best candidate of each
+ * interval, and in a partial round the last candidate taken and the first
+ * left out. */
+static void orq_bisect(const float *y, int64_t nj, int L, float *lev,
+                       uint8_t *tie) {
+  int cnt = 2;
+  lev[0] = y[0];
+  lev[1] = y[nj - 1];
+  if (y[0] == y[nj - 1]) {
+    for (int j = 0; j < L; ++j) lev[j] = y[0];
+    return;
+  }
+  double *A = (double *)malloc((size_t)nj * sizeof(double));
+  double *B = (double *)malloc((size_t)nj * sizeof(double));
+  float cand[16];
+  double gain[16];
+  while (cnt < L) {
+    int m = 0;
+    int64_t lo = 0;
+    for (int j = 0; j + 1 < cnt; ++j) {
+      float a = lev[j], b = lev[j + 1];
+      if (!(a < b)) continue;
+      while (lo < nj && !(y[lo] > a)) ++lo;
+      int64_t hi = lo;
+      while (hi < nj && y[hi] < b) ++hi; /* interior values are y[lo..hi) */
+      if (hi == lo) continue;
+      nsum acc = {0, 0};
+      for (int64_t t = lo; t < hi; ++t) {
+        nadd(&acc, (double)y[t] - (double)a);
+        A[t] = nval(&acc);
+      }
+      acc.s = acc.c = 0.0;
+      for (int64_t t = hi - 1; t >= lo; --t) {
+        B[t] = nval(&acc);
+        nadd(&acc, (double)b - (double)y[t]);
+      }
+      double best = -1.0, second = -1.0;
+      float bestc = 0.0f;
+      for (int64_t t = lo; t < hi; ++t) {
+        if (t + 1 < hi && y[t + 1] == y[t]) continue;
+        double c = (double)y[t];
+        double G = ((double)b - c) * A[t] + (c - (double)a) * B[t];
+        if (G > best) {
+          second = best;
+          best = G;
+          bestc = y[t];
+        } else if (G > second) {
+          second = G;
+        }
+      }
+      if (tie && second >= best * (1.0 - TIE_REL)) *tie = 1;
+      cand[m] = bestc;
+      gain[m] = best;
+      ++m;
+      lo = hi;
+    }
+    if (m == 0) {
+      for (int j = cnt; j < L; ++j) lev[j] = y[nj - 1];
+      break;
+    }
+    int room = L - cnt;
+    if (m > room) {
+      /* keep the room largest gains (ties: smaller c, i.e. earlier) */
+      for (int a = 0; a < m; ++a)
+        for (int b = a + 1; b < m; ++b)
+          if (gain[b] > gain[a]) {
+            double tg = gain[a]; gain[a] = gain[b]; gain[b] = tg;
+            float tc = cand[a]; cand[a] = cand[b]; cand[b] = tc;
+          }
+      if (tie && gain[room] >= gain[room - 1] * (1.0 - TIE_REL)) *tie = 1;
+      m = room;
+    }
+    for (int k = 0; k < m; ++k) {
+      int pos = cnt;
+      while (pos > 0 && lev[pos - 1] > cand[k]) {
+        lev[pos] = lev[pos - 1];
+        --pos;
+      }
+      lev[pos] = cand[k];
+      ++cnt;
+    }
+  }
+  free(A);
+  free(B);
+}
+
 /* ========================================================== per bucket == */
 typedef struct {
   int scheme, d, s, L, flags, bits, k;
@@ -472,7 +565,8 @@ static void select_bucket(const params *pr, const float *p, int64_t nj,
         memcpy(v, p, (size_t)nj * sizeof(float));
       }
       float *y = sorted_copy(v, nj);
-      orq_greedy(y, nj, pr->L, meta, tie);
+      if (pr->flags & 8) orq_bisect(y, nj, pr->L, meta, tie);
+      else orq_greedy(y, nj, pr->L, meta, tie);
       free(y);
       if (!pc) free(v);
       break;
@@ -619,6 +713,7 @@ static int make_params(params *pr, int scheme, int d, int s, int L, int flags,
   pr->dense = (flags & 2) ? 1 : 0;
   pr->nearest = (flags & 4) ? 1 : 0;
   if (pr->nearest && scheme != UNIFORM && scheme != ORQ) return -1;
+  if ((flags & 8) && scheme != ORQ) return -1; /* bisection: ORQ only */
   pr->A = scheme == UNIFORM ? 2 * s + 1 : (scheme == ORQ ? L : 2);
   pr->w = pr->dense ? gqref_dense_width(pr->A) : 0;
   if (pr->dense && pr->w < 0) return -1;

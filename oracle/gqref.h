@@ -25,7 +25,8 @@
  * Scheme numbers: 0 uniform (QSGD / ternary / INT8), 1 two-level sign split,
  * 2 two-level optimal split (BinGrad-b), 3 ORQ.  flags bit 0 = clip, bit 1 =
  * dense packing (digits: c + s for the uniform scheme, the code otherwise),
- * bit 2 = deterministic rounding to the nearest level (uniform and ORQ).
+ * bit 2 = deterministic rounding to the nearest level (uniform and ORQ),
+ * bit 3 = ORQ levels by recursive bisection instead of one at a time.
  *
  * Return value: 0 on success, -1 on an invalid argument.
  */
