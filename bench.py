@@ -417,6 +417,16 @@ def suite_orq(torch, gq, WL, stream, tb, reps):
                                  host, dict(scheme=3, d=512, L=L, flags=clip,
                                             clip_sigma=3.0), False, seed=3)))
             del c, m, q
+    # the recursive-bisection reading of the level selection
+    for L in (5, 9):
+        d = gq.desc(gq.GQ_ORQ, 512, levels=L, flags=gq.GQ_FLAG_BISECT)
+        c, m = gq.alloc_payload(d, n)
+        q = gq.PreparedQuantize(d, g, None, c, m, stream)
+        ms = tb(lambda i: q(3, 0), max(3, reps // 2))
+        out.append(entry(f"quantize orq L={L} bisect d=512 n={n}", ms,
+                         quant_bytes(gq.gq_code_bits(d), L, 512, n, False), n,
+                         bound="alu"))
+        del c, m, q
     return out
 
 

@@ -32,7 +32,8 @@ int check_desc(const gq_desc* d, gq::LaunchDesc* L) {
   if (d == nullptr) return GQ_EINVAL;
   const int b = d->bucket;
   if (b < 64 || b > 32768 || (b & (b - 1)) != 0) return GQ_EINVAL;
-  if (d->flags & ~(GQ_FLAG_CLIP | GQ_FLAG_DENSE | GQ_FLAG_NEAREST)) return GQ_EINVAL;
+  if (d->flags & ~(GQ_FLAG_CLIP | GQ_FLAG_DENSE | GQ_FLAG_NEAREST | GQ_FLAG_BISECT))
+    return GQ_EINVAL;
   L->scheme = d->scheme;
   L->d = b;
   L->s = d->s;
@@ -65,6 +66,8 @@ int check_desc(const gq_desc* d, gq::LaunchDesc* L) {
     if (!(d->clip_sigma > 0.f) || !std::isfinite(d->clip_sigma)) return GQ_EINVAL;
   }
   if ((d->flags & GQ_FLAG_NEAREST) && d->scheme != GQ_UNIFORM && d->scheme != GQ_ORQ)
+    return GQ_EUNSUPPORTED;
+  if ((d->flags & GQ_FLAG_BISECT) && (d->scheme != GQ_ORQ || b > 512))
     return GQ_EUNSUPPORTED;
   L->dense = 0;
   L->A = L->W = 0;

@@ -740,7 +740,7 @@ __device__ __forceinline__ void store_vec(float* __restrict__ a, int64_t i,
   }
 }
 
-template <int SCHEME, int BITS, int D>
+template <int SCHEME, int BITS, int D, bool BISECT>
 __global__ __launch_bounds__(kGroupThreads)
 void k_wave_sort_quant(
     int64_t n, int64_t nb, const float* __restrict__ g, float* __restrict__ e,
@@ -903,6 +903,8 @@ void k_wave_sort_quant(
     // Each sorted value keeps its segment (index of the last level <= y)
     // and the segment's end points (a, b); inserting c into (a0, b0) moves
     // every y >= c one segment up and splits (a0, b0) into (a0, c), (c, b0).
+    // One level per step (greedy), or with GQ_FLAG_BISECT one per segment
+    // per round (recursive bisection).
     const float ymin = wave_at<E, G>(y, 0), ymax = wave_at<E, G>(y, nj - 1);
 #pragma unroll
     for (int j = 0; j < 16; ++j) lv[j] = __builtin_inff();
@@ -965,17 +967,18 @@ void k_wave_sort_quant(
       const double cb = group_seg_carry<G, true>(fb, sb, lane);
       double best = -1.0;
       int bestk = 0x7fffffff;
+      // Gs[m]: first the sum of (b - y) over the values after m in m's
+      // segment, then m's gain G (-1 for a value that is no candidate)
+      double Gs[E];
       {
-        // Bv[m]: sum of (b - y) over the values after m in m's segment
-        double Bv[E];
         double run = cb;
 #pragma unroll
         for (int m = E - 1; m >= 0; --m) {
           if (tail(m)) {
-            Bv[m] = 0.0;
+            Gs[m] = 0.0;
             run = vb(m);
           } else {
-            Bv[m] = run;
+            Gs[m] = run;
             run = run + vb(m);
           }
         }
@@ -988,27 +991,21 @@ void k_wave_sort_quant(
           const float ynext = (m + 1 < E) ? y[m + 1] : y_next_run;
           const bool cand = pos < nj && seg[m] + 1 < cnt && yv > a_of[m] &&
                             (pos + 1 >= nj || ynext != yv);
+          double Gv = -1.0;
           if (cand) {
             const double c = (double)yv;
-            const double Gv = ((double)b_of[m] - c) * A + (c - (double)a_of[m]) * Bv[m];
+            Gv = ((double)b_of[m] - c) * A + (c - (double)a_of[m]) * Gs[m];
             if (Gv > best) {
               best = Gv;
               bestk = pos;
             }
           }
+          Gs[m] = Gv;
         }
       }
-      double bestG;
-      const int kstar = group_argmax<G>(best, bestk, &bestG);
-      if (bestG < 0.0) {
-        // fewer distinct values than levels: repeat the maximum
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (j >= cnt && j < L) lv[j] = ymax;
-        cnt = L;
-      } else {
-        // insert c after every level <= c (levels stay ascending)
-        const float c = wave_at<E, G>(y, kstar);
+      // insert c after every level <= c (levels stay ascending) and update
+      // the segment state of every value
+      auto insert_level = [&](float c) {
         int ins = 0;
 #pragma unroll
         for (int j = 0; j < 16; ++j) ins += (lv[j] <= c) ? 1 : 0;
@@ -1029,6 +1026,79 @@ void k_wave_sort_quant(
           seg[m] += up ? 1 : 0;
         }
         ++cnt;
+      };
+      auto fill_with_max = [&]() {
+        // fewer distinct values than levels: repeat the maximum
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (j >= cnt && j < L) lv[j] = ymax;
+        cnt = L;
+      };
+      if constexpr (!BISECT) {
+        double bestG;
+        const int kstar = group_argmax<G>(best, bestk, &bestG);
+        if (bestG < 0.0) fill_with_max();
+        else insert_level(wave_at<E, G>(y, kstar));
+      } else {
+        // Recursive bisection: the best value of every segment, segment j
+        // kept by lane j mod G in slot j / G; then the round's candidates
+        // are inserted, all of them or (when they would pass L levels) the
+        // largest gains first, equal gains by position.
+        constexpr int NSL = (15 + G - 1) / G;
+        double sg[NSL];
+        int sk[NSL];
+#pragma unroll
+        for (int t = 0; t < NSL; ++t) {
+          sg[t] = -1.0;
+          sk[t] = 0x7fffffff;
+        }
+        const int nseg = cnt - 1;
+        for (int j = 0; j < nseg; ++j) {
+          double bj = -1.0;
+          int kj = 0x7fffffff;
+#pragma unroll
+          for (int m = 0; m < E; ++m)
+            if (seg[m] == j && Gs[m] > bj) {
+              bj = Gs[m];
+              kj = r0 + m;
+            }
+          double bg;
+          const int kg = group_argmax<G>(bj, kj, &bg);
+#pragma unroll
+          for (int t = 0; t < NSL; ++t)
+            if (j == lane + G * t && bg >= 0.0) {
+              sg[t] = bg;
+              sk[t] = kg;
+            }
+        }
+        int have = 0;
+#pragma unroll
+        for (int t = 0; t < NSL; ++t) have += sg[t] >= 0.0 ? 1 : 0;
+        have = group_sum_i<G>(have);
+        if (have == 0) {
+          fill_with_max();
+        } else {
+          const int take = have < L - cnt ? have : L - cnt;
+          for (int t2 = 0; t2 < take; ++t2) {
+            double lb = -1.0;
+            int lk = 0x7fffffff;
+#pragma unroll
+            for (int t = 0; t < NSL; ++t)
+              if (sg[t] > lb || (sg[t] == lb && sk[t] < lk)) {
+                lb = sg[t];
+                lk = sk[t];
+              }
+            double gb;
+            const int kb = group_argmax<G>(lb, lk, &gb);
+#pragma unroll
+            for (int t = 0; t < NSL; ++t)
+              if (sk[t] == kb) {
+                sg[t] = -1.0;
+                sk[t] = 0x7fffffff;
+              }
+            insert_level(wave_at<E, G>(y, kb));
+          }
+        }
       }
     }
 #pragma unroll
@@ -1146,10 +1216,22 @@ int launch_sort_one(int64_t n, const float* g, float* e, uint64_t seed,
   if constexpr (D <= 512) {
     constexpr int per_block = kGroupThreads / WaveCfg<D>::G;
     const int64_t blocks = (nb + per_block - 1) / per_block;
-    hipLaunchKernelGGL((k_wave_sort_quant<SCHEME, BITS, D>), dim3((uint32_t)blocks),
-                       dim3(kGroupThreads), 0, st, n, nb, g, e,
-                       (uint32_t)seed, (uint32_t)(seed >> 32), step, L, flags,
-                       clip_sigma, codes, meta, code_bytes, A4, W);
+    bool bisect = false;
+    if constexpr (SCHEME == ORQ) {
+      if (flags & GQ_FLAG_BISECT) {
+        bisect = true;
+        hipLaunchKernelGGL((k_wave_sort_quant<SCHEME, BITS, D, true>),
+                           dim3((uint32_t)blocks), dim3(kGroupThreads), 0, st,
+                           n, nb, g, e, (uint32_t)seed, (uint32_t)(seed >> 32),
+                           step, L, flags, clip_sigma, codes, meta, code_bytes,
+                           A4, W);
+      }
+    }
+    if (!bisect)
+      hipLaunchKernelGGL((k_wave_sort_quant<SCHEME, BITS, D, false>),
+                         dim3((uint32_t)blocks), dim3(kGroupThreads), 0, st, n,
+                         nb, g, e, (uint32_t)seed, (uint32_t)(seed >> 32), step,
+                         L, flags, clip_sigma, codes, meta, code_bytes, A4, W);
   } else {
     hipLaunchKernelGGL((k_sort_quant<SCHEME, BITS, D>), dim3((uint32_t)nb),
                        dim3(SortCfg<D>::T), 0, st, n, g, e, (uint32_t)seed,
@@ -1191,7 +1273,7 @@ int sort_dispatch_d(int d, int64_t n, const float* g, float* e, uint64_t seed,
 int launch_sort_quant(const LaunchDesc& L, int64_t n, const float* g, float* e,
                       uint64_t seed, uint32_t step, uint8_t* codes, float* meta,
                       int64_t code_bytes, hipStream_t st) {
-  const int flags = L.flags & (GQ_FLAG_CLIP | GQ_FLAG_NEAREST);
+  const int flags = L.flags & (GQ_FLAG_CLIP | GQ_FLAG_NEAREST | GQ_FLAG_BISECT);
   if (L.scheme == BIN_OPT)
     return sort_dispatch_d<BIN_OPT, 1>(L.d, n, g, e, seed, step, 2, 0, 0.f,
                                        codes, meta, code_bytes, 0u, 0, st);

@@ -21,6 +21,7 @@ GQ_UNIFORM, GQ_BIN_SIGN, GQ_BIN_OPT, GQ_ORQ = 0, 1, 2, 3
 GQ_FLAG_CLIP = 1
 GQ_FLAG_DENSE = 2
 GQ_FLAG_NEAREST = 4
+GQ_FLAG_BISECT = 8
 GQ_OK, GQ_EINVAL, GQ_EUNSUPPORTED, GQ_ELAUNCH, GQ_ETOOMANY = 0, -1, -2, -3, -4
 GQ_MAX_PAYLOADS = 16
 

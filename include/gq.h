@@ -91,8 +91,16 @@ typedef enum {
  * magnitude for GQ_UNIFORM).  This is the random rule with u = 1/2 for every
  * element; seed and step are ignored.  The two-level schemes are already
  * deterministic and return GQ_EUNSUPPORTED for it.  Payloads are read the
- * same way with or without the flag. */
-enum { GQ_FLAG_CLIP = 1, GQ_FLAG_DENSE = 2, GQ_FLAG_NEAREST = 4 };
+ * same way with or without the flag.
+ * GQ_FLAG_BISECT (GQ_ORQ with d <= 512): the levels by recursive bisection,
+ * the other reading of the review's greedy selection (same section; its
+ * 3 / 5 / 9 levels are 2^k + 1): rounds in which every interval between
+ * adjacent levels receives its own best level at once; a round that would
+ * pass L levels inserts its largest gains first (equal gains: the smaller
+ * value).  Without the flag one level is inserted per step, the one with
+ * the largest gain over all intervals.  GQ_EUNSUPPORTED for other schemes
+ * and for d > 512. */
+enum { GQ_FLAG_CLIP = 1, GQ_FLAG_DENSE = 2, GQ_FLAG_NEAREST = 4, GQ_FLAG_BISECT = 8 };
 
 typedef struct {
   int32_t scheme;     /* gq_scheme                                          */

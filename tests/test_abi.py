@@ -64,7 +64,8 @@ def test_payload_sizes(gq):
     (dict(bucket=63), -1), (dict(bucket=96), -1), (dict(bucket=65536), -1),
     (dict(bucket=32), -1), (dict(s=0), -2), (dict(s=128), -2),
     (dict(scheme=3, levels=1), -2), (dict(scheme=3, levels=17), -2),
-    (dict(scheme=7), -2), (dict(flags=8), -1), (dict(flags=1), -2),
+    (dict(scheme=7), -2), (dict(flags=16), -1), (dict(flags=1), -2),
+    (dict(flags=8), -2), (dict(scheme=3, bucket=1024, flags=8), -2),
     (dict(scheme=1, flags=4), -2), (dict(scheme=2, flags=4), -2),
     (dict(s=8, flags=2), -2), (dict(scheme=3, bucket=256, flags=2), -2),
     (dict(scheme=3, flags=1, clip_sigma=0.0), -1),
@@ -109,7 +110,7 @@ def test_dense_flag_rules_and_sizes(gq):
         gq.gq_payload_size(gq.desc(gq.GQ_ORQ, 256, levels=9, flags=D), 100)
     assert ex.value.status == gq.GQ_EUNSUPPORTED
     with pytest.raises(gq.GQError) as ex:
-        gq.gq_payload_size(gq.desc(gq.GQ_UNIFORM, 512, s=1, flags=8), 100)
+        gq.gq_payload_size(gq.desc(gq.GQ_UNIFORM, 512, s=1, flags=16), 100)
     assert ex.value.status == gq.GQ_EINVAL
     # sizes agree with the oracle's dense layout
     for scheme, d, s, L in [(0, 64, 1, 5), (0, 512, 4, 5), (0, 4096, 7, 5),
@@ -178,3 +179,19 @@ def test_layer_entry_points_validate_before_launch(gq):
               None) == gq.GQ_EINVAL
     assert dq(C.byref(gq.desc(gq.GQ_ORQ, 512, levels=3)), 100, 2, fake, 1, cp,
               mp, 1.0, 0.0, fake * 4, None) == gq.GQ_EUNSUPPORTED
+
+
+def test_bisect_flag_rules(gq):
+    """Recursive bisection: ORQ with d <= 512 only; the layout is unchanged."""
+    Bf = gq.GQ_FLAG_BISECT
+    assert Bf == 8
+    for d in (64, 512):
+        a = gq.gq_payload_size(gq.desc(gq.GQ_ORQ, d, levels=9, flags=Bf), 5000)
+        b = gq.gq_payload_size(gq.desc(gq.GQ_ORQ, d, levels=9), 5000)
+        assert a == b
+    for kw in (dict(scheme=gq.GQ_ORQ, bucket=1024, levels=5),
+               dict(scheme=gq.GQ_UNIFORM, bucket=512),
+               dict(scheme=gq.GQ_BIN_OPT, bucket=512)):
+        with pytest.raises(gq.GQError) as ex:
+            gq.gq_payload_size(gq.desc(**kw, flags=Bf), 100)
+        assert ex.value.status == gq.GQ_EUNSUPPORTED

@@ -1,0 +1,67 @@
+"""GPU parity of ORQ levels by recursive bisection (GQ_FLAG_BISECT, d <=
+512) against the oracle: every bucket size of the lane-group kernel, L from
+3 to 16 (full rounds and rounds that keep their largest gains), clipping,
+dense packing, nearest rounding, error feedback, a skewed bucket where
+bisection and the greedy differ, and the 100M ORQ-9 gradient on sampled
+bucket runs."""
+import numpy as np
+import pytest
+
+import oracle as O
+from communication_efficient_gradient_amd import workloads as WL
+from tests.parity import sample_runs, say
+from tests.test_gpu_small import check_quantize, dev, run_gpu  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+
+B = O.FLAG_BISECT
+
+
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+@pytest.mark.parametrize("L", [3, 5, 6, 9, 12, 16])
+@pytest.mark.parametrize("clip", [0, O.FLAG_CLIP])
+def test_bisect_every_bucket(dev, d, L, clip):
+    n = 3 * d + 45
+    g = WL.orq_gradient(n)
+    check_quantize(dev, O.Desc(O.ORQ, d, L=L, flags=B | clip, clip_sigma=3.0),
+                   g, None, seed=L)
+
+
+@pytest.mark.parametrize("flags", [B | O.FLAG_DENSE, B | O.FLAG_NEAREST,
+                                   B | O.FLAG_DENSE | O.FLAG_NEAREST])
+def test_bisect_with_other_flags(dev, flags):
+    n = 4 * 512 + 7
+    g = WL.small_mixture(n, seed=flags, kind="heavy")
+    e = WL.small_mixture(n, seed=flags + 1) * np.float32(0.05)
+    for L in (5, 9):
+        check_quantize(dev, O.Desc(O.ORQ, 512, L=L, flags=flags), g, e, seed=2, step=3)
+
+
+def test_skewed_buckets_where_the_readings_differ(dev):
+    rng = np.random.default_rng(1)
+    blocks = []
+    for k in range(8):
+        blocks.append(np.concatenate([rng.uniform(0, 1, 480),
+                                      rng.uniform(-10, 0, 32)]))
+    g = np.concatenate(blocks).astype(np.float32)
+    desc = O.Desc(O.ORQ, 512, L=5, flags=B)
+    _, mb, _, _ = O.quantize(desc, g)
+    _, mg, _, _ = O.quantize(O.Desc(O.ORQ, 512, L=5), g)
+    assert not np.array_equal(mb, mg)
+    check_quantize(dev, desc, g, None, seed=4)
+
+
+def test_orq9_bisect_100m_sampled(dev):
+    gq, torch = dev
+    d = O.Desc(O.ORQ, 512, L=9, flags=B)
+    n = WL.ORQ_N
+    say(f"orq bisect L=9 n={n}")
+    g = WL.orq_gradient()
+    G = torch.from_numpy(g).cuda()
+    gd = gq.desc(d.scheme, d.d, d.s, d.L, d.flags, d.clip_sigma)
+    codes, meta = gq.alloc_payload(gd, n)
+    gq.gq_quantize(gd, G, None, 3, 0, codes, meta)
+    torch.cuda.synchronize()
+    from tests.test_gpu_full import check_runs
+    check_runs(d, n, lambda lo, hi: g[lo:hi], None, codes, meta, None, 3, 0,
+               sample_runs(d.nb(n), 12, 16, seed=99))
