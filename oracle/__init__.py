@@ -69,6 +69,12 @@ def lib():
         L.gqref_dequantize_accumulate_layers.argtypes = [
             i32, i32, i64, i32, C.c_void_p, i32, C.POINTER(C.c_void_p),
             C.POINTER(C.c_void_p), C.c_float, C.c_float, fp]
+        L.gqref_topk_record_words.argtypes = [i32, i32, i32]
+        L.gqref_quantize_topk.argtypes = [i32, i32, i32, i32, i64, cfp, fp,
+                                          u64, u32, u8p, fp]
+        L.gqref_dequantize_accumulate_topk.argtypes = [
+            i32, i32, i32, i32, i64, i32, C.POINTER(C.c_void_p),
+            C.POINTER(C.c_void_p), C.c_float, C.c_float, fp]
         L.gqref_dense_width.argtypes = [i32]
         L.gqref_pack_dense.argtypes = [i32, i64, C.c_void_p, u8p]
         L.gqref_pack_dense.restype = None
@@ -268,6 +274,46 @@ def dequantize_accumulate_layers(desc: Desc, offsets, n: int, codes_list,
         beta, _ptr(out))
     if rc:
         raise ValueError("oracle dequantize_accumulate_layers: invalid arguments")
+    return out
+
+
+def topk_record_words(d: int, s: int, K: int) -> int:
+    return lib().gqref_topk_record_words(d, s, K)
+
+
+def quantize_topk(d: int, s: int, K: int, g, e=None, seed: int = 0,
+                  step: int = 0, flags: int = 0):
+    """Top-K + uniform quantization per bucket.  Returns (codes u8, meta
+    f32[nb], e_new or None)."""
+    g = _f32(g)
+    n = g.size
+    R = topk_record_words(d, s, K)
+    if R < 0:
+        raise ValueError("oracle quantize_topk: invalid arguments")
+    nb = (n + d - 1) // d
+    e_new = None if e is None else _f32(e).copy()
+    codes = np.zeros(nb * R * 4, dtype=np.uint8)
+    meta = np.zeros(nb, dtype=np.float32)
+    rc = lib().gqref_quantize_topk(d, s, K, flags, n, _ptr(g), _ptr(e_new),
+                                   seed, step, _ptr(codes), _ptr(meta))
+    if rc:
+        raise ValueError("oracle quantize_topk: invalid arguments")
+    return codes, meta, e_new
+
+
+def dequantize_accumulate_topk(d: int, s: int, K: int, n: int, codes_list,
+                               meta_list, alpha: float = 1.0,
+                               beta: float = 0.0, out=None, flags: int = 0):
+    W = len(codes_list)
+    cl = [np.ascontiguousarray(c, dtype=np.uint8) for c in codes_list]
+    ml = [_f32(m) for m in meta_list]
+    out = np.zeros(n, dtype=np.float32) if out is None else _f32(out).copy()
+    cp = (C.c_void_p * W)(*[c.ctypes.data for c in cl])
+    mp = (C.c_void_p * W)(*[m.ctypes.data for m in ml])
+    rc = lib().gqref_dequantize_accumulate_topk(d, s, K, flags, n, W, cp, mp,
+                                                alpha, beta, _ptr(out))
+    if rc:
+        raise ValueError("oracle dequantize_accumulate_topk: invalid arguments")
     return out
 
 

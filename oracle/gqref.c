@@ -908,6 +908,121 @@ int gqref_dequantize_accumulate_layers(int s, int flags, int64_t n, int nl,
   return 0;
 }
 
+/* --------------------------------------------------------------- top-k --
+ * Top-K sparsification combined with quantization ("gradient quantization
+ * for communication" glossary, §Quantization Schemes: send only the largest
+ * gradients, combined with quantization; error feedback keeps the rest).
+ * Per bucket j (n_j real elements) the k_j = min(K, n_j) elements of largest
+ * |p| are sent (equal magnitudes: the lower index first); their values are
+ * rounded on the bucket's uniform grid exactly as gqref_quantize does for
+ * the uniform scheme (M_j = max |p|, s levels per sign, u of the element's
+ * flat index), the others count as 0.  Payload: meta[j] = M_j; codes: a
+ * record of R = ceil(K (ib + b) / 32) 32-bit words per bucket (ib = log2 d
+ * index bits, b the uniform code width), record j at byte 4 R j; slot t
+ * (the kept elements in increasing index) holds the index within the
+ * bucket, then the code (two's complement), LSB first from bit t (ib + b);
+ * unused slots and pad bits are 0. */
+int gqref_topk_record_words(int d, int s, int K) {
+  int b = gqref_bits(UNIFORM, s, 2);
+  if (b < 0 || d < 64 || (d & (d - 1)) || K < 1 || K > d) return -1;
+  int ib = ceil_log2(d);
+  return (int)(((int64_t)K * (ib + b) + 31) / 32);
+}
+
+typedef struct {
+  float a;
+  int64_t i;
+} mag_idx;
+
+static int by_mag_then_index(const void *x, const void *y) {
+  const mag_idx *p = (const mag_idx *)x, *q = (const mag_idx *)y;
+  if (p->a > q->a) return -1;
+  if (p->a < q->a) return 1;
+  return (p->i > q->i) - (p->i < q->i);
+}
+
+int gqref_quantize_topk(int d, int s, int K, int flags, int64_t n,
+                        const float *g, float *e, uint64_t seed, uint32_t step,
+                        uint8_t *codes, float *meta) {
+  params pr;
+  int R = gqref_topk_record_words(d, s, K);
+  if (R < 0 || n < 1 || (flags & ~4) || !g || !codes || !meta) return -1;
+  if (make_params(&pr, UNIFORM, d, s, 2, flags, 0.f)) return -1;
+  int ib = ceil_log2(d), b = pr.bits;
+  int64_t nb = (n + d - 1) / d;
+  memset(codes, 0, (size_t)(nb * R * 4));
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < nb; ++j) {
+    int64_t lo = j * d, nj = (n - lo < d) ? n - lo : d;
+    int64_t k = nj < K ? nj : K;
+    float *p = (float *)malloc((size_t)nj * sizeof(float));
+    mag_idx *o = (mag_idx *)malloc((size_t)nj * sizeof(mag_idx));
+    uint8_t *keep = (uint8_t *)calloc((size_t)nj, 1);
+    float M = 0.0f;
+    for (int64_t t = 0; t < nj; ++t) {
+      p[t] = e ? g[lo + t] + e[lo + t] : g[lo + t];
+      o[t].a = fabsf(p[t]);
+      o[t].i = t;
+      if (o[t].a > M) M = o[t].a;
+    }
+    meta[j] = M;
+    qsort(o, (size_t)nj, sizeof(mag_idx), by_mag_then_index);
+    for (int64_t t = 0; t < k; ++t) keep[o[t].i] = 1;
+    uint8_t *rec = codes + (size_t)j * R * 4;
+    int64_t slot = 0;
+    for (int64_t t = 0; t < nj; ++t) {
+      float xh = 0.0f;
+      if (keep[t]) {
+        int32_t c = code_uniform(&pr, p[t], M,
+                                 pr.nearest ? 0.0f : uniform_u(seed, step, lo + t));
+        uint64_t field = (uint64_t)t | ((uint64_t)((uint32_t)c & ((1u << b) - 1u)) << ib);
+        put_bits(rec, slot * (ib + b), ib + b, field);
+        ++slot;
+        xh = dequant_one(&pr, c, meta + j);
+      }
+      if (e) e[lo + t] = p[t] - xh;
+    }
+    free(p);
+    free(o);
+    free(keep);
+  }
+  return 0;
+}
+
+int gqref_dequantize_accumulate_topk(int d, int s, int K, int flags, int64_t n,
+                                     int W, const uint8_t *const *codes,
+                                     const float *const *meta, float alpha,
+                                     float beta, float *out) {
+  params pr;
+  int R = gqref_topk_record_words(d, s, K);
+  if (R < 0 || n < 1 || W < 1 || (flags & ~4)) return -1;
+  if (make_params(&pr, UNIFORM, d, s, 2, flags, 0.f)) return -1;
+  int ib = ceil_log2(d), b = pr.bits;
+  int64_t nb = (n + d - 1) / d;
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < nb; ++j) {
+    int64_t lo = j * d, nj = (n - lo < d) ? n - lo : d;
+    int64_t k = nj < K ? nj : K;
+    nsum *acc = (nsum *)calloc((size_t)nj, sizeof(nsum));
+    for (int w = 0; w < W; ++w) {
+      const uint8_t *rec = codes[w] + (size_t)j * R * 4;
+      for (int64_t t = 0; t < k; ++t) {
+        uint64_t field = get_bits(rec, t * (ib + b), ib + b);
+        int64_t idx = (int64_t)(field & ((1u << ib) - 1u));
+        int32_t c = sext((uint32_t)(field >> ib), b);
+        if (idx < nj) nadd(&acc[idx], (double)dequant_one(&pr, c, meta[w] + j));
+      }
+    }
+    for (int64_t t = 0; t < nj; ++t) {
+      double v = (double)alpha * nval(&acc[t]);
+      if (beta != 0.0f) v += (double)beta * (double)out[lo + t];
+      out[lo + t] = (float)v;
+    }
+    free(acc);
+  }
+  return 0;
+}
+
 void gqref_set_threads(int t) {
   if (t > 0) omp_set_num_threads(t);
 }

@@ -97,6 +97,21 @@ int gqref_dequantize_accumulate_layers(int s, int flags, int64_t n, int nl,
                                        const float *const *meta, float alpha,
                                        float beta, float *out);
 
+/* Top-K sparsification with quantization: per bucket the min(K, n_j)
+ * elements of largest |p| (ties: lower index) are rounded on the uniform
+ * grid of s levels per sign; the rest count as 0 (the residual keeps them).
+ * codes: nb records of gqref_topk_record_words(d, s, K) 32-bit words, slot t
+ * = (index within the bucket: log2 d bits, code: b bits), LSB first.
+ * meta: nb floats (max-abs).  flags: bit 2 (nearest) only. */
+int gqref_topk_record_words(int d, int s, int K);
+int gqref_quantize_topk(int d, int s, int K, int flags, int64_t n,
+                        const float *g, float *e, uint64_t seed, uint32_t step,
+                        uint8_t *codes, float *meta);
+int gqref_dequantize_accumulate_topk(int d, int s, int K, int flags, int64_t n,
+                                     int W, const uint8_t *const *codes,
+                                     const float *const *meta, float alpha,
+                                     float beta, float *out);
+
 /* Dense packing (flags bit 1): groups of 8 codes as one base-A integer,
  * first code least significant, in fields of gqref_dense_width(A) =
  * ceil(log2(A^8)) bits of the LSB-first stream; A <= 16. */
