@@ -247,7 +247,7 @@ def entry(name, ms, nbytes, n, bound="hbm", extra=None):
 def suite(torch, gq, WL, stream, reps: int, only: str | None = None):
     """Every other workload's kernels, each timed back to back (only the
     workloads whose name contains `only`: qsgd, orq, bingrad, workers,
-    dense, nearest, layers)."""
+    dense, nearest, layers, topk)."""
     out = []
     tb = lambda f, r=reps: time_back_to_back(torch, stream, f, r)  # noqa: E731
     want = lambda name: only is None or only in name  # noqa: E731
@@ -266,6 +266,32 @@ def suite(torch, gq, WL, stream, reps: int, only: str | None = None):
         out += suite_nearest(torch, gq, WL, stream, tb, reps)
     if want("layers"):
         out += suite_layers(torch, gq, WL, stream, tb)
+    if want("topk"):
+        out += suite_topk(torch, gq, WL, stream, tb)
+    return out
+
+
+def suite_topk(torch, gq, WL, stream, tb):
+    """Top-K with quantization: the 25.6M layered gradient, K = 26 of every
+    512 (about 5 %), 4-bit values (s = 4), error feedback; and its
+    dequantize."""
+    out = []
+    G = [torch.from_numpy(WL.ternary_gradient(t)).cuda() for t in range(2)]
+    n = G[0].numel()
+    E = [torch.zeros(n, dtype=torch.float32, device="cuda") for _ in range(2)]
+    d = gq.desc(gq.GQ_TOPK, 512, s=4, levels=26)
+    cb, _, mf = gq.gq_payload_size(d, n)
+    P = [gq.alloc_payload(d, n) for _ in range(2)]
+    O_ = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(2)]
+    qs = [gq.PreparedQuantize(d, G[k], E[k], P[k][0], P[k][1], stream) for k in range(2)]
+    ms = tb(lambda i: qs[i % 2](2, i))
+    out.append(entry(f"quantize top-k 26/512 s=4 +ef n={n}", ms,
+                     12 * n + cb + 4 * mf, n,
+                     extra={"compression_vs_fp32": round(4 * n / (cb + 4 * mf), 3)}))
+    dqs = [gq.PreparedDequantizeAccumulate(d, n, [P[k][0]], [P[k][1]], 1.0, 0.0,
+                                           O_[k], stream) for k in range(2)]
+    ms = tb(lambda i: dqs[i % 2]())
+    out.append(entry(f"dequantize top-k 26/512 W=1 n={n}", ms, cb + 4 * mf + 4 * n, n))
     return out
 
 
@@ -548,7 +574,7 @@ def main() -> int:
     ap.add_argument("--suite", choices=("main", "all"), default="all")
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--only", choices=("qsgd", "orq", "bingrad", "workers",
-                                       "dense", "nearest", "layers"),
+                                       "dense", "nearest", "layers", "topk"),
                     help="time only this workload's kernels after the headline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--counters", action="store_true",

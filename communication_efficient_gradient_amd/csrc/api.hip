@@ -58,6 +58,16 @@ int check_desc(const gq_desc* d, gq::LaunchDesc* L) {
       L->bits = ceil_log2(d->levels);
       L->k = d->levels;
       break;
+    case GQ_TOPK: {
+      // K = levels kept per bucket; values on the uniform grid of s levels
+      if (d->s < 1 || d->s > 127 || b > 512) return GQ_EUNSUPPORTED;
+      if (d->levels < 1 || d->levels > b) return GQ_EINVAL;
+      const int w = ceil_log2(2 * d->s + 1);
+      L->bits = w <= 4 ? w : 8;
+      L->k = 1;
+      if (d->flags & ~GQ_FLAG_NEAREST) return GQ_EUNSUPPORTED;
+      break;
+    }
     default:
       return GQ_EUNSUPPORTED;
   }
@@ -65,7 +75,8 @@ int check_desc(const gq_desc* d, gq::LaunchDesc* L) {
     if (d->scheme != GQ_ORQ) return GQ_EUNSUPPORTED;
     if (!(d->clip_sigma > 0.f) || !std::isfinite(d->clip_sigma)) return GQ_EINVAL;
   }
-  if ((d->flags & GQ_FLAG_NEAREST) && d->scheme != GQ_UNIFORM && d->scheme != GQ_ORQ)
+  if ((d->flags & GQ_FLAG_NEAREST) && d->scheme != GQ_UNIFORM && d->scheme != GQ_ORQ &&
+      d->scheme != GQ_TOPK)
     return GQ_EUNSUPPORTED;
   if ((d->flags & GQ_FLAG_BISECT) && (d->scheme != GQ_ORQ || b > 512))
     return GQ_EUNSUPPORTED;
@@ -93,6 +104,8 @@ int check_desc(const gq_desc* d, gq::LaunchDesc* L) {
 }
 
 int64_t code_bytes_of(const gq::LaunchDesc& L, int64_t n) {
+  if (L.scheme == GQ_TOPK)
+    return ((n + L.d - 1) / L.d) * 4 * (int64_t)gq::topk_record_words(L.d, L.bits, L.L);
   if (L.dense) return (((n + 7) / 8) * L.W + 7) / 8;
   return (n * L.bits + 7) / 8;
 }
@@ -134,7 +147,8 @@ int gq_code_bits(const gq_desc* desc, int32_t* bits) {
   const int rc = check_desc(desc, &L);
   if (rc) return rc;
   if (bits == nullptr) return GQ_EINVAL;
-  *bits = L.bits;
+  // Top-K: one slot = bucket index bits + code bits
+  *bits = L.scheme == GQ_TOPK ? ceil_log2(L.d) + L.bits : L.bits;
   return GQ_OK;
 }
 
@@ -156,6 +170,7 @@ int gq_select_levels(const gq_desc* desc, int64_t n, const float* g,
   gq::LaunchDesc L;
   int rc = check_desc(desc, &L);
   if (rc) return rc;
+  if (L.scheme == GQ_TOPK) return GQ_EUNSUPPORTED;
   if (n < 1 || n > kMaxN || !g || !meta) return GQ_EINVAL;
   if (!aligned16(g) || !aligned16(meta) || (e && !aligned16(e))) return GQ_EINVAL;
   if (overlap(meta, 4 * meta_floats_of(L, n), g, 4 * n) ||
@@ -189,6 +204,8 @@ int gq_quantize(const gq_desc* desc, int64_t n, const float* g, float* e,
       overlap(codes, cap, meta, mb))
     return GQ_EINVAL;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (L.scheme == GQ_TOPK)
+    return launch_status(gq::launch_topk_quant(L, n, g, e, seed, step, codes, meta, st));
   if (is_sort_scheme(L))
     return launch_status(
         gq::launch_sort_quant(L, n, g, e, seed, step, codes, meta, cb, st));
@@ -201,6 +218,7 @@ int gq_error_feedback(const gq_desc* desc, int64_t n, const float* g, float* e,
   gq::LaunchDesc L;
   int rc = check_desc(desc, &L);
   if (rc) return rc;
+  if (L.scheme == GQ_TOPK) return GQ_EUNSUPPORTED;
   if (n < 1 || n > kMaxN || !g || !e || !codes || !meta) return GQ_EINVAL;
   if (!aligned16(g) || !aligned16(e) || !aligned16(codes) || !aligned16(meta))
     return GQ_EINVAL;
@@ -234,6 +252,9 @@ int gq_dequantize_accumulate(const gq_desc* desc, int64_t n, int32_t W,
     pp.codes[w] = codes[w];
     pp.meta[w] = meta[w];
   }
+  if (L.scheme == GQ_TOPK)
+    return launch_status(gq::launch_topk_deq(L, n, W, pp, alpha, beta, out,
+                                             static_cast<hipStream_t>(stream)));
   return launch_status(gq::launch_deq_acc(L, n, W, pp, alpha, beta, out, cb,
                                           static_cast<hipStream_t>(stream)));
 }

@@ -12,7 +12,7 @@
 
 namespace gq {
 
-enum Scheme { UNIFORM = 0, BIN_SIGN = 1, BIN_OPT = 2, ORQ = 3 };
+enum Scheme { UNIFORM = 0, BIN_SIGN = 1, BIN_OPT = 2, ORQ = 3, TOPK = 4 };
 
 constexpr int kMaxPayloads = 16;
 
@@ -582,6 +582,14 @@ int launch_deq_acc(const LaunchDesc& L, int64_t n, int W, const PayloadPtrs& pp,
 int launch_error_feedback(const LaunchDesc& L, int64_t n, const float* g,
                           float* e, const uint8_t* codes, const float* meta,
                           int64_t code_bytes, hipStream_t st);
+// Top-K sparsification with quantization (d <= 512; L = K): record words per
+// bucket, quantize (with the residual), dequantize-accumulate
+int topk_record_words(int d, int bits, int K);
+int launch_topk_quant(const LaunchDesc& L, int64_t n, const float* g, float* e,
+                      uint64_t seed, uint32_t step, uint8_t* codes,
+                      float* meta, hipStream_t st);
+int launch_topk_deq(const LaunchDesc& L, int64_t n, int W, const PayloadPtrs& pp,
+                    float alpha, float beta, float* out, hipStream_t st);
 // per-layer scale (uniform scheme): max-abs pass then rounding pass
 // (codes == nullptr: the max-abs pass only)
 int launch_layer_quant(const LaunchDesc& L, int64_t n, int nl,

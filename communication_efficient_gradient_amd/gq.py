@@ -17,7 +17,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgq.so")
 
-GQ_UNIFORM, GQ_BIN_SIGN, GQ_BIN_OPT, GQ_ORQ = 0, 1, 2, 3
+GQ_UNIFORM, GQ_BIN_SIGN, GQ_BIN_OPT, GQ_ORQ, GQ_TOPK = 0, 1, 2, 3, 4
 GQ_FLAG_CLIP = 1
 GQ_FLAG_DENSE = 2
 GQ_FLAG_NEAREST = 4

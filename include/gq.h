@@ -67,12 +67,31 @@ extern "C" {
  *             method); deterministic, 1-bit.
  * GQ_ORQ      L levels picked greedily to minimise the summed random-
  *             rounding variance sum (b-x)(x-a), random rounding between
- *             adjacent levels (ORQ, same section); optional clip. */
+ *             adjacent levels (ORQ, same section); optional clip.
+ * GQ_TOPK     Top-K sparsification combined with quantization ("gradient
+ *             quantization for communication" glossary, §Quantization
+ *             Schemes): per bucket only the K = desc.levels elements of
+ *             largest |p| are sent (all of a bucket with fewer; equal
+ *             magnitudes: the lower index first), each rounded on the
+ *             bucket's uniform grid of s levels per sign exactly as
+ *             GQ_UNIFORM rounds it (same scale M = max |p|, same Philox
+ *             word); the others decode as 0 and stay in the residual.
+ *             d <= 512, 1 <= K <= d, flags: GQ_FLAG_NEAREST only.  Codes:
+ *             bucket j owns R = ceil(K (log2 d + b) / 32) 32-bit words at
+ *             byte 4 R j (b = the GQ_UNIFORM code width); slot t, the t-th
+ *             kept element in increasing index, holds its index within the
+ *             bucket (log2 d bits) then its code (b bits, two's complement)
+ *             at bits [t w, t w + w) of the record, w = log2 d + b, LSB
+ *             first; unused slots and pad bits are 0.  meta: the bucket's
+ *             max-abs.  gq_code_bits reports w.  gq_select_levels and
+ *             gq_error_feedback return GQ_EUNSUPPORTED (gq_quantize writes
+ *             the residual). */
 typedef enum {
   GQ_UNIFORM = 0,
   GQ_BIN_SIGN = 1,
   GQ_BIN_OPT = 2,
-  GQ_ORQ = 3
+  GQ_ORQ = 3,
+  GQ_TOPK = 4
 } gq_scheme;
 
 /* GQ_FLAG_CLIP (GQ_ORQ only): clip every value of a bucket to

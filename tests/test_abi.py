@@ -195,3 +195,35 @@ def test_bisect_flag_rules(gq):
         with pytest.raises(gq.GQError) as ex:
             gq.gq_payload_size(gq.desc(**kw, flags=Bf), 100)
         assert ex.value.status == gq.GQ_EUNSUPPORTED
+
+
+def test_topk_rules_and_sizes(gq):
+    """Top-K: d <= 512, 1 <= K <= d, nearest flag only; sizes from the
+    record layout."""
+    import numpy as np
+
+    import oracle as O
+    T = gq.GQ_TOPK
+    assert T == 4
+    for d, s, K in [(64, 1, 1), (512, 4, 26), (512, 127, 512), (128, 7, 100)]:
+        cb, cap, mf = gq.gq_payload_size(gq.desc(T, d, s=s, levels=K), 10_000)
+        nb = (10_000 + d - 1) // d
+        assert cb == nb * 4 * O.topk_record_words(d, s, K)
+        assert mf == nb and cap % 16 == 0 and cap >= cb
+        b = O.Desc(O.UNIFORM, d, s=s).bits
+        assert gq.gq_code_bits(gq.desc(T, d, s=s, levels=K)) == int(np.log2(d)) + b
+    for kw, status in [(dict(bucket=1024, levels=5), gq.GQ_EUNSUPPORTED),
+                       (dict(levels=0), gq.GQ_EINVAL),
+                       (dict(bucket=64, levels=65), gq.GQ_EINVAL),
+                       (dict(levels=5, flags=gq.GQ_FLAG_DENSE), gq.GQ_EUNSUPPORTED),
+                       (dict(levels=5, s=128), gq.GQ_EUNSUPPORTED)]:
+        with pytest.raises(gq.GQError) as ex:
+            gq.gq_payload_size(gq.desc(T, **{"bucket": 512, **kw}), 100)
+        assert ex.value.status == status
+    assert gq.gq_payload_size(gq.desc(T, 512, levels=5, flags=gq.GQ_FLAG_NEAREST), 100)
+    L = gq.lib()
+    fake = 1 << 20
+    d = gq.desc(T, 512, s=4, levels=26)
+    assert L.gq_select_levels(C.byref(d), 100, fake, None, fake * 2, None) == gq.GQ_EUNSUPPORTED
+    assert L.gq_error_feedback(C.byref(d), 100, fake, fake * 2, fake * 3, fake * 4,
+                               None) == gq.GQ_EUNSUPPORTED
