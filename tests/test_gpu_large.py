@@ -1,0 +1,121 @@
+"""GPU parity past the 32-bit limits, in the launch configuration of every
+other call: n = 2^31 + 517 elements (element indices, code byte offsets and
+bucket counts beyond int32) with 8-bit codes and error feedback, and
+n = 2^34 + 1029 elements (Philox counters i/4 >= 2^32, so the high counter
+word is in use) with ternary codes, fixed and dense.  The gradient is drawn
+on the device (torch's seeded normal generator) and the oracle recomputes
+sampled runs of buckets, always including the first and the last, from the
+same values copied to the host; the dequantizer is checked on the same
+runs.  Needs about 80 GB of device memory; skipped on smaller devices."""
+import numpy as np
+import pytest
+
+import oracle as O
+from tests.parity import compare_codes, compare_meta, compare_values, sample_runs, say
+
+pytestmark = pytest.mark.gpu
+
+RUN_LEN = 8
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from communication_efficient_gradient_amd import gq
+    return gq, torch
+
+
+def _need(torch, nbytes):
+    free, _ = torch.cuda.mem_get_info()
+    if free < nbytes * 1.1:
+        pytest.skip(f"needs {nbytes / 2**30:.0f} GiB of free device memory")
+
+
+def _byte_range(d: O.Desc, lo: int, hi: int):
+    if d.dense:
+        w = d.field_bits
+        return (lo // 8) * w // 8, (((hi + 7) // 8) * w + 7) // 8
+    return lo * d.bits // 8, (hi * d.bits + 7) // 8
+
+
+def _check(gq, torch, d, n, G, E0, E, codes, meta, seed, step):
+    runs = sample_runs(d.nb(n), 6, RUN_LEN, seed=n % 1000)
+    for j0 in runs:
+        j1 = min(d.nb(n), j0 + RUN_LEN)
+        lo, hi = j0 * d.d, min(n, j1 * d.d)
+        say(f"  run buckets {j0}..{j1} elements {lo}..{hi}")
+        g = G[lo:hi].cpu().numpy()
+        e0 = None if E0 is None else E0[lo:hi]
+        rc, rm, re_, _ = O.quantize(d, g, e0, seed=seed, step=step, i0=lo)
+        b0, b1 = _byte_range(d, lo, hi)
+        compare_codes(d, hi - lo, codes[b0:b1].cpu().numpy(), rc)
+        compare_meta(d, meta[j0:j1].cpu().numpy().reshape(-1, 1), rm, exact=True)
+        if E is not None:
+            assert np.array_equal(E[lo:hi].cpu().numpy().view(np.uint32),
+                                  re_.view(np.uint32))
+    return runs
+
+
+def test_int8_ef_past_2_31(dev):
+    gq, torch = dev
+    n = 2**31 + 517
+    _need(torch, n * 4 * 3 + n)
+    d = O.Desc(O.UNIFORM, 512, s=127)
+    gd = gq.desc(0, 512, s=127)
+    say(f"int8 + ef n={n}")
+    gen = torch.Generator(device="cuda").manual_seed(31)
+    G = torch.randn(n, device="cuda", generator=gen) * 1e-3
+    E = torch.randn(n, device="cuda", generator=gen) * 1e-5
+    runs = sample_runs(d.nb(n), 6, RUN_LEN, seed=n % 1000)
+    E0 = {}
+    for j0 in runs:
+        lo, hi = j0 * 512, min(n, (j0 + RUN_LEN) * 512)
+        E0[(lo, hi)] = E[lo:hi].cpu().numpy()
+    codes, meta = gq.alloc_payload(gd, n)
+    gq.gq_quantize(gd, G, E, 7, 3, codes, meta)
+    torch.cuda.synchronize()
+
+    class _E0:
+        def __getitem__(self, s):
+            return E0[(s.start, s.stop)]
+
+    _check(gq, torch, d, n, G, _E0(), E, codes, meta, 7, 3)
+    # the dequantizer on the same runs
+    out = G  # reuse the gradient's memory for the output
+    gq.gq_dequantize_accumulate(gd, n, [codes], [meta], 1.0, 0.0, out)
+    torch.cuda.synchronize()
+    for j0 in runs:
+        j1 = min(d.nb(n), j0 + RUN_LEN)
+        lo, hi = j0 * 512, min(n, j1 * 512)
+        b0, b1 = _byte_range(d, lo, hi)
+        xr = O.dequantize(d, hi - lo, codes[b0:b1].cpu().numpy(),
+                          meta[j0:j1].cpu().numpy())
+        compare_values(out[lo:hi].cpu().numpy(), xr, np.abs(xr), exact=True)
+    del G, E, codes, meta, out
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("flags", [0, O.FLAG_DENSE])
+def test_ternary_past_2_34(dev, flags):
+    gq, torch = dev
+    n = 2**34 + 1029
+    _need(torch, n * 4 + n // 4 + n // 64)
+    d = O.Desc(O.UNIFORM, 512, s=1, flags=flags)
+    gd = gq.desc(0, 512, s=1, flags=flags)
+    say(f"ternary n={n} flags={flags}")
+    gen = torch.Generator(device="cuda").manual_seed(34)
+    G = torch.empty(n, device="cuda")
+    step = 1 << 30
+    for a in range(0, n, step):   # chunks keep the generator's own workspace small
+        G[a:a + step].normal_(0.0, 1e-3, generator=gen)
+    codes, meta = gq.alloc_payload(gd, n)
+    gq.gq_quantize(gd, G, None, 11, 5, codes, meta)
+    torch.cuda.synchronize()
+    runs = _check(gq, torch, d, n, G, None, None, codes, meta, 11, 5)
+    # the last run (always sampled) holds elements whose counter i/4 needs
+    # the high word
+    assert runs[-1] + RUN_LEN >= d.nb(n) and (n - 1) // 4 >= 2**32
+    del G, codes, meta
+    torch.cuda.empty_cache()
