@@ -209,27 +209,37 @@ def copy_reference(torch, stream, nbytes: int = 1 << 30) -> dict:
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
 
 
+def time_oracle(run, size: int, d: int, budget: float = 0.5,
+                max_n: int = 1 << 22):
+    """Throughput (GB/s of fp32 input) of run(n), a CPU oracle call on the
+    first n elements (whole buckets of d), n growing until `budget` seconds."""
+    import oracle as O
+
+    n = min(size, 1 << 16)
+    n -= n % d if n > d else 0
+    while True:
+        t0 = time.perf_counter()
+        run(n)
+        dt = time.perf_counter() - t0
+        if dt >= budget or n >= min(max_n, size):
+            return {"oracle_GBps": round(4 * n / dt / 1e9, 4),
+                    "oracle_elements": n, "oracle_threads": O.threads()}
+        n = min(4 * n, max_n, size)
+
+
 def oracle_rate(host_g, desc_kw, ef: bool, seed: int = 0, budget: float = 0.5,
                 max_n: int = 1 << 22):
-    """The CPU oracle's quantize throughput (GB/s of fp32 input) on a prefix
-    of the same input: whole buckets, growing until `budget` seconds."""
+    """The CPU oracle's quantize throughput on a prefix of the same input."""
     import numpy as np
 
     import oracle as O
 
     od = O.Desc(**desc_kw)
-    n = min(host_g.size, 1 << 16)
-    n -= n % od.d if n > od.d else 0
-    while True:
-        g = host_g[:n]
+
+    def run(n):
         e = np.zeros(n, dtype=np.float32) if ef else None
-        t0 = time.perf_counter()
-        O.quantize(od, g, e, seed=seed, step=0)
-        dt = time.perf_counter() - t0
-        if dt >= budget or n >= min(max_n, host_g.size):
-            return {"oracle_GBps": round(4 * n / dt / 1e9, 4),
-                    "oracle_elements": n, "oracle_threads": O.threads()}
-        n = min(4 * n, max_n, host_g.size)
+        O.quantize(od, host_g[:n], e, seed=seed, step=0)
+    return time_oracle(run, host_g.size, od.d, budget, max_n)
 
 
 def entry(name, ms, nbytes, n, bound="hbm", extra=None):
@@ -275,8 +285,13 @@ def suite_topk(torch, gq, WL, stream, tb):
     """Top-K with quantization: the 25.6M layered gradient, K = 26 of every
     512 (about 5 %), 4-bit values (s = 4), error feedback; and its
     dequantize."""
+    import numpy as np
+
+    import oracle as O
     out = []
-    G = [torch.from_numpy(WL.ternary_gradient(t)).cuda() for t in range(2)]
+    host = WL.ternary_gradient(0)
+    G = [torch.from_numpy(host).cuda(),
+         torch.from_numpy(WL.ternary_gradient(1)).cuda()]
     n = G[0].numel()
     E = [torch.zeros(n, dtype=torch.float32, device="cuda") for _ in range(2)]
     d = gq.desc(gq.GQ_TOPK, 512, s=4, levels=26)
@@ -285,9 +300,13 @@ def suite_topk(torch, gq, WL, stream, tb):
     O_ = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(2)]
     qs = [gq.PreparedQuantize(d, G[k], E[k], P[k][0], P[k][1], stream) for k in range(2)]
     ms = tb(lambda i: qs[i % 2](2, i))
+    oracle = time_oracle(lambda k: O.quantize_topk(512, 4, 26, host[:k],
+                                                   np.zeros(k, np.float32), seed=2),
+                         n, 512)
     out.append(entry(f"quantize top-k 26/512 s=4 +ef n={n}", ms,
                      12 * n + cb + 4 * mf, n,
-                     extra={"compression_vs_fp32": round(4 * n / (cb + 4 * mf), 3)}))
+                     extra={"compression_vs_fp32": round(4 * n / (cb + 4 * mf), 3),
+                            **oracle}))
     dqs = [gq.PreparedDequantizeAccumulate(d, n, [P[k][0]], [P[k][1]], 1.0, 0.0,
                                            O_[k], stream) for k in range(2)]
     ms = tb(lambda i: dqs[i % 2]())
@@ -302,10 +321,14 @@ def suite_layers(torch, gq, WL, stream, tb):
     plus codes and scales."""
     import numpy as np
     out = []
+    import oracle as O
     sizes, _ = WL.ternary_layout()
-    off = torch.from_numpy(np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)).cuda()
+    off_h = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    off = torch.from_numpy(off_h).cuda()
     nl = len(sizes)
-    G = [torch.from_numpy(WL.ternary_gradient(t)).cuda() for t in range(2)]
+    host = WL.ternary_gradient(0)
+    G = [torch.from_numpy(host).cuda(),
+         torch.from_numpy(WL.ternary_gradient(1)).cuda()]
     n = G[0].numel()
     E = [torch.zeros(n, dtype=torch.float32, device="cuda") for _ in range(2)]
     d = gq.desc(gq.GQ_UNIFORM, 512, s=1)
@@ -315,8 +338,13 @@ def suite_layers(torch, gq, WL, stream, tb):
     O_ = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(2)]
     ms = tb(lambda i: gq.gq_quantize_layers(d, off, G[i % 2], E[i % 2], 2, i,
                                             C[i % 2], M[i % 2], stream))
+    def oracle_layers(k):
+        o = [int(x) for x in off_h if x < k] + [k]
+        O.quantize_layers(O.Desc(O.UNIFORM, s=1), o, host[:k],
+                          np.zeros(k, np.float32), seed=2)
     out.append(entry(f"quantize ternary+ef per-layer scale ({nl} layers) n={n}",
-                     ms, 20 * n + (2 * n + 7) // 8 + 4 * nl, n))
+                     ms, 20 * n + (2 * n + 7) // 8 + 4 * nl, n,
+                     extra=time_oracle(oracle_layers, n, 512)))
     ms = tb(lambda i: gq.gq_dequantize_accumulate_layers(
         d, n, off, [C[i % 2]], [M[i % 2]], 1.0, 0.0, O_[i % 2], stream))
     out.append(entry(f"dequantize ternary per-layer scale W=1 n={n}", ms,
@@ -338,16 +366,21 @@ def suite_nearest(torch, gq, WL, stream, tb, reps):
     q = gq.PreparedQuantize(d, g, e, c, m, stream)
     ms = tb(lambda i: q(2, i))
     out.append(entry(f"quantize ternary+ef nearest d=512 n={n}", ms,
-                     quant_bytes(2, 1, 512, n, True), n))
+                     quant_bytes(2, 1, 512, n, True), n,
+                     extra=oracle_rate(host, dict(scheme=0, d=512, s=1, flags=N),
+                                       True, seed=2)))
     del g, e, c, m, q, host
-    g = torch.from_numpy(WL.orq_gradient()).cuda()
+    host = WL.orq_gradient()
+    g = torch.from_numpy(host).cuda()
     n = g.numel()
     d = gq.desc(gq.GQ_ORQ, 512, levels=9, flags=N)
     c, m = gq.alloc_payload(d, n)
     q = gq.PreparedQuantize(d, g, None, c, m, stream)
     ms = tb(lambda i: q(3, 0), max(3, reps // 2))
     out.append(entry(f"quantize orq L=9 nearest d=512 n={n}", ms,
-                     quant_bytes(4, 9, 512, n, False), n, bound="alu"))
+                     quant_bytes(4, 9, 512, n, False), n, bound="alu",
+                     extra=oracle_rate(host, dict(scheme=3, d=512, L=9, flags=N),
+                                       False, seed=3)))
     return out
 
 
@@ -404,7 +437,8 @@ def suite_dense(torch, gq, WL, stream, tb, reps):
 def suite_qsgd(torch, gq, WL, stream, tb):
     """QSGD s=4, 65,536 elements: cache-resident, latency-bound."""
     out = []
-    g = torch.from_numpy(WL.qsgd_gradient()).cuda()
+    host = WL.qsgd_gradient()
+    g = torch.from_numpy(host).cuda()
     d = gq.desc(gq.GQ_UNIFORM, 512, s=4)
     c, m = gq.alloc_payload(d, g.numel())
     o = torch.empty_like(g)
@@ -412,7 +446,8 @@ def suite_qsgd(torch, gq, WL, stream, tb):
     ms = tb(lambda i: q(0, 0))
     out.append(entry("quantize qsgd s=4 d=512 n=65536", ms,
                      quant_bytes(4, 1, 512, g.numel(), False), g.numel(),
-                     bound="latency"))
+                     bound="latency",
+                     extra=oracle_rate(host, dict(scheme=0, d=512, s=4), False)))
     dq = gq.PreparedDequantizeAccumulate(d, g.numel(), [c], [m], 1.0, 0.0, o,
                                          stream)
     ms = tb(lambda i: dq())
@@ -451,7 +486,9 @@ def suite_orq(torch, gq, WL, stream, tb, reps):
         ms = tb(lambda i: q(3, 0), max(3, reps // 2))
         out.append(entry(f"quantize orq L={L} bisect d=512 n={n}", ms,
                          quant_bytes(gq.gq_code_bits(d), L, 512, n, False), n,
-                         bound="alu"))
+                         bound="alu", extra=oracle_rate(
+                             host, dict(scheme=3, d=512, L=L, flags=8), False,
+                             seed=3)))
         del c, m, q
     return out
 
