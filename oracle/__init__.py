@@ -19,6 +19,9 @@ Parity status of each routine (what pins it is in ``tests/test_oracle_*``):
     dense pack / unpack   Python big-integer base-A arithmetic, field widths
                           from exact integer powers, round trips
     dequantize_accumulate exact rational sums (fractions) on small inputs
+    elias encode / decode textbook gamma codewords (golden file), a bit-string
+                          parser written in the test, lengths from the
+                          code-length formula, round trips
 """
 from __future__ import annotations
 
@@ -75,6 +78,12 @@ def lib():
         L.gqref_dequantize_accumulate_topk.argtypes = [
             i32, i32, i32, i32, i64, i32, C.POINTER(C.c_void_p),
             C.POINTER(C.c_void_p), C.c_float, C.c_float, fp]
+        L.gqref_elias_max_words.argtypes = [i32, i32, i64]
+        L.gqref_elias_max_words.restype = i64
+        L.gqref_elias_encode.argtypes = [i32, i32, i64, u8p, C.c_void_p,
+                                         C.c_void_p]
+        L.gqref_elias_decode.argtypes = [i32, i32, i64, C.c_void_p, C.c_void_p,
+                                         u8p]
         L.gqref_dense_width.argtypes = [i32]
         L.gqref_pack_dense.argtypes = [i32, i64, C.c_void_p, u8p]
         L.gqref_pack_dense.restype = None
@@ -360,3 +369,36 @@ def signed_codes(desc: Desc, n: int, codes) -> np.ndarray:
         m = 1 << (desc.bits - 1)
         v = (v ^ m) - m
     return v
+
+
+def elias_max_words(d: int, s: int, n: int) -> int:
+    return int(lib().gqref_elias_max_words(d, s, n))
+
+
+def elias_encode(d: int, s: int, n: int, codes):
+    """Elias gamma stream of n uniform-scheme codes (fixed-width stream, s
+    levels per sign).  Returns (off u64[nb + 1], words u32[off[nb]])."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    nb = (n + d - 1) // d
+    off = np.zeros(nb + 1, dtype=np.uint64)
+    if lib().gqref_elias_encode(d, s, n, _ptr(codes), _ptr(off), None):
+        raise ValueError("oracle elias_encode: invalid arguments or codes")
+    words = np.zeros(max(int(off[-1]), 1), dtype=np.uint32)
+    if lib().gqref_elias_encode(d, s, n, _ptr(codes), _ptr(off), _ptr(words)):
+        raise ValueError("oracle elias_encode: invalid arguments or codes")
+    return off, words[:int(off[-1])]
+
+
+def elias_decode(d: int, s: int, n: int, off, words):
+    """Fixed-width codes (ceil(n * bits / 8) bytes) back from an Elias stream."""
+    off = np.ascontiguousarray(off, dtype=np.uint64)
+    words = np.ascontiguousarray(words, dtype=np.uint32)
+    if words.size == 0:
+        words = np.zeros(1, dtype=np.uint32)
+    b = lib().gqref_bits(UNIFORM, s, 2)
+    if b < 0:
+        raise ValueError("oracle elias_decode: invalid arguments")
+    codes = np.zeros((n * b + 7) // 8, dtype=np.uint8)
+    if lib().gqref_elias_decode(d, s, n, _ptr(off), _ptr(words), _ptr(codes)):
+        raise ValueError("oracle elias_decode: invalid arguments or stream")
+    return codes

@@ -1023,6 +1023,108 @@ int gqref_dequantize_accumulate_topk(int d, int s, int K, int flags, int64_t n,
   return 0;
 }
 
+/* ------------------------------------------------ Elias gamma coding --
+ * QSGD compresses its quantized integers further with Elias integer coding
+ * ("Gradient Quantization" glossary, QSGD paragraph).  Reading: every code c
+ * of the uniform scheme, in element order, becomes the Elias gamma code of
+ * the positive integer m = |c| + 1 (floor(log2 m) zero bits, then the
+ * floor(log2 m) + 1 binary digits of m, most significant first), followed by
+ * one sign bit (1 = negative) when c != 0.  Each bucket's record starts on a
+ * 32-bit word boundary (pad bits 0); off[j] is the first word of bucket j's
+ * record, off[nb] the stream's word count.  Stream bit t of a record is bit
+ * t mod 32 of its word t / 32.  Codes must lie in [-s, s]. */
+static void word_put_bit(uint32_t *w, int64_t t, int bit) {
+  if (bit) w[t / 32] |= 1u << (t % 32);
+}
+
+static int word_get_bit(const uint32_t *w, int64_t t) {
+  return (int)((w[t / 32] >> (t % 32)) & 1u);
+}
+
+static int floor_log2_u(uint32_t m) {
+  int L = 0;
+  while ((m >> (L + 1)) != 0) ++L;
+  return L;
+}
+
+static int64_t gamma_bits(int32_t c) {
+  uint32_t m = (uint32_t)(c < 0 ? -c : c) + 1u;
+  return 2 * floor_log2_u(m) + 1 + (c != 0);
+}
+
+int64_t gqref_elias_max_words(int d, int s, int64_t n) {
+  if (d < 64 || (d & (d - 1)) || s < 1 || s > 127 || n < 1) return -1;
+  int64_t worst = gamma_bits(s), nb = (n + d - 1) / d, tot = 0;
+  for (int64_t j = 0; j < nb; ++j) {
+    int64_t nj = (n - j * d < d) ? n - j * d : d;
+    tot += (nj * worst + 31) / 32;
+  }
+  return tot;
+}
+
+int gqref_elias_encode(int d, int s, int64_t n, const uint8_t *codes,
+                       uint64_t *off, uint32_t *words) {
+  int b = gqref_bits(UNIFORM, s, 2);
+  if (b < 0 || d < 64 || (d & (d - 1)) || n < 1 || !codes || !off) return -1;
+  int64_t nb = (n + d - 1) / d;
+  /* lengths first: the word offsets */
+  off[0] = 0;
+  for (int64_t j = 0; j < nb; ++j) {
+    int64_t nj = (n - j * d < d) ? n - j * d : d, bits = 0;
+    for (int64_t t = 0; t < nj; ++t) {
+      int32_t c = sext(get_code(codes, j * d + t, b), b);
+      if (c < -s || c > s) return -1;
+      bits += gamma_bits(c);
+    }
+    off[j + 1] = off[j] + (uint64_t)((bits + 31) / 32);
+  }
+  if (!words) return 0;
+  memset(words, 0, (size_t)off[nb] * 4);
+  for (int64_t j = 0; j < nb; ++j) {
+    int64_t nj = (n - j * d < d) ? n - j * d : d;
+    uint32_t *rec = words + off[j];
+    int64_t t = 0;  /* bit cursor in the record */
+    for (int64_t i = 0; i < nj; ++i) {
+      int32_t c = sext(get_code(codes, j * d + i, b), b);
+      uint32_t m = (uint32_t)(c < 0 ? -c : c) + 1u;
+      int L = floor_log2_u(m);
+      for (int k = 0; k < L; ++k) word_put_bit(rec, t++, 0);
+      for (int k = L; k >= 0; --k) word_put_bit(rec, t++, (int)((m >> k) & 1u));
+      if (c != 0) word_put_bit(rec, t++, c < 0);
+    }
+  }
+  return 0;
+}
+
+int gqref_elias_decode(int d, int s, int64_t n, const uint64_t *off,
+                       const uint32_t *words, uint8_t *codes) {
+  int b = gqref_bits(UNIFORM, s, 2);
+  if (b < 0 || d < 64 || (d & (d - 1)) || n < 1 || !off || !words || !codes)
+    return -1;
+  int64_t nb = (n + d - 1) / d;
+  memset(codes, 0, (size_t)((n * b + 7) / 8));
+  for (int64_t j = 0; j < nb; ++j) {
+    int64_t nj = (n - j * d < d) ? n - j * d : d;
+    const uint32_t *rec = words + off[j];
+    int64_t t = 0, tmax = 32 * (int64_t)(off[j + 1] - off[j]);
+    for (int64_t i = 0; i < nj; ++i) {
+      int L = 0;
+      while (t < tmax && word_get_bit(rec, t) == 0) { ++L; ++t; }
+      if (L > 7 || t + L + 1 > tmax) return -1;  /* |c| + 1 <= 128 */
+      uint32_t m = 0;
+      for (int k = 0; k <= L; ++k) m = (m << 1) | (uint32_t)word_get_bit(rec, t++);
+      int32_t c = (int32_t)(m - 1u);
+      if (c > s) return -1;
+      if (c != 0) {
+        if (t >= tmax) return -1;
+        if (word_get_bit(rec, t++)) c = -c;
+      }
+      put_code(codes, j * d + i, b, (uint32_t)c & ((1u << b) - 1u));
+    }
+  }
+  return 0;
+}
+
 void gqref_set_threads(int t) {
   if (t > 0) omp_set_num_threads(t);
 }

@@ -123,6 +123,17 @@ void gqref_unpack_dense(int A, int64_t n, const uint8_t *codes, uint32_t *digits
 void gqref_pack(int bits, int64_t n, const uint32_t *vals, uint8_t *codes);
 void gqref_unpack(int bits, int64_t n, const uint8_t *codes, uint32_t *vals);
 
+/* Elias gamma coding of uniform-scheme codes (QSGD's lossless integer
+ * coding): code c -> gamma(|c| + 1), then a sign bit (1 = negative) when
+ * c != 0; bucket records word-aligned; off: nb + 1 word offsets (off[0] = 0,
+ * off[nb] = words used).  encode with words == NULL fills off only.
+ * max_words: the stream size when every code has |c| = s. */
+int64_t gqref_elias_max_words(int d, int s, int64_t n);
+int gqref_elias_encode(int d, int s, int64_t n, const uint8_t *codes,
+                       uint64_t *off, uint32_t *words);
+int gqref_elias_decode(int d, int s, int64_t n, const uint64_t *off,
+                       const uint32_t *words, uint8_t *codes);
+
 void gqref_set_threads(int t);
 int gqref_get_threads(void);
 
