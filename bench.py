@@ -257,7 +257,7 @@ def entry(name, ms, nbytes, n, bound="hbm", extra=None):
 def suite(torch, gq, WL, stream, reps: int, only: str | None = None):
     """Every other workload's kernels, each timed back to back (only the
     workloads whose name contains `only`: qsgd, orq, bingrad, workers,
-    dense, nearest, layers, topk)."""
+    dense, nearest, layers, topk, elias)."""
     out = []
     tb = lambda f, r=reps: time_back_to_back(torch, stream, f, r)  # noqa: E731
     want = lambda name: only is None or only in name  # noqa: E731
@@ -278,6 +278,53 @@ def suite(torch, gq, WL, stream, reps: int, only: str | None = None):
         out += suite_layers(torch, gq, WL, stream, tb)
     if want("topk"):
         out += suite_topk(torch, gq, WL, stream, tb)
+    if want("elias"):
+        out += suite_elias(torch, gq, WL, stream, tb)
+    return out
+
+
+def suite_elias(torch, gq, WL, stream, tb):
+    """Elias gamma coding of the 25.6M layered gradient's codes (d = 512),
+    QSGD s = 4 and ternary s = 1: encode (count, scan and record passes) and
+    decode, two alternating payloads.  Moved bytes: encode reads the codes
+    twice and writes the stream and the offsets; decode reads the stream and
+    offsets and writes the codes."""
+    import numpy as np
+
+    import oracle as O
+    out = []
+    hosts = [WL.ternary_gradient(0), WL.ternary_gradient(1)]
+    G = [torch.from_numpy(h).cuda() for h in hosts]
+    n = G[0].numel()
+    for s in (4, 1):
+        d = gq.desc(gq.GQ_UNIFORM, 512, s=s)
+        cb, cap, mf = gq.gq_payload_size(d, n)
+        P = [gq.alloc_payload(d, n) for _ in range(2)]
+        for k in range(2):
+            gq.gq_quantize(d, G[k], None, 2, k, P[k][0], P[k][1], stream)
+        S = [gq.alloc_elias(d, n) for _ in range(2)]
+        back = [torch.empty(cap, dtype=torch.uint8, device="cuda") for _ in range(2)]
+        ms = tb(lambda i: gq.gq_elias_encode(d, n, P[i % 2][0], S[i % 2][0],
+                                             S[i % 2][1], stream))
+        torch.cuda.synchronize()
+        nb = S[0][0].numel() - 1
+        nw = int(S[0][0][-1].item())
+        codes_h = P[0][0][:cb].cpu().numpy()
+        oracle = time_oracle(lambda k: O.elias_encode(512, s, k, codes_h), n, 512)
+        stream_bytes = 4 * nw + 8 * (nb + 1)
+        extra = {"bits_per_element": round(32 * nw / n, 4),
+                 "fixed_bits": 8 * cb / n,
+                 "compression_vs_fp32": round(4 * n / (stream_bytes + 4 * mf), 3),
+                 "compression_fixed": round(4 * n / (cb + 4 * mf), 3)}
+        out.append(entry(f"elias encode s={s} d=512 n={n}", ms,
+                         2 * cb + 4 * nw + 3 * 8 * nb, n, extra={**extra, **oracle}))
+        ms = tb(lambda i: gq.gq_elias_decode(d, n, S[i % 2][0], S[i % 2][1],
+                                             back[i % 2], stream=stream))
+        out.append(entry(f"elias decode s={s} d=512 n={n}", ms,
+                         4 * nw + 8 * (nb + 1) + cb, n, bound="latency"))
+        torch.cuda.synchronize()
+        assert torch.equal(back[0][:cb], P[0][0][:cb])
+        del P, S, back
     return out
 
 
@@ -611,7 +658,8 @@ def main() -> int:
     ap.add_argument("--suite", choices=("main", "all"), default="all")
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--only", choices=("qsgd", "orq", "bingrad", "workers",
-                                       "dense", "nearest", "layers", "topk"),
+                                       "dense", "nearest", "layers", "topk",
+                                       "elias"),
                     help="time only this workload's kernels after the headline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--counters", action="store_true",

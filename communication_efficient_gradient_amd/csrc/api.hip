@@ -320,4 +320,56 @@ int gq_dequantize_accumulate_layers(const gq_desc* desc, int64_t n, int32_t nl,
                                             static_cast<hipStream_t>(stream)));
 }
 
+// Elias gamma coding: GQ_UNIFORM payloads in the fixed-width layout only.
+static int check_elias(const gq_desc* desc, int64_t n, gq::LaunchDesc* L) {
+  int rc = check_desc(desc, L);
+  if (rc) return rc;
+  if (L->scheme != GQ_UNIFORM || L->dense) return GQ_EUNSUPPORTED;
+  if (n < 1 || n > kMaxN) return GQ_EINVAL;
+  return GQ_OK;
+}
+
+int gq_elias_max_words(const gq_desc* desc, int64_t n, int64_t* max_words) {
+  gq::LaunchDesc L;
+  int rc = check_elias(desc, n, &L);
+  if (rc) return rc;
+  if (!max_words) return GQ_EINVAL;
+  *max_words = gq::elias_max_words(L, n);
+  return GQ_OK;
+}
+
+int gq_elias_encode(const gq_desc* desc, int64_t n, const uint8_t* codes,
+                    uint64_t* offsets, uint32_t* words, void* stream) {
+  gq::LaunchDesc L;
+  int rc = check_elias(desc, n, &L);
+  if (rc) return rc;
+  if (!codes || !offsets || !words) return GQ_EINVAL;
+  if (!aligned16(codes) || !aligned16(offsets) || !aligned16(words)) return GQ_EINVAL;
+  const int64_t cap = (code_bytes_of(L, n) + 15) / 16 * 16;
+  const int64_t ob = 8 * ((n + L.d - 1) / L.d + 1);
+  const int64_t wb = 4 * gq::elias_max_words(L, n);
+  if (overlap(codes, cap, offsets, ob) || overlap(codes, cap, words, wb) ||
+      overlap(offsets, ob, words, wb))
+    return GQ_EINVAL;
+  return launch_status(gq::launch_elias_encode(L, n, codes, offsets, words,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int gq_elias_decode(const gq_desc* desc, int64_t n, const uint64_t* offsets,
+                    const uint32_t* words, int64_t n_words, uint8_t* codes,
+                    void* stream) {
+  gq::LaunchDesc L;
+  int rc = check_elias(desc, n, &L);
+  if (rc) return rc;
+  if (!codes || !offsets || !words || n_words < 1) return GQ_EINVAL;
+  if (!aligned16(codes) || !aligned16(offsets) || !aligned16(words)) return GQ_EINVAL;
+  const int64_t cap = (code_bytes_of(L, n) + 15) / 16 * 16;
+  const int64_t ob = 8 * ((n + L.d - 1) / L.d + 1);
+  if (overlap(codes, cap, offsets, ob) || overlap(codes, cap, words, 4 * n_words))
+    return GQ_EINVAL;
+  return launch_status(gq::launch_elias_decode(L, n, offsets, words, n_words,
+                                               codes,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

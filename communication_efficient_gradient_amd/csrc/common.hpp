@@ -590,6 +590,14 @@ int launch_topk_quant(const LaunchDesc& L, int64_t n, const float* g, float* e,
                       float* meta, hipStream_t st);
 int launch_topk_deq(const LaunchDesc& L, int64_t n, int W, const PayloadPtrs& pp,
                     float alpha, float beta, float* out, hipStream_t st);
+// Elias gamma coding of uniform-scheme codes: worst-case stream words,
+// encode (three launches: counts, scan, records), decode (codes re-packed)
+int64_t elias_max_words(const LaunchDesc& L, int64_t n);
+int launch_elias_encode(const LaunchDesc& L, int64_t n, const uint8_t* codes,
+                        uint64_t* off, uint32_t* words, hipStream_t st);
+int launch_elias_decode(const LaunchDesc& L, int64_t n, const uint64_t* off,
+                        const uint32_t* words, int64_t n_words, uint8_t* codes,
+                        hipStream_t st);
 // per-layer scale (uniform scheme): max-abs pass then rounding pass
 // (codes == nullptr: the max-abs pass only)
 int launch_layer_quant(const LaunchDesc& L, int64_t n, int nl,

@@ -28,6 +28,7 @@ GQ_MAX_PAYLOADS = 16
 SYMBOLS = ("gq_code_bits", "gq_payload_size", "gq_select_levels",
            "gq_quantize", "gq_error_feedback", "gq_dequantize_accumulate",
            "gq_quantize_layers", "gq_dequantize_accumulate_layers",
+           "gq_elias_max_words", "gq_elias_encode", "gq_elias_decode",
            "gq_strerror", "gq_version")
 
 
@@ -71,6 +72,9 @@ def _load():
     lib.gq_dequantize_accumulate_layers.argtypes = [
         D, i64, i32, P, i32, C.POINTER(P), C.POINTER(P), C.c_float, C.c_float,
         P, P]
+    lib.gq_elias_max_words.argtypes = [D, i64, C.POINTER(i64)]
+    lib.gq_elias_encode.argtypes = [D, i64, P, P, P, P]
+    lib.gq_elias_decode.argtypes = [D, i64, P, P, i64, P, P]
     lib.gq_strerror.argtypes = [C.c_int]
     lib.gq_strerror.restype = C.c_char_p
     lib.gq_version.argtypes = []
@@ -274,6 +278,54 @@ def gq_dequantize_accumulate_layers(d: gq_desc, n: int,
 # Prepared calls: validate and marshal the arguments once, then re-issue the
 # same launch with only (seed, step) changing.  For launch loops where the
 # per-call Python checks above would otherwise dominate a ~10 us kernel.
+def gq_elias_max_words(d: gq_desc, n: int) -> int:
+    w = C.c_int64()
+    _check(_lib.gq_elias_max_words(C.byref(d), n, C.byref(w)), "gq_elias_max_words")
+    return w.value
+
+
+def alloc_elias(d: gq_desc, n: int, device="cuda"):
+    """Device buffers for one Elias stream: (offsets i64[nb + 1], words
+    i32[gq_elias_max_words]); the bits are those of the C ABI's uint64 /
+    uint32 arrays."""
+    nb = (n + d.bucket - 1) // d.bucket
+    off = torch.empty(nb + 1, dtype=torch.int64, device=device)
+    words = torch.empty(max(gq_elias_max_words(d, n), 1), dtype=torch.int32,
+                        device=device)
+    return off, words
+
+
+def gq_elias_encode(d: gq_desc, n: int, codes: torch.Tensor,
+                    offsets: torch.Tensor, words: torch.Tensor,
+                    stream=None) -> None:
+    """Elias gamma stream of a gq_quantize payload's codes."""
+    _, cap, _ = gq_payload_size(d, n)
+    _need(codes, cap, "codes")
+    _need(offsets, (n + d.bucket - 1) // d.bucket + 1, "offsets")
+    _need(words, gq_elias_max_words(d, n), "words")
+    _check(_lib.gq_elias_encode(
+        C.byref(d), n, _ptr(codes, torch.uint8, "codes"),
+        _ptr(offsets, torch.int64, "offsets"), _ptr(words, torch.int32, "words"),
+        _stream(stream, codes)), "gq_elias_encode")
+
+
+def gq_elias_decode(d: gq_desc, n: int, offsets: torch.Tensor,
+                    words: torch.Tensor, codes: torch.Tensor,
+                    n_words: int | None = None, stream=None) -> None:
+    """Fixed-width codes back from an Elias stream (n_words: the readable
+    length of words, default its size)."""
+    _, cap, _ = gq_payload_size(d, n)
+    _need(codes, cap, "codes")
+    _need(offsets, (n + d.bucket - 1) // d.bucket + 1, "offsets")
+    nw = words.numel() if n_words is None else int(n_words)
+    if nw > words.numel():
+        raise ValueError("n_words exceeds the words tensor")
+    _check(_lib.gq_elias_decode(
+        C.byref(d), n, _ptr(offsets, torch.int64, "offsets"),
+        _ptr(words, torch.int32, "words"), nw, _ptr(codes, torch.uint8, "codes"),
+        _stream(stream, codes)), "gq_elias_decode")
+
+
 class PreparedQuantize:
     def __init__(self, d: gq_desc, g: torch.Tensor, e: torch.Tensor | None,
                  codes: torch.Tensor, meta: torch.Tensor, stream=None):

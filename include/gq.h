@@ -217,6 +217,41 @@ int gq_dequantize_accumulate_layers(const gq_desc* desc, int64_t n, int32_t nl,
                                     const float* const* meta, float alpha,
                                     float beta, float* out, void* stream);
 
+/* Elias gamma coding of GQ_UNIFORM codes, the lossless integer coding QSGD
+ * applies after quantizing ("Gradient Quantization" glossary, QSGD
+ * paragraph).  Code c (in element order) is written as the Elias gamma code
+ * of m = |c| + 1 (floor(log2 m) zero bits, then the floor(log2 m) + 1 binary
+ * digits of m, most significant first) followed, when c != 0, by one sign
+ * bit (1 = negative): 0 takes 1 bit, +-1 and +-2 take 4, +-3 .. +-6 take 6.
+ * Stream bit t is bit t mod 32 of 32-bit word t / 32.  Each bucket's record
+ * starts on a word; pad bits are 0.  offsets: nb + 1 uint64 word offsets,
+ * offsets[j] = first word of bucket j's record, offsets[0] = 0,
+ * offsets[nb] = words used; a receiver needs them with the words.
+ * desc: GQ_UNIFORM without GQ_FLAG_DENSE (GQ_EUNSUPPORTED otherwise;
+ * GQ_FLAG_NEAREST does not change the codes' layout). */
+
+/* Words the stream needs at most: every code with |c| = s.  Host-only. */
+int gq_elias_max_words(const gq_desc* desc, int64_t n, int64_t* max_words);
+
+/* Encode the n codes of a gq_quantize payload (codes: code_capacity bytes,
+ * fixed-width layout) into words (gq_elias_max_words words) and offsets
+ * (nb + 1).  Codes outside [-s, s] (never written by gq_quantize) are
+ * clamped to that range.  Three launches; offsets doubles as the scan's
+ * workspace, so no other memory is used.  codes, offsets and words must not
+ * overlap. */
+int gq_elias_encode(const gq_desc* desc, int64_t n, const uint8_t* codes,
+                    uint64_t* offsets, uint32_t* words, void* stream);
+
+/* Decode an Elias stream back into the fixed-width codes gq_quantize wrote
+ * (bit-identical for a stream from gq_elias_encode), ready for
+ * gq_dequantize_accumulate.  n_words >= 1: the readable length of words
+ * (reads stay below it; offsets are clamped to it).  Writes ceil(code_bytes / 4)
+ * 32-bit words of codes (capacity: code_capacity bytes).  A corrupt stream
+ * gives unspecified codes but no out-of-bounds access. */
+int gq_elias_decode(const gq_desc* desc, int64_t n, const uint64_t* offsets,
+                    const uint32_t* words, int64_t n_words, uint8_t* codes,
+                    void* stream);
+
 /* Static description of a status code. */
 const char* gq_strerror(int status);
 

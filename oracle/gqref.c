@@ -1067,19 +1067,24 @@ int gqref_elias_encode(int d, int s, int64_t n, const uint8_t *codes,
   int b = gqref_bits(UNIFORM, s, 2);
   if (b < 0 || d < 64 || (d & (d - 1)) || n < 1 || !codes || !off) return -1;
   int64_t nb = (n + d - 1) / d;
-  /* lengths first: the word offsets */
-  off[0] = 0;
+  int bad = 0;
+  /* each record's length, then the word offsets as their running sum */
+#pragma omp parallel for schedule(static) reduction(| : bad)
   for (int64_t j = 0; j < nb; ++j) {
     int64_t nj = (n - j * d < d) ? n - j * d : d, bits = 0;
     for (int64_t t = 0; t < nj; ++t) {
       int32_t c = sext(get_code(codes, j * d + t, b), b);
-      if (c < -s || c > s) return -1;
+      if (c < -s || c > s) bad = 1;
       bits += gamma_bits(c);
     }
-    off[j + 1] = off[j] + (uint64_t)((bits + 31) / 32);
+    off[j + 1] = (uint64_t)((bits + 31) / 32);
   }
+  if (bad) return -1;
+  off[0] = 0;
+  for (int64_t j = 0; j < nb; ++j) off[j + 1] += off[j];
   if (!words) return 0;
   memset(words, 0, (size_t)off[nb] * 4);
+#pragma omp parallel for schedule(static)
   for (int64_t j = 0; j < nb; ++j) {
     int64_t nj = (n - j * d < d) ? n - j * d : d;
     uint32_t *rec = words + off[j];
@@ -1096,33 +1101,45 @@ int gqref_elias_encode(int d, int s, int64_t n, const uint8_t *codes,
   return 0;
 }
 
+static int decode_record(const uint32_t *rec, int64_t tmax, int64_t nj, int b,
+                         int s, int64_t e0, uint8_t *codes) {
+  int64_t t = 0;
+  for (int64_t i = 0; i < nj; ++i) {
+    int L = 0;
+    while (t < tmax && word_get_bit(rec, t) == 0) { ++L; ++t; }
+    if (L > 7 || t + L + 1 > tmax) return -1;  /* |c| + 1 <= 128 */
+    uint32_t m = 0;
+    for (int k = 0; k <= L; ++k) m = (m << 1) | (uint32_t)word_get_bit(rec, t++);
+    int32_t c = (int32_t)(m - 1u);
+    if (c > s) return -1;
+    if (c != 0) {
+      if (t >= tmax) return -1;
+      if (word_get_bit(rec, t++)) c = -c;
+    }
+    put_code(codes, e0 + i, b, (uint32_t)c & ((1u << b) - 1u));
+  }
+  return 0;
+}
+
 int gqref_elias_decode(int d, int s, int64_t n, const uint64_t *off,
                        const uint32_t *words, uint8_t *codes) {
   int b = gqref_bits(UNIFORM, s, 2);
   if (b < 0 || d < 64 || (d & (d - 1)) || n < 1 || !off || !words || !codes)
     return -1;
   int64_t nb = (n + d - 1) / d;
+  for (int64_t j = 0; j < nb; ++j)
+    if (off[j + 1] < off[j]) return -1;
   memset(codes, 0, (size_t)((n * b + 7) / 8));
+  int bad = 0;
+  /* buckets own whole bytes of codes (d * b is a multiple of 8) */
+#pragma omp parallel for schedule(static) reduction(| : bad)
   for (int64_t j = 0; j < nb; ++j) {
     int64_t nj = (n - j * d < d) ? n - j * d : d;
-    const uint32_t *rec = words + off[j];
-    int64_t t = 0, tmax = 32 * (int64_t)(off[j + 1] - off[j]);
-    for (int64_t i = 0; i < nj; ++i) {
-      int L = 0;
-      while (t < tmax && word_get_bit(rec, t) == 0) { ++L; ++t; }
-      if (L > 7 || t + L + 1 > tmax) return -1;  /* |c| + 1 <= 128 */
-      uint32_t m = 0;
-      for (int k = 0; k <= L; ++k) m = (m << 1) | (uint32_t)word_get_bit(rec, t++);
-      int32_t c = (int32_t)(m - 1u);
-      if (c > s) return -1;
-      if (c != 0) {
-        if (t >= tmax) return -1;
-        if (word_get_bit(rec, t++)) c = -c;
-      }
-      put_code(codes, j * d + i, b, (uint32_t)c & ((1u << b) - 1u));
-    }
+    if (decode_record(words + off[j], 32 * (int64_t)(off[j + 1] - off[j]), nj,
+                      b, s, j * d, codes))
+      bad = 1;
   }
-  return 0;
+  return bad ? -1 : 0;
 }
 
 void gqref_set_threads(int t) {

@@ -227,3 +227,33 @@ def test_topk_rules_and_sizes(gq):
     assert L.gq_select_levels(C.byref(d), 100, fake, None, fake * 2, None) == gq.GQ_EUNSUPPORTED
     assert L.gq_error_feedback(C.byref(d), 100, fake, fake * 2, fake * 3, fake * 4,
                                None) == gq.GQ_EUNSUPPORTED
+
+
+def test_elias_rules_and_sizes(gq):
+    """Elias coding: GQ_UNIFORM in the fixed-width layout only; the worst-case
+    size agrees with the oracle's; argument errors are found on the host."""
+    import oracle as O
+    L = gq.lib()
+    fake = 1 << 20
+    for d, s, n in [(64, 1, 1), (512, 4, 25_600_000), (4096, 127, 100_003),
+                    (128, 2, 129), (32768, 7, 3 * 32768 + 1)]:
+        assert gq.gq_elias_max_words(gq.desc(gq.GQ_UNIFORM, d, s), n) == \
+            O.elias_max_words(d, s, n)
+    for kw in (dict(scheme=gq.GQ_ORQ, levels=5), dict(scheme=gq.GQ_BIN_SIGN),
+               dict(scheme=gq.GQ_UNIFORM, s=1, flags=gq.GQ_FLAG_DENSE),
+               dict(scheme=gq.GQ_TOPK, s=4, levels=26)):
+        with pytest.raises(gq.GQError) as ex:
+            gq.gq_elias_max_words(gq.desc(bucket=512, **kw), 1000)
+        assert ex.value.status == gq.GQ_EUNSUPPORTED
+    d = gq.desc(gq.GQ_UNIFORM, 512, 4, flags=gq.GQ_FLAG_NEAREST)
+    assert gq.gq_elias_max_words(d, 1000) == O.elias_max_words(512, 4, 1000)
+    enc, dec = L.gq_elias_encode, L.gq_elias_decode
+    assert enc(C.byref(d), 0, fake, fake * 2, fake * 3, None) == gq.GQ_EINVAL
+    assert enc(C.byref(d), 1000, None, fake * 2, fake * 3, None) == gq.GQ_EINVAL
+    assert enc(C.byref(d), 1000, fake, fake * 2 + 8, fake * 3, None) == gq.GQ_EINVAL
+    assert enc(C.byref(d), 1000, fake, fake + 64, fake * 3, None) == gq.GQ_EINVAL
+    assert dec(C.byref(d), 1000, fake, fake * 2, 0, fake * 3, None) == gq.GQ_EINVAL
+    assert dec(C.byref(d), 1000, fake, fake * 2, 10, fake * 2 + 16,
+               None) == gq.GQ_EINVAL                           # codes overlap words
+    assert dec(C.byref(gq.desc(gq.GQ_ORQ, 512, levels=5)), 1000, fake, fake * 2,
+               10, fake * 3, None) == gq.GQ_EUNSUPPORTED
