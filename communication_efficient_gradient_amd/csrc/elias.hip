@@ -6,12 +6,13 @@
 // off[j] is the first word of record j and off[nb] the stream's length.
 //
 // Encode: three launches, no scratch memory.
-//   1. k_elias_count: a block owns kChunk consecutive buckets, a wave one
-//      bucket at a time.  Each bucket's word count, then the chunk's
-//      inclusive scan: off[j + 1] = words of the chunk's buckets up to j.
+//   1. k_elias_count: a block owns kChunk consecutive buckets, a wave
+//      kPerWave of them (their loads issued together).  Each bucket's word
+//      count, then the chunk's inclusive scan: off[j + 1] = words of the
+//      chunk's buckets up to j.
 //   2. k_elias_scan: one block turns the chunk totals (each sits at its
 //      chunk's last entry) into global inclusive sums in place; off[0] = 0.
-//   3. k_elias_write: one wave per bucket.  Its record starts at
+//   3. k_elias_write: one wave (and block) per bucket.  Record j starts at
 //      off[chunk start] + off[j] (entries at chunk starts are final after
 //      step 2; the wave writes the final off[j] back).  Per segment of 64 G
 //      elements, lane l takes G consecutive codes, a wave scan of their bit
@@ -19,17 +20,25 @@
 //      32 at a time, and the segment's whole words go out; the last partial
 //      word carries into the next segment.
 // Decode: one lane per bucket parses its record serially from a 64-bit
-// window kept above 32 bits from a ring of kLook words loaded ahead, and
-// packs the codes back into the fixed-width layout 32 bits at a time.
+// window kept above 32 bits.  A step looks the window's next kLutBits bits
+// up in an LDS table of the whole codewords they hold (codes already in the
+// b-bit output format) and takes them all; a longer codeword is decoded
+// directly.  The window is fed from an LDS row of the lane's next kRow
+// stream words, staged with kRow independent loads and restaged for the
+// whole wave when some lane has used its row.
 #include "common.hpp"
 
 namespace gq {
 namespace {
 
-constexpr int kWaves = 4;     // waves per block (count and write passes)
-constexpr int kChunk = 64;    // buckets per block in the count pass
+constexpr int kChunk = 64;       // buckets per block in the count pass
+constexpr int kCountWaves = 16;  // waves per block of the count pass
+constexpr int kPerWave = kChunk / kCountWaves;
 constexpr int kScan = 1024;   // threads of the one-block scan
-constexpr int kLook = 4;      // decode: words loaded ahead of the window
+constexpr int kDecWaves = 1;  // waves per block of the decoder
+constexpr int kRow = 32;      // decode: stream words staged per lane
+constexpr int kLutBits = 10;  // decode: stream bits that index the table
+constexpr int kLut = 1 << kLutBits;
 
 __device__ __forceinline__ int sext_clamp(uint32_t raw, int b, int s) {
   const int c = (int)(raw << (32 - b)) >> (32 - b);
@@ -54,29 +63,53 @@ __device__ __forceinline__ uint64_t stream_bits(const uint32_t* __restrict__ w,
   return v >> sh;
 }
 
+// Inclusive prefix sum over the wave: shifts of 1, 2, 4, 8 lanes inside
+// each row of 16 (lanes shifted in from outside the row read 0), then each
+// row's total broadcast into the rows above it (lane 15 into rows 1 and 3,
+// lane 31 into rows 2 and 3).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = (uint32_t)__shfl_up((int)v, o, 64);
-    if (lane >= o) v += t;
-  }
-  return v;
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false); // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false); // row_bcast:31
+  return (uint32_t)x;
 }
 
-// Lane's G codes of a segment: count of live ones and their gamma fields.
+// Per-code tables for code widths b <= 4 (raw b-bit code r, clamped to
+// [-s, s]): len = bits [4r, 4r + 4) of len_t; field = byte r of
+// field_t[r / 8] (gamma codewords of |c| <= 7 fit in 8 bits).  b = 8 uses
+// gamma_field directly.
+struct GammaTab {
+  uint64_t len_t;
+  uint64_t field_t[2];
+};
+
+// The lane's G codes of a segment, starting at element e0 (ge of them live).
 template <int G>
-__device__ __forceinline__ int lane_fields(const uint32_t* __restrict__ codes,
-                                           int64_t e0, int ge, int b, int s,
-                                           uint32_t (&f)[G], int (&l)[G]) {
-  uint64_t x = 0;
-  if (ge > 0) x = stream_bits(codes, e0 * b, ge * b);
+__device__ __forceinline__ uint64_t lane_codes(const uint32_t* __restrict__ codes,
+                                               int64_t e0, int ge, int b) {
+  return ge > 0 ? stream_bits(codes, e0 * b, ge * b) : 0ull;
+}
+
+// Gamma fields and lengths of the lane's codes; returns their total bits.
+template <int G>
+__device__ __forceinline__ int lane_fields(uint64_t x, int ge, int b, int s,
+                                           const GammaTab& T, uint32_t (&f)[G],
+                                           int (&l)[G]) {
   const uint32_t mask = (1u << b) - 1u;
   int tot = 0;
 #pragma unroll
   for (int k = 0; k < G; ++k) {
-    const int c = sext_clamp((uint32_t)(x >> (k * b)) & mask, b, s);
-    f[k] = gamma_field(c, l[k]);
+    const uint32_t r = (uint32_t)(x >> (k * b)) & mask;
+    if (b <= 4) {
+      l[k] = (int)((T.len_t >> (4 * r)) & 15u);
+      f[k] = (uint32_t)((T.field_t[r >> 3] >> (8 * (r & 7))) & 255u);
+    } else {
+      f[k] = gamma_field(sext_clamp(r, b, s), l[k]);
+    }
     if (k >= ge) {
       f[k] = 0u;
       l[k] = 0;
@@ -86,34 +119,66 @@ __device__ __forceinline__ int lane_fields(const uint32_t* __restrict__ codes,
   return tot;
 }
 
+// Total gamma bits of the lane's codes (lengths only).
 template <int G>
-__global__ __launch_bounds__(64 * kWaves) void k_elias_count(
-    int64_t n, int64_t nb, int d, int b, int s,
+__device__ __forceinline__ int lane_bits(uint64_t x, int ge, int b, int s,
+                                         uint64_t len_t) {
+  const uint32_t mask = (1u << b) - 1u;
+  int tot = 0;
+#pragma unroll
+  for (int k = 0; k < G; ++k) {
+    const uint32_t r = (uint32_t)(x >> (k * b)) & mask;
+    int len;
+    if (b <= 4) {
+      len = (int)((len_t >> (4 * r)) & 15u);
+    } else {
+      const int c = sext_clamp(r, b, s);
+      const int a = c < 0 ? -c : c;
+      len = c == 0 ? 1 : 2 * (31 - __clz(a + 1)) + 2;
+    }
+    tot += k < ge ? len : 0;
+  }
+  return tot;
+}
+
+// kCountWaves waves per block, kPerWave buckets per wave: the loads of a
+// wave's buckets are issued together.
+template <int G>
+__global__ __launch_bounds__(64 * kCountWaves) void k_elias_count(
+    int64_t n, int64_t nb, int d, int b, int s, uint64_t len_t,
     const uint32_t* __restrict__ codes, uint64_t* __restrict__ off) {
   __shared__ uint32_t cnt[kChunk];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t j0 = (int64_t)blockIdx.x * kChunk;
-  for (int t = wave; t < kChunk; t += kWaves) {
-    const int64_t j = j0 + t;
-    uint32_t bits = 0;
-    if (j < nb) {
-      const int64_t base = j * d;
-      const int nj = (int)((n - base) < d ? (n - base) : d);
-      for (int seg = 0; seg < nj; seg += 64 * G) {
-        const int i0 = seg + lane * G;
-        const int ge = max(0, min(G, nj - i0));
-        uint32_t f[G];
-        int l[G];
-        bits += (uint32_t)lane_fields<G>(codes, base + i0, ge, b, s, f, l);
-      }
-      bits = (uint32_t)group_sum_i<64>((int)bits);
+  const int64_t j0 = (int64_t)blockIdx.x * kChunk + wave * kPerWave;
+  int nj[kPerWave];
+#pragma unroll
+  for (int t = 0; t < kPerWave; ++t) {
+    const int64_t r = n - (j0 + t) * d;
+    nj[t] = j0 + t < nb ? (int)(r < d ? r : d) : 0;
+  }
+  int bits[kPerWave] = {};
+  const int nseg = d / (64 * G);
+  for (int sg = 0; sg < nseg; ++sg) {
+    const int i0 = sg * 64 * G + lane * G;
+    uint64_t x[kPerWave];
+    int ge[kPerWave];
+#pragma unroll
+    for (int t = 0; t < kPerWave; ++t) {
+      ge[t] = max(0, min(G, nj[t] - i0));
+      x[t] = lane_codes<G>(codes, (j0 + t) * d + i0, ge[t], b);
     }
-    if (lane == 0) cnt[t] = (bits + 31u) >> 5;
+#pragma unroll
+    for (int t = 0; t < kPerWave; ++t) bits[t] += lane_bits<G>(x[t], ge[t], b, s, len_t);
+  }
+#pragma unroll
+  for (int t = 0; t < kPerWave; ++t) {
+    const uint32_t tb = (uint32_t)group_sum_i<64>(bits[t]);
+    if (lane == 0) cnt[wave * kPerWave + t] = (tb + 31u) >> 5;
   }
   __syncthreads();
   if (wave == 0) {
     const uint32_t v = wave_incl_scan(cnt[lane]);
-    const int64_t j = j0 + lane;
+    const int64_t j = (int64_t)blockIdx.x * kChunk + lane;
     if (j < nb) off[j + 1] = v;
   }
 }
@@ -146,37 +211,32 @@ __global__ __launch_bounds__(kScan) void k_elias_scan(int64_t nb,
 }
 
 template <int G>
-__global__ __launch_bounds__(64 * kWaves) void k_elias_write(
-    int64_t n, int64_t nb, int d, int b, int s, int64_t cap,
+__global__ __launch_bounds__(64) void k_elias_write(
+    int64_t n, int64_t nb, int d, int b, int s, int64_t cap, GammaTab T,
     const uint32_t* __restrict__ codes, uint64_t* __restrict__ off,
     uint32_t* __restrict__ words) {
   // worst segment: 64 G codes of 16 bits, shifted by up to 31 carried bits
   constexpr int kWin = 32 * G + 2;
-  __shared__ uint32_t win_all[kWaves][kWin];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t* win = win_all[wave];
-  const int64_t j = (int64_t)blockIdx.x * kWaves + wave;
-  const bool live = j < nb;
-  int64_t start = 0;
-  int nj = 0;
-  if (live) {
-    const int64_t cs = j - j % kChunk;
-    const uint64_t oj = off[j];
-    start = (int64_t)(j == cs ? oj : off[cs] + oj);
-    nj = (int)((n - j * d) < d ? (n - j * d) : d);
-  }
-  if (live && j % kChunk != 0 && lane == 0) off[j] = (uint64_t)start;
+  __shared__ uint32_t win[kWin];
+  const int lane = threadIdx.x;
+  const int64_t j = blockIdx.x;
+  const int64_t cs = j - j % kChunk;  // the chunk's first bucket
+  const uint64_t oj = off[j];
+  const int64_t start = (int64_t)(j == cs ? oj : off[cs] + oj);
+  const int nj = (int)((n - j * d) < d ? (n - j * d) : d);
+  if (j != cs && lane == 0) off[j] = (uint64_t)start;
   uint32_t carry = 0;  // low bits of the record's current partial word
   int pos = 0;         // record bits written so far
-  const int nseg = d / (64 * G);  // the same for every wave of the block
+  const int nseg = d / (64 * G);
   for (int sg = 0; sg < nseg; ++sg) {
     const int i0 = sg * 64 * G + lane * G;
     const int ge = max(0, min(G, nj - i0));
     uint32_t f[G];
     int l[G];
-    const int tot = lane_fields<G>(codes, j * d + i0, ge, b, s, f, l);
+    const int tot =
+        lane_fields<G>(lane_codes<G>(codes, j * d + i0, ge, b), ge, b, s, T, f, l);
     const int incl = (int)wave_incl_scan((uint32_t)tot);
-    const int seg_bits = __shfl(incl, 63, 64);
+    const int seg_bits = __builtin_amdgcn_readlane(incl, 63);
     const int p0 = pos & 31;
     const int nw = (p0 + seg_bits + 31) >> 5;
     for (int w = lane; w < nw; w += 64) win[w] = w == 0 ? carry : 0u;
@@ -203,70 +263,143 @@ __global__ __launch_bounds__(64 * kWaves) void k_elias_write(
     const int64_t w0 = start + (pos >> 5);
     // cap (the worst-case stream length) is a guard only: records sized by
     // the count pass never reach it
-    if (live)
-      for (int w = lane; w < full; w += 64)
-        if (w0 + w < cap) words[w0 + w] = win[w];
+    for (int w = lane; w < full; w += 64)
+      if (w0 + w < cap) words[w0 + w] = win[w];
     carry = ((p0 + seg_bits) & 31) ? win[full] : 0u;
     pos += seg_bits;
     __syncthreads();
   }
-  if (live && lane == 0 && (pos & 31) && start + (pos >> 5) < cap)
+  if (lane == 0 && (pos & 31) && start + (pos >> 5) < cap)
     words[start + (pos >> 5)] = carry;
 }
 
-__global__ __launch_bounds__(256) void k_elias_decode(
+// Decode table entry for the next kLutBits stream bits v: the complete
+// codewords they hold from bit 0, as codes packed b bits each (at most 32
+// bits of codes), their count k and their total length.  k = 0: the first
+// codeword is longer than kLutBits (or v holds no whole codeword).
+constexpr uint64_t lut_entry(uint32_t v, int b) {
+  const uint32_t mask = (1u << b) - 1u;
+  uint32_t out = 0;
+  int k = 0, pos = 0;
+  for (;;) {
+    const uint32_t rest = v >> pos;
+    if (rest == 0) break;  // only zeros left: no codeword ends here
+    int L = 0;
+    while (((rest >> L) & 1u) == 0) ++L;
+    const int len = L == 0 ? 1 : 2 * L + 2;
+    if (pos + len > kLutBits || (k + 1) * b > 32) break;
+    uint32_t m = 0;  // the L + 1 digits, most significant first
+    for (int t = 0; t <= L; ++t) m = (m << 1) | ((rest >> (L + t)) & 1u);
+    int c = (int)m - 1;
+    if (L > 0 && ((rest >> (2 * L + 1)) & 1u)) c = -c;
+    out |= ((uint32_t)c & mask) << (k * b);
+    ++k;
+    pos += len;
+  }
+  return (uint64_t)out | ((uint64_t)k << 32) | ((uint64_t)pos << 40);
+}
+
+// The decode tables of the four code widths, built at compile time.
+struct DecodeLut {
+  uint64_t e[kLut];
+  constexpr explicit DecodeLut(int b) : e{} {
+    for (uint32_t v = 0; v < (uint32_t)kLut; ++v) e[v] = lut_entry(v, b);
+  }
+};
+__device__ constexpr DecodeLut kLut2{2};
+__device__ constexpr DecodeLut kLut3{3};
+__device__ constexpr DecodeLut kLut4{4};
+__device__ constexpr DecodeLut kLut8{8};
+
+__global__ __launch_bounds__(64 * kDecWaves) void k_elias_decode(
     int64_t n, int64_t nb, int d, int b, int64_t n_words,
     const uint64_t* __restrict__ off, const uint32_t* __restrict__ words,
     uint32_t* __restrict__ codes) {
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (j >= nb) return;
+  __shared__ uint64_t lut[kLut];
+  // each lane's next kRow stream words (padded rows: no bank conflicts when
+  // every lane stages word k at once)
+  __shared__ uint32_t rows_all[kDecWaves][64][kRow + 1];
+  const uint64_t* src =
+      b == 2 ? kLut2.e : (b == 3 ? kLut3.e : (b == 4 ? kLut4.e : kLut8.e));
+  for (int t = threadIdx.x; t < kLut; t += 64 * kDecWaves) lut[t] = src[t];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t j = ((int64_t)blockIdx.x * kDecWaves + wave) * 64 + lane;
+  const bool live = j < nb;
+  uint32_t* row = rows_all[wave][lane];
   const uint64_t lim = (uint64_t)n_words;  // >= 1
-  const uint64_t a = min(off[j], lim);
-  const uint64_t e = min(max(off[j + 1], a), lim);
-  // ring slot r holds stream word widx + r; loads are unconditional (index
-  // clamped into the stream) and words past the record are zeroed when used,
-  // so a slot's load is only waited for when the slot is consumed
-  uint32_t ring[kLook];
+  uint64_t base = 0, e = 0;                // row[0] holds stream word base
+  int nj = 0;
+  if (live) {
+    base = min(off[j], lim);
+    e = min(max(off[j + 1], base), lim);
+    nj = (int)((n - j * d) < d ? (n - j * d) : d);
+  }
+  // all kRow loads of a lane are issued before the first is used; words
+  // past the record (or the readable stream) are staged as 0
+  auto restage = [&]() {
+    uint32_t v[kRow];
 #pragma unroll
-  for (int k = 0; k < kLook; ++k) ring[k] = words[min(a + k, lim - 1)];
-  uint64_t widx = a;
+    for (int k = 0; k < kRow; ++k) v[k] = words[min(base + k, lim - 1)];
+#pragma unroll
+    for (int k = 0; k < kRow; ++k) row[k] = base + k < e ? v[k] : 0u;
+  };
+  restage();
+  __syncthreads();  // the table
+  int rp = 0;       // next row word for the window
   uint64_t win = 0;
   int avail = 0;
   const uint32_t mask = (1u << b) - 1u;
   uint64_t ob = 0;
   int obits = 0;
-  int64_t ow = j * (d / 32) * b;  // the bucket's first code word
-  const int nj = (int)((n - j * d) < d ? (n - j * d) : d);
-  int i = 0;
-  while (i < nj) {
-#pragma unroll
-    for (int r = 0; r < kLook; ++r) {
-      win |= (uint64_t)(widx < e ? ring[r] : 0u) << avail;
-      avail += 32;
-      ring[r] = words[min(widx + kLook, lim - 1)];
-      ++widx;
-      for (; avail > 32 && i < nj; ++i) {
-        // a zero run longer than 15 only occurs in a corrupt stream
+  int64_t ow = j * (int64_t)(d / 32) * b;  // the bucket's first code word
+  const int64_t ow_end = ow + (((int64_t)nj * b + 31) >> 5);
+  int i = 0;  // codes decoded
+  // every step of a lane takes at least one codeword (refills: at most one
+  // row word per step), so the loop ends within d steps
+  while (__any(i < nj)) {
+    if (__any(i < nj && avail <= 32 && rp >= kRow)) {
+      base += (uint64_t)rp;
+      rp = 0;
+      restage();
+    }
+    if (i < nj) {
+      if (avail <= 32) {
+        win |= (uint64_t)row[rp] << avail;
+        avail += 32;
+        ++rp;
+      }
+      const uint64_t ent = lut[(uint32_t)win & (kLut - 1)];
+      uint32_t out = (uint32_t)ent;
+      int k = (int)(ent >> 32) & 255;
+      int len = (int)(ent >> 40) & 255;
+      if (k == 0) {
+        // one long codeword; a zero run past 15 only occurs in a corrupt stream
         const int L = __builtin_ctzll(win | (1ull << 15));
         const uint32_t dig = (uint32_t)(win >> L) & ((2u << L) - 1u);
-        const uint32_t m = __brev(dig) >> (31 - L);
+        const int mag = (int)(__brev(dig) >> (31 - L)) - 1;
         const bool neg = (win >> (2 * L + 1)) & 1ull;
-        const int mag = (int)m - 1;
-        const int c = L == 0 ? 0 : (neg ? -mag : mag);
-        const int len = L == 0 ? 1 : 2 * L + 2;
-        win >>= len;
-        avail -= len;
-        ob |= (uint64_t)((uint32_t)c & mask) << obits;
-        obits += b;
-        if (obits >= 32) {
-          codes[ow++] = (uint32_t)ob;
-          ob >>= 32;
-          obits -= 32;
-        }
+        out = (uint32_t)(L == 0 ? 0 : (neg ? -mag : mag)) & mask;
+        k = 1;
+        len = L == 0 ? 1 : 2 * L + 2;
+      }
+      if (k > nj - i) {  // codes past the bucket's last element are dropped
+        k = nj - i;
+        out &= (1u << (k * b)) - 1u;
+      }
+      win >>= len;
+      avail -= len;
+      i += k;
+      ob |= (uint64_t)out << obits;
+      obits += k * b;
+      if (obits >= 32) {
+        if (ow < ow_end) codes[ow] = (uint32_t)ob;
+        ++ow;
+        ob >>= 32;
+        obits -= 32;
       }
     }
   }
-  if (obits > 0) codes[ow] = (uint32_t)ob;
+  if (obits > 0 && ow < ow_end) codes[ow] = (uint32_t)ob;
 }
 
 }  // namespace
@@ -275,17 +408,37 @@ int64_t elias_max_words(const LaunchDesc& L, int64_t n);
 
 namespace {
 
+GammaTab gamma_tab(int b, int s) {
+  GammaTab T{0, {0, 0}};
+  if (b > 4) return T;
+  for (uint32_t r = 0; r < (1u << b); ++r) {
+    int c = (int)(r << (32 - b)) >> (32 - b);
+    c = c < -s ? -s : (c > s ? s : c);
+    const uint32_t m = (uint32_t)(c < 0 ? -c : c) + 1u;
+    int L = 0;
+    while ((m >> (L + 1)) != 0) ++L;
+    // L zeros, the L + 1 digits of m from the most significant, the sign
+    uint32_t f = 0;
+    int t = L;
+    for (int k = L; k >= 0; --k, ++t) f |= ((m >> k) & 1u) << t;
+    if (c != 0) f |= (c < 0 ? 1u : 0u) << t++;
+    T.len_t |= (uint64_t)t << (4 * r);
+    T.field_t[r >> 3] |= (uint64_t)f << (8 * (r & 7));
+  }
+  return T;
+}
+
 template <int G>
 int encode_g(const LaunchDesc& L, int64_t n, const uint32_t* codes,
              uint64_t* off, uint32_t* words, hipStream_t st) {
   const int64_t nb = (n + L.d - 1) / L.d;
   const int64_t nblk = (nb + kChunk - 1) / kChunk;
-  hipLaunchKernelGGL(k_elias_count<G>, dim3((unsigned)nblk), dim3(64 * kWaves), 0,
-                     st, n, nb, L.d, L.bits, L.s, codes, off);
+  const GammaTab T = gamma_tab(L.bits, L.s);
+  hipLaunchKernelGGL(k_elias_count<G>, dim3((unsigned)nblk), dim3(64 * kCountWaves), 0,
+                     st, n, nb, L.d, L.bits, L.s, T.len_t, codes, off);
   hipLaunchKernelGGL(k_elias_scan, dim3(1), dim3(kScan), 0, st, nb, off);
-  hipLaunchKernelGGL(k_elias_write<G>, dim3((unsigned)((nb + kWaves - 1) / kWaves)),
-                     dim3(64 * kWaves), 0, st, n, nb, L.d, L.bits, L.s,
-                     elias_max_words(L, n), codes, off, words);
+  hipLaunchKernelGGL(k_elias_write<G>, dim3((unsigned)nb), dim3(64), 0, st, n, nb,
+                     L.d, L.bits, L.s, elias_max_words(L, n), T, codes, off, words);
   return (int)hipGetLastError();
 }
 
@@ -316,7 +469,9 @@ int launch_elias_decode(const LaunchDesc& L, int64_t n, const uint64_t* off,
                         const uint32_t* words, int64_t n_words, uint8_t* codes,
                         hipStream_t st) {
   const int64_t nb = (n + L.d - 1) / L.d;
-  hipLaunchKernelGGL(k_elias_decode, dim3((unsigned)((nb + 255) / 256)), dim3(256),
+  const int64_t per_block = 64 * kDecWaves;
+  hipLaunchKernelGGL(k_elias_decode, dim3((unsigned)((nb + per_block - 1) / per_block)),
+                     dim3(64 * kDecWaves),
                      0, st, n, nb, L.d, L.bits, n_words, off, words,
                      reinterpret_cast<uint32_t*>(codes));
   return (int)hipGetLastError();
