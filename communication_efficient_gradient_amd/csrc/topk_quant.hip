@@ -9,7 +9,8 @@
 //   1. p = g (+ e); key = the bits of |p| (monotone in |p| for finite values)
 //      for real elements, -1 for absent ones; M = max |p|.
 //   2. The k = min(K, n_j)-th largest key T, bit by bit from the top: a bit
-//      stays set when at least k keys reach the candidate (counts by ballot).
+//      stays set when at least k keys reach the candidate (counts by ballot);
+//      the search stops once a single key is left between the bounds.
 //   3. Kept: key > T, and the first k - #(key > T) elements with key == T in
 //      index order.  Ranks in index order come from per-element ballots
 //      (elements before (v, lane, c) are those of earlier v, of lower lanes at
@@ -114,12 +115,32 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_topk_quant(
   const float M = group_max<64>(mloc);
 
   // ---- 2. threshold: the k-th largest key -----------------------------------
+  // After the round for bit b the k-th largest key lies in [T, T + 2^b), with
+  // c_lo keys >= T (c_lo >= kk) and c_hi keys >= T + 2^b (c_hi < kk).  Once
+  // that interval holds a single key (c_lo - c_hi = 1) it is the k-th
+  // largest: the smallest key >= T.
   const int kk = nj < K ? nj : K;
   int T = 0;
   if (kk > 0) {
-    for (int bit = 30; bit >= 0; --bit) {
+    int c_lo = nj, c_hi = 0;
+    for (int bit = 30; bit >= 0 && c_lo - c_hi > 1; --bit) {
       const int cand = T | (1 << bit);
-      if (count_ge<V>(key, cand) >= kk) T = cand;
+      const int c = count_ge<V>(key, cand);
+      if (c >= kk) {
+        T = cand;
+        c_lo = c;
+      } else {
+        c_hi = c;
+      }
+    }
+    if (c_lo - c_hi == 1) {
+      int m = 0x7fffffff;
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (key[v][c] >= T) m = min(m, key[v][c]);
+      T = group_reduce<64>(m, [](int a, int b) { return min(a, b); });
     }
   }
   const int above = count_ge<V>(key, T + 1);
