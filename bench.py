@@ -541,8 +541,8 @@ def suite_orq(torch, gq, WL, stream, tb, reps):
 
 
 def suite_bingrad(torch, gq, WL, stream, tb, reps):
-    """BinGrad-b (optimal two-level) and the sign split with error feedback,
-    1B elements, over the bucket sweep."""
+    """BinGrad-b (optimal two-level), the sign split and the min/max two-level
+    quantizer with error feedback, 1B elements, over the bucket sweep."""
     out = []
     t0 = time.time()
     host = WL.bingrad_gradient()
@@ -562,6 +562,17 @@ def suite_bingrad(torch, gq, WL, stream, tb, reps):
                              extra=oracle_rate(host, dict(scheme=scheme, d=dd),
                                                True)))
             del c, m, q
+    # the min/max two-level quantizer (ORQ with L = 2, read as BinGrad-pb)
+    for dd in (128, 512, 2048, 8192, 32768):
+        d = gq.desc(gq.GQ_ORQ, dd, levels=2)
+        c, m = gq.alloc_payload(d, n)
+        e.zero_()
+        q = gq.PreparedQuantize(d, g, e, c, m, stream)
+        ms = tb(lambda i: q(0, i), max(3, reps // 2))
+        out.append(entry(f"quantize bin_pb (orq L=2)+ef d={dd} n={n}", ms,
+                         quant_bytes(1, 2, dd, n, True), n,
+                         extra=oracle_rate(host, dict(scheme=3, d=dd, L=2), True)))
+        del c, m, q
     return out
 
 

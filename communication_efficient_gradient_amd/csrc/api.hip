@@ -115,7 +115,10 @@ int64_t meta_floats_of(const gq::LaunchDesc& L, int64_t n) {
 
 int launch_status(int hip_rc) { return hip_rc == 0 ? GQ_OK : GQ_ELAUNCH; }
 
+// ORQ with two levels and no clipping keeps the bucket's minimum and
+// maximum: a reduction, so it runs in the streaming quantizer.
 bool is_sort_scheme(const gq::LaunchDesc& L) {
+  if (L.scheme == GQ_ORQ && L.L == 2 && !(L.flags & GQ_FLAG_CLIP)) return false;
   return L.scheme == GQ_BIN_OPT || L.scheme == GQ_ORQ;
 }
 

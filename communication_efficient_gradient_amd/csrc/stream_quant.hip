@@ -1,5 +1,8 @@
 // stream_quant.hip — one-pass quantizers whose per-bucket levels come from a
-// reduction: max-abs uniform (QSGD / ternary / INT8) and the sign split.
+// reduction: max-abs uniform (QSGD / ternary / INT8), the sign split, and
+// two levels at the bucket's minimum and maximum with random rounding
+// (ORQ with L = 2 and no clipping: the levels of the greedy before any
+// insertion, read as BinGrad-pb).
 //
 // One HBM pass per bucket: 128-bit loads of g (and e), p = g + e kept in
 // registers, a group reduction for the bucket's levels, then Philox rounding,
@@ -95,8 +98,10 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
     uint32_t A4, int W) {
   constexpr int D = 4 * G * V;
   constexpr bool DENSE = BITS == 0;
+  constexpr bool RANDOM = SCHEME == UNIFORM || SCHEME == ORQ;  // Philox draws
   constexpr int NW = G > 64 ? G / 64 : 1;
   __shared__ float red_f[NW];
+  __shared__ float red_f2[NW];
   __shared__ double red_d[2 * NW];
   __shared__ int red_i[2 * NW];
 
@@ -110,9 +115,9 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
   // Random words for the uniform scheme, or (nearest) words whose u is
   // exactly 1/2, so that a value rounds up iff q > 1/2.  They depend on the
   // element index only and are drawn while the loads are in flight.
-  uint4 wr[SCHEME == UNIFORM ? V : 1];
+  uint4 wr[RANDOM ? V : 1];
   auto draw = [&]() {
-    if constexpr (SCHEME == UNIFORM) {
+    if constexpr (RANDOM) {
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         wr[v] = make_uint4(kHalfWord, kHalfWord, kHalfWord, kHalfWord);
@@ -165,7 +170,8 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
 
   // ---- per-bucket levels ----------------------------------------------
   // UNIFORM: M = max |p| (absent tail elements load as 0, which never
-  // raises a max-abs).  BIN_SIGN: side means over the real elements.
+  // raises a max-abs).  ORQ (L = 2): minimum and maximum over the real
+  // elements.  BIN_SIGN: side means over the real elements.
   float lvl0 = 0.f, lvl1 = 0.f;
   if constexpr (SCHEME == UNIFORM) {
     float m = 0.f;
@@ -174,6 +180,25 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
       m = fmaxf(m, fmaxf(fmaxf(fabsf(p[v].x), fabsf(p[v].y)),
                          fmaxf(fabsf(p[v].z), fabsf(p[v].w))));
     lvl0 = bucket_max<G>(m, red_f);
+  } else if constexpr (SCHEME == ORQ) {
+    float hi = -INFINITY, nlo = -INFINITY;  // max p and max (-p)
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int64_t i = base + 4 * (lane + G * v);
+      const int nreal = i + 4 <= n ? 4 : (i < n ? (int)(n - i) : 0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float x = comp(p[v], k);
+        hi = k < nreal ? fmaxf(hi, x) : hi;
+        nlo = k < nreal ? fmaxf(nlo, -x) : nlo;
+      }
+    }
+    lvl1 = bucket_max<G>(hi, red_f);
+    lvl0 = -bucket_max<G>(nlo, red_f2);
+    // a zero level is +0 (levels are values of the sorted bucket, in which
+    // -0 and +0 are one value)
+    lvl0 = lvl0 == 0.f ? 0.f : lvl0;
+    lvl1 = lvl1 == 0.f ? 0.f : lvl1;
   } else {
     // Each lane sums its own values of one sign in plain fp64, then the
     // lanes' sums are added up the same way.
@@ -236,6 +261,22 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
           sc[k] = ci;
           c[k] = DENSE ? 0u : ((uint32_t)ci & ((1u << BITS) - 1u));
           const float xk = (float)ci * delta;
+          if (k == 0) xh.x = xk;
+          if (k == 1) xh.y = xk;
+          if (k == 2) xh.z = xk;
+          if (k == 3) xh.w = xk;
+        }
+      } else if constexpr (SCHEME == ORQ) {
+        // q = (p - a) / (b - a) in fp32; up iff u < q (nearest: q > 1/2); a
+        // value equal to a level takes it (the lower one when a = b)
+        const uint32_t ws[4] = {wr[v].x, wr[v].y, wr[v].z, wr[v].w};
+        const float den = lvl1 - lvl0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float x = comp(p[v], k);
+          const float q = (x - lvl0) / den;
+          c[k] = x == lvl0 ? 0u : (x == lvl1 || u24(ws[k]) < q ? 1u : 0u);
+          const float xk = c[k] ? lvl1 : lvl0;
           if (k == 0) xh.x = xk;
           if (k == 1) xh.y = xk;
           if (k == 2) xh.z = xk;
@@ -334,6 +375,7 @@ int launch_stream_quant(const LaunchDesc& L, int64_t n, const float* g,
                            (L.flags & GQ_FLAG_NEAREST) ? 1 : 0, codes, meta,  \
                            code_bytes, L.A4, L.W, st)
   if (L.scheme == BIN_SIGN) return GQ_D(BIN_SIGN, 1);
+  if (L.scheme == ORQ) return GQ_D(ORQ, 1);  // L = 2, no clipping
   if (L.dense) return GQ_D(UNIFORM, 0);
   switch (L.bits) {
     case 2:

@@ -67,7 +67,10 @@ extern "C" {
  *             method); deterministic, 1-bit.
  * GQ_ORQ      L levels picked greedily to minimise the summed random-
  *             rounding variance sum (b-x)(x-a), random rounding between
- *             adjacent levels (ORQ, same section); optional clip.
+ *             adjacent levels (ORQ, same section); optional clip.  With
+ *             L = 2 the levels are the bucket's minimum and maximum: the
+ *             unbiased wide-range two-level quantizer the review contrasts
+ *             with BinGrad-b (BinGrad-pb, as read here).
  * GQ_TOPK     Top-K sparsification combined with quantization ("gradient
  *             quantization for communication" glossary, §Quantization
  *             Schemes): per bucket only the K = desc.levels elements of
