@@ -142,44 +142,49 @@ __device__ __forceinline__ int lane_bits(uint64_t x, int ge, int b, int s,
 }
 
 // kCountWaves waves per block, kPerWave buckets per wave: the loads of a
-// wave's buckets are issued together.
+// wave's buckets are issued together.  A grid smaller than the number of
+// chunks strides over them.
 template <int G>
 __global__ __launch_bounds__(64 * kCountWaves) void k_elias_count(
     int64_t n, int64_t nb, int d, int b, int s, uint64_t len_t,
     const uint32_t* __restrict__ codes, uint64_t* __restrict__ off) {
   __shared__ uint32_t cnt[kChunk];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t j0 = (int64_t)blockIdx.x * kChunk + wave * kPerWave;
-  int nj[kPerWave];
-#pragma unroll
-  for (int t = 0; t < kPerWave; ++t) {
-    const int64_t r = n - (j0 + t) * d;
-    nj[t] = j0 + t < nb ? (int)(r < d ? r : d) : 0;
-  }
-  int bits[kPerWave] = {};
-  const int nseg = d / (64 * G);
-  for (int sg = 0; sg < nseg; ++sg) {
-    const int i0 = sg * 64 * G + lane * G;
-    uint64_t x[kPerWave];
-    int ge[kPerWave];
+  const int64_t nc = (nb + kChunk - 1) / kChunk;
+  for (int64_t chunk = blockIdx.x; chunk < nc; chunk += gridDim.x) {
+    const int64_t j0 = chunk * kChunk + wave * kPerWave;
+    int nj[kPerWave];
 #pragma unroll
     for (int t = 0; t < kPerWave; ++t) {
-      ge[t] = max(0, min(G, nj[t] - i0));
-      x[t] = lane_codes<G>(codes, (j0 + t) * d + i0, ge[t], b);
+      const int64_t r = n - (j0 + t) * d;
+      nj[t] = j0 + t < nb ? (int)(r < d ? r : d) : 0;
+    }
+    int bits[kPerWave] = {};
+    const int nseg = d / (64 * G);
+    for (int sg = 0; sg < nseg; ++sg) {
+      const int i0 = sg * 64 * G + lane * G;
+      uint64_t x[kPerWave];
+      int ge[kPerWave];
+#pragma unroll
+      for (int t = 0; t < kPerWave; ++t) {
+        ge[t] = max(0, min(G, nj[t] - i0));
+        x[t] = lane_codes<G>(codes, (j0 + t) * d + i0, ge[t], b);
+      }
+#pragma unroll
+      for (int t = 0; t < kPerWave; ++t) bits[t] += lane_bits<G>(x[t], ge[t], b, s, len_t);
     }
 #pragma unroll
-    for (int t = 0; t < kPerWave; ++t) bits[t] += lane_bits<G>(x[t], ge[t], b, s, len_t);
-  }
-#pragma unroll
-  for (int t = 0; t < kPerWave; ++t) {
-    const uint32_t tb = (uint32_t)group_sum_i<64>(bits[t]);
-    if (lane == 0) cnt[wave * kPerWave + t] = (tb + 31u) >> 5;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const uint32_t v = wave_incl_scan(cnt[lane]);
-    const int64_t j = (int64_t)blockIdx.x * kChunk + lane;
-    if (j < nb) off[j + 1] = v;
+    for (int t = 0; t < kPerWave; ++t) {
+      const uint32_t tb = (uint32_t)group_sum_i<64>(bits[t]);
+      if (lane == 0) cnt[wave * kPerWave + t] = (tb + 31u) >> 5;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const uint32_t v = wave_incl_scan(cnt[lane]);
+      const int64_t j = chunk * kChunk + lane;
+      if (j < nb) off[j + 1] = v;
+    }
+    __syncthreads();  // cnt is reused by the next chunk
   }
 }
 
@@ -191,6 +196,7 @@ __global__ __launch_bounds__(kScan) void k_elias_scan(int64_t nb,
   const int64_t per = (nc + kScan - 1) / kScan;
   const int64_t c0 = (int64_t)t * per, c1 = min(nc, c0 + per);
   uint64_t sum = 0;
+#pragma unroll 8
   for (int64_t c = c0; c < c1; ++c) sum += off[min((c + 1) * kChunk, nb)];
   part[0][t] = sum;
   __syncthreads();
@@ -219,58 +225,61 @@ __global__ __launch_bounds__(64) void k_elias_write(
   constexpr int kWin = 32 * G + 2;
   __shared__ uint32_t win[kWin];
   const int lane = threadIdx.x;
-  const int64_t j = blockIdx.x;
-  const int64_t cs = j - j % kChunk;  // the chunk's first bucket
-  const uint64_t oj = off[j];
-  const int64_t start = (int64_t)(j == cs ? oj : off[cs] + oj);
-  const int nj = (int)((n - j * d) < d ? (n - j * d) : d);
-  if (j != cs && lane == 0) off[j] = (uint64_t)start;
-  uint32_t carry = 0;  // low bits of the record's current partial word
-  int pos = 0;         // record bits written so far
-  const int nseg = d / (64 * G);
-  for (int sg = 0; sg < nseg; ++sg) {
-    const int i0 = sg * 64 * G + lane * G;
-    const int ge = max(0, min(G, nj - i0));
-    uint32_t f[G];
-    int l[G];
-    const int tot =
-        lane_fields<G>(lane_codes<G>(codes, j * d + i0, ge, b), ge, b, s, T, f, l);
-    const int incl = (int)wave_incl_scan((uint32_t)tot);
-    const int seg_bits = __builtin_amdgcn_readlane(incl, 63);
-    const int p0 = pos & 31;
-    const int nw = (p0 + seg_bits + 31) >> 5;
-    for (int w = lane; w < nw; w += 64) win[w] = w == 0 ? carry : 0u;
-    __syncthreads();
-    if (tot > 0) {
-      const int at = p0 + incl - tot;
-      int wi = at >> 5, ab = at & 31;
-      uint64_t acc = 0;
+  // one bucket per block; a grid smaller than nb strides (uniform per block)
+  for (int64_t j = blockIdx.x; j < nb; j += gridDim.x) {
+    const int64_t cs = j - j % kChunk;  // the chunk's first bucket
+    const uint64_t oj = off[j];
+    const int64_t start = (int64_t)(j == cs ? oj : off[cs] + oj);
+    const int nj = (int)((n - j * d) < d ? (n - j * d) : d);
+    if (j != cs && lane == 0) off[j] = (uint64_t)start;
+    uint32_t carry = 0;  // low bits of the record's current partial word
+    int pos = 0;         // record bits written so far
+    const int nseg = d / (64 * G);
+    for (int sg = 0; sg < nseg; ++sg) {
+      const int i0 = sg * 64 * G + lane * G;
+      const int ge = max(0, min(G, nj - i0));
+      uint32_t f[G];
+      int l[G];
+      const int tot =
+          lane_fields<G>(lane_codes<G>(codes, j * d + i0, ge, b), ge, b, s, T, f, l);
+      const int incl = (int)wave_incl_scan((uint32_t)tot);
+      const int seg_bits = __builtin_amdgcn_readlane(incl, 63);
+      const int p0 = pos & 31;
+      const int nw = (p0 + seg_bits + 31) >> 5;
+      for (int w = lane; w < nw; w += 64) win[w] = w == 0 ? carry : 0u;
+      __syncthreads();
+      if (tot > 0) {
+        const int at = p0 + incl - tot;
+        int wi = at >> 5, ab = at & 31;
+        uint64_t acc = 0;
 #pragma unroll
-      for (int k = 0; k < G; ++k) {
-        acc |= (uint64_t)f[k] << ab;
-        ab += l[k];
-        if (ab >= 32) {
-          atomicOr(&win[wi], (uint32_t)acc);
-          acc >>= 32;
-          ab -= 32;
-          ++wi;
+        for (int k = 0; k < G; ++k) {
+          acc |= (uint64_t)f[k] << ab;
+          ab += l[k];
+          if (ab >= 32) {
+            atomicOr(&win[wi], (uint32_t)acc);
+            acc >>= 32;
+            ab -= 32;
+            ++wi;
+          }
         }
+        if (ab > 0) atomicOr(&win[wi], (uint32_t)acc);
       }
-      if (ab > 0) atomicOr(&win[wi], (uint32_t)acc);
+      __syncthreads();
+      const int full = (p0 + seg_bits) >> 5;
+      const int64_t w0 = start + (pos >> 5);
+      // cap (the worst-case stream length) is a guard only: records sized by
+      // the count pass never reach it
+      for (int w = lane; w < full; w += 64)
+        if (w0 + w < cap) words[w0 + w] = win[w];
+      carry = ((p0 + seg_bits) & 31) ? win[full] : 0u;
+      pos += seg_bits;
+      __syncthreads();
     }
-    __syncthreads();
-    const int full = (p0 + seg_bits) >> 5;
-    const int64_t w0 = start + (pos >> 5);
-    // cap (the worst-case stream length) is a guard only: records sized by
-    // the count pass never reach it
-    for (int w = lane; w < full; w += 64)
-      if (w0 + w < cap) words[w0 + w] = win[w];
-    carry = ((p0 + seg_bits) & 31) ? win[full] : 0u;
-    pos += seg_bits;
-    __syncthreads();
+    if (lane == 0 && (pos & 31) && start + (pos >> 5) < cap)
+      words[start + (pos >> 5)] = carry;
+    __syncthreads();  // the window is reused by the next bucket
   }
-  if (lane == 0 && (pos & 31) && start + (pos >> 5) < cap)
-    words[start + (pos >> 5)] = carry;
 }
 
 // Decode table entry for the next kLutBits stream bits v: the complete
@@ -322,84 +331,88 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_elias_decode(
   const uint64_t* src =
       b == 2 ? kLut2.e : (b == 3 ? kLut3.e : (b == 4 ? kLut4.e : kLut8.e));
   for (int t = threadIdx.x; t < kLut; t += 64 * kDecWaves) lut[t] = src[t];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t j = ((int64_t)blockIdx.x * kDecWaves + wave) * 64 + lane;
-  const bool live = j < nb;
-  uint32_t* row = rows_all[wave][lane];
-  const uint64_t lim = (uint64_t)n_words;  // >= 1
-  uint64_t base = 0, e = 0;                // row[0] holds stream word base
-  int nj = 0;
-  if (live) {
-    base = min(off[j], lim);
-    e = min(max(off[j + 1], base), lim);
-    nj = (int)((n - j * d) < d ? (n - j * d) : d);
-  }
-  // all kRow loads of a lane are issued before the first is used; words
-  // past the record (or the readable stream) are staged as 0
-  auto restage = [&]() {
-    uint32_t v[kRow];
-#pragma unroll
-    for (int k = 0; k < kRow; ++k) v[k] = words[min(base + k, lim - 1)];
-#pragma unroll
-    for (int k = 0; k < kRow; ++k) row[k] = base + k < e ? v[k] : 0u;
-  };
-  restage();
   __syncthreads();  // the table
-  int rp = 0;       // next row word for the window
-  uint64_t win = 0;
-  int avail = 0;
-  const uint32_t mask = (1u << b) - 1u;
-  uint64_t ob = 0;
-  int obits = 0;
-  int64_t ow = j * (int64_t)(d / 32) * b;  // the bucket's first code word
-  const int64_t ow_end = ow + (((int64_t)nj * b + 31) >> 5);
-  int i = 0;  // codes decoded
-  // every step of a lane takes at least one codeword (refills: at most one
-  // row word per step), so the loop ends within d steps
-  while (__any(i < nj)) {
-    if (__any(i < nj && avail <= 32 && rp >= kRow)) {
-      base += (uint64_t)rp;
-      rp = 0;
-      restage();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // one lane per bucket; a grid smaller than nb / 64 strides (uniform per wave)
+  const int64_t stride = (int64_t)gridDim.x * kDecWaves * 64;
+  for (int64_t j0 = ((int64_t)blockIdx.x * kDecWaves + wave) * 64; j0 < nb; j0 += stride) {
+    const int64_t j = j0 + lane;
+    const bool live = j < nb;
+    uint32_t* row = rows_all[wave][lane];
+    const uint64_t lim = (uint64_t)n_words;  // >= 1
+    uint64_t base = 0, e = 0;                // row[0] holds stream word base
+    int nj = 0;
+    if (live) {
+      base = min(off[j], lim);
+      e = min(max(off[j + 1], base), lim);
+      nj = (int)((n - j * d) < d ? (n - j * d) : d);
     }
-    if (i < nj) {
-      if (avail <= 32) {
-        win |= (uint64_t)row[rp] << avail;
-        avail += 32;
-        ++rp;
+    // all kRow loads of a lane are issued before the first is used; words
+    // past the record (or the readable stream) are staged as 0
+    auto restage = [&]() {
+      uint32_t v[kRow];
+#pragma unroll
+      for (int k = 0; k < kRow; ++k) v[k] = words[min(base + k, lim - 1)];
+#pragma unroll
+      for (int k = 0; k < kRow; ++k) row[k] = base + k < e ? v[k] : 0u;
+    };
+    restage();
+    int rp = 0;  // next row word for the window
+    uint64_t win = 0;
+    int avail = 0;
+    const uint32_t mask = (1u << b) - 1u;
+    uint64_t ob = 0;
+    int obits = 0;
+    int64_t ow = j * (int64_t)(d / 32) * b;  // the bucket's first code word
+    const int64_t ow_end = ow + (((int64_t)nj * b + 31) >> 5);
+    int i = 0;  // codes decoded
+    // every step of a lane takes at least one codeword (refills: at most one
+    // row word per step), so the loop ends within d steps
+    while (__any(i < nj)) {
+      if (__any(i < nj && avail <= 32 && rp >= kRow)) {
+        base += (uint64_t)rp;
+        rp = 0;
+        restage();
       }
-      const uint64_t ent = lut[(uint32_t)win & (kLut - 1)];
-      uint32_t out = (uint32_t)ent;
-      int k = (int)(ent >> 32) & 255;
-      int len = (int)(ent >> 40) & 255;
-      if (k == 0) {
-        // one long codeword; a zero run past 15 only occurs in a corrupt stream
-        const int L = __builtin_ctzll(win | (1ull << 15));
-        const uint32_t dig = (uint32_t)(win >> L) & ((2u << L) - 1u);
-        const int mag = (int)(__brev(dig) >> (31 - L)) - 1;
-        const bool neg = (win >> (2 * L + 1)) & 1ull;
-        out = (uint32_t)(L == 0 ? 0 : (neg ? -mag : mag)) & mask;
-        k = 1;
-        len = L == 0 ? 1 : 2 * L + 2;
-      }
-      if (k > nj - i) {  // codes past the bucket's last element are dropped
-        k = nj - i;
-        out &= (1u << (k * b)) - 1u;
-      }
-      win >>= len;
-      avail -= len;
-      i += k;
-      ob |= (uint64_t)out << obits;
-      obits += k * b;
-      if (obits >= 32) {
-        if (ow < ow_end) codes[ow] = (uint32_t)ob;
-        ++ow;
-        ob >>= 32;
-        obits -= 32;
+      if (i < nj) {
+        if (avail <= 32) {
+          win |= (uint64_t)row[rp] << avail;
+          avail += 32;
+          ++rp;
+        }
+        const uint64_t ent = lut[(uint32_t)win & (kLut - 1)];
+        uint32_t out = (uint32_t)ent;
+        int k = (int)(ent >> 32) & 255;
+        int len = (int)(ent >> 40) & 255;
+        if (k == 0) {
+          // one long codeword; a zero run past 15 only occurs in a corrupt stream
+          const int L = __builtin_ctzll(win | (1ull << 15));
+          const uint32_t dig = (uint32_t)(win >> L) & ((2u << L) - 1u);
+          const int mag = (int)(__brev(dig) >> (31 - L)) - 1;
+          const bool neg = (win >> (2 * L + 1)) & 1ull;
+          out = (uint32_t)(L == 0 ? 0 : (neg ? -mag : mag)) & mask;
+          k = 1;
+          len = L == 0 ? 1 : 2 * L + 2;
+        }
+        if (k > nj - i) {  // codes past the bucket's last element are dropped
+          k = nj - i;
+          out &= (1u << (k * b)) - 1u;
+        }
+        win >>= len;
+        avail -= len;
+        i += k;
+        ob |= (uint64_t)out << obits;
+        obits += k * b;
+        if (obits >= 32) {
+          if (ow < ow_end) codes[ow] = (uint32_t)ob;
+          ++ow;
+          ob >>= 32;
+          obits -= 32;
+        }
       }
     }
+    if (obits > 0 && ow < ow_end) codes[ow] = (uint32_t)ob;
   }
-  if (obits > 0 && ow < ow_end) codes[ow] = (uint32_t)ob;
 }
 
 }  // namespace
@@ -432,12 +445,15 @@ template <int G>
 int encode_g(const LaunchDesc& L, int64_t n, const uint32_t* codes,
              uint64_t* off, uint32_t* words, hipStream_t st) {
   const int64_t nb = (n + L.d - 1) / L.d;
-  const int64_t nblk = (nb + kChunk - 1) / kChunk;
+  // grids stay below 2^32 work-items (a dispatch's limit); larger inputs stride
+  const int64_t nc = (nb + kChunk - 1) / kChunk;
+  const int64_t nblk = nc < (int64_t(1) << 20) ? nc : (int64_t(1) << 20);
   const GammaTab T = gamma_tab(L.bits, L.s);
   hipLaunchKernelGGL(k_elias_count<G>, dim3((unsigned)nblk), dim3(64 * kCountWaves), 0,
                      st, n, nb, L.d, L.bits, L.s, T.len_t, codes, off);
   hipLaunchKernelGGL(k_elias_scan, dim3(1), dim3(kScan), 0, st, nb, off);
-  hipLaunchKernelGGL(k_elias_write<G>, dim3((unsigned)nb), dim3(64), 0, st, n, nb,
+  const int64_t wgrid = nb < (int64_t(1) << 24) ? nb : (int64_t(1) << 24);
+  hipLaunchKernelGGL(k_elias_write<G>, dim3((unsigned)wgrid), dim3(64), 0, st, n, nb,
                      L.d, L.bits, L.s, elias_max_words(L, n), T, codes, off, words);
   return (int)hipGetLastError();
 }
@@ -470,7 +486,9 @@ int launch_elias_decode(const LaunchDesc& L, int64_t n, const uint64_t* off,
                         hipStream_t st) {
   const int64_t nb = (n + L.d - 1) / L.d;
   const int64_t per_block = 64 * kDecWaves;
-  hipLaunchKernelGGL(k_elias_decode, dim3((unsigned)((nb + per_block - 1) / per_block)),
+  int64_t grid = (nb + per_block - 1) / per_block;
+  grid = grid < (int64_t(1) << 24) ? grid : (int64_t(1) << 24);
+  hipLaunchKernelGGL(k_elias_decode, dim3((unsigned)grid),
                      dim3(64 * kDecWaves),
                      0, st, n, nb, L.d, L.bits, n_words, off, words,
                      reinterpret_cast<uint32_t*>(codes));

@@ -39,7 +39,12 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is enqueued asynchronously; nothing synchronizes the device.
  *   - Argument errors are detected on the host before any launch and
- *     returned; a failed launch returns GQ_ELAUNCH.
+ *     returned; a failed launch returns GQ_ELAUNCH.  A GPU dispatch holds
+ *     fewer than 2^32 work-items, which bounds n per call for the kernels
+ *     with a thread per few elements: about 2^35 for the quantizers and
+ *     the dequantizer at d >= 512 (2^34 at d = 64), 2^32 * d / 512 for
+ *     GQ_TOPK; beyond that the launch fails and GQ_ELAUNCH is returned
+ *     with nothing written.  The Elias calls stride and take any n.
  *   - Inputs must be finite; NaN/Inf inputs give unspecified outputs but
  *     never out-of-bounds accesses.
  *   - Outputs are a pure function of (inputs, desc, seed, step): they do not

@@ -119,3 +119,52 @@ def test_ternary_past_2_34(dev, flags):
     assert runs[-1] + RUN_LEN >= d.nb(n) and (n - 1) // 4 >= 2**32
     del G, codes, meta
     torch.cuda.empty_cache()
+
+
+def test_elias_past_2_30_buckets(dev):
+    """Elias coding of n = 2^36 + 327 ternary codes at d = 64: 2^30 + 6
+    buckets (the record pass's grid strides), about 6.4e9 stream words
+    (word offsets past 2^32).  Sampled buckets, always including the first,
+    those past 2^30 and the last, are checked against the oracle's record of
+    that bucket alone; the GPU decode of the whole stream gives the codes
+    back."""
+    gq, torch = dev
+    d, s = 64, 1
+    n = 2**36 + 5 * 64 + 7
+    gd = gq.desc(0, d, s=s)
+    nb = (n + d - 1) // d
+    cb, cap, _ = gq.gq_payload_size(gd, n)
+    mw = gq.gq_elias_max_words(gd, n)
+    _need(torch, 2 * cap + 8 * (nb + 1) + 4 * mw)
+    say(f"elias n={n} nb={nb} max_words={mw}")
+    gen = torch.Generator(device="cuda").manual_seed(36)
+    codes = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    step = 1 << 32
+    for a in range(0, cap, step):  # random valid 2-bit codes: field 10 (-2) -> 00
+        x = torch.randint(0, 256, (min(step, cap - a),), dtype=torch.uint8,
+                          device="cuda", generator=gen)
+        bad = (x >> 1) & ~x & 0x55
+        codes[a:a + x.numel()] = x & ~(bad << 1)
+        del x, bad
+    off, words = gq.alloc_elias(gd, n)
+    gq.gq_elias_encode(gd, n, codes, off, words)
+    torch.cuda.synchronize()
+    total = int(off[-1].item())
+    say(f"  stream words {total}")
+    assert total > 2**32
+    picks = sorted({0, 1, 63, 64, 2**30 - 1, 2**30, 2**30 + 1, nb - 2, nb - 1}
+                   | set(int(j) for j in np.random.default_rng(7).integers(0, nb, 24)))
+    for j in picks:
+        lo, hi = j * d, min(n, (j + 1) * d)
+        c = codes[lo * 2 // 8:(hi * 2 + 7) // 8].cpu().numpy()
+        roff, rw = O.elias_encode(d, s, hi - lo, c)
+        o0, o1 = int(off[j].item()), int(off[j + 1].item())
+        assert o1 - o0 == int(roff[-1]), j
+        got = words[o0:o1].cpu().numpy().view(np.uint32)
+        assert np.array_equal(got, rw), j
+    back = torch.empty_like(codes)
+    gq.gq_elias_decode(gd, n, off, words, back)
+    torch.cuda.synchronize()
+    assert torch.equal(back[:cb], codes[:cb])
+    del codes, back, off, words
+    torch.cuda.empty_cache()
