@@ -42,8 +42,8 @@
  *     returned; a failed launch returns GQ_ELAUNCH.  A GPU dispatch holds
  *     fewer than 2^32 work-items, which bounds n per call for the kernels
  *     with a thread per few elements: about 2^35 for the quantizers and
- *     the dequantizer at d >= 512 (2^34 at d = 64), 2^32 * d / 512 for
- *     GQ_TOPK; beyond that a launch fails, the call returns GQ_ELAUNCH
+ *     the dequantizer at d >= 512 (2^34 at d = 64), 2^26 * d for GQ_TOPK
+ *     (a wave per bucket); beyond that a launch fails, the call returns GQ_ELAUNCH
  *     and its outputs are unspecified.  The Elias calls stride and take
  *     any n.
  *   - Inputs must be finite; NaN/Inf inputs give unspecified outputs but
