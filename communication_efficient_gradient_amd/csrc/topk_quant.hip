@@ -15,10 +15,11 @@
 //      index order.  Ranks in index order come from per-element ballots
 //      (elements before (v, lane, c) are those of earlier v, of lower lanes at
 //      the same v, and earlier c in the same group).
-//   4. A kept element's slot is its rank among the kept; its field (index
-//      within the bucket, then the uniform code of gq_quantize with the same
-//      Philox word) goes to LDS by slot, and lane w then assembles record
-//      word w from the slots that meet it (records are word-aligned).
+//   4. A kept element's slot is its rank among the kept; its index and value
+//      go to LDS by slot, lane t codes slot t (the uniform code of
+//      gq_quantize with the same Philox word, drawn for kept elements
+//      only), and lane w then assembles record word w from the slots that
+//      meet it (records are word-aligned).
 //   5. Residual e = p - xhat (0 for elements not sent).
 // The decoder gives every bucket an LDS row of d floats, adds each payload's
 // slots in payload order, and writes the row as alpha * row (+ beta * out).
@@ -71,8 +72,11 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_topk_quant(
     const float* __restrict__ g, float* __restrict__ e, uint32_t k0,
     uint32_t k1, uint32_t step, int s, int nearest,
     uint8_t* __restrict__ codes, float* __restrict__ meta) {
-  // slot fields of the wave's bucket, written once per kept element
+  // per slot (kept element, in index order) of the wave's bucket: first its
+  // index within the bucket, then its record field; and its value p, then
+  // its dequantized value
   __shared__ uint32_t slots_all[kWavesPerBlock][512];
+  __shared__ float vals_all[kWavesPerBlock][512];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t bucket = (int64_t)blockIdx.x * kWavesPerBlock + wave;
@@ -80,10 +84,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_topk_quant(
   const int64_t base = bucket * d;
   const int nj = live ? (int)((n - base) < d ? (n - base) : d) : 0;
   uint32_t* slot_field = slots_all[wave];
+  float* slot_val = vals_all[wave];
 
   // ---- 1. load, keys, scale -------------------------------------------------
   float4 p[V];
-  uint4 wr[V];
   int key[V][4];
 #pragma unroll
   for (int v = 0; v < V; ++v) {
@@ -99,9 +103,6 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_topk_quant(
         p[v].w = p[v].w + r.w;
       }
     }
-    const uint64_t ctr = (uint64_t)(base + i) >> 2;
-    wr[v] = nearest ? make_uint4(kHalfWord, kHalfWord, kHalfWord, kHalfWord)
-                    : philox4x32_10(k0, k1, (uint32_t)ctr, (uint32_t)(ctr >> 32), step, 0u);
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       key[v][c] = i + c < nj ? (int)__float_as_uint(fabsf(comp(p[v], c))) : -1;
@@ -160,29 +161,45 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_topk_quant(
       kept[v][c] = kk > 0 && (key[v][c] > T || (tie[v][c] && r[v][c] < kk - above));
   rank_before<V>(kept, r);
 
+  // ---- 5. codes, by slot: lane t codes the kept elements of slots t, t + 64,
+  // ... with the Philox word of its element (one draw per kept element)
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (kept[v][c]) {
+        slot_field[r[v][c]] = (uint32_t)(4 * (lane + 64 * v) + c);
+        slot_val[r[v][c]] = comp(p[v], c);
+      }
+  __syncthreads();
   const float sf = (float)s;
   const float up = M < 0x1p-96f ? 0x1p96f : 1.0f;
   const float inv = M > 0.f ? sf / (M * up) : 0.f;
   const float delta = M / sf;
   const int fw = ib + BITS;  // slot width
+  for (int t = lane; t < kk; t += 64) {
+    const uint32_t idx = slot_field[t];
+    const uint64_t ctr = (uint64_t)(base + idx) >> 2;
+    uint32_t w = kHalfWord;
+    if (!nearest) {
+      const uint4 r4 = philox4x32_10(k0, k1, (uint32_t)ctr, (uint32_t)(ctr >> 32), step, 0u);
+      const uint32_t sub = idx & 3u;
+      w = sub == 0 ? r4.x : (sub == 1 ? r4.y : (sub == 2 ? r4.z : r4.w));
+    }
+    const int ci = up == 1.0f ? uniform_code<false>(slot_val[t], up, inv, sf, w)
+                              : uniform_code<true>(slot_val[t], up, inv, sf, w);
+    slot_field[t] = idx | (((uint32_t)ci & ((1u << BITS) - 1u)) << ib);
+    slot_val[t] = (float)ci * delta;
+  }
+  __syncthreads();
   float4 xh[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    const uint32_t ws[4] = {wr[v].x, wr[v].y, wr[v].z, wr[v].w};
     float x[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      x[c] = 0.f;
-      if (kept[v][c]) {
-        const int ci = uniform_code<true>(comp(p[v], c), up, inv, sf, ws[c]);
-        x[c] = (float)ci * delta;
-        const uint32_t idx = (uint32_t)(4 * (lane + 64 * v) + c);
-        slot_field[r[v][c]] = idx | (((uint32_t)ci & ((1u << BITS) - 1u)) << ib);
-      }
-    }
+    for (int c = 0; c < 4; ++c) x[c] = kept[v][c] ? slot_val[r[v][c]] : 0.f;
     xh[v] = make_float4(x[0], x[1], x[2], x[3]);
   }
-  __syncthreads();
 
   // ---- store: record words, scale, residual ---------------------------------
   if (live) {
