@@ -227,19 +227,35 @@ def time_oracle(run, size: int, d: int, budget: float = 0.5,
         n = min(4 * n, max_n, size)
 
 
+# Oracle timings wait here until every GPU measurement is done: the oracle's
+# OpenMP threads, run between two GPU timings, slowed the next GPU kernel by
+# up to 8 % (INT8 W = 8 dequantize-accumulate: 514 -> 557 us).
+DEFERRED = []
+
+
 def oracle_rate(host_g, desc_kw, ef: bool, seed: int = 0, budget: float = 0.5,
                 max_n: int = 1 << 22):
-    """The CPU oracle's quantize throughput on a prefix of the same input."""
+    """The CPU oracle's quantize throughput on a prefix of the same input,
+    measured later by run_deferred() (entry() registers the job)."""
     import numpy as np
 
     import oracle as O
 
     od = O.Desc(**desc_kw)
+    host_g = host_g[:max_n].copy()
 
     def run(n):
         e = np.zeros(n, dtype=np.float32) if ef else None
         O.quantize(od, host_g[:n], e, seed=seed, step=0)
-    return time_oracle(run, host_g.size, od.d, budget, max_n)
+    return {"_oracle": lambda: time_oracle(run, host_g.size, od.d, budget,
+                                           max_n)}
+
+
+def run_deferred() -> None:
+    """Runs the oracle timings entry() queued and fills in their entries."""
+    for r, job in DEFERRED:
+        r.update(job())
+    DEFERRED.clear()
 
 
 def entry(name, ms, nbytes, n, bound="hbm", extra=None):
@@ -251,6 +267,9 @@ def entry(name, ms, nbytes, n, bound="hbm", extra=None):
          "bound": bound}
     if extra:
         r.update(extra)
+        job = r.pop("_oracle", None)
+        if job is not None:
+            DEFERRED.append((r, job))
     return r
 
 
@@ -262,24 +281,23 @@ def suite(torch, gq, WL, stream, reps: int, only: str | None = None):
     tb = lambda f, r=reps: time_back_to_back(torch, stream, f, r)  # noqa: E731
     want = lambda name: only is None or only in name  # noqa: E731
 
-    if want("qsgd"):
-        out += suite_qsgd(torch, gq, WL, stream, tb)
-    if want("orq"):
-        out += suite_orq(torch, gq, WL, stream, tb, reps)
-    if want("bingrad"):
-        out += suite_bingrad(torch, gq, WL, stream, tb, reps)
-    if want("workers"):
-        out += suite_workers(torch, gq, WL, stream, tb)
-    if want("dense"):
-        out += suite_dense(torch, gq, WL, stream, tb, reps)
-    if want("nearest"):
-        out += suite_nearest(torch, gq, WL, stream, tb, reps)
-    if want("layers"):
-        out += suite_layers(torch, gq, WL, stream, tb)
-    if want("topk"):
-        out += suite_topk(torch, gq, WL, stream, tb)
-    if want("elias"):
-        out += suite_elias(torch, gq, WL, stream, tb)
+    suites = [("qsgd", lambda: suite_qsgd(torch, gq, WL, stream, tb)),
+              ("orq", lambda: suite_orq(torch, gq, WL, stream, tb, reps)),
+              ("bingrad", lambda: suite_bingrad(torch, gq, WL, stream, tb, reps)),
+              ("workers", lambda: suite_workers(torch, gq, WL, stream, tb)),
+              ("dense", lambda: suite_dense(torch, gq, WL, stream, tb, reps)),
+              ("nearest", lambda: suite_nearest(torch, gq, WL, stream, tb, reps)),
+              ("layers", lambda: suite_layers(torch, gq, WL, stream, tb)),
+              ("topk", lambda: suite_topk(torch, gq, WL, stream, tb)),
+              ("elias", lambda: suite_elias(torch, gq, WL, stream, tb))]
+    for name, run in suites:
+        if want(name):
+            out += run()
+            # each workload starts from memory handed back to the driver: a
+            # suite placed in the 18 GB the workers suite left cached ran up
+            # to 20 % slower than alone
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
     return out
 
 
@@ -747,15 +765,18 @@ def main() -> int:
         entry("dequantize ternary W=1 n=25.6M (headline)", d_ms,
               mw.dbytes(), n),
     ]
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(mw)
-        log(f"cpu baseline: {cpu}")
     if args.suite == "all":
         del mw.q, mw.G
         torch.cuda.empty_cache()
         kernels.append(copy_reference(torch, stream))
         kernels += suite(torch, gq, WL, stream, args.reps, args.only)
+    # host work after every GPU timing (see DEFERRED)
+    torch.cuda.synchronize()
+    run_deferred()
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(mw)
+        log(f"cpu baseline: {cpu}")
 
     line = {
         "metric": METRIC,

@@ -262,6 +262,199 @@ __global__ __launch_bounds__(kThreads) void k_deq_acc(
   }
 }
 
+// Wide code loads for 4- and 8-bit codes.  A wave owns a run of kWideRun =
+// 256 consecutive groups (1024 elements); a payload's codes for the run are
+// one contiguous block of 128*BITS bytes (1 KiB of INT8 codes), loaded as one
+// 2*BITS-byte vector per lane (128-bit for 8-bit codes) instead of one 4*BITS-
+// bit word per group, so a wave keeps 4x more bytes in flight per load
+// instruction.  The block passes through the wave's own LDS row, from which
+// lane l reads the code word of group 64v + l of the run: the output stores
+// stay lane-contiguous as in k_deq_acc.  Payload batches of NB (up to 8) are
+// loaded before any is used; accumulation order and arithmetic are those of
+// k_deq_acc, so both kernels give the same bits.  A run that reaches past
+// the last whole group loads group by group as k_deq_acc does.
+constexpr int kWideKV = 4;                         // groups per lane
+constexpr int kWideRun = 64 * kWideKV;             // groups per wave
+constexpr int kWideBlockGroups = kThreads / 64 * kWideRun;
+
+template <int BITS> struct WideVec;
+template <> struct WideVec<8> { using T = uint4; };
+template <> struct WideVec<4> { using T = uint2; };
+
+// Nontemporal 128/64-bit code loads (NT): for payloads that together exceed
+// the last-level cache, where no code is read twice.
+template <int BITS>
+__device__ __forceinline__ typename WideVec<BITS>::T load_wide_nt(const uint8_t* p) {
+  if constexpr (BITS == 8) {
+    typedef unsigned nt_u4 __attribute__((ext_vector_type(4)));
+    const nt_u4 t = __builtin_nontemporal_load(reinterpret_cast<const nt_u4*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+  } else {
+    typedef unsigned nt_u2 __attribute__((ext_vector_type(2)));
+    const nt_u2 t = __builtin_nontemporal_load(reinterpret_cast<const nt_u2*>(p));
+    return make_uint2(t.x, t.y);
+  }
+}
+
+template <int SCHEME, int BITS, int NB, bool NT>
+__global__ __launch_bounds__(kThreads) void k_deq_acc_wide(
+    int64_t n, int dsh, int s, int L, int W, PayloadPtrs pp, float alpha,
+    float beta, float* __restrict__ out, int64_t code_bytes) {
+  static_assert(BITS == 4 || BITS == 8, "wide loads are for 4- and 8-bit codes");
+  using VecT = typename WideVec<BITS>::T;
+  constexpr int kRunWords = kWideRun * BITS / 8;   // 32-bit words of a run's codes
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t ngroups = (n + 3) >> 2;
+  const int64_t tile = (int64_t)blockIdx.x * kWideBlockGroups;
+  const int64_t run0 = tile + (int64_t)wave * kWideRun;
+  // every group of the run is whole, so all its code bytes are in the stream
+  const bool whole = 4 * (run0 + kWideRun) <= n;
+  const int64_t run_byte0 = run0 * BITS / 2;       // 4*BITS bits per group
+
+  constexpr bool TABLE = NB >= 4;
+  constexpr int MK = SCHEME == UNIFORM ? (TABLE ? 0 : 1) : 0;
+  // whole runs: the lane's slice of the run's codes; tail runs: the code
+  // words of the lane's own groups 64v + l, packed as the slice would hold
+  // them after the exchange (word v of a uint4, or half-word v of a uint2)
+  VecT vec[NB];
+  float mv[NB][kWideKV][MK > 0 ? MK : 1];
+  auto load_batch = [&](int p0) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int p = p0 + j;
+      const uint8_t* c = pp.codes[p < W ? p : 0];
+      if (whole) {
+        const uint8_t* q = c + run_byte0 + (int64_t)lane * sizeof(VecT);
+        if (p >= W) vec[j] = VecT{};
+        else if constexpr (NT) vec[j] = load_wide_nt<BITS>(q);
+        else vec[j] = *reinterpret_cast<const VecT*>(q);
+      } else {
+        uint32_t t[kWideKV];
+#pragma unroll
+        for (int v = 0; v < kWideKV; ++v) {
+          const int64_t f = run0 + 64 * v + lane;
+          t[v] = (p < W && f < ngroups)
+                     ? load_codes4<BITS>(c, f, 4 * f + 4 <= n, code_bytes)
+                     : 0u;
+        }
+        if constexpr (BITS == 8) vec[j] = make_uint4(t[0], t[1], t[2], t[3]);
+        else vec[j] = make_uint2(t[0] | (t[1] << 16), t[2] | (t[3] << 16));
+      }
+      if constexpr (MK > 0) {
+#pragma unroll
+        for (int v = 0; v < kWideKV; ++v) {
+          const int64_t f = run0 + 64 * v + lane;
+          const bool live = p < W && f < ngroups;
+          mv[j][v][0] = live ? pp.meta[p < W ? p : 0][(4 * f) >> dsh] : 0.f;
+        }
+      }
+    }
+  };
+  load_batch(0);
+
+  __shared__ float delta_tab[TABLE ? kMaxPayloads * (kWideBlockGroups * 4 / 64 + 1) : 1];
+  __shared__ uint32_t xrow[kThreads / 64][kRunWords];
+  const int64_t b0 = (4 * tile) >> dsh;
+  int nbk = 0;
+  if constexpr (SCHEME == UNIFORM && TABLE) {
+    const int64_t last = (4 * (tile + kWideBlockGroups) - 1) >> dsh;
+    const int64_t nb = (n + ((int64_t)1 << dsh) - 1) >> dsh;
+    nbk = (int)(last - b0 + 1);
+    for (int t = threadIdx.x; t < W * nbk; t += kThreads) {
+      const int p = t / nbk, j = t % nbk;
+      const int64_t bucket = b0 + j;
+      delta_tab[t] = bucket < nb ? pp.meta[p][bucket] / (float)s : 0.f;
+    }
+    __syncthreads();
+  }
+
+  float4 acc0[kWideKV], acc1[kWideKV];
+#pragma unroll
+  for (int v = 0; v < kWideKV; ++v) {
+    acc0[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+    acc1[v] = acc0[v];
+  }
+  for (int p0 = 0; p0 < W; p0 += NB) {
+    if (p0 > 0) load_batch(p0);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int p = p0 + j;
+      if (p >= W) break;
+      uint32_t cw[kWideKV];
+      if (whole) {
+        // the wave's row: written by every lane, then read lane-contiguously;
+        // LDS accesses of one wave execute in order, so no barrier is needed
+        // between this write, the reads and the next payload's write
+        reinterpret_cast<VecT*>(xrow[wave])[lane] = vec[j];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int v = 0; v < kWideKV; ++v) {
+          if constexpr (BITS == 8)
+            cw[v] = xrow[wave][64 * v + lane];
+          else
+            cw[v] = reinterpret_cast<const uint16_t*>(xrow[wave])[64 * v + lane];
+        }
+        __builtin_amdgcn_wave_barrier();
+      } else if constexpr (BITS == 8) {
+        cw[0] = vec[j].x; cw[1] = vec[j].y; cw[2] = vec[j].z; cw[3] = vec[j].w;
+      } else {
+        cw[0] = vec[j].x & 0xFFFFu; cw[1] = vec[j].x >> 16;
+        cw[2] = vec[j].y & 0xFFFFu; cw[3] = vec[j].y >> 16;
+      }
+#pragma unroll
+      for (int v = 0; v < kWideKV; ++v) {
+        const int64_t f = run0 + 64 * v + lane;
+        if (f >= ngroups) continue;
+        const int64_t bucket = (4 * f) >> dsh;
+        float4 x;
+        if constexpr (SCHEME == UNIFORM) {
+          float delta;
+          if constexpr (TABLE) delta = delta_tab[p * nbk + (int)(bucket - b0)];
+          else delta = mv[j][v][0] / (float)s;
+          x.x = (float)code_value<SCHEME, BITS>(cw[v], 0, s) * delta;
+          x.y = (float)code_value<SCHEME, BITS>(cw[v], 1, s) * delta;
+          x.z = (float)code_value<SCHEME, BITS>(cw[v], 2, s) * delta;
+          x.w = (float)code_value<SCHEME, BITS>(cw[v], 3, s) * delta;
+        } else {
+          x = dequant4<SCHEME, BITS>(cw[v], pp.meta[p], bucket, s, L);
+        }
+        if (p == 0) acc0[v] = x;
+        else if (p == 1) acc1[v] = x;
+        else if (p & 1) acc1[v] = add4(acc1[v], x);
+        else acc0[v] = add4(acc0[v], x);
+      }
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < kWideKV; ++v) {
+    const int64_t f = run0 + 64 * v + lane;
+    if (f >= ngroups) continue;
+    float4 a = W > 1 ? add4(acc0[v], acc1[v]) : acc0[v];
+    float4 r = make_float4(alpha * a.x, alpha * a.y, alpha * a.z, alpha * a.w);
+    float* o = out + 4 * f;
+    if (4 * f + 4 <= n) {
+      if (beta != 0.f) {
+        const float4 old = load4_nt(o);
+        r.x = r.x + beta * old.x;
+        r.y = r.y + beta * old.y;
+        r.z = r.z + beta * old.z;
+        r.w = r.w + beta * old.w;
+      }
+      store4_nt(o, r);
+    } else {
+      const int rem = (int)(n - 4 * f);
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        if (k < rem) {
+          float rk = comp(r, k);
+          if (beta != 0.f) rk = rk + beta * o[k];
+          o[k] = rk;
+        }
+      }
+    }
+  }
+}
+
 template <int SCHEME, int BITS>
 __global__ __launch_bounds__(kThreads) void k_error_feedback(
     int64_t n, int dsh, int s, int L, const float* __restrict__ g,
@@ -431,9 +624,34 @@ DenseCfg dense_cfg(const LaunchDesc& L) {
 int dshift(const LaunchDesc& L) { return __builtin_ctz((unsigned)L.d); }
 
 template <int SCHEME, int BITS>
+int deq_wide(const LaunchDesc& L, int64_t n, int W, const PayloadPtrs& pp,
+             float alpha, float beta, float* out, int64_t code_bytes,
+             hipStream_t st) {
+  const int64_t ngroups = (n + 3) >> 2;
+  const dim3 grid((uint32_t)((ngroups + kWideBlockGroups - 1) / kWideBlockGroups)),
+      block(kThreads);
+  // payloads whose codes together exceed the 256 MiB last-level cache are
+  // streamed past it (measured: INT8, W = 8, n = 256M 537 -> 512 us; on
+  // cache-resident payloads the hint costs up to 25 %)
+  const bool nt = (double)W * (double)code_bytes > 256.0 * 1024 * 1024;
+#define GQ_WIDE(NB, NT)                                                          \
+  hipLaunchKernelGGL((k_deq_acc_wide<SCHEME, BITS, NB, NT>), grid, block, 0, st, \
+                     n, dshift(L), L.s, L.L, W, pp, alpha, beta, out,            \
+                     code_bytes)
+  if (W == 1) { if (nt) GQ_WIDE(1, true); else GQ_WIDE(1, false); }
+  else if (W == 2) { if (nt) GQ_WIDE(2, true); else GQ_WIDE(2, false); }
+  else if (W <= 4) { if (nt) GQ_WIDE(4, true); else GQ_WIDE(4, false); }
+  else { if (nt) GQ_WIDE(8, true); else GQ_WIDE(8, false); }
+#undef GQ_WIDE
+  return (int)hipGetLastError();
+}
+
+template <int SCHEME, int BITS>
 int deq_one(const LaunchDesc& L, int64_t n, int W, const PayloadPtrs& pp,
             float alpha, float beta, float* out, int64_t code_bytes,
             hipStream_t st) {
+  if constexpr ((BITS == 4 || BITS == 8) && (SCHEME == UNIFORM || SCHEME == ORQ))
+    return deq_wide<SCHEME, BITS>(L, n, W, pp, alpha, beta, out, code_bytes, st);
   const dim3 grid((uint32_t)blocks_for(n)), block(kThreads);
   const DenseCfg dc = dense_cfg(L);
   if (W == 1)

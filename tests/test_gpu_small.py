@@ -199,6 +199,34 @@ def test_dequantize_accumulate(dev, scheme, s, L, W):
         compare_values(got, ref, scale, exact=(W == 1 and alpha == 1.0 and beta == 0.0))
 
 
+@pytest.mark.parametrize("scheme,s,L", [(O.UNIFORM, 127, 5), (O.UNIFORM, 4, 5),
+                                        (O.ORQ, 4, 9)])
+@pytest.mark.parametrize("bucket", [64, 512, 8192])
+@pytest.mark.parametrize("W", [1, 5, 16])
+def test_dequantize_accumulate_tiles(dev, scheme, s, L, bucket, W):
+    """4- and 8-bit codes over several 4096-element tiles and a ragged tail:
+    per-tile step tables of up to 64 buckets, whole and partial wave runs."""
+    n = 6 * 4096 + 777
+    d = O.Desc(scheme, bucket, s=s, L=L)
+    cl, ml = [], []
+    for w in range(W):
+        g = WL.small_mixture(n, seed=300 + w)
+        c, m, _, _ = O.quantize(d, g, seed=w + 1)
+        cl.append(c)
+        ml.append(m)
+    xs = [O.dequantize(d, n, c, m).astype(np.float64) for c, m in zip(cl, ml)]
+    absum = np.sum([np.abs(x) for x in xs], axis=0)
+    for alpha, beta in [(1.0, 0.0), (1.0 / W, 0.0), (0.5, 2.0)]:
+        say(f"deq tiles scheme={scheme} d={bucket} W={W} alpha={alpha} beta={beta}")
+        out0 = WL.small_mixture(n, seed=9)
+        got = gpu_deq(dev, d, n, cl, ml, alpha, beta, out0 if beta else None)
+        ref = O.dequantize_accumulate(d, n, cl, ml, alpha, beta,
+                                      out0 if beta else None)
+        scale = abs(beta) * np.abs(out0.astype(np.float64)) + abs(alpha) * absum
+        compare_values(got, ref, scale,
+                       exact=(W == 1 and alpha == 1.0 and beta == 0.0))
+
+
 @pytest.mark.parametrize("scheme,s,L", [(O.UNIFORM, 1, 5), (O.UNIFORM, 127, 5),
                                         (O.UNIFORM, 2, 5), (O.BIN_OPT, 4, 5),
                                         (O.ORQ, 4, 9)])
