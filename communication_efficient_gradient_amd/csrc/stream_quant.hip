@@ -44,6 +44,31 @@ __device__ __forceinline__ float bucket_max(float v, float* red) {
   }
 }
 
+// Two maxima over the bucket with one barrier (G > 64).
+template <int G>
+__device__ __forceinline__ void bucket_max2(float& a, float& b, float* red) {
+  if constexpr (G <= 64) {
+    a = group_max<G>(a);
+    b = group_max<G>(b);
+  } else {
+    a = group_max<64>(a);
+    b = group_max<64>(b);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+      red[2 * wave + 0] = a;
+      red[2 * wave + 1] = b;
+    }
+    __syncthreads();
+    a = red[0];
+    b = red[1];
+#pragma unroll
+    for (int w = 1; w < G / 64; ++w) {
+      a = fmaxf(a, red[2 * w + 0]);
+      b = fmaxf(b, red[2 * w + 1]);
+    }
+  }
+}
+
 // Side sums and counts of the sign split over the bucket.  Each side's
 // values share a sign, so plain fp64 sums have no cancellation: relative
 // error below d * 2^-53 (< 4e-12 at d = 32768), far inside what rounding the
@@ -101,7 +126,7 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
   constexpr bool RANDOM = SCHEME == UNIFORM || SCHEME == ORQ;  // Philox draws
   constexpr int NW = G > 64 ? G / 64 : 1;
   __shared__ float red_f[NW];
-  __shared__ float red_f2[NW];
+  __shared__ float red_f2[2 * NW];
   __shared__ double red_d[2 * NW];
   __shared__ int red_i[2 * NW];
 
@@ -193,8 +218,9 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
         nlo = k < nreal ? fmaxf(nlo, -x) : nlo;
       }
     }
-    lvl1 = bucket_max<G>(hi, red_f);
-    lvl0 = -bucket_max<G>(nlo, red_f2);
+    bucket_max2<G>(hi, nlo, red_f2);
+    lvl1 = hi;
+    lvl0 = -nlo;
     // a zero level is +0 (levels are values of the sorted bucket, in which
     // -0 and +0 are one value)
     lvl0 = lvl0 == 0.f ? 0.f : lvl0;
