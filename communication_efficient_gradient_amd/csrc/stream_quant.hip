@@ -379,6 +379,13 @@ int dispatch_d(int d, int64_t n, const float* g, float* e, uint64_t seed,
   // each beat one wave holding 8 per lane (d = 2048: 550 -> 506 us; 8192:
   // 540 -> 485 us); d = 1024 keeps one wave (4 waves: 71 % against 79 % for
   // the sign split)
+  // 8-bit codes at d = 512: two waves of one float4 per lane (INT8 + EF on
+  // 256M: 572 -> 556 us; the 2-bit headline is 1 % slower that way)
+  if constexpr (BITS == 8) {
+    if (d == 512)
+      return launch_one<SCHEME, BITS, 128, 1>(n, g, e, seed, step, s, nearest,
+                                              codes, meta, code_bytes, A4, W, st);
+  }
   switch (d) {
     GQ_CASE(64, 16, 1)
     GQ_CASE(128, 32, 1)
