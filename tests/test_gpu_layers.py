@@ -35,6 +35,10 @@ LAYOUTS = {
     "tiny_many": [1] * 40 + [3] * 30 + [1000],   # > 32 layer starts in a tile
     "tile_sized": [2048] * 4 + [2049, 2047],
     "ragged": [5, 4099, 17, 65, 3000, 1],
+    # layers spanning several 2048-element tiles, and 65 layer starts
+    # within 5,240 elements
+    "multi_tile": [4096] * 3 + [4097, 4095, 8192, 8191, 1],
+    "many_starts": [100] * 45 + [37] * 20 + [9000],
 }
 
 
