@@ -238,7 +238,7 @@ template <int BITS>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void k_topk_deq(
     int64_t n, int64_t nb, int d, int ib, int K, int R, int s, int W,
     PayloadPtrs pp, float alpha, float beta, float* __restrict__ out) {
-  __shared__ float row_all[kWavesPerBlock][512];
+  __shared__ __align__(16) float row_all[kWavesPerBlock][512];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t bucket = (int64_t)blockIdx.x * kWavesPerBlock + wave;
@@ -247,7 +247,16 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_topk_deq(
   const int nj = (int)((n - base) < d ? (n - base) : d);
   const int kk = nj < K ? nj : K;
   float* row = row_all[wave];
-  for (int i = lane; i < nj; i += 64) row[i] = 0.f;
+  // whole buckets (nj = d, a multiple of 4) clear and read the row with
+  // 128-bit LDS accesses and store the output nontemporally, as the other
+  // dequantizers do
+  const bool whole = nj == d;
+  if (whole) {
+    for (int i = 4 * lane; i < nj; i += 256)
+      *reinterpret_cast<float4*>(row + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+  } else {
+    for (int i = lane; i < nj; i += 64) row[i] = 0.f;
+  }
   const int fw = ib + BITS;
   const uint32_t imask = (1u << ib) - 1u;
   for (int w = 0; w < W; ++w) {
@@ -267,8 +276,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_topk_deq(
     }
   }
   for (int i = 4 * lane; i < nj; i += 256) {
-    float4 a = make_float4(row[i], i + 1 < nj ? row[i + 1] : 0.f,
-                           i + 2 < nj ? row[i + 2] : 0.f, i + 3 < nj ? row[i + 3] : 0.f);
+    float4 a = whole ? *reinterpret_cast<const float4*>(row + i)
+                     : make_float4(row[i], i + 1 < nj ? row[i + 1] : 0.f,
+                                   i + 2 < nj ? row[i + 2] : 0.f,
+                                   i + 3 < nj ? row[i + 3] : 0.f);
     float4 rr = make_float4(alpha * a.x, alpha * a.y, alpha * a.z, alpha * a.w);
     if (beta != 0.f) {
       const float4 old = load4(out, base + i, base + nj);
@@ -277,7 +288,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_topk_deq(
       rr.z = rr.z + beta * old.z;
       rr.w = rr.w + beta * old.w;
     }
-    store4(out, base + i, base + nj, rr);
+    if (whole) store4_nt(out + base + i, rr);
+    else store4(out, base + i, base + nj, rr);
   }
 }
 
