@@ -94,9 +94,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_topk_quant(
     const int i = 4 * (lane + 64 * v);  // index within the bucket
     p[v] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (i < nj) {
-      p[v] = load4(g, base + i, base + nj);
+      const bool full = i + 4 <= nj;  // nontemporal 128-bit streams
+      p[v] = full ? load4_nt(g + base + i) : load4(g, base + i, base + nj);
       if (e != nullptr) {
-        const float4 r = load4(e, base + i, base + nj);
+        const float4 r = full ? load4_nt(e + base + i) : load4(e, base + i, base + nj);
         p[v].x = p[v].x + r.x;
         p[v].y = p[v].y + r.y;
         p[v].z = p[v].z + r.z;
@@ -227,7 +228,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_topk_quant(
           rr.y = p[v].y - xh[v].y;
           rr.z = p[v].z - xh[v].z;
           rr.w = p[v].w - xh[v].w;
-          store4(e, base + i, base + nj, rr);
+          if (i + 4 <= nj) store4_nt(e + base + i, rr);
+          else store4(e, base + i, base + nj, rr);
         }
       }
     }
