@@ -703,11 +703,13 @@ __device__ __forceinline__ float wave_at(const float (&y)[E], int pos) {
   return __shfl(v, pos / E, G);
 }
 
-template <int VEC>
+// NT: nontemporal 128-bit access for whole float4s (streams read or written
+// once; ORQ's first read is not one: it reads its bucket again from cache)
+template <int VEC, bool NT = false>
 __device__ __forceinline__ void load_vec(const float* __restrict__ a,
                                          int64_t i, int64_t n, float (&x)[VEC]) {
   if constexpr (VEC == 4) {
-    const float4 v = load4(a, i, n);
+    const float4 v = (NT && i + 4 <= n) ? load4_nt(a + i) : load4(a, i, n);
     x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
   } else {
     if (i + VEC <= n) {
@@ -724,11 +726,12 @@ __device__ __forceinline__ void load_vec(const float* __restrict__ a,
   }
 }
 
-template <int VEC>
+template <int VEC, bool NT = false>
 __device__ __forceinline__ void store_vec(float* __restrict__ a, int64_t i,
                                           int64_t n, const float (&x)[VEC]) {
   if constexpr (VEC == 4) {
-    store4(a, i, n, make_float4(x[0], x[1], x[2], x[3]));
+    if (NT && i + 4 <= n) store4_nt(a + i, make_float4(x[0], x[1], x[2], x[3]));
+    else store4(a, i, n, make_float4(x[0], x[1], x[2], x[3]));
   } else {
     if (i + VEC <= n) {
       if constexpr (VEC == 2) *reinterpret_cast<float2*>(a + i) = make_float2(x[0], x[1]);
@@ -764,10 +767,10 @@ void k_wave_sort_quant(
   for (int q = 0; q < NQ; ++q) {
     const int64_t i = base + (int64_t)VEC * (lane + G * q);
     float x[VEC];
-    load_vec<VEC>(g, i, n, x);
+    load_vec<VEC, SCHEME == BIN_OPT>(g, i, n, x);
     if (e != nullptr) {
       float r[VEC];
-      load_vec<VEC>(e, i, n, r);
+      load_vec<VEC, SCHEME == BIN_OPT>(e, i, n, r);
 #pragma unroll
       for (int c = 0; c < VEC; ++c) x[c] = x[c] + r[c];
     }
@@ -1194,7 +1197,7 @@ void k_wave_sort_quant(
     }
     if constexpr (BITS == 0) dfield[q] = field;
     else store_chunk<BITS, VEC>(codes, i0, lane, field, code_bytes);
-    if (e != nullptr && i0 < n) store_vec<VEC>(e, i0, n, r);
+    if (e != nullptr && i0 < n) store_vec<VEC, true>(e, i0, n, r);
   }
   // Dense fields are stored once the values and levels are dead.  Dense ORQ
   // runs with d >= 512 only, so here a bucket is one wave.
