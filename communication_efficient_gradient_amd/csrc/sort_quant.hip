@@ -273,13 +273,20 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
   // ---- 1. load p = g (+ e); element order: thread t holds the float4s
   //         t, t + T, ... of the bucket -------------------------------------
   constexpr int NQ = E / 4;
+  // For d <= 4096 p stays in registers for the coding pass, so the bucket is
+  // read once, nontemporally.  Larger buckets read it again in the coding
+  // pass: keeping it costs 10 VGPRs, which at 1024 threads per block leaves
+  // room for one block per CU instead of two (BinGrad-b + EF on 1B, d = 8192:
+  // 13.0 -> 17.6 ms), and at d = 32768 registers are at the limit already.
+  constexpr bool KEEP = E <= 8 && T <= 512;
   float p[E];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int64_t i = base + 4 * (tid + (int64_t)T * q);
-    float4 x = load4(g, i, n);
+    const bool nt = KEEP && i + 4 <= n;
+    float4 x = nt ? load4_nt(g + i) : load4(g, i, n);
     if (e != nullptr) {
-      const float4 r = load4(e, i, n);
+      const float4 r = nt ? load4_nt(e + i) : load4(e, i, n);
       x.x = x.x + r.x;
       x.y = x.y + r.y;
       x.z = x.z + r.z;
@@ -554,7 +561,8 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
 
   if (codes == nullptr) return;  // levels only
 
-  // ---- 5. codes, packing, residual (element order, bucket read again) ----
+  // ---- 5. codes, packing, residual (element order; p kept, or the bucket
+  //         read again: the same g + e in fp32) -----------------------------
   float lv[16];
   if constexpr (SCHEME == ORQ) {
 #pragma unroll
@@ -564,13 +572,18 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int64_t i0 = base + 4 * (tid + (int64_t)T * q);
-    float4 pv = load4(g, i0, n);
-    if (e != nullptr) {
-      const float4 r = load4(e, i0, n);
-      pv.x = pv.x + r.x;
-      pv.y = pv.y + r.y;
-      pv.z = pv.z + r.z;
-      pv.w = pv.w + r.w;
+    float4 pv;
+    if constexpr (KEEP) {
+      pv = make_float4(p[4 * q + 0], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]);
+    } else {
+      pv = load4(g, i0, n);
+      if (e != nullptr) {
+        const float4 r = load4(e, i0, n);
+        pv.x = pv.x + r.x;
+        pv.y = pv.y + r.y;
+        pv.z = pv.z + r.z;
+        pv.w = pv.w + r.w;
+      }
     }
     const float px[4] = {pv.x, pv.y, pv.z, pv.w};
     uint4 w = make_uint4(0u, 0u, 0u, 0u);
@@ -630,7 +643,10 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
                         code_bytes);
     else
       store_chunk<BITS, 4>(codes, i0, lane, field, code_bytes);
-    if (e != nullptr && i0 < n) store4(e, i0, n, make_float4(rr[0], rr[1], rr[2], rr[3]));
+    if (e != nullptr && i0 < n) {
+      if (i0 + 4 <= n) store4_nt(e + i0, make_float4(rr[0], rr[1], rr[2], rr[3]));
+      else store4(e, i0, n, make_float4(rr[0], rr[1], rr[2], rr[3]));
+    }
   }
 }
 
