@@ -209,6 +209,19 @@ def copy_reference(torch, stream, nbytes: int = 1 << 30) -> dict:
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
 
 
+def read_reference(torch, stream, nbytes: int = 1 << 30) -> dict:
+    """A plain read-once pass of known size (torch's sum over nbytes of
+    fp32): the ceiling of read-dominated kernels (quantizers without error
+    feedback) on this GPU, which sits well below a copy's read + write."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    src.normal_()
+    ms = time_back_to_back(torch, stream, lambda i: src.sum(), 20)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": f"reference read (sum over {nbytes >> 20} MiB)",
+            "ms": round(ms, 5), "moved_GBps": round(gbs, 2),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
+
+
 def time_oracle(run, size: int, d: int, budget: float = 0.5,
                 max_n: int = 1 << 22):
     """Throughput (GB/s of fp32 input) of run(n), a CPU oracle call on the
@@ -519,6 +532,22 @@ def suite_qsgd(torch, gq, WL, stream, tb):
     out.append(entry("dequantize qsgd W=1 n=65536", ms,
                      deq_bytes(4, 1, 512, g.numel(), 1, 0.0), g.numel(),
                      bound="latency"))
+    del g, c, m, o, q, dq
+    # supplementary: the same recipe and shape at n = 2^28 (the stream's first
+    # 65,536 values are the workload above), where the uniform no-EF path is
+    # HBM-bound rather than launch-bound
+    n = 1 << 28
+    g = torch.from_numpy(WL.qsgd_gradient(n)).cuda()
+    c, m = gq.alloc_payload(d, n)
+    o = torch.empty_like(g)
+    q = gq.PreparedQuantize(d, g, None, c, m, stream)
+    ms = tb(lambda i: q(0, 0))
+    out.append(entry(f"quantize qsgd s=4 d=512 n={n} (supplementary)", ms,
+                     quant_bytes(4, 1, 512, n, False), n))
+    dq = gq.PreparedDequantizeAccumulate(d, n, [c], [m], 1.0, 0.0, o, stream)
+    ms = tb(lambda i: dq())
+    out.append(entry(f"dequantize qsgd W=1 n={n} (supplementary)", ms,
+                     deq_bytes(4, 1, 512, n, 1, 0.0), n))
     return out
 
 
@@ -769,6 +798,8 @@ def main() -> int:
         del mw.q, mw.G
         torch.cuda.empty_cache()
         kernels.append(copy_reference(torch, stream))
+        kernels.append(read_reference(torch, stream))
+        torch.cuda.empty_cache()
         kernels += suite(torch, gq, WL, stream, args.reps, args.only)
     # host work after every GPU timing (see DEFERRED)
     torch.cuda.synchronize()
