@@ -478,11 +478,9 @@ __device__ __forceinline__ int layer_of_wave(const int64_t* __restrict__ off,
   return lo;
 }
 
-// The layers of a tile: lf holds its first element; starts[k] =
-// off[lf + 1 + k] for the ns layers that start inside it, or ns = -1 when
-// there are more than kMaxStarts.  offc: off[0..nl] when nl < kOffCache.
+// LDS of a tile's layer search: offc = off[0..nl] when nl < kOffCache,
+// otherwise starts[k] = off[lf + 1 + k] for the layers starting inside it.
 struct TileLayers {
-  int lf, ns;
   int64_t starts[kMaxStarts];
   int64_t offc[kOffCache];
 };
@@ -498,54 +496,70 @@ __device__ __forceinline__ void prefetch_offsets(int64_t (&o)[kOffPerThread],
   }
 }
 
-// Step 2: the tile [t0, t1).  Blocks of 256 threads; every thread calls it.
+// Step 2: the tile [t0, t1).  Blocks of 256 threads; every thread calls it
+// and gets the tile's first layer lf and the number ns of layers starting
+// inside it (-1 when there are more than kMaxStarts).  With off in LDS
+// (nl < kOffCache) one barrier: lf and lf + ns are the counts of off[1..nl)
+// at or below t0 and t1 - 1 (the largest l with off[l] <= x, empty layers
+// passed over), summed over the block; the starts are then read from the
+// LDS copy.  Otherwise two waves search off in global memory and the starts
+// are copied into LDS.
 __device__ void find_tile_layers(TileLayers& T, const int64_t (&o)[kOffPerThread],
                                  const int64_t* __restrict__ off, int nl,
-                                 int64_t t0, int64_t t1) {
+                                 int64_t t0, int64_t t1, int& lf, int& ns) {
   __shared__ int ends[2];
+  __shared__ int cnt[2][4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (nl < kOffCache) {
+    int c0 = 0, c1 = 0;
 #pragma unroll
     for (int j = 0; j < kOffPerThread; ++j) {
       const int idx = threadIdx.x + 256 * j;
       if (idx <= nl) T.offc[idx] = o[j];
+      if (idx >= 1 && idx < nl) {
+        c0 += o[j] <= t0 ? 1 : 0;
+        c1 += o[j] <= t1 - 1 ? 1 : 0;
+      }
+    }
+    auto addi = [](int a, int b) { return a + b; };
+    c0 = group_reduce<64>(c0, addi);
+    c1 = group_reduce<64>(c1, addi);
+    if (lane == 0) {
+      cnt[0][wave] = c0;
+      cnt[1][wave] = c1;
     }
     __syncthreads();
-    if (threadIdx.x < 2) ends[threadIdx.x] = layer_of(T.offc, nl, threadIdx.x ? t1 - 1 : t0);
-  } else {
-    const int wave = threadIdx.x >> 6;
-    if (wave < 2) {
-      const int l = layer_of_wave(off, nl, wave == 0 ? t0 : t1 - 1);
-      if ((threadIdx.x & 63) == 0) ends[wave] = l;
-    }
+    lf = cnt[0][0] + cnt[0][1] + cnt[0][2] + cnt[0][3];
+    const int ll = cnt[1][0] + cnt[1][1] + cnt[1][2] + cnt[1][3];
+    ns = (ll < lf || ll - lf > kMaxStarts) ? -1 : ll - lf;
+    return;
+  }
+  if (wave < 2) {
+    const int l = layer_of_wave(off, nl, wave == 0 ? t0 : t1 - 1);
+    if (lane == 0) ends[wave] = l;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const int lf = ends[0], ll = ends[1];
-    T.lf = lf;
-    T.ns = (ll < lf || ll - lf > kMaxStarts) ? -1 : ll - lf;
-  }
-  __syncthreads();
-  const int ns = T.ns;
-  if (ns > 0 && (int)threadIdx.x < ns)
-    T.starts[threadIdx.x] = nl < kOffCache ? T.offc[T.lf + 1 + threadIdx.x]
-                                           : off[T.lf + 1 + threadIdx.x];
+  lf = ends[0];
+  const int ll = ends[1];
+  ns = (ll < lf || ll - lf > kMaxStarts) ? -1 : ll - lf;
+  if (ns > 0 && (int)threadIdx.x < ns) T.starts[threadIdx.x] = off[lf + 1 + threadIdx.x];
   __syncthreads();
 }
 
-// Layer of flat element i of the tile.
-__device__ __forceinline__ int elem_layer(const TileLayers& T,
+// Layer of flat element i of the tile (lf, ns from find_tile_layers).
+__device__ __forceinline__ int elem_layer(const TileLayers& T, int lf, int ns,
                                           const int64_t* __restrict__ off,
                                           int nl, int64_t i) {
-  const int ns = T.ns;
-  if (ns == 0) return T.lf;
+  if (ns == 0) return lf;
   if (ns < 0) return layer_of(nl < kOffCache ? T.offc : off, nl, i);
+  const int64_t* st = nl < kOffCache ? T.offc + lf + 1 : T.starts;
   int lo = 0, hi = ns;  // count of starts <= i
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
-    if (T.starts[mid] <= i) lo = mid + 1;
+    if (st[mid] <= i) lo = mid + 1;
     else hi = mid;
   }
-  return T.lf + lo;
+  return lf + lo;
 }
 
 }  // namespace gq

@@ -521,11 +521,11 @@ __global__ __launch_bounds__(kThreads) void k_layer_deq(
     }
   };
   load_batch(0);
-  find_tile_layers(T, o, off, nl, t0, t1);
-  const int ns = T.ns;
+  int lf, ns;
+  find_tile_layers(T, o, off, nl, t0, t1, lf, ns);
   const int nent = ns >= 0 ? ns + 1 : 0;
   for (int t = threadIdx.x; t < W * nent; t += kThreads)
-    dtab[t / nent][t % nent] = pp.meta[t / nent][T.lf + t % nent] / (float)s;
+    dtab[t / nent][t % nent] = pp.meta[t / nent][lf + t % nent] / (float)s;
   __syncthreads();
 
   // layer of each element (ns != 0): its LDS column, or (ns < 0) the layer
@@ -537,8 +537,8 @@ __global__ __launch_bounds__(kThreads) void k_layer_deq(
     for (int k = 0; k < 4; ++k) {
       li[v][k] = 0;
       if (ns != 0) {
-        const int l = elem_layer(T, off, nl, i + k < n ? i + k : n - 1);
-        li[v][k] = ns > 0 ? l - T.lf : l;
+        const int l = elem_layer(T, lf, ns, off, nl, i + k < n ? i + k : n - 1);
+        li[v][k] = ns > 0 ? l - lf : l;
       }
     }
   }

@@ -105,8 +105,9 @@ __global__ __launch_bounds__(kLThreads) void k_layer_absmax(
     // flight
     float4 p[kLV];
     if ((int)threadIdx.x <= kMaxStarts) smax[threadIdx.x] = 0u;
-    load_tile(p, g, e, tile_g, ngroups, n, [&] { find_tile_layers(T, o, off, nl, t0, t1); });
-    const int ns = T.ns;
+    int lf = 0, ns = 0;
+    load_tile(p, g, e, tile_g, ngroups, n,
+              [&] { find_tile_layers(T, o, off, nl, t0, t1, lf, ns); });
 #pragma unroll
     for (int v = 0; v < kLV; ++v) {
       const int64_t i = 4 * (tile_g + threadIdx.x + (int64_t)kLThreads * v);
@@ -124,8 +125,8 @@ __global__ __launch_bounds__(kLThreads) void k_layer_absmax(
           if (i + k >= n) break;
           const uint32_t b = __float_as_uint(fabsf(comp(p[v], k)));
           if (b == 0u) continue;
-          const int l = elem_layer(T, off, nl, i + k);
-          if (ns > 0) atomicMax(&smax[l - T.lf], b);
+          const int l = elem_layer(T, lf, ns, off, nl, i + k);
+          if (ns > 0) atomicMax(&smax[l - lf], b);
           else atomicMax(&meta_bits[l], b);
         }
       }
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(kLThreads) void k_layer_absmax(
     __syncthreads();
     if (threadIdx.x == 0 && ns >= 0) {
       for (int k = 0; k <= ns; ++k) {
-        const int l = T.lf + k;
+        const int l = lf + k;
         const uint32_t m = smax[k];
         if (l == cur_l) {
           cur_m = m > cur_m ? m : cur_m;
@@ -195,13 +196,13 @@ __global__ __launch_bounds__(kLThreads) void k_layer_quant(
   // loads are in flight (neither depends on them)
   int64_t o[kOffPerThread];
   prefetch_offsets(o, off, nl);
+  int lf = 0, ns = 0;
   load_tile(p, g, e, tile_g, ngroups, n, [&] {
     draw();
-    find_tile_layers(T, o, off, nl, t0, t1);
+    find_tile_layers(T, o, off, nl, t0, t1, lf, ns);
   });
-  const int ns = T.ns;
   if (ns >= 0 && (int)threadIdx.x <= ns)
-    sc[threadIdx.x] = layer_scale(meta[T.lf + threadIdx.x], sf);
+    sc[threadIdx.x] = layer_scale(meta[lf + threadIdx.x], sf);
   __syncthreads();
   const LayerScale c0 = ns >= 0 ? sc[0] : LayerScale{1.f, 0.f, 0.f};
 
@@ -217,8 +218,8 @@ __global__ __launch_bounds__(kLThreads) void k_layer_quant(
     for (int k = 0; k < 4; ++k) {
       LayerScale c = c0;
       if (ns != 0) {
-        const int l = elem_layer(T, off, nl, i + k < n ? i + k : n - 1);
-        c = ns > 0 ? sc[l - T.lf] : layer_scale(meta[l], sf);
+        const int l = elem_layer(T, lf, ns, off, nl, i + k < n ? i + k : n - 1);
+        c = ns > 0 ? sc[l - lf] : layer_scale(meta[l], sf);
       }
       const int ci = k < nreal ? uniform_code<true>(comp(p[v], k), c.up, c.inv, sf, ws[k]) : 0;
       sc4[k] = ci;

@@ -39,6 +39,9 @@ LAYOUTS = {
     # within 5,240 elements
     "multi_tile": [4096] * 3 + [4097, 4095, 8192, 8191, 1],
     "many_starts": [100] * 45 + [37] * 20 + [9000],
+    # 1024 layers or more: the layer search runs in global memory
+    "over_1024_layers": [200] * 1100 + [7],
+    "over_1024_tiny": [3] * 1200 + [5000],
 }
 
 
