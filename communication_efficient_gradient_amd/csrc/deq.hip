@@ -523,10 +523,23 @@ __global__ __launch_bounds__(kThreads) void k_layer_deq(
   load_batch(0);
   int lf, ns;
   find_tile_layers(T, o, off, nl, t0, t1, lf, ns);
-  const int nent = ns >= 0 ? ns + 1 : 0;
-  for (int t = threadIdx.x; t < W * nent; t += kThreads)
-    dtab[t / nent][t % nent] = pp.meta[t / nent][lf + t % nent] / (float)s;
-  __syncthreads();
+  // a tile inside one layer (ns = 0, block-uniform) reads each payload's
+  // step itself, without the LDS table and its barrier
+  if (ns != 0) {
+    const int nent = ns > 0 ? ns + 1 : 0;
+    for (int t = threadIdx.x; t < W * nent; t += kThreads)
+      dtab[t / nent][t % nent] = pp.meta[t / nent][lf + t % nent] / (float)s;
+    __syncthreads();
+  }
+  float dl[NB];  // ns = 0: the batch's steps
+  auto batch_steps = [&](int p0) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int p = p0 + j;
+      dl[j] = (ns == 0 && p < W) ? pp.meta[p][lf] / (float)s : 0.f;
+    }
+  };
+  batch_steps(0);
 
   // layer of each element (ns != 0): its LDS column, or (ns < 0) the layer
   int li[kV][4];
@@ -549,7 +562,10 @@ __global__ __launch_bounds__(kThreads) void k_layer_deq(
     acc1[v] = acc0[v];
   }
   for (int p0 = 0; p0 < W; p0 += NB) {
-    if (p0 > 0) load_batch(p0);
+    if (p0 > 0) {
+      load_batch(p0);
+      batch_steps(p0);
+    }
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int p = p0 + j;
@@ -561,7 +577,7 @@ __global__ __launch_bounds__(kThreads) void k_layer_deq(
         float x[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const float delta = ns == 0 ? dtab[p][0]
+          const float delta = ns == 0 ? dl[j]
                               : (ns > 0 ? dtab[p][li[v][k]]
                                         : pp.meta[p][li[v][k]] / (float)s);
           x[k] = (float)code_value<UNIFORM, BITS>(cw[j][v], k, s) * delta;

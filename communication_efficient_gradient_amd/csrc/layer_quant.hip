@@ -201,10 +201,17 @@ __global__ __launch_bounds__(kLThreads) void k_layer_quant(
     draw();
     find_tile_layers(T, o, off, nl, t0, t1, lf, ns);
   });
-  if (ns >= 0 && (int)threadIdx.x <= ns)
-    sc[threadIdx.x] = layer_scale(meta[lf + threadIdx.x], sf);
-  __syncthreads();
-  const LayerScale c0 = ns >= 0 ? sc[0] : LayerScale{1.f, 0.f, 0.f};
+  // a tile inside one layer (ns = 0, block-uniform) takes its layer's
+  // constants without the LDS table and its barrier
+  LayerScale c0{1.f, 0.f, 0.f};
+  if (ns == 0) {
+    c0 = layer_scale(meta[lf], sf);
+  } else {
+    if (ns > 0 && (int)threadIdx.x <= ns)
+      sc[threadIdx.x] = layer_scale(meta[lf + threadIdx.x], sf);
+    __syncthreads();
+    if (ns > 0) c0 = sc[0];
+  }
 
 #pragma unroll
   for (int v = 0; v < kLV; ++v) {
