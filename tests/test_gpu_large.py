@@ -6,7 +6,9 @@ word is in use) with ternary codes, fixed and dense.  The gradient is drawn
 on the device (torch's seeded normal generator) and the oracle recomputes
 sampled runs of buckets, always including the first and the last, from the
 same values copied to the host; the dequantizer is checked on the same
-runs.  Needs about 80 GB of device memory; skipped on smaller devices."""
+runs.  Needs about 80 GB of device memory; skipped on smaller devices.
+Also the aggregation of 8 payloads whose codes pass 256 MiB (the
+nontemporal path) with a ragged last run."""
 import numpy as np
 import pytest
 
@@ -167,4 +169,50 @@ def test_elias_past_2_30_buckets(dev):
     torch.cuda.synchronize()
     assert torch.equal(back[:cb], codes[:cb])
     del codes, back, off, words
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("s,bits", [(127, 8), (7, 4)])
+def test_aggregation_past_the_cache_ragged(dev, s, bits):
+    """W = 8 payloads whose codes together pass 256 MiB (the aggregation then
+    streams them nontemporally) with a ragged last wave run: n = 40M + 333
+    (8-bit) or 80M + 333 (4-bit).  Codes are drawn directly (every value of
+    the code range, -s..s) with positive scales; sampled runs, the last
+    bucket included, against the oracle's exact sum."""
+    gq, torch = dev
+    n = (40_000_000 if bits == 8 else 80_000_000) + 333
+    W = 8
+    d = O.Desc(O.UNIFORM, 512, s=s)
+    gd = gq.desc(0, 512, s=s)
+    nb = d.nb(n)
+    cb = d.code_bytes(n)
+    _need(torch, W * (cb + 4 * nb) + 4 * n)
+    say(f"aggregation s={s} n={n} W={W}")
+    rng = np.random.default_rng(77 + bits)
+    C, M = [], []
+    for w in range(W):
+        c = rng.integers(-s, s + 1, size=n, dtype=np.int64)
+        packed = O.pack(bits, (c & ((1 << bits) - 1)).astype(np.uint32))
+        cap = gq.gq_payload_size(gd, n)[1]
+        ct = torch.zeros(cap, dtype=torch.uint8, device="cuda")
+        ct[:cb] = torch.from_numpy(packed).cuda()
+        mt = torch.from_numpy(rng.uniform(1e-4, 1e-2, nb).astype(np.float32)).cuda()
+        C.append(ct)
+        M.append(mt)
+    out = torch.full((n,), float("nan"), device="cuda")
+    gq.gq_dequantize_accumulate(gd, n, C, M, 1.0 / W, 0.0, out)
+    torch.cuda.synchronize()
+    runs = sample_runs(nb, 6, RUN_LEN, seed=bits)
+    for j0 in runs:
+        j1 = min(nb, j0 + RUN_LEN)
+        lo, hi = j0 * 512, min(n, j1 * 512)
+        b0, b1 = _byte_range(d, lo, hi)
+        cl = [C[w][b0:b1].cpu().numpy() for w in range(W)]
+        ml = [M[w][j0:j1].cpu().numpy() for w in range(W)]
+        ref = O.dequantize_accumulate(d, hi - lo, cl, ml, 1.0 / W, 0.0)
+        xs = [np.abs(O.dequantize(d, hi - lo, c_, m_).astype(np.float64))
+              for c_, m_ in zip(cl, ml)]
+        compare_values(out[lo:hi].cpu().numpy(), ref, np.sum(xs, axis=0) / W)
+    assert not torch.isnan(out).any().item()
+    del C, M, out
     torch.cuda.empty_cache()
