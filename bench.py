@@ -209,19 +209,6 @@ def copy_reference(torch, stream, nbytes: int = 1 << 30) -> dict:
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
 
 
-def read_reference(torch, stream, nbytes: int = 1 << 30) -> dict:
-    """A plain read-once pass of known size (torch's sum over nbytes of
-    fp32): the ceiling of read-dominated kernels (quantizers without error
-    feedback) on this GPU, which sits well below a copy's read + write."""
-    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
-    src.normal_()
-    ms = time_back_to_back(torch, stream, lambda i: src.sum(), 20)
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"kernel": f"reference read (sum over {nbytes >> 20} MiB)",
-            "ms": round(ms, 5), "moved_GBps": round(gbs, 2),
-            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bound": "hbm"}
-
-
 def time_oracle(run, size: int, d: int, budget: float = 0.5,
                 max_n: int = 1 << 22):
     """Throughput (GB/s of fp32 input) of run(n), a CPU oracle call on the
@@ -798,7 +785,6 @@ def main() -> int:
         del mw.q, mw.G
         torch.cuda.empty_cache()
         kernels.append(copy_reference(torch, stream))
-        kernels.append(read_reference(torch, stream))
         torch.cuda.empty_cache()
         kernels += suite(torch, gq, WL, stream, args.reps, args.only)
     # host work after every GPU timing (see DEFERRED)
