@@ -759,8 +759,11 @@ __device__ __forceinline__ void store_vec(float* __restrict__ a, int64_t i,
   }
 }
 
+// At most 128 VGPRs (4 waves per SIMD): the recursive-bisection variant
+// would take 132 and run at 3 (ORQ-9 by bisection on 100M: 2.20 -> 1.94 ms
+// at 4 with 16 bytes per lane spilled); the others fit without spilling.
 template <int SCHEME, int BITS, int D, bool BISECT>
-__global__ __launch_bounds__(kGroupThreads)
+__global__ __launch_bounds__(kGroupThreads, 4)
 void k_wave_sort_quant(
     int64_t n, int64_t nb, const float* __restrict__ g, float* __restrict__ e,
     uint32_t k0, uint32_t k1, uint32_t step, int L, int flags, float clip_sigma,
