@@ -22,6 +22,12 @@ Parity status of each routine (what pins it is in ``tests/test_oracle_*``):
     elias encode / decode textbook gamma codewords (golden file), a bit-string
                           parser written in the test, lengths from the
                           code-length formula, round trips
+    allocate_layer_bits   brute force over every allocation of small
+                          layouts (exact rational bounds), monotone widths,
+                          budget extremes
+    *_layers_alloc        values on each layer's grid next to p, exact
+                          residual, segment sizes and padding, exact
+                          rational aggregation, one width = per-layer path
 """
 from __future__ import annotations
 
@@ -402,3 +408,147 @@ def elias_decode(d: int, s: int, n: int, off, words):
     if lib().gqref_elias_decode(d, s, n, _ptr(off), _ptr(words), _ptr(codes)):
         raise ValueError("oracle elias_decode: invalid arguments or stream")
     return codes
+
+
+# ------------------------------------------------ layer-wise bit allocation --
+# "Gradient Quantization" glossary, layer-wise quantization paragraph: layers
+# with larger gradient variance get wider codes; the page gives no rule.
+# Reading: widths b in {2, 3, 4, 8} with s = 2^(b-1) - 1 levels per sign on
+# the per-layer scale path (the most a b-bit two's-complement code holds
+# symmetrically); the objective is the sum over layers of the bound
+# n_l * M_l^2 / (4 s_l^2) on the layer's rounding variance (every element's
+# (b - x)(x - a) is at most step^2 / 4, step = M_l / s_l); every layer starts
+# at 2 bits and upgrades are taken in decreasing order of bound reduction per
+# added bit, M_l^2 (1/s_b^2 - 1/s_b'^2) / (4 (b' - b)), equal reductions by
+# layer then width, until the first that does not fit the budget of code
+# bits; upgrades that reduce nothing (M_l = 0, empty layers) are not taken.
+# Parity status: pinned by brute force over every allocation of small
+# layouts (the greedy's bound is the least of all allocations using no more
+# bits), monotonicity in M_l, budget and extremes (tests/test_oracle_alloc).
+ALLOC_WIDTHS = (2, 3, 4, 8)
+
+
+def alloc_levels(bits: int) -> int:
+    """s for a width b of the allocation: 2^(b-1) - 1."""
+    return (1 << (bits - 1)) - 1
+
+
+def alloc_gain_per_bit(scale: float, b0: int, b1: int) -> float:
+    """Bound reduction per added code bit of one element when a layer of
+    max-abs `scale` goes from b0 to b1 bits (fp64; the element count
+    cancels)."""
+    s0, s1 = alloc_levels(b0), alloc_levels(b1)
+    m2 = float(np.float64(np.float32(scale))) ** 2
+    return m2 * ((1.0 / (s0 * s0) - 1.0 / (s1 * s1)) / (4.0 * (b1 - b0)))
+
+
+def allocate_layer_bits(sizes, scales, budget_bits: int):
+    """Code width of every layer under a budget of total code bits.
+
+    sizes: element count n_l of each layer; scales: its max-abs M_l (fp32);
+    budget_bits: at least 2 * sum(sizes).  Returns (widths, bits used)."""
+    sizes = [int(x) for x in sizes]
+    nl = len(sizes)
+    if len(scales) != nl or any(x < 0 for x in sizes):
+        raise ValueError("allocate_layer_bits: sizes and scales differ")
+    used = 2 * sum(sizes)
+    if budget_bits < used:
+        raise ValueError("allocate_layer_bits: budget below 2 bits per element")
+    widths = [2] * nl
+    ups = []
+    for lay in range(nl):
+        for b0, b1 in zip(ALLOC_WIDTHS[:-1], ALLOC_WIDTHS[1:]):
+            ups.append((alloc_gain_per_bit(scales[lay], b0, b1), lay, b0, b1))
+    ups.sort(key=lambda t: (-t[0], t[1], t[2]))
+    for gain, lay, b0, b1 in ups:
+        if gain <= 0.0:
+            break  # the rest reduce nothing either
+        if sizes[lay] == 0:
+            continue
+        cost = sizes[lay] * (b1 - b0)
+        if used + cost > budget_bits:
+            break
+        assert widths[lay] == b0  # a layer's gains per bit strictly decrease
+        widths[lay] = b1
+        used += cost
+    return widths, used
+
+
+def alloc_segments(sizes, widths):
+    """Byte offsets of the layers' code segments in a payload of the
+    allocation: layer l's n_l codes LSB-first at widths[l] bits, each segment
+    padded to a multiple of 16 bytes; the last entry is the payload size."""
+    seg = [0]
+    for n_l, b in zip(sizes, widths):
+        nbytes = (int(n_l) * int(b) + 7) // 8
+        seg.append(seg[-1] + (nbytes + 15) // 16 * 16)
+    return seg
+
+
+def quantize_layers_alloc(offsets, g, e, widths, seed: int = 0, step: int = 0,
+                          flags: int = 0):
+    """The per-layer scale path with layer l at widths[l] bits: each layer's
+    codes are those quantize_layers gives at s = 2^(b-1) - 1 (same scale,
+    random word and rounding), stored in the layer's own segment.  Returns
+    (payload u8, meta f32[nl] = the layers' max-abs, e_new or None)."""
+    g = _f32(g)
+    n = g.size
+    off = _offsets(offsets, n)
+    nl = off.size - 1
+    if len(widths) != nl or any(b not in ALLOC_WIDTHS for b in widths):
+        raise ValueError("quantize_layers_alloc: one width from ALLOC_WIDTHS per layer")
+    sizes = np.diff(off)
+    seg = alloc_segments(sizes, widths)
+    payload = np.zeros(seg[-1], dtype=np.uint8)
+    e_new = None if e is None else np.empty(n, dtype=np.float32)
+    meta = np.zeros(nl, dtype=np.float32)
+    for b in sorted(set(widths)):
+        d = Desc(UNIFORM, 512, s=alloc_levels(b), flags=flags)
+        codes, m, en = quantize_layers(d, off, g, e, seed=seed, step=step)
+        fields = unpack(b, n, codes)
+        for lay in range(nl):
+            if widths[lay] != b:
+                continue
+            lo, hi = int(off[lay]), int(off[lay + 1])
+            meta[lay] = m[lay]
+            if hi > lo:
+                packed = pack(b, fields[lo:hi])
+                payload[seg[lay]:seg[lay] + packed.size] = packed
+            if e is not None:
+                e_new[lo:hi] = en[lo:hi]
+    return payload, meta, e_new
+
+
+def dequantize_layers_alloc(offsets, n: int, payload, meta, widths):
+    """x_hat of one allocation payload: each layer's codes times its step
+    M_l / s_l, as dequantize_accumulate_layers gives at that layer's s."""
+    off = _offsets(offsets, n)
+    nl = off.size - 1
+    sizes = np.diff(off)
+    seg = alloc_segments(sizes, widths)
+    pay = np.ascontiguousarray(payload, dtype=np.uint8)
+    x = np.zeros(n, dtype=np.float32)
+    for b in sorted(set(widths)):
+        fields = np.zeros(n, dtype=np.uint32)
+        for lay in range(nl):
+            lo, hi = int(off[lay]), int(off[lay + 1])
+            if widths[lay] == b and hi > lo:
+                fields[lo:hi] = unpack(b, hi - lo, pay[seg[lay]:seg[lay + 1]])
+        d = Desc(UNIFORM, 512, s=alloc_levels(b))
+        xb = dequantize_accumulate_layers(d, off, n, [pack(b, fields)], [meta])
+        for lay in range(nl):
+            if widths[lay] == b:
+                x[int(off[lay]):int(off[lay + 1])] = xb[int(off[lay]):int(off[lay + 1])]
+    return x
+
+
+def dequantize_accumulate_layers_alloc(offsets, n: int, payloads, metas,
+                                       widths_list, alpha: float = 1.0,
+                                       beta: float = 0.0, out=None):
+    """out <- beta * out + alpha * sum_w x_hat_w over W allocation payloads
+    (each with its own widths), summed in fp64 and rounded once."""
+    acc = np.zeros(n, dtype=np.float64)
+    for pay, m, wd in zip(payloads, metas, widths_list):
+        acc += dequantize_layers_alloc(offsets, n, pay, m, wd).astype(np.float64)
+    base = np.zeros(n) if out is None else _f32(out).astype(np.float64)
+    return (float(beta) * base + float(alpha) * acc).astype(np.float32)
