@@ -161,3 +161,17 @@ def test_aggregate_is_the_exact_sum_rounded_once():
             Fraction(float(x[i])) for x in xs)
         ref = np.float32(float(exact))
         assert abs(float(got[i]) - float(ref)) <= 1e-6 * (abs(float(ref)) + 1e-30)
+
+
+def test_gain_is_per_added_bit():
+    """Hand-worked: two layers of 10 elements, M = 3e-3 and 1e-3.  Bound
+    reductions per added bit, M^2 (1/s^2 - 1/s'^2) / (4 (b' - b)):
+    A 2->3 2.0e-6, B 2->3 2.2e-7, A 3->4 2.0e-7, B 3->4 2.3e-8, A 4->8
+    1.1e-8 (a 4->8 step adds 4 bits per element).  With 100 bits: A, B to 3
+    (60 bits), A, B to 4 (80 bits), then A 4->8 needs 40 more: stop at
+    (4, 4).  Ranking the 4->8 step by its whole reduction (4.6e-8, above
+    B 3->4) would stop at (4, 3) with 70 bits."""
+    widths, used = O.allocate_layer_bits([10, 10], [3e-3, 1e-3], 100)
+    assert widths == [4, 4] and used == 80
+    widths, used = O.allocate_layer_bits([10, 10], [3e-3, 1e-3], 120)
+    assert widths == [8, 4] and used == 120
