@@ -290,6 +290,26 @@ int gq_quantize_layers(const gq_desc* desc, int64_t n, int32_t nl,
                                               static_cast<hipStream_t>(stream)));
 }
 
+int gq_allocate_layer_bits(int64_t n, int32_t nl, const int64_t* layer_offsets,
+                           const float* scales, int64_t budget_bits,
+                           int32_t* widths, int64_t* segments, void* stream) {
+  if (n < 1 || n > kMaxN || nl < 1 || !layer_offsets || !scales || !widths ||
+      !segments || budget_bits < 2 * n)
+    return GQ_EINVAL;
+  if (nl > 1024) return GQ_EUNSUPPORTED;
+  if (!aligned16(scales) || !aligned16(widths) || !aligned16(segments) ||
+      reinterpret_cast<uintptr_t>(layer_offsets) % 8)
+    return GQ_EINVAL;
+  const int64_t ob = 8 * ((int64_t)nl + 1), sb = 4 * (int64_t)nl;
+  if (overlap(widths, sb, layer_offsets, ob) || overlap(widths, sb, scales, sb) ||
+      overlap(segments, ob, layer_offsets, ob) || overlap(segments, ob, scales, sb) ||
+      overlap(widths, sb, segments, ob))
+    return GQ_EINVAL;
+  return launch_status(gq::launch_layer_alloc(nl, layer_offsets, scales,
+                                              budget_bits, widths, segments,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 int gq_dequantize_accumulate_layers(const gq_desc* desc, int64_t n, int32_t nl,
                                     const int64_t* layer_offsets, int32_t W,
                                     const uint8_t* const* codes,

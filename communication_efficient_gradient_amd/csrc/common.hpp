@@ -618,6 +618,9 @@ int launch_layer_quant(const LaunchDesc& L, int64_t n, int nl,
                        const int64_t* off, const float* g, float* e,
                        uint64_t seed, uint32_t step, uint8_t* codes,
                        float* meta, int64_t code_bytes, hipStream_t st);
+int launch_layer_alloc(int nl, const int64_t* off, const float* scales,
+                       int64_t budget, int32_t* widths, int64_t* seg,
+                       hipStream_t st);
 int launch_layer_deq(const LaunchDesc& L, int64_t n, int nl,
                      const int64_t* off, int W, const PayloadPtrs& pp,
                      float alpha, float beta, float* out, int64_t code_bytes,

@@ -258,7 +258,158 @@ __global__ __launch_bounds__(kLThreads) void k_layer_quant(
   }
 }
 
+// ------------------------------------------------ layer-wise bit allocation
+// ("Gradient Quantization" glossary, layer-wise quantization paragraph:
+// wider codes for layers with larger gradient variance).  One block: widths
+// b in {2, 3, 4, 8} (s = 2^(b-1) - 1) start at 2; the 3 nl upgrades
+// (2->3, 3->4, 4->8 of each layer) are sorted by the reduction of the
+// layer's variance bound n_l M_l^2 / (4 s^2) per added bit,
+// M_l^2 (1/s_b^2 - 1/s_b'^2) / (4 (b' - b)) in fp64, equal reductions by
+// layer, then width (bitonic sort in LDS), and taken in that order up to the
+// first that does not fit the budget of code bits; upgrades that reduce
+// nothing end the list, those of empty layers are passed over.  Then each
+// layer's code segment: its n_l codes at its width, padded to 16 bytes.
+constexpr int kAllocThreads = 1024;
+constexpr int kAllocMaxLayers = 1024;
+constexpr int kAllocSlots = 4096;  // >= 3 * kAllocMaxLayers, a power of two
+
+__device__ __forceinline__ double alloc_step_gain(float m, int k) {
+  // k = 0, 1, 2: 2->3, 3->4, 4->8 (s = 1, 3, 7, 127)
+  const double s0 = k == 0 ? 1.0 : (k == 1 ? 3.0 : 7.0);
+  const double s1 = k == 0 ? 3.0 : (k == 1 ? 7.0 : 127.0);
+  const double db = k == 2 ? 4.0 : 1.0;
+  const double m2 = (double)m * (double)m;
+  return m2 * ((1.0 / (s0 * s0) - 1.0 / (s1 * s1)) / (4.0 * db));
+}
+
+// Inclusive block scan of one int64 per thread (1024 threads).
+__device__ int64_t alloc_block_scan(int64_t v, int64_t* tmp) {
+  const int t = threadIdx.x;
+  tmp[t] = v;
+  __syncthreads();
+  for (int o = 1; o < kAllocThreads; o <<= 1) {
+    const int64_t add = t >= o ? tmp[t - o] : 0;
+    __syncthreads();
+    tmp[t] += add;
+    __syncthreads();
+  }
+  const int64_t r = tmp[t];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kAllocThreads) void k_layer_alloc(
+    int nl, const int64_t* __restrict__ off, const float* __restrict__ scales,
+    int64_t budget, int32_t* __restrict__ widths, int64_t* __restrict__ seg) {
+  __shared__ double gain[kAllocSlots];
+  __shared__ int key[kAllocSlots];          // layer * 3 + step
+  __shared__ int64_t scan[kAllocThreads];
+  __shared__ int wid[kAllocMaxLayers];
+  __shared__ int64_t nsz[kAllocMaxLayers];
+  __shared__ int first_stop;
+  __shared__ int64_t used_sh;
+  const int t = threadIdx.x;
+  if (t < nl) {
+    const int64_t a = off[t], b = off[t + 1];
+    nsz[t] = b > a ? b - a : 0;
+    wid[t] = 2;
+  }
+  if (t == 0) first_stop = kAllocSlots;
+  for (int i = t; i < kAllocSlots; i += kAllocThreads) {
+    const int lay = i / 3;
+    if (lay < nl) {
+      gain[i] = alloc_step_gain(scales[lay], i % 3);
+      key[i] = i;
+    } else {
+      gain[i] = -1.0;  // padding sorts last (real gains are >= 0)
+      key[i] = 0x7fffffff;
+    }
+  }
+  __syncthreads();
+  // bitonic sort: larger gain first, then smaller key
+  for (int k = 2; k <= kAllocSlots; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = t; i < kAllocSlots; i += kAllocThreads) {
+        const int p = i ^ j;
+        if (p > i) {
+          const bool before_ip = gain[i] > gain[p] || (gain[i] == gain[p] && key[i] < key[p]);
+          const bool want = (i & k) == 0;  // this run ascending in "before"
+          if (before_ip != want) {
+            const double g0 = gain[i];
+            gain[i] = gain[p];
+            gain[p] = g0;
+            const int k0 = key[i];
+            key[i] = key[p];
+            key[p] = k0;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // costs in sorted order (4 slots per thread), their running total, and
+  // the first slot that ends the list (no reduction, or over the budget)
+  // bits of every layer at 2: the block's total, from the last thread
+  {
+    const int64_t incl = alloc_block_scan(t < nl ? 2 * nsz[t] : 0, scan);
+    if (t == kAllocThreads - 1) used_sh = incl;
+    __syncthreads();
+  }
+  const int64_t used0 = used_sh;
+  int64_t c[4];
+  int64_t loc = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = 4 * t + q;
+    const int kk = key[i];
+    int64_t cost = 0;
+    if (kk != 0x7fffffff) {
+      const int lay = kk / 3, st = kk % 3;
+      cost = nsz[lay] * (st == 2 ? 4 : 1);
+    }
+    loc += cost;
+    c[q] = loc;
+  }
+  const int64_t excl = alloc_block_scan(loc, scan) - loc;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = 4 * t + q;
+    const bool stop = !(gain[i] > 0.0) || used0 + excl + c[q] > budget;
+    if (stop) atomicMin(&first_stop, i);
+  }
+  __syncthreads();
+  const int fs = first_stop;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = 4 * t + q;
+    if (i < fs) {
+      const int kk = key[i];
+      const int lay = kk / 3, st = kk % 3;
+      if (nsz[lay] > 0) atomicMax(&wid[lay], st == 0 ? 3 : (st == 1 ? 4 : 8));
+    }
+  }
+  __syncthreads();
+  // segments: each layer's codes at its width, padded to 16 bytes
+  int64_t bytes = 0;
+  if (t < nl) {
+    widths[t] = wid[t];
+    bytes = ((nsz[t] * wid[t] + 7) / 8 + 15) / 16 * 16;
+  }
+  const int64_t incl = alloc_block_scan(bytes, scan);
+  if (t < nl) seg[t + 1] = incl;
+  if (t == 0) seg[0] = 0;
+}
+
 }  // namespace
+
+int launch_layer_alloc(int nl, const int64_t* off, const float* scales,
+                       int64_t budget, int32_t* widths, int64_t* seg,
+                       hipStream_t st) {
+  if (nl < 1 || nl > kAllocMaxLayers) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_layer_alloc, dim3(1), dim3(kAllocThreads), 0, st, nl,
+                     off, scales, budget, widths, seg);
+  return (int)hipGetLastError();
+}
 
 int launch_layer_quant(const LaunchDesc& L, int64_t n, int nl,
                        const int64_t* off, const float* g, float* e,

@@ -28,6 +28,7 @@ GQ_MAX_PAYLOADS = 16
 SYMBOLS = ("gq_code_bits", "gq_payload_size", "gq_select_levels",
            "gq_quantize", "gq_error_feedback", "gq_dequantize_accumulate",
            "gq_quantize_layers", "gq_dequantize_accumulate_layers",
+           "gq_allocate_layer_bits",
            "gq_elias_max_words", "gq_elias_encode", "gq_elias_decode",
            "gq_strerror", "gq_version")
 
@@ -72,6 +73,7 @@ def _load():
     lib.gq_dequantize_accumulate_layers.argtypes = [
         D, i64, i32, P, i32, C.POINTER(P), C.POINTER(P), C.c_float, C.c_float,
         P, P]
+    lib.gq_allocate_layer_bits.argtypes = [i64, i32, P, P, i64, P, P, P]
     lib.gq_elias_max_words.argtypes = [D, i64, C.POINTER(i64)]
     lib.gq_elias_encode.argtypes = [D, i64, P, P, P, P]
     lib.gq_elias_decode.argtypes = [D, i64, P, P, i64, P, P]
@@ -368,3 +370,20 @@ class PreparedDequantizeAccumulate:
     def __call__(self) -> None:
         _check(_lib.gq_dequantize_accumulate(*self._args),
                "gq_dequantize_accumulate")
+
+
+def gq_allocate_layer_bits(n: int, layer_offsets: torch.Tensor,
+                           scales: torch.Tensor, budget_bits: int,
+                           widths: torch.Tensor, segments: torch.Tensor,
+                           stream=None) -> None:
+    """Widths (int32[nl]) and code segment offsets (int64[nl + 1]) of the
+    layer-wise allocation; see include/gq.h."""
+    nl = layer_offsets.numel() - 1
+    _need(scales, nl, "scales")
+    _need(widths, nl, "widths")
+    _need(segments, nl + 1, "segments")
+    _check(_lib.gq_allocate_layer_bits(
+        n, nl, _ptr(layer_offsets, torch.int64, "layer_offsets"),
+        _ptr(scales, torch.float32, "scales"), budget_bits,
+        _ptr(widths, torch.int32, "widths"), _ptr(segments, torch.int64, "segments"),
+        _stream(stream, scales)), "gq_allocate_layer_bits")

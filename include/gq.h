@@ -226,6 +226,28 @@ int gq_dequantize_accumulate_layers(const gq_desc* desc, int64_t n, int32_t nl,
                                     const float* const* meta, float alpha,
                                     float beta, float* out, void* stream);
 
+/* Layer-wise bit allocation ("Gradient Quantization" glossary, layer-wise
+ * quantization paragraph: wider codes for layers with larger gradient
+ * variance; the page gives no rule).  For the per-layer scale path: each of
+ * the nl <= 1024 layers (layer_offsets as in gq_quantize_layers) gets a
+ * width b in {2, 3, 4, 8}, with s = 2^(b-1) - 1 levels per sign.  All start
+ * at 2; the upgrades 2->3, 3->4, 4->8 of every layer are ranked by the
+ * reduction of the layer's bound n_l * M_l^2 / (4 s^2) on its rounding
+ * variance per added bit, M_l^2 * (1/s_b^2 - 1/s_b'^2) / (4 (b' - b)) in
+ * fp64 (M_l = scales[l], e.g. the meta gq_quantize_layers writes), equal
+ * values by layer, then width, and taken in that order up to the first
+ * that would pass budget_bits total code bits (budget_bits >= 2 n;
+ * upgrades that reduce nothing end the list; empty layers keep 2).
+ * Outputs (DEVICE): widths[nl] int32, segments[nl + 1] int64 byte offsets
+ * of each layer's code segment in a payload of the allocation (its n_l
+ * codes at its width, padded to 16 bytes; segments[nl] = payload bytes).
+ * GQ_EUNSUPPORTED for nl > 1024.  One block on the stream; offsets are not
+ * read on the host (other contents: unspecified outputs, in-bounds
+ * accesses). */
+int gq_allocate_layer_bits(int64_t n, int32_t nl, const int64_t* layer_offsets,
+                           const float* scales, int64_t budget_bits,
+                           int32_t* widths, int64_t* segments, void* stream);
+
 /* Elias gamma coding of GQ_UNIFORM codes, the lossless integer coding QSGD
  * applies after quantizing ("Gradient Quantization" glossary, QSGD
  * paragraph).  Code c (in element order) is written as the Elias gamma code
