@@ -328,7 +328,8 @@ def suite_elias(torch, gq, WL, stream, tb):
         nb = S[0][0].numel() - 1
         nw = int(S[0][0][-1].item())
         codes_h = P[0][0][:cb].cpu().numpy()
-        oracle = time_oracle(lambda k: O.elias_encode(512, s, k, codes_h), n, 512)
+        oracle = {"_oracle": lambda s_=s, ch=codes_h: time_oracle(
+            lambda k: O.elias_encode(512, s_, k, ch), n, 512)}
         stream_bytes = 4 * nw + 8 * (nb + 1)
         extra = {"bits_per_element": round(32 * nw / n, 4),
                  "fixed_bits": 8 * cb / n,
@@ -365,9 +366,9 @@ def suite_topk(torch, gq, WL, stream, tb):
     O_ = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(2)]
     qs = [gq.PreparedQuantize(d, G[k], E[k], P[k][0], P[k][1], stream) for k in range(2)]
     ms = tb(lambda i: qs[i % 2](2, i))
-    oracle = time_oracle(lambda k: O.quantize_topk(512, 4, 26, host[:k],
-                                                   np.zeros(k, np.float32), seed=2),
-                         n, 512)
+    oracle = {"_oracle": lambda: time_oracle(
+        lambda k: O.quantize_topk(512, 4, 26, host[:k], np.zeros(k, np.float32),
+                                  seed=2), n, 512)}
     out.append(entry(f"quantize top-k 26/512 s=4 +ef n={n}", ms,
                      12 * n + cb + 4 * mf, n,
                      extra={"compression_vs_fp32": round(4 * n / (cb + 4 * mf), 3),
@@ -409,11 +410,20 @@ def suite_layers(torch, gq, WL, stream, tb):
                           np.zeros(k, np.float32), seed=2)
     out.append(entry(f"quantize ternary+ef per-layer scale ({nl} layers) n={n}",
                      ms, 20 * n + (2 * n + 7) // 8 + 4 * nl, n,
-                     extra=time_oracle(oracle_layers, n, 512)))
+                     extra={"_oracle": lambda: time_oracle(oracle_layers, n, 512)}))
     ms = tb(lambda i: gq.gq_dequantize_accumulate_layers(
         d, n, off, [C[i % 2]], [M[i % 2]], 1.0, 0.0, O_[i % 2], stream))
     out.append(entry(f"dequantize ternary per-layer scale W=1 n={n}", ms,
                      (2 * n + 7) // 8 + 4 * nl + 4 * n, n))
+    # layer-wise bit allocation over the same layers and their scales: one
+    # block, latency-bound (reads offsets and scales, writes widths and
+    # segment offsets)
+    Wd = torch.empty(nl, dtype=torch.int32, device="cuda")
+    Sg = torch.empty(nl + 1, dtype=torch.int64, device="cuda")
+    ms = tb(lambda i: gq.gq_allocate_layer_bits(n, off, M[0], 3 * n, Wd, Sg, stream))
+    out.append(entry(f"allocate layer bits ({nl} layers, 3 bits per element)", ms,
+                     8 * (nl + 1) + 4 * nl + 4 * nl + 8 * (nl + 1), nl,
+                     bound="latency"))
     return out
 
 
