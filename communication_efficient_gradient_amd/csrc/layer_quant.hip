@@ -282,20 +282,21 @@ __device__ __forceinline__ double alloc_step_gain(float m, int k) {
   return m2 * ((1.0 / (s0 * s0) - 1.0 / (s1 * s1)) / (4.0 * db));
 }
 
-// Inclusive block scan of one int64 per thread (1024 threads).
+// Inclusive block scan of one int64 per thread (1024 threads): a shuffle
+// scan in each wave, the 16 wave totals through LDS, one barrier.
 __device__ int64_t alloc_block_scan(int64_t v, int64_t* tmp) {
-  const int t = threadIdx.x;
-  tmp[t] = v;
-  __syncthreads();
-  for (int o = 1; o < kAllocThreads; o <<= 1) {
-    const int64_t add = t >= o ? tmp[t - o] : 0;
-    __syncthreads();
-    tmp[t] += add;
-    __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
   }
-  const int64_t r = tmp[t];
+  if (lane == 63) tmp[wave] = v;
   __syncthreads();
-  return r;
+  int64_t before = 0;
+  for (int w = 0; w < wave; ++w) before += tmp[w];
+  __syncthreads();  // tmp is reused by the next scan
+  return v + before;
 }
 
 __global__ __launch_bounds__(kAllocThreads) void k_layer_alloc(
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(kAllocThreads) void k_layer_alloc(
     int64_t budget, int32_t* __restrict__ widths, int64_t* __restrict__ seg) {
   __shared__ double gain[kAllocSlots];
   __shared__ int key[kAllocSlots];          // layer * 3 + step
-  __shared__ int64_t scan[kAllocThreads];
+  __shared__ int64_t scan[kAllocThreads / 64];
   __shared__ int wid[kAllocMaxLayers];
   __shared__ int64_t nsz[kAllocMaxLayers];
   __shared__ int first_stop;
@@ -326,10 +327,13 @@ __global__ __launch_bounds__(kAllocThreads) void k_layer_alloc(
     }
   }
   __syncthreads();
-  // bitonic sort: larger gain first, then smaller key
-  for (int k = 2; k <= kAllocSlots; k <<= 1) {
+  // bitonic sort of the first P slots (P: the power of two >= 3 nl; the
+  // rest is padding already in place): larger gain first, then smaller key
+  int P = 1;
+  while (P < 3 * nl) P <<= 1;
+  for (int k = 2; k <= P; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = t; i < kAllocSlots; i += kAllocThreads) {
+      for (int i = t; i < P; i += kAllocThreads) {
         const int p = i ^ j;
         if (p > i) {
           const bool before_ip = gain[i] > gain[p] || (gain[i] == gain[p] && key[i] < key[p]);
