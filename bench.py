@@ -797,6 +797,12 @@ def main() -> int:
         kernels.append(copy_reference(torch, stream))
         torch.cuda.empty_cache()
         kernels += suite(torch, gq, WL, stream, args.reps, args.only)
+    # every HBM-bound entry also as a fraction of the plain copy of this run
+    ref = next((k for k in kernels if k["kernel"].startswith("reference copy")), None)
+    if ref is not None:
+        for k in kernels:
+            if k.get("bound") == "hbm" and k is not ref:
+                k["copy_frac"] = round(k["moved_GBps"] / ref["moved_GBps"], 4)
     # host work after every GPU timing (see DEFERRED)
     torch.cuda.synchronize()
     run_deferred()
