@@ -310,6 +310,80 @@ int gq_allocate_layer_bits(int64_t n, int32_t nl, const int64_t* layer_offsets,
                                               static_cast<hipStream_t>(stream)));
 }
 
+// Room for the payload of any allocation: every code at 8 bits plus the
+// padding of every segment.
+static int64_t alloc_capacity(int64_t n, int32_t nl) { return n + 16 * (int64_t)nl; }
+
+int gq_alloc_payload_bytes(int64_t n, int32_t nl, int64_t* bytes) {
+  if (n < 1 || n > kMaxN || nl < 1 || !bytes) return GQ_EINVAL;
+  *bytes = alloc_capacity(n, nl);
+  return GQ_OK;
+}
+
+int gq_quantize_layers_alloc(int64_t n, int32_t nl, const int64_t* layer_offsets,
+                             const float* g, float* e, const int32_t* widths,
+                             const int64_t* segments, uint64_t seed,
+                             uint32_t step, int32_t flags, uint8_t* payload,
+                             int64_t payload_bytes, float* meta, void* stream) {
+  if (n < 1 || n > kMaxN || nl < 1 || !layer_offsets || !g || !widths ||
+      !segments || !payload || !meta || (flags & ~GQ_FLAG_NEAREST))
+    return GQ_EINVAL;
+  if (payload_bytes < alloc_capacity(n, nl)) return GQ_EINVAL;
+  if (!aligned16(g) || !aligned16(payload) || !aligned16(meta) ||
+      (e && !aligned16(e)) || reinterpret_cast<uintptr_t>(layer_offsets) % 8 ||
+      reinterpret_cast<uintptr_t>(widths) % 4 ||
+      reinterpret_cast<uintptr_t>(segments) % 8)
+    return GQ_EINVAL;
+  const int64_t mb = 4 * (int64_t)nl, ob = 8 * ((int64_t)nl + 1);
+  const int64_t pb = payload_bytes;
+  const void* in[4] = {layer_offsets, widths, segments, g};
+  const int64_t in_b[4] = {ob, mb, ob, 4 * n};
+  for (int k = 0; k < 4; ++k) {
+    if (overlap(payload, pb, in[k], in_b[k]) || overlap(meta, mb, in[k], in_b[k]) ||
+        (e && overlap(e, 4 * n, in[k], in_b[k])))
+      return GQ_EINVAL;
+  }
+  if (overlap(payload, pb, meta, mb) || (e && (overlap(e, 4 * n, payload, pb) ||
+                                              overlap(e, 4 * n, meta, mb))))
+    return GQ_EINVAL;
+  return launch_status(gq::launch_alloc_quant(
+      n, nl, layer_offsets, g, e, widths, segments, seed, step,
+      (flags & GQ_FLAG_NEAREST) ? 1 : 0, payload, payload_bytes, meta,
+      static_cast<hipStream_t>(stream)));
+}
+
+int gq_dequantize_accumulate_layers_alloc(
+    int64_t n, int32_t nl, const int64_t* layer_offsets, int32_t W,
+    const uint8_t* const* payloads, const float* const* meta,
+    const int32_t* const* widths, const int64_t* const* segments, float alpha,
+    float beta, float* out, void* stream) {
+  if (W > GQ_MAX_PAYLOADS) return GQ_ETOOMANY;
+  if (n < 1 || n > kMaxN || nl < 1 || W < 1 || !layer_offsets || !payloads ||
+      !meta || !widths || !segments || !out)
+    return GQ_EINVAL;
+  if (!aligned16(out) || reinterpret_cast<uintptr_t>(layer_offsets) % 8 ||
+      !std::isfinite(alpha) || !std::isfinite(beta))
+    return GQ_EINVAL;
+  const int64_t mb = 4 * (int64_t)nl, ob = 8 * ((int64_t)nl + 1);
+  if (overlap(out, 4 * n, layer_offsets, ob)) return GQ_EINVAL;
+  for (int w = 0; w < W; ++w) {
+    if (!payloads[w] || !meta[w] || !widths[w] || !segments[w] ||
+        !aligned16(payloads[w]) || !aligned16(meta[w]) ||
+        reinterpret_cast<uintptr_t>(widths[w]) % 4 ||
+        reinterpret_cast<uintptr_t>(segments[w]) % 8)
+      return GQ_EINVAL;
+    // a payload's size lives on the device (segments[nl]); its first
+    // 16 bytes, the tables and the scales must lie outside out
+    if (overlap(out, 4 * n, payloads[w], 16) || overlap(out, 4 * n, meta[w], mb) ||
+        overlap(out, 4 * n, widths[w], mb) || overlap(out, 4 * n, segments[w], ob))
+      return GQ_EINVAL;
+  }
+  return launch_status(gq::launch_alloc_deq(n, nl, layer_offsets, W, payloads,
+                                            meta, widths, segments, alpha,
+                                            beta, out,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 int gq_dequantize_accumulate_layers(const gq_desc* desc, int64_t n, int32_t nl,
                                     const int64_t* layer_offsets, int32_t W,
                                     const uint8_t* const* codes,

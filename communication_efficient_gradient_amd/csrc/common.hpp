@@ -72,6 +72,20 @@ __device__ __forceinline__ int uniform_code(float x, float up, float inv,
   return x < 0.f ? -mag : mag;
 }
 
+// Per-layer constants of the uniform rounding: scale-up factor, s / (M up)
+// and the step M / s.
+struct LayerScale {
+  float up, inv, delta;
+};
+
+__device__ __forceinline__ LayerScale layer_scale(float M, float sf) {
+  LayerScale c;
+  c.up = M < 0x1p-96f ? 0x1p96f : 1.0f;
+  c.inv = M > 0.f ? sf / (M * c.up) : 0.f;
+  c.delta = M / sf;
+  return c;
+}
+
 // ------------------------------------------------------- lane exchange --
 // Value of lane (lane ^ o) for o = 1, 2, 4, .., 32 and for the mirror masks
 // 3, 7, 15, 31, 63, without the LDS crossbar: DPP quad permutes for 1, 2
@@ -621,6 +635,18 @@ int launch_layer_quant(const LaunchDesc& L, int64_t n, int nl,
 int launch_layer_alloc(int nl, const int64_t* off, const float* scales,
                        int64_t budget, int32_t* widths, int64_t* seg,
                        hipStream_t st);
+// payload of a layer-wise bit allocation: max-abs pass, then the codes
+// of each layer at its own width in its own segment (and the residual);
+// dequantize-accumulate of W such payloads
+int launch_alloc_quant(int64_t n, int nl, const int64_t* off, const float* g,
+                       float* e, const int32_t* widths, const int64_t* seg,
+                       uint64_t seed, uint32_t step, int nearest,
+                       uint8_t* payload, int64_t payload_bytes, float* meta,
+                       hipStream_t st);
+int launch_alloc_deq(int64_t n, int nl, const int64_t* off, int W,
+                     const uint8_t* const* pay, const float* const* meta,
+                     const int32_t* const* widths, const int64_t* const* seg,
+                     float alpha, float beta, float* out, hipStream_t st);
 int launch_layer_deq(const LaunchDesc& L, int64_t n, int nl,
                      const int64_t* off, int W, const PayloadPtrs& pp,
                      float alpha, float beta, float* out, int64_t code_bytes,

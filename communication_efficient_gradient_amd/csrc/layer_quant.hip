@@ -150,20 +150,6 @@ __global__ __launch_bounds__(kLThreads) void k_layer_absmax(
   if (threadIdx.x == 0 && cur_l >= 0 && cur_m != 0u) atomicMax(&meta_bits[cur_l], cur_m);
 }
 
-// Per-layer constants of the uniform rounding: scale-up factor, s / (M up)
-// and the step M / s.
-struct LayerScale {
-  float up, inv, delta;
-};
-
-__device__ __forceinline__ LayerScale layer_scale(float M, float sf) {
-  LayerScale c;
-  c.up = M < 0x1p-96f ? 0x1p96f : 1.0f;
-  c.inv = M > 0.f ? sf / (M * c.up) : 0.f;
-  c.delta = M / sf;
-  return c;
-}
-
 template <int BITS>
 __global__ __launch_bounds__(kLThreads) void k_layer_quant(
     int64_t n, int nl, const int64_t* __restrict__ off,

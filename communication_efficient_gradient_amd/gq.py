@@ -28,7 +28,8 @@ GQ_MAX_PAYLOADS = 16
 SYMBOLS = ("gq_code_bits", "gq_payload_size", "gq_select_levels",
            "gq_quantize", "gq_error_feedback", "gq_dequantize_accumulate",
            "gq_quantize_layers", "gq_dequantize_accumulate_layers",
-           "gq_allocate_layer_bits",
+           "gq_allocate_layer_bits", "gq_alloc_payload_bytes",
+           "gq_quantize_layers_alloc", "gq_dequantize_accumulate_layers_alloc",
            "gq_elias_max_words", "gq_elias_encode", "gq_elias_decode",
            "gq_strerror", "gq_version")
 
@@ -74,6 +75,12 @@ def _load():
         D, i64, i32, P, i32, C.POINTER(P), C.POINTER(P), C.c_float, C.c_float,
         P, P]
     lib.gq_allocate_layer_bits.argtypes = [i64, i32, P, P, i64, P, P, P]
+    lib.gq_alloc_payload_bytes.argtypes = [i64, i32, C.POINTER(i64)]
+    lib.gq_quantize_layers_alloc.argtypes = [i64, i32, P, P, P, P, P, C.c_uint64,
+                                             C.c_uint32, i32, P, i64, P, P]
+    lib.gq_dequantize_accumulate_layers_alloc.argtypes = [
+        i64, i32, P, i32, C.POINTER(P), C.POINTER(P), C.POINTER(P),
+        C.POINTER(P), C.c_float, C.c_float, P, P]
     lib.gq_elias_max_words.argtypes = [D, i64, C.POINTER(i64)]
     lib.gq_elias_encode.argtypes = [D, i64, P, P, P, P]
     lib.gq_elias_decode.argtypes = [D, i64, P, P, i64, P, P]
@@ -387,3 +394,64 @@ def gq_allocate_layer_bits(n: int, layer_offsets: torch.Tensor,
         _ptr(scales, torch.float32, "scales"), budget_bits,
         _ptr(widths, torch.int32, "widths"), _ptr(segments, torch.int64, "segments"),
         _stream(stream, scales)), "gq_allocate_layer_bits")
+
+
+def gq_alloc_payload_bytes(n: int, nl: int) -> int:
+    """Bytes a payload of any layer-wise allocation of n elements in nl
+    layers needs (n + 16 nl)."""
+    b = C.c_int64(0)
+    _check(_lib.gq_alloc_payload_bytes(n, nl, C.byref(b)), "gq_alloc_payload_bytes")
+    return b.value
+
+
+def gq_quantize_layers_alloc(layer_offsets: torch.Tensor, g: torch.Tensor,
+                             e: torch.Tensor | None, widths: torch.Tensor,
+                             segments: torch.Tensor, seed: int, step: int,
+                             payload: torch.Tensor, meta: torch.Tensor,
+                             flags: int = 0, stream=None) -> None:
+    """Codes of each layer at its allocated width in its own segment (and
+    the residual); see include/gq.h."""
+    n = g.numel()
+    nl = layer_offsets.numel() - 1
+    if e is not None and e.numel() != n:
+        raise ValueError("e and g differ in size")
+    _need(widths, nl, "widths")
+    _need(segments, nl + 1, "segments")
+    _need(meta, nl, "meta")
+    _check(_lib.gq_quantize_layers_alloc(
+        n, nl, _offsets(layer_offsets), _ptr(g, torch.float32, "g"),
+        _ptr(e, torch.float32, "e"), _ptr(widths, torch.int32, "widths"),
+        _ptr(segments, torch.int64, "segments"), seed, step, flags,
+        _ptr(payload, torch.uint8, "payload"), payload.numel(),
+        _ptr(meta, torch.float32, "meta"), _stream(stream, g)),
+        "gq_quantize_layers_alloc")
+
+
+def gq_dequantize_accumulate_layers_alloc(n: int, layer_offsets: torch.Tensor,
+                                          payloads: Sequence[torch.Tensor],
+                                          meta: Sequence[torch.Tensor],
+                                          widths: Sequence[torch.Tensor],
+                                          segments: Sequence[torch.Tensor],
+                                          alpha: float, beta: float,
+                                          out: torch.Tensor, stream=None) -> None:
+    """out <- beta out + alpha sum of the payloads' x_hat; see include/gq.h."""
+    W = len(payloads)
+    if not (len(meta) == len(widths) == len(segments) == W):
+        raise ValueError("payloads, meta, widths and segments differ in length")
+    if out.numel() < n:
+        raise ValueError("out is smaller than n")
+    nl = layer_offsets.numel() - 1
+    for m, wd, sg in zip(meta, widths, segments):
+        _need(m, nl, "meta")
+        _need(wd, nl, "widths")
+        _need(sg, nl + 1, "segments")
+
+    def arr(ts, dt, what):
+        return (C.c_void_p * max(W, 1))(*[_ptr(t, dt, what) for t in ts])
+
+    _check(_lib.gq_dequantize_accumulate_layers_alloc(
+        n, nl, _offsets(layer_offsets), W, arr(payloads, torch.uint8, "payload"),
+        arr(meta, torch.float32, "meta"), arr(widths, torch.int32, "widths"),
+        arr(segments, torch.int64, "segments"), alpha, beta,
+        _ptr(out, torch.float32, "out"), _stream(stream, out)),
+        "gq_dequantize_accumulate_layers_alloc")

@@ -248,6 +248,51 @@ int gq_allocate_layer_bits(int64_t n, int32_t nl, const int64_t* layer_offsets,
                            const float* scales, int64_t budget_bits,
                            int32_t* widths, int64_t* segments, void* stream);
 
+/* Capacity a payload of any allocation needs: n + 16 nl bytes (every code at
+ * 8 bits plus every segment's padding).  GQ_EINVAL for n or nl out of range
+ * or a null bytes. */
+int gq_alloc_payload_bytes(int64_t n, int32_t nl, int64_t* bytes);
+
+/* Quantize with a layer-wise bit allocation (same glossary paragraph): the
+ * per-layer scale path of gq_quantize_layers with layer l coded at
+ * widths[l] bits, s = 2^(b-1) - 1, the uniform scheme.  Inputs as in
+ * gq_quantize_layers (g, e, layer_offsets, seed, step; flags: 0 or
+ * GQ_FLAG_NEAREST) plus widths[nl] int32 and segments[nl + 1] int64 (DEVICE,
+ * as gq_allocate_layer_bits writes them: widths in {2, 3, 4, 8}, segments
+ * the 16-byte-padded byte offsets).  Outputs (DEVICE): meta[nl] fp32 = each
+ * layer's max-abs of p = g (+ e); payload bytes [segments[l],
+ * segments[l+1]) = layer l's n_l codes as an LSB-first bit stream (code k at
+ * bits [k b, k b + b), two's complement), zero past the last code; e <- p -
+ * x_hat when e is given.  A layer's codes are exactly those gq_quantize_layers
+ * gives with s = 2^(b-1) - 1 (same scale, Philox word per flat index and
+ * rounding).  payload_bytes >= gq_alloc_payload_bytes(n, nl) (GQ_EINVAL
+ * otherwise); bytes past segments[nl] are not written.  Alignment: g, e,
+ * payload, meta 16 bytes; layer_offsets and segments 8; widths 4.  No buffer
+ * written may overlap another buffer of the call.  Device tables are not
+ * read on the host: a width outside {2, 3, 4, 8} writes zero codes for that
+ * layer, and other contents give unspecified outputs but only in-bounds
+ * stores.  Two launches on the stream (max-abs, codes). */
+int gq_quantize_layers_alloc(int64_t n, int32_t nl, const int64_t* layer_offsets,
+                             const float* g, float* e, const int32_t* widths,
+                             const int64_t* segments, uint64_t seed,
+                             uint32_t step, int32_t flags, uint8_t* payload,
+                             int64_t payload_bytes, float* meta, void* stream);
+
+/* out <- beta * out + alpha * sum_w x_hat_w over W <= GQ_MAX_PAYLOADS
+ * payloads of gq_quantize_layers_alloc (one layer layout; each payload has
+ * its own meta[w], widths[w] and segments[w], DEVICE, alignments as
+ * above).  Summation order as in gq_dequantize_accumulate.  GQ_ETOOMANY for
+ * W > GQ_MAX_PAYLOADS; GQ_EINVAL for null or misaligned pointers, a
+ * non-finite alpha or beta, or out overlapping layer_offsets, a table, a
+ * scale array or the start of a payload.  The payloads are read within
+ * [0, segments[w][nl]) when widths and segments are those the allocation
+ * wrote; other contents are the caller's error. */
+int gq_dequantize_accumulate_layers_alloc(
+    int64_t n, int32_t nl, const int64_t* layer_offsets, int32_t W,
+    const uint8_t* const* payloads, const float* const* meta,
+    const int32_t* const* widths, const int64_t* const* segments, float alpha,
+    float beta, float* out, void* stream);
+
 /* Elias gamma coding of GQ_UNIFORM codes, the lossless integer coding QSGD
  * applies after quantizing ("Gradient Quantization" glossary, QSGD
  * paragraph).  Code c (in element order) is written as the Elias gamma code
