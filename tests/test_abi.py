@@ -181,6 +181,55 @@ def test_layer_entry_points_validate_before_launch(gq):
               mp, 1.0, 0.0, fake * 4, None) == gq.GQ_EUNSUPPORTED
 
 
+def test_alloc_payload_entry_points_validate_before_launch(gq):
+    """Layer-wise allocation payload: capacity, flags, alignment and overlap
+    errors are found on the host (widths, segments and offsets are device
+    memory and are not read there)."""
+    L = gq.lib()
+    P = C.c_void_p
+    fake = 1 << 20
+    assert gq.gq_alloc_payload_bytes(100, 2) == 132
+    out = C.c_int64(0)
+    assert L.gq_alloc_payload_bytes(0, 2, C.byref(out)) == gq.GQ_EINVAL
+    assert L.gq_alloc_payload_bytes(100, 0, C.byref(out)) == gq.GQ_EINVAL
+    q = L.gq_quantize_layers_alloc
+
+    def call(**kw):
+        a = dict(n=100, nl=2, off=fake, g=fake * 2, e=None, wd=fake * 5,
+                 sg=fake * 6, flags=0, pay=fake * 3, pb=132, meta=fake * 4)
+        a.update(kw)
+        return q(a["n"], a["nl"], a["off"], a["g"], a["e"], a["wd"], a["sg"], 0, 0,
+                 a["flags"], a["pay"], a["pb"], a["meta"], None)
+
+    assert call(pb=131) == gq.GQ_EINVAL                  # below the capacity
+    assert call(flags=gq.GQ_FLAG_CLIP) == gq.GQ_EINVAL
+    assert call(flags=gq.GQ_FLAG_DENSE) == gq.GQ_EINVAL
+    assert call(nl=0) == gq.GQ_EINVAL
+    assert call(wd=None) == gq.GQ_EINVAL
+    assert call(wd=fake * 5 + 2) == gq.GQ_EINVAL         # misaligned widths
+    assert call(sg=fake * 6 + 4) == gq.GQ_EINVAL         # misaligned segments
+    assert call(pay=fake * 3 + 8) == gq.GQ_EINVAL        # misaligned payload
+    assert call(pay=fake * 2) == gq.GQ_EINVAL            # payload over g
+    assert call(meta=fake * 3 + 128) == gq.GQ_EINVAL     # meta inside the payload
+    assert call(e=fake * 6) == gq.GQ_EINVAL              # e over the segments
+    dq = L.gq_dequantize_accumulate_layers_alloc
+    pp = (P * 17)(*([fake * 2] * 17))
+    mp = (P * 17)(*([fake * 3] * 17))
+    wp = (P * 17)(*([fake * 5] * 17))
+    sp = (P * 17)(*([fake * 6] * 17))
+    assert dq(100, 2, fake, 17, pp, mp, wp, sp, 1.0, 0.0, fake * 4,
+              None) == gq.GQ_ETOOMANY
+    assert dq(100, 2, fake, 0, pp, mp, wp, sp, 1.0, 0.0, fake * 4,
+              None) == gq.GQ_EINVAL
+    assert dq(100, 2, fake, 1, pp, mp, wp, sp, float("inf"), 0.0, fake * 4,
+              None) == gq.GQ_EINVAL
+    assert dq(100, 2, fake, 1, pp, mp, wp, sp, 1.0, 0.0, fake * 5 - 64,
+              None) == gq.GQ_EINVAL                      # out over a widths table
+    bad = (P * 1)(fake * 6 + 4)
+    assert dq(100, 2, fake, 1, pp, mp, wp, bad, 1.0, 0.0, fake * 4,
+              None) == gq.GQ_EINVAL                      # misaligned segments
+
+
 def test_bisect_flag_rules(gq):
     """Recursive bisection: ORQ with d <= 512 only; the layout is unchanged."""
     Bf = gq.GQ_FLAG_BISECT
