@@ -424,6 +424,31 @@ def suite_layers(torch, gq, WL, stream, tb):
     out.append(entry(f"allocate layer bits ({nl} layers, 3 bits per element)", ms,
                      8 * (nl + 1) + 4 * nl + 4 * nl + 8 * (nl + 1), nl,
                      bound="latency"))
+    # the payload of that allocation: each layer at its own width (two
+    # passes as above: 8 + 12 bytes per element, plus the mixed-width codes)
+    gq.gq_allocate_layer_bits(n, off, M[0], 3 * n, Wd, Sg, stream)
+    torch.cuda.synchronize()
+    widths_h = Wd.cpu().numpy().tolist()
+    pb = int(Sg[-1].item())
+    cap_a = gq.gq_alloc_payload_bytes(n, nl)
+    PA = [torch.empty(cap_a, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    ms = tb(lambda i: gq.gq_quantize_layers_alloc(off, G[i % 2], E[i % 2], Wd, Sg, 2,
+                                                  i, PA[i % 2], M[i % 2],
+                                                  stream=stream))
+
+    def oracle_alloc(k):
+        o = [int(x) for x in off_h if x < k] + [k]
+        O.quantize_layers_alloc(o, host[:k], np.zeros(k, np.float32),
+                                widths_h[:len(o) - 1], seed=2)
+    wset = "/".join(str(b) for b in sorted(set(widths_h)))
+    out.append(entry(f"quantize layer-wise widths {wset} ({nl} layers, "
+                     f"{8 * pb / n:.2f} bits per element) +ef n={n}",
+                     ms, 20 * n + pb + 4 * nl + 12 * nl, n,
+                     extra={"_oracle": lambda: time_oracle(oracle_alloc, n, 512)}))
+    ms = tb(lambda i: gq.gq_dequantize_accumulate_layers_alloc(
+        n, off, [PA[i % 2]], [M[i % 2]], [Wd], [Sg], 1.0, 0.0, O_[i % 2], stream))
+    out.append(entry(f"dequantize layer-wise widths W=1 n={n}", ms,
+                     pb + 16 * nl + 4 * n, n))
     return out
 
 

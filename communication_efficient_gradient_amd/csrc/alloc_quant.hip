@@ -36,8 +36,8 @@ __device__ __forceinline__ bool alloc_width_ok(int b) {
 // index l of the layer holding position x: off[l] <= x < off[l+1]
 // (0 <= x < off[nl]; empty layers are never returned)
 __device__ __forceinline__ int layer_of(const int64_t* __restrict__ off, int nl,
-                                        int64_t x) {
-  int lo = 0, hi = nl;  // off[lo] <= x < off[hi]
+                                        int64_t x, int lo = 0) {
+  int hi = nl;  // off[lo] <= x < off[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (off[mid] <= x) lo = mid;
@@ -46,68 +46,139 @@ __device__ __forceinline__ int layer_of(const int64_t* __restrict__ off, int nl,
   return lo;
 }
 
+constexpr int kWaveElems = 1024;  // elements one wave codes at most (2 bits)
+
+// The codes of one lane at width B: CNT = 32 nw / B consecutive codes of
+// its layer, elements [i0, i0 + nreal) of the flat gradient, whose p the
+// wave has staged in LDS (sp = that row, from element e_lo; -1 entries:
+// outside the staged run, code 0).  Residuals go back to the same slots.
+template <int B>
+__device__ __forceinline__ void alloc_quant_group(
+    float* sp, int64_t e_lo, int64_t i0, int nreal, uint32_t k0, uint32_t k1,
+    uint32_t step, int nearest, const LayerScale& c,
+    uint32_t* __restrict__ payload, int64_t w, int64_t sw1, int64_t cap_words,
+    bool ef) {
+  constexpr int NW = B == 3 ? 3 : 1;
+  constexpr int CNT = 32 * NW / B;
+  constexpr int NF = CNT / 4 + 1;  // Philox counters the run can touch
+  constexpr int S = (1 << (B - 1)) - 1;
+  constexpr uint32_t MASK = (1u << B) - 1u;
+  const float sf = (float)S;
+  const int64_t r0 = i0 - e_lo;  // first slot in the staged row
+  const int64_t f0 = i0 >> 2;
+  uint32_t rw[4 * NF];
+#pragma unroll
+  for (int q = 0; q < NF; ++q) {
+    const int64_t f = f0 + q;
+    const uint4 r = nearest ? make_uint4(kHalfWord, kHalfWord, kHalfWord, kHalfWord)
+                            : philox4x32_10(k0, k1, (uint32_t)f, (uint32_t)(f >> 32), step, 0u);
+    rw[4 * q] = r.x;
+    rw[4 * q + 1] = r.y;
+    rw[4 * q + 2] = r.z;
+    rw[4 * q + 3] = r.w;
+  }
+  const int a = (int)(i0 & 3);  // word of element i0 within its counter
+  uint32_t wd[NW];
+#pragma unroll
+  for (int m = 0; m < NW; ++m) wd[m] = 0u;
+#pragma unroll
+  for (int j = 0; j < CNT; ++j) {
+    const int64_t slot = r0 + j;
+    const bool live = j < nreal && slot >= 0 && slot < kWaveElems;
+    const float p = live ? sp[slot] : 0.f;
+    // rw[a + j] without a dynamically indexed array: a is 0..3
+    const uint32_t u = a == 0 ? rw[j] : a == 1 ? rw[j + 1] : a == 2 ? rw[j + 2] : rw[j + 3];
+    const int ci = live ? uniform_code<true>(p, c.up, c.inv, sf, u) : 0;
+    const uint32_t fld = (uint32_t)ci & MASK;
+    const int pos = j * B;
+    wd[pos >> 5] |= fld << (pos & 31);
+    if ((pos & 31) + B > 32) wd[(pos >> 5) + 1] |= fld >> (32 - (pos & 31));
+    if (ef && live) sp[slot] = p - (float)ci * c.delta;
+  }
+  payload[w] = wd[0];
+#pragma unroll
+  for (int m = 1; m < NW; ++m)  // the group may run past the segment's end
+    if (w + m < sw1 && w + m < cap_words) payload[w + m] = wd[m];
+}
+
 __global__ __launch_bounds__(kAThreads) void k_alloc_quant(
     int64_t n, int nl, const int64_t* __restrict__ off, const float* __restrict__ g,
     float* __restrict__ e, const int32_t* __restrict__ widths,
     const int64_t* __restrict__ seg, uint32_t k0, uint32_t k1, uint32_t step,
     int nearest, uint32_t* __restrict__ payload, int64_t cap_words,
     const float* __restrict__ meta) {
+  __shared__ float stage[kAThreads / 64][kWaveElems];
+  const int lane = threadIdx.x & 63;
+  float* sp = stage[threadIdx.x >> 6];
   const int64_t w = (int64_t)blockIdx.x * kAThreads + threadIdx.x;
-  if (w >= cap_words) return;
   const int64_t total = seg[nl];
-  if (4 * w >= total) return;
-  const int l = layer_of(seg, nl, 4 * w);
-  const int b = widths[l];
-  if (!alloc_width_ok(b)) {
-    payload[w] = 0u;
-    return;
-  }
-  // 3-bit codes straddle words: one thread takes three words (32 codes),
-  // so every code, and its residual, belongs to one thread
-  const int nw = b == 3 ? 3 : 1;
-  const int64_t sw0 = seg[l] >> 2, sw1 = seg[l + 1] >> 2;
-  if ((w - sw0) % nw != 0) return;
-  const int64_t lo = off[l];
-  const int64_t nlay = off[l + 1] - lo;
-  const int64_t kfirst = 32 * (w - sw0) / b;  // first code of the group
-  int64_t kend = kfirst + 32 * nw / b;
-  if (kend > nlay) kend = nlay;
-  if (lo < 0) kend = kfirst;           // offsets outside [0, n] read nothing
-  else if (kend > n - lo) kend = n - lo;
-  const int s = (1 << (b - 1)) - 1;
-  const float sf = (float)s;
-  const uint32_t mask = (1u << b) - 1u;
-  const LayerScale c = layer_scale(meta[l], sf);
-  uint64_t acc0 = 0u, acc1 = 0u;  // bits 0..63 and 64..127 of the group
-  int64_t cur = -1;
-  uint4 r = make_uint4(0u, 0u, 0u, 0u);
-  for (int64_t k = kfirst; k < kend; ++k) {
-    const int64_t i = lo + k;
-    const int64_t f = i >> 2;
-    if (!nearest && f != cur) {
-      r = philox4x32_10(k0, k1, (uint32_t)f, (uint32_t)(f >> 32), step, 0u);
-      cur = f;
-    }
-    const int q = (int)(i & 3);
-    const uint32_t u = nearest ? kHalfWord : (q == 0 ? r.x : q == 1 ? r.y : q == 2 ? r.z : r.w);
-    const float gi = g[i];
-    const float p = e != nullptr ? gi + e[i] : gi;
-    const int ci = uniform_code<true>(p, c.up, c.inv, sf, u);
-    const uint64_t fld = (uint64_t)((uint32_t)ci & mask);
-    const int pos = (int)((k - kfirst) * b);  // 0 .. 32 nw - b
-    if (pos < 64) {
-      acc0 |= fld << pos;
-      if (pos + b > 64) acc1 |= fld >> (64 - pos);
+  // this lane's layer, width and run of elements (empty for lanes past the
+  // payload, the second and third words of a 3-bit group, padding words)
+  const bool word = w < cap_words && 4 * w < total;
+  int l = 0, b = 0;
+  int64_t sw1 = 0, i0 = 0, i1 = 0;
+  bool lead = false;
+  if (word) {
+    l = layer_of(seg, nl, 4 * w);
+    b = widths[l];
+    const int64_t sw0 = seg[l] >> 2;
+    sw1 = seg[l + 1] >> 2;
+    if (!alloc_width_ok(b)) {
+      payload[w] = 0u;
     } else {
-      acc1 |= fld << (pos - 64);
+      // 3-bit codes straddle words: one lane takes three words (32 codes),
+      // so every code, and its residual, belongs to one lane
+      const int nw = b == 3 ? 3 : 1;
+      lead = (w - sw0) % nw == 0;
+      if (lead) {
+        const int64_t lo = off[l];
+        const int64_t nlay = off[l + 1] - lo;
+        const int64_t kfirst = 32 * (w - sw0) / b;
+        int64_t kend = kfirst + 32 * nw / b;
+        if (kend > nlay) kend = nlay;
+        if (lo < 0) kend = kfirst;  // offsets outside [0, n] read nothing
+        else if (kend > n - lo) kend = n - lo;
+        if (kend < kfirst) kend = kfirst;
+        i0 = lo + kfirst;
+        i1 = lo + kend;
+      }
     }
-    if (e != nullptr) e[i] = p - (float)ci * c.delta;
   }
-  payload[w] = (uint32_t)acc0;
-  if (nw == 3) {
-    // the group may run past the segment's padded end (or the capacity)
-    if (w + 1 < sw1 && w + 1 < cap_words) payload[w + 1] = (uint32_t)(acc0 >> 32);
-    if (w + 2 < sw1 && w + 2 < cap_words) payload[w + 2] = (uint32_t)acc1;
+  // the wave's runs are consecutive (layers follow each other in both the
+  // gradient and the payload): stage [first run's start, last run's end)
+  const uint64_t busy = __ballot(lead && i1 > i0);
+  int64_t e_lo = 0, e_hi = 0;
+  if (busy != 0) {
+    const int first = __ffsll((long long)busy) - 1;
+    const int last = 63 - __clzll((long long)busy);
+    e_lo = __shfl(i0, first, 64);
+    e_hi = __shfl(i1, last, 64);
+    if (e_hi > e_lo + kWaveElems) e_hi = e_lo + kWaveElems;
+  }
+#pragma unroll
+  for (int t = 0; t < kWaveElems / 64; ++t) {
+    const int64_t i = e_lo + 64 * t + lane;
+    if (i < e_hi) sp[64 * t + lane] = e != nullptr ? g[i] + e[i] : g[i];
+  }
+  __syncthreads();
+  if (lead) {
+    const int nreal = (int)(i1 - i0);
+    const LayerScale c = layer_scale(meta[l], (float)((1 << (b - 1)) - 1));
+    const bool ef = e != nullptr;
+    switch (b) {
+      case 2: alloc_quant_group<2>(sp, e_lo, i0, nreal, k0, k1, step, nearest, c, payload, w, sw1, cap_words, ef); break;
+      case 3: alloc_quant_group<3>(sp, e_lo, i0, nreal, k0, k1, step, nearest, c, payload, w, sw1, cap_words, ef); break;
+      case 4: alloc_quant_group<4>(sp, e_lo, i0, nreal, k0, k1, step, nearest, c, payload, w, sw1, cap_words, ef); break;
+      default: alloc_quant_group<8>(sp, e_lo, i0, nreal, k0, k1, step, nearest, c, payload, w, sw1, cap_words, ef); break;
+    }
+  }
+  __syncthreads();
+  if (e != nullptr) {
+#pragma unroll
+    for (int t = 0; t < kWaveElems / 64; ++t) {
+      const int64_t i = e_lo + 64 * t + lane;
+      if (i < e_hi) e[i] = sp[64 * t + lane];
+    }
   }
 }
 
@@ -135,12 +206,18 @@ __device__ __forceinline__ float alloc_value(const AllocPtrs& P, int p, int l,
 __global__ __launch_bounds__(kAThreads) void k_alloc_deq(
     int64_t n, int nl, const int64_t* __restrict__ off, int W, AllocPtrs P,
     float alpha, float beta, float* __restrict__ out) {
+  // the layer of the block's first element, searched once; a thread's own
+  // search starts there and is skipped when its four elements lie in it
+  __shared__ int l_blk;
   const int64_t f = (int64_t)blockIdx.x * kAThreads + threadIdx.x;
   const int64_t i0 = 4 * f;
+  if (threadIdx.x == 0) l_blk = layer_of(off, nl, 4 * (int64_t)blockIdx.x * kAThreads);
+  __syncthreads();
   if (i0 >= n) return;
   const int nreal = i0 + 4 <= n ? 4 : (int)(n - i0);
   int li[4];
-  int l = layer_of(off, nl, i0);
+  int l = l_blk;
+  if (off[l + 1] <= i0) l = layer_of(off, nl, i0, l);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     if (k < nreal)
@@ -148,15 +225,40 @@ __global__ __launch_bounds__(kAThreads) void k_alloc_deq(
     li[k] = l;
   }
   float a0[4] = {0.f, 0.f, 0.f, 0.f}, a1[4] = {0.f, 0.f, 0.f, 0.f};
+  const bool one = li[0] == li[nreal - 1];
+  const int64_t kl = i0 - off[li[0]];  // layer-relative index of element i0
   for (int p = 0; p < W; ++p) {
+    float x[4];
+    if (one) {
+      // the four codes lie in one layer: one table lookup and a 64-bit
+      // window of at most two payload words
+      const int l = li[0];
+      const int b = P.widths[p][l];
+      const bool ok = alloc_width_ok(b);
+      const int bb = ok ? b : 2;
+      const int64_t bit = 8 * P.seg[p][l] + kl * bb;
+      const uint32_t* wp = P.pay[p] + (bit >> 5);
+      const int sh = (int)(bit & 31);
+      uint64_t v = ok ? wp[0] : 0u;
+      if (ok && sh + nreal * bb > 32) v |= (uint64_t)wp[1] << 32;
+      const float delta = P.meta[p][l] / (float)((1 << (bb - 1)) - 1);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t fld = (uint32_t)(v >> (sh + k * bb));
+        const int code = (int)(fld << (32 - bb)) >> (32 - bb);
+        x[k] = ok ? (float)code * delta : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        x[k] = k < nreal ? alloc_value(P, p, li[k], i0 + k - off[li[k]]) : 0.f;
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      if (k >= nreal) continue;
-      const float x = alloc_value(P, p, li[k], i0 + k - off[li[k]]);
-      if (p == 0) a0[k] = x;
-      else if (p == 1) a1[k] = x;
-      else if (p & 1) a1[k] = a1[k] + x;
-      else a0[k] = a0[k] + x;
+      if (p == 0) a0[k] = x[k];
+      else if (p == 1) a1[k] = x[k];
+      else if (p & 1) a1[k] = a1[k] + x[k];
+      else a0[k] = a0[k] + x[k];
     }
   }
   float r[4];
