@@ -46,13 +46,35 @@ __device__ __forceinline__ int layer_of(const int64_t* __restrict__ off, int nl,
   return lo;
 }
 
+// The same search by a whole wave (every lane passes the same x): each
+// round one load per lane at 64 evenly spaced candidates, so 160 layers take
+// two rounds of one memory latency each instead of eight.
+__device__ __forceinline__ int wave_layer_of(const int64_t* __restrict__ off,
+                                             int nl, int64_t x) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = nl;  // off[lo] <= x < off[hi]
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int idx = lo + lane * step;
+    const bool le = idx < hi && off[idx] <= x;  // true for a prefix of lanes
+    const int cnt = __popcll(__ballot(le));     // >= 1: lane 0 reads off[lo]
+    lo += (cnt - 1) * step;
+    hi = lo + step < hi ? lo + step : hi;
+  }
+  return lo;
+}
+
+// LDS slot of staged element s: one pad word every 16 keeps the lanes of a
+// strided read (16 consecutive elements per lane at 2 bits) on distinct banks
+__device__ __forceinline__ int stage_slot(int s) { return s + (s >> 4); }
+
 constexpr int kWaveElems = 1024;  // elements one wave codes at most (2 bits)
 
 // The codes of one lane at width B: CNT = 32 nw / B consecutive codes of
 // its layer, elements [i0, i0 + nreal) of the flat gradient, whose p the
 // wave has staged in LDS (sp = that row, from element e_lo; -1 entries:
 // outside the staged run, code 0).  Residuals go back to the same slots.
-template <int B>
+template <int B, int A>
 __device__ __forceinline__ void alloc_quant_group(
     float* sp, int64_t e_lo, int64_t i0, int nreal, uint32_t k0, uint32_t k1,
     uint32_t step, int nearest, const LayerScale& c,
@@ -77,7 +99,8 @@ __device__ __forceinline__ void alloc_quant_group(
     rw[4 * q + 2] = r.z;
     rw[4 * q + 3] = r.w;
   }
-  const int a = (int)(i0 & 3);  // word of element i0 within its counter
+  // A = i0 mod 4, the word of element i0 within its counter (a template
+  // argument, so that rw is indexed statically and stays in registers)
   uint32_t wd[NW];
 #pragma unroll
   for (int m = 0; m < NW; ++m) wd[m] = 0u;
@@ -85,15 +108,14 @@ __device__ __forceinline__ void alloc_quant_group(
   for (int j = 0; j < CNT; ++j) {
     const int64_t slot = r0 + j;
     const bool live = j < nreal && slot >= 0 && slot < kWaveElems;
-    const float p = live ? sp[slot] : 0.f;
-    // rw[a + j] without a dynamically indexed array: a is 0..3
-    const uint32_t u = a == 0 ? rw[j] : a == 1 ? rw[j + 1] : a == 2 ? rw[j + 2] : rw[j + 3];
+    const float p = live ? sp[stage_slot((int)slot)] : 0.f;
+    const uint32_t u = rw[A + j];
     const int ci = live ? uniform_code<true>(p, c.up, c.inv, sf, u) : 0;
     const uint32_t fld = (uint32_t)ci & MASK;
     const int pos = j * B;
     wd[pos >> 5] |= fld << (pos & 31);
     if ((pos & 31) + B > 32) wd[(pos >> 5) + 1] |= fld >> (32 - (pos & 31));
-    if (ef && live) sp[slot] = p - (float)ci * c.delta;
+    if (ef && live) sp[stage_slot((int)slot)] = p - (float)ci * c.delta;
   }
   payload[w] = wd[0];
 #pragma unroll
@@ -107,7 +129,7 @@ __global__ __launch_bounds__(kAThreads) void k_alloc_quant(
     const int64_t* __restrict__ seg, uint32_t k0, uint32_t k1, uint32_t step,
     int nearest, uint32_t* __restrict__ payload, int64_t cap_words,
     const float* __restrict__ meta) {
-  __shared__ float stage[kAThreads / 64][kWaveElems];
+  __shared__ float stage[kAThreads / 64][kWaveElems + kWaveElems / 16];
   const int lane = threadIdx.x & 63;
   float* sp = stage[threadIdx.x >> 6];
   const int64_t w = (int64_t)blockIdx.x * kAThreads + threadIdx.x;
@@ -115,11 +137,16 @@ __global__ __launch_bounds__(kAThreads) void k_alloc_quant(
   // this lane's layer, width and run of elements (empty for lanes past the
   // payload, the second and third words of a 3-bit group, padding words)
   const bool word = w < cap_words && 4 * w < total;
+  // the layer of the wave's first word, searched by the whole wave; a lane
+  // past that layer searches on from there
+  const int64_t wfirst = w - (threadIdx.x & 63);
+  const int lw = 4 * wfirst < total ? wave_layer_of(seg, nl, 4 * wfirst) : 0;
   int l = 0, b = 0;
   int64_t sw1 = 0, i0 = 0, i1 = 0;
   bool lead = false;
   if (word) {
-    l = layer_of(seg, nl, 4 * w);
+    l = lw;
+    if (seg[l + 1] <= 4 * w) l = layer_of(seg, nl, 4 * w, l + 1);
     b = widths[l];
     const int64_t sw0 = seg[l] >> 2;
     sw1 = seg[l + 1] >> 2;
@@ -158,26 +185,38 @@ __global__ __launch_bounds__(kAThreads) void k_alloc_quant(
 #pragma unroll
   for (int t = 0; t < kWaveElems / 64; ++t) {
     const int64_t i = e_lo + 64 * t + lane;
-    if (i < e_hi) sp[64 * t + lane] = e != nullptr ? g[i] + e[i] : g[i];
+    if (i < e_hi) sp[stage_slot(64 * t + lane)] = e != nullptr ? g[i] + e[i] : g[i];
   }
   __syncthreads();
   if (lead) {
     const int nreal = (int)(i1 - i0);
     const LayerScale c = layer_scale(meta[l], (float)((1 << (b - 1)) - 1));
     const bool ef = e != nullptr;
+#define GQ_AQ(B, A)                                                          \
+  alloc_quant_group<B, A>(sp, e_lo, i0, nreal, k0, k1, step, nearest, c,     \
+                          payload, w, sw1, cap_words, ef)
+#define GQ_AQ4(B)                     \
+  switch ((int)(i0 & 3)) {            \
+    case 0: GQ_AQ(B, 0); break;       \
+    case 1: GQ_AQ(B, 1); break;       \
+    case 2: GQ_AQ(B, 2); break;       \
+    default: GQ_AQ(B, 3); break;      \
+  }
     switch (b) {
-      case 2: alloc_quant_group<2>(sp, e_lo, i0, nreal, k0, k1, step, nearest, c, payload, w, sw1, cap_words, ef); break;
-      case 3: alloc_quant_group<3>(sp, e_lo, i0, nreal, k0, k1, step, nearest, c, payload, w, sw1, cap_words, ef); break;
-      case 4: alloc_quant_group<4>(sp, e_lo, i0, nreal, k0, k1, step, nearest, c, payload, w, sw1, cap_words, ef); break;
-      default: alloc_quant_group<8>(sp, e_lo, i0, nreal, k0, k1, step, nearest, c, payload, w, sw1, cap_words, ef); break;
+      case 2: GQ_AQ4(2); break;
+      case 3: GQ_AQ4(3); break;
+      case 4: GQ_AQ4(4); break;
+      default: GQ_AQ4(8); break;
     }
+#undef GQ_AQ4
+#undef GQ_AQ
   }
   __syncthreads();
   if (e != nullptr) {
 #pragma unroll
     for (int t = 0; t < kWaveElems / 64; ++t) {
       const int64_t i = e_lo + 64 * t + lane;
-      if (i < e_hi) e[i] = sp[64 * t + lane];
+      if (i < e_hi) e[i] = sp[stage_slot(64 * t + lane)];
     }
   }
 }
@@ -203,21 +242,16 @@ __device__ __forceinline__ float alloc_value(const AllocPtrs& P, int p, int l,
   return (float)code * (P.meta[p][l] / (float)s);
 }
 
-__global__ __launch_bounds__(kAThreads) void k_alloc_deq(
-    int64_t n, int nl, const int64_t* __restrict__ off, int W, AllocPtrs P,
-    float alpha, float beta, float* __restrict__ out) {
-  // the layer of the block's first element, searched once; a thread's own
-  // search starts there and is skipped when its four elements lie in it
-  __shared__ int l_blk;
-  const int64_t f = (int64_t)blockIdx.x * kAThreads + threadIdx.x;
-  const int64_t i0 = 4 * f;
-  if (threadIdx.x == 0) l_blk = layer_of(off, nl, 4 * (int64_t)blockIdx.x * kAThreads);
-  __syncthreads();
-  if (i0 >= n) return;
+constexpr int kDeqV = 4;  // float4 groups per thread
+
+// One float4 group of the output, elements [i0, i0 + 4) (those at or past n
+// absent); l: a layer at or before that of i0 (off[l] <= i0).
+__device__ __forceinline__ void alloc_deq_group(
+    int64_t n, int nl, const int64_t* __restrict__ off, int W, const AllocPtrs& P,
+    float alpha, float beta, float* __restrict__ out, int64_t i0, int l) {
   const int nreal = i0 + 4 <= n ? 4 : (int)(n - i0);
   int li[4];
-  int l = l_blk;
-  if (off[l + 1] <= i0) l = layer_of(off, nl, i0, l);
+  if (off[l + 1] <= i0) l = layer_of(off, nl, i0, l + 1);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     if (k < nreal)
@@ -232,16 +266,16 @@ __global__ __launch_bounds__(kAThreads) void k_alloc_deq(
     if (one) {
       // the four codes lie in one layer: one table lookup and a 64-bit
       // window of at most two payload words
-      const int l = li[0];
-      const int b = P.widths[p][l];
+      const int lq = li[0];
+      const int b = P.widths[p][lq];
       const bool ok = alloc_width_ok(b);
       const int bb = ok ? b : 2;
-      const int64_t bit = 8 * P.seg[p][l] + kl * bb;
+      const int64_t bit = 8 * P.seg[p][lq] + kl * bb;
       const uint32_t* wp = P.pay[p] + (bit >> 5);
       const int sh = (int)(bit & 31);
       uint64_t v = ok ? wp[0] : 0u;
       if (ok && sh + nreal * bb > 32) v |= (uint64_t)wp[1] << 32;
-      const float delta = P.meta[p][l] / (float)((1 << (bb - 1)) - 1);
+      const float delta = P.meta[p][lq] / (float)((1 << (bb - 1)) - 1);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t fld = (uint32_t)(v >> (sh + k * bb));
@@ -286,6 +320,22 @@ __global__ __launch_bounds__(kAThreads) void k_alloc_deq(
   }
 }
 
+__global__ __launch_bounds__(kAThreads) void k_alloc_deq(
+    int64_t n, int nl, const int64_t* __restrict__ off, int W, AllocPtrs P,
+    float alpha, float beta, float* __restrict__ out) {
+  // thread t of a block owns groups t, t + 256, t + 512, t + 768 of the
+  // block's 1024; the layer of the wave's first element is searched by the
+  // whole wave and each group's search starts there (and is skipped when
+  // its four elements lie in that layer)
+  const int64_t f0 = (int64_t)blockIdx.x * kAThreads * kDeqV + threadIdx.x;
+  const int l0 = wave_layer_of(off, nl, 4 * (f0 - (threadIdx.x & 63)));
+#pragma unroll
+  for (int v = 0; v < kDeqV; ++v) {
+    const int64_t i0 = 4 * (f0 + (int64_t)kAThreads * v);
+    if (i0 < n) alloc_deq_group(n, nl, off, W, P, alpha, beta, out, i0, l0);
+  }
+}
+
 }  // namespace
 
 int launch_alloc_quant(int64_t n, int nl, const int64_t* off, const float* g,
@@ -319,7 +369,7 @@ int launch_alloc_deq(int64_t n, int nl, const int64_t* off, int W,
     P.seg[p] = seg[p];
   }
   const int64_t groups = (n + 3) / 4;
-  const int64_t blocks = (groups + kAThreads - 1) / kAThreads;
+  const int64_t blocks = (groups + kAThreads * kDeqV - 1) / (kAThreads * kDeqV);
   hipLaunchKernelGGL(k_alloc_deq, dim3((uint32_t)blocks), dim3(kAThreads), 0,
                      st, n, nl, off, W, P, alpha, beta, out);
   return (int)hipGetLastError();
