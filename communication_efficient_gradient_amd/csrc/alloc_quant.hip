@@ -329,6 +329,60 @@ __global__ __launch_bounds__(kAThreads) void k_alloc_deq(
   // its four elements lie in that layer)
   const int64_t f0 = (int64_t)blockIdx.x * kAThreads * kDeqV + threadIdx.x;
   const int l0 = wave_layer_of(off, nl, 4 * (f0 - (threadIdx.x & 63)));
+  const int64_t ilast = 4 * (f0 + (int64_t)kAThreads * (kDeqV - 1)) + 3;
+  if (ilast < n && ilast < off[l0 + 1]) {
+    // all sixteen elements in layer l0: per payload one table lookup, and
+    // the four groups' payload windows loaded together
+    const int64_t base = 4 * f0 - off[l0];  // layer-relative index, group 0
+    float a0[kDeqV][4], a1[kDeqV][4];
+    for (int p = 0; p < W; ++p) {
+      const int b = P.widths[p][l0];
+      const bool ok = alloc_width_ok(b);
+      const int bb = ok ? b : 2;
+      const int64_t bit0 = 8 * P.seg[p][l0];
+      const float delta = P.meta[p][l0] / (float)((1 << (bb - 1)) - 1);
+      uint64_t win[kDeqV];
+      int sh[kDeqV];
+#pragma unroll
+      for (int v = 0; v < kDeqV; ++v) {
+        const int64_t bit = bit0 + (base + 4 * kAThreads * v) * bb;
+        const uint32_t* wp = P.pay[p] + (bit >> 5);
+        sh[v] = (int)(bit & 31);
+        win[v] = ok ? wp[0] : 0u;
+        if (ok && sh[v] + 4 * bb > 32) win[v] |= (uint64_t)wp[1] << 32;
+      }
+#pragma unroll
+      for (int v = 0; v < kDeqV; ++v) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t fld = (uint32_t)(win[v] >> (sh[v] + k * bb));
+          const int code = (int)(fld << (32 - bb)) >> (32 - bb);
+          const float x = ok ? (float)code * delta : 0.f;
+          if (p == 0) a0[v][k] = x;
+          else if (p == 1) a1[v][k] = x;
+          else if (p & 1) a1[v][k] = a1[v][k] + x;
+          else a0[v][k] = a0[v][k] + x;
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < kDeqV; ++v) {
+      const int64_t i0 = 4 * (f0 + (int64_t)kAThreads * v);
+      float r[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) r[k] = alpha * (W > 1 ? a0[v][k] + a1[v][k] : a0[v][k]);
+      float4 rv = make_float4(r[0], r[1], r[2], r[3]);
+      if (beta != 0.f) {
+        const float4 old = *reinterpret_cast<const float4*>(out + i0);
+        rv.x = rv.x + beta * old.x;
+        rv.y = rv.y + beta * old.y;
+        rv.z = rv.z + beta * old.z;
+        rv.w = rv.w + beta * old.w;
+      }
+      *reinterpret_cast<float4*>(out + i0) = rv;
+    }
+    return;
+  }
 #pragma unroll
   for (int v = 0; v < kDeqV; ++v) {
     const int64_t i0 = 4 * (f0 + (int64_t)kAThreads * v);
