@@ -134,6 +134,9 @@ __global__ __launch_bounds__(kAThreads) void k_alloc_quant(
   float* sp = stage[threadIdx.x >> 6];
   const int64_t w = (int64_t)blockIdx.x * kAThreads + threadIdx.x;
   const int64_t total = seg[nl];
+  // blocks wholly past the payload (the grid covers the capacity) leave at
+  // once, before any barrier (block-uniform)
+  if (4 * ((int64_t)blockIdx.x * kAThreads) >= total) return;
   // this lane's layer, width and run of elements (empty for lanes past the
   // payload, the second and third words of a 3-bit group, padding words)
   const bool word = w < cap_words && 4 * w < total;
@@ -182,10 +185,28 @@ __global__ __launch_bounds__(kAThreads) void k_alloc_quant(
     e_hi = __shfl(i1, last, 64);
     if (e_hi > e_lo + kWaveElems) e_hi = e_lo + kWaveElems;
   }
+  if (busy != 0) {
+    // every load issued before any is used: the indexes past the run are
+    // clamped to its last element (in bounds, the same cache line), only
+    // the LDS writes are predicated
+    float gv[kWaveElems / 64], ev[kWaveElems / 64];
 #pragma unroll
-  for (int t = 0; t < kWaveElems / 64; ++t) {
-    const int64_t i = e_lo + 64 * t + lane;
-    if (i < e_hi) sp[stage_slot(64 * t + lane)] = e != nullptr ? g[i] + e[i] : g[i];
+    for (int t = 0; t < kWaveElems / 64; ++t) {
+      const int64_t i = e_lo + 64 * t + lane;
+      gv[t] = g[i < e_hi ? i : e_hi - 1];
+    }
+    if (e != nullptr) {
+#pragma unroll
+      for (int t = 0; t < kWaveElems / 64; ++t) {
+        const int64_t i = e_lo + 64 * t + lane;
+        ev[t] = e[i < e_hi ? i : e_hi - 1];
+      }
+#pragma unroll
+      for (int t = 0; t < kWaveElems / 64; ++t) gv[t] = gv[t] + ev[t];
+    }
+#pragma unroll
+    for (int t = 0; t < kWaveElems / 64; ++t)
+      if (e_lo + 64 * t + lane < e_hi) sp[stage_slot(64 * t + lane)] = gv[t];
   }
   __syncthreads();
   if (lead) {
