@@ -146,13 +146,26 @@ __global__ __launch_bounds__(kAThreads) void k_alloc_quant(
   const int lw = 4 * wfirst < total ? wave_layer_of(seg, nl, 4 * wfirst) : 0;
   int l = 0, b = 0;
   int64_t sw1 = 0, i0 = 0, i1 = 0;
+  float mx = 0.f;
   bool lead = false;
   if (word) {
+    // the tables of the wave's layer loaded together (one memory latency),
+    // again for the layer of a lane past it
     l = lw;
-    if (seg[l + 1] <= 4 * w) l = layer_of(seg, nl, 4 * w, l + 1);
+    int64_t s0 = seg[l], s1 = seg[l + 1], o0 = off[l], o1 = off[l + 1];
     b = widths[l];
-    const int64_t sw0 = seg[l] >> 2;
-    sw1 = seg[l + 1] >> 2;
+    mx = meta[l];
+    if (s1 <= 4 * w) {
+      l = layer_of(seg, nl, 4 * w, l + 1);
+      s0 = seg[l];
+      s1 = seg[l + 1];
+      o0 = off[l];
+      o1 = off[l + 1];
+      b = widths[l];
+      mx = meta[l];
+    }
+    const int64_t sw0 = s0 >> 2;
+    sw1 = s1 >> 2;
     if (!alloc_width_ok(b)) {
       payload[w] = 0u;
     } else {
@@ -161,8 +174,8 @@ __global__ __launch_bounds__(kAThreads) void k_alloc_quant(
       const int nw = b == 3 ? 3 : 1;
       lead = (w - sw0) % nw == 0;
       if (lead) {
-        const int64_t lo = off[l];
-        const int64_t nlay = off[l + 1] - lo;
+        const int64_t lo = o0;
+        const int64_t nlay = o1 - lo;
         const int64_t kfirst = 32 * (w - sw0) / b;
         int64_t kend = kfirst + 32 * nw / b;
         if (kend > nlay) kend = nlay;
@@ -211,7 +224,7 @@ __global__ __launch_bounds__(kAThreads) void k_alloc_quant(
   __syncthreads();
   if (lead) {
     const int nreal = (int)(i1 - i0);
-    const LayerScale c = layer_scale(meta[l], (float)((1 << (b - 1)) - 1));
+    const LayerScale c = layer_scale(mx, (float)((1 << (b - 1)) - 1));
     const bool ef = e != nullptr;
 #define GQ_AQ(B, A)                                                          \
   alloc_quant_group<B, A>(sp, e_lo, i0, nreal, k0, k1, step, nearest, c,     \
