@@ -199,27 +199,35 @@ __global__ __launch_bounds__(kAThreads) void k_alloc_quant(
     if (e_hi > e_lo + kWaveElems) e_hi = e_lo + kWaveElems;
   }
   if (busy != 0) {
-    // every load issued before any is used: the indexes past the run are
-    // clamped to its last element (in bounds, the same cache line), only
-    // the LDS writes are predicated
-    float gv[kWaveElems / 64], ev[kWaveElems / 64];
+    // in chunks of eight rows of 64 (wave-uniform; chunks past the run are
+    // skipped): a chunk's sixteen loads are issued before any is used, the
+    // indexes past the run clamped to its last element (in bounds, the same
+    // cache line) and only the LDS writes predicated.  Holding all sixteen
+    // rows at once took 112 VGPRs (4 waves per SIMD).
+    const int nrows = (int)((e_hi - e_lo + 63) >> 6);
 #pragma unroll
-    for (int t = 0; t < kWaveElems / 64; ++t) {
-      const int64_t i = e_lo + 64 * t + lane;
-      gv[t] = g[i < e_hi ? i : e_hi - 1];
-    }
-    if (e != nullptr) {
+    for (int c = 0; c < kWaveElems / 64; c += 8) {
+      if (c < nrows) {
+        float gv[8], ev[8];
 #pragma unroll
-      for (int t = 0; t < kWaveElems / 64; ++t) {
-        const int64_t i = e_lo + 64 * t + lane;
-        ev[t] = e[i < e_hi ? i : e_hi - 1];
+        for (int t = 0; t < 8; ++t) {
+          const int64_t i = e_lo + 64 * (c + t) + lane;
+          gv[t] = g[i < e_hi ? i : e_hi - 1];
+        }
+        if (e != nullptr) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int64_t i = e_lo + 64 * (c + t) + lane;
+            ev[t] = e[i < e_hi ? i : e_hi - 1];
+          }
+#pragma unroll
+          for (int t = 0; t < 8; ++t) gv[t] = gv[t] + ev[t];
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (e_lo + 64 * (c + t) + lane < e_hi) sp[stage_slot(64 * (c + t) + lane)] = gv[t];
       }
-#pragma unroll
-      for (int t = 0; t < kWaveElems / 64; ++t) gv[t] = gv[t] + ev[t];
     }
-#pragma unroll
-    for (int t = 0; t < kWaveElems / 64; ++t)
-      if (e_lo + 64 * t + lane < e_hi) sp[stage_slot(64 * t + lane)] = gv[t];
   }
   __syncthreads();
   if (lead) {
