@@ -372,17 +372,23 @@ __global__ __launch_bounds__(kAThreads) void k_alloc_deq(
   const int64_t f0 = (int64_t)blockIdx.x * kAThreads * kDeqV + threadIdx.x;
   const int l0 = wave_layer_of(off, nl, 4 * (f0 - (threadIdx.x & 63)));
   const int64_t ilast = 4 * (f0 + (int64_t)kAThreads * (kDeqV - 1)) + 3;
-  if (ilast < n && ilast < off[l0 + 1]) {
+  // the first payload's tables for that layer are loaded with the layer's
+  // end (they depend on l0 alone), one memory latency for both
+  const int64_t end0 = off[l0 + 1];
+  const int b0 = P.widths[0][l0];
+  const int64_t seg0 = P.seg[0][l0];
+  const float m0 = P.meta[0][l0];
+  if (ilast < n && ilast < end0) {
     // all sixteen elements in layer l0: per payload one table lookup, and
     // the four groups' payload windows loaded together
     const int64_t base = 4 * f0 - off[l0];  // layer-relative index, group 0
     float a0[kDeqV][4], a1[kDeqV][4];
     for (int p = 0; p < W; ++p) {
-      const int b = P.widths[p][l0];
+      const int b = p == 0 ? b0 : P.widths[p][l0];
       const bool ok = alloc_width_ok(b);
       const int bb = ok ? b : 2;
-      const int64_t bit0 = 8 * P.seg[p][l0];
-      const float delta = P.meta[p][l0] / (float)((1 << (bb - 1)) - 1);
+      const int64_t bit0 = 8 * (p == 0 ? seg0 : P.seg[p][l0]);
+      const float delta = (p == 0 ? m0 : P.meta[p][l0]) / (float)((1 << (bb - 1)) - 1);
       uint64_t win[kDeqV];
       int sh[kDeqV];
 #pragma unroll
