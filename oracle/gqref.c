@@ -507,13 +507,22 @@ static void orq_bisect(const float *y, int64_t nj, int L, float *lev,
     }
     int room = L - cnt;
     if (m > room) {
-      /* keep the room largest gains (ties: smaller c, i.e. earlier) */
-      for (int a = 0; a < m; ++a)
-        for (int b = a + 1; b < m; ++b)
-          if (gain[b] > gain[a]) {
-            double tg = gain[a]; gain[a] = gain[b]; gain[b] = tg;
-            float tc = cand[a]; cand[a] = cand[b]; cand[b] = tc;
-          }
+      /* keep the room largest gains; equal gains keep the smaller c.  The
+       * candidates arrive in ascending c (intervals are visited in order),
+       * and a stable insertion sort by decreasing gain keeps that order
+       * among equal gains. */
+      for (int a = 1; a < m; ++a) {
+        double tg = gain[a];
+        float tc = cand[a];
+        int b = a;
+        while (b > 0 && gain[b - 1] < tg) {
+          gain[b] = gain[b - 1];
+          cand[b] = cand[b - 1];
+          --b;
+        }
+        gain[b] = tg;
+        cand[b] = tc;
+      }
       if (tie && gain[room] >= gain[room - 1] * (1.0 - TIE_REL)) *tie = 1;
       m = room;
     }

@@ -65,3 +65,26 @@ def test_orq9_bisect_100m_sampled(dev):
     from tests.test_gpu_full import check_runs
     check_runs(d, n, lambda lo, hi: g[lo:hi], None, codes, meta, None, 3, 0,
                sample_runs(d.nb(n), 12, 16, seed=99))
+
+
+def test_exact_tie_rounds_bit_for_bit(dev):
+    """Buckets of small integers, where gains tie exactly in any fp64 order:
+    the kernel's partial rounds take the smaller value on equal gains like
+    the oracle, so levels and codes must agree in every bucket, flagged ties
+    included."""
+    gq, torch = dev
+    from tests.test_gpu_small import run_gpu
+    rows = [np.array([-6, -6, -4, -2, -1, -1, -1, -1, 0, 0, 1, 2, 6, 6, 6, 6, 6]
+                     + [6] * 47, dtype=np.float32)]
+    for s in range(63):
+        rng = np.random.default_rng(7000 + s)
+        rows.append(rng.integers(-6, 7, 64).astype(np.float32))
+    g = np.concatenate(rows)
+    for L in (7, 8, 9):
+        d = O.Desc(O.ORQ, 64, L=L, flags=B)
+        say(f"bisect exact ties L={L} n={g.size}")
+        rc, rm, _, tie = O.quantize(d, g, None, seed=5, step=0)
+        gc, gm, _ = run_gpu(dev, d, g, None, 5, 0)
+        assert tie.sum() > 0
+        assert np.array_equal(gm, rm)
+        assert np.array_equal(gc[:d.code_bytes(g.size)], rc)

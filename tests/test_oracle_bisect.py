@@ -119,3 +119,30 @@ def test_flag_is_orq_only():
     for scheme in (O.UNIFORM, O.BIN_SIGN, O.BIN_OPT):
         with pytest.raises(ValueError):
             O.quantize(O.Desc(scheme, 64, flags=B), np.ones(8, np.float32))
+
+
+def test_exact_tie_round_takes_the_smaller_value():
+    """A partial round whose cut falls between equal gains keeps the smaller
+    candidate value: integer data make every gain exact in fp64, so the
+    ties are real ties, and the bucket is checked although it is flagged."""
+    x = np.array([-6, -6, -4, -2, -1, -1, -1, -1, 0, 0, 1, 2, 6, 6, 6, 6, 6],
+                 dtype=np.float32)
+    _, m, _, tie = O.quantize(O.Desc(O.ORQ, 64, L=7, flags=B), x)
+    assert tie[0] == 1
+    assert m[0].tolist() == [-6, -4, -2, -1, 1, 2, 6]
+    assert m[0].tolist() == _brute_bisect(x, 7)
+
+
+@pytest.mark.parametrize("L", [7, 8, 9])
+def test_small_integer_buckets_ties_included(L):
+    """Random small-integer buckets (many exact gain ties, none skipped)
+    against the brute-force rounds with their (-gain, value) order."""
+    flagged = 0
+    for s in range(120):
+        rng = np.random.default_rng(5000 + s)
+        n = int(rng.integers(10, 40))
+        x = rng.integers(-6, 7, n).astype(np.float32)
+        _, m, _, tie = O.quantize(O.Desc(O.ORQ, 64, L=L, flags=B), x)
+        flagged += int(tie[0])
+        assert m[0].astype(np.float64).tolist() == _brute_bisect(x, L), (s, x)
+    assert flagged > 0
