@@ -52,11 +52,14 @@ class GQError(RuntimeError):
 
 
 def _load():
-    if not os.path.exists(LIB_PATH):
+    # GQ_LIBRARY: load another build of the same sources instead (the host
+    # sanitizer test loads an AddressSanitizer build of the C ABI this way)
+    path = os.environ.get("GQ_LIBRARY", LIB_PATH)
+    if not os.path.exists(path):
         raise ImportError(
-            f"libgq.so not found at {LIB_PATH}; build it with "
+            f"libgq.so not found at {path}; build it with "
             "`python -m communication_efficient_gradient_amd.build`")
-    lib = C.CDLL(LIB_PATH)
+    lib = C.CDLL(path)
     P = C.c_void_p
     D = C.POINTER(gq_desc)
     i64, i32 = C.c_int64, C.c_int32

@@ -51,9 +51,14 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if _build.needs_build():
-            _build.build()
-        L = C.CDLL(_build.LIB)
+        # GQREF_LIBRARY: another build of gqref.c (the sanitizer test loads
+        # an AddressSanitizer / UBSan build through it)
+        path = os.environ.get("GQREF_LIBRARY")
+        if path is None:
+            if _build.needs_build():
+                _build.build()
+            path = _build.LIB
+        L = C.CDLL(path)
         i64, u64, u32, i32 = C.c_int64, C.c_uint64, C.c_uint32, C.c_int
         fp, cfp, u8p = C.c_void_p, C.c_void_p, C.c_void_p
         L.gqref_philox.argtypes = [u64, u64, u32, C.POINTER(C.c_uint32)]
