@@ -270,8 +270,11 @@ int gq_alloc_payload_bytes(int64_t n, int32_t nl, int64_t* bytes);
  * payload, meta 16 bytes; layer_offsets and segments 8; widths 4.  No buffer
  * written may overlap another buffer of the call.  Device tables are not
  * read on the host: a width outside {2, 3, 4, 8} writes zero codes for that
- * layer, and other contents give unspecified outputs but only in-bounds
- * stores.  Two launches on the stream (max-abs, codes). */
+ * layer and leaves its residual unspecified (the identity e = p - x_hat is
+ * kept only for layers of a valid width), and other contents (segments off
+ * 16-byte boundaries, offsets that disagree with the segments) give
+ * unspecified outputs but only in-bounds stores.  Two launches on the
+ * stream (max-abs, codes). */
 int gq_quantize_layers_alloc(int64_t n, int32_t nl, const int64_t* layer_offsets,
                              const float* g, float* e, const int32_t* widths,
                              const int64_t* segments, uint64_t seed,

@@ -1,14 +1,28 @@
 """GPU parity at the workloads' full sizes, in the launch configuration
 bench.py times (one gq_quantize / gq_dequantize_accumulate call over the
-whole gradient).
+whole gradient), compared on EVERY bucket.
 
-The HIP library runs on the full gradient; the CPU oracle recomputes runs of
-consecutive buckets (always the first and the partial last one) from the
-same seeded inputs, with the same global element index for the random
-counter, and the two are compared element by element on those runs.  The
-ternary workload is small enough to be compared whole, over its five
-error-feedback steps.
+The HIP library runs on the full gradient; the CPU oracle recomputes the
+whole payload chunk by chunk (2^25 elements, whole buckets, with the global
+element index of the chunk's first element for the random counter) from the
+same seeded inputs, and the two are compared element by element:
+
+* codes / packed bytes bit for bit; for the sorted schemes (BinGrad-b, ORQ)
+  a differing bucket must be one the oracle recorded as a near-tie, and the
+  GPU's choice there must still be a valid one (a threshold split whose
+  squared error equals the optimum's within the tie tolerance; ORQ levels
+  that are ascending bucket values spanning [min, max] with every code on
+  one of the two levels around its value), with its residual exactly
+  fl(p - x_hat) of the GPU's own levels;
+* levels / scales and residuals within the stated tolerances elsewhere.
+
+Each configuration's counts (buckets, oracle tie buckets, mismatched
+buckets, mismatched elements) are printed and, when GQ_PARITY_RECORD names a
+file, recorded there as JSON.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 
@@ -20,6 +34,7 @@ from tests.parity import (bucket_mask, compare_codes, compare_meta,
 pytestmark = pytest.mark.gpu
 
 RUNS, RUN_LEN = 12, 16
+CHUNK = 1 << 25          # a multiple of every bucket size and of 512
 
 
 @pytest.fixture(scope="module")
@@ -44,12 +59,135 @@ def byte_range(d: O.Desc, lo: int, hi: int):
     return lo * d.bits // 8, (hi * d.bits + 7) // 8
 
 
+def code_values(d: O.Desc, m: int, codes) -> np.ndarray:
+    """The m unsigned code fields (level indices / two's complement bits)."""
+    if d.dense:
+        return O.unpack_dense(d.alphabet, m, codes).astype(np.int64)
+    return O.unpack(d.bits, m, codes).astype(np.int64)
+
+
+def record(config: str, counts: dict) -> None:
+    say(f"parity {config}: {counts}")
+    path = os.environ.get("GQ_PARITY_RECORD")
+    if not path:
+        return
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    rec[config] = counts
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+
+
+def _valid_alternative(d: O.Desc, p: np.ndarray, cv: np.ndarray,
+                       lev: np.ndarray, ref_lev: np.ndarray,
+                       ref_cv: np.ndarray) -> None:
+    """A bucket whose GPU codes differ from the oracle's (an oracle near-tie):
+    the GPU's levels and codes must still be a valid result of the method."""
+    p64 = p.astype(np.float64)
+    if d.scheme == O.BIN_OPT:
+        lo_side, hi_side = p64[cv == 0], p64[cv == 1]
+        if lo_side.size and hi_side.size:
+            assert lo_side.max() < hi_side.min(), "not a threshold split"
+        for side, level in ((lo_side, lev[0]), (hi_side, lev[1])):
+            if side.size:
+                mu = side.mean()
+                assert abs(level - mu) <= 1e-5 * abs(mu), "level is not its side's mean"
+
+        def sse(codes):
+            s = 0.0
+            for k in (0, 1):
+                side = p64[codes == k]
+                if side.size:
+                    s += float(np.sum((side - side.mean()) ** 2))
+            return s
+        s_gpu, s_ref = sse(cv), sse(ref_cv)
+        assert s_gpu <= s_ref * (1 + 1e-9) + 1e-300, (s_gpu, s_ref)
+        return
+    assert d.scheme == O.ORQ
+    assert np.all(np.diff(lev.astype(np.float64)) >= 0), "levels not ascending"
+    if not d.flags & O.FLAG_CLIP:
+        assert lev[0] == p.min() and lev[-1] == p.max(), "levels do not span the bucket"
+        assert np.all(np.isin(lev, p)), "a level is not a bucket value"
+        pc = p
+    else:
+        pc = np.clip(p, lev[0], lev[-1])
+    L = lev.size
+    assert cv.max() < L
+    x = lev[cv]
+    j = np.clip(np.searchsorted(lev, pc, side="right") - 1, 0, L - 1)
+    below = lev[j]
+    above = lev[np.minimum(j + 1, L - 1)]
+    assert np.all((x == below) | (x == above) | (x == pc)), "code off its interval"
+
+
+def compare_whole(d: O.Desc, n: int, g_host, e_old_host, gpu_codes, gpu_meta,
+                  gpu_e_new, seed: int, step: int) -> dict:
+    """Compare the whole payload (and residual) chunk by chunk; returns the
+    counts.  g_host / e_old_host are callables (lo, hi) -> fp32 host arrays
+    (e_old_host None: no error feedback); gpu_* are device tensors."""
+    nb = d.nb(n)
+    k = d.k
+    exact = d.scheme in (O.UNIFORM, O.BIN_SIGN)
+    c = {"elements": n, "buckets": nb, "tie_buckets": 0,
+         "mismatched_buckets": 0, "mismatched_elements": 0,
+         "mismatched_buckets_outside_ties": 0}
+    for lo in range(0, n, CHUNK):
+        hi = min(n, lo + CHUNK)
+        m = hi - lo
+        j0, j1 = lo // d.d, (hi + d.d - 1) // d.d
+        g = g_host(lo, hi)
+        e = None if e_old_host is None else e_old_host(lo, hi)
+        rc, rm, re_, tie = O.quantize(d, g, e, seed=seed, step=step, i0=lo)
+        b0, b1 = byte_range(d, lo, hi)
+        gc = gpu_codes[b0:b1].cpu().numpy()
+        gm = gpu_meta[j0 * k: j1 * k].cpu().numpy().reshape(-1, k)
+        c["tie_buckets"] += int(tie.sum())
+        bad = compare_codes(d, m, gc, rc, tie, exact=exact)
+        p = g if e is None else (g + e)
+        if bad.size:
+            c["mismatched_buckets"] += int(bad.size)
+            gv, rv = code_values(d, m, gc), code_values(d, m, rc)
+            c["mismatched_elements"] += int(np.count_nonzero(gv != rv))
+            for b in bad:
+                s0, s1 = b * d.d, min(m, (b + 1) * d.d)
+                _valid_alternative(d, p[s0:s1], gv[s0:s1], gm[b], rm[b], rv[s0:s1])
+        if d.scheme == O.UNIFORM:
+            compare_meta(d, gm, rm, exact=True)
+        elif d.scheme == O.ORQ and not d.flags & O.FLAG_CLIP:
+            keep = np.ones(rm.shape[0], bool)
+            keep[bad] = False
+            assert np.array_equal(gm[keep], rm[keep]), "unclipped ORQ levels differ"
+        else:
+            compare_meta(d, gm, rm, skip=bad)
+        if e is not None:
+            ge = gpu_e_new[lo:hi].cpu().numpy()
+            if d.scheme == O.UNIFORM:
+                assert np.array_equal(ge.view(np.uint32), re_.view(np.uint32)), \
+                    f"residual differs in chunk at {lo}"
+            else:
+                p64 = p.astype(np.float64)
+                mk = bucket_mask(d, m, bad)
+                scale = np.maximum(np.abs(p64), np.abs(p64 - re_))
+                compare_values(ge[mk], re_[mk], scale[mk],
+                               extra=1e-5 * np.abs(p64 - re_)[mk])
+                for b in bad:
+                    s0, s1 = b * d.d, min(m, (b + 1) * d.d)
+                    gv = code_values(d, m, gc)[s0:s1]
+                    own = (p[s0:s1] - gm[b][gv]).astype(np.float32)
+                    assert np.array_equal(ge[s0:s1].view(np.uint32),
+                                          own.view(np.uint32)), \
+                        "tie bucket residual is not p - x_hat of its own levels"
+    return c
+
+
 def check_runs(d: O.Desc, n, g_host, e_old_host, gpu_codes, gpu_meta,
                gpu_e_new, seed, step, runs):
-    """Compare sampled bucket runs; returns {run start: oracle tie flags}.
-
-    g_host / e_old_host are callables (lo, hi) -> fp32 host arrays;
-    gpu_* are device tensors of the whole payload / residual."""
+    """Compare sampled bucket runs (for workloads compared whole elsewhere);
+    returns the number of oracle tie buckets seen."""
     nb = d.nb(n)
     exact = d.scheme in (O.UNIFORM, O.BIN_SIGN)
     ties = 0
@@ -96,6 +234,10 @@ def test_qsgd_whole(dev):
     compare_meta(d, meta.cpu().numpy().reshape(-1, 1), rm, exact=True)
     xr = O.dequantize(d, n, rc, rm)
     compare_values(out.cpu().numpy(), xr, np.abs(xr), exact=True)
+    record("qsgd s=4 d=512 n=65536", {"elements": n, "buckets": d.nb(n),
+                                      "tie_buckets": 0, "mismatched_buckets": 0,
+                                      "mismatched_elements": 0,
+                                      "mismatched_buckets_outside_ties": 0})
 
 
 @pytest.mark.parametrize("flags", [0, O.FLAG_DENSE])
@@ -125,64 +267,53 @@ def test_ternary_ef_five_steps_whole(dev, flags):
         xr = O.dequantize(d, n, rc, rm)
         assert np.array_equal(out.cpu().numpy().view(np.uint32),
                               xr.view(np.uint32)), f"dequantized, step {t}"
+    record(f"ternary+ef d=512 n={n} steps=5{' dense' if flags else ''}",
+           {"elements": n * WL.TERNARY_STEPS, "buckets": d.nb(n) * WL.TERNARY_STEPS,
+            "tie_buckets": 0, "mismatched_buckets": 0, "mismatched_elements": 0,
+            "mismatched_buckets_outside_ties": 0})
+
+
+_ORQ = {}
+
+
+def _orq_host():
+    if "g" not in _ORQ:
+        _ORQ["g"] = WL.orq_gradient()
+    return _ORQ["g"]
 
 
 @pytest.mark.parametrize("L,clip", [(5, 0), (5, 1), (9, 0), (9, 1),
                                     (3, O.FLAG_DENSE), (9, O.FLAG_DENSE)])
-def test_orq_100m_sampled(dev, L, clip):
+def test_orq_100m_whole(dev, L, clip):
     gq, torch = dev
     d = O.Desc(O.ORQ, 512, L=L, flags=clip, clip_sigma=3.0)
     n = WL.ORQ_N
-    say(f"orq L={L} clip={clip} n={n}")
-    g = WL.orq_gradient()
+    say(f"orq L={L} flags={clip} n={n}")
+    g = _orq_host()
     G = torch.from_numpy(g).cuda()
     codes, meta = gq.alloc_payload(gdesc(gq, d), n)
     gq.gq_quantize(gdesc(gq, d), G, None, 3, 0, codes, meta)
     torch.cuda.synchronize()
-    runs = sample_runs(d.nb(n), RUNS, RUN_LEN, seed=L + 10 * clip)
-    check_runs(d, n, lambda lo, hi: g[lo:hi], None, codes, meta, None, 3, 0,
-               runs)
-    # every code names a level of its bucket, on the whole payload
-    if d.dense:
-        v = O.unpack_dense(L, n, codes.cpu().numpy())
-    else:
-        v = O.unpack(d.bits, n, codes.cpu().numpy())
-    assert int(v.max()) < L
+    cnt = compare_whole(d, n, lambda lo, hi: g[lo:hi], None, codes, meta, None,
+                        3, 0)
+    name = {0: "", 1: " clip=3sigma", O.FLAG_DENSE: " dense"}[clip]
+    record(f"orq L={L}{name} d=512 n={n}", cnt)
 
 
-@pytest.mark.parametrize("bucket", [128, 512, 2048, 8192, 32768])
-@pytest.mark.parametrize("scheme", [O.BIN_OPT, O.BIN_SIGN])
-def test_bingrad_1b_two_steps_sampled(dev, bucket, scheme):
-    """1B elements, two error-feedback steps on the same gradient.  For the
-    sorted scheme the oracle's step 1 starts from the GPU's step-0 residual
-    (checked within tolerance first), so ulp-level level differences cannot
-    cascade."""
+@pytest.mark.parametrize("L", [5, 9])
+def test_orq_bisect_100m_whole(dev, L):
     gq, torch = dev
-    d = O.Desc(scheme, bucket)
-    n = WL.BINGRAD_N
-    say(f"bingrad scheme={scheme} d={bucket} n={n}")
-    g = _bingrad_host()
+    d = O.Desc(O.ORQ, 512, L=L, flags=O.FLAG_BISECT)
+    n = WL.ORQ_N
+    say(f"orq bisect L={L} n={n}")
+    g = _orq_host()
     G = torch.from_numpy(g).cuda()
-    E = torch.zeros(n, device="cuda")
     codes, meta = gq.alloc_payload(gdesc(gq, d), n)
-    runs = sample_runs(d.nb(n), RUNS, RUN_LEN, seed=bucket + scheme)
-    e_prev = None
-    for step in (0, 1):
-        gq.gq_quantize(gdesc(gq, d), G, E, 0, step, codes, meta)
-        torch.cuda.synchronize()
-        if step == 0:
-            e_old = lambda lo, hi: np.zeros(hi - lo, dtype=np.float32)  # noqa: E731
-        else:
-            e_old = lambda lo, hi: e_prev[(lo, hi)]  # noqa: E731
-        check_runs(d, n, lambda lo, hi: g[lo:hi], e_old, codes, meta, E, 0,
-                   step, runs)
-        nb = d.nb(n)
-        e_prev = {}
-        for j0 in runs:
-            lo, hi = j0 * bucket, min(n, min(nb, j0 + RUN_LEN) * bucket)
-            e_prev[(lo, hi)] = E[lo:hi].cpu().numpy()
-    del G, E, codes, meta
-    torch.cuda.empty_cache()
+    gq.gq_quantize(gdesc(gq, d), G, None, 3, 0, codes, meta)
+    torch.cuda.synchronize()
+    cnt = compare_whole(d, n, lambda lo, hi: g[lo:hi], None, codes, meta, None,
+                        3, 0)
+    record(f"orq L={L} bisect d=512 n={n}", cnt)
 
 
 _BINGRAD = {}
@@ -194,42 +325,99 @@ def _bingrad_host():
     return _BINGRAD["g"]
 
 
-def test_eight_workers_int8_ef_and_average(dev):
-    """8 x 256M INT8 + EF quantizations, then the W = 8 average over all
-    256M outputs, compared on sampled bucket runs."""
+@pytest.mark.parametrize("bucket", [128, 512, 2048, 8192, 32768])
+@pytest.mark.parametrize("scheme", [O.BIN_OPT, O.BIN_SIGN])
+def test_bingrad_1b_two_steps_whole(dev, bucket, scheme):
+    """1B elements, two error-feedback steps on the same gradient, every
+    bucket.  The oracle's step 1 starts from the GPU's step-0 residual (which
+    step 0 has checked within tolerance), so ulp-level level differences
+    cannot cascade."""
+    gq, torch = dev
+    d = O.Desc(scheme, bucket)
+    n = WL.BINGRAD_N
+    say(f"bingrad scheme={scheme} d={bucket} n={n}")
+    g = _bingrad_host()
+    G = torch.from_numpy(g).cuda()
+    E = torch.zeros(n, device="cuda")
+    codes, meta = gq.alloc_payload(gdesc(gq, d), n)
+    e_prev = None
+    for step in (0, 1):
+        if step == 1:
+            e_prev = E.cpu().numpy()
+        gq.gq_quantize(gdesc(gq, d), G, E, 0, step, codes, meta)
+        torch.cuda.synchronize()
+        if step == 0:
+            e_old = lambda lo, hi: np.zeros(hi - lo, dtype=np.float32)  # noqa: E731
+        else:
+            e_old = lambda lo, hi: e_prev[lo:hi]  # noqa: E731
+        cnt = compare_whole(d, n, lambda lo, hi: g[lo:hi], e_old, codes, meta,
+                            E, 0, step)
+        nm = "bin_opt" if scheme == O.BIN_OPT else "bin_sign"
+        record(f"{nm}+ef d={bucket} n={n} step={step}", cnt)
+    del G, E, codes, meta, e_prev
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------ eight workers, INT8 + EF --
+@pytest.fixture(scope="module")
+def workers(dev):
+    """The eight workers' INT8 + EF payloads and residuals (step 0 from a
+    zero residual, Philox seed w), computed once on the GPU."""
     gq, torch = dev
     d = O.Desc(O.UNIFORM, 512, s=127)
     W, n = WL.WORKERS_W, WL.WORKERS_N
-    runs = sample_runs(d.nb(n), RUNS, RUN_LEN, seed=5)
-    spans = [(j0 * 512, min(n, (j0 + RUN_LEN) * 512)) for j0 in runs]
-    codes_l, meta_l, ref_codes, ref_meta = [], [], [], []
+    res = {"d": d, "W": W, "n": n, "C": [], "M": [], "E": []}
     for w in range(1, W + 1):
-        say(f"worker {w}")
-        g = WL.worker_gradient(w)
-        G = torch.from_numpy(g).cuda()
+        say(f"worker {w}: GPU quantize")
+        G = torch.from_numpy(WL.worker_gradient(w)).cuda()
         E = torch.zeros(n, device="cuda")
         c, m = gq.alloc_payload(gdesc(gq, d), n)
         gq.gq_quantize(gdesc(gq, d), G, E, w, 0, c, m)
         torch.cuda.synchronize()
-        check_runs(d, n, lambda lo, hi: g[lo:hi],
-                   lambda lo, hi: np.zeros(hi - lo, dtype=np.float32),
-                   c, m, E, w, 0, runs)
-        codes_l.append(c)
-        meta_l.append(m)
-        ref_codes.append([c[lo:hi].cpu().numpy() for lo, hi in spans])
-        ref_meta.append([m[lo // 512: (hi + 511) // 512].cpu().numpy()
-                         for lo, hi in spans])
-        del G, E, g
+        del G
+        res["C"].append(c)
+        res["M"].append(m)
+        res["E"].append(E)
+    yield res
+    res.clear()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("w", range(1, 9))
+def test_worker_int8_ef_whole(dev, workers, w):
+    d, n = workers["d"], workers["n"]
+    say(f"worker {w}: compare the whole payload")
+    g = WL.worker_gradient(w)
+    cnt = compare_whole(d, n, lambda lo, hi: g[lo:hi],
+                        lambda lo, hi: np.zeros(hi - lo, dtype=np.float32),
+                        workers["C"][w - 1], workers["M"][w - 1],
+                        workers["E"][w - 1], w, 0)
+    record(f"int8+ef d=512 n={n} worker={w}", cnt)
+
+
+def test_workers_average_whole(dev, workers):
+    """The W = 8 average of the eight payloads over all 256M outputs against
+    the oracle's fp64 sum of the same payloads, rounded once."""
+    gq, torch = dev
+    d, n, W = workers["d"], workers["n"], workers["W"]
     out = torch.full((n,), float("nan"), device="cuda")
-    gq.gq_dequantize_accumulate(gdesc(gq, d), n, codes_l, meta_l, 1.0 / W, 0.0,
-                                out)
+    gq.gq_dequantize_accumulate(gdesc(gq, d), n, workers["C"], workers["M"],
+                                1.0 / W, 0.0, out)
     torch.cuda.synchronize()
-    for s, (lo, hi) in enumerate(spans):
-        cl = [ref_codes[w][s] for w in range(W)]
-        ml = [ref_meta[w][s] for w in range(W)]
-        ref = O.dequantize_accumulate(d, hi - lo, cl, ml, 1.0 / W, 0.0)
-        xs = [np.abs(O.dequantize(d, hi - lo, c, m).astype(np.float64))
-              for c, m in zip(cl, ml)]
+    step = 1 << 24
+    exact = 0
+    for lo in range(0, n, step):
+        hi = min(n, lo + step)
+        m = hi - lo
+        j0, j1 = lo // 512, (hi + 511) // 512
+        cl = [c[lo:hi].cpu().numpy() for c in workers["C"]]
+        ml = [mm[j0:j1].cpu().numpy().reshape(-1, 1) for mm in workers["M"]]
+        ref = O.dequantize_accumulate(d, m, cl, ml, 1.0 / W, 0.0)
+        xs = np.zeros(m, dtype=np.float64)
+        for c_, m_ in zip(cl, ml):
+            xs += np.abs(O.dequantize(d, m, c_, m_).astype(np.float64))
         got = out[lo:hi].cpu().numpy()
-        compare_values(got, ref, np.sum(xs, axis=0) / W)
-    assert not torch.isnan(out).any().item()
+        compare_values(got, ref, xs / W)
+        exact += int(np.count_nonzero(got.view(np.uint32) == ref.view(np.uint32)))
+    record(f"dequantize_accumulate int8 W={W} n={n}",
+           {"elements": n, "within_tolerance": n, "bit_exact_elements": exact})
