@@ -2,20 +2,22 @@
 """Throughput of bucketed stochastic gradient quantization with error feedback
 on one MI355X.
 
-A step of the headline workload is one error-feedback step of ternary
-(TernGrad-style, s = 1, 2-bit) quantization over a 25.6M-element fp32 gradient
-made of 160 Laplace "layers", bucket d = 512: p = g + e, per-bucket max-abs
-scale, Philox random rounding, packing, residual write-back (one fused kernel),
-then the receiving side's unpack + dequantize + accumulate (W = 1).  Five
-seeded gradients are resident in HBM and cycled, and the residual is carried
-from step to step.
+A step of the headline workload is the whole data-parallel path for eight
+simulated workers on one GPU: each worker's 256M-element fp32 gradient goes
+through one fused INT8 (s = 127) error-feedback quantize (p = g + e, per-bucket
+max-abs scale with d = 512, Philox random rounding, 8-bit packing, residual
+write-back), then the receiving side unpacks, dequantizes and averages the
+eight payloads into one fp32 buffer (W = 8, alpha = 1/8).  The eight seeded
+gradients are resident in HBM and every worker carries its residual from step
+to step.
 
 Printed: ONE JSON line with the whole-job throughput (GB/s of fp32 gradient
-through quantize + dequantize), the roofline of the dominant kernel (the fused
-quantizer) from HIP events on the launch stream, the CPU oracle timed on the
-host as a baseline, and one entry per other kernel/workload (QSGD latency,
-ORQ-5/9, BinGrad-b / sign over the bucket sweep, INT8 + EF for 8 workers and
-their W = 8 aggregation).
+through quantize + aggregate), the roofline of the dominant kernel (the fused
+INT8 quantizer) from HIP events recorded around every launch of the timed
+region on the launch stream, the CPU oracle timed on the host as a baseline,
+and one entry per other kernel/workload (QSGD latency, ternary + EF on the
+layered 25.6M gradient, ORQ-5/9, BinGrad-b / sign over the bucket sweep, and
+the variants).
 
     python bench.py [--steps K] [--warmup W] [--suite main|all]
     python bench.py --counters          # short run for rocprofv3 --pmc
@@ -38,8 +40,16 @@ if ROOT not in sys.path:
 METRIC = ("GB/s of fp32 gradient quantized+packed (and dequant+accumulated); "
           "% HBM peak")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-VALU_PEAK_TOPS = 157.3         # fp32 vector, published (256 CU x 2.4 GHz)
+# VALU peak in lane-operations per second for 32-bit and fp64 add / multiply /
+# fused multiply-add without packed fp32: 256 CUs x 4 SIMDs x 16 lanes x
+# 2.4 GHz = 39.3 T (one wave64 instruction per CU per cycle).  The published
+# 157.3 TFLOP/s fp32 figure counts packed fp32 (two lanes' worth per
+# instruction) and two flops per FMA; this library is built without packed
+# fp32.  The rate was measured on the GPU with independent chains of each
+# instruction (see the measured-peaks table in the design notes).
+VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+PARITY_FILE = os.path.join(ROOT, "profiles", "parity_full.json")
 _CSRC = "communication_efficient_gradient_amd/csrc/"
 # the sources (and build flags) each measured kernel is compiled from
 KERNEL_SOURCES = {
@@ -77,6 +87,72 @@ def deq_bytes(bits: int, k: int, d: int, n: int, W: int, beta: float) -> int:
     return W * per + 4 * n + (4 * n if beta != 0.0 else 0)
 
 
+# ------------------------------------------------------ algorithmic ops --
+# Lane-operations per element of the ALU-bound kernels' algorithms (each
+# fp32 / int32 / fp64 add, multiply, fused multiply-add, min, max, compare,
+# select, shift or logic op counts one; a division counts one), as the design
+# notes derive them.  Shared parts:
+#   bitonic sort of a d-bucket: log2 d (log2 d + 1) / 4 compare-exchanges per
+#     element, two ops each (min and max);
+#   Philox4x32-10: 10 rounds x (2 multiply-low + 2 multiply-high + 2 three-
+#     input xor + 2 key adds) per 4 elements = 20 per element;
+#   random rounding between two levels and packing: 10 per element.
+PHILOX_OPS = 20
+ROUND_PACK_OPS = 10
+
+
+def _log2(d: int) -> int:
+    return d.bit_length() - 1
+
+
+def sort_ops(d: int) -> float:
+    lg = _log2(d)
+    return 2 * lg * (lg + 1) / 4
+
+
+def orq_ops(L: int, d: int, clip: bool = False, bisect: bool = False) -> float:
+    """ORQ-L: sort; optional clip (square-accumulate, two clamps: 4); each
+    greedy step rescans the bucket (two fp64 prefix sums of (y - a) and
+    (b - y): 4, the gain (b - c) A + (c - a) B: 5, the argmax compare: 1 =
+    10 per element), L - 2 steps (bisection: ceil(log2(L - 1)) rounds of one
+    rescan each); level search log2 L compares; Philox; rounding and
+    packing."""
+    steps = (L - 2) if not bisect else (L - 2).bit_length()
+    return (sort_ops(d) + (4 if clip else 0) + 10 * steps + _log2(L)
+            + PHILOX_OPS + ROUND_PACK_OPS)
+
+
+def binopt_ops(d: int) -> float:
+    """BinGrad-b with error feedback: EF add (1); sort; one fp64 prefix sum
+    (convert + add: 2); the split objective P^2/k + (S - P)^2/(n - k) (one
+    subtract, two multiplies, two divides, one add: 6) and the argmax compare
+    (1); threshold compare, level select, residual subtract, pack (4)."""
+    return 1 + sort_ops(d) + 2 + 6 + 1 + 4
+
+
+def topk_ops(d: int, K: int) -> float:
+    """Top-K with quantization and error feedback: EF add and |p| key (2);
+    a 31-round bitwise selection of the K-th largest key (compare + count
+    per round: 62); rank of the kept (2); residual (2); the kept elements'
+    Philox, rounding and packing (K / d of 30)."""
+    return 2 + 62 + 2 + 2 + (K / d) * (PHILOX_OPS + ROUND_PACK_OPS)
+
+
+def elias_encode_ops() -> float:
+    """Elias gamma encode: code unpack (2), codeword length (3), the count
+    pass's sum (1), the record pass's prefix sum (1) and bit placement
+    (shift, or, and word split: 4)."""
+    return 11.0
+
+
+def alu_fields(ops_per_element: float, n: int, ms: float) -> dict:
+    achieved = ops_per_element * n / (ms * 1e-3)
+    return {"alu_ops_per_element": round(ops_per_element, 2),
+            "alu_achieved_Tops": round(achieved / 1e12, 3),
+            "alu_peak_Tops": round(VALU_PEAK_LANE_OPS / 1e12, 2),
+            "alu_frac": round(achieved / VALU_PEAK_LANE_OPS, 4)}
+
+
 # ------------------------------------------------------------- GPU timing --
 def load_traffic(key: str, kernel: str):
     """HBM bytes per launch from the rocprofv3 counter runs, if they were
@@ -93,7 +169,66 @@ def load_traffic(key: str, kernel: str):
 
 
 # --------------------------------------------------------------- workloads --
-class Main:
+class Headline:
+    """Eight workers' INT8 (s = 127) + error-feedback quantize of 256M fp32
+    elements each (bucket d = 512, Philox seed w, step t), then the W = 8
+    dequantize-accumulate into one fp32 average (alpha = 1/8, beta = 0).
+
+    The eight gradients (seeded, resident in HBM), residuals and payloads
+    are 18.4 GB, so no launch finds its working set in the 256 MB last-level
+    cache; each worker's residual is carried from step to step."""
+
+    KEY = "int8_ef_d512_n256M"
+    AGG_KEY = "int8_w8_n256M:aggregate"
+    CPU_PREFIX = 1 << 25        # elements of each worker kept for the oracle
+
+    def __init__(self, torch, gq, WL, stream):
+        self.torch, self.gq, self.stream = torch, gq, stream
+        self.W, self.n = WL.WORKERS_W, WL.WORKERS_N
+        self.desc = gq.desc(gq.GQ_UNIFORM, 512, s=127)
+        self.bits = gq.gq_code_bits(self.desc)
+        t0 = time.time()
+        self.G, self.E, self.C, self.M, self.host = [], [], [], [], []
+        for w in range(1, self.W + 1):
+            h = WL.worker_gradient(w)
+            self.host.append(h[: self.CPU_PREFIX].copy())
+            self.G.append(torch.from_numpy(h).cuda())
+            del h
+            self.E.append(torch.zeros(self.n, dtype=torch.float32, device="cuda"))
+            c, m = gq.alloc_payload(self.desc, self.n)
+            self.C.append(c)
+            self.M.append(m)
+        self.avg = torch.empty(self.n, dtype=torch.float32, device="cuda")
+        log(f"headline: {self.W} x {self.n} worker inputs in {time.time() - t0:.1f}s")
+        self.q = [gq.PreparedQuantize(self.desc, self.G[w], self.E[w], self.C[w],
+                                      self.M[w], stream) for w in range(self.W)]
+        self.dq = gq.PreparedDequantizeAccumulate(
+            self.desc, self.n, self.C, self.M, 1.0 / self.W, 0.0, self.avg, stream)
+
+    def step(self, t: int, ev=None):
+        """One step; with ev (W + 2 events) an event is recorded on the
+        launch stream before every launch and after the last."""
+        for w in range(self.W):
+            if ev is not None:
+                ev[w].record(self.stream)
+            self.q[w](w + 1, t)
+        if ev is not None:
+            ev[self.W].record(self.stream)
+        self.dq()
+        if ev is not None:
+            ev[self.W + 1].record(self.stream)
+
+    def qbytes(self):
+        return quant_bytes(self.bits, 1, 512, self.n, True)
+
+    def dbytes(self):
+        return deq_bytes(self.bits, 1, 512, self.n, self.W, 0.0)
+
+    def release(self):
+        del self.q, self.dq, self.G, self.E, self.C, self.M, self.avg
+
+
+class Ternary:
     """Ternary + error feedback over the 25.6M-element layered gradient,
     then dequantize (W = 1), cycling the five seeded steps.
 
@@ -111,9 +246,7 @@ class Main:
     def __init__(self, torch, gq, WL, stream):
         self.torch, self.gq, self.stream = torch, gq, stream
         self.n = WL.TERNARY_N
-        t0 = time.time()
         self.host = [WL.ternary_gradient(t) for t in range(WL.TERNARY_STEPS)]
-        log(f"main: generated {len(self.host)} x {self.n} in {time.time() - t0:.1f}s")
         self.G = [torch.from_numpy(h).cuda() for h in self.host]
         self.desc = gq.desc(gq.GQ_UNIFORM, 512, s=1)
         self.bits = gq.gq_code_bits(self.desc)
@@ -151,48 +284,100 @@ class Main:
         return deq_bytes(self.bits, 1, 512, self.n, 1, 0.0)
 
 
-def cpu_baseline(main: Main, min_wall: float = 1.0):
-    """The oracle on the host, on the headline workload: consecutive error-
-    feedback steps (quantize with the carried residual, then dequantize),
-    repeated until at least `min_wall` seconds have passed."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(hl: Headline, repeats: int = 3):
+    """The oracle on the host, on a bounded sample of the headline step: the
+    first 2^25 elements of each of the eight workers (whole buckets),
+    quantized INT8 + error feedback from a zero residual (Philox seed w, step
+    0, global element indices from 0), then their W = 8 average.  Best of
+    `repeats` wall times with all the OpenMP threads the host gives the
+    oracle, and again with one thread on the first 2^22 elements of each
+    worker."""
     import numpy as np
 
     import oracle as O
 
-    od = O.Desc(O.UNIFORM, 512, s=1)
-    e = np.zeros(main.n, dtype=np.float32)
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        g = main.host[steps % len(main.host)]
-        c, m, e, _ = O.quantize(od, g, e, seed=Main.SEED, step=steps)
-        O.dequantize_accumulate(od, g.size, [c], [m], 1.0, 0.0)
-        steps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_wall:
-            break
+    od = O.Desc(O.UNIFORM, 512, s=127)
+
+    def run(m: int) -> float:
+        best = float("inf")
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            cs, ms_ = [], []
+            for w in range(hl.W):
+                g = hl.host[w][:m]
+                c, mm, _, _ = O.quantize(od, g, np.zeros(m, np.float32),
+                                         seed=w + 1, step=0)
+                cs.append(c)
+                ms_.append(mm)
+            O.dequantize_accumulate(od, m, cs, ms_, 1.0 / hl.W, 0.0)
+            best = min(best, time.perf_counter() - t0)
+        return best
+
     th = O.threads()
-    return {"value": round(4 * main.n * steps / dt / 1e9, 4), "unit": "GB/s",
-            "cores": th, "kind": "oracle",
-            "sample": (f"{steps} error-feedback step(s) of the headline "
-                       f"workload ({main.n} elements each): quantize + "
-                       f"dequantize, {dt:.2f} s wall on {th} OpenMP threads "
-                       f"({dt * th:.1f} thread-seconds)")}
+    m_all = hl.CPU_PREFIX
+    t_all = run(m_all)
+    O.set_threads(1)
+    try:
+        m_one = 1 << 22
+        t_one = run(m_one)
+    finally:
+        O.set_threads(th)
+    gbs = lambda m, t: round(4 * m * hl.W / t / 1e9, 4)  # noqa: E731
+    return {"value": gbs(m_all, t_all), "unit": "GB/s", "cores": th,
+            "kind": "oracle",
+            "sample": (f"the headline step on the first {m_all} elements of "
+                       f"each of {hl.W} workers: INT8 + EF quantize, then the "
+                       f"W={hl.W} average; best of {repeats}: {t_all:.3f} s "
+                       f"wall on {th} OpenMP threads"),
+            "t1_value": gbs(m_one, t_one),
+            "t1_sample": (f"same step on the first {m_one} elements of each "
+                          f"worker, one thread, best of {repeats}: "
+                          f"{t_one:.3f} s"),
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+
+
+_LAST_TIMING = {}
+
+
+def _stats(durs):
+    """Median, mean, 10th / 90th percentile and count of per-launch times."""
+    s = sorted(durs)
+    q = lambda f: s[min(len(s) - 1, int(f * (len(s) - 1) + 0.5))]  # noqa: E731
+    return {"median": q(0.5), "mean": sum(s) / len(s), "p10": q(0.1),
+            "p90": q(0.9), "runs": len(s)}
+
+
+def time_launches(torch, stream, launch, reps: int, warm: int = 3) -> dict:
+    """Per-launch durations of `reps` launches, each bracketed by its own
+    pair of HIP events on the launch stream (the events of consecutive
+    launches are shared, so the launches stay back to back)."""
+    for i in range(warm):
+        launch(i)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        launch(warm + i)
+        ev[i + 1].record(stream)
+    ev[-1].synchronize()
+    st = _stats([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
+    _LAST_TIMING["stats"] = st
+    return st
 
 
 def time_back_to_back(torch, stream, launch, reps: int, warm: int = 3) -> float:
-    """Average duration of `reps` launches issued back to back, bracketed by
-    one pair of HIP events on the launch stream."""
-    for i in range(warm):
-        launch(i)
-    ev = torch.cuda.Event
-    a, b = ev(enable_timing=True), ev(enable_timing=True)
-    a.record(stream)
-    for i in range(reps):
-        launch(warm + i)
-    b.record(stream)
-    b.synchronize()
-    return a.elapsed_time(b) / reps
+    """Median per-launch duration in ms (see time_launches)."""
+    return time_launches(torch, stream, launch, reps, warm)["median"]
 
 
 def copy_reference(torch, stream, nbytes: int = 1 << 30) -> dict:
@@ -258,13 +443,22 @@ def run_deferred() -> None:
     DEFERRED.clear()
 
 
-def entry(name, ms, nbytes, n, bound="hbm", extra=None):
+def entry(name, ms, nbytes, n, bound="hbm", extra=None, alu=None):
+    """One kernel's line: `ms` is the median per-launch duration of the
+    timing just taken (its spread is attached), `alu` the algorithmic
+    lane-operations per element of an ALU-bound kernel."""
     gbs = nbytes / (ms * 1e-3) / 1e9
     r = {"kernel": name, "ms": round(ms, 5),
          "elements_per_s": round(n / (ms * 1e-3)),
          "logical_GBps": round(4 * n / (ms * 1e-3) / 1e9, 2),
          "moved_GBps": round(gbs, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
          "bound": bound}
+    st = _LAST_TIMING.pop("stats", None)
+    if st is not None and st["median"] == ms:
+        r.update({"ms_mean": round(st["mean"], 5), "ms_p10": round(st["p10"], 5),
+                  "ms_p90": round(st["p90"], 5), "runs": st["runs"]})
+    if alu is not None:
+        r.update(alu_fields(alu, n, ms))
     if extra:
         r.update(extra)
         job = r.pop("_oracle", None)
@@ -275,7 +469,7 @@ def entry(name, ms, nbytes, n, bound="hbm", extra=None):
 
 def suite(torch, gq, WL, stream, reps: int, only: str | None = None):
     """Every other workload's kernels, each timed back to back (only the
-    workloads whose name contains `only`: qsgd, orq, bingrad, workers,
+    workloads whose name contains `only`: qsgd, orq, bingrad, ternary,
     dense, nearest, layers, topk, elias)."""
     out = []
     tb = lambda f, r=reps: time_back_to_back(torch, stream, f, r)  # noqa: E731
@@ -284,7 +478,7 @@ def suite(torch, gq, WL, stream, reps: int, only: str | None = None):
     suites = [("qsgd", lambda: suite_qsgd(torch, gq, WL, stream, tb)),
               ("orq", lambda: suite_orq(torch, gq, WL, stream, tb, reps)),
               ("bingrad", lambda: suite_bingrad(torch, gq, WL, stream, tb, reps)),
-              ("workers", lambda: suite_workers(torch, gq, WL, stream, tb)),
+              ("ternary", lambda: suite_ternary(torch, gq, WL, stream, tb, reps)),
               ("dense", lambda: suite_dense(torch, gq, WL, stream, tb, reps)),
               ("nearest", lambda: suite_nearest(torch, gq, WL, stream, tb, reps)),
               ("layers", lambda: suite_layers(torch, gq, WL, stream, tb)),
@@ -294,7 +488,7 @@ def suite(torch, gq, WL, stream, reps: int, only: str | None = None):
         if want(name):
             out += run()
             # each workload starts from memory handed back to the driver: a
-            # suite placed in the 18 GB the workers suite left cached ran up
+            # suite placed in the 18 GB the headline's buffers left cached ran up
             # to 20 % slower than alone
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
@@ -336,7 +530,8 @@ def suite_elias(torch, gq, WL, stream, tb):
                  "compression_vs_fp32": round(4 * n / (stream_bytes + 4 * mf), 3),
                  "compression_fixed": round(4 * n / (cb + 4 * mf), 3)}
         out.append(entry(f"elias encode s={s} d=512 n={n}", ms,
-                         2 * cb + 4 * nw + 3 * 8 * nb, n, extra={**extra, **oracle}))
+                         2 * cb + 4 * nw + 3 * 8 * nb, n, bound="alu",
+                         extra={**extra, **oracle}, alu=elias_encode_ops()))
         ms = tb(lambda i: gq.gq_elias_decode(d, n, S[i % 2][0], S[i % 2][1],
                                              back[i % 2], stream=stream))
         out.append(entry(f"elias decode s={s} d=512 n={n}", ms,
@@ -370,7 +565,7 @@ def suite_topk(torch, gq, WL, stream, tb):
         lambda k: O.quantize_topk(512, 4, 26, host[:k], np.zeros(k, np.float32),
                                   seed=2), n, 512)}
     out.append(entry(f"quantize top-k 26/512 s=4 +ef n={n}", ms,
-                     12 * n + cb + 4 * mf, n,
+                     12 * n + cb + 4 * mf, n, bound="alu", alu=topk_ops(512, 26),
                      extra={"compression_vs_fp32": round(4 * n / (cb + 4 * mf), 3),
                             **oracle}))
     dqs = [gq.PreparedDequantizeAccumulate(d, n, [P[k][0]], [P[k][1]], 1.0, 0.0,
@@ -479,6 +674,7 @@ def suite_nearest(torch, gq, WL, stream, tb, reps):
     ms = tb(lambda i: q(3, 0), max(3, reps // 2))
     out.append(entry(f"quantize orq L=9 nearest d=512 n={n}", ms,
                      quant_bytes(4, 9, 512, n, False), n, bound="alu",
+                     alu=orq_ops(9, 512),
                      extra=oracle_rate(host, dict(scheme=3, d=512, L=9, flags=N),
                                        False, seed=3)))
     return out
@@ -526,7 +722,7 @@ def suite_dense(torch, gq, WL, stream, tb, reps):
         cb = ratio(d, n)
         out.append(entry(f"quantize orq L={L} dense d=512 n={n}", ms,
                          4 * n + cb["code_bytes"] + 4 * L * ((n + 511) // 512),
-                         n, bound="alu",
+                         n, bound="alu", alu=orq_ops(L, 512),
                          extra={**cb, **oracle_rate(host, dict(scheme=3, d=512,
                                                                L=L, flags=2),
                                                     False, seed=3)}))
@@ -590,7 +786,8 @@ def suite_orq(torch, gq, WL, stream, tb, reps):
             ms = tb(lambda i: q(3, 0), max(3, reps // 2))
             out.append(entry(f"quantize orq L={L} clip={clip} d=512 n={n}", ms,
                              quant_bytes(bits, L, 512, n, False), n,
-                             bound="alu", extra=oracle_rate(
+                             bound="alu", alu=orq_ops(L, 512, clip=bool(clip)),
+                             extra=oracle_rate(
                                  host, dict(scheme=3, d=512, L=L, flags=clip,
                                             clip_sigma=3.0), False, seed=3)))
             del c, m, q
@@ -602,7 +799,8 @@ def suite_orq(torch, gq, WL, stream, tb, reps):
         ms = tb(lambda i: q(3, 0), max(3, reps // 2))
         out.append(entry(f"quantize orq L={L} bisect d=512 n={n}", ms,
                          quant_bytes(gq.gq_code_bits(d), L, 512, n, False), n,
-                         bound="alu", extra=oracle_rate(
+                         bound="alu", alu=orq_ops(L, 512, bisect=True),
+                         extra=oracle_rate(
                              host, dict(scheme=3, d=512, L=L, flags=8), False,
                              seed=3)))
         del c, m, q
@@ -628,6 +826,7 @@ def suite_bingrad(torch, gq, WL, stream, tb, reps):
             ms = tb(lambda i: q(0, i), max(3, reps // 2))
             out.append(entry(f"quantize {nm}+ef d={dd} n={n}", ms,
                              quant_bytes(1, 2, dd, n, True), n,
+                             alu=binopt_ops(dd) if scheme == gq.GQ_BIN_OPT else None,
                              extra=oracle_rate(host, dict(scheme=scheme, d=dd),
                                                True)))
             del c, m, q
@@ -645,38 +844,22 @@ def suite_bingrad(torch, gq, WL, stream, tb, reps):
     return out
 
 
-def suite_workers(torch, gq, WL, stream, tb):
-    """INT8 + EF for 8 workers of 256M each, then the W = 8 average."""
+def suite_ternary(torch, gq, WL, stream, tb, reps):
+    """Ternary (s = 1, 2-bit) + error feedback on the 25.6M layered gradient
+    (160 Laplace layers, d = 512), quantize and dequantize W = 1, with two
+    alternating buffer sets so no launch finds its data in the last-level
+    cache; and the whole step (quantize + dequantize) back to back."""
+    tw = Ternary(torch, gq, WL, stream)
     out = []
-    W, n = WL.WORKERS_W, WL.WORKERS_N
-    d = gq.desc(gq.GQ_UNIFORM, 512, s=127)
-    Gs, Es, Cs, Ms = [], [], [], []
-    t0 = time.time()
-    host1 = None
-    for w in range(1, W + 1):
-        h = WL.worker_gradient(w)
-        if w == 1:
-            host1 = h[: 1 << 22].copy()
-        Gs.append(torch.from_numpy(h).cuda())
-        del h
-        Es.append(torch.zeros(n, dtype=torch.float32, device="cuda"))
-        c, m = gq.alloc_payload(d, n)
-        Cs.append(c)
-        Ms.append(m)
-    log(f"suite: worker inputs in {time.time() - t0:.1f}s")
-    qs = [gq.PreparedQuantize(d, Gs[w], Es[w], Cs[w], Ms[w], stream)
-          for w in range(W)]
-    ms = tb(lambda i: qs[i % W](i % W + 1, 0), 2 * W)
-    out.append(entry(f"quantize int8+ef d=512 n={n} (per worker)", ms,
-                     quant_bytes(8, 1, 512, n, True), n,
-                     extra=oracle_rate(host1, dict(scheme=0, d=512, s=127),
-                                       True, seed=1)))
-    avg = torch.empty(n, dtype=torch.float32, device="cuda")
-    dq = gq.PreparedDequantizeAccumulate(d, n, Cs, Ms, 1.0 / W, 0.0, avg,
-                                         stream)
-    ms = tb(lambda i: dq())
-    out.append(entry(f"dequantize_accumulate int8 W={W} n={n}", ms,
-                     deq_bytes(8, 1, 512, n, W, 0.0), n * W))
+    ms = tb(tw.quantize, max(20, reps))
+    out.append(entry(f"quantize ternary+ef d=512 n={tw.n}", ms, tw.qbytes(),
+                     tw.n, extra=oracle_rate(tw.host[0], dict(scheme=0, d=512, s=1),
+                                             True, seed=2)))
+    ms = tb(tw.dequantize, max(20, reps))
+    out.append(entry(f"dequantize ternary W=1 n={tw.n}", ms, tw.dbytes(), tw.n))
+    ms = tb(tw.step, max(20, reps))
+    out.append(entry(f"step ternary+ef quantize + dequantize n={tw.n}", ms,
+                     tw.qbytes() + tw.dbytes(), tw.n))
     return out
 
 
@@ -714,8 +897,8 @@ def ingest(dirs):
         "write_scale": round(w_scale, 5),
         "note": ("counters are KiB per dispatch; traffic = FETCH_SIZE*1024*"
                  "fetch_scale + WRITE_SIZE*1024*write_scale")}}
-    for key, tag in ((Main.KEY, "k_stream_quant"),
-                     (Main.KEY + ":dequantize", "k_deq_acc")):
+    for key, tag in ((Headline.KEY, "k_stream_quant"),
+                     (Headline.AGG_KEY, "k_deq_acc")):
         kname, f = med("FETCH_SIZE", lambda k, t=tag: t in k)
         _, w = med("WRITE_SIZE", lambda k, t=tag: t in k)
         res[key] = {"kernel": kname, "source_digest": source_digest(tag),
@@ -730,20 +913,31 @@ def ingest(dirs):
 
 
 # -------------------------------------------------------------------- main --
+def load_parity():
+    """Whole-payload parity counts of the full-size workloads, as the GPU
+    tests last recorded them (tie buckets and mismatched elements per
+    configuration), or None."""
+    try:
+        with open(PARITY_FILE) as f:
+            return json.load(f)
+    except (OSError, ValueError):
+        return None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--suite", choices=("main", "all"), default="all")
     ap.add_argument("--reps", type=int, default=20)
-    ap.add_argument("--only", choices=("qsgd", "orq", "bingrad", "workers",
+    ap.add_argument("--only", choices=("qsgd", "orq", "bingrad", "ternary",
                                        "dense", "nearest", "layers", "topk",
                                        "elias"),
                     help="time only this workload's kernels after the headline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--counters", action="store_true",
-                    help="short run for rocprofv3 --pmc: main steps + a copy")
+                    help="short run for rocprofv3 --pmc: headline steps + a copy")
     ap.add_argument("--ingest", nargs="+", metavar="DIR")
     args = ap.parse_args()
 
@@ -771,10 +965,10 @@ def main() -> int:
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
 
-    mw = Main(torch, gq, WL, stream)
+    hl = Headline(torch, gq, WL, stream)
     if args.counters:
-        for t in range(4):
-            mw.step(t)
+        for t in range(2):
+            hl.step(t)
         # calibration: one plain elementwise pass (read COPY_BYTES, write
         # COPY_BYTES); torch's negation kernel is the only one of its kind here
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -784,40 +978,52 @@ def main() -> int:
         log("counters run done")
         return 0
 
-    # ---- the timed region: K whole steps --------------------------------
+    # ---- the timed region: K whole steps, an event around every launch ----
     for t in range(args.warmup):
-        mw.step(t)
+        hl.step(t)
     torch.cuda.synchronize()
-    ev0, ev1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+    W = hl.W
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(W + 2)]
+           for _ in range(args.steps)]
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for t in range(args.warmup, args.warmup + args.steps):
-        mw.step(t)
-    ev1.record(stream)
+    for k, t in enumerate(range(args.warmup, args.warmup + args.steps)):
+        hl.step(t, evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    gpu_ms_step = ev0.elapsed_time(ev1) / args.steps
+    gpu_ms_step = evs[0][0].elapsed_time(evs[-1][-1]) / args.steps
+    q_durs = [ev[w].elapsed_time(ev[w + 1]) for ev in evs for w in range(W)]
+    d_durs = [ev[W].elapsed_time(ev[W + 1]) for ev in evs]
+    qs, ds = _stats(q_durs), _stats(d_durs)
+    n = hl.n
+    qb, db = hl.qbytes(), hl.dbytes()
+    achieved = qb / (qs["mean"] * 1e-3) / 1e9
+    traffic = load_traffic(Headline.KEY, "k_stream_quant")
+    agg_traffic = load_traffic(Headline.AGG_KEY, "k_deq_acc")
+    log(f"headline: {ms_step * 1e3:.1f} us/step wall ({gpu_ms_step * 1e3:.1f} us "
+        f"GPU); quantize mean {qs['mean'] * 1e3:.1f} us median "
+        f"{qs['median'] * 1e3:.1f} us ({achieved:.0f} GB/s); aggregate mean "
+        f"{ds['mean'] * 1e3:.1f} us")
 
-    # ---- per-kernel durations: each kernel back to back ------------------
-    reps = max(20, min(args.steps, 200))
-    q_ms = time_back_to_back(torch, stream, mw.quantize, reps)
-    d_ms = time_back_to_back(torch, stream, mw.dequantize, reps)
-    n = mw.n
-    qb = mw.qbytes()
-    achieved = qb / (q_ms * 1e-3) / 1e9
-    traffic = load_traffic(Main.KEY, "k_stream_quant")
-    log(f"main: {ms_step * 1e3:.1f} us/step wall ({gpu_ms_step * 1e3:.1f} us "
-        f"GPU), quantize {q_ms * 1e3:.1f} us ({achieved:.0f} GB/s), "
-        f"dequantize {d_ms * 1e3:.1f} us")
+    def live(name, st, nbytes, elements):
+        r = entry(name, st["median"], nbytes, elements)
+        r.update({"ms_mean": round(st["mean"], 5), "ms_p10": round(st["p10"], 5),
+                  "ms_p90": round(st["p90"], 5), "runs": st["runs"],
+                  "timed": "inside the headline's timed region"})
+        return r
 
     kernels = [
-        entry("quantize ternary+ef d=512 n=25.6M (headline)", q_ms, qb, n),
-        entry("dequantize ternary W=1 n=25.6M (headline)", d_ms,
-              mw.dbytes(), n),
+        live(f"quantize int8+ef d=512 n={n} (headline, per worker)", qs, qb, n),
+        live(f"dequantize_accumulate int8 W={W} n={n} (headline)", ds, db, n * W),
     ]
+    kernels[0].update(oracle_rate(hl.host[0], dict(scheme=0, d=512, s=127),
+                                  True, seed=1))
+    job = kernels[0].pop("_oracle")
+    DEFERRED.append((kernels[0], job))
+    kernels[1]["traffic"] = agg_traffic
     if args.suite == "all":
-        del mw.q, mw.G
+        hl.release()
+        torch.cuda.synchronize()
         torch.cuda.empty_cache()
         kernels.append(copy_reference(torch, stream))
         torch.cuda.empty_cache()
@@ -833,12 +1039,12 @@ def main() -> int:
     run_deferred()
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(mw)
+        cpu = cpu_baseline(hl)
         log(f"cpu baseline: {cpu}")
 
     line = {
         "metric": METRIC,
-        "value": round(4 * n / (ms_step * 1e-3) / 1e9, 3),
+        "value": round(4 * n * W / (ms_step * 1e-3) / 1e9, 3),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -850,25 +1056,35 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": ("ternary (s=1, 2-bit) + error feedback, 25.6M fp32 "
-                         "elements in 160 Laplace layers, d=512, Philox "
-                         "rounding; quantize + dequantize per step"),
-            "elements": n, "bucket": 512, "code_bits": 2,
-            "hbm_bytes_per_step": qb + mw.dbytes(),
+            "workload": (f"{W} simulated workers x {n} fp32 elements "
+                         "(N(0,1e-3^2) own + shared component): INT8 (s=127) "
+                         "+ error feedback, d=512, Philox rounding, then the "
+                         f"W={W} dequantize-accumulate average; one step = "
+                         f"{W} quantizes + 1 aggregation"),
+            "elements_per_worker": n, "workers": W, "bucket": 512,
+            "code_bits": hl.bits,
+            "hbm_bytes_per_step": W * qb + db,
             "gpu_ms_per_step": round(gpu_ms_step, 5),
+            "hbm_frac_per_step": round((W * qb + db) / (ms_step * 1e-3) / 1e9
+                                       / HBM_PEAK_GBS, 4),
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_stream_quant (ternary, error feedback, d=512)",
+            "kernel": "k_stream_quant (INT8 s=127, error feedback, d=512)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes": qb,
-            "avg_launch_us": round(q_ms * 1e3, 3),
+            "avg_launch_us": round(qs["mean"] * 1e3, 3),
+            "median_launch_us": round(qs["median"] * 1e3, 3),
+            "p10_p90_launch_us": [round(qs["p10"] * 1e3, 3),
+                                  round(qs["p90"] * 1e3, 3)],
+            "launches": qs["runs"],
         },
         "cpu_baseline": cpu,
+        "parity_full_size": load_parity(),
         "kernels": kernels,
     }
     print(json.dumps(line), flush=True)
