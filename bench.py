@@ -130,6 +130,18 @@ def binopt_ops(d: int) -> float:
     return 1 + sort_ops(d) + 2 + 6 + 1 + 4
 
 
+def binopt_prune_ops() -> float:
+    """BinGrad-b with error feedback by the sort-free split search (buckets of
+    4096 and more): EF add (1); order-preserving key (2); bucket minimum,
+    maximum, sum and absolute sum (4); the first level's bin, fixed-point
+    value and LDS add for every element (5); the second level's range test
+    and insertion, which reaches nearly every element (7); three more levels'
+    range tests (6); the exact stage's sums below the ranges and survivor test
+    (7); threshold compare, level select, residual subtract, pack (4).  The
+    bin evaluation and the survivor sort are per bucket, not per element."""
+    return 1 + 2 + 4 + 5 + 7 + 6 + 7 + 4
+
+
 def topk_ops(d: int, K: int) -> float:
     """Top-K with quantization and error feedback: EF add and |p| key (2);
     a 31-round bitwise selection of the K-th largest key (compare + count
@@ -826,7 +838,8 @@ def suite_bingrad(torch, gq, WL, stream, tb, reps):
             ms = tb(lambda i: q(0, i), max(3, reps // 2))
             out.append(entry(f"quantize {nm}+ef d={dd} n={n}", ms,
                              quant_bytes(1, 2, dd, n, True), n,
-                             alu=binopt_ops(dd) if scheme == gq.GQ_BIN_OPT else None,
+                             alu=(None if scheme != gq.GQ_BIN_OPT else
+                                  binopt_prune_ops() if dd >= 4096 else binopt_ops(dd)),
                              extra=oracle_rate(host, dict(scheme=scheme, d=dd),
                                                True)))
             del c, m, q

@@ -21,7 +21,7 @@ OBJDIR = os.path.join(ROOT, "_build", "libgq")
 LIB = os.path.join(HERE, "libgq.so")
 SOURCES = ["api.hip", "stream_quant.hip", "sort_quant.hip", "deq.hip",
            "layer_quant.hip", "topk_quant.hip", "elias.hip",
-           "alloc_quant.hip"]
+           "alloc_quant.hip", "binopt_quant.hip"]
 ARCH = os.environ.get("GQ_OFFLOAD_ARCH", "gfx950")
 
 # -ffp-contract=off: the rounding decisions must see exactly the fp32

@@ -1,0 +1,807 @@
+// binopt_quant.hip — BinGrad-b (the two-level quantizer whose levels
+// minimise the squared error: the exact 1-D 2-means split of each bucket;
+// "Optimal Gradient Quantization Condition" review, §Proposed method) with
+// error feedback, for large buckets (d >= 4096), without sorting the bucket.
+//
+// The split that maximises F(k) = P_k^2 / k + (S - P_k)^2 / (n - k) (P_k the
+// sum of the k smallest values, S the bucket sum; the squared error is
+// sum(y^2) - F) is found by bounding F over groups of candidate splits.  One
+// workgroup owns a bucket, 32 values per thread, held as order-preserving
+// integer keys of the canonical values:
+//
+//   1. Levels of refinement.  Each level cuts the candidate key ranges (at
+//      most two; the first level one range, [min, max]) into 16 bins of equal
+//      width in key space (so a bin is a run of consecutive sorted values, and
+//      its value bounds lo, hi are exact floats).  Every thread adds its
+//      values into its lane's LDS column of the 16-bin (count, sum) histogram
+//      with one 64-bit integer atomic per value (count in the high bits, the
+//      value in fixed point below: exact, order-independent and, on this
+//      GPU, about 30x cheaper than fp32 LDS atomics; lanes of different waves
+//      share a column, which integer atomics keep exact).  Prefix sums give,
+//      at every bin edge, the split position K and the (quantized) sum P of
+//      the values below it.
+//   2. Bounds.  F at every bin edge is a lower bound LB of the optimum.  For
+//      the splits inside a bin, (k, P_k) lies in the parallelogram between
+//      the lines of slope lo and hi from the bin's first edge and into its
+//      last edge; F is jointly convex in (k, P), so its maximum over the
+//      parallelogram (clipped to 0 < k < n) is at a vertex.  A bin whose
+//      upper bound stays below LB by more than the quantization of the sums
+//      allows cannot hold the optimum and is dropped.  The surviving bins form
+//      at most two new ranges: with survivors in both previous ranges the
+//      hull of each, else the first run of surviving bins and the hull of the
+//      rest.  The first wave evaluates the bins and passes the new ranges to
+//      the others through LDS.
+//   3. When the surviving ranges hold at most 64 values, those values are
+//      gathered, sorted by the first wave, and F is evaluated exactly (fp64
+//      sums of the values below each range, fp64 prefix sums inside) at every
+//      split between distinct values in or at the edges of the ranges; the
+//      largest F wins, the smaller split on equality.
+//   4. Codes [p >= y_k*] (compared in key space), the levels as the two
+//      cluster means, the residual p - x_hat; the bucket is read once.
+//
+// A bucket whose candidates do not shrink to 64 values within ten levels
+// (values so evenly spread that many splits tie) is marked with NaN levels
+// and left untouched; the caller then runs the sort-based kernel over the
+// marked buckets only.
+#include "common.hpp"
+
+namespace gq {
+namespace {
+
+constexpr int kBins = 16;     // bins per level
+constexpr int kCap = 64;      // values the exact stage sorts (one per lane)
+constexpr int kLevels = 10;   // levels before a bucket falls back to the sort
+constexpr int kRow = 64 + 4;  // LDS words per bin row (a column per lane, padded)
+constexpr int kE = 32;        // values per thread
+
+// Order-preserving key of a canonical fp32 value (no -0) and its inverse.
+__device__ __forceinline__ uint32_t fkey(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float funkey(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+// The value of a held key, recomputed where it is used: the empty asm hides
+// that the key is loop-invariant, so the compiler does not keep a second
+// register array of values across the refinement loop.
+__device__ __forceinline__ float kval(uint32_t k) {
+  asm volatile("" : "+v"(k));
+  return funkey(k);
+}
+
+// F at split k with P the sum below it (bounds: reciprocals refined by one
+// Newton step, accurate to a few units in the last place).
+__device__ __forceinline__ double obj_fast(double P, double k, double S, double n) {
+  const double Q = S - P;
+  double r1 = __builtin_amdgcn_rcp(k);
+  r1 = __builtin_fma(r1, __builtin_fma(-k, r1, 1.0), r1);
+  double r2 = __builtin_amdgcn_rcp(n - k);
+  r2 = __builtin_fma(r2, __builtin_fma(-(n - k), r2, 1.0), r2);
+  return P * P * r1 + Q * Q * r2;
+}
+
+// F with IEEE divisions, for the exact stage.
+__device__ __forceinline__ double obj_exact(double P, double k, double S, double n) {
+  const double Q = S - P;
+  return P * P / k + Q * Q / (n - k);
+}
+
+template <int G>
+__device__ __forceinline__ uint32_t group_min_u(uint32_t v) {
+  return group_reduce<G>(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+template <int G>
+__device__ __forceinline__ uint32_t group_max_u(uint32_t v) {
+  return group_reduce<G>(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+template <int G>
+__device__ __forceinline__ double group_sum_d(double v) {
+  return group_reduce<G>(v, [](double a, double b) { return a + b; });
+}
+template <int G>
+__device__ __forceinline__ double group_max_d(double v) {
+  return group_reduce<G>(v, [](double a, double b) { return a > b ? a : b; });
+}
+
+// Group argmax of (value, key): larger value, then smaller key.
+template <int G>
+__device__ __forceinline__ void group_argmax_dk(double& v, int& key) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) {
+    const double v2 = xshfl(v, o);
+    const int k2 = xshfl(key, o);
+    if (v2 > v || (v2 == v && k2 < key)) {
+      v = v2;
+      key = k2;
+    }
+  }
+}
+
+// Sort of the kCap = G * E2 values a group holds E2 per lane (lane t:
+// positions t E2 .. t E2 + E2 - 1), ascending, bitonic in flip form: merge
+// level K compares position i with i ^ (K - 1), then with i ^ J for
+// J = K/4, ..., 1, the smaller value to the lower position.  Partners in the
+// same lane: register compare-exchanges; in another lane: one lane exchange
+// and one median of three (med3(a, b, -inf) = min, med3(a, b, +inf) = max).
+template <int E2, int MASK, bool MIRROR>
+__device__ __forceinline__ void sv_stage(float (&y)[E2], int t) {
+  constexpr int TOP = MIRROR ? (MASK + 1) / 2 : MASK;
+  if constexpr (MASK < E2) {
+#pragma unroll
+    for (int r = 0; r < E2; ++r) {
+      const int r2 = r ^ MASK;
+      if (r2 > r) {
+        const float a = y[r], b = y[r2];
+        y[r] = fminf(a, b);
+        y[r2] = fmaxf(a, b);
+      }
+    }
+  } else {
+    constexpr int LM = MASK / E2;
+    const float sel = (t & (TOP / E2)) == 0 ? -__builtin_inff() : __builtin_inff();
+    float o[E2];
+#pragma unroll
+    for (int r = 0; r < E2; ++r) o[r] = xshfl(y[MIRROR ? E2 - 1 - r : r], LM);
+#pragma unroll
+    for (int r = 0; r < E2; ++r) y[r] = __builtin_amdgcn_fmed3f(y[r], o[r], sel);
+  }
+}
+
+template <int E2, int K, int J>
+__device__ __forceinline__ void sv_halves(float (&y)[E2], int t) {
+  if constexpr (J >= 1) {
+    sv_stage<E2, J, false>(y, t);
+    sv_halves<E2, K, J / 2>(y, t);
+  }
+}
+
+template <int E2, int N, int K>
+__device__ __forceinline__ void sv_levels(float (&y)[E2], int t) {
+  sv_stage<E2, K - 1, true>(y, t);
+  sv_halves<E2, K, K / 4>(y, t);
+  if constexpr (K < N) sv_levels<E2, N, 2 * K>(y, t);
+}
+
+template <int G>
+__device__ __forceinline__ uint64_t group_lanes(int grp) {
+  if constexpr (G == 64) return ~0ull;
+  else return ((1ull << G) - 1ull) << (grp * G);
+}
+
+// Value of the lane N places lower in the same 16-lane row (0 in the row's
+// first N lanes): one DPP move, no LDS.
+template <int N>
+__device__ __forceinline__ int row_shr(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, 0x110 + N, 0xF, 0xF, false);
+}
+template <int N>
+__device__ __forceinline__ double row_shr(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)row_shr<N>((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)row_shr<N>((int)(uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// Last lane of the previous row (rows 1 and 3 for BC = 15; rows 2 and 3
+// take lane 31 for BC = 31), 0 in the other rows.
+template <int BC>
+__device__ __forceinline__ double row_bcast(double v) {
+  constexpr int ctrl = BC == 15 ? 0x142 : 0x143;
+  constexpr int rows = BC == 15 ? 0xA : 0xC;
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, ctrl, rows, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), ctrl, rows, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+template <int N>
+__device__ __forceinline__ long long row_shr(long long v) {
+  return __double_as_longlong(row_shr<N>(__longlong_as_double(v)));
+}
+__device__ __forceinline__ long long xshfl(long long v, int o) {
+  return __double_as_longlong(gq::xshfl(__longlong_as_double(v), o));
+}
+
+// Exclusive prefix over the 16 bins that sit in the lanes of a row (bin b
+// in row lane b), restarting at bin `first`.
+template <typename V>
+__device__ __forceinline__ V bin_exclusive(V own, int b, int first) {
+  V v = row_shr<1>(own);
+  if (b <= first) v = V(0);
+  V t = row_shr<1>(v);
+  if (b - 1 >= first) v = v + t;
+  t = row_shr<2>(v);
+  if (b - 2 >= first) v = v + t;
+  t = row_shr<4>(v);
+  if (b - 4 >= first) v = v + t;
+  t = row_shr<8>(v);
+  if (b - 8 >= first) v = v + t;
+  return v;
+}
+
+// The value row lane `idx` holds, in every lane of the row.
+template <typename V>
+__device__ __forceinline__ V row_pick(V v, int b, int idx) {
+  V x = b == idx ? v : V(0);
+  x = x + xshfl(x, 8);
+  x = x + xshfl(x, 4);
+  x = x + xshfl(x, 2);
+  x = x + xshfl(x, 1);
+  return x;
+}
+
+// Inclusive prefix over the G lanes of a group (G = 16, 32, 64).
+template <int G>
+__device__ __forceinline__ double group_inclusive(double v) {
+  v = v + row_shr<1>(v);
+  v = v + row_shr<2>(v);
+  v = v + row_shr<4>(v);
+  v = v + row_shr<8>(v);
+  if constexpr (G >= 32) v = v + row_bcast<15>(v);
+  if constexpr (G >= 64) v = v + row_bcast<31>(v);
+  return v;
+}
+
+template <int G>
+__device__ __forceinline__ int group_min_i(int v) {
+  return group_reduce<G>(v, [](int a, int b) { return a < b ? a : b; });
+}
+
+template <int D>
+__global__ __launch_bounds__(D / kE, D / kE == 256 ? 3 : 1) void k_binopt_block(
+    int64_t n, const float* __restrict__ g, float* __restrict__ e,
+    uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes) {
+  constexpr int T = D / kE;
+  constexpr int E = kE;
+  constexpr int NQ = E / 4;
+  constexpr int NW = T / 64;
+  struct Shared {
+    // per bin, one column per lane: count << 48 plus the fixed-point sum
+    unsigned long long h[kBins * kRow];
+    float v[kCap];             // survivors
+    double rd[4][NW];          // per-wave partials: S, A, sums below the ranges
+    uint32_t ru[2][NW];        // per-wave key minima / maxima
+    int cnt;                   // survivors gathered
+    uint32_t kthr;             // exact stage result: threshold key,
+    float la, lb;              //   levels,
+    int flag;                  //   0 done, 1 recompute sums, 2 fall back
+    double ks;                 //   split position
+    double s2[4][NW];          // compensated cluster sums (rare path)
+    // the next level's ranges, from the first wave
+    uint32_t nlo[2], nhi[2];
+    int nk[2], nc[2], nst, nnr;
+    long long nq[2];
+    double nlb;
+  };
+  __shared__ __align__(16) Shared sh;
+
+  const int tid = threadIdx.x, wv = tid >> 6, wl = tid & 63;
+  const int b = wl & 15;     // the bin of this lane in the bin stages
+  const int part = wl >> 4;  // which 16 columns' partials it sums
+  const int64_t bucket = blockIdx.x;
+  const int64_t base = bucket * D;
+  const int nj = (int)((n - base) < D ? (n - base) : D);
+  const bool full = nj == D;
+  auto valid = [&](int m) { return full || 4 * (tid + T * (m / 4)) + (m % 4) < nj; };
+
+  // ---- load p = g (+ e); thread t holds the float4s t, t + T, ...; keep
+  //      the keys of the canonical values (-0 -> +0) and which were -0 -----
+  uint32_t kk[E];
+  uint32_t negz = 0u;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int64_t i = base + 4 * (tid + (int64_t)T * q);
+    float4 x = full ? load4_nt(g + i) : load4(g, i, n);
+    if (e != nullptr) {
+      const float4 r = full ? load4_nt(e + i) : load4(e, i, n);
+      x.x = x.x + r.x;
+      x.y = x.y + r.y;
+      x.z = x.z + r.z;
+      x.w = x.w + r.w;
+    }
+    const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float v = xs[c];
+      if (v == 0.f && __float_as_uint(v) != 0u) negz |= 1u << (4 * q + c);
+      kk[4 * q + c] = fkey(v == 0.f ? 0.f : v);
+    }
+  }
+
+  // ---- bucket statistics: key range, S = sum, A = sum |p| (fp64; wave
+  //      partials combined in wave order) ---------------------------------
+  uint32_t kmn = 0xffffffffu, kmx = 0u;
+  double S = 0.0, A = 0.0;
+#pragma unroll
+  for (int m = 0; m < E; ++m) {
+    if (valid(m)) {
+      const float x = kval(kk[m]);
+      kmn = kk[m] < kmn ? kk[m] : kmn;
+      kmx = kk[m] > kmx ? kk[m] : kmx;
+      S = S + (double)x;
+      A = A + (double)fabsf(x);
+    }
+  }
+  kmn = group_min_u<64>(kmn);
+  kmx = group_max_u<64>(kmx);
+  S = group_sum_d<64>(S);
+  A = group_sum_d<64>(A);
+  if (wl == 0) {
+    sh.ru[0][wv] = kmn;
+    sh.ru[1][wv] = kmx;
+    sh.rd[0][wv] = S;
+    sh.rd[1][wv] = A;
+  }
+  __syncthreads();
+  kmn = sh.ru[0][0];
+  kmx = sh.ru[1][0];
+  S = sh.rd[0][0];
+  A = sh.rd[1][0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    kmn = sh.ru[0][w] < kmn ? sh.ru[0][w] : kmn;
+    kmx = sh.ru[1][w] > kmx ? sh.ru[1][w] : kmx;
+    S = S + sh.rd[0][w];
+    A = A + sh.rd[1][w];
+  }
+  const double dn = (double)nj;
+
+  // The histogram sums are fixed point: value x adds q = trunc(x 2^f), with
+  // 2^f chosen so that |q| < 2^30 for every value (so any sum of at most
+  // 2^16 of them stays below 2^47 and fits under the count, which sits from
+  // bit 48).  The sum of the quantized values below any split is then exact,
+  // and |P_q - P| < nj 2^-f =: dP.  F moves by at most 2 |a - b| d + 4 d^2
+  // when P moves by d, and |a - b| <= max - min.
+  const float amax = fmaxf(fabsf(funkey(kmn)), fabsf(funkey(kmx)));
+  int ex = 0;
+  frexpf(amax, &ex);  // amax < 2^ex
+  const int fsh = 30 - ex;
+  const float fscale = ldexpf(1.0f, fsh);
+  const double funit = ldexp(1.0, -fsh);  // value of one fixed-point unit
+  const double dP = dn * funit;
+  const double span = (double)funkey(kmx) - (double)funkey(kmn);
+  const double errF = 2.0 * span * dP + 4.0 * dP * dP;
+
+  // candidate ranges (keys, inclusive), the split position K and the
+  // fixed-point sum below each range start, and the count in each (the same
+  // in every thread)
+  int nr = 1;
+  uint32_t rlo0 = kmn, rhi0 = kmx, rlo1 = 0u, rhi1 = 0u;
+  int rk0 = 0, rk1 = 0, rc0 = nj, rc1 = 0;
+  long long rq0 = 0, rq1 = 0;
+  double LB = -1.0;
+
+  const bool split_exists = kmn < kmx;
+  // 0: refining, 1: exact stage, 2: fall back to the sort.  Buckets whose
+  // scale 2^f would leave fp32's range go to the sort directly.
+  const bool sane = amax < 0x1p90f && amax > 0x1p-90f;
+  auto packed = [&](uint32_t k) {
+    const long long q = (long long)(int)(kval(k) * fscale);
+    return (unsigned long long)(q + (1ll << 48));
+  };
+  int state = !split_exists ? 1 : (nj <= kCap ? 1 : (sane ? 0 : 2));
+
+  for (int lev = 0; lev < kLevels && state == 0; ++lev) {
+    const int nbr = kBins / nr;  // bins per range
+    // shift of each range: (hi - lo) >> sh < nbr
+    const uint32_t span0 = rhi0 - rlo0, span1 = rhi1 - rlo1;
+    const int sh0 = span0 < (uint32_t)nbr ? 0 : 32 - __clz((int)(span0 / (uint32_t)nbr));
+    const int sh1 = span1 < (uint32_t)nbr ? 0 : 32 - __clz((int)(span1 / (uint32_t)nbr));
+    // clear the histogram (after every wave read the previous level's)
+    for (int i = tid; i < kBins * 64; i += T) sh.h[(i >> 6) * kRow + (i & 63)] = 0ull;
+    __syncthreads();
+    if (lev == 0) {
+      // one range, [min, max]: every value has a bin
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        if (!valid(m)) continue;
+        const int bin = (int)((kk[m] - rlo0) >> sh0);
+        atomicAdd(&sh.h[bin * kRow + wl], packed(kk[m]));
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        const uint32_t k = kk[m];
+        const bool in0 = k - rlo0 <= span0;
+        const bool in1 = nr == 2 && k - rlo1 <= span1;
+        if (!valid(m) || !(in0 || in1)) continue;
+        const int bin = in0 ? (int)((k - rlo0) >> sh0) : nbr + (int)((k - rlo1) >> sh1);
+        atomicAdd(&sh.h[bin * kRow + wl], packed(k));
+      }
+    }
+    __syncthreads();
+    if (wv == 0) {
+    // ---- per-bin totals (row lane b holds bin b, in every row) -----------
+    long long bq = 0;
+    int bc = 0;
+    {
+      const ulonglong2* h2 = reinterpret_cast<const ulonglong2*>(sh.h + b * kRow + part * 16);
+      unsigned long long tot = 0ull;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const ulonglong2 v = h2[t];
+        tot += v.x + v.y;
+      }
+      long long st = (long long)tot;
+      st += xshfl(st, 16);
+      st += xshfl(st, 32);
+      bc = (int)((st + (1ll << 47)) >> 48);
+      bq = st - ((long long)bc << 48);
+    }
+    // ---- edges: K and P at the bin's first edge --------------------------
+    const int r = b / nbr;      // range of this bin
+    const int first = r * nbr;  // its first bin
+    const int j = b - first;    // bin within the range
+    const int exK = bin_exclusive(bc, b, first);
+    const long long exQ = bin_exclusive(bq, b, first);
+    const uint32_t rlo = r == 0 ? rlo0 : rlo1, rhi = r == 0 ? rhi0 : rhi1;
+    const int shr = r == 0 ? sh0 : sh1;
+    const int Kb = (r == 0 ? rk0 : rk1) + exK;
+    const long long Qb = (r == 0 ? rq0 : rq1) + exQ;
+    const double Pb = (double)Qb * funit;
+    const double bs = (double)bq * funit;
+    const uint64_t klo64 = (uint64_t)rlo + ((uint64_t)j << shr);
+    uint64_t khi64 = (uint64_t)rlo + ((uint64_t)(j + 1) << shr) - 1;
+    if (khi64 > rhi) khi64 = rhi;
+    const bool live = klo64 <= (uint64_t)rhi && bc > 0;
+    const uint32_t klo = (uint32_t)(live ? klo64 : rlo);
+    const uint32_t khi = (uint32_t)(live ? khi64 : rlo);
+    // lower bound: F at both edges of every non-empty bin
+    double lb = -1.0;
+    if (live) {
+      if (Kb > 0) lb = obj_fast(Pb, (double)Kb, S, dn);
+      if (Kb + bc < nj) {
+        const double f = obj_fast(Pb + bs, (double)(Kb + bc), S, dn);
+        lb = f > lb ? f : lb;
+      }
+    }
+    LB = fmax(LB, group_max_d<16>(lb));
+    // upper bound: vertices of the clipped parallelogram
+    double ub = -1.0;
+    if (live) {
+      const double lo = (double)funkey(klo), hi = (double)funkey(khi);
+      const double c = (double)bc;
+      const double j0 = Kb == 0 ? 1.0 : 0.0;
+      const double j1 = Kb + bc == nj ? c - 1.0 : c;
+      if (j0 <= j1) {
+        auto Lw = [&](double jj) { return Pb + fmax(jj * lo, bs - (c - jj) * hi); };
+        auto Up = [&](double jj) { return Pb + fmin(jj * hi, bs - (c - jj) * lo); };
+        auto at = [&](double jj, double P) {
+          const double f = obj_fast(P, (double)Kb + jj, S, dn);
+          ub = f > ub ? f : ub;
+        };
+        at(j0, Lw(j0));
+        at(j0, Up(j0));
+        at(j1, Lw(j1));
+        at(j1, Up(j1));
+        if (hi > lo) {
+          const double jl = (c * hi - bs) / (hi - lo);  // lower boundary's corner
+          const double ju = (bs - c * lo) / (hi - lo);  // upper boundary's corner
+          if (jl > j0 && jl < j1) at(jl, Pb + jl * lo);
+          if (ju > j0 && ju < j1) at(ju, Pb + ju * hi);
+        }
+      }
+    }
+    const double slack = 1e-12 * fabs(LB);
+    const bool keep = live && ub + errF + slack >= LB - errF - slack;
+    // ---- survivors -> at most two ranges (row 0's bits) -------------------
+    const uint32_t mask = (uint32_t)(__ballot(keep) & 0xFFFFull);
+    if (mask == 0u) {
+      state = 2;
+    } else {
+      const uint32_t m0 = mask & ((1u << nbr) - 1u);
+      const uint32_t m1 = nr == 2 ? mask >> nbr : 0u;
+      int a0, a1, b0, b1;
+      if (m0 != 0u && m1 != 0u) {
+        a0 = __builtin_ctz(m0);
+        a1 = 31 - __builtin_clz(m0);
+        b0 = nbr + __builtin_ctz(m1);
+        b1 = nbr + 31 - __builtin_clz(m1);
+      } else {
+        a0 = __builtin_ctz(mask);
+        const uint32_t run = ~(mask >> a0);  // first zero after the run
+        a1 = a0 + __builtin_ctz(run) - 1;
+        const uint32_t rest = mask >> (a1 + 1);
+        b0 = rest ? a1 + 1 + __builtin_ctz(rest) : -1;
+        b1 = 31 - __builtin_clz(mask);
+      }
+      auto bin_lo = [&](int bn) {
+        const int rr = bn / nbr;
+        return (rr == 0 ? rlo0 : rlo1) + (uint32_t)((uint64_t)(bn - rr * nbr) << (rr == 0 ? sh0 : sh1));
+      };
+      auto bin_hi = [&](int bn) {
+        const int rr = bn / nbr;
+        const uint64_t h = (uint64_t)(rr == 0 ? rlo0 : rlo1) +
+                           ((uint64_t)(bn - rr * nbr + 1) << (rr == 0 ? sh0 : sh1)) - 1;
+        const uint32_t top = rr == 0 ? rhi0 : rhi1;
+        return h > top ? top : (uint32_t)h;
+      };
+      // K at a first edge and at a last edge, packed (both <= 2^15, so the
+      // pair fits in 32 unsigned bits)
+      const uint32_t endK = (uint32_t)(Kb + bc);
+      const uint32_t pa =
+          row_pick((b == a0 ? (uint32_t)Kb : 0u) + (b == a1 ? endK << 16 : 0u), b, b);
+      const long long qA = row_pick(Qb, b, a0);
+      const int nk0 = (int)(pa & 0xFFFFu);
+      const int nc0 = (int)(pa >> 16) - nk0;
+      int nk1 = 0, nc1 = 0;
+      long long nq1 = 0;
+      const bool two = b0 >= 0;
+      if (two) {
+        const uint32_t pb =
+            row_pick((b == b0 ? (uint32_t)Kb : 0u) + (b == b1 ? endK << 16 : 0u), b, b);
+        nk1 = (int)(pb & 0xFFFFu);
+        nc1 = (int)(pb >> 16) - nk1;
+        nq1 = row_pick(Qb, b, b0);
+      }
+      const uint32_t nlo0 = bin_lo(a0), nhi0 = bin_hi(a1);
+      const uint32_t nlo1 = two ? bin_lo(b0) : 0u, nhi1 = two ? bin_hi(b1) : 0u;
+      rlo0 = nlo0;
+      rhi0 = nhi0;
+      rk0 = nk0;
+      rq0 = qA;
+      rc0 = nc0;
+      nr = two ? 2 : 1;
+      rlo1 = nlo1;
+      rhi1 = nhi1;
+      rk1 = nk1;
+      rq1 = nq1;
+      rc1 = nc1;
+      if (rc0 + rc1 <= kCap) state = 1;
+      else if (lev + 1 == kLevels) state = 2;
+    }
+    if (wl == 0) {
+      sh.nlo[0] = rlo0;
+      sh.nhi[0] = rhi0;
+      sh.nk[0] = rk0;
+      sh.nq[0] = rq0;
+      sh.nc[0] = rc0;
+      sh.nlo[1] = rlo1;
+      sh.nhi[1] = rhi1;
+      sh.nk[1] = rk1;
+      sh.nq[1] = rq1;
+      sh.nc[1] = rc1;
+      sh.nnr = nr;
+      sh.nst = state;
+      sh.nlb = LB;
+    }
+    }  // first wave
+    __syncthreads();
+    rlo0 = sh.nlo[0];
+    rhi0 = sh.nhi[0];
+    rk0 = sh.nk[0];
+    rq0 = sh.nq[0];
+    rc0 = sh.nc[0];
+    rlo1 = sh.nlo[1];
+    rhi1 = sh.nhi[1];
+    rk1 = sh.nk[1];
+    rq1 = sh.nq[1];
+    rc1 = sh.nc[1];
+    nr = sh.nnr;
+    state = sh.nst;
+    LB = sh.nlb;
+    __syncthreads();  // the next level clears the histogram
+  }
+  if (state == 0) state = 2;
+
+  if (state == 2) {
+    // not resolved: NaN levels mark the bucket for the sort-based kernel;
+    // codes and residual are left to it
+    if (tid == 0) {
+      meta[2 * bucket + 0] = __builtin_nanf("");
+      meta[2 * bucket + 1] = __builtin_nanf("");
+    }
+    return;
+  }
+
+  // ---- exact stage over the values of the ranges --------------------------
+  float la, lb_;
+  uint32_t kthr;
+  if (!split_exists) {
+    la = lb_ = funkey(kmn);
+    kthr = 0xffffffffu;  // every code 0 (keys of finite values are below
+                         // 0xff800000)
+  } else {
+    auto in_ranges = [&](uint32_t k) {
+      return (k - rlo0 <= rhi0 - rlo0) || (nr == 2 && k - rlo1 <= rhi1 - rlo1);
+    };
+    // this wave's survivors, then one LDS reservation per wave
+    int wcnt = 0;
+    double p0 = 0.0, p1 = 0.0;  // sums below each range start (fp64)
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+      const bool v = valid(m);
+      const uint32_t k = kk[m];
+      const double dx = (double)kval(k);
+      if (v && k < rlo0) p0 = p0 + dx;
+      if (v && nr == 2 && k < rlo1) p1 = p1 + dx;
+      wcnt += (int)__builtin_popcountll(__ballot(v && in_ranges(k)));
+    }
+    p0 = group_sum_d<64>(p0);
+    p1 = group_sum_d<64>(p1);
+    if (tid == 0) sh.cnt = 0;
+    if (wl == 0) {
+      sh.rd[2][wv] = p0;
+      sh.rd[3][wv] = p1;
+    }
+    __syncthreads();
+    int wbase = 0;
+    if (wl == 0 && wcnt > 0) wbase = atomicAdd(&sh.cnt, wcnt);
+    wbase = __builtin_amdgcn_readfirstlane(wbase);
+    int run = 0;
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+      const uint32_t k = kk[m];
+      const bool in = valid(m) && in_ranges(k);
+      const uint64_t bal = __ballot(in);
+      const int pos = wbase + run + (int)__builtin_popcountll(bal & ((1ull << wl) - 1ull));
+      if (in && pos < kCap) sh.v[pos] = kval(k);
+      run += (int)__builtin_popcountll(bal);
+    }
+    __syncthreads();
+    p0 = sh.rd[2][0];
+    p1 = sh.rd[3][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      p0 = p0 + sh.rd[2][w];
+      p1 = p1 + sh.rd[3][w];
+    }
+    const int cnt = sh.cnt;
+    if (wv == 0) {
+      // one survivor per lane, sorted
+      float y[1];
+      y[0] = wl < cnt ? sh.v[wl] : __builtin_inff();
+      sv_levels<1, kCap, 2>(y, wl);
+      const double own = wl < cnt ? (double)y[0] : 0.0;
+      const double pre0 = group_inclusive<64>(own) - own;  // sum before this position
+      const int off1 = rc0;                                  // start of range 1
+      const double pre_off1 = group_sum_d<64>(wl == off1 ? pre0 : 0.0);
+      const double pre_end = group_sum_d<64>(own);         // all survivors
+      const float y_prev = __shfl_up(y[0], 1, 64);
+      double bestF = -1.0;
+      int bestK = 0x7fffffff;
+      uint32_t bestT = 0u;
+      double bestP = 0.0;
+      auto consider = [&](int k, double P, uint32_t kt) {
+        if (k <= 0 || k >= nj) return;
+        const double f = obj_exact(P, (double)k, S, dn);
+        if (f > bestF || (f == bestF && k < bestK)) {
+          bestF = f;
+          bestK = k;
+          bestT = kt;
+          bestP = P;
+        }
+      };
+      if (wl < cnt) {
+        const bool r1 = wl >= off1;
+        const int start = r1 ? off1 : 0;
+        const bool distinct = wl == start || y_prev < y[0];
+        const int k = (r1 ? rk1 : rk0) + (wl - start);
+        const double P = (r1 ? p1 : p0) + (pre0 - (r1 ? pre_off1 : 0.0));
+        if (distinct) consider(k, P, fkey(y[0]));
+        // the split after the range's last value
+        const bool last = wl + 1 == (r1 ? cnt : off1);
+        if (last) {
+          const int k2 = r1 ? rk1 + rc1 : rk0 + rc0;
+          const double P2 = (r1 ? p1 : p0) + ((pre0 + own) - (r1 ? pre_off1 : 0.0));
+          consider(k2, P2, (r1 ? rhi1 : rhi0) + 1u);
+        }
+      }
+      (void)pre_end;
+      double gF = bestF;
+      int gK = bestK;
+      group_argmax_dk<64>(gF, gK);
+      const int win = group_min_i<64>(bestK == gK && bestF == gF ? wl : 64);
+      const uint32_t kt = (uint32_t)group_sum_i<64>(wl == win ? (int)bestT : 0);
+      const double Ps = group_sum_d<64>(wl == win ? bestP : 0.0);
+      if (wl == 0) {
+        if (gF < 0.0 || cnt > kCap) {
+          sh.flag = 2;  // no candidate (cannot happen when the bounds hold)
+        } else {
+          const double ks = (double)gK;
+          sh.kthr = kt;
+          sh.ks = ks;
+          sh.la = (float)(Ps / ks);
+          sh.lb = (float)((S - Ps) / (dn - ks));
+          // cluster sums with cancellation beyond the plain fp64 sums'
+          // accuracy (rare): recompute both sides with compensated sums
+          const double tiny = 0x1p-20 * A;
+          sh.flag = (fabs(Ps) < tiny || fabs(S - Ps) < tiny) ? 1 : 0;
+        }
+      }
+    }
+    __syncthreads();
+    const int flag = sh.flag;
+    if (flag == 2) {
+      if (tid == 0) {
+        meta[2 * bucket + 0] = __builtin_nanf("");
+        meta[2 * bucket + 1] = __builtin_nanf("");
+      }
+      return;
+    }
+    kthr = sh.kthr;
+    la = sh.la;
+    lb_ = sh.lb;
+    if (flag == 1) {
+      Sum2 lo{0.0, 0.0}, hi{0.0, 0.0};
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        if (!valid(m)) continue;
+        const double x = (double)kval(kk[m]);
+        if (kk[m] < kthr) two_sum_add(lo, x);
+        else two_sum_add(hi, x);
+      }
+      lo = group_sum2<64>(lo);
+      hi = group_sum2<64>(hi);
+      if (wl == 0) {
+        sh.s2[0][wv] = lo.s;
+        sh.s2[1][wv] = lo.c;
+        sh.s2[2][wv] = hi.s;
+        sh.s2[3][wv] = hi.c;
+      }
+      __syncthreads();
+      Sum2 L{sh.s2[0][0], sh.s2[1][0]}, H{sh.s2[2][0], sh.s2[3][0]};
+#pragma unroll
+      for (int w = 1; w < NW; ++w) {
+        L = two_sum_merge(L, Sum2{sh.s2[0][w], sh.s2[1][w]});
+        H = two_sum_merge(H, Sum2{sh.s2[2][w], sh.s2[3][w]});
+      }
+      const double ks = sh.ks;
+      la = (float)((L.s + L.c) / ks);
+      lb_ = (float)((H.s + H.c) / (dn - ks));
+    }
+  }
+  if (tid == 0) {
+    meta[2 * bucket + 0] = la;
+    meta[2 * bucket + 1] = lb_;
+  }
+  if (codes == nullptr) return;  // levels only
+
+  // ---- codes, packing, residual (element order) ---------------------------
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int64_t i0 = base + 4 * (tid + (int64_t)T * q);
+    uint32_t field = 0u;
+    float r[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int m = 4 * q + c;
+      const uint32_t code = (valid(m) && kk[m] >= kthr) ? 1u : 0u;
+      field |= code << c;
+      const float pv = (negz >> m) & 1u ? -0.0f : kval(kk[m]);
+      r[c] = pv - (code ? lb_ : la);
+    }
+    store_chunk<1, 4>(codes, i0, wl, field, code_bytes);
+    if (e != nullptr && i0 < n) {
+      if (full) store4_nt(e + i0, make_float4(r[0], r[1], r[2], r[3]));
+      else store4(e, i0, n, make_float4(r[0], r[1], r[2], r[3]));
+    }
+  }
+}
+
+template <int D>
+int launch_one(int64_t n, const float* g, float* e, uint8_t* codes, float* meta,
+               int64_t code_bytes, hipStream_t st) {
+  const int64_t nb = (n + D - 1) / D;
+  hipLaunchKernelGGL((k_binopt_block<D>), dim3((uint32_t)nb), dim3(D / kE), 0, st,
+                     n, g, e, codes, meta, code_bytes);
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+bool binopt_prune_supported(int d) { return d >= 4096 && d <= 32768; }
+
+int launch_binopt_prune(int d, int64_t n, const float* g, float* e,
+                        uint8_t* codes, float* meta, int64_t code_bytes,
+                        hipStream_t st) {
+  switch (d) {
+    case 4096: return launch_one<4096>(n, g, e, codes, meta, code_bytes, st);
+    case 8192: return launch_one<8192>(n, g, e, codes, meta, code_bytes, st);
+    case 16384: return launch_one<16384>(n, g, e, codes, meta, code_bytes, st);
+    case 32768: return launch_one<32768>(n, g, e, codes, meta, code_bytes, st);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gq

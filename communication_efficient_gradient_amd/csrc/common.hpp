@@ -604,6 +604,12 @@ int launch_stream_quant(const LaunchDesc& L, int64_t n, const float* g,
 int launch_sort_quant(const LaunchDesc& L, int64_t n, const float* g, float* e,
                       uint64_t seed, uint32_t step, uint8_t* codes, float* meta,
                       int64_t code_bytes, hipStream_t st);
+// BinGrad-b without sorting the bucket (bucket sizes 128 .. 2048); buckets it
+// leaves unresolved get NaN levels and untouched codes and residuals.
+bool binopt_prune_supported(int d);
+int launch_binopt_prune(int d, int64_t n, const float* g, float* e,
+                        uint8_t* codes, float* meta, int64_t code_bytes,
+                        hipStream_t st);
 int launch_deq_acc(const LaunchDesc& L, int64_t n, int W, const PayloadPtrs& pp,
                    float alpha, float beta, float* out, int64_t code_bytes,
                    hipStream_t st);

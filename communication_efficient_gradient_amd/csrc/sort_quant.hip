@@ -259,7 +259,7 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
     int64_t n, const float* __restrict__ g, float* __restrict__ e,
     uint32_t k0, uint32_t k1, uint32_t step, int L, int flags, float clip_sigma,
     uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes,
-    uint32_t A4, int W) {
+    uint32_t A4, int W, int redo) {
   constexpr int T = SortCfg<D>::T;
   constexpr int E = SortCfg<D>::E;
   __shared__ float sorted[D];
@@ -267,6 +267,11 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
 
   const int tid = threadIdx.x;
   const int64_t bucket = blockIdx.x;
+  // redo: only the buckets the sort-free BinGrad-b kernel marked with NaN
+  // levels (block-uniform, before any barrier)
+  if constexpr (SCHEME == BIN_OPT) {
+    if (redo && meta[2 * bucket] == meta[2 * bucket]) return;
+  }
   const int64_t base = bucket * D;
   const int nj = (int)((n - base) < D ? (n - base) : D);
 
@@ -768,7 +773,7 @@ void k_wave_sort_quant(
     int64_t n, int64_t nb, const float* __restrict__ g, float* __restrict__ e,
     uint32_t k0, uint32_t k1, uint32_t step, int L, int flags, float clip_sigma,
     uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes,
-    uint32_t A4, int W) {
+    uint32_t A4, int W, int redo) {
   constexpr int E = WaveCfg<D>::E;
   constexpr int G = WaveCfg<D>::G;
   constexpr int VEC = 4;
@@ -777,6 +782,11 @@ void k_wave_sort_quant(
   const int64_t bucket =
       (int64_t)blockIdx.x * (kGroupThreads / G) + threadIdx.x / G;
   if (bucket >= nb) return;  // whole groups leave together
+  // redo: only the buckets the sort-free BinGrad-b kernel marked with NaN
+  // levels (group-uniform)
+  if constexpr (SCHEME == BIN_OPT) {
+    if (redo && meta[2 * bucket] == meta[2 * bucket]) return;
+  }
   const int64_t base = bucket * D;
   const int nj = (int)((n - base) < D ? (n - base) : D);
 
@@ -1232,7 +1242,7 @@ template <int SCHEME, int BITS, int D>
 int launch_sort_one(int64_t n, const float* g, float* e, uint64_t seed,
                     uint32_t step, int L, int flags, float clip_sigma,
                     uint8_t* codes, float* meta, int64_t code_bytes,
-                    uint32_t A4, int W, hipStream_t st) {
+                    uint32_t A4, int W, int redo, hipStream_t st) {
   const int64_t nb = (n + D - 1) / D;
   if (BITS == 0 && D < 512) return (int)hipErrorInvalidValue;  // dense: d >= 512
   if constexpr (D <= 512) {
@@ -1246,19 +1256,20 @@ int launch_sort_one(int64_t n, const float* g, float* e, uint64_t seed,
                            dim3((uint32_t)blocks), dim3(kGroupThreads), 0, st,
                            n, nb, g, e, (uint32_t)seed, (uint32_t)(seed >> 32),
                            step, L, flags, clip_sigma, codes, meta, code_bytes,
-                           A4, W);
+                           A4, W, redo);
       }
     }
     if (!bisect)
       hipLaunchKernelGGL((k_wave_sort_quant<SCHEME, BITS, D, false>),
                          dim3((uint32_t)blocks), dim3(kGroupThreads), 0, st, n,
                          nb, g, e, (uint32_t)seed, (uint32_t)(seed >> 32), step,
-                         L, flags, clip_sigma, codes, meta, code_bytes, A4, W);
+                         L, flags, clip_sigma, codes, meta, code_bytes, A4, W,
+                         redo);
   } else {
     hipLaunchKernelGGL((k_sort_quant<SCHEME, BITS, D>), dim3((uint32_t)nb),
                        dim3(SortCfg<D>::T), 0, st, n, g, e, (uint32_t)seed,
                        (uint32_t)(seed >> 32), step, L, flags, clip_sigma, codes,
-                       meta, code_bytes, A4, W);
+                       meta, code_bytes, A4, W, redo);
   }
   return (int)hipGetLastError();
 }
@@ -1267,12 +1278,12 @@ template <int SCHEME, int BITS>
 int sort_dispatch_d(int d, int64_t n, const float* g, float* e, uint64_t seed,
                     uint32_t step, int L, int flags, float clip_sigma,
                     uint8_t* codes, float* meta, int64_t code_bytes,
-                    uint32_t A4, int W, hipStream_t st) {
+                    uint32_t A4, int W, hipStream_t st, int redo = 0) {
 #define GQ_SCASE(D_)                                                        \
   case D_:                                                                  \
     return launch_sort_one<SCHEME, BITS, D_>(n, g, e, seed, step, L, flags, \
                                              clip_sigma, codes, meta,       \
-                                             code_bytes, A4, W, st);
+                                             code_bytes, A4, W, redo, st);
   switch (d) {
     GQ_SCASE(64)
     GQ_SCASE(128)
@@ -1296,9 +1307,18 @@ int launch_sort_quant(const LaunchDesc& L, int64_t n, const float* g, float* e,
                       uint64_t seed, uint32_t step, uint8_t* codes, float* meta,
                       int64_t code_bytes, hipStream_t st) {
   const int flags = L.flags & (GQ_FLAG_CLIP | GQ_FLAG_NEAREST | GQ_FLAG_BISECT);
-  if (L.scheme == BIN_OPT)
+  if (L.scheme == BIN_OPT) {
+    // sort-free split search where it is built, then the sort-based kernel
+    // over the buckets it leaves unresolved (marked by NaN levels)
+    if (binopt_prune_supported(L.d)) {
+      const int rc = launch_binopt_prune(L.d, n, g, e, codes, meta, code_bytes, st);
+      if (rc != 0) return rc;
+      return sort_dispatch_d<BIN_OPT, 1>(L.d, n, g, e, seed, step, 2, 0, 0.f,
+                                         codes, meta, code_bytes, 0u, 0, st, 1);
+    }
     return sort_dispatch_d<BIN_OPT, 1>(L.d, n, g, e, seed, step, 2, 0, 0.f,
                                        codes, meta, code_bytes, 0u, 0, st);
+  }
 #define GQ_ORQ(BITS)                                                          \
   sort_dispatch_d<ORQ, BITS>(L.d, n, g, e, seed, step, L.L, flags,            \
                              L.clip_sigma, codes, meta, code_bytes, L.A4, L.W, \

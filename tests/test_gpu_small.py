@@ -145,6 +145,33 @@ def test_two_level_ragged_and_degenerate(dev, n):
         check_quantize(dev, O.Desc(scheme, 64), g, np.zeros_like(g))
 
 
+@pytest.mark.parametrize("d", [4096, 32768])
+def test_binopt_large_bucket_edge_cases(dev, d):
+    """Large BinGrad-b buckets that take every branch of the sort-free split
+    search: no split (one value), signed zeros, small integers (ties the
+    search cannot narrow: the bucket goes to the sort-based path), cluster
+    sums that cancel (the compensated recomputation), scales outside the
+    fixed-point range (straight to the sort), evenly spread values, and a
+    ragged tail of more than 64 values."""
+    rng = np.random.default_rng(d)
+    zeros = np.where(rng.random(d) < 0.5, -0.0, 0.0).astype(np.float32)
+    zeros[rng.choice(d, 40, replace=False)] = rng.standard_normal(40).astype(np.float32)
+    v = rng.standard_normal(d // 2 - 8).astype(np.float32)
+    cancel = np.concatenate([v, -v, np.full(16, 100.0, np.float32)])
+    cancel[0] += np.float32(1e-3)
+    spread = np.linspace(-1, 1, d, dtype=np.float32)
+    parts = [np.full(d, 2.5, np.float32), zeros,
+             rng.integers(-3, 4, d).astype(np.float32),
+             rng.permutation(cancel),
+             (rng.standard_normal(d) * 1e30).astype(np.float32),
+             (rng.standard_normal(d) * 1e-30).astype(np.float32),
+             rng.permutation(spread),
+             rng.standard_normal(100).astype(np.float32)]
+    g = np.concatenate(parts)
+    check_quantize(dev, O.Desc(O.BIN_OPT, d), g, None)
+    check_quantize(dev, O.Desc(O.BIN_OPT, d), g, np.zeros_like(g), step=1)
+
+
 @pytest.mark.parametrize("d", [64, 128, 256, 512, 1024, 2048, 4096])
 @pytest.mark.parametrize("L", [2, 3, 5, 9, 16])
 @pytest.mark.parametrize("clip", [0, 1])
