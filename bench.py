@@ -57,7 +57,11 @@ KERNEL_SOURCES = {
                        "communication_efficient_gradient_amd/build.py"],
     "k_deq_acc": [_CSRC + "common.hpp", _CSRC + "deq.hip",
                   "communication_efficient_gradient_amd/build.py"],
+    "bin_opt": [_CSRC + "common.hpp", _CSRC + "sort_quant.hip",
+                _CSRC + "binopt_quant.hip",
+                "communication_efficient_gradient_amd/build.py"],
 }
+BINGRAD_BUCKETS = (128, 512, 2048, 8192, 32768)
 COPY_BYTES = 1 << 29           # known-size copy for counter calibration
 
 
@@ -192,6 +196,8 @@ class Headline:
 
     KEY = "int8_ef_d512_n256M"
     AGG_KEY = "int8_w8_n256M:aggregate"
+    KERNEL = "k_stream_quant<0, 8, 128, 1>"      # its kernels in the counter runs
+    AGG_KERNEL = "k_deq_acc_wide<0, 8, 8, true>"
     CPU_PREFIX = 1 << 25        # elements of each worker kept for the oracle
 
     def __init__(self, torch, gq, WL, stream):
@@ -830,7 +836,7 @@ def suite_bingrad(torch, gq, WL, stream, tb, reps):
     n = g.numel()
     e = torch.zeros_like(g)
     for scheme, nm in ((gq.GQ_BIN_OPT, "bin_opt"), (gq.GQ_BIN_SIGN, "bin_sign")):
-        for dd in (128, 512, 2048, 8192, 32768):
+        for dd in BINGRAD_BUCKETS:
             d = gq.desc(scheme, dd)
             c, m = gq.alloc_payload(d, n)
             e.zero_()
@@ -842,6 +848,12 @@ def suite_bingrad(torch, gq, WL, stream, tb, reps):
                                   binopt_prune_ops() if dd >= 4096 else binopt_ops(dd)),
                              extra=oracle_rate(host, dict(scheme=scheme, d=dd),
                                                True)))
+            if scheme == gq.GQ_BIN_OPT:
+                tr = load_traffic(f"bin_opt_ef_d{dd}_n1B", "bin_opt")
+                out[-1]["traffic"] = tr
+                if tr:
+                    out[-1]["traffic_ratio"] = round(
+                        tr / quant_bytes(1, 2, dd, n, True), 4)
             del c, m, q
     # the min/max two-level quantizer (ORQ with L = 2, read as BinGrad-pb)
     for dd in (128, 512, 2048, 8192, 32768):
@@ -910,14 +922,34 @@ def ingest(dirs):
         "write_scale": round(w_scale, 5),
         "note": ("counters are KiB per dispatch; traffic = FETCH_SIZE*1024*"
                  "fetch_scale + WRITE_SIZE*1024*write_scale")}}
-    for key, tag in ((Headline.KEY, "k_stream_quant"),
-                     (Headline.AGG_KEY, "k_deq_acc")):
-        kname, f = med("FETCH_SIZE", lambda k, t=tag: t in k)
-        _, w = med("WRITE_SIZE", lambda k, t=tag: t in k)
+    for key, tag, sig in ((Headline.KEY, "k_stream_quant", Headline.KERNEL),
+                          (Headline.AGG_KEY, "k_deq_acc", Headline.AGG_KERNEL)):
+        kname, f = med("FETCH_SIZE", lambda k, t=sig: t in k)
+        _, w = med("WRITE_SIZE", lambda k, t=sig: t in k)
         res[key] = {"kernel": kname, "source_digest": source_digest(tag),
                     "fetch_kib": f, "write_kib": w,
                     "bytes_per_launch": round(f * 1024 * f_scale +
                                               w * 1024 * w_scale)}
+    # BinGrad-b + EF on 1B (from `--counters --only bingrad`): a quantize
+    # launch is the sort kernel (d <= 2048) or the sort-free kernel plus the
+    # sort kernel's pass over the buckets it left (d >= 4096)
+    for dd in BINGRAD_BUCKETS:
+        sigs = (f"k_wave_sort_quant<2, 1, {dd},", f"k_sort_quant<2, 1, {dd}>",
+                f"k_binopt_block<{dd}>")
+        names, fk, wk = [], 0.0, 0.0
+        for sig in sigs:
+            try:
+                kname, f = med("FETCH_SIZE", lambda k, t=sig: t in k)
+                _, w = med("WRITE_SIZE", lambda k, t=sig: t in k)
+            except KeyError:
+                continue
+            names.append(kname)
+            fk, wk = fk + f, wk + w
+        if names:
+            res[f"bin_opt_ef_d{dd}_n1B"] = {
+                "kernel": " + ".join(names), "source_digest": source_digest("bin_opt"),
+                "fetch_kib": fk, "write_kib": wk,
+                "bytes_per_launch": round(fk * 1024 * f_scale + wk * 1024 * w_scale)}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(res, f, indent=1)
@@ -988,6 +1020,14 @@ def main() -> int:
         dst = torch.empty_like(src)
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
+        del src, dst
+        if args.only:
+            hl.release()
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            suite(torch, gq, WL, stream, 1, args.only)
+            torch.cuda.synchronize()
+            DEFERRED.clear()  # no oracle timings in a counter run
         log("counters run done")
         return 0
 

@@ -6,7 +6,7 @@
 // The split that maximises F(k) = P_k^2 / k + (S - P_k)^2 / (n - k) (P_k the
 // sum of the k smallest values, S the bucket sum; the squared error is
 // sum(y^2) - F) is found by bounding F over groups of candidate splits.  One
-// workgroup owns a bucket, 32 values per thread, held as order-preserving
+// workgroup owns a bucket, 32 or 64 values per thread, held as order-preserving
 // integer keys of the canonical values:
 //
 //   1. Levels of refinement.  Each level cuts the candidate key ranges (at
@@ -43,6 +43,8 @@
 // (values so evenly spread that many splits tie) is marked with NaN levels
 // and left untouched; the caller then runs the sort-based kernel over the
 // marked buckets only.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace gq {
@@ -52,7 +54,10 @@ constexpr int kBins = 16;     // bins per level
 constexpr int kCap = 64;      // values the exact stage sorts (one per lane)
 constexpr int kLevels = 10;   // levels before a bucket falls back to the sort
 constexpr int kRow = 64 + 4;  // LDS words per bin row (a column per lane, padded)
-constexpr int kE = 32;        // values per thread
+// values per thread: 32, and 64 for the largest buckets (512 threads with
+// room for 64 held keys instead of 1024 threads capped at 128 registers,
+// which spilled to scratch memory)
+__host__ __device__ constexpr int elems_per_thread(int d) { return d >= 32768 ? 64 : 32; }
 
 // Order-preserving key of a canonical fp32 value (no -0) and its inverse.
 __device__ __forceinline__ uint32_t fkey(float x) {
@@ -68,6 +73,14 @@ __device__ __forceinline__ float funkey(uint32_t k) {
 __device__ __forceinline__ float kval(uint32_t k) {
   asm volatile("" : "+v"(k));
   return funkey(k);
+}
+
+// A held key as an opaque value: the two passes over the keys in the exact
+// stage recompute their range tests instead of keeping one predicate per
+// key alive between them.
+__device__ __forceinline__ uint32_t opaque(uint32_t k) {
+  asm volatile("" : "+v"(k));
+  return k;
 }
 
 // F at split k with P the sum below it (bounds: reciprocals refined by one
@@ -248,11 +261,12 @@ __device__ __forceinline__ int group_min_i(int v) {
 }
 
 template <int D>
-__global__ __launch_bounds__(D / kE, D / kE == 256 ? 3 : 1) void k_binopt_block(
+__global__ __launch_bounds__(D / elems_per_thread(D), D / elems_per_thread(D) == 256 ? 3 : 1)
+void k_binopt_block(
     int64_t n, const float* __restrict__ g, float* __restrict__ e,
     uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes) {
-  constexpr int T = D / kE;
-  constexpr int E = kE;
+  constexpr int E = elems_per_thread(D);
+  constexpr int T = D / E;
   constexpr int NQ = E / 4;
   constexpr int NW = T / 64;
   struct Shared {
@@ -282,14 +296,23 @@ __global__ __launch_bounds__(D / kE, D / kE == 256 ? 3 : 1) void k_binopt_block(
   const int64_t base = bucket * D;
   const int nj = (int)((n - base) < D ? (n - base) : D);
   const bool full = nj == D;
-  auto valid = [&](int m) { return full || 4 * (tid + T * (m / 4)) + (m % 4) < nj; };
+  // whether held value m is in the gradient (recomputed at each use: kept,
+  // the tests of the last bucket took one scalar register pair per value)
+  const int rem = nj - 4 * tid;
+  auto valid = [&](int m) {
+    return full | (4 * T * (m / 4) + (m % 4) < (int)opaque((uint32_t)rem));
+  };
 
   // ---- load p = g (+ e); thread t holds the float4s t, t + T, ...; keep
   //      the keys of the canonical values (-0 -> +0) and which were -0 -----
   uint32_t kk[E];
-  uint32_t negz = 0u;
+  using Mask = std::conditional_t<(E > 32), uint64_t, uint32_t>;
+  Mask negz = 0u;
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
+    // at most eight float4 pairs in flight: with 64 values per thread, all
+    // sixteen pairs at once left no registers for the rest
+    if (q % 8 == 0 && q > 0) asm volatile("" ::: "memory");
     const int64_t i = base + 4 * (tid + (int64_t)T * q);
     float4 x = full ? load4_nt(g + i) : load4(g, i, n);
     if (e != nullptr) {
@@ -303,9 +326,18 @@ __global__ __launch_bounds__(D / kE, D / kE == 256 ? 3 : 1) void k_binopt_block(
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float v = xs[c];
-      if (v == 0.f && __float_as_uint(v) != 0u) negz |= 1u << (4 * q + c);
+      if (v == 0.f && __float_as_uint(v) != 0u) negz |= Mask(1) << (4 * q + c);
       kk[4 * q + c] = fkey(v == 0.f ? 0.f : v);
     }
+  }
+  // the -0 flags as one integer from here on (not one predicate per value)
+  if constexpr (E > 32) {
+    uint32_t lo = (uint32_t)negz, hi = (uint32_t)(negz >> 32);
+    lo = opaque(lo);
+    hi = opaque(hi);
+    negz = ((Mask)hi << 32) | lo;
+  } else {
+    negz = opaque(negz);
   }
 
   // ---- bucket statistics: key range, S = sum, A = sum |p| (fp64; wave
@@ -603,20 +635,24 @@ __global__ __launch_bounds__(D / kE, D / kE == 256 ? 3 : 1) void k_binopt_block(
                          // 0xff800000)
   } else {
     auto in_ranges = [&](uint32_t k) {
-      return (k - rlo0 <= rhi0 - rlo0) || (nr == 2 && k - rlo1 <= rhi1 - rlo1);
+      // bitwise, not short-circuit: no branch per value
+      return (k - rlo0 <= rhi0 - rlo0) | ((nr == 2) & (k - rlo1 <= rhi1 - rlo1));
     };
-    // this wave's survivors, then one LDS reservation per wave
-    int wcnt = 0;
+    // each lane's survivors, their offsets in the wave, then one LDS
+    // reservation per wave
+    int own = 0;
     double p0 = 0.0, p1 = 0.0;  // sums below each range start (fp64)
 #pragma unroll
     for (int m = 0; m < E; ++m) {
       const bool v = valid(m);
-      const uint32_t k = kk[m];
+      const uint32_t k = opaque(kk[m]);
       const double dx = (double)kval(k);
-      if (v && k < rlo0) p0 = p0 + dx;
-      if (v && nr == 2 && k < rlo1) p1 = p1 + dx;
-      wcnt += (int)__builtin_popcountll(__ballot(v && in_ranges(k)));
+      p0 = (v & (k < rlo0)) ? p0 + dx : p0;
+      p1 = (v & (nr == 2) & (k < rlo1)) ? p1 + dx : p1;
+      own += (int)(v & in_ranges(k));
     }
+    const int incl = (int)group_inclusive<64>((double)own);
+    const int wcnt = __builtin_amdgcn_readlane(incl, 63);
     p0 = group_sum_d<64>(p0);
     p1 = group_sum_d<64>(p1);
     if (tid == 0) sh.cnt = 0;
@@ -628,15 +664,13 @@ __global__ __launch_bounds__(D / kE, D / kE == 256 ? 3 : 1) void k_binopt_block(
     int wbase = 0;
     if (wl == 0 && wcnt > 0) wbase = atomicAdd(&sh.cnt, wcnt);
     wbase = __builtin_amdgcn_readfirstlane(wbase);
-    int run = 0;
+    int pos = wbase + incl - own;
 #pragma unroll
     for (int m = 0; m < E; ++m) {
-      const uint32_t k = kk[m];
-      const bool in = valid(m) && in_ranges(k);
-      const uint64_t bal = __ballot(in);
-      const int pos = wbase + run + (int)__builtin_popcountll(bal & ((1ull << wl) - 1ull));
-      if (in && pos < kCap) sh.v[pos] = kval(k);
-      run += (int)__builtin_popcountll(bal);
+      const uint32_t k = opaque(kk[m]);
+      const bool in = valid(m) & in_ranges(k);
+      if (in & (pos < kCap)) sh.v[pos] = kval(k);
+      pos += (int)in;
     }
     __syncthreads();
     p0 = sh.rd[2][0];
@@ -783,7 +817,7 @@ template <int D>
 int launch_one(int64_t n, const float* g, float* e, uint8_t* codes, float* meta,
                int64_t code_bytes, hipStream_t st) {
   const int64_t nb = (n + D - 1) / D;
-  hipLaunchKernelGGL((k_binopt_block<D>), dim3((uint32_t)nb), dim3(D / kE), 0, st,
+  hipLaunchKernelGGL((k_binopt_block<D>), dim3((uint32_t)nb), dim3(D / elems_per_thread(D)), 0, st,
                      n, g, e, codes, meta, code_bytes);
   return (int)hipGetLastError();
 }

@@ -49,3 +49,54 @@ def test_alu_op_counts():
     assert bench.binopt_prune_ops() == 36
     f = bench.alu_fields(100.0, 10 ** 8, 1.0)
     assert abs(f["alu_frac"] - 1e10 / 1e-3 / bench.VALU_PEAK_LANE_OPS) < 1e-4
+
+
+def test_ingest_counter_runs(tmp_path, monkeypatch):
+    """`bench.py --ingest` turns two counter databases (FETCH_SIZE, WRITE_SIZE
+    in KiB per dispatch) into bytes per launch, scaled by what the counters
+    read for the known-size copy, per headline kernel and per BinGrad-b
+    bucket size (the sort-free kernel and the sort kernel's pass summed)."""
+    import sqlite3
+    sys.path.insert(0, ROOT)
+    import bench
+    copy_kib = bench.COPY_BYTES / 1024
+    rows = {
+        "FETCH_SIZE": [("at::neg_kernel", copy_kib / 2),
+                       (f"void gq::{bench.Headline.KERNEL}(long)", 1000.0),
+                       ("void gq::k_stream_quant<1, 1, 64, 2>(long)", 7.0),
+                       (f"void gq::{bench.Headline.AGG_KERNEL}(long)", 2000.0),
+                       ("void gq::k_binopt_block<8192>(long)", 300.0),
+                       ("void gq::k_sort_quant<2, 1, 8192>(long)", 1.0),
+                       ("void gq::k_wave_sort_quant<2, 1, 512, false>(long)", 400.0)],
+        "WRITE_SIZE": [("at::neg_kernel", copy_kib),
+                       (f"void gq::{bench.Headline.KERNEL}(long)", 100.0),
+                       ("void gq::k_stream_quant<1, 1, 64, 2>(long)", 9.0),
+                       (f"void gq::{bench.Headline.AGG_KERNEL}(long)", 200.0),
+                       ("void gq::k_binopt_block<8192>(long)", 30.0),
+                       ("void gq::k_sort_quant<2, 1, 8192>(long)", 0.5),
+                       ("void gq::k_wave_sort_quant<2, 1, 512, false>(long)", 40.0)],
+    }
+    dirs = []
+    for cn, kv in rows.items():
+        d = tmp_path / cn
+        d.mkdir()
+        con = sqlite3.connect(str(d / "run.db"))
+        con.execute("create table counters_collection "
+                    "(kernel_name text, counter_name text, value real)")
+        for name, v in kv:
+            con.execute("insert into counters_collection values (?, ?, ?)", (name, cn, v))
+        con.commit()
+        con.close()
+        dirs.append(str(d))
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    bench.ingest(dirs)
+    import json
+    t = json.loads(out.read_text())
+    assert t["_calibration"]["fetch_scale"] == 2.0
+    assert t["_calibration"]["write_scale"] == 1.0
+    assert t[bench.Headline.KEY]["bytes_per_launch"] == 1000 * 2048 + 100 * 1024
+    assert t[bench.Headline.AGG_KEY]["bytes_per_launch"] == 2000 * 2048 + 200 * 1024
+    assert t["bin_opt_ef_d8192_n1B"]["bytes_per_launch"] == 301 * 2048 + 30.5 * 1024
+    assert t["bin_opt_ef_d512_n1B"]["bytes_per_launch"] == 400 * 2048 + 40 * 1024
+    assert "bin_opt_ef_d2048_n1B" not in t
