@@ -136,7 +136,7 @@ def binopt_ops(d: int) -> float:
 
 def binopt_prune_ops() -> float:
     """BinGrad-b with error feedback by the sort-free split search (buckets of
-    4096 and more): EF add (1); order-preserving key (2); bucket minimum,
+    1024 and more): EF add (1); order-preserving key (2); bucket minimum,
     maximum, sum and absolute sum (4); the first level's bin, fixed-point
     value and LDS add for every element (5); the second level's range test
     and insertion, which reaches nearly every element (7); three more levels'
@@ -845,7 +845,7 @@ def suite_bingrad(torch, gq, WL, stream, tb, reps):
             out.append(entry(f"quantize {nm}+ef d={dd} n={n}", ms,
                              quant_bytes(1, 2, dd, n, True), n,
                              alu=(None if scheme != gq.GQ_BIN_OPT else
-                                  binopt_prune_ops() if dd >= 4096 else binopt_ops(dd)),
+                                  binopt_prune_ops() if dd >= 1024 else binopt_ops(dd)),
                              extra=oracle_rate(host, dict(scheme=scheme, d=dd),
                                                True)))
             if scheme == gq.GQ_BIN_OPT:
@@ -931,8 +931,8 @@ def ingest(dirs):
                     "bytes_per_launch": round(f * 1024 * f_scale +
                                               w * 1024 * w_scale)}
     # BinGrad-b + EF on 1B (from `--counters --only bingrad`): a quantize
-    # launch is the sort kernel (d <= 2048) or the sort-free kernel plus the
-    # sort kernel's pass over the buckets it left (d >= 4096)
+    # launch is the sort kernel (d <= 512) or the sort-free kernel plus the
+    # sort kernel's pass over the buckets it left (d >= 1024)
     for dd in BINGRAD_BUCKETS:
         sigs = (f"k_wave_sort_quant<2, 1, {dd},", f"k_sort_quant<2, 1, {dd}>",
                 f"k_binopt_block<{dd}>")

@@ -1,12 +1,12 @@
 // binopt_quant.hip — BinGrad-b (the two-level quantizer whose levels
 // minimise the squared error: the exact 1-D 2-means split of each bucket;
 // "Optimal Gradient Quantization Condition" review, §Proposed method) with
-// error feedback, for large buckets (d >= 4096), without sorting the bucket.
+// error feedback, for buckets of 1024 and more, without sorting the bucket.
 //
 // The split that maximises F(k) = P_k^2 / k + (S - P_k)^2 / (n - k) (P_k the
 // sum of the k smallest values, S the bucket sum; the squared error is
 // sum(y^2) - F) is found by bounding F over groups of candidate splits.  One
-// workgroup owns a bucket, 32 or 64 values per thread, held as order-preserving
+// workgroup owns a bucket, 16 or 32 values per thread, held as order-preserving
 // integer keys of the canonical values:
 //
 //   1. Levels of refinement.  Each level cuts the candidate key ranges (at
@@ -16,7 +16,7 @@
 //      values into its lane's LDS column of the 16-bin (count, sum) histogram
 //      with one 64-bit integer atomic per value (count in the high bits, the
 //      value in fixed point below: exact, order-independent and, on this
-//      GPU, about 30x cheaper than fp32 LDS atomics; lanes of different waves
+//      GPU, over 20x cheaper than fp32 LDS atomics; lanes of different waves
 //      share a column, which integer atomics keep exact).  Prefix sums give,
 //      at every bin edge, the split position K and the (quantized) sum P of
 //      the values below it.
@@ -40,11 +40,10 @@
 //      cluster means, the residual p - x_hat; the bucket is read once.
 //
 // A bucket whose candidates do not shrink to 64 values within ten levels
-// (values so evenly spread that many splits tie) is marked with NaN levels
+// (many equal values, whose splits the bounds cannot tell apart), or whose
+// scale leaves the fixed-point range, is marked with NaN levels
 // and left untouched; the caller then runs the sort-based kernel over the
 // marked buckets only.
-#include <type_traits>
-
 #include "common.hpp"
 
 namespace gq {
@@ -54,10 +53,11 @@ constexpr int kBins = 16;     // bins per level
 constexpr int kCap = 64;      // values the exact stage sorts (one per lane)
 constexpr int kLevels = 10;   // levels before a bucket falls back to the sort
 constexpr int kRow = 64 + 4;  // LDS words per bin row (a column per lane, padded)
-// values per thread: 32, and 64 for the largest buckets (512 threads with
-// room for 64 held keys instead of 1024 threads capped at 128 registers,
-// which spilled to scratch memory)
-__host__ __device__ constexpr int elems_per_thread(int d) { return d >= 32768 ? 64 : 32; }
+// values per thread: 32 (workgroups of 64 to 1024 threads), 16 at d = 1024
+// (one wave).  Every instance fits in 128 VGPRs without spilling (four waves
+// per SIMD); 64 values per thread, tried at d = 16384 and 32768, gave fewer
+// waves per CU and no gain.
+__host__ __device__ constexpr int elems_per_thread(int d) { return d == 1024 ? 16 : 32; }
 
 // Order-preserving key of a canonical fp32 value (no -0) and its inverse.
 __device__ __forceinline__ uint32_t fkey(float x) {
@@ -304,56 +304,64 @@ void k_binopt_block(
   };
 
   // ---- load p = g (+ e); thread t holds the float4s t, t + T, ...; keep
-  //      the keys of the canonical values (-0 -> +0) and which were -0 -----
+  //      the keys of the canonical values (-0 -> +0) and which were -0;
+  //      bucket statistics on the way: key range, S = sum, A = sum |p|
+  //      (fp64; wave partials combined in wave order) ----------------------
   uint32_t kk[E];
-  using Mask = std::conditional_t<(E > 32), uint64_t, uint32_t>;
-  Mask negz = 0u;
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    // at most eight float4 pairs in flight: with 64 values per thread, all
-    // sixteen pairs at once left no registers for the rest
-    if (q % 8 == 0 && q > 0) asm volatile("" ::: "memory");
-    const int64_t i = base + 4 * (tid + (int64_t)T * q);
-    float4 x = full ? load4_nt(g + i) : load4(g, i, n);
-    if (e != nullptr) {
-      const float4 r = full ? load4_nt(e + i) : load4(e, i, n);
-      x.x = x.x + r.x;
-      x.y = x.y + r.y;
-      x.z = x.z + r.z;
-      x.w = x.w + r.w;
-    }
+  static_assert(E <= 32, "one bit per held value in negz");
+  uint32_t negz = 0u;
+  uint32_t kmn = 0xffffffffu, kmx = 0u;
+  double S = 0.0, A = 0.0;
+  auto take = [&](int q, float4 x) {
     const float xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float v = xs[c];
-      if (v == 0.f && __float_as_uint(v) != 0u) negz |= Mask(1) << (4 * q + c);
-      kk[4 * q + c] = fkey(v == 0.f ? 0.f : v);
+      if (v == 0.f && __float_as_uint(v) != 0u) negz |= 1u << (4 * q + c);
+      const float cv = v == 0.f ? 0.f : v;
+      const uint32_t key = fkey(cv);
+      kk[4 * q + c] = key;
+      const bool ok = valid(4 * q + c);
+      kmn = (ok & (key < kmn)) ? key : kmn;
+      kmx = (ok & (key > kmx)) ? key : kmx;
+      S = ok ? S + (double)cv : S;
+      A = ok ? A + (double)fabsf(cv) : A;
+    }
+  };
+  if (full) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int64_t i = base + 4 * (tid + (int64_t)T * q);
+      float4 x = load4_nt(g + i);
+      if (e != nullptr) {
+        const float4 r = load4_nt(e + i);
+        x.x = x.x + r.x;
+        x.y = x.y + r.y;
+        x.z = x.z + r.z;
+        x.w = x.w + r.w;
+      }
+      take(q, x);
+    }
+  } else {
+    // the last bucket: element-wise bounds, one float4 at a time
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      asm volatile("" ::: "memory");
+      const int64_t i = base + 4 * (tid + (int64_t)T * q);
+      float4 x = load4(g, i, n);
+      if (e != nullptr) {
+        const float4 r = load4(e, i, n);
+        x.x = x.x + r.x;
+        x.y = x.y + r.y;
+        x.z = x.z + r.z;
+        x.w = x.w + r.w;
+      }
+      take(q, x);
     }
   }
   // the -0 flags as one integer from here on (not one predicate per value)
-  if constexpr (E > 32) {
-    uint32_t lo = (uint32_t)negz, hi = (uint32_t)(negz >> 32);
-    lo = opaque(lo);
-    hi = opaque(hi);
-    negz = ((Mask)hi << 32) | lo;
-  } else {
-    negz = opaque(negz);
-  }
+  negz = opaque(negz);
 
-  // ---- bucket statistics: key range, S = sum, A = sum |p| (fp64; wave
-  //      partials combined in wave order) ---------------------------------
-  uint32_t kmn = 0xffffffffu, kmx = 0u;
-  double S = 0.0, A = 0.0;
-#pragma unroll
-  for (int m = 0; m < E; ++m) {
-    if (valid(m)) {
-      const float x = kval(kk[m]);
-      kmn = kk[m] < kmn ? kk[m] : kmn;
-      kmx = kk[m] > kmx ? kk[m] : kmx;
-      S = S + (double)x;
-      A = A + (double)fabsf(x);
-    }
-  }
   kmn = group_min_u<64>(kmn);
   kmx = group_max_u<64>(kmx);
   S = group_sum_d<64>(S);
@@ -376,6 +384,9 @@ void k_binopt_block(
     S = S + sh.rd[0][w];
     A = A + sh.rd[1][w];
   }
+  // combined here, not where first used (the wave partials' loads were
+  // otherwise kept in registers, or spilled, until the exact stage)
+  asm volatile("" : "+v"(S), "+v"(A));
   const double dn = (double)nj;
 
   // The histogram sums are fixed point: value x adds q = trunc(x 2^f), with
@@ -412,6 +423,13 @@ void k_binopt_block(
     return (unsigned long long)(q + (1ll << 48));
   };
   int state = !split_exists ? 1 : (nj <= kCap ? 1 : (sane ? 0 : 2));
+  // this lane's histogram column as an LDS-space pointer (32-bit address
+  // arithmetic per insertion)
+  typedef __attribute__((address_space(3))) unsigned long long lds_u64;
+  lds_u64* const col = (lds_u64*)(sh.h + wl);
+  auto hist_add = [&](int bin, unsigned long long v) {
+    __atomic_fetch_add(col + __umul24((uint32_t)bin, (uint32_t)kRow), v, __ATOMIC_RELAXED);
+  };
 
   for (int lev = 0; lev < kLevels && state == 0; ++lev) {
     const int nbr = kBins / nr;  // bins per range
@@ -428,7 +446,7 @@ void k_binopt_block(
       for (int m = 0; m < E; ++m) {
         if (!valid(m)) continue;
         const int bin = (int)((kk[m] - rlo0) >> sh0);
-        atomicAdd(&sh.h[bin * kRow + wl], packed(kk[m]));
+        hist_add(bin, packed(kk[m]));
       }
     } else {
 #pragma unroll
@@ -438,7 +456,7 @@ void k_binopt_block(
         const bool in1 = nr == 2 && k - rlo1 <= span1;
         if (!valid(m) || !(in0 || in1)) continue;
         const int bin = in0 ? (int)((k - rlo0) >> sh0) : nbr + (int)((k - rlo1) >> sh1);
-        atomicAdd(&sh.h[bin * kRow + wl], packed(k));
+        hist_add(bin, packed(k));
       }
     }
     __syncthreads();
@@ -824,12 +842,14 @@ int launch_one(int64_t n, const float* g, float* e, uint8_t* codes, float* meta,
 
 }  // namespace
 
-bool binopt_prune_supported(int d) { return d >= 4096 && d <= 32768; }
+bool binopt_prune_supported(int d) { return d >= 1024 && d <= 32768; }
 
 int launch_binopt_prune(int d, int64_t n, const float* g, float* e,
                         uint8_t* codes, float* meta, int64_t code_bytes,
                         hipStream_t st) {
   switch (d) {
+    case 1024: return launch_one<1024>(n, g, e, codes, meta, code_bytes, st);
+    case 2048: return launch_one<2048>(n, g, e, codes, meta, code_bytes, st);
     case 4096: return launch_one<4096>(n, g, e, codes, meta, code_bytes, st);
     case 8192: return launch_one<8192>(n, g, e, codes, meta, code_bytes, st);
     case 16384: return launch_one<16384>(n, g, e, codes, meta, code_bytes, st);

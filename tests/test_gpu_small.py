@@ -145,7 +145,7 @@ def test_two_level_ragged_and_degenerate(dev, n):
         check_quantize(dev, O.Desc(scheme, 64), g, np.zeros_like(g))
 
 
-@pytest.mark.parametrize("d", [4096, 32768])
+@pytest.mark.parametrize("d", [1024, 4096, 16384, 32768])
 def test_binopt_large_bucket_edge_cases(dev, d):
     """Large BinGrad-b buckets that take every branch of the sort-free split
     search: no split (one value), signed zeros, small integers (ties the
