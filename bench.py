@@ -844,6 +844,7 @@ def suite_bingrad(torch, gq, WL, stream, tb, reps):
             ms = tb(lambda i: q(0, i), max(3, reps // 2))
             out.append(entry(f"quantize {nm}+ef d={dd} n={n}", ms,
                              quant_bytes(1, 2, dd, n, True), n,
+                             bound="alu" if scheme == gq.GQ_BIN_OPT else "hbm",
                              alu=(None if scheme != gq.GQ_BIN_OPT else
                                   binopt_prune_ops() if dd >= 1024 else binopt_ops(dd)),
                              extra=oracle_rate(host, dict(scheme=scheme, d=dd),
