@@ -19,6 +19,8 @@
 //                 and inserts the block argmax (smallest c on equality);
 //   5. back in element order: codes, packing, residual.
 // The bucket is read from HBM once; everything after the load is on-chip.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace gq {
@@ -676,6 +678,87 @@ struct WaveCfg {
   static constexpr int G = D / E;
 };
 
+// DPP moves (no LDS): the value N lanes lower in the same 16-lane row (0 in
+// the row's first N lanes), and the last lane of the previous row (BC = 15:
+// rows 1 and 3) or lane 31 (BC = 31: rows 2 and 3), 0 elsewhere.
+template <int N>
+__device__ __forceinline__ int dpp_shr(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, 0x110 + N, 0xF, 0xF, false);
+}
+template <int BC>
+__device__ __forceinline__ int dpp_bcast(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, BC == 15 ? 0x142 : 0x143,
+                                     BC == 15 ? 0xA : 0xC, 0xF, false);
+}
+template <int N>
+__device__ __forceinline__ double dpp_shr(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)dpp_shr<N>((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)dpp_shr<N>((int)(uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+template <int BC>
+__device__ __forceinline__ double dpp_bcast(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)dpp_bcast<BC>((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)dpp_bcast<BC>((int)(uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Inclusive segmented scan over the G lanes of a group in lane order, by DPP
+// steps: (f, s) of the lanes up to this one combined as in block_seg_carry.
+template <int G>
+__device__ __forceinline__ void group_seg_incl(int& f, double& s, int gl) {
+  auto step = [&](double sp, int fp) {
+    s = f ? s : sp + s;
+    f |= fp;
+  };
+  auto shr = [&](auto tag) {
+    constexpr int N = decltype(tag)::value;
+    double sp = dpp_shr<N>(s);
+    int fp = dpp_shr<N>(f);
+    if (G < 16 && gl < N) {  // two groups share a row
+      sp = 0.0;
+      fp = 0;
+    }
+    step(sp, fp);
+  };
+  shr(std::integral_constant<int, 1>());
+  shr(std::integral_constant<int, 2>());
+  shr(std::integral_constant<int, 4>());
+  if constexpr (G >= 16) shr(std::integral_constant<int, 8>());
+  if constexpr (G >= 32) step(dpp_bcast<15>(s), dpp_bcast<15>(f));
+  if constexpr (G >= 64) step(dpp_bcast<31>(s), dpp_bcast<31>(f));
+}
+
+// Exclusive segmented carry over the G lanes of a group: the combination of
+// the aggregates (f, s) of the lanes before this one (REV = false) or after
+// it (REV = true; the group's lanes mirrored, scanned, mirrored back).
+template <int G, bool REV>
+__device__ __forceinline__ double group_seg_carry_dpp(bool f, double s, int gl) {
+  int fi = f ? 1 : 0;
+  if constexpr (REV) {
+    s = xshfl(s, G - 1);
+    fi = xshfl(fi, G - 1);
+  }
+  // scan and shift in physical lane order (mirrored order for REV)
+  group_seg_incl<G>(fi, s, gl);
+  double ex = __shfl_up(s, 1, G);
+  if (gl == 0) ex = 0.0;
+  if constexpr (REV) ex = xshfl(ex, G - 1);
+  return ex;
+}
+
+// Number of entries below x in a row of 16 ascending floats (+inf padded)
+// in LDS, for x not above the row's last finite entry: 0 .. 15.
+__device__ __forceinline__ int lds_rank16(const float* row, float x) {
+  int pos = row[7] < x ? 8 : 0;
+  pos += row[pos + 3] < x ? 4 : 0;
+  pos += row[pos + 1] < x ? 2 : 0;
+  pos += row[pos] < x ? 1 : 0;
+  return pos;
+}
+
 // Exclusive segmented scan over the G lanes of a group (see block_seg_carry):
 // returns the combination of the aggregates (f, s) of the lanes before this
 // one (REV = false) or after it (REV = true).
@@ -839,7 +922,8 @@ void k_wave_sort_quant(
 
   float lvl_a = 0.f, lvl_b = 0.f, thr = 0.f;
   bool no_split = false;
-  float lv[16];
+  // ORQ: each group's levels, ascending, +inf past the current count
+  __shared__ float lvt[kGroupThreads / G][16];
 
   if constexpr (SCHEME == BIN_OPT) {
     // ---- 4a. best split -------------------------------------------------
@@ -931,72 +1015,76 @@ void k_wave_sort_quant(
       meta[2 * bucket + 1] = lvl_b;
     }
   } else {
-    // ---- 4b. ORQ greedy levels (lv[j] = +inf past the current count) ------
-    // Each sorted value keeps its segment (index of the last level <= y)
-    // and the segment's end points (a, b); inserting c into (a0, b0) moves
-    // every y >= c one segment up and splits (a0, b0) into (a0, c), (c, b0).
-    // One level per step (greedy), or with GQ_FLAG_BISECT one per segment
-    // per round (recursive bisection).
+    // ---- 4b. ORQ greedy levels --------------------------------------------
+    // The levels live in the group's LDS row T, ascending, +inf past the
+    // current count.  Each sorted value keeps its segment's end points
+    // (a, b) (a = the last level <= y; the top segment, y >= max, has
+    // a = b = max) and, for the bisection, the segment's index; inserting c
+    // into (a0, b0) splits it into (a0, c), (c, b0).  One level per step
+    // (greedy), or with GQ_FLAG_BISECT one per segment per round (recursive
+    // bisection).
+    float* T = lvt[threadIdx.x / G];
     const float ymin = wave_at<E, G>(y, 0), ymax = wave_at<E, G>(y, nj - 1);
+    const bool flat = !(ymin < ymax);
+    for (int j = lane; j < 16; j += G)
+      T[j] = flat ? (j < L ? ymin : __builtin_inff())
+                  : (j == 0 ? ymin : (j == 1 ? ymax : __builtin_inff()));
+    int cnt = flat ? L : 2;
+    // the +inf padding past the bucket's end becomes ymax here: it then sits
+    // in the top segment with y - a = b - y = 0 and is never a candidate
 #pragma unroll
-    for (int j = 0; j < 16; ++j) lv[j] = __builtin_inff();
-    lv[0] = ymin;
-    lv[1] = ymax;
-    int cnt = 2;
-    if (ymin == ymax) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) lv[j] = j < L ? ymin : __builtin_inff();
-      cnt = L;
-    }
-    int seg[E];
+    for (int m = 0; m < E; ++m) y[m] = r0 + m < nj ? y[m] : ymax;
+    int seg[BISECT ? E : 1];
     float a_of[E], b_of[E];
 #pragma unroll
     for (int m = 0; m < E; ++m) {
       const bool top = y[m] >= ymax;
-      seg[m] = top ? 1 : 0;
+      if constexpr (BISECT) seg[m] = top ? 1 : 0;
       a_of[m] = top ? ymax : ymin;
       b_of[m] = ymax;
     }
+    // a segment identifier: its index, or the bits of its lower end (the
+    // levels are distinct values)
+    auto sid = [&](int m) {
+      if constexpr (BISECT) return seg[m];
+      else return __float_as_int(a_of[m]);
+    };
     while (cnt < L) {
-      int seg_prev = __shfl_up(seg[E - 1], 1, G);
-      if (lane == 0) seg_prev = -1;
-      int seg_next = __shfl_down(seg[0], 1, G);
-      if (lane == G - 1 || r0 + E >= nj) seg_next = -1;
-      // (y - a) and (b - y) of real values, 0 for the +inf padding
-      auto va = [&](int m) {
-        return r0 + m < nj ? (double)y[m] - (double)a_of[m] : 0.0;
-      };
-      auto vb = [&](int m) {
-        return r0 + m < nj ? (double)b_of[m] - (double)y[m] : 0.0;
-      };
+      int seg_prev = __shfl_up(sid(E - 1), 1, G);
+      const bool first_lane = lane == 0;
+      int seg_next = __shfl_down(sid(0), 1, G);
+      const bool last_lane = lane == G - 1 || r0 + E >= nj;
+      // (b - y) once per step, (y - a) at each use; both exact in fp64
+      double dB[E];
+#pragma unroll
+      for (int m = 0; m < E; ++m) dB[m] = (double)b_of[m] - (double)y[m];
+      auto va = [&](int m) { return (double)y[m] - (double)a_of[m]; };
+      auto vb = [&](int m) { return dB[m]; };
       auto head = [&](int m) {
-        return m == 0 ? seg_prev != seg[0] : seg[m] != seg[m - 1];
+        return m == 0 ? (first_lane || seg_prev != sid(0)) : sid(m) != sid(m - 1);
       };
       auto tail = [&](int m) {
-        return m == E - 1 ? seg_next != seg[E - 1] : seg[m] != seg[m + 1];
+        return m == E - 1 ? (last_lane || seg_next != sid(E - 1)) : sid(m) != sid(m + 1);
       };
-      bool fa = false, fb = false;
+      // this lane's partial sums (branch-free), then the group's carries
+      int fa = 0, fb = 0;
       double sa = 0.0, sb = 0.0;
 #pragma unroll
       for (int m = 0; m < E; ++m) {
-        if (head(m)) {
-          fa = true;
-          sa = va(m);
-        } else {
-          sa = sa + va(m);
-        }
+        const bool h = head(m);
+        const double v = va(m);
+        sa = h ? v : sa + v;
+        fa |= h ? 1 : 0;
       }
 #pragma unroll
       for (int m = E - 1; m >= 0; --m) {
-        if (tail(m)) {
-          fb = true;
-          sb = vb(m);
-        } else {
-          sb = sb + vb(m);
-        }
+        const bool t = tail(m);
+        const double v = vb(m);
+        sb = t ? v : sb + v;
+        fb |= t ? 1 : 0;
       }
-      const double ca = group_seg_carry<G, false>(fa, sa, lane);
-      const double cb = group_seg_carry<G, true>(fb, sb, lane);
+      const double ca = group_seg_carry_dpp<G, false>(fa != 0, sa, lane);
+      const double cb = group_seg_carry_dpp<G, true>(fb != 0, sb, lane);
       double best = -1.0;
       int bestk = 0x7fffffff;
       // Gs[m]: first the sum of (b - y) over the values after m in m's
@@ -1006,64 +1094,62 @@ void k_wave_sort_quant(
         double run = cb;
 #pragma unroll
         for (int m = E - 1; m >= 0; --m) {
-          if (tail(m)) {
-            Gs[m] = 0.0;
-            run = vb(m);
-          } else {
-            Gs[m] = run;
-            run = run + vb(m);
-          }
+          const bool t = tail(m);
+          const double v = vb(m);
+          Gs[m] = t ? 0.0 : run;
+          run = t ? v : run + v;
         }
         double A = ca;
 #pragma unroll
         for (int m = 0; m < E; ++m) {
-          A = head(m) ? va(m) : A + va(m);
+          const double v = va(m);
+          A = head(m) ? v : A + v;
           const int pos = r0 + m;
           const float yv = y[m];
           const float ynext = (m + 1 < E) ? y[m + 1] : y_next_run;
-          const bool cand = pos < nj && seg[m] + 1 < cnt && yv > a_of[m] &&
+          // strictly inside a segment other than the top one, the last of
+          // a run of equal values
+          const bool cand = pos < nj && a_of[m] < ymax && yv > a_of[m] &&
                             (pos + 1 >= nj || ynext != yv);
-          double Gv = -1.0;
-          if (cand) {
-            const double c = (double)yv;
-            Gv = ((double)b_of[m] - c) * A + (c - (double)a_of[m]) * Gs[m];
-            if (Gv > best) {
-              best = Gv;
-              bestk = pos;
-            }
-          }
+          // (b - c) A + (c - a) B, with b - c and c - a exact in fp64
+          const double Gv = cand ? vb(m) * A + v * Gs[m] : -1.0;
+          const bool better = Gv > best;
+          best = better ? Gv : best;
+          bestk = better ? pos : bestk;
           Gs[m] = Gv;
         }
       }
-      // insert c after every level <= c (levels stay ascending) and update
-      // the segment state of every value
+      // insert c after every level below it (levels stay ascending; c lies
+      // strictly inside a segment, so no level equals it) and update the
+      // segment state of every value
       auto insert_level = [&](float c) {
-        int ins = 0;
+        const int ins = lds_rank16(T, c);
+        constexpr int NJ = (16 + G - 1) / G;
+        float old[NJ];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) ins += (lv[j] <= c) ? 1 : 0;
-        float nl[16];
+        for (int t = 0; t < NJ; ++t) {
+          const int j = lane + G * t;
+          old[t] = (j >= 1 && j < 16) ? T[j - 1] : 0.f;
+        }
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          nl[j] = j < ins ? lv[j] : (j == ins ? c : lv[j > 0 ? j - 1 : 0]);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) lv[j] = nl[j];
+        for (int t = 0; t < NJ; ++t) {
+          const int j = lane + G * t;
+          if (j < 16 && j >= ins && j <= cnt) T[j] = j == ins ? c : old[t];
+        }
 #pragma unroll
         for (int m = 0; m < E; ++m) {
-          const bool split = seg[m] == ins - 1;
+          const bool split = a_of[m] < c && c < b_of[m];
           const bool up = y[m] >= c;
-          if (split) {
-            if (up) a_of[m] = c;
-            else b_of[m] = c;
-          }
-          seg[m] += up ? 1 : 0;
+          a_of[m] = (split && up) ? c : a_of[m];
+          b_of[m] = (split && !up) ? c : b_of[m];
+          if constexpr (BISECT) seg[m] += up ? 1 : 0;
         }
         ++cnt;
       };
       auto fill_with_max = [&]() {
         // fewer distinct values than levels: repeat the maximum
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (j >= cnt && j < L) lv[j] = ymax;
+        for (int j = lane; j < 16; j += G)
+          if (j >= cnt && j < L) T[j] = ymax;
         cnt = L;
       };
       if constexpr (!BISECT) {
@@ -1133,19 +1219,12 @@ void k_wave_sort_quant(
         }
       }
     }
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j % G == lane && j < L) meta[bucket * L + j] = lv[j];
+    for (int j = lane; j < L; j += G) meta[bucket * L + j] = T[j];
   }
 
   if (codes == nullptr) return;  // levels only
 
   // ---- 5. codes, packing, residual (element order) ----------------------
-  if constexpr (SCHEME == ORQ) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j >= L) lv[j] = __builtin_inff();
-  }
   // ORQ reads its bucket again here (from cache in practice) rather than
   // holding p through the level search: fewer live registers, more waves.
   if constexpr (SCHEME == ORQ) {
@@ -1193,32 +1272,21 @@ void k_wave_sort_quant(
         code = (!no_split && p[m] >= thr) ? 1u : 0u;
         xh = code ? lvl_b : lvl_a;
       } else {
+        // the levels around x by binary search in the group's LDS row: a
+        // value on a level takes it (the first equal one); otherwise it
+        // rounds between the levels below and above
+        const float* T = lvt[threadIdx.x / G];
         const float x = clipped(p[m]);
-        int first_eq = -1, below = 0;
-#pragma unroll
-        for (int j = 15; j >= 0; --j)
-          if (j < L && lv[j] == x) first_eq = j;
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (j < L && lv[j] < x) below = j;
-        if (first_eq >= 0) {
-          code = (uint32_t)first_eq;
-        } else {
-          const int sub = (int)(i & 3);
-          const uint32_t word = sub == 0 ? w.x : sub == 1 ? w.y : sub == 2 ? w.z : w.w;
-          float lo = lv[0], hi = lv[1];
-#pragma unroll
-          for (int j = 0; j < 15; ++j)
-            if (j == below) {
-              lo = lv[j];
-              hi = lv[j + 1];
-            }
-          const float qf = (x - lo) / (hi - lo);
-          code = (uint32_t)(below + (u24(word) < qf ? 1 : 0));
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if ((uint32_t)j == code) xh = lv[j];
+        const int above = lds_rank16(T, x);  // levels below x
+        const float hi = T[above];
+        const float lo = T[above > 0 ? above - 1 : 0];
+        const int sub = (int)(i & 3);
+        const uint32_t word = sub == 0 ? w.x : sub == 1 ? w.y : sub == 2 ? w.z : w.w;
+        const float qf = (x - lo) / (hi - lo);
+        const bool up = u24(word) < qf;
+        const bool on = hi == x;
+        code = (uint32_t)(on ? above : above - 1 + (up ? 1 : 0));
+        xh = on ? x : (up ? hi : lo);
       }
       if (!real) code = 0u;
       field |= code << ((BITS == 0 ? 4 : BITS) * c);
