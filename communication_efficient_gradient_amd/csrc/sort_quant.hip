@@ -797,6 +797,20 @@ __device__ __forceinline__ int group_argmax(double v, int key, double* best_out)
   return key;
 }
 
+// The same argmax in two reductions: the group maximum of the value, then
+// the smallest key among the lanes holding it.
+template <int G>
+__device__ __forceinline__ int group_argmax2(double v, int key, double* best_out) {
+  double mx = v;
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) mx = fmax(mx, xshfl(mx, o));
+  int k = v == mx ? key : 0x7fffffff;
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) k = min(k, xshfl(k, o));
+  *best_out = mx;
+  return k;
+}
+
 // Sorted value at group-uniform position pos.
 template <int E, int G>
 __device__ __forceinline__ float wave_at(const float (&y)[E], int pos) {
@@ -991,7 +1005,7 @@ void k_wave_sort_quant(
       }
     }
     double bestF;
-    const int kstar = group_argmax<G>(best, bestk, &bestF);
+    const int kstar = group_argmax2<G>(best, bestk, &bestF);
     if (bestF < 0.0) {
       no_split = true;
       thr = wave_at<E, G>(y, 0);
