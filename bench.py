@@ -29,6 +29,7 @@ import argparse
 import glob
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -376,19 +377,36 @@ def _stats(durs):
             "p90": q(0.9), "runs": len(s)}
 
 
-def time_launches(torch, stream, launch, reps: int, warm: int = 3) -> dict:
-    """Per-launch durations of `reps` launches, each bracketed by its own
-    pair of HIP events on the launch stream (the events of consecutive
-    launches are shared, so the launches stay back to back)."""
+def time_launches(torch, stream, launch, reps: int, warm: int = 3,
+                  min_sample_ms: float = 0.5) -> dict:
+    """Per-launch durations from `reps` samples on the launch stream: each
+    sample is a batch of B back-to-back launches between two HIP events,
+    B chosen so a sample lasts at least `min_sample_ms` (1 for launches of
+    that length and more), and its per-launch time the batch time / B.  An
+    event pair around every short launch would add the event's own
+    dispatch (~4-5 us) to each; back to back, the samples carry only the
+    gaps between consecutive kernels."""
     for i in range(warm):
         launch(i)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    launch(warm)
+    b.record(stream)
+    b.synchronize()
+    est = a.elapsed_time(b)
+    B = max(1, min(256, int(math.ceil(min_sample_ms / max(est, 1e-4)))))
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    k = warm + 1
     ev[0].record(stream)
-    for i in range(reps):
-        launch(warm + i)
-        ev[i + 1].record(stream)
+    for r in range(reps):
+        for _ in range(B):
+            launch(k)
+            k += 1
+        ev[r + 1].record(stream)
     ev[-1].synchronize()
-    st = _stats([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
+    st = _stats([ev[r].elapsed_time(ev[r + 1]) / B for r in range(reps)])
+    st["batch"] = B
     _LAST_TIMING["stats"] = st
     return st
 
@@ -474,7 +492,8 @@ def entry(name, ms, nbytes, n, bound="hbm", extra=None, alu=None):
     st = _LAST_TIMING.pop("stats", None)
     if st is not None and st["median"] == ms:
         r.update({"ms_mean": round(st["mean"], 5), "ms_p10": round(st["p10"], 5),
-                  "ms_p90": round(st["p90"], 5), "runs": st["runs"]})
+                  "ms_p90": round(st["p90"], 5), "runs": st["runs"],
+                  "launches_per_run": st.get("batch", 1)})
     if alu is not None:
         r.update(alu_fields(alu, n, ms))
     if extra:
