@@ -978,6 +978,148 @@ def ingest(dirs):
 
 
 # -------------------------------------------------------------------- main --
+DIGEST_FILE = os.path.join(ROOT, "tests", "golden", "workload_digests.json")
+CPU_CONFIGS_FILE = os.path.join(ROOT, "profiles", "cpu_oracle_configs.json")
+
+
+def check_inputs(WL, named) -> dict:
+    """numpy's version and whether the first 2^24-element chunk of each named
+    input (name -> array, or list of arrays) hashes to its recorded digest."""
+    import numpy as np
+    try:
+        with open(DIGEST_FILE) as f:
+            ref = json.load(f)
+    except (OSError, ValueError):
+        return {"numpy": np.__version__, "digests": None}
+    ok = {}
+    for name, (arr, pick) in named.items():
+        ok[name] = WL.chunk_sha256(arr[:WL.CHUNK])[0] == pick(ref)[0]
+    return {"numpy": np.__version__, "digests_numpy": ref.get("numpy"),
+            "first_chunk_sha256_match": ok,
+            "digests": os.path.relpath(DIGEST_FILE, ROOT)}
+
+
+def load_cpu_configs():
+    """The oracle's rates at the workloads' full sizes (`bench.py
+    --cpu-configs`, taken on the GPU machine's host), or None."""
+    try:
+        with open(CPU_CONFIGS_FILE) as f:
+            return json.load(f)
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_configs() -> dict:
+    """The CPU oracle on every workload at its full size (no prefix), on this
+    host: all the OpenMP threads it gives the oracle and one thread.  Best
+    of 3 for QSGD, ternary and ORQ, one run for BinGrad-b / sign split on 1B
+    (two EF steps; one thread: step 0 at d = 512 only) and for the eight
+    INT8 + EF workers and their average (all threads only).  Times exclude
+    drawing the inputs.  Throughput = 4 bytes per input element per second
+    (every element of every step or worker; the aggregation's inputs are
+    counted once, with the quantizes)."""
+    import numpy as np
+
+    import oracle as O
+    from communication_efficient_gradient_amd import workloads as WL
+
+    th = O.threads()
+    res = {"cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+           "threads": th, "numpy": np.__version__, "configs": []}
+
+    def best(fn, reps):
+        b = float("inf")
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            b = min(b, time.perf_counter() - t0)
+        return b
+
+    def add(name, n, fn, reps, one_reps):
+        t = best(fn, reps)
+        rec = {"config": name, "elements": n, "threads": th, "runs": reps,
+               "s": round(t, 4), "elements_per_s": round(n / t),
+               "GBps": round(4 * n / t / 1e9, 4)}
+        if one_reps:
+            O.set_threads(1)
+            try:
+                t1 = best(fn, one_reps)
+            finally:
+                O.set_threads(th)
+            rec.update({"t1_runs": one_reps, "t1_s": round(t1, 4),
+                        "t1_GBps": round(4 * n / t1 / 1e9, 4)})
+        res["configs"].append(rec)
+        log(f"cpu config: {rec}")
+
+    # C1 QSGD s=4, 65,536, quantize + dequantize
+    g = WL.qsgd_gradient()
+    d1 = O.Desc(O.UNIFORM, 512, s=4)
+
+    def c1():
+        c, m, _, _ = O.quantize(d1, g, None, seed=0, step=0)
+        O.dequantize_accumulate(d1, g.size, [c], [m], 1.0, 0.0)
+    add("qsgd s=4 d=512 n=65536, quantize + dequantize", g.size, c1, 3, 3)
+    # C2 ternary + EF, 5 steps over the 160-layer 25.6M gradient
+    steps = [WL.ternary_gradient(t) for t in range(WL.TERNARY_STEPS)]
+    d2 = O.Desc(O.UNIFORM, 512, s=1)
+
+    def c2():
+        e = np.zeros(WL.TERNARY_N, np.float32)
+        for t, gt in enumerate(steps):
+            c, m, e, _ = O.quantize(d2, gt, e, seed=2, step=t)
+            O.dequantize_accumulate(d2, gt.size, [c], [m], 1.0, 0.0)
+    add("ternary + EF d=512 n=25600000, 5 steps of quantize + dequantize",
+        WL.TERNARY_N * WL.TERNARY_STEPS, c2, 3, 3)
+    del steps
+    # C3 ORQ-5 / ORQ-9, clip off / on, 100M
+    g = WL.orq_gradient()
+    for L in (5, 9):
+        for clip in (0, 1):
+            d3 = O.Desc(O.ORQ, 512, L=L, flags=clip, clip_sigma=3.0)
+            add(f"orq L={L} clip={clip} d=512 n={g.size}", g.size,
+                lambda d3=d3: O.quantize(d3, g, None, seed=3, step=0), 3, 3)
+    del g
+    # C4 BinGrad-b / sign split + EF, 1B, two steps
+    g = WL.bingrad_gradient()
+    for scheme, nm in ((O.BIN_OPT, "bin_opt"), (O.BIN_SIGN, "bin_sign")):
+        for dd in BINGRAD_BUCKETS:
+            d4 = O.Desc(scheme, dd)
+
+            def c4(d4=d4):
+                e = np.zeros(g.size, np.float32)
+                for t in range(2):
+                    _, _, e, _ = O.quantize(d4, g, e, seed=0, step=t)
+            add(f"{nm} + EF d={dd} n={g.size}, steps 0 and 1", 2 * g.size, c4, 1, 0)
+        d4 = O.Desc(scheme, 512)
+        O.set_threads(1)
+        try:
+            t1 = best(lambda: O.quantize(d4, g, np.zeros(g.size, np.float32),
+                                         seed=0, step=0), 1)
+        finally:
+            O.set_threads(th)
+        rec = next(r for r in res["configs"]
+                   if r["config"].startswith(f"{nm} + EF d=512 "))
+        rec.update({"t1_runs": 1, "t1_s": round(t1, 4), "t1_config": "step 0 only",
+                    "t1_GBps": round(4 * g.size / t1 / 1e9, 4)})
+        log(f"cpu config: {rec}")
+    del g
+    # C5 eight INT8 + EF workers of 256M and their W = 8 average
+    d5 = O.Desc(O.UNIFORM, 512, s=127)
+    gs = [WL.worker_gradient(w) for w in range(1, WL.WORKERS_W + 1)]
+
+    def c5():
+        cs, ms_ = [], []
+        for w, gw in enumerate(gs, start=1):
+            c, m, _, _ = O.quantize(d5, gw, np.zeros(gw.size, np.float32),
+                                    seed=w, step=0)
+            cs.append(c)
+            ms_.append(m)
+        O.dequantize_accumulate(d5, WL.WORKERS_N, cs, ms_, 1.0 / WL.WORKERS_W, 0.0)
+    add(f"int8 + EF d=512, {WL.WORKERS_W} workers x {WL.WORKERS_N}, then the "
+        f"W={WL.WORKERS_W} average", WL.WORKERS_W * WL.WORKERS_N, c5, 1, 0)
+    return res
+
+
 def load_parity():
     """Whole-payload parity counts of the full-size workloads, as the GPU
     tests last recorded them (tie buckets and mismatched elements per
@@ -1004,10 +1146,21 @@ def main() -> int:
     ap.add_argument("--counters", action="store_true",
                     help="short run for rocprofv3 --pmc: headline steps + a copy")
     ap.add_argument("--ingest", nargs="+", metavar="DIR")
+    ap.add_argument("--cpu-configs", action="store_true",
+                    help="time the CPU oracle on every workload at its full "
+                         "size and store the result in profiles/ (no GPU)")
     args = ap.parse_args()
 
     if args.ingest:
         ingest(args.ingest)
+        return 0
+    if args.cpu_configs:
+        res = cpu_configs()
+        os.makedirs(os.path.dirname(CPU_CONFIGS_FILE), exist_ok=True)
+        with open(CPU_CONFIGS_FILE, "w") as f:
+            json.dump(res, f, indent=1)
+            f.write("\n")
+        print(json.dumps(res))
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -1115,6 +1268,10 @@ def main() -> int:
         cpu = cpu_baseline(hl)
         log(f"cpu baseline: {cpu}")
 
+    inputs = check_inputs(WL, {
+        f"worker {w}": (hl.host[w - 1], lambda r, w=w: r["workers"][w - 1])
+        for w in range(1, hl.W + 1)})
+
     line = {
         "metric": METRIC,
         "value": round(4 * n * W / (ms_step * 1e-3) / 1e9, 3),
@@ -1158,6 +1315,8 @@ def main() -> int:
         },
         "cpu_baseline": cpu,
         "parity_full_size": load_parity(),
+        "cpu_oracle_full_size": load_cpu_configs(),
+        "inputs": inputs,
         "kernels": kernels,
     }
     print(json.dumps(line), flush=True)

@@ -107,6 +107,16 @@ __device__ __forceinline__ int block_argmax(double v, int key, double* redv,
   return key;
 }
 
+// Number of entries below x in a row of 16 ascending floats (+inf padded)
+// in LDS, for x not above the row's last finite entry: 0 .. 15.
+__device__ __forceinline__ int lds_rank16(const float* row, float x) {
+  int pos = row[7] < x ? 8 : 0;
+  pos += row[pos + 3] < x ? 4 : 0;
+  pos += row[pos + 1] < x ? 2 : 0;
+  pos += row[pos] < x ? 1 : 0;
+  return pos;
+}
+
 // Carry for a block-wide segmented scan over per-thread aggregates (f, s):
 // f = the thread's run contains a segment boundary, s = the sum that flows
 // on to the next thread.  Combining an earlier aggregate a with a later b
@@ -564,17 +574,15 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
       __syncthreads();
     }
     if (tid < L) meta[bucket * L + tid] = sh.lev[tid];
+    // +inf past the L levels, for the search of the coding pass
+    if (tid >= L && tid < 16) sh.lev[tid] = __builtin_inff();
+    __syncthreads();
   }
 
   if (codes == nullptr) return;  // levels only
 
   // ---- 5. codes, packing, residual (element order; p kept, or the bucket
   //         read again: the same g + e in fp32) -----------------------------
-  float lv[16];
-  if constexpr (SCHEME == ORQ) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) lv[j] = j < L ? sh.lev[j] : __builtin_inff();
-  }
   const int lane = tid & 63;
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
@@ -616,30 +624,18 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
         code = (!no_split && px[c] >= thr) ? 1u : 0u;
         xh = code ? lvl_b : lvl_a;
       } else {
+        // the levels around x by binary search in LDS: a value on a level
+        // takes it (the first equal one), otherwise it rounds between the
+        // levels below and above
         const float x = clipped(px[c]);
-        int first_eq = -1, below = 0;
-#pragma unroll
-        for (int j = 15; j >= 0; --j)
-          if (j < L && lv[j] == x) first_eq = j;
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (j < L && lv[j] < x) below = j;
-        if (first_eq >= 0) {
-          code = (uint32_t)first_eq;
-        } else {
-          float lo = lv[0], hi = lv[1];
-#pragma unroll
-          for (int j = 0; j < 15; ++j)
-            if (j == below) {
-              lo = lv[j];
-              hi = lv[j + 1];
-            }
-          const float qf = (x - lo) / (hi - lo);
-          code = (uint32_t)(below + (u24(ws[c]) < qf ? 1 : 0));
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if ((uint32_t)j == code) xh = lv[j];
+        const int above = lds_rank16(sh.lev, x);  // levels below x
+        const float hi = sh.lev[above];
+        const float lo = sh.lev[above > 0 ? above - 1 : 0];
+        const float qf = (x - lo) / (hi - lo);
+        const bool up = u24(ws[c]) < qf;
+        const bool on = hi == x;
+        code = (uint32_t)(on ? above : above - 1 + (up ? 1 : 0));
+        xh = on ? x : (up ? hi : lo);
       }
       if (i0 + c >= n) code = 0u;
       field |= code << ((BITS == 0 ? 4 : BITS) * c);
@@ -747,16 +743,6 @@ __device__ __forceinline__ double group_seg_carry_dpp(bool f, double s, int gl) 
   if (gl == 0) ex = 0.0;
   if constexpr (REV) ex = xshfl(ex, G - 1);
   return ex;
-}
-
-// Number of entries below x in a row of 16 ascending floats (+inf padded)
-// in LDS, for x not above the row's last finite entry: 0 .. 15.
-__device__ __forceinline__ int lds_rank16(const float* row, float x) {
-  int pos = row[7] < x ? 8 : 0;
-  pos += row[pos + 3] < x ? 4 : 0;
-  pos += row[pos + 1] < x ? 2 : 0;
-  pos += row[pos] < x ? 1 : 0;
-  return pos;
 }
 
 // Exclusive segmented scan over the G lanes of a group (see block_seg_carry):
