@@ -225,9 +225,11 @@ __device__ __forceinline__ void fb_stage(float (&y)[E], float* lds, int tid,
       __syncthreads();
     }
     (void)lane;
+    // the smaller value to the lower thread: the median of (y, o, -inf) is
+    // min(y, o), of (y, o, +inf) max(y, o); one instruction per value
+    const float sel = lower ? -__builtin_inff() : __builtin_inff();
 #pragma unroll
-    for (int r = 0; r < E; ++r)
-      y[r] = lower ? fminf(y[r], o[r]) : fmaxf(y[r], o[r]);
+    for (int r = 0; r < E; ++r) y[r] = __builtin_amdgcn_fmed3f(y[r], o[r], sel);
   }
 }
 
