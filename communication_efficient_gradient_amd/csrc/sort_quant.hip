@@ -933,8 +933,8 @@ void k_wave_sort_quant(
 #pragma unroll
     for (int m = 0; m < E; ++m)
       if (r0 + m < nj) tot = tot + (double)y[m];
-    const double pre = group_seg_carry<G, false>(false, tot, lane);
-    const double suf = group_seg_carry<G, true>(false, tot, lane);
+    const double pre = group_seg_carry_dpp<G, false>(false, tot, lane);
+    const double suf = group_seg_carry_dpp<G, true>(false, tot, lane);
     double Qrun[E];
     {
       double acc = suf;
@@ -977,6 +977,7 @@ void k_wave_sort_quant(
     const float screen = fmax32 * (1.0f - 1e-5f);
     double best = -1.0;
     int bestk = 0x7fffffff;
+    double bestP = 0.0;  // the sum below this lane's best split
     {
       double P = pre;
 #pragma unroll
@@ -988,6 +989,7 @@ void k_wave_sort_quant(
           if (F > best) {
             best = F;
             bestk = k;
+            bestP = P;
           }
         }
       }
@@ -1000,17 +1002,29 @@ void k_wave_sort_quant(
       lvl_a = lvl_b = thr;
     } else {
       thr = wave_at<E, G>(y, kstar);
-      Sum2 lo{0.0, 0.0}, hi{0.0, 0.0};
+      // the cluster sums: the prefix sum at the split (from the lane that
+      // holds its last lower value) and the rest of the bucket sum; where a
+      // sum is small against the bucket's magnitude (cancellation) both are
+      // recomputed with compensated sums
+      const double Ps = __shfl(bestP, (kstar - 1) / E, G);
+      const double Stot = __shfl(pre + tot + suf, 0, G);  // one value per group
+      const double tiny = 0x1p-20 * (double)amax * (double)nj;
+      double slo = Ps, shi = Stot - Ps;
+      if (fabs(slo) < tiny || fabs(shi) < tiny) {
+        Sum2 lo{0.0, 0.0}, hi{0.0, 0.0};
 #pragma unroll
-      for (int m = 0; m < E; ++m) {
-        const int pos = r0 + m;
-        if (pos < kstar) two_sum_add(lo, (double)y[m]);
-        else if (pos < nj) two_sum_add(hi, (double)y[m]);
+        for (int m = 0; m < E; ++m) {
+          const int pos = r0 + m;
+          if (pos < kstar) two_sum_add(lo, (double)y[m]);
+          else if (pos < nj) two_sum_add(hi, (double)y[m]);
+        }
+        lo = group_sum2<G>(lo);
+        hi = group_sum2<G>(hi);
+        slo = lo.s + lo.c;
+        shi = hi.s + hi.c;
       }
-      lo = group_sum2<G>(lo);
-      hi = group_sum2<G>(hi);
-      lvl_a = (float)((lo.s + lo.c) / (double)kstar);
-      lvl_b = (float)((hi.s + hi.c) / (double)(nj - kstar));
+      lvl_a = (float)(slo / (double)kstar);
+      lvl_b = (float)(shi / (double)(nj - kstar));
     }
     if (lane == 0) {
       meta[2 * bucket + 0] = lvl_a;

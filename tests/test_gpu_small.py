@@ -145,14 +145,15 @@ def test_two_level_ragged_and_degenerate(dev, n):
         check_quantize(dev, O.Desc(scheme, 64), g, np.zeros_like(g))
 
 
-@pytest.mark.parametrize("d", [1024, 4096, 16384, 32768])
+@pytest.mark.parametrize("d", [64, 512, 1024, 4096, 16384, 32768])
 def test_binopt_large_bucket_edge_cases(dev, d):
-    """Large BinGrad-b buckets that take every branch of the sort-free split
-    search: no split (one value), signed zeros, small integers (ties the
+    """BinGrad-b buckets that take every branch of the split selection, in
+    the register-sort kernel (d <= 512) and the sort-free search (d >=
+    1024): no split (one value), signed zeros, small integers (ties the
     search cannot narrow: the bucket goes to the sort-based path), cluster
     sums that cancel (the compensated recomputation), scales outside the
-    fixed-point range (straight to the sort), evenly spread values, and a
-    ragged tail of more than 64 values."""
+    search's fixed-point range (straight to the sort), evenly spread
+    values, and a ragged tail of 100 values."""
     rng = np.random.default_rng(d)
     zeros = np.where(rng.random(d) < 0.5, -0.0, 0.0).astype(np.float32)
     zeros[rng.choice(d, 40, replace=False)] = rng.standard_normal(40).astype(np.float32)
