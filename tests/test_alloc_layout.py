@@ -10,7 +10,13 @@ segment (32 whole codes).  Checked over random layouts and width mixes:
 - the words the threads assemble from their codes are the oracle's packing
   of each layer (LSB-first, segments padded to 16 bytes), and the reads of
   the dequantizer (one word, or two when a 3-bit code straddles) stay
-  inside the segments."""
+  inside the segments.
+
+This is a design aid for the kernel's indexing, written in Python: it can
+pass while the HIP code drifts from it.  The kernel itself is checked by
+tests/test_gpu_alloc_payload.py, whose payloads, maxima and residuals must
+equal the oracle's bit for bit, with the bytes past the last segment
+checked untouched."""
 import numpy as np
 import pytest
 
