@@ -10,16 +10,16 @@
 // integer keys of the canonical values:
 //
 //   1. Levels of refinement.  Each level cuts the candidate key ranges (at
-//      most two; the first level one range, [min, max]) into 16 bins of equal
+//      most two; the first level one range, [min, max]) into 64 bins of equal
 //      width in key space (so a bin is a run of consecutive sorted values, and
 //      its value bounds lo, hi are exact floats).  Every thread adds its
-//      values into its lane's LDS column of the 16-bin (count, sum) histogram
-//      with one 64-bit integer atomic per value (count in the high bits, the
-//      value in fixed point below: exact, order-independent and, on this
-//      GPU, over 20x cheaper than fp32 LDS atomics; lanes of different waves
-//      share a column, which integer atomics keep exact).  Prefix sums give,
-//      at every bin edge, the split position K and the (quantized) sum P of
-//      the values below it.
+//      values into the 64-bin (count, sum) histogram in LDS with one 64-bit
+//      integer atomic per value (count in the high bits, the value in fixed
+//      point below: exact, order-independent and, on this GPU, over 20x
+//      cheaper than fp32 LDS atomics), each bin split into 16 columns by
+//      lane so that few lanes of a wave meet on one address.  Prefix sums
+//      give, at every bin edge, the split position K and the (quantized)
+//      sum P of the values below it.
 //   2. Bounds.  F at every bin edge is a lower bound LB of the optimum.  For
 //      the splits inside a bin, (k, P_k) lies in the parallelogram between
 //      the lines of slope lo and hi from the bin's first edge and into its
@@ -29,8 +29,8 @@
 //      allows cannot hold the optimum and is dropped.  The surviving bins form
 //      at most two new ranges: with survivors in both previous ranges the
 //      hull of each, else the first run of surviving bins and the hull of the
-//      rest.  The first wave evaluates the bins and passes the new ranges to
-//      the others through LDS.
+//      rest.  The first wave evaluates the bins (lane b: bin b) and passes
+//      the new ranges to the others through LDS.
 //   3. When the surviving ranges hold at most 64 values, those values are
 //      gathered, sorted by the first wave, and F is evaluated exactly (fp64
 //      sums of the values below each range, fp64 prefix sums inside) at every
@@ -49,10 +49,11 @@
 namespace gq {
 namespace {
 
-constexpr int kBins = 16;     // bins per level
+constexpr int kBins = 64;     // bins per level (one per lane of the first wave)
+constexpr int kCols = 16;     // LDS columns per bin (lane mod 16)
 constexpr int kCap = 64;      // values the exact stage sorts (one per lane)
 constexpr int kLevels = 10;   // levels before a bucket falls back to the sort
-constexpr int kRow = 64 + 4;  // LDS words per bin row (a column per lane, padded)
+constexpr int kRow = kCols + 2;  // LDS words per bin row (padded)
 // values per thread: 32 (workgroups of 64 to 1024 threads), 16 at d = 1024
 // (one wave).  Every instance fits in 128 VGPRs without spilling (four waves
 // per SIMD); 64 values per thread, tried at d = 16384 and 32768, gave fewer
@@ -207,40 +208,19 @@ __device__ __forceinline__ double row_bcast(double v) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
+template <int BC>
+__device__ __forceinline__ int row_bcast(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, BC == 15 ? 0x142 : 0x143,
+                                     BC == 15 ? 0xA : 0xC, 0xF, false);
+}
+template <int BC>
+__device__ __forceinline__ long long row_bcast(long long v) {
+  return __double_as_longlong(row_bcast<BC>(__longlong_as_double(v)));
+}
+
 template <int N>
 __device__ __forceinline__ long long row_shr(long long v) {
   return __double_as_longlong(row_shr<N>(__longlong_as_double(v)));
-}
-__device__ __forceinline__ long long xshfl(long long v, int o) {
-  return __double_as_longlong(gq::xshfl(__longlong_as_double(v), o));
-}
-
-// Exclusive prefix over the 16 bins that sit in the lanes of a row (bin b
-// in row lane b), restarting at bin `first`.
-template <typename V>
-__device__ __forceinline__ V bin_exclusive(V own, int b, int first) {
-  V v = row_shr<1>(own);
-  if (b <= first) v = V(0);
-  V t = row_shr<1>(v);
-  if (b - 1 >= first) v = v + t;
-  t = row_shr<2>(v);
-  if (b - 2 >= first) v = v + t;
-  t = row_shr<4>(v);
-  if (b - 4 >= first) v = v + t;
-  t = row_shr<8>(v);
-  if (b - 8 >= first) v = v + t;
-  return v;
-}
-
-// The value row lane `idx` holds, in every lane of the row.
-template <typename V>
-__device__ __forceinline__ V row_pick(V v, int b, int idx) {
-  V x = b == idx ? v : V(0);
-  x = x + xshfl(x, 8);
-  x = x + xshfl(x, 4);
-  x = x + xshfl(x, 2);
-  x = x + xshfl(x, 1);
-  return x;
 }
 
 // Inclusive prefix over the G lanes of a group (G = 16, 32, 64).
@@ -253,6 +233,26 @@ __device__ __forceinline__ double group_inclusive(double v) {
   if constexpr (G >= 32) v = v + row_bcast<15>(v);
   if constexpr (G >= 64) v = v + row_bcast<31>(v);
   return v;
+}
+
+// Inclusive prefix over the 64 lanes of a wave (DPP row shifts, then the
+// row broadcasts).
+template <typename V>
+__device__ __forceinline__ V wave_inclusive(V v) {
+  v = v + row_shr<1>(v);
+  v = v + row_shr<2>(v);
+  v = v + row_shr<4>(v);
+  v = v + row_shr<8>(v);
+  v = v + row_bcast<15>(v);
+  v = v + row_bcast<31>(v);
+  return v;
+}
+
+// A 64-bit value of lane `idx` (wave-uniform) in every lane.
+__device__ __forceinline__ long long readlane64(long long v, int idx) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, idx);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), idx);
+  return (long long)(((uint64_t)hi << 32) | lo);
 }
 
 template <int G>
@@ -290,8 +290,7 @@ void k_binopt_block(
   __shared__ __align__(16) Shared sh;
 
   const int tid = threadIdx.x, wv = tid >> 6, wl = tid & 63;
-  const int b = wl & 15;     // the bin of this lane in the bin stages
-  const int part = wl >> 4;  // which 16 columns' partials it sums
+  const int b = wl;  // the bin of this lane in the bin stages (first wave)
   const int64_t bucket = blockIdx.x;
   const int64_t base = bucket * D;
   const int nj = (int)((n - base) < D ? (n - base) : D);
@@ -426,7 +425,7 @@ void k_binopt_block(
   // this lane's histogram column as an LDS-space pointer (32-bit address
   // arithmetic per insertion)
   typedef __attribute__((address_space(3))) unsigned long long lds_u64;
-  lds_u64* const col = (lds_u64*)(sh.h + wl);
+  lds_u64* const col = (lds_u64*)(sh.h + (wl & (kCols - 1)));
   auto hist_add = [&](int bin, unsigned long long v) {
     __atomic_fetch_add(col + __umul24((uint32_t)bin, (uint32_t)kRow), v, __ATOMIC_RELAXED);
   };
@@ -438,7 +437,7 @@ void k_binopt_block(
     const int sh0 = span0 < (uint32_t)nbr ? 0 : 32 - __clz((int)(span0 / (uint32_t)nbr));
     const int sh1 = span1 < (uint32_t)nbr ? 0 : 32 - __clz((int)(span1 / (uint32_t)nbr));
     // clear the histogram (after every wave read the previous level's)
-    for (int i = tid; i < kBins * 64; i += T) sh.h[(i >> 6) * kRow + (i & 63)] = 0ull;
+    for (int i = tid; i < kBins * kCols; i += T) sh.h[(i / kCols) * kRow + (i % kCols)] = 0ull;
     __syncthreads();
     if (lev == 0) {
       // one range, [min, max]: every value has a bin
@@ -461,20 +460,18 @@ void k_binopt_block(
     }
     __syncthreads();
     if (wv == 0) {
-    // ---- per-bin totals (row lane b holds bin b, in every row) -----------
+    // ---- per-bin totals (lane b holds bin b) -----------------------------
     long long bq = 0;
     int bc = 0;
     {
-      const ulonglong2* h2 = reinterpret_cast<const ulonglong2*>(sh.h + b * kRow + part * 16);
+      const ulonglong2* h2 = reinterpret_cast<const ulonglong2*>(sh.h + b * kRow);
       unsigned long long tot = 0ull;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
+      for (int t = 0; t < kCols / 2; ++t) {
         const ulonglong2 v = h2[t];
         tot += v.x + v.y;
       }
-      long long st = (long long)tot;
-      st += xshfl(st, 16);
-      st += xshfl(st, 32);
+      const long long st = (long long)tot;
       bc = (int)((st + (1ll << 47)) >> 48);
       bq = st - ((long long)bc << 48);
     }
@@ -482,8 +479,13 @@ void k_binopt_block(
     const int r = b / nbr;      // range of this bin
     const int first = r * nbr;  // its first bin
     const int j = b - first;    // bin within the range
-    const int exK = bin_exclusive(bc, b, first);
-    const long long exQ = bin_exclusive(bq, b, first);
+    // prefix over the wave, the second range's restarted at its first bin
+    const int inK = wave_inclusive(bc);
+    const long long inQ = wave_inclusive(bq);
+    const int cutK = r == 1 ? __builtin_amdgcn_readlane(inK, nbr - 1) : 0;
+    const long long cutQ = r == 1 ? readlane64(inQ, nbr - 1) : 0ll;
+    const int exK = inK - bc - cutK;
+    const long long exQ = inQ - bq - cutQ;
     const uint32_t rlo = r == 0 ? rlo0 : rlo1, rhi = r == 0 ? rhi0 : rhi1;
     const int shr = r == 0 ? sh0 : sh1;
     const int Kb = (r == 0 ? rk0 : rk1) + exK;
@@ -505,7 +507,7 @@ void k_binopt_block(
         lb = f > lb ? f : lb;
       }
     }
-    LB = fmax(LB, group_max_d<16>(lb));
+    LB = fmax(LB, group_max_d<64>(lb));
     // upper bound: vertices of the clipped parallelogram
     double ub = -1.0;
     if (live) {
@@ -534,26 +536,26 @@ void k_binopt_block(
     }
     const double slack = 1e-12 * fabs(LB);
     const bool keep = live && ub + errF + slack >= LB - errF - slack;
-    // ---- survivors -> at most two ranges (row 0's bits) -------------------
-    const uint32_t mask = (uint32_t)(__ballot(keep) & 0xFFFFull);
-    if (mask == 0u) {
+    // ---- survivors -> at most two ranges ---------------------------------
+    const uint64_t mask = (uint64_t)__ballot(keep);
+    if (mask == 0ull) {
       state = 2;
     } else {
-      const uint32_t m0 = mask & ((1u << nbr) - 1u);
-      const uint32_t m1 = nr == 2 ? mask >> nbr : 0u;
+      const uint64_t m0 = nbr == 64 ? mask : mask & ((1ull << nbr) - 1ull);
+      const uint64_t m1 = nr == 2 ? mask >> nbr : 0ull;
       int a0, a1, b0, b1;
-      if (m0 != 0u && m1 != 0u) {
-        a0 = __builtin_ctz(m0);
-        a1 = 31 - __builtin_clz(m0);
-        b0 = nbr + __builtin_ctz(m1);
-        b1 = nbr + 31 - __builtin_clz(m1);
+      if (m0 != 0ull && m1 != 0ull) {
+        a0 = __builtin_ctzll(m0);
+        a1 = 63 - __builtin_clzll(m0);
+        b0 = nbr + __builtin_ctzll(m1);
+        b1 = nbr + 63 - __builtin_clzll(m1);
       } else {
-        a0 = __builtin_ctz(mask);
-        const uint32_t run = ~(mask >> a0);  // first zero after the run
-        a1 = a0 + __builtin_ctz(run) - 1;
-        const uint32_t rest = mask >> (a1 + 1);
-        b0 = rest ? a1 + 1 + __builtin_ctz(rest) : -1;
-        b1 = 31 - __builtin_clz(mask);
+        a0 = __builtin_ctzll(mask);
+        const uint64_t run = ~(mask >> a0);  // first zero after the run
+        a1 = run == 0ull ? 63 : a0 + __builtin_ctzll(run) - 1;
+        const uint64_t rest = a1 == 63 ? 0ull : mask >> (a1 + 1);
+        b0 = rest ? a1 + 1 + __builtin_ctzll(rest) : -1;
+        b1 = 63 - __builtin_clzll(mask);
       }
       auto bin_lo = [&](int bn) {
         const int rr = bn / nbr;
@@ -566,23 +568,19 @@ void k_binopt_block(
         const uint32_t top = rr == 0 ? rhi0 : rhi1;
         return h > top ? top : (uint32_t)h;
       };
-      // K at a first edge and at a last edge, packed (both <= 2^15, so the
-      // pair fits in 32 unsigned bits)
-      const uint32_t endK = (uint32_t)(Kb + bc);
-      const uint32_t pa =
-          row_pick((b == a0 ? (uint32_t)Kb : 0u) + (b == a1 ? endK << 16 : 0u), b, b);
-      const long long qA = row_pick(Qb, b, a0);
-      const int nk0 = (int)(pa & 0xFFFFu);
-      const int nc0 = (int)(pa >> 16) - nk0;
+      // K at the chosen first and last edges and P at the first edges, from
+      // the lanes of those bins (uniform indices)
+      const int endK = Kb + bc;
+      const int nk0 = __builtin_amdgcn_readlane(Kb, a0);
+      const int nc0 = __builtin_amdgcn_readlane(endK, a1) - nk0;
+      const long long qA = readlane64(Qb, a0);
       int nk1 = 0, nc1 = 0;
       long long nq1 = 0;
       const bool two = b0 >= 0;
       if (two) {
-        const uint32_t pb =
-            row_pick((b == b0 ? (uint32_t)Kb : 0u) + (b == b1 ? endK << 16 : 0u), b, b);
-        nk1 = (int)(pb & 0xFFFFu);
-        nc1 = (int)(pb >> 16) - nk1;
-        nq1 = row_pick(Qb, b, b0);
+        nk1 = __builtin_amdgcn_readlane(Kb, b0);
+        nc1 = __builtin_amdgcn_readlane(endK, b1) - nk1;
+        nq1 = readlane64(Qb, b0);
       }
       const uint32_t nlo0 = bin_lo(a0), nhi0 = bin_hi(a1);
       const uint32_t nlo1 = two ? bin_lo(b0) : 0u, nhi1 = two ? bin_hi(b1) : 0u;
