@@ -140,11 +140,12 @@ def binopt_prune_ops() -> float:
     1024 and more): EF add (1); order-preserving key (2); bucket minimum,
     maximum, sum and absolute sum (4); the first level's bin, fixed-point
     value and LDS add for every element (5); the second level's range test
-    and insertion, which reaches nearly every element (7); three more levels'
-    range tests (6); the exact stage's sums below the ranges and survivor test
-    (7); threshold compare, level select, residual subtract, pack (4).  The
-    bin evaluation and the survivor sort are per bucket, not per element."""
-    return 1 + 2 + 4 + 5 + 7 + 6 + 7 + 4
+    and insertion, which reaches nearly every element (7); one more level's
+    range test (2; 64 bins per level leave 2-3 levels); the exact stage's
+    sums below the ranges and survivor test (7); threshold compare, level
+    select, residual subtract, pack (4).  The bin evaluation and the
+    survivor sort are per bucket, not per element."""
+    return 1 + 2 + 4 + 5 + 7 + 2 + 7 + 4
 
 
 def topk_ops(d: int, K: int) -> float:

@@ -46,7 +46,7 @@ def test_alu_op_counts():
     assert bench.orq_ops(9, 512, bisect=True) == 45 + 30 + 3 + 20 + 10
     assert bench.orq_ops(5, 512, bisect=True) == 45 + 20 + 2 + 20 + 10
     assert bench.binopt_ops(512) == 1 + 45 + 2 + 6 + 1 + 4
-    assert bench.binopt_prune_ops() == 36
+    assert bench.binopt_prune_ops() == 32
     f = bench.alu_fields(100.0, 10 ** 8, 1.0)
     assert abs(f["alu_frac"] - 1e10 / 1e-3 / bench.VALU_PEAK_LANE_OPS) < 1e-4
 
