@@ -156,14 +156,12 @@ int gq_code_bits(const gq_desc* desc, int32_t* bits) {
 }
 
 int gq_payload_size(const gq_desc* desc, int64_t n, int64_t* code_bytes,
-                    int64_t* code_capacity, int64_t* meta_floats) {
+                    int64_t* meta_floats) {
   gq::LaunchDesc L;
   const int rc = check_desc(desc, &L);
   if (rc) return rc;
   if (n < 1 || n > kMaxN) return GQ_EINVAL;
-  const int64_t cb = code_bytes_of(L, n);
-  if (code_bytes) *code_bytes = cb;
-  if (code_capacity) *code_capacity = (cb + 15) / 16 * 16;
+  if (code_bytes) *code_bytes = code_bytes_of(L, n);
   if (meta_floats) *meta_floats = meta_floats_of(L, n);
   return GQ_OK;
 }

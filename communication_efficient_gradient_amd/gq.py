@@ -64,8 +64,7 @@ def _load():
     D = C.POINTER(gq_desc)
     i64, i32 = C.c_int64, C.c_int32
     lib.gq_code_bits.argtypes = [D, C.POINTER(i32)]
-    lib.gq_payload_size.argtypes = [D, i64, C.POINTER(i64), C.POINTER(i64),
-                                    C.POINTER(i64)]
+    lib.gq_payload_size.argtypes = [D, i64, C.POINTER(i64), C.POINTER(i64)]
     lib.gq_select_levels.argtypes = [D, i64, P, P, P, P]
     lib.gq_quantize.argtypes = [D, i64, P, P, C.c_uint64, C.c_uint32, P, P, P]
     lib.gq_error_feedback.argtypes = [D, i64, P, P, P, P, P]
@@ -128,11 +127,13 @@ def gq_code_bits(d: gq_desc) -> int:
 
 
 def gq_payload_size(d: gq_desc, n: int):
-    """Returns (code_bytes, code_capacity, meta_floats)."""
-    cb, cap, mf = C.c_int64(), C.c_int64(), C.c_int64()
-    _check(_lib.gq_payload_size(C.byref(d), n, C.byref(cb), C.byref(cap),
-                                C.byref(mf)), "gq_payload_size")
-    return cb.value, cap.value, mf.value
+    """Returns (code_bytes, code_capacity, meta_floats); code_capacity is
+    code_bytes rounded up to a multiple of 16, the size of a codes buffer
+    that gq_quantize writes."""
+    cb, mf = C.c_int64(), C.c_int64()
+    _check(_lib.gq_payload_size(C.byref(d), n, C.byref(cb), C.byref(mf)),
+           "gq_payload_size")
+    return cb.value, (cb.value + 15) // 16 * 16, mf.value
 
 
 def _ptr(t, dtype, what):

@@ -157,12 +157,12 @@ enum {
 int gq_code_bits(const gq_desc* desc, int32_t* bits);
 
 /* Payload sizes for n elements: code_bytes = ceil(n*bits/8) (dense:
- * ceil(ceil(n/8)*W/8)); code_capacity
- * = code_bytes rounded up to a multiple of 16 (the size a codes buffer
- * written by gq_quantize must have); meta_floats = ceil(n/d) * k.
- * Any output pointer may be NULL.  Host-only. */
+ * ceil(ceil(n/8)*W/8)); meta_floats = ceil(n/d) * k.  A codes buffer that
+ * gq_quantize writes must hold code_bytes rounded up to a multiple of 16
+ * (it stores whole 32-bit words; the bytes past code_bytes are written as
+ * 0).  Either output pointer may be NULL.  Host-only. */
 int gq_payload_size(const gq_desc* desc, int64_t n, int64_t* code_bytes,
-                    int64_t* code_capacity, int64_t* meta_floats);
+                    int64_t* meta_floats);
 
 /* Per-bucket levels of p = g (+ e when e != NULL) into meta, exactly as
  * gq_quantize would compute them; nothing else is written. */
@@ -174,7 +174,8 @@ int gq_select_levels(const gq_desc* desc, int64_t n, const float* g,
  * (i/4, step); element i uses word i mod 4, u = (word >> 8) * 2^-24; with
  * GQ_FLAG_NEAREST u = 1/2), pack.
  * With e != NULL, e is read and then overwritten in place with the residual
- * p - dequant(code) (unclipped p).  codes: code_capacity bytes.  e must not
+ * p - dequant(code) (unclipped p).  codes: code_bytes rounded up to a
+ * multiple of 16 bytes.  e must not
  * overlap g, codes or meta. */
 int gq_quantize(const gq_desc* desc, int64_t n, const float* g, float* e,
                 uint64_t seed, uint32_t step, uint8_t* codes, float* meta,
@@ -312,8 +313,8 @@ int gq_dequantize_accumulate_layers_alloc(
 /* Words the stream needs at most: every code with |c| = s.  Host-only. */
 int gq_elias_max_words(const gq_desc* desc, int64_t n, int64_t* max_words);
 
-/* Encode the n codes of a gq_quantize payload (codes: code_capacity bytes,
- * fixed-width layout) into words (gq_elias_max_words words) and offsets
+/* Encode the n codes of a gq_quantize payload (codes: code_bytes rounded
+ * up to 16, fixed-width layout) into words (gq_elias_max_words words) and offsets
  * (nb + 1).  Codes outside [-s, s] (never written by gq_quantize) are
  * clamped to that range.  Three launches; offsets doubles as the scan's
  * workspace, so no other memory is used.  codes, offsets and words must not
@@ -324,9 +325,10 @@ int gq_elias_encode(const gq_desc* desc, int64_t n, const uint8_t* codes,
 /* Decode an Elias stream back into the fixed-width codes gq_quantize wrote
  * (bit-identical for a stream from gq_elias_encode), ready for
  * gq_dequantize_accumulate.  n_words >= 1: the readable length of words
- * (reads stay below it; offsets are clamped to it).  Writes ceil(code_bytes / 4)
- * 32-bit words of codes (capacity: code_capacity bytes).  A corrupt stream
- * gives unspecified codes but no out-of-bounds access. */
+ * (reads stay below it; offsets are clamped to it).  Writes
+ * ceil(code_bytes / 4) 32-bit words of codes (capacity: code_bytes rounded
+ * up to 16).  A corrupt stream gives unspecified codes but no out-of-bounds
+ * access. */
 int gq_elias_decode(const gq_desc* desc, int64_t n, const uint64_t* offsets,
                     const uint32_t* words, int64_t n_words, uint8_t* codes,
                     void* stream);

@@ -95,7 +95,7 @@ def test_validation_before_launch(gq):
     assert L.gq_dequantize_accumulate(C.byref(d), 100, 0, cp, mp, 1.0, 0.0, fake, None) == -1
     assert L.gq_dequantize_accumulate(C.byref(d), 100, 2, cp, mp, float("nan"), 0.0, fake, None) == -1
     assert L.gq_dequantize_accumulate(C.byref(d), 100, 2, cp, mp, 1.0, 0.0, fake * 2, None) == -1
-    assert L.gq_payload_size(C.byref(d), 0, None, None, None) == -1
+    assert L.gq_payload_size(C.byref(d), 0, None, None) == -1
     assert L.gq_code_bits(None, None) == -1
 
 
