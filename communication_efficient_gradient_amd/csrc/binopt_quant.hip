@@ -260,22 +260,40 @@ __device__ __forceinline__ int group_min_i(int v) {
   return group_reduce<G>(v, [](int a, int b) { return a < b ? a : b; });
 }
 
-template <int D>
+// Key of a raw fp32 bit pattern with -0 folded onto +0 (keys of finite
+// values lie in [0x00800000, 0xff7fffff]).
+__device__ __forceinline__ uint32_t canon_key(uint32_t b, bool negz) {
+  const uint32_t k = b ^ ((uint32_t)((int)b >> 31) | 0x80000000u);
+  return k + (negz ? 1u : 0u);  // ~0x80000000 + 1 = key of +0
+}
+
+// 1 / x in fp64: hardware estimate and one Newton step (a few ulps).
+__device__ __forceinline__ double rcp_nr(double x) {
+  const double r = __builtin_amdgcn_rcp(x);
+  return __builtin_fma(r, __builtin_fma(-x, r, 1.0), r);
+}
+
+// FULL: every bucket of the launch holds D values (the last, shorter bucket
+// has a launch of its own, so the main grid carries no bounds tests).
+template <int D, bool EF, bool FULL>
 __global__ __launch_bounds__(D / elems_per_thread(D), D / elems_per_thread(D) == 256 ? 3 : 1)
 void k_binopt_block(
     int64_t n, const float* __restrict__ g, float* __restrict__ e,
-    uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes) {
+    uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes,
+    int64_t first_bucket) {
   constexpr int E = elems_per_thread(D);
   constexpr int T = D / E;
   constexpr int NQ = E / 4;
   constexpr int NW = T / 64;
   struct Shared {
-    // per bin, one column per lane: count << 48 plus the fixed-point sum
+    // per bin, one column per lane: count << 48 plus the biased fixed-point sum
     unsigned long long h[kBins * kRow];
-    float v[kCap];             // survivors
-    double rd[4][NW];          // per-wave partials: S, A, sums below the ranges
+    float v[NW][2 * kCap];     // survivors, gathered per wave (the upper
+                               // half takes the other lanes' stores)
+    int wc[NW];                // survivors per wave
+    double rd[4][NW];          // per-wave partials: S, sums below the ranges
+    float ra[NW];              // per-wave sum |p|
     uint32_t ru[2][NW];        // per-wave key minima / maxima
-    int cnt;                   // survivors gathered
     uint32_t kthr;             // exact stage result: threshold key,
     float la, lb;              //   levels,
     int flag;                  //   0 done, 1 recompute sums, 2 fall back
@@ -291,56 +309,61 @@ void k_binopt_block(
 
   const int tid = threadIdx.x, wv = tid >> 6, wl = tid & 63;
   const int b = wl;  // the bin of this lane in the bin stages (first wave)
-  const int64_t bucket = blockIdx.x;
+  const int64_t bucket = first_bucket + blockIdx.x;
   const int64_t base = bucket * D;
-  const int nj = (int)((n - base) < D ? (n - base) : D);
-  const bool full = nj == D;
+  const int nj = FULL ? D : (int)((n - base) < D ? (n - base) : D);
   // whether held value m is in the gradient (recomputed at each use: kept,
   // the tests of the last bucket took one scalar register pair per value)
   const int rem = nj - 4 * tid;
   auto valid = [&](int m) {
-    return full | (4 * T * (m / 4) + (m % 4) < (int)opaque((uint32_t)rem));
+    if constexpr (FULL) return true;
+    else return 4 * T * (m / 4) + (m % 4) < (int)opaque((uint32_t)rem);
   };
 
   // ---- load p = g (+ e); thread t holds the float4s t, t + T, ...; keep
-  //      the keys of the canonical values (-0 -> +0) and which were -0;
-  //      bucket statistics on the way: key range, S = sum, A = sum |p|
-  //      (fp64; wave partials combined in wave order) ----------------------
+  //      the keys of the canonical values (-0 -> +0); whether the wave saw a
+  //      -0 at all (one scalar mask: the residual of a -0 differs from that
+  //      of +0 only when its level is +0, and that rare case re-reads p);
+  //      bucket statistics on the way: key range, S = sum (fp64), A = sum |p|
+  //      (only a scale for a threshold: fp32) -----------------------------
   uint32_t kk[E];
-  static_assert(E <= 32, "one bit per held value in negz");
-  uint32_t negz = 0u;
+  uint64_t zmask = 0ull;
   uint32_t kmn = 0xffffffffu, kmx = 0u;
-  double S = 0.0, A = 0.0;
+  double S = 0.0;
+  float Af = 0.f;
   auto take = [&](int q, float4 x) {
     const float xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float v = xs[c];
-      if (v == 0.f && __float_as_uint(v) != 0u) negz |= 1u << (4 * q + c);
-      const float cv = v == 0.f ? 0.f : v;
-      const uint32_t key = fkey(cv);
+      const uint32_t bits = __float_as_uint(v);
+      const bool nz = bits == 0x80000000u;
+      zmask |= __ballot(nz);
+      const uint32_t key = canon_key(bits, nz);
       kk[4 * q + c] = key;
       const bool ok = valid(4 * q + c);
       kmn = (ok & (key < kmn)) ? key : kmn;
       kmx = (ok & (key > kmx)) ? key : kmx;
-      S = ok ? S + (double)cv : S;
-      A = ok ? A + (double)fabsf(cv) : A;
+      S = ok ? S + (double)v : S;
+      Af = ok ? Af + fabsf(v) : Af;
     }
   };
-  if (full) {
+  if constexpr (FULL) {
+    float4 xq[NQ];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int64_t i = base + 4 * (tid + (int64_t)T * q);
-      float4 x = load4_nt(g + i);
-      if (e != nullptr) {
-        const float4 r = load4_nt(e + i);
-        x.x = x.x + r.x;
-        x.y = x.y + r.y;
-        x.z = x.z + r.z;
-        x.w = x.w + r.w;
+    for (int q = 0; q < NQ; ++q) xq[q] = load4_nt(g + base + 4 * (tid + (int64_t)T * q));
+    if constexpr (EF) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const float4 r = load4_nt(e + base + 4 * (tid + (int64_t)T * q));
+        xq[q].x = xq[q].x + r.x;
+        xq[q].y = xq[q].y + r.y;
+        xq[q].z = xq[q].z + r.z;
+        xq[q].w = xq[q].w + r.w;
       }
-      take(q, x);
     }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) take(q, xq[q]);
   } else {
     // the last bucket: element-wise bounds, one float4 at a time
 #pragma unroll
@@ -348,7 +371,7 @@ void k_binopt_block(
       asm volatile("" ::: "memory");
       const int64_t i = base + 4 * (tid + (int64_t)T * q);
       float4 x = load4(g, i, n);
-      if (e != nullptr) {
+      if constexpr (EF) {
         const float4 r = load4(e, i, n);
         x.x = x.x + r.x;
         x.y = x.y + r.y;
@@ -358,42 +381,42 @@ void k_binopt_block(
       take(q, x);
     }
   }
-  // the -0 flags as one integer from here on (not one predicate per value)
-  negz = opaque(negz);
 
   kmn = group_min_u<64>(kmn);
   kmx = group_max_u<64>(kmx);
   S = group_sum_d<64>(S);
-  A = group_sum_d<64>(A);
+  Af = group_reduce<64>(Af, [](float a, float c) { return a + c; });
   if (wl == 0) {
     sh.ru[0][wv] = kmn;
     sh.ru[1][wv] = kmx;
     sh.rd[0][wv] = S;
-    sh.rd[1][wv] = A;
+    sh.ra[wv] = Af;
   }
   __syncthreads();
   kmn = sh.ru[0][0];
   kmx = sh.ru[1][0];
   S = sh.rd[0][0];
-  A = sh.rd[1][0];
+  Af = sh.ra[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) {
     kmn = sh.ru[0][w] < kmn ? sh.ru[0][w] : kmn;
     kmx = sh.ru[1][w] > kmx ? sh.ru[1][w] : kmx;
     S = S + sh.rd[0][w];
-    A = A + sh.rd[1][w];
+    Af = Af + sh.ra[w];
   }
   // combined here, not where first used (the wave partials' loads were
   // otherwise kept in registers, or spilled, until the exact stage)
-  asm volatile("" : "+v"(S), "+v"(A));
+  asm volatile("" : "+v"(S), "+v"(Af));
+  const double A = (double)Af;
   const double dn = (double)nj;
 
   // The histogram sums are fixed point: value x adds q = trunc(x 2^f), with
-  // 2^f chosen so that |q| < 2^30 for every value (so any sum of at most
-  // 2^16 of them stays below 2^47 and fits under the count, which sits from
-  // bit 48).  The sum of the quantized values below any split is then exact,
-  // and |P_q - P| < nj 2^-f =: dP.  F moves by at most 2 |a - b| d + 4 d^2
-  // when P moves by d, and |a - b| <= max - min.
+  // 2^f chosen so that |q| < 2^30 for every value; the LDS word holds
+  // 2^48 + q + 2^30 (count from bit 48, a nonnegative sum below it: at most
+  // 2^15 values of less than 2^31 stay below 2^46).  The sum of the
+  // quantized values below any split is then exact, and |P_q - P| < nj 2^-f
+  // =: dP.  F moves by at most 2 |a - b| d + 4 d^2 when P moves by d, and
+  // |a - b| <= max - min.
   const float amax = fmaxf(fabsf(funkey(kmn)), fabsf(funkey(kmx)));
   int ex = 0;
   frexpf(amax, &ex);  // amax < 2^ex
@@ -417,45 +440,61 @@ void k_binopt_block(
   // 0: refining, 1: exact stage, 2: fall back to the sort.  Buckets whose
   // scale 2^f would leave fp32's range go to the sort directly.
   const bool sane = amax < 0x1p90f && amax > 0x1p-90f;
-  auto packed = [&](uint32_t k) {
-    const long long q = (long long)(int)(kval(k) * fscale);
-    return (unsigned long long)(q + (1ll << 48));
-  };
   int state = !split_exists ? 1 : (nj <= kCap ? 1 : (sane ? 0 : 2));
   // this lane's histogram column as an LDS-space pointer (32-bit address
   // arithmetic per insertion)
   typedef __attribute__((address_space(3))) unsigned long long lds_u64;
   lds_u64* const col = (lds_u64*)(sh.h + (wl & (kCols - 1)));
-  auto hist_add = [&](int bin, unsigned long long v) {
+  auto hist_add = [&](int bin, uint32_t k) {
+    const uint32_t q = (uint32_t)((int)(kval(k) * fscale) + (1 << 30));
+    const unsigned long long v = (0x10000ull << 32) | q;
     __atomic_fetch_add(col + __umul24((uint32_t)bin, (uint32_t)kRow), v, __ATOMIC_RELAXED);
+  };
+  auto uni = [](uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); };
+  auto uni64 = [](long long x) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+    return (long long)(((uint64_t)hi << 32) | lo);
   };
 
   for (int lev = 0; lev < kLevels && state == 0; ++lev) {
-    const int nbr = kBins / nr;  // bins per range
+    const int lgb = nr == 2 ? 5 : 6;  // log2 of the bins per range
+    const int nbr = 1 << lgb;
     // shift of each range: (hi - lo) >> sh < nbr
     const uint32_t span0 = rhi0 - rlo0, span1 = rhi1 - rlo1;
-    const int sh0 = span0 < (uint32_t)nbr ? 0 : 32 - __clz((int)(span0 / (uint32_t)nbr));
-    const int sh1 = span1 < (uint32_t)nbr ? 0 : 32 - __clz((int)(span1 / (uint32_t)nbr));
-    // clear the histogram (after every wave read the previous level's)
-    for (int i = tid; i < kBins * kCols; i += T) sh.h[(i / kCols) * kRow + (i % kCols)] = 0ull;
+    const int sh0 = (span0 >> lgb) == 0u ? 0 : 32 - __clz((int)(span0 >> lgb));
+    const int sh1 = (span1 >> lgb) == 0u ? 0 : 32 - __clz((int)(span1 >> lgb));
+    // clear the histogram's columns (after every wave read the previous
+    // level's), 16 bytes per store
+    {
+      ulonglong2* const h2 = reinterpret_cast<ulonglong2*>(sh.h);
+#pragma unroll
+      for (int i = tid; i < kBins * kCols / 2; i += T)
+        h2[(i / (kCols / 2)) * (kRow / 2) + (i % (kCols / 2))] = make_ulonglong2(0ull, 0ull);
+    }
     __syncthreads();
     if (lev == 0) {
       // one range, [min, max]: every value has a bin
 #pragma unroll
       for (int m = 0; m < E; ++m) {
         if (!valid(m)) continue;
-        const int bin = (int)((kk[m] - rlo0) >> sh0);
-        hist_add(bin, packed(kk[m]));
+        hist_add((int)((kk[m] - rlo0) >> sh0), kk[m]);
+      }
+    } else if (nr == 1) {
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        const uint32_t t0 = kk[m] - rlo0;
+        if (!valid(m) | (t0 > span0)) continue;
+        hist_add((int)(t0 >> sh0), kk[m]);
       }
     } else {
 #pragma unroll
       for (int m = 0; m < E; ++m) {
         const uint32_t k = kk[m];
-        const bool in0 = k - rlo0 <= span0;
-        const bool in1 = nr == 2 && k - rlo1 <= span1;
-        if (!valid(m) || !(in0 || in1)) continue;
-        const int bin = in0 ? (int)((k - rlo0) >> sh0) : nbr + (int)((k - rlo1) >> sh1);
-        hist_add(bin, packed(k));
+        const uint32_t t0 = k - rlo0, t1 = k - rlo1;
+        const bool in0 = t0 <= span0;
+        if (!valid(m) | !(in0 | (t1 <= span1))) continue;
+        hist_add(in0 ? (int)(t0 >> sh0) : nbr + (int)(t1 >> sh1), k);
       }
     }
     __syncthreads();
@@ -471,14 +510,12 @@ void k_binopt_block(
         const ulonglong2 v = h2[t];
         tot += v.x + v.y;
       }
-      const long long st = (long long)tot;
-      bc = (int)((st + (1ll << 47)) >> 48);
-      bq = st - ((long long)bc << 48);
+      bc = (int)(tot >> 48);
+      bq = (long long)(tot & 0xffffffffffffull) - ((long long)bc << 30);
     }
     // ---- edges: K and P at the bin's first edge --------------------------
-    const int r = b / nbr;      // range of this bin
-    const int first = r * nbr;  // its first bin
-    const int j = b - first;    // bin within the range
+    const int r = b >> lgb;     // range of this bin
+    const int j = b - (r << lgb);  // bin within the range
     // prefix over the wave, the second range's restarted at its first bin
     const int inK = wave_inclusive(bc);
     const long long inQ = wave_inclusive(bq);
@@ -493,47 +530,49 @@ void k_binopt_block(
     const double Pb = (double)Qb * funit;
     const double bs = (double)bq * funit;
     const uint64_t klo64 = (uint64_t)rlo + ((uint64_t)j << shr);
-    uint64_t khi64 = (uint64_t)rlo + ((uint64_t)(j + 1) << shr) - 1;
+    uint64_t khi64 = klo64 + ((uint64_t)1 << shr) - 1;
     if (khi64 > rhi) khi64 = rhi;
     const bool live = klo64 <= (uint64_t)rhi && bc > 0;
     const uint32_t klo = (uint32_t)(live ? klo64 : rlo);
     const uint32_t khi = (uint32_t)(live ? khi64 : rlo);
-    // lower bound: F at both edges of every non-empty bin
-    double lb = -1.0;
-    if (live) {
-      if (Kb > 0) lb = obj_fast(Pb, (double)Kb, S, dn);
-      if (Kb + bc < nj) {
-        const double f = obj_fast(Pb + bs, (double)(Kb + bc), S, dn);
-        lb = f > lb ? f : lb;
+    // The splits inside the bin: (Kb + j, P) with j in [j0, j1] (the
+    // bucket's ends excluded) and P - Pb between the lower boundary
+    // max(j lo, bs - (c - j) hi) and the upper min(j hi, bs - (c - j) lo).
+    // F is convex, so its maximum there is at a vertex: the bin's edges (or,
+    // at a bucket end, the two boundary points at j0 or j1) and the two
+    // corners of the boundaries.  F at an inner edge is also a lower bound.
+    const double lo = (double)funkey(klo), hi = (double)funkey(khi);
+    const double c = (double)bc;
+    const bool ext0 = Kb == 0, ext1 = Kb + bc == nj;
+    const double j0 = ext0 ? 1.0 : 0.0;
+    const double j1 = ext1 ? c - 1.0 : c;
+    const bool has = live && j0 <= j1;
+    const double dK = (double)Kb;
+    auto Lw = [&](double jj) { return Pb + fmax(jj * lo, bs - (c - jj) * hi); };
+    auto Up = [&](double jj) { return Pb + fmin(jj * hi, bs - (c - jj) * lo); };
+    double lb = -1.0, ub = -1.0;
+    if (has) {
+      const double fa = obj_fast(ext0 ? Lw(j0) : Pb, dK + j0, S, dn);
+      const double fc = obj_fast(ext1 ? Up(j1) : Pb + bs, dK + j1, S, dn);
+      ub = fmax(fa, fc);
+      lb = fmax(ext0 ? -1.0 : fa, ext1 ? -1.0 : fc);
+      if (hi > lo) {
+        const double rd = rcp_nr(hi - lo);
+        const double jl = (c * hi - bs) * rd;  // lower boundary's corner
+        const double ju = (bs - c * lo) * rd;  // upper boundary's corner
+        if (jl > j0 && jl < j1) ub = fmax(ub, obj_fast(Pb + jl * lo, dK + jl, S, dn));
+        if (ju > j0 && ju < j1) ub = fmax(ub, obj_fast(Pb + ju * hi, dK + ju, S, dn));
+      }
+    }
+    // the other boundary point at a clipped end (bins holding the bucket's
+    // smallest or largest value)
+    if (__ballot(has & (ext0 | ext1)) != 0ull) {
+      if (has & (ext0 | ext1)) {
+        ub = fmax(ub, obj_fast(ext0 ? Up(j0) : Pb, dK + j0, S, dn));
+        ub = fmax(ub, obj_fast(ext1 ? Lw(j1) : Pb + bs, dK + j1, S, dn));
       }
     }
     LB = fmax(LB, group_max_d<64>(lb));
-    // upper bound: vertices of the clipped parallelogram
-    double ub = -1.0;
-    if (live) {
-      const double lo = (double)funkey(klo), hi = (double)funkey(khi);
-      const double c = (double)bc;
-      const double j0 = Kb == 0 ? 1.0 : 0.0;
-      const double j1 = Kb + bc == nj ? c - 1.0 : c;
-      if (j0 <= j1) {
-        auto Lw = [&](double jj) { return Pb + fmax(jj * lo, bs - (c - jj) * hi); };
-        auto Up = [&](double jj) { return Pb + fmin(jj * hi, bs - (c - jj) * lo); };
-        auto at = [&](double jj, double P) {
-          const double f = obj_fast(P, (double)Kb + jj, S, dn);
-          ub = f > ub ? f : ub;
-        };
-        at(j0, Lw(j0));
-        at(j0, Up(j0));
-        at(j1, Lw(j1));
-        at(j1, Up(j1));
-        if (hi > lo) {
-          const double jl = (c * hi - bs) / (hi - lo);  // lower boundary's corner
-          const double ju = (bs - c * lo) / (hi - lo);  // upper boundary's corner
-          if (jl > j0 && jl < j1) at(jl, Pb + jl * lo);
-          if (ju > j0 && ju < j1) at(ju, Pb + ju * hi);
-        }
-      }
-    }
     const double slack = 1e-12 * fabs(LB);
     const bool keep = live && ub + errF + slack >= LB - errF - slack;
     // ---- survivors -> at most two ranges ---------------------------------
@@ -558,13 +597,13 @@ void k_binopt_block(
         b1 = 63 - __builtin_clzll(mask);
       }
       auto bin_lo = [&](int bn) {
-        const int rr = bn / nbr;
-        return (rr == 0 ? rlo0 : rlo1) + (uint32_t)((uint64_t)(bn - rr * nbr) << (rr == 0 ? sh0 : sh1));
+        const int rr = bn >> lgb;
+        return (rr == 0 ? rlo0 : rlo1) + (uint32_t)((uint64_t)(bn - (rr << lgb)) << (rr == 0 ? sh0 : sh1));
       };
       auto bin_hi = [&](int bn) {
-        const int rr = bn / nbr;
+        const int rr = bn >> lgb;
         const uint64_t h = (uint64_t)(rr == 0 ? rlo0 : rlo1) +
-                           ((uint64_t)(bn - rr * nbr + 1) << (rr == 0 ? sh0 : sh1)) - 1;
+                           ((uint64_t)(bn - (rr << lgb) + 1) << (rr == 0 ? sh0 : sh1)) - 1;
         const uint32_t top = rr == 0 ? rhi0 : rhi1;
         return h > top ? top : (uint32_t)h;
       };
@@ -615,19 +654,20 @@ void k_binopt_block(
     }
     }  // first wave
     __syncthreads();
-    rlo0 = sh.nlo[0];
-    rhi0 = sh.nhi[0];
-    rk0 = sh.nk[0];
-    rq0 = sh.nq[0];
-    rc0 = sh.nc[0];
-    rlo1 = sh.nlo[1];
-    rhi1 = sh.nhi[1];
-    rk1 = sh.nk[1];
-    rq1 = sh.nq[1];
-    rc1 = sh.nc[1];
-    nr = sh.nnr;
-    state = sh.nst;
-    LB = sh.nlb;
+    // the same in every lane: scalar registers from here
+    rlo0 = uni(sh.nlo[0]);
+    rhi0 = uni(sh.nhi[0]);
+    rk0 = (int)uni((uint32_t)sh.nk[0]);
+    rq0 = uni64(sh.nq[0]);
+    rc0 = (int)uni((uint32_t)sh.nc[0]);
+    rlo1 = uni(sh.nlo[1]);
+    rhi1 = uni(sh.nhi[1]);
+    rk1 = (int)uni((uint32_t)sh.nk[1]);
+    rq1 = uni64(sh.nq[1]);
+    rc1 = (int)uni((uint32_t)sh.nc[1]);
+    nr = (int)uni((uint32_t)sh.nnr);
+    state = (int)uni((uint32_t)sh.nst);
+    LB = __longlong_as_double(uni64(__double_as_longlong(sh.nlb)));
     __syncthreads();  // the next level clears the histogram
   }
   if (state == 0) state = 2;
@@ -650,43 +690,37 @@ void k_binopt_block(
     kthr = 0xffffffffu;  // every code 0 (keys of finite values are below
                          // 0xff800000)
   } else {
-    auto in_ranges = [&](uint32_t k) {
-      // bitwise, not short-circuit: no branch per value
-      return (k - rlo0 <= rhi0 - rlo0) | ((nr == 2) & (k - rlo1 <= rhi1 - rlo1));
-    };
-    // each lane's survivors, their offsets in the wave, then one LDS
-    // reservation per wave
-    int own = 0;
-    double p0 = 0.0, p1 = 0.0;  // sums below each range start (fp64)
+    // one pass: the fp64 sums below each range start, and the survivors
+    // appended to this wave's list (offsets from the wave's ballot).  With
+    // one range, rlo1 = rhi1 = 0 hold no key of a finite value.
+    double p0 = 0.0, p1 = 0.0;
+    int woff = 0;
+    // x times 1.0 or 0.0 (the selected constant has a zero low word)
+    auto gate = [](bool c) { return __hiloint2double(c ? 0x3ff00000 : 0, 0); };
 #pragma unroll
     for (int m = 0; m < E; ++m) {
       const bool v = valid(m);
-      const uint32_t k = opaque(kk[m]);
-      const double dx = (double)kval(k);
-      p0 = (v & (k < rlo0)) ? p0 + dx : p0;
-      p1 = (v & (nr == 2) & (k < rlo1)) ? p1 + dx : p1;
-      own += (int)(v & in_ranges(k));
+      const uint32_t k = kk[m];
+      const float x = kval(k);
+      const double dx = (double)x;
+      p0 = __builtin_fma(dx, gate(v & (k < rlo0)), p0);
+      p1 = __builtin_fma(dx, gate(v & (k < rlo1)), p1);
+      const bool in0 = v & (k - rlo0 <= rhi0 - rlo0);
+      const bool in1 = v & (k - rlo1 <= rhi1 - rlo1);
+      const uint64_t bal = (uint64_t)__ballot(in0) | (uint64_t)__ballot(in1);
+      const int pos = woff + (int)__builtin_amdgcn_mbcnt_hi(
+                                 (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      // every lane stores (no branch per value): the others to a slot of
+      // their own above the list
+      sh.v[wv][((in0 | in1) & (pos < kCap)) ? pos : kCap + wl] = x;
+      woff += __popcll(bal);
     }
-    const int incl = (int)group_inclusive<64>((double)own);
-    const int wcnt = __builtin_amdgcn_readlane(incl, 63);
     p0 = group_sum_d<64>(p0);
     p1 = group_sum_d<64>(p1);
-    if (tid == 0) sh.cnt = 0;
     if (wl == 0) {
       sh.rd[2][wv] = p0;
       sh.rd[3][wv] = p1;
-    }
-    __syncthreads();
-    int wbase = 0;
-    if (wl == 0 && wcnt > 0) wbase = atomicAdd(&sh.cnt, wcnt);
-    wbase = __builtin_amdgcn_readfirstlane(wbase);
-    int pos = wbase + incl - own;
-#pragma unroll
-    for (int m = 0; m < E; ++m) {
-      const uint32_t k = opaque(kk[m]);
-      const bool in = valid(m) & in_ranges(k);
-      if (in & (pos < kCap)) sh.v[pos] = kval(k);
-      pos += (int)in;
+      sh.wc[wv] = woff;
     }
     __syncthreads();
     p0 = sh.rd[2][0];
@@ -696,25 +730,32 @@ void k_binopt_block(
       p0 = p0 + sh.rd[2][w];
       p1 = p1 + sh.rd[3][w];
     }
-    const int cnt = sh.cnt;
     if (wv == 0) {
-      // one survivor per lane, sorted
-      float y[1];
-      y[0] = wl < cnt ? sh.v[wl] : __builtin_inff();
+      // one survivor per lane (the waves' lists in wave order), sorted
+      int cnt = 0;
+      float y[1] = {__builtin_inff()};
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int cw = sh.wc[w];
+        const int at = wl - cnt;
+        if (at >= 0 && at < cw && at < kCap) y[0] = sh.v[w][at];
+        cnt += cw;
+      }
       sv_levels<1, kCap, 2>(y, wl);
       const double own = wl < cnt ? (double)y[0] : 0.0;
       const double pre0 = group_inclusive<64>(own) - own;  // sum before this position
       const int off1 = rc0;                                  // start of range 1
-      const double pre_off1 = group_sum_d<64>(wl == off1 ? pre0 : 0.0);
-      const double pre_end = group_sum_d<64>(own);         // all survivors
+      const double pre_off1 = off1 < 64 ? __longlong_as_double(readlane64(__double_as_longlong(pre0), off1)) : 0.0;
       const float y_prev = __shfl_up(y[0], 1, 64);
       double bestF = -1.0;
       int bestK = 0x7fffffff;
       uint32_t bestT = 0u;
       double bestP = 0.0;
+      // F to a few ulps: buckets whose best two splits are closer than
+      // that are ties, and either split is correct there
       auto consider = [&](int k, double P, uint32_t kt) {
         if (k <= 0 || k >= nj) return;
-        const double f = obj_exact(P, (double)k, S, dn);
+        const double f = obj_fast(P, (double)k, S, dn);
         if (f > bestF || (f == bestF && k < bestK)) {
           bestF = f;
           bestK = k;
@@ -737,13 +778,14 @@ void k_binopt_block(
           consider(k2, P2, (r1 ? rhi1 : rhi0) + 1u);
         }
       }
-      (void)pre_end;
-      double gF = bestF;
-      int gK = bestK;
-      group_argmax_dk<64>(gF, gK);
-      const int win = group_min_i<64>(bestK == gK && bestF == gF ? wl : 64);
-      const uint32_t kt = (uint32_t)group_sum_i<64>(wl == win ? (int)bestT : 0);
-      const double Ps = group_sum_d<64>(wl == win ? bestP : 0.0);
+      // the largest F, then the smallest split: lanes hold increasing
+      // splits, so the first lane reaching the maximum
+      const double gF = group_max_d<64>(bestF);
+      const uint64_t at_max = (uint64_t)__ballot(bestF == gF);
+      const int win = __builtin_ctzll(at_max);
+      const int gK = __builtin_amdgcn_readlane(bestK, win);
+      const uint32_t kt = (uint32_t)__builtin_amdgcn_readlane((int)bestT, win);
+      const double Ps = __longlong_as_double(readlane64(__double_as_longlong(bestP), win));
       if (wl == 0) {
         if (gF < 0.0 || cnt > kCap) {
           sh.flag = 2;  // no candidate (cannot happen when the bounds hold)
@@ -808,33 +850,58 @@ void k_binopt_block(
   if (codes == nullptr) return;  // levels only
 
   // ---- codes, packing, residual (element order) ---------------------------
+  // A -0 keeps its sign in the residual only against a +0 level; a wave
+  // holding a -0 in a bucket with a zero level re-reads p for its residual.
+  const bool reread = EF && zmask != 0ull && (la == 0.f || lb_ == 0.f);
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int64_t i0 = base + 4 * (tid + (int64_t)T * q);
     uint32_t field = 0u;
     float r[4];
+    float4 praw = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (reread) {
+      praw = load4(g, i0, n);
+      const float4 er = load4(e, i0, n);
+      praw.x = praw.x + er.x;
+      praw.y = praw.y + er.y;
+      praw.z = praw.z + er.z;
+      praw.w = praw.w + er.w;
+    }
+    const float pr[4] = {praw.x, praw.y, praw.z, praw.w};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int m = 4 * q + c;
       const uint32_t code = (valid(m) && kk[m] >= kthr) ? 1u : 0u;
       field |= code << c;
-      const float pv = (negz >> m) & 1u ? -0.0f : kval(kk[m]);
+      const float pv = reread ? pr[c] : kval(kk[m]);
       r[c] = pv - (code ? lb_ : la);
     }
     store_chunk<1, 4>(codes, i0, wl, field, code_bytes);
-    if (e != nullptr && i0 < n) {
-      if (full) store4_nt(e + i0, make_float4(r[0], r[1], r[2], r[3]));
+    if (EF && i0 < n) {
+      if constexpr (FULL) store4_nt(e + i0, make_float4(r[0], r[1], r[2], r[3]));
       else store4(e, i0, n, make_float4(r[0], r[1], r[2], r[3]));
     }
   }
 }
 
+template <int D, bool EF>
+void launch_ef(int64_t n, const float* g, float* e, uint8_t* codes, float* meta,
+               int64_t code_bytes, hipStream_t st) {
+  const int64_t nfull = n / D;
+  const dim3 block(D / elems_per_thread(D));
+  if (nfull > 0)
+    hipLaunchKernelGGL((k_binopt_block<D, EF, true>), dim3((uint32_t)nfull), block, 0, st,
+                       n, g, e, codes, meta, code_bytes, (int64_t)0);
+  if (n % D != 0)
+    hipLaunchKernelGGL((k_binopt_block<D, EF, false>), dim3(1), block, 0, st,
+                       n, g, e, codes, meta, code_bytes, nfull);
+}
+
 template <int D>
 int launch_one(int64_t n, const float* g, float* e, uint8_t* codes, float* meta,
                int64_t code_bytes, hipStream_t st) {
-  const int64_t nb = (n + D - 1) / D;
-  hipLaunchKernelGGL((k_binopt_block<D>), dim3((uint32_t)nb), dim3(D / elems_per_thread(D)), 0, st,
-                     n, g, e, codes, meta, code_bytes);
+  if (e != nullptr) launch_ef<D, true>(n, g, e, codes, meta, code_bytes, st);
+  else launch_ef<D, false>(n, g, e, codes, meta, code_bytes, st);
   return (int)hipGetLastError();
 }
 
