@@ -811,10 +811,14 @@ __device__ __forceinline__ float wave_at(const float (&y)[E], int pos) {
 
 // NT: nontemporal 128-bit access for whole float4s (streams read or written
 // once; ORQ's first read is not one: it reads its bucket again from cache)
-template <int VEC, bool NT = false>
+// INB: the vector is known to lie inside the gradient (no bounds tests).
+template <int VEC, bool NT = false, bool INB = false>
 __device__ __forceinline__ void load_vec(const float* __restrict__ a,
                                          int64_t i, int64_t n, float (&x)[VEC]) {
-  if constexpr (VEC == 4) {
+  if constexpr (VEC == 4 && INB) {
+    const float4 v = NT ? load4_nt(a + i) : *reinterpret_cast<const float4*>(a + i);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  } else if constexpr (VEC == 4) {
     const float4 v = (NT && i + 4 <= n) ? load4_nt(a + i) : load4(a, i, n);
     x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
   } else {
@@ -832,10 +836,13 @@ __device__ __forceinline__ void load_vec(const float* __restrict__ a,
   }
 }
 
-template <int VEC, bool NT = false>
+template <int VEC, bool NT = false, bool INB = false>
 __device__ __forceinline__ void store_vec(float* __restrict__ a, int64_t i,
                                           int64_t n, const float (&x)[VEC]) {
-  if constexpr (VEC == 4) {
+  if constexpr (VEC == 4 && INB) {
+    if (NT) store4_nt(a + i, make_float4(x[0], x[1], x[2], x[3]));
+    else *reinterpret_cast<float4*>(a + i) = make_float4(x[0], x[1], x[2], x[3]);
+  } else if constexpr (VEC == 4) {
     if (NT && i + 4 <= n) store4_nt(a + i, make_float4(x[0], x[1], x[2], x[3]));
     else store4(a, i, n, make_float4(x[0], x[1], x[2], x[3]));
   } else {
@@ -852,10 +859,13 @@ __device__ __forceinline__ void store_vec(float* __restrict__ a, int64_t i,
 // At most 128 VGPRs (4 waves per SIMD): the recursive-bisection variant
 // would take 132 and run at 3 (ORQ-9 by bisection on 100M: 2.20 -> 1.94 ms
 // at 4 with 16 bytes per lane spilled); the others fit without spilling.
-template <int SCHEME, int BITS, int D, bool BISECT>
+// FULL: every bucket of the launch holds D values (a short last bucket runs
+// in a launch of its own), so no value needs a bounds test.  Buckets
+// b0 .. nb-1.
+template <int SCHEME, int BITS, int D, bool BISECT, bool FULL>
 __global__ __launch_bounds__(kGroupThreads, 4)
 void k_wave_sort_quant(
-    int64_t n, int64_t nb, const float* __restrict__ g, float* __restrict__ e,
+    int64_t n, int64_t b0, int64_t nb, const float* __restrict__ g, float* __restrict__ e,
     uint32_t k0, uint32_t k1, uint32_t step, int L, int flags, float clip_sigma,
     uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes,
     uint32_t A4, int W, int redo) {
@@ -865,7 +875,7 @@ void k_wave_sort_quant(
   constexpr int NQ = E / VEC;
   const int lane = threadIdx.x % G;  // lane within the bucket's group
   const int64_t bucket =
-      (int64_t)blockIdx.x * (kGroupThreads / G) + threadIdx.x / G;
+      b0 + (int64_t)blockIdx.x * (kGroupThreads / G) + threadIdx.x / G;
   if (bucket >= nb) return;  // whole groups leave together
   // redo: only the buckets the sort-free BinGrad-b kernel marked with NaN
   // levels (group-uniform)
@@ -873,7 +883,7 @@ void k_wave_sort_quant(
     if (redo && meta[2 * bucket] == meta[2 * bucket]) return;
   }
   const int64_t base = bucket * D;
-  const int nj = (int)((n - base) < D ? (n - base) : D);
+  const int nj = FULL ? D : (int)((n - base) < D ? (n - base) : D);
 
   // ---- 1. load p = g (+ e), element order --------------------------------
   float p[E];
@@ -881,10 +891,10 @@ void k_wave_sort_quant(
   for (int q = 0; q < NQ; ++q) {
     const int64_t i = base + (int64_t)VEC * (lane + G * q);
     float x[VEC];
-    load_vec<VEC, SCHEME == BIN_OPT>(g, i, n, x);
+    load_vec<VEC, SCHEME == BIN_OPT, FULL>(g, i, n, x);
     if (e != nullptr) {
       float r[VEC];
-      load_vec<VEC, SCHEME == BIN_OPT>(e, i, n, r);
+      load_vec<VEC, SCHEME == BIN_OPT, FULL>(e, i, n, r);
 #pragma unroll
       for (int c = 0; c < VEC; ++c) x[c] = x[c] + r[c];
     }
@@ -1248,10 +1258,10 @@ void k_wave_sort_quant(
     for (int q = 0; q < NQ; ++q) {
       const int64_t i = base + (int64_t)VEC * (lane + G * q);
       float x[VEC];
-      load_vec<VEC>(g, i, n, x);
+      load_vec<VEC, false, FULL>(g, i, n, x);
       if (e != nullptr) {
         float r[VEC];
-        load_vec<VEC>(e, i, n, r);
+        load_vec<VEC, false, FULL>(e, i, n, r);
 #pragma unroll
         for (int c = 0; c < VEC; ++c) x[c] = x[c] + r[c];
       }
@@ -1281,7 +1291,7 @@ void k_wave_sort_quant(
     for (int c = 0; c < VEC; ++c) {
       const int m = VEC * q + c;
       const int64_t i = i0 + c;
-      const bool real = i < n;
+      const bool real = FULL || i < n;
       uint32_t code = 0u;
       float xh = 0.f;
       if constexpr (SCHEME == BIN_OPT) {
@@ -1310,7 +1320,7 @@ void k_wave_sort_quant(
     }
     if constexpr (BITS == 0) dfield[q] = field;
     else store_chunk<BITS, VEC>(codes, i0, lane, field, code_bytes);
-    if (e != nullptr && i0 < n) store_vec<VEC, true>(e, i0, n, r);
+    if (e != nullptr && (FULL || i0 < n)) store_vec<VEC, true, FULL>(e, i0, n, r);
   }
   // Dense fields are stored once the values and levels are dead.  Dense ORQ
   // runs with d >= 512 only, so here a bucket is one wave.
@@ -1331,24 +1341,26 @@ int launch_sort_one(int64_t n, const float* g, float* e, uint64_t seed,
   if (BITS == 0 && D < 512) return (int)hipErrorInvalidValue;  // dense: d >= 512
   if constexpr (D <= 512) {
     constexpr int per_block = kGroupThreads / WaveCfg<D>::G;
-    const int64_t blocks = (nb + per_block - 1) / per_block;
-    bool bisect = false;
-    if constexpr (SCHEME == ORQ) {
-      if (flags & GQ_FLAG_BISECT) {
-        bisect = true;
-        hipLaunchKernelGGL((k_wave_sort_quant<SCHEME, BITS, D, true>),
-                           dim3((uint32_t)blocks), dim3(kGroupThreads), 0, st,
-                           n, nb, g, e, (uint32_t)seed, (uint32_t)(seed >> 32),
+    // the whole buckets, then (one block) the short last one
+    const int64_t nfull = n / D;
+    auto go = [&](auto kern, int64_t first, int64_t end) {
+      const int64_t blocks = (end - first + per_block - 1) / per_block;
+      if (blocks > 0)
+        hipLaunchKernelGGL(kern, dim3((uint32_t)blocks), dim3(kGroupThreads), 0, st,
+                           n, first, end, g, e, (uint32_t)seed, (uint32_t)(seed >> 32),
                            step, L, flags, clip_sigma, codes, meta, code_bytes,
                            A4, W, redo);
+    };
+    const bool bisect = SCHEME == ORQ && (flags & GQ_FLAG_BISECT) != 0;
+    if (bisect) {
+      if constexpr (SCHEME == ORQ) {
+        go(k_wave_sort_quant<SCHEME, BITS, D, true, true>, 0, nfull);
+        go(k_wave_sort_quant<SCHEME, BITS, D, true, false>, nfull, nb);
       }
+    } else {
+      go(k_wave_sort_quant<SCHEME, BITS, D, false, true>, 0, nfull);
+      go(k_wave_sort_quant<SCHEME, BITS, D, false, false>, nfull, nb);
     }
-    if (!bisect)
-      hipLaunchKernelGGL((k_wave_sort_quant<SCHEME, BITS, D, false>),
-                         dim3((uint32_t)blocks), dim3(kGroupThreads), 0, st, n,
-                         nb, g, e, (uint32_t)seed, (uint32_t)(seed >> 32), step,
-                         L, flags, clip_sigma, codes, meta, code_bytes, A4, W,
-                         redo);
   } else {
     hipLaunchKernelGGL((k_sort_quant<SCHEME, BITS, D>), dim3((uint32_t)nb),
                        dim3(SortCfg<D>::T), 0, st, n, g, e, (uint32_t)seed,
