@@ -154,6 +154,23 @@ __device__ __forceinline__ double xshfl(double v, int o) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
+// The value of lane (lane ^ M) through the LDS crossbar: ds_swizzle inside
+// 32-lane halves (bit-mask mode: and 0x1f, xor M), ds_bpermute across them.
+// No VALU instruction for the exchange itself, so a VALU-bound kernel with
+// several independent exchanges in flight leaves them to the LDS pipe (a
+// single dependent exchange is faster with xshfl's DPP moves).  Workgroups
+// are whole waves, so threadIdx.x & 63 is the lane.
+template <int M>
+__device__ __forceinline__ float lane_xor_ds(float v) {
+  static_assert(M > 0 && M < 64, "lane mask");
+  if constexpr (M < 32) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1f | (M << 10)));
+  } else {
+    const int src = (int)((threadIdx.x & 63u) ^ (unsigned)M) << 2;
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v)));
+  }
+}
+
 // ------------------------------------------------------- group reductions --
 // Butterfly reductions over aligned groups of G lanes inside one wave
 // (G <= 64): exchange distances G/2, G/4, ..., 1, unrolled at compile time.

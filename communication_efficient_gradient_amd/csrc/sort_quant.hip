@@ -182,7 +182,8 @@ __device__ __forceinline__ double block_seg_carry(bool f, double s,
 // compile time.
 
 // stage with partner i ^ MASK; MASK = K-1 (mirror) or J (power of two)
-template <int E, int MASK, bool MIRROR>
+// WIDE: the sort spans 64 lanes or more (a wave or a workgroup).
+template <int E, int MASK, bool MIRROR, bool WIDE>
 __device__ __forceinline__ void fb_stage(float (&y)[E], float* lds, int tid,
                                          int lane) {
   constexpr int TOP = MIRROR ? (MASK + 1) / 2 : MASK;  // bit deciding lower
@@ -203,8 +204,15 @@ __device__ __forceinline__ void fb_stage(float (&y)[E], float* lds, int tid,
     const bool lower = (tid & (TOP / E)) == 0;
     float o[E];
     if constexpr (LM < 64) {
+      // through the LDS crossbar (no VALU work), except, in groups of at
+      // most 32 lanes (fewer exchanges in flight per lane group), the
+      // partners that one DPP move reaches
+      constexpr bool dpp = LM == 1 || LM == 2 || LM == 3 || LM == 7 || LM == 8 || LM == 15;
 #pragma unroll
-      for (int r = 0; r < E; ++r) o[r] = xshfl(y[MIRROR ? E - 1 - r : r], LM);
+      for (int r = 0; r < E; ++r) {
+        if constexpr (dpp && !WIDE) o[r] = xshfl(y[MIRROR ? E - 1 - r : r], LM);
+        else o[r] = lane_xor_ds<LM>(y[MIRROR ? E - 1 - r : r]);
+      }
     } else {
       float4* l4 = reinterpret_cast<float4*>(lds);
 #pragma unroll
@@ -233,21 +241,36 @@ __device__ __forceinline__ void fb_stage(float (&y)[E], float* lds, int tid,
   }
 }
 
-template <int E, int K, int J>
+template <int E, int K, int J, bool WIDE>
 __device__ __forceinline__ void fb_halves(float (&y)[E], float* lds, int tid,
                                           int lane) {
   if constexpr (J >= 1) {
-    fb_stage<E, J, false>(y, lds, tid, lane);
-    fb_halves<E, K, J / 2>(y, lds, tid, lane);
+    fb_stage<E, J, false, WIDE>(y, lds, tid, lane);
+    fb_halves<E, K, J / 2, WIDE>(y, lds, tid, lane);
   }
 }
 
 template <int E, int N, int K>
 __device__ __forceinline__ void fb_levels(float (&y)[E], float* lds, int tid,
                                           int lane) {
-  fb_stage<E, K - 1, true>(y, lds, tid, lane);
-  fb_halves<E, K, K / 4>(y, lds, tid, lane);
+  constexpr bool WIDE = N / E >= 64;
+  fb_stage<E, K - 1, true, WIDE>(y, lds, tid, lane);
+  fb_halves<E, K, K / 4, WIDE>(y, lds, tid, lane);
   if constexpr (K < N) fb_levels<E, N, 2 * K>(y, lds, tid, lane);
+}
+
+// The 8 values of one thread ascending: a 19-comparator network (depth 6)
+// in place of the bitonic levels 2, 4 and 8 (24 comparators).
+__device__ __forceinline__ void sort8(float (&y)[8]) {
+  constexpr int net[19][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}, {0, 4}, {1, 5}, {2, 6},
+                              {3, 7}, {0, 1}, {2, 3}, {4, 5}, {6, 7}, {2, 4}, {3, 5},
+                              {1, 4}, {3, 6}, {1, 2}, {3, 4}, {5, 6}};
+#pragma unroll
+  for (int c = 0; c < 19; ++c) {
+    const float a = y[net[c][0]], b = y[net[c][1]];
+    y[net[c][0]] = fminf(a, b);
+    y[net[c][1]] = fmaxf(a, b);
+  }
 }
 
 // Sort N = T*E values (T threads of a workgroup, or the lanes of one group
@@ -256,7 +279,12 @@ __device__ __forceinline__ void fb_levels(float (&y)[E], float* lds, int tid,
 template <int E, int N>
 __device__ __forceinline__ void flip_bitonic(float (&y)[E], float* lds,
                                              int tid) {
-  fb_levels<E, N, 2>(y, lds, tid, tid & 63);
+  if constexpr (E == 8 && N > 8) {
+    sort8(y);
+    fb_levels<E, N, 16>(y, lds, tid, tid & 63);
+  } else {
+    fb_levels<E, N, 2>(y, lds, tid, tid & 63);
+  }
 }
 
 struct SortShared {
