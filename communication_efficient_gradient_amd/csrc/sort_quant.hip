@@ -731,12 +731,31 @@ __device__ __forceinline__ double dpp_bcast(double v) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
+// 1.0 where c holds, else 0.0 (one select: the low word is zero in both).
+// fma(x, gate(c), y) is c ? x + y : y for finite x, with x + y rounded once.
+__device__ __forceinline__ double gate(bool c) {
+  return __hiloint2double(c ? 0x3ff00000 : 0, 0);
+}
+
+// lane ^ M through the LDS crossbar, for ints and doubles.
+template <int M>
+__device__ __forceinline__ int lane_xor_ds_i(int v) {
+  return __float_as_int(lane_xor_ds<M>(__int_as_float(v)));
+}
+template <int M>
+__device__ __forceinline__ double lane_xor_ds_d(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)lane_xor_ds_i<M>((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)lane_xor_ds_i<M>((int)(uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 // Inclusive segmented scan over the G lanes of a group in lane order, by DPP
 // steps: (f, s) of the lanes up to this one combined as in block_seg_carry.
 template <int G>
 __device__ __forceinline__ void group_seg_incl(int& f, double& s, int gl) {
   auto step = [&](double sp, int fp) {
-    s = f ? s : sp + s;
+    s = __builtin_fma(sp, gate(f == 0), s);  // f ? s : sp + s
     f |= fp;
   };
   auto shr = [&](auto tag) {
@@ -763,15 +782,15 @@ __device__ __forceinline__ void group_seg_incl(int& f, double& s, int gl) {
 template <int G, bool REV>
 __device__ __forceinline__ double group_seg_carry_dpp(bool f, double s, int gl) {
   int fi = f ? 1 : 0;
-  if constexpr (REV) {
-    s = xshfl(s, G - 1);
-    fi = xshfl(fi, G - 1);
+  if constexpr (REV) {  // the mirror through the LDS crossbar
+    s = lane_xor_ds_d<G - 1>(s);
+    fi = lane_xor_ds_i<G - 1>(fi);
   }
   // scan and shift in physical lane order (mirrored order for REV)
   group_seg_incl<G>(fi, s, gl);
   double ex = __shfl_up(s, 1, G);
   if (gl == 0) ex = 0.0;
-  if constexpr (REV) ex = xshfl(ex, G - 1);
+  if constexpr (REV) ex = lane_xor_ds_d<G - 1>(ex);
   return ex;
 }
 
@@ -811,6 +830,24 @@ __device__ __forceinline__ int group_argmax(double v, int key, double* best_out)
   }
   *best_out = v;
   return key;
+}
+
+// The same where keys increase with the lane: the key of the first lane of
+// the group holding the maximum (a max reduction, a ballot, one read).
+template <int G>
+__device__ __forceinline__ int group_argmax_first(double v, int key, double* best_out) {
+  double m = v;
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) m = fmax(m, xshfl(m, o));
+  *best_out = m;
+  const uint64_t at = (uint64_t)__ballot(v == m);
+  if constexpr (G == 64) {
+    return __builtin_amdgcn_readlane(key, __builtin_ctzll(at));
+  } else {
+    const int base = (int)(threadIdx.x & 63u) & ~(G - 1);
+    const uint32_t mine = (uint32_t)(at >> base) & (uint32_t)((1ull << G) - 1ull);
+    return __shfl(key, base + __builtin_ctz(mine), 64);
+  }
 }
 
 // The same argmax in two reductions: the group maximum of the value, then
@@ -1126,15 +1163,13 @@ void k_wave_sort_quant(
 #pragma unroll
       for (int m = 0; m < E; ++m) {
         const bool h = head(m);
-        const double v = va(m);
-        sa = h ? v : sa + v;
+        sa = __builtin_fma(sa, gate(!h), va(m));  // h ? v : sa + v
         fa |= h ? 1 : 0;
       }
 #pragma unroll
       for (int m = E - 1; m >= 0; --m) {
         const bool t = tail(m);
-        const double v = vb(m);
-        sb = t ? v : sb + v;
+        sb = __builtin_fma(sb, gate(!t), vb(m));
         fb |= t ? 1 : 0;
       }
       const double ca = group_seg_carry_dpp<G, false>(fa != 0, sa, lane);
@@ -1145,19 +1180,18 @@ void k_wave_sort_quant(
       // segment, then m's gain G (-1 for a value that is no candidate)
       double Gs[E];
       {
-        double run = cb;
+        double run = cb;  // >= 0
 #pragma unroll
         for (int m = E - 1; m >= 0; --m) {
           const bool t = tail(m);
-          const double v = vb(m);
-          Gs[m] = t ? 0.0 : run;
-          run = t ? v : run + v;
+          Gs[m] = run * gate(!t);  // t ? 0 : run
+          run = __builtin_fma(run, gate(!t), vb(m));
         }
         double A = ca;
 #pragma unroll
         for (int m = 0; m < E; ++m) {
           const double v = va(m);
-          A = head(m) ? v : A + v;
+          A = __builtin_fma(A, gate(!head(m)), v);
           const int pos = r0 + m;
           const float yv = y[m];
           const float ynext = (m + 1 < E) ? y[m + 1] : y_next_run;
@@ -1166,11 +1200,11 @@ void k_wave_sort_quant(
           const bool cand = pos < nj && a_of[m] < ymax && yv > a_of[m] &&
                             (pos + 1 >= nj || ynext != yv);
           // (b - c) A + (c - a) B, with b - c and c - a exact in fp64
-          const double Gv = cand ? vb(m) * A + v * Gs[m] : -1.0;
-          const bool better = Gv > best;
+          const double Gv = vb(m) * A + v * Gs[m];
+          const bool better = cand && Gv > best;
           best = better ? Gv : best;
           bestk = better ? pos : bestk;
-          Gs[m] = Gv;
+          if constexpr (BISECT) Gs[m] = cand ? Gv : -1.0;
         }
       }
       // insert c after every level below it (levels stay ascending; c lies
@@ -1208,7 +1242,7 @@ void k_wave_sort_quant(
       };
       if constexpr (!BISECT) {
         double bestG;
-        const int kstar = group_argmax<G>(best, bestk, &bestG);
+        const int kstar = group_argmax_first<G>(best, bestk, &bestG);
         if (bestG < 0.0) fill_with_max();
         else insert_level(wave_at<E, G>(y, kstar));
       } else {
