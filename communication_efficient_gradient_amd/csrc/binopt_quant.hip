@@ -187,7 +187,8 @@ __device__ __forceinline__ uint64_t group_lanes(int grp) {
 // first N lanes): one DPP move, no LDS.
 template <int N>
 __device__ __forceinline__ int row_shr(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, 0x110 + N, 0xF, 0xF, false);
+  // every lane written (bound_ctrl zero-fills the first N of a row)
+  return __builtin_amdgcn_mov_dpp(v, 0x110 + N, 0xF, 0xF, true);
 }
 template <int N>
 __device__ __forceinline__ double row_shr(double v) {

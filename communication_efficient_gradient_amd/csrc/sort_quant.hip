@@ -709,7 +709,9 @@ struct WaveCfg {
 // rows 1 and 3) or lane 31 (BC = 31: rows 2 and 3), 0 elsewhere.
 template <int N>
 __device__ __forceinline__ int dpp_shr(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, 0x110 + N, 0xF, 0xF, false);
+  // every lane written (bound_ctrl zero-fills the first N of a row), so no
+  // old value to set up
+  return __builtin_amdgcn_mov_dpp(v, 0x110 + N, 0xF, 0xF, true);
 }
 template <int BC>
 __device__ __forceinline__ int dpp_bcast(int v) {
