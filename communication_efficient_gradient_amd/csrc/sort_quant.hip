@@ -1159,19 +1159,27 @@ void k_wave_sort_quant(
       auto tail = [&](int m) {
         return m == E - 1 ? (last_lane || seg_next != sid(E - 1)) : sid(m) != sid(m + 1);
       };
+      // restart ? v : s + v; the greedy kernel takes it as one fma with a
+      // 1.0/0.0 factor (one select instead of two), the bisection kernel
+      // (more live state) as selects, which need no register pair for the
+      // factor
+      auto acc = [](double s, bool restart, double v) {
+        if constexpr (BISECT) return restart ? v : s + v;
+        else return __builtin_fma(s, gate(!restart), v);
+      };
       // this lane's partial sums (branch-free), then the group's carries
       int fa = 0, fb = 0;
       double sa = 0.0, sb = 0.0;
 #pragma unroll
       for (int m = 0; m < E; ++m) {
         const bool h = head(m);
-        sa = __builtin_fma(sa, gate(!h), va(m));  // h ? v : sa + v
+        sa = acc(sa, h, va(m));
         fa |= h ? 1 : 0;
       }
 #pragma unroll
       for (int m = E - 1; m >= 0; --m) {
         const bool t = tail(m);
-        sb = __builtin_fma(sb, gate(!t), vb(m));
+        sb = acc(sb, t, vb(m));
         fb |= t ? 1 : 0;
       }
       const double ca = group_seg_carry_dpp<G, false>(fa != 0, sa, lane);
@@ -1186,14 +1194,14 @@ void k_wave_sort_quant(
 #pragma unroll
         for (int m = E - 1; m >= 0; --m) {
           const bool t = tail(m);
-          Gs[m] = run * gate(!t);  // t ? 0 : run
-          run = __builtin_fma(run, gate(!t), vb(m));
+          Gs[m] = t ? 0.0 : run;
+          run = acc(run, t, vb(m));
         }
         double A = ca;
 #pragma unroll
         for (int m = 0; m < E; ++m) {
           const double v = va(m);
-          A = __builtin_fma(A, gate(!head(m)), v);
+          A = acc(A, head(m), v);
           const int pos = r0 + m;
           const float yv = y[m];
           const float ynext = (m + 1 < E) ? y[m + 1] : y_next_run;
@@ -1202,11 +1210,18 @@ void k_wave_sort_quant(
           const bool cand = pos < nj && a_of[m] < ymax && yv > a_of[m] &&
                             (pos + 1 >= nj || ynext != yv);
           // (b - c) A + (c - a) B, with b - c and c - a exact in fp64
-          const double Gv = vb(m) * A + v * Gs[m];
-          const bool better = cand && Gv > best;
-          best = better ? Gv : best;
-          bestk = better ? pos : bestk;
-          if constexpr (BISECT) Gs[m] = cand ? Gv : -1.0;
+          if constexpr (BISECT) {
+            const double Gv = cand ? vb(m) * A + v * Gs[m] : -1.0;
+            const bool better = Gv > best;
+            best = better ? Gv : best;
+            bestk = better ? pos : bestk;
+            Gs[m] = Gv;
+          } else {
+            const double Gv = vb(m) * A + v * Gs[m];
+            const bool better = cand && Gv > best;
+            best = better ? Gv : best;
+            bestk = better ? pos : bestk;
+          }
         }
       }
       // insert c after every level below it (levels stay ascending; c lies
