@@ -733,6 +733,12 @@ __device__ __forceinline__ double dpp_bcast(double v) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
+// 1 / x in fp64: hardware estimate and one Newton step (a few ulps).
+__device__ __forceinline__ double rcp_nr(double x) {
+  const double r = __builtin_amdgcn_rcp(x);
+  return __builtin_fma(r, __builtin_fma(-x, r, 1.0), r);
+}
+
 // 1.0 where c holds, else 0.0 (one select: the low word is zero in both).
 // fma(x, gate(c), y) is c ? x + y : y for finite x, with x + y rounded once.
 __device__ __forceinline__ double gate(bool c) {
@@ -1022,10 +1028,12 @@ void k_wave_sort_quant(
       }
     }
     // F(k) = P^2/k + Q^2/(n-k) at every split between distinct values: first
-    // in fp32 (a screen), then exactly in fp64 only where the screen is
-    // within 1e-5 of its maximum (two fp64 divisions per split otherwise).  The screen's error (< 1e-6 relative,
-    // both terms >= 0, values scaled by a power of two so |P|, |Q| <= d)
-    // keeps the exact maximum and every exact tie among the candidates.
+    // in fp32 (a screen), then in fp64 only where the screen is within 1e-5
+    // of its maximum.  The screen's error (< 1e-6 relative, both terms >= 0,
+    // values scaled by a power of two so |P|, |Q| <= d) keeps the maximum
+    // and every tie among the candidates.  The fp64 values take refined
+    // reciprocals (a few ulps): splits closer than that are ties, where
+    // either is correct.
     const float amax = fmaxf(fabsf(wave_at<E, G>(y, 0)), fabsf(wave_at<E, G>(y, nj - 1)));
     int ex = 0;
     frexpf(amax, &ex);
@@ -1062,7 +1070,7 @@ void k_wave_sort_quant(
         if (r0 + m < nj) P = P + (double)y[m];
         if (Fa[m] >= 0.f && Fa[m] >= screen) {
           const int k = r0 + m + 1;
-          const double F = P * P / (double)k + Qrun[m] * Qrun[m] / (double)(nj - k);
+          const double F = P * P * rcp_nr((double)k) + Qrun[m] * Qrun[m] * rcp_nr((double)(nj - k));
           if (F > best) {
             best = F;
             bestk = k;
@@ -1071,8 +1079,9 @@ void k_wave_sort_quant(
         }
       }
     }
+    // the largest F, then the smallest split (lanes hold increasing splits)
     double bestF;
-    const int kstar = group_argmax2<G>(best, bestk, &bestF);
+    const int kstar = group_argmax_first<G>(best, bestk, &bestF);
     if (bestF < 0.0) {
       no_split = true;
       thr = wave_at<E, G>(y, 0);
