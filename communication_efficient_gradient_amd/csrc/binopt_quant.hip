@@ -54,11 +54,19 @@ constexpr int kCols = 16;     // LDS columns per bin (lane mod 16)
 constexpr int kCap = 64;      // values the exact stage sorts (one per lane)
 constexpr int kLevels = 10;   // levels before a bucket falls back to the sort
 constexpr int kRow = kCols + 2;  // LDS words per bin row (padded)
-// values per thread: 32 (workgroups of 64 to 1024 threads), 16 at d = 1024
-// (one wave).  Every instance fits in 128 VGPRs without spilling (four waves
-// per SIMD); 64 values per thread, tried at d = 16384 and 32768, gave fewer
-// waves per CU and no gain.
-__host__ __device__ constexpr int elems_per_thread(int d) { return d == 1024 ? 16 : 32; }
+// values per thread: 32 (workgroups of 64 to 512 threads), 16 at d = 1024
+// (one wave), 64 at d = 32768 (512 threads, 32 of the keys in registers and
+// 32 in LDS: two workgroups per CU, so one bucket's single-wave phases, its
+// load and its stores overlap the other's work; with 1024 threads and all
+// keys in registers a CU held one workgroup).  Every instance fits in 128
+// VGPRs without spilling (four waves per SIMD).
+__host__ __device__ constexpr int elems_per_thread(int d) {
+  return d == 1024 ? 16 : (d == 32768 ? 64 : 32);
+}
+// held keys in registers (the rest in LDS)
+__host__ __device__ constexpr int keys_in_regs(int d) {
+  return elems_per_thread(d) < 32 ? elems_per_thread(d) : 32;
+}
 
 // Order-preserving key of a canonical fp32 value (no -0) and its inverse.
 __device__ __forceinline__ uint32_t fkey(float x) {
@@ -276,8 +284,12 @@ __device__ __forceinline__ double rcp_nr(double x) {
 
 // FULL: every bucket of the launch holds D values (the last, shorter bucket
 // has a launch of its own, so the main grid carries no bounds tests).
+// The second bound is the minimum number of waves per SIMD: 3 for the
+// 256-thread instances, 4 (128 VGPRs) where keys live partly in LDS.
 template <int D, bool EF, bool FULL>
-__global__ __launch_bounds__(D / elems_per_thread(D), D / elems_per_thread(D) == 256 ? 3 : 1)
+__global__ __launch_bounds__(D / elems_per_thread(D),
+                             D / elems_per_thread(D) == 256 ? 3
+                             : (keys_in_regs(D) < elems_per_thread(D) ? 4 : 1))
 void k_binopt_block(
     int64_t n, const float* __restrict__ g, float* __restrict__ e,
     uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes,
@@ -286,6 +298,8 @@ void k_binopt_block(
   constexpr int T = D / E;
   constexpr int NQ = E / 4;
   constexpr int NW = T / 64;
+  constexpr int ER = keys_in_regs(D);  // keys 0 .. ER-1 in registers
+  constexpr int EL = E - ER;           // keys ER .. E-1 in LDS
   struct Shared {
     // per bin, one column per lane: count << 48 plus the biased fixed-point sum
     unsigned long long h[kBins * kRow];
@@ -305,6 +319,8 @@ void k_binopt_block(
     int nk[2], nc[2], nst, nnr;
     long long nq[2];
     double nlb;
+    // key ER + j of thread t at [j][t] (last: h keeps its 16-byte alignment)
+    uint32_t kx[EL > 0 ? EL : 1][EL > 0 ? T : 1];
   };
   __shared__ __align__(16) Shared sh;
 
@@ -327,7 +343,12 @@ void k_binopt_block(
   //      of +0 only when its level is +0, and that rare case re-reads p);
   //      bucket statistics on the way: key range, S = sum (fp64), A = sum |p|
   //      (only a scale for a threshold: fp32) -----------------------------
-  uint32_t kk[E];
+  uint32_t kk[ER];
+  // held key m (m a compile-time index after unrolling)
+  auto key = [&](int m) -> uint32_t {
+    if (m < ER) return kk[m < ER ? m : 0];
+    return sh.kx[m < ER ? 0 : m - ER][tid];
+  };
   uint64_t zmask = 0ull;
   uint32_t kmn = 0xffffffffu, kmx = 0u;
   double S = 0.0;
@@ -340,31 +361,37 @@ void k_binopt_block(
       const uint32_t bits = __float_as_uint(v);
       const bool nz = bits == 0x80000000u;
       zmask |= __ballot(nz);
-      const uint32_t key = canon_key(bits, nz);
-      kk[4 * q + c] = key;
+      const uint32_t kv = canon_key(bits, nz);
+      if (4 * q + c < ER) kk[4 * q + c < ER ? 4 * q + c : 0] = kv;
+      else sh.kx[4 * q + c < ER ? 0 : 4 * q + c - ER][tid] = kv;
       const bool ok = valid(4 * q + c);
-      kmn = (ok & (key < kmn)) ? key : kmn;
-      kmx = (ok & (key > kmx)) ? key : kmx;
+      kmn = (ok & (kv < kmn)) ? kv : kmn;
+      kmx = (ok & (kv > kmx)) ? kv : kmx;
       S = ok ? S + (double)v : S;
       Af = ok ? Af + fabsf(v) : Af;
     }
   };
   if constexpr (FULL) {
-    float4 xq[NQ];
+    // at most eight float4s per stream in flight
+    constexpr int QC = NQ < 8 ? NQ : 8;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) xq[q] = load4_nt(g + base + 4 * (tid + (int64_t)T * q));
-    if constexpr (EF) {
+    for (int q0 = 0; q0 < NQ; q0 += QC) {
+      float4 xq[QC];
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const float4 r = load4_nt(e + base + 4 * (tid + (int64_t)T * q));
-        xq[q].x = xq[q].x + r.x;
-        xq[q].y = xq[q].y + r.y;
-        xq[q].z = xq[q].z + r.z;
-        xq[q].w = xq[q].w + r.w;
+      for (int q = 0; q < QC; ++q) xq[q] = load4_nt(g + base + 4 * (tid + (int64_t)T * (q0 + q)));
+      if constexpr (EF) {
+#pragma unroll
+        for (int q = 0; q < QC; ++q) {
+          const float4 r = load4_nt(e + base + 4 * (tid + (int64_t)T * (q0 + q)));
+          xq[q].x = xq[q].x + r.x;
+          xq[q].y = xq[q].y + r.y;
+          xq[q].z = xq[q].z + r.z;
+          xq[q].w = xq[q].w + r.w;
+        }
       }
-    }
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) take(q, xq[q]);
+      for (int q = 0; q < QC; ++q) take(q0 + q, xq[q]);
+    }
   } else {
     // the last bucket: element-wise bounds, one float4 at a time
 #pragma unroll
@@ -479,19 +506,21 @@ void k_binopt_block(
 #pragma unroll
       for (int m = 0; m < E; ++m) {
         if (!valid(m)) continue;
-        hist_add((int)((kk[m] - rlo0) >> sh0), kk[m]);
+        const uint32_t k = key(m);
+        hist_add((int)((k - rlo0) >> sh0), k);
       }
     } else if (nr == 1) {
 #pragma unroll
       for (int m = 0; m < E; ++m) {
-        const uint32_t t0 = kk[m] - rlo0;
+        const uint32_t k = key(m);
+        const uint32_t t0 = k - rlo0;
         if (!valid(m) | (t0 > span0)) continue;
-        hist_add((int)(t0 >> sh0), kk[m]);
+        hist_add((int)(t0 >> sh0), k);
       }
     } else {
 #pragma unroll
       for (int m = 0; m < E; ++m) {
-        const uint32_t k = kk[m];
+        const uint32_t k = key(m);
         const uint32_t t0 = k - rlo0, t1 = k - rlo1;
         const bool in0 = t0 <= span0;
         if (!valid(m) | !(in0 | (t1 <= span1))) continue;
@@ -701,7 +730,7 @@ void k_binopt_block(
 #pragma unroll
     for (int m = 0; m < E; ++m) {
       const bool v = valid(m);
-      const uint32_t k = kk[m];
+      const uint32_t k = key(m);
       const float x = kval(k);
       const double dx = (double)x;
       p0 = __builtin_fma(dx, gate(v & (k < rlo0)), p0);
@@ -820,8 +849,9 @@ void k_binopt_block(
 #pragma unroll
       for (int m = 0; m < E; ++m) {
         if (!valid(m)) continue;
-        const double x = (double)kval(kk[m]);
-        if (kk[m] < kthr) two_sum_add(lo, x);
+        const uint32_t k = key(m);
+        const double x = (double)kval(k);
+        if (k < kthr) two_sum_add(lo, x);
         else two_sum_add(hi, x);
       }
       lo = group_sum2<64>(lo);
@@ -872,9 +902,10 @@ void k_binopt_block(
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int m = 4 * q + c;
-      const uint32_t code = (valid(m) && kk[m] >= kthr) ? 1u : 0u;
+      const uint32_t k = key(m);
+      const uint32_t code = (valid(m) && k >= kthr) ? 1u : 0u;
       field |= code << c;
-      const float pv = reread ? pr[c] : kval(kk[m]);
+      const float pv = reread ? pr[c] : kval(k);
       r[c] = pv - (code ? lb_ : la);
     }
     store_chunk<1, 4>(codes, i0, wl, field, code_bytes);
