@@ -61,7 +61,14 @@ KERNEL_SOURCES = {
     "bin_opt": [_CSRC + "common.hpp", _CSRC + "sort_quant.hip",
                 _CSRC + "binopt_quant.hip",
                 "communication_efficient_gradient_amd/build.py"],
+    "orq": [_CSRC + "common.hpp", _CSRC + "sort_quant.hip",
+            "communication_efficient_gradient_amd/build.py"],
 }
+ORQ_TRAFFIC = ((5, False), (9, False), (5, True), (9, True))  # (L, bisection)
+
+
+def orq_traffic_key(L: int, bisect: bool) -> str:
+    return f"orq_L{L}{'_bisect' if bisect else ''}_d512_n100M"
 BINGRAD_BUCKETS = (128, 512, 2048, 8192, 32768)
 COPY_BYTES = 1 << 29           # known-size copy for counter calibration
 
@@ -807,6 +814,13 @@ def suite_qsgd(torch, gq, WL, stream, tb):
     return out
 
 
+def orq_attach_traffic(ent: dict, L: int, bisect: bool, algorithmic: int) -> None:
+    tr = load_traffic(orq_traffic_key(L, bisect), "orq")
+    ent["traffic"] = tr
+    if tr:
+        ent["traffic_ratio"] = round(tr / algorithmic, 4)
+
+
 def suite_orq(torch, gq, WL, stream, tb, reps):
     """ORQ-5 / ORQ-9 on 100M elements, clip off / on."""
     out = []
@@ -828,6 +842,7 @@ def suite_orq(torch, gq, WL, stream, tb, reps):
                              extra=oracle_rate(
                                  host, dict(scheme=3, d=512, L=L, flags=clip,
                                             clip_sigma=3.0), False, seed=3)))
+            orq_attach_traffic(out[-1], L, False, quant_bytes(bits, L, 512, n, False))
             del c, m, q
     # the recursive-bisection reading of the level selection
     for L in (5, 9):
@@ -841,6 +856,8 @@ def suite_orq(torch, gq, WL, stream, tb, reps):
                          extra=oracle_rate(
                              host, dict(scheme=3, d=512, L=L, flags=8), False,
                              seed=3)))
+        orq_attach_traffic(out[-1], L, True,
+                           quant_bytes(gq.gq_code_bits(d), L, 512, n, False))
         del c, m, q
     return out
 
@@ -953,10 +970,12 @@ def ingest(dirs):
                                               w * 1024 * w_scale)}
     # BinGrad-b + EF on 1B (from `--counters --only bingrad`): a quantize
     # launch is the sort kernel (d <= 512) or the sort-free kernel plus the
-    # sort kernel's pass over the buckets it left (d >= 1024)
+    # sort kernel's pass over the buckets it left (d >= 1024); the whole-
+    # bucket launches (the one-block launch of a short last bucket, when
+    # there is one, is left out: under 1e-5 of the bytes)
     for dd in BINGRAD_BUCKETS:
-        sigs = (f"k_wave_sort_quant<2, 1, {dd},", f"k_sort_quant<2, 1, {dd}>",
-                f"k_binopt_block<{dd}>")
+        sigs = (f"k_wave_sort_quant<2, 1, {dd}, false, true>", f"k_sort_quant<2, 1, {dd}>",
+                f"k_binopt_block<{dd}, true, true>")
         names, fk, wk = [], 0.0, 0.0
         for sig in sigs:
             try:
@@ -971,6 +990,19 @@ def ingest(dirs):
                 "kernel": " + ".join(names), "source_digest": source_digest("bin_opt"),
                 "fetch_kib": fk, "write_kib": wk,
                 "bytes_per_launch": round(fk * 1024 * f_scale + wk * 1024 * w_scale)}
+    # ORQ on 100M, d = 512 (from `--counters --only orq`): one kernel per
+    # (L, bisection); clip on and off share it and move the same bytes
+    for L, bis in ORQ_TRAFFIC:
+        sig = f"k_wave_sort_quant<3, {3 if L == 5 else 4}, 512, {'true' if bis else 'false'}, true>"
+        try:
+            kname, f = med("FETCH_SIZE", lambda k, t=sig: t in k)
+            _, w = med("WRITE_SIZE", lambda k, t=sig: t in k)
+        except KeyError:
+            continue
+        res[orq_traffic_key(L, bis)] = {
+            "kernel": kname, "source_digest": source_digest("orq"),
+            "fetch_kib": f, "write_kib": w,
+            "bytes_per_launch": round(f * 1024 * f_scale + w * 1024 * w_scale)}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(res, f, indent=1)

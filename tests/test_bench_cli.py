@@ -65,16 +65,22 @@ def test_ingest_counter_runs(tmp_path, monkeypatch):
                        (f"void gq::{bench.Headline.KERNEL}(long)", 1000.0),
                        ("void gq::k_stream_quant<1, 1, 64, 2>(long)", 7.0),
                        (f"void gq::{bench.Headline.AGG_KERNEL}(long)", 2000.0),
-                       ("void gq::k_binopt_block<8192>(long)", 300.0),
+                       ("void gq::k_binopt_block<8192, true, true>(long)", 300.0),
+                       ("void gq::k_binopt_block<8192, true, false>(long)", 3.0),
                        ("void gq::k_sort_quant<2, 1, 8192>(long)", 1.0),
-                       ("void gq::k_wave_sort_quant<2, 1, 512, false>(long)", 400.0)],
+                       ("void gq::k_wave_sort_quant<2, 1, 512, false, true>(long)", 400.0),
+                       ("void gq::k_wave_sort_quant<3, 4, 512, true, true>(long)", 50.0),
+                       ("void gq::k_wave_sort_quant<3, 4, 512, true, false>(long)", 0.5)],
         "WRITE_SIZE": [("at::neg_kernel", copy_kib),
                        (f"void gq::{bench.Headline.KERNEL}(long)", 100.0),
                        ("void gq::k_stream_quant<1, 1, 64, 2>(long)", 9.0),
                        (f"void gq::{bench.Headline.AGG_KERNEL}(long)", 200.0),
-                       ("void gq::k_binopt_block<8192>(long)", 30.0),
+                       ("void gq::k_binopt_block<8192, true, true>(long)", 30.0),
+                       ("void gq::k_binopt_block<8192, true, false>(long)", 0.3),
                        ("void gq::k_sort_quant<2, 1, 8192>(long)", 0.5),
-                       ("void gq::k_wave_sort_quant<2, 1, 512, false>(long)", 40.0)],
+                       ("void gq::k_wave_sort_quant<2, 1, 512, false, true>(long)", 40.0),
+                       ("void gq::k_wave_sort_quant<3, 4, 512, true, true>(long)", 5.0),
+                       ("void gq::k_wave_sort_quant<3, 4, 512, true, false>(long)", 0.05)],
     }
     dirs = []
     for cn, kv in rows.items():
@@ -100,3 +106,6 @@ def test_ingest_counter_runs(tmp_path, monkeypatch):
     assert t["bin_opt_ef_d8192_n1B"]["bytes_per_launch"] == 301 * 2048 + 30.5 * 1024
     assert t["bin_opt_ef_d512_n1B"]["bytes_per_launch"] == 400 * 2048 + 40 * 1024
     assert "bin_opt_ef_d2048_n1B" not in t
+    # ORQ: the whole-bucket kernel of each (L, bisection) seen in the runs
+    assert t["orq_L9_bisect_d512_n100M"]["bytes_per_launch"] == 50 * 2048 + 5 * 1024
+    assert "orq_L5_d512_n100M" not in t
