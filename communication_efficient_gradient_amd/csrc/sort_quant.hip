@@ -947,8 +947,19 @@ void k_wave_sort_quant(
   constexpr int VEC = 4;
   constexpr int NQ = E / VEC;
   const int lane = threadIdx.x % G;  // lane within the bucket's group
-  const int64_t bucket =
-      b0 + (int64_t)blockIdx.x * (kGroupThreads / G) + threadIdx.x / G;
+  // With one bucket per wave the index is wave-uniform: as a scalar it puts
+  // every address in the scalar-base + lane-offset form, so no 64-bit
+  // per-lane address has to live (and spill) from the loads to the stores.
+  const int64_t bucket = [&] {
+    const int64_t bk = b0 + (int64_t)blockIdx.x * (kGroupThreads / G) + threadIdx.x / G;
+    if constexpr (G == 64) {
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bk);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)bk >> 32));
+      return (int64_t)(((uint64_t)hi << 32) | lo);
+    } else {
+      return bk;
+    }
+  }();
   if (bucket >= nb) return;  // whole groups leave together
   // redo: only the buckets the sort-free BinGrad-b kernel marked with NaN
   // levels (group-uniform)
@@ -957,6 +968,10 @@ void k_wave_sort_quant(
   }
   const int64_t base = bucket * D;
   const int nj = FULL ? D : (int)((n - base) < D ? (n - base) : D);
+  // whole buckets address their values as bucket base + 32-bit offset
+  const float* const gB = g + base;
+  float* const eB = e == nullptr ? nullptr : e + base;
+  auto off = [&](int q) { return (uint32_t)(VEC * (lane + G * q)); };
 
   // ---- 1. load p = g (+ e), element order --------------------------------
   float p[E];
@@ -964,10 +979,12 @@ void k_wave_sort_quant(
   for (int q = 0; q < NQ; ++q) {
     const int64_t i = base + (int64_t)VEC * (lane + G * q);
     float x[VEC];
-    load_vec<VEC, SCHEME == BIN_OPT, FULL>(g, i, n, x);
+    if constexpr (FULL) load_vec<VEC, SCHEME == BIN_OPT, true>(gB, off(q), n, x);
+    else load_vec<VEC, SCHEME == BIN_OPT, false>(g, i, n, x);
     if (e != nullptr) {
       float r[VEC];
-      load_vec<VEC, SCHEME == BIN_OPT, FULL>(e, i, n, r);
+      if constexpr (FULL) load_vec<VEC, SCHEME == BIN_OPT, true>(eB, off(q), n, r);
+      else load_vec<VEC, SCHEME == BIN_OPT, false>(e, i, n, r);
 #pragma unroll
       for (int c = 0; c < VEC; ++c) x[c] = x[c] + r[c];
     }
@@ -1346,10 +1363,12 @@ void k_wave_sort_quant(
     for (int q = 0; q < NQ; ++q) {
       const int64_t i = base + (int64_t)VEC * (lane + G * q);
       float x[VEC];
-      load_vec<VEC, false, FULL>(g, i, n, x);
+      if constexpr (FULL) load_vec<VEC, false, true>(gB, off(q), n, x);
+      else load_vec<VEC, false, false>(g, i, n, x);
       if (e != nullptr) {
         float r[VEC];
-        load_vec<VEC, false, FULL>(e, i, n, r);
+        if constexpr (FULL) load_vec<VEC, false, true>(eB, off(q), n, r);
+        else load_vec<VEC, false, false>(e, i, n, r);
 #pragma unroll
         for (int c = 0; c < VEC; ++c) x[c] = x[c] + r[c];
       }
@@ -1408,7 +1427,11 @@ void k_wave_sort_quant(
     }
     if constexpr (BITS == 0) dfield[q] = field;
     else store_chunk<BITS, VEC>(codes, i0, lane, field, code_bytes);
-    if (e != nullptr && (FULL || i0 < n)) store_vec<VEC, true, FULL>(e, i0, n, r);
+    if constexpr (FULL) {
+      if (e != nullptr) store_vec<VEC, true, true>(eB, off(q), n, r);
+    } else {
+      if (e != nullptr && i0 < n) store_vec<VEC, true, false>(e, i0, n, r);
+    }
   }
   // Dense fields are stored once the values and levels are dead.  Dense ORQ
   // runs with d >= 512 only, so here a bucket is one wave.
