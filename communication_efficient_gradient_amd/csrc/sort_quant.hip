@@ -1195,15 +1195,18 @@ void k_wave_sort_quant(
       };
       // this lane's partial sums (branch-free), then the group's carries
       int fa = 0, fb = 0;
-      double sa = 0.0, sb = 0.0;
+      // (from 0, the first value's sum is the value itself)
+      double sa = va(0), sb = vb(E - 1);
+      fa = head(0) ? 1 : 0;
+      fb = tail(E - 1) ? 1 : 0;
 #pragma unroll
-      for (int m = 0; m < E; ++m) {
+      for (int m = 1; m < E; ++m) {
         const bool h = head(m);
         sa = acc(sa, h, va(m));
         fa |= h ? 1 : 0;
       }
 #pragma unroll
-      for (int m = E - 1; m >= 0; --m) {
+      for (int m = E - 2; m >= 0; --m) {
         const bool t = tail(m);
         sb = acc(sb, t, vb(m));
         fb |= t ? 1 : 0;
@@ -1220,8 +1223,14 @@ void k_wave_sort_quant(
 #pragma unroll
         for (int m = E - 1; m >= 0; --m) {
           const bool t = tail(m);
-          Gs[m] = t ? 0.0 : run;
-          run = acc(run, t, vb(m));
+          if constexpr (BISECT) {
+            Gs[m] = t ? 0.0 : run;
+            run = acc(run, t, vb(m));
+          } else {  // one factor for both
+            const double k = gate(!t);
+            Gs[m] = run * k;
+            run = __builtin_fma(run, k, vb(m));
+          }
         }
         double A = ca;
 #pragma unroll
