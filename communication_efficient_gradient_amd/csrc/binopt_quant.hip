@@ -285,10 +285,13 @@ __device__ __forceinline__ double rcp_nr(double x) {
 // FULL: every bucket of the launch holds D values (the last, shorter bucket
 // has a launch of its own, so the main grid carries no bounds tests).
 // The second bound is the minimum number of waves per SIMD: 3 for the
-// 256-thread instances, 4 (128 VGPRs) where keys live partly in LDS.
+// 256-thread instances, 4 (128 VGPRs) where keys live partly in LDS; none
+// for the one-block launch of a short last bucket (no occupancy to keep,
+// so no spilling to fit it).
 template <int D, bool EF, bool FULL>
 __global__ __launch_bounds__(D / elems_per_thread(D),
-                             D / elems_per_thread(D) == 256 ? 3
+                             !FULL ? 1
+                             : D / elems_per_thread(D) == 256 ? 3
                              : (keys_in_regs(D) < elems_per_thread(D) ? 4 : 1))
 void k_binopt_block(
     int64_t n, const float* __restrict__ g, float* __restrict__ e,

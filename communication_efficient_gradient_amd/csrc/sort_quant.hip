@@ -296,24 +296,19 @@ struct SortShared {
   float thr;
 };
 
+// One bucket by one workgroup (the body of k_sort_quant).
 template <int SCHEME, int BITS, int D>
-__global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
-    int64_t n, const float* __restrict__ g, float* __restrict__ e,
+__device__ __forceinline__ void sort_quant_bucket(
+    int64_t bucket, int64_t n, const float* __restrict__ g, float* __restrict__ e,
     uint32_t k0, uint32_t k1, uint32_t step, int L, int flags, float clip_sigma,
     uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes,
-    uint32_t A4, int W, int redo) {
+    uint32_t A4, int W) {
   constexpr int T = SortCfg<D>::T;
   constexpr int E = SortCfg<D>::E;
   __shared__ float sorted[D];
   __shared__ SortShared sh;
 
   const int tid = threadIdx.x;
-  const int64_t bucket = blockIdx.x;
-  // redo: only the buckets the sort-free BinGrad-b kernel marked with NaN
-  // levels (block-uniform, before any barrier)
-  if constexpr (SCHEME == BIN_OPT) {
-    if (redo && meta[2 * bucket] == meta[2 * bucket]) return;
-  }
   const int64_t base = bucket * D;
   const int nj = (int)((n - base) < D ? (n - base) : D);
 
@@ -681,6 +676,47 @@ __global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
       else store4(e, i0, n, make_float4(rr[0], rr[1], rr[2], rr[3]));
     }
   }
+}
+
+// A workgroup per bucket, or (redo) only the buckets the sort-free BinGrad-b
+// kernel marked with NaN levels: then a workgroup checks 64 buckets (one
+// level read per lane of its first wave) and sorts the marked ones in turn,
+// so the pass costs a grid of nb / 64 short workgroups rather than nb (and
+// marked buckets, which are rare, seldom share a workgroup).
+template <int SCHEME, int BITS, int D>
+__global__ __launch_bounds__(SortCfg<D>::T) void k_sort_quant(
+    int64_t n, const float* __restrict__ g, float* __restrict__ e,
+    uint32_t k0, uint32_t k1, uint32_t step, int L, int flags, float clip_sigma,
+    uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes,
+    uint32_t A4, int W, int redo) {
+  if constexpr (SCHEME == BIN_OPT) {
+    if (redo) {
+      __shared__ uint64_t marks;
+      const int64_t nb = (n + D - 1) / D;
+      const int64_t first = (int64_t)blockIdx.x * 64;
+      if (threadIdx.x < 64) {
+        const int64_t b = first + threadIdx.x;
+        const float lv = b < nb ? meta[2 * b] : 0.f;
+        const uint64_t m = (uint64_t)__ballot(lv != lv);
+        if (threadIdx.x == 0) marks = m;
+      }
+      __syncthreads();
+      // the same in every thread: scalar, so the loop is workgroup-uniform
+      const uint64_t mv = marks;
+      uint64_t mw = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(mv >> 32)) << 32) |
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)mv);
+      while (mw != 0ull) {
+        const int bit = __builtin_ctzll(mw);
+        mw &= mw - 1ull;
+        sort_quant_bucket<SCHEME, BITS, D>(first + bit, n, g, e, k0, k1, step, L, flags,
+                                           clip_sigma, codes, meta, code_bytes, A4, W);
+        __syncthreads();  // the next bucket reuses the LDS
+      }
+      return;
+    }
+  }
+  sort_quant_bucket<SCHEME, BITS, D>(blockIdx.x, n, g, e, k0, k1, step, L, flags,
+                                     clip_sigma, codes, meta, code_bytes, A4, W);
 }
 
 // ------------------------------------------- one lane group per bucket --
@@ -1482,7 +1518,9 @@ int launch_sort_one(int64_t n, const float* g, float* e, uint64_t seed,
       go(k_wave_sort_quant<SCHEME, BITS, D, false, false>, nfull, nb);
     }
   } else {
-    hipLaunchKernelGGL((k_sort_quant<SCHEME, BITS, D>), dim3((uint32_t)nb),
+    // the redo pass: one workgroup per 64 buckets (see k_sort_quant)
+    const int64_t grid = redo ? (nb + 63) / 64 : nb;
+    hipLaunchKernelGGL((k_sort_quant<SCHEME, BITS, D>), dim3((uint32_t)grid),
                        dim3(SortCfg<D>::T), 0, st, n, g, e, (uint32_t)seed,
                        (uint32_t)(seed >> 32), step, L, flags, clip_sigma, codes,
                        meta, code_bytes, A4, W, redo);
