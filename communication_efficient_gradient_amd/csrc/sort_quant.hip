@@ -859,6 +859,31 @@ __device__ __forceinline__ double group_seg_carry(bool f, double s, int gl) {
   return ex;
 }
 
+// Exclusive sum over the G lanes of a group: of the lanes before this one
+// (REV = false) or after it (REV = true; mirrored, scanned, mirrored back).
+// The same additions in the same order as group_seg_carry_dpp without
+// segment starts, without its flag bookkeeping.
+template <int G, bool REV>
+__device__ __forceinline__ double group_excl_sum(double s, int gl) {
+  if constexpr (REV) s = lane_xor_ds_d<G - 1>(s);
+  auto shr = [&](auto tag) {
+    constexpr int N = decltype(tag)::value;
+    double sp = dpp_shr<N>(s);
+    if (G < 16 && gl < N) sp = 0.0;  // two groups share a row
+    s = sp + s;
+  };
+  shr(std::integral_constant<int, 1>());
+  shr(std::integral_constant<int, 2>());
+  shr(std::integral_constant<int, 4>());
+  if constexpr (G >= 16) shr(std::integral_constant<int, 8>());
+  if constexpr (G >= 32) s = dpp_bcast<15>(s) + s;
+  if constexpr (G >= 64) s = dpp_bcast<31>(s) + s;
+  double ex = __shfl_up(s, 1, G);
+  if (gl == 0) ex = 0.0;
+  if constexpr (REV) ex = lane_xor_ds_d<G - 1>(ex);
+  return ex;
+}
+
 // Group argmax of (value, key): larger value wins, equal values -> smaller
 // key; every lane of the group gets the winner.
 template <int G>
@@ -1069,8 +1094,8 @@ void k_wave_sort_quant(
 #pragma unroll
     for (int m = 0; m < E; ++m)
       if (r0 + m < nj) tot = tot + (double)y[m];
-    const double pre = group_seg_carry_dpp<G, false>(false, tot, lane);
-    const double suf = group_seg_carry_dpp<G, true>(false, tot, lane);
+    const double pre = group_excl_sum<G, false>(tot, lane);
+    const double suf = group_excl_sum<G, true>(tot, lane);
     double Qrun[E];
     {
       double acc = suf;
@@ -1091,23 +1116,23 @@ void k_wave_sort_quant(
     int ex = 0;
     frexpf(amax, &ex);
     const double sc = ldexp(1.0, -ex);
-    auto screen_at = [&](int m, double P) -> float {
-      const int pos = r0 + m;
-      const int k = pos + 1;
-      const float yk = (m + 1 < E) ? y[m + 1] : y_next_run;
-      if (k >= nj || !(y[m] < yk)) return -1.f;
-      const float p32 = (float)(P * sc), q32 = (float)(Qrun[m] * sc);
-      return p32 * p32 * __builtin_amdgcn_rcpf((float)k) +
-             q32 * q32 * __builtin_amdgcn_rcpf((float)(nj - k));
-    };
+    // (branch-free: every slot evaluated, -1 selected where no split lies;
+    // k and n - k as floats stepped from the lane's first split)
     float Fa[E];
     float fmax32 = -1.f;
     {
+      float kf0 = (float)(r0 + 1), nkf0 = (float)(nj - r0 - 1);
+      // (opaque: otherwise folded back into one conversion per slot)
+      asm volatile("" : "+v"(kf0), "+v"(nkf0));
       double P = pre;
 #pragma unroll
       for (int m = 0; m < E; ++m) {
         if (r0 + m < nj) P = P + (double)y[m];
-        Fa[m] = screen_at(m, P);
+        const float yk = (m + 1 < E) ? y[m + 1] : y_next_run;
+        const float p32 = (float)(P * sc), q32 = (float)(Qrun[m] * sc);
+        const float f = __builtin_fmaf(p32 * p32, __builtin_amdgcn_rcpf(kf0 + (float)m),
+                                       (q32 * q32) * __builtin_amdgcn_rcpf(nkf0 - (float)m));
+        Fa[m] = (r0 + m + 1 < nj && y[m] < yk) ? f : -1.f;
         fmax32 = fmaxf(fmax32, Fa[m]);
       }
     }
@@ -1121,7 +1146,7 @@ void k_wave_sort_quant(
 #pragma unroll
       for (int m = 0; m < E; ++m) {
         if (r0 + m < nj) P = P + (double)y[m];
-        if (Fa[m] >= 0.f && Fa[m] >= screen) {
+        if (Fa[m] >= screen) {  // (screen > -1: no slot without a split)
           const int k = r0 + m + 1;
           const double F = P * P * rcp_nr((double)k) + Qrun[m] * Qrun[m] * rcp_nr((double)(nj - k));
           if (F > best) {
