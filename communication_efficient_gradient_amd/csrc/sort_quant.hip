@@ -1029,10 +1029,19 @@ void k_wave_sort_quant(
   }
   const int64_t base = bucket * D;
   const int nj = FULL ? D : (int)((n - base) < D ? (n - base) : D);
-  // whole buckets address their values as bucket base + 32-bit offset
-  const float* const gB = g + base;
-  float* const eB = e == nullptr ? nullptr : e + base;
-  auto off = [&](int q) { return (uint32_t)(VEC * (lane + G * q)); };
+  // whole buckets address their values as the base of the wave's first
+  // bucket (a scalar: the wave's buckets are consecutive) + a 32-bit offset
+  const int64_t wbase = [&] {
+    const int64_t wb = (b0 + (int64_t)blockIdx.x * (kGroupThreads / G) +
+                        (int64_t)(threadIdx.x / 64) * (64 / G)) * D;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)wb);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)wb >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+  }();
+  const float* const gB = g + wbase;
+  float* const eB = e == nullptr ? nullptr : e + wbase;
+  const uint32_t goff = (uint32_t)(((threadIdx.x & 63) / G) * D);  // group in wave
+  auto off = [&](int q) { return goff + (uint32_t)(VEC * (lane + G * q)); };
 
   // ---- 1. load p = g (+ e), element order --------------------------------
   float p[E];
