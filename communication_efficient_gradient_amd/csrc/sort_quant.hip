@@ -1083,8 +1083,8 @@ void k_wave_sort_quant(
   float y[E];
 #pragma unroll
   for (int m = 0; m < E; ++m) {
-    const float x = clipped(p[m]);
-    y[m] = epos(m) < nj ? (x == 0.f ? 0.f : x) : __builtin_inff();
+    // x + 0 is x, except -0 + 0 = +0 (denormals are kept)
+    y[m] = epos(m) < nj ? clipped(p[m]) + 0.f : __builtin_inff();
   }
   flip_bitonic<E, D>(y, nullptr, lane);
 
@@ -1145,7 +1145,10 @@ void k_wave_sort_quant(
         fmax32 = fmaxf(fmax32, Fa[m]);
       }
     }
-    fmax32 = group_max<G>(fmax32);
+    // (as integers: the order of the bit patterns of floats >= 0, and -1
+    // below them all)
+    fmax32 = __int_as_float(group_reduce<G>(__float_as_int(fmax32),
+                                            [](int a, int b) { return a > b ? a : b; }));
     const float screen = fmax32 * (1.0f - 1e-5f);
     double best = -1.0;
     int bestk = 0x7fffffff;
@@ -1166,9 +1169,23 @@ void k_wave_sort_quant(
         }
       }
     }
-    // the largest F, then the smallest split (lanes hold increasing splits)
+    // the largest F, then the smallest split (lanes hold increasing splits);
+    // where no group has candidates in more than one lane (the usual case)
+    // the candidate lane's own best
     double bestF;
-    const int kstar = group_argmax_first<G>(best, bestk, &bestF);
+    int kstar;
+    {
+      const uint64_t cl = (uint64_t)__ballot(best >= 0.0);
+      const int gbase = (int)(threadIdx.x & 63u) & ~(G - 1);
+      const uint64_t mine = G == 64 ? cl : (cl >> gbase) & ((1ull << (G & 63)) - 1ull);
+      if (__ballot((mine & (mine - 1ull)) != 0ull) == 0ull) {
+        const int src = gbase + (mine ? __builtin_ctzll(mine) : 0);
+        kstar = __shfl(bestk, src, 64);
+        bestF = mine ? __shfl(best, src, 64) : -1.0;
+      } else {
+        kstar = group_argmax_first<G>(best, bestk, &bestF);
+      }
+    }
     if (bestF < 0.0) {
       no_split = true;
       thr = wave_at<E, G>(y, 0);
