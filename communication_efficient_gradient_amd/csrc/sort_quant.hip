@@ -1105,26 +1105,21 @@ void k_wave_sort_quant(
       if (r0 + m < nj) tot = tot + (double)y[m];
     const double pre = group_excl_sum<G, false>(tot, lane);
     const double suf = group_excl_sum<G, true>(tot, lane);
-    double Qrun[E];
-    {
-      double acc = suf;
-#pragma unroll
-      for (int m = E - 1; m >= 0; --m) {
-        Qrun[m] = acc;
-        if (r0 + m < nj) acc = acc + (double)y[m];
-      }
-    }
-    // F(k) = P^2/k + Q^2/(n-k) at every split between distinct values: first
-    // in fp32 (a screen), then in fp64 only where the screen is within 1e-5
-    // of its maximum.  The screen's error (< 1e-6 relative, both terms >= 0,
-    // values scaled by a power of two so |P|, |Q| <= d) keeps the maximum
-    // and every tie among the candidates.  The fp64 values take refined
-    // reciprocals (a few ulps): splits closer than that are ties, where
-    // either is correct.
+    // F(k) = P^2/k + Q^2/(n-k) at every split between distinct values.  With
+    // mu = S/n and the centred sum C = P - k mu, F(k) = S^2/n + n D(k),
+    // D(k) = C^2 / (k (n-k)), so F and D peak at the same splits.  D is
+    // screened in fp32 (C from fp64 running sums, scaled by a power of two
+    // so |C| <= 2d: relative error < 1e-6, below 1e-5 of the maximum), then
+    // F is evaluated in fp64 only at splits whose D is within 1e-5 of the
+    // screen's maximum, with P and Q = S - P summed from the lane's carries
+    // in the order of the values.  The screen keeps the maximum and every
+    // near tie; the fp64 values take refined reciprocals (a few ulps):
+    // splits closer than that are ties, where either is correct.
     const float amax = fmaxf(fabsf(wave_at<E, G>(y, 0)), fabsf(wave_at<E, G>(y, nj - 1)));
     int ex = 0;
     frexpf(amax, &ex);
     const double sc = ldexp(1.0, -ex);
+    const double mu = __shfl(pre + tot + suf, 0, G) / (double)nj;  // one value per group
     // (branch-free: every slot evaluated, -1 selected where no split lies;
     // k and n - k as floats stepped from the lane's first split)
     float Fa[E];
@@ -1133,14 +1128,14 @@ void k_wave_sort_quant(
       float kf0 = (float)(r0 + 1), nkf0 = (float)(nj - r0 - 1);
       // (opaque: otherwise folded back into one conversion per slot)
       asm volatile("" : "+v"(kf0), "+v"(nkf0));
-      double P = pre;
+      double Cs = pre - (double)r0 * mu;
 #pragma unroll
       for (int m = 0; m < E; ++m) {
-        if (r0 + m < nj) P = P + (double)y[m];
+        if (r0 + m < nj) Cs = Cs + ((double)y[m] - mu);
         const float yk = (m + 1 < E) ? y[m + 1] : y_next_run;
-        const float p32 = (float)(P * sc), q32 = (float)(Qrun[m] * sc);
-        const float f = __builtin_fmaf(p32 * p32, __builtin_amdgcn_rcpf(kf0 + (float)m),
-                                       (q32 * q32) * __builtin_amdgcn_rcpf(nkf0 - (float)m));
+        const float c32 = (float)(Cs * sc);
+        const float kk = (kf0 + (float)m) * (nkf0 - (float)m);
+        const float f = c32 * c32 * __builtin_amdgcn_rcpf(kk);
         Fa[m] = (r0 + m + 1 < nj && y[m] < yk) ? f : -1.f;
         fmax32 = fmaxf(fmax32, Fa[m]);
       }
@@ -1153,19 +1148,29 @@ void k_wave_sort_quant(
     double best = -1.0;
     int bestk = 0x7fffffff;
     double bestP = 0.0;  // the sum below this lane's best split
-    {
-      double P = pre;
 #pragma unroll
-      for (int m = 0; m < E; ++m) {
-        if (r0 + m < nj) P = P + (double)y[m];
-        if (Fa[m] >= screen) {  // (screen > -1: no slot without a split)
-          const int k = r0 + m + 1;
-          const double F = P * P * rcp_nr((double)k) + Qrun[m] * Qrun[m] * rcp_nr((double)(nj - k));
-          if (F > best) {
-            best = F;
-            bestk = k;
-            bestP = P;
-          }
+    for (int m = 0; m < E; ++m) {
+      if (Fa[m] >= screen) {  // (screen > -1: no slot without a split)
+        // (the values reread as opaque floats: no fp64 copies kept live)
+        double P = pre, Q = suf;
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          float v = y[i];
+          asm volatile("" : "+v"(v));
+          if (i <= m && r0 + i < nj) P = P + (double)v;
+        }
+#pragma unroll
+        for (int i = E - 1; i > m; --i) {
+          float v = y[i];
+          asm volatile("" : "+v"(v));
+          if (r0 + i < nj) Q = Q + (double)v;
+        }
+        const int k = r0 + m + 1;
+        const double F = P * P * rcp_nr((double)k) + Q * Q * rcp_nr((double)(nj - k));
+        if (F > best) {
+          best = F;
+          bestk = k;
+          bestP = P;
         }
       }
     }
