@@ -1148,9 +1148,44 @@ void k_wave_sort_quant(
     double best = -1.0;
     int bestk = 0x7fffffff;
     double bestP = 0.0;  // the sum below this lane's best split
+    // Four or more groups in a wave meet their candidates in different
+    // slots; where no lane holds two, each lane sums for its own slot in one
+    // pass (the other values add 0.0, which leaves the sums as they are).
+    bool done = false;
+    if constexpr (G <= 16) {
+      int nc = 0, mc = 0;
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        const bool c = Fa[m] >= screen;
+        nc += c ? 1 : 0;
+        mc = c ? m : mc;
+      }
+      if (__ballot(nc > 1) == 0ull) {
+        done = true;
+        if (nc == 1) {
+          double P = pre, Q = suf;
+#pragma unroll
+          for (int i = 0; i < E; ++i) {
+            float v = y[i];
+            asm volatile("" : "+v"(v));
+            P = P + (i <= mc ? (double)v : 0.0);  // (slot mc has a split: i < nj)
+          }
+#pragma unroll
+          for (int i = E - 1; i >= 0; --i) {
+            float v = y[i];
+            asm volatile("" : "+v"(v));
+            Q = Q + (i > mc && r0 + i < nj ? (double)v : 0.0);
+          }
+          const int k = r0 + mc + 1;
+          best = P * P * rcp_nr((double)k) + Q * Q * rcp_nr((double)(nj - k));
+          bestk = k;
+          bestP = P;
+        }
+      }
+    }
 #pragma unroll
     for (int m = 0; m < E; ++m) {
-      if (Fa[m] >= screen) {  // (screen > -1: no slot without a split)
+      if (!done && Fa[m] >= screen) {  // (screen > -1: no slot without a split)
         // (the values reread as opaque floats: no fp64 copies kept live)
         double P = pre, Q = suf;
 #pragma unroll
