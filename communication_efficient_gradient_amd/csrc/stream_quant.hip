@@ -115,8 +115,22 @@ __device__ __forceinline__ void bucket_side_sums(double& sn, double& sp, int& nn
 // (per v, the wave's 64 lanes cover 256 consecutive elements), and groups
 // past the last bucket stay to the end: all their loads and stores are
 // bounds-checked, and the field assembly needs all 64 lanes.
+// CHUNKED (1024 lanes of 8 float4s, d = 32768; the min/max and the packed
+// uniform quantizers): at most 64 VGPRs, so that two buckets share a CU and
+// one's reduction barrier overlaps the other's loads and stores (one bucket
+// per CU left the CU without memory traffic while its waves met).  The
+// float4s are loaded in two halves, the first summed before the second is
+// issued, and the random words are drawn per float4 in the coding pass
+// instead of during the loads.  (The sign split's fp64 side sums and the
+// dense packing do not fit 64 VGPRs without spilling.)
 template <int SCHEME, int BITS, int G, int V>
-__global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
+constexpr bool stream_chunked() {
+  return G == 1024 && V == 8 && (SCHEME == ORQ || (SCHEME == UNIFORM && BITS != 0));
+}
+
+template <int SCHEME, int BITS, int G, int V>
+__global__ __launch_bounds__(BlockCfg<G>::kThreads, (stream_chunked<SCHEME, BITS, G, V>() ? 8 : 1))
+void k_stream_quant(
     int64_t n, int64_t nb, const float* __restrict__ g, float* __restrict__ e,
     uint32_t k0, uint32_t k1, uint32_t step, int s, int nearest,
     uint8_t* __restrict__ codes, float* __restrict__ meta, int64_t code_bytes,
@@ -140,19 +154,25 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
   // Random words for the uniform scheme, or (nearest) words whose u is
   // exactly 1/2, so that a value rounds up iff q > 1/2.  They depend on the
   // element index only and are drawn while the loads are in flight.
-  uint4 wr[RANDOM ? V : 1];
-  auto draw = [&]() {
-    if constexpr (RANDOM) {
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        wr[v] = make_uint4(kHalfWord, kHalfWord, kHalfWord, kHalfWord);
-        if (!nearest && codes != nullptr) {
-          const uint64_t ctr = (uint64_t)(base + 4 * (lane + G * v)) >> 2;
-          wr[v] = philox4x32_10(k0, k1, (uint32_t)ctr, (uint32_t)(ctr >> 32),
-                                step, 0u);
-        }
-      }
+  constexpr bool CHUNKED = stream_chunked<SCHEME, BITS, G, V>();
+  auto word4 = [&](int v) {
+    uint4 w = make_uint4(kHalfWord, kHalfWord, kHalfWord, kHalfWord);
+    if (!nearest && codes != nullptr) {
+      const uint64_t ctr = (uint64_t)(base + 4 * (lane + G * v)) >> 2;
+      w = philox4x32_10(k0, k1, (uint32_t)ctr, (uint32_t)(ctr >> 32), step, 0u);
     }
+    return w;
+  };
+  uint4 wr[RANDOM && !CHUNKED ? V : 1];
+  auto draw = [&]() {
+    if constexpr (RANDOM && !CHUNKED) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) wr[v] = word4(v);
+    }
+  };
+  auto words = [&](int v) {
+    if constexpr (CHUNKED) return word4(v);
+    else return wr[RANDOM ? v : 0];
   };
   float4 p[V], r[V];
   auto add_residual = [&]() {
@@ -171,7 +191,28 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
   // nontemporal loads, all issued before any use; the last bucket checks
   // each element.
   const bool whole = base + D <= n;
-  if (whole) {
+  // elements of the bucket inside the gradient (0 for groups past the end)
+  const int rem = (int)(n - base < D ? (n - base > 0 ? n - base : 0) : D);
+  if (whole && CHUNKED) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // (the second half's loads stay behind the first half's sums)
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int v = h * (V / 2); v < (h + 1) * (V / 2); ++v)
+        p[v] = load4_nt(g + base + 4 * (lane + G * v));
+      if (e != nullptr) {
+#pragma unroll
+        for (int v = h * (V / 2); v < (h + 1) * (V / 2); ++v) {
+          const float4 rv = load4_nt(e + base + 4 * (lane + G * v));
+          p[v].x = p[v].x + rv.x;
+          p[v].y = p[v].y + rv.y;
+          p[v].z = p[v].z + rv.z;
+          p[v].w = p[v].w + rv.w;
+        }
+      }
+    }
+  } else if (whole) {
 #pragma unroll
     for (int v = 0; v < V; ++v)
       p[v] = load4_nt(g + base + 4 * (lane + G * v));
@@ -182,6 +223,20 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
     }
     draw();
     add_residual();
+  } else if (CHUNKED) {
+    // (32-bit offsets from the bucket's base: no 64-bit index per float4)
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int off = 4 * (lane + G * v);
+      p[v] = load4(g + base, off, rem);
+      if (e != nullptr) {
+        const float4 rv = load4(e + base, off, rem);
+        p[v].x = p[v].x + rv.x;
+        p[v].y = p[v].y + rv.y;
+        p[v].z = p[v].z + rv.z;
+        p[v].w = p[v].w + rv.w;
+      }
+    }
   } else {
 #pragma unroll
     for (int v = 0; v < V; ++v) {
@@ -193,6 +248,20 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
     add_residual();
   }
 
+  // The rest, with the elements of each float4 that lie in the gradient
+  // known to be all four where WH (CHUNKED whole buckets: one bucket per
+  // block, so every thread of the block takes the same instance; elsewhere
+  // groups of one wave may differ, and the dense packing exchanges lanes).
+  auto finish = [&](auto wh_tag) {
+  constexpr bool WH = decltype(wh_tag)::value;
+  auto nreal_of = [&](int v) -> int {
+    if constexpr (WH) {
+      return 4;
+    } else {
+      const int left = rem - 4 * (lane + G * v);
+      return left >= 4 ? 4 : (left > 0 ? left : 0);
+    }
+  };
   // ---- per-bucket levels ----------------------------------------------
   // UNIFORM: M = max |p| (absent tail elements load as 0, which never
   // raises a max-abs).  ORQ (L = 2): minimum and maximum over the real
@@ -209,8 +278,7 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
     float hi = -INFINITY, nlo = -INFINITY;  // max p and max (-p)
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      const int64_t i = base + 4 * (lane + G * v);
-      const int nreal = i + 4 <= n ? 4 : (i < n ? (int)(n - i) : 0);
+      const int nreal = nreal_of(v);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float x = comp(p[v], k);
@@ -232,8 +300,7 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
     int nn = 0, np = 0;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      const int64_t i = base + 4 * (lane + G * v);
-      const int nreal = i + 4 <= n ? 4 : (i < n ? (int)(n - i) : 0);
+      const int nreal = nreal_of(v);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float x = comp(p[v], k);
@@ -280,7 +347,8 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
       int sc[4] = {0, 0, 0, 0};  // signed codes (dense digits are sc + s)
       float4 xh;
       if constexpr (SCHEME == UNIFORM) {
-        const uint32_t ws[4] = {wr[v].x, wr[v].y, wr[v].z, wr[v].w};
+        const uint4 wv = words(v);
+        const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int ci = uniform_code<SCALED>(comp(p[v], k), up, inv, sf, ws[k]);
@@ -295,7 +363,8 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
       } else if constexpr (SCHEME == ORQ) {
         // q = (p - a) / (b - a) in fp32; up iff u < q (nearest: q > 1/2); a
         // value equal to a level takes it (the lower one when a = b)
-        const uint32_t ws[4] = {wr[v].x, wr[v].y, wr[v].z, wr[v].w};
+        const uint4 wv = words(v);
+        const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
         const float den = lvl1 - lvl0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -321,7 +390,7 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
         }
       }
       // absent tail elements pack as 0
-      const int nreal = i + 4 <= n ? 4 : (i < n ? (int)(n - i) : 0);
+      const int nreal = nreal_of(v);
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         if (k >= nreal) c[k] = 0u;
@@ -336,19 +405,22 @@ __global__ __launch_bounds__(BlockCfg<G>::kThreads) void k_stream_quant(
         store_field<BITS, G>(codes, i, lane, field4<BITS>(c[0], c[1], c[2], c[3]),
                              code_bytes);
       }
-      if (e != nullptr && i < n) {
+      if (e != nullptr && (WH || i < n)) {
         float4 r;
         r.x = p[v].x - xh.x;
         r.y = p[v].y - xh.y;
         r.z = p[v].z - xh.z;
         r.w = p[v].w - xh.w;
-        if (whole) store4_nt(e + i, r);
+        if (WH || whole) store4_nt(e + i, r);
         else store4(e, i, n, r);
       }
     }
   };
   if (up == 1.0f) code_pass(std::false_type{});
   else code_pass(std::true_type{});
+  };
+  if (CHUNKED && whole) finish(std::true_type{});
+  else finish(std::false_type{});
 }
 
 template <int SCHEME, int BITS, int G, int V>
