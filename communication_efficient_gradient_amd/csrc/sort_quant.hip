@@ -862,9 +862,10 @@ __device__ __forceinline__ double group_seg_carry(bool f, double s, int gl) {
 // Exclusive sum over the G lanes of a group: of the lanes before this one
 // (REV = false) or after it (REV = true; mirrored, scanned, mirrored back).
 // The same additions in the same order as group_seg_carry_dpp without
-// segment starts, without its flag bookkeeping.
+// segment starts, without its flag bookkeeping.  *total (REV = false): the
+// group's sum (the last lane's inclusive value) in every lane.
 template <int G, bool REV>
-__device__ __forceinline__ double group_excl_sum(double s, int gl) {
+__device__ __forceinline__ double group_excl_sum(double s, int gl, double* total = nullptr) {
   if constexpr (REV) s = lane_xor_ds_d<G - 1>(s);
   auto shr = [&](auto tag) {
     constexpr int N = decltype(tag)::value;
@@ -881,6 +882,9 @@ __device__ __forceinline__ double group_excl_sum(double s, int gl) {
   double ex = __shfl_up(s, 1, G);
   if (gl == 0) ex = 0.0;
   if constexpr (REV) ex = lane_xor_ds_d<G - 1>(ex);
+  if constexpr (!REV) {
+    if (total != nullptr) *total = __shfl(s, G - 1, G);
+  }
   return ex;
 }
 
@@ -1099,12 +1103,18 @@ void k_wave_sort_quant(
 
   if constexpr (SCHEME == BIN_OPT) {
     // ---- 4a. best split -------------------------------------------------
-    double tot = 0.0;
+    // (from the first value: 0 + y would cost an add; y is never -0)
+    double tot = r0 < nj ? (double)y[0] : 0.0;
 #pragma unroll
-    for (int m = 0; m < E; ++m)
+    for (int m = 1; m < E; ++m)
       if (r0 + m < nj) tot = tot + (double)y[m];
-    const double pre = group_excl_sum<G, false>(tot, lane);
-    const double suf = group_excl_sum<G, true>(tot, lane);
+    // the sum of the lanes before this one (P's start), the bucket sum S and
+    // what follows this lane's values, S - (pre + tot) (Q's start: its
+    // rounding differs from a suffix sum's by a few ulps of S, which moves F
+    // by far less than the tie tolerance)
+    double Sg;
+    const double pre = group_excl_sum<G, false>(tot, lane, &Sg);
+    const double suf = Sg - (pre + tot);
     // F(k) = P^2/k + Q^2/(n-k) at every split between distinct values.  With
     // mu = S/n and the centred sum C = P - k mu, F(k) = S^2/n + n D(k),
     // D(k) = C^2 / (k (n-k)), so F and D peak at the same splits.  D is
@@ -1119,22 +1129,24 @@ void k_wave_sort_quant(
     int ex = 0;
     frexpf(amax, &ex);
     const double sc = ldexp(1.0, -ex);
-    const double mu = __shfl(pre + tot + suf, 0, G) / (double)nj;  // one value per group
+    const double mu = Sg / (double)nj;
     // (branch-free: every slot evaluated, -1 selected where no split lies;
-    // k and n - k as floats stepped from the lane's first split)
+    // k (n - k) = k0 n0 + m (n0 - k0 - m) from the lane's first split k0,
+    // n0 = n - k0, exact in fp32 for n <= 4096)
     float Fa[E];
     float fmax32 = -1.f;
     {
       float kf0 = (float)(r0 + 1), nkf0 = (float)(nj - r0 - 1);
-      // (opaque: otherwise folded back into one conversion per slot)
+      // (opaque: otherwise folded back into conversions per slot)
       asm volatile("" : "+v"(kf0), "+v"(nkf0));
+      const float kkA = kf0 * nkf0, kkB = nkf0 - kf0;
       double Cs = pre - (double)r0 * mu;
 #pragma unroll
       for (int m = 0; m < E; ++m) {
         if (r0 + m < nj) Cs = Cs + ((double)y[m] - mu);
         const float yk = (m + 1 < E) ? y[m + 1] : y_next_run;
         const float c32 = (float)(Cs * sc);
-        const float kk = (kf0 + (float)m) * (nkf0 - (float)m);
+        const float kk = m == 0 ? kkA : __builtin_fmaf((float)m, kkB - (float)m, kkA);
         const float f = c32 * c32 * __builtin_amdgcn_rcpf(kk);
         Fa[m] = (r0 + m + 1 < nj && y[m] < yk) ? f : -1.f;
         fmax32 = fmaxf(fmax32, Fa[m]);
@@ -1237,7 +1249,7 @@ void k_wave_sort_quant(
       // sum is small against the bucket's magnitude (cancellation) both are
       // recomputed with compensated sums
       const double Ps = __shfl(bestP, (kstar - 1) / E, G);
-      const double Stot = __shfl(pre + tot + suf, 0, G);  // one value per group
+      const double Stot = Sg;
       const double tiny = 0x1p-20 * (double)amax * (double)nj;
       double slo = Ps, shi = Stot - Ps;
       if (fabs(slo) < tiny || fabs(shi) < tiny) {
