@@ -44,6 +44,8 @@
 // scale leaves the fixed-point range, is marked with NaN levels
 // and left untouched; the caller then runs the sort-based kernel over the
 // marked buckets only.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace gq {
@@ -724,30 +726,37 @@ void k_binopt_block(
                          // 0xff800000)
   } else {
     // one pass: the fp64 sums below each range start, and the survivors
-    // appended to this wave's list (offsets from the wave's ballot).  With
-    // one range, rlo1 = rhi1 = 0 hold no key of a finite value.
+    // appended to this wave's list (offsets from the wave's ballot); with
+    // one range (nr is the same in every thread) the second range's sum and
+    // test are left out (p1 stays 0, no value lies in it)
     double p0 = 0.0, p1 = 0.0;
     int woff = 0;
     // x times 1.0 or 0.0 (the selected constant has a zero low word)
     auto gate = [](bool c) { return __hiloint2double(c ? 0x3ff00000 : 0, 0); };
+    auto pass = [&](auto two_tag) {
+      constexpr bool TWO = decltype(two_tag)::value;
 #pragma unroll
-    for (int m = 0; m < E; ++m) {
-      const bool v = valid(m);
-      const uint32_t k = key(m);
-      const float x = kval(k);
-      const double dx = (double)x;
-      p0 = __builtin_fma(dx, gate(v & (k < rlo0)), p0);
-      p1 = __builtin_fma(dx, gate(v & (k < rlo1)), p1);
-      const bool in0 = v & (k - rlo0 <= rhi0 - rlo0);
-      const bool in1 = v & (k - rlo1 <= rhi1 - rlo1);
-      const uint64_t bal = (uint64_t)__ballot(in0) | (uint64_t)__ballot(in1);
-      const int pos = woff + (int)__builtin_amdgcn_mbcnt_hi(
-                                 (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-      // every lane stores (no branch per value): the others to a slot of
-      // their own above the list
-      sh.v[wv][((in0 | in1) & (pos < kCap)) ? pos : kCap + wl] = x;
-      woff += __popcll(bal);
-    }
+      for (int m = 0; m < E; ++m) {
+        const bool v = valid(m);
+        const uint32_t k = key(m);
+        const float x = kval(k);
+        const double dx = (double)x;
+        p0 = __builtin_fma(dx, gate(v & (k < rlo0)), p0);
+        if constexpr (TWO) p1 = __builtin_fma(dx, gate(v & (k < rlo1)), p1);
+        const bool in0 = v & (k - rlo0 <= rhi0 - rlo0);
+        const bool in1 = TWO && (v & (k - rlo1 <= rhi1 - rlo1));
+        const uint64_t bal = TWO ? ((uint64_t)__ballot(in0) | (uint64_t)__ballot(in1))
+                                 : (uint64_t)__ballot(in0);
+        const int pos = woff + (int)__builtin_amdgcn_mbcnt_hi(
+                                   (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        // every lane stores (no branch per value): the others to a slot of
+        // their own above the list
+        sh.v[wv][((in0 | in1) & (pos < kCap)) ? pos : kCap + wl] = x;
+        woff += __popcll(bal);
+      }
+    };
+    if (nr == 2) pass(std::true_type{});
+    else pass(std::false_type{});
     p0 = group_sum_d<64>(p0);
     p1 = group_sum_d<64>(p1);
     if (wl == 0) {
