@@ -312,7 +312,6 @@ void k_binopt_block(
                                // half takes the other lanes' stores)
     int wc[NW];                // survivors per wave
     double rd[4][NW];          // per-wave partials: S, sums below the ranges
-    float ra[NW];              // per-wave sum |p|
     uint32_t ru[2][NW];        // per-wave key minima / maxima
     uint32_t kthr;             // exact stage result: threshold key,
     float la, lb;              //   levels,
@@ -346,8 +345,7 @@ void k_binopt_block(
   //      the keys of the canonical values (-0 -> +0); whether the wave saw a
   //      -0 at all (one scalar mask: the residual of a -0 differs from that
   //      of +0 only when its level is +0, and that rare case re-reads p);
-  //      bucket statistics on the way: key range, S = sum (fp64), A = sum |p|
-  //      (only a scale for a threshold: fp32) -----------------------------
+  //      bucket statistics on the way: key range and S = sum (fp64) -------
   uint32_t kk[ER];
   // held key m (m a compile-time index after unrolling)
   auto key = [&](int m) -> uint32_t {
@@ -357,7 +355,6 @@ void k_binopt_block(
   uint64_t zmask = 0ull;
   uint32_t kmn = 0xffffffffu, kmx = 0u;
   double S = 0.0;
-  float Af = 0.f;
   auto take = [&](int q, float4 x) {
     const float xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
@@ -373,7 +370,6 @@ void k_binopt_block(
       kmn = (ok & (kv < kmn)) ? kv : kmn;
       kmx = (ok & (kv > kmx)) ? kv : kmx;
       S = ok ? S + (double)v : S;
-      Af = ok ? Af + fabsf(v) : Af;
     }
   };
   if constexpr (FULL) {
@@ -418,29 +414,24 @@ void k_binopt_block(
   kmn = group_min_u<64>(kmn);
   kmx = group_max_u<64>(kmx);
   S = group_sum_d<64>(S);
-  Af = group_reduce<64>(Af, [](float a, float c) { return a + c; });
   if (wl == 0) {
     sh.ru[0][wv] = kmn;
     sh.ru[1][wv] = kmx;
     sh.rd[0][wv] = S;
-    sh.ra[wv] = Af;
   }
   __syncthreads();
   kmn = sh.ru[0][0];
   kmx = sh.ru[1][0];
   S = sh.rd[0][0];
-  Af = sh.ra[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) {
     kmn = sh.ru[0][w] < kmn ? sh.ru[0][w] : kmn;
     kmx = sh.ru[1][w] > kmx ? sh.ru[1][w] : kmx;
     S = S + sh.rd[0][w];
-    Af = Af + sh.ra[w];
   }
   // combined here, not where first used (the wave partials' loads were
   // otherwise kept in registers, or spilled, until the exact stage)
-  asm volatile("" : "+v"(S), "+v"(Af));
-  const double A = (double)Af;
+  asm volatile("" : "+v"(S));
   const double dn = (double)nj;
 
   // The histogram sums are fixed point: value x adds q = trunc(x 2^f), with
@@ -838,8 +829,9 @@ void k_binopt_block(
           sh.la = (float)(Ps / ks);
           sh.lb = (float)((S - Ps) / (dn - ks));
           // cluster sums with cancellation beyond the plain fp64 sums'
-          // accuracy (rare): recompute both sides with compensated sums
-          const double tiny = 0x1p-20 * A;
+          // accuracy (rare; the bucket's scale is max |p| times n): recompute
+          // both sides with compensated sums
+          const double tiny = 0x1p-20 * (double)amax * dn;
           sh.flag = (fabs(Ps) < tiny || fabs(S - Ps) < tiny) ? 1 : 0;
         }
       }
