@@ -738,12 +738,16 @@ void k_binopt_block(
         const bool in1 = TWO && (v & (k - rlo1 <= rhi1 - rlo1));
         const uint64_t bal = TWO ? ((uint64_t)__ballot(in0) | (uint64_t)__ballot(in1))
                                  : (uint64_t)__ballot(in0);
-        const int pos = woff + (int)__builtin_amdgcn_mbcnt_hi(
-                                   (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-        // every lane stores (no branch per value): the others to a slot of
-        // their own above the list
-        sh.v[wv][((in0 | in1) & (pos < kCap)) ? pos : kCap + wl] = x;
-        woff += __popcll(bal);
+        // most slots hold no survivor in any lane of the wave: the gather is
+        // skipped for them (a wave-uniform branch)
+        if (bal != 0ull) {
+          const int pos = woff + (int)__builtin_amdgcn_mbcnt_hi(
+                                     (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+          // every lane stores (no branch per value): the others to a slot
+          // of their own above the list
+          sh.v[wv][((in0 | in1) & (pos < kCap)) ? pos : kCap + wl] = x;
+          woff += __popcll(bal);
+        }
       }
     };
     if (nr == 2) pass(std::true_type{});
