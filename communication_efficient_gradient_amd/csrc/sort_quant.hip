@@ -1379,10 +1379,10 @@ void k_wave_sort_quant(
           const int pos = r0 + m;
           const float yv = y[m];
           const float ynext = (m + 1 < E) ? y[m + 1] : y_next_run;
-          // strictly inside a segment other than the top one, the last of
-          // a run of equal values
-          const bool cand = pos < nj && a_of[m] < ymax && yv > a_of[m] &&
-                            (pos + 1 >= nj || ynext != yv);
+          // strictly inside a segment other than the top one (a value of
+          // the top segment equals its lower end, ymax), the last of a run
+          // of equal values
+          const bool cand = pos < nj && yv > a_of[m] && (pos + 1 >= nj || ynext != yv);
           // (b - c) A + (c - a) B, with b - c and c - a exact in fp64
           if constexpr (BISECT) {
             const double Gv = cand ? vb(m) * A + v * Gs[m] : -1.0;
