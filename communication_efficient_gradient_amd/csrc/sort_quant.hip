@@ -353,8 +353,10 @@ __device__ __forceinline__ void sort_quant_bucket(
     const double sigma = sqrt((sq.s + sq.c) / (double)nj);
     C = (float)((double)clip_sigma * sigma);
   }
+  // (C = +inf without clipping: the median of x, -C, C is then x)
   auto clipped = [&](float x) {
-    return (SCHEME == ORQ && clip) ? fminf(fmaxf(x, -C), C) : x;
+    if constexpr (SCHEME == ORQ) return __builtin_amdgcn_fmed3f(x, -C, C);
+    else return x;
   };
 
   // ---- 3. sort (canonical +0, +inf padding), then publish it in LDS ------
@@ -1079,8 +1081,10 @@ void k_wave_sort_quant(
     const double sigma = sqrt((sq.s + sq.c) / (double)nj);
     C = (float)((double)clip_sigma * sigma);
   }
+  // (C = +inf without clipping: the median of x, -C, C is then x)
   auto clipped = [&](float x) {
-    return (SCHEME == ORQ && clip) ? fminf(fmaxf(x, -C), C) : x;
+    if constexpr (SCHEME == ORQ) return __builtin_amdgcn_fmed3f(x, -C, C);
+    else return x;
   };
 
   // ---- 3. sort in registers (canonical +0, +inf padding) -----------------
