@@ -54,6 +54,7 @@ namespace {
 constexpr int kBins = 64;     // bins per level (one per lane of the first wave)
 constexpr int kCols = 16;     // LDS columns per bin (lane mod 16)
 constexpr int kCap = 64;      // values the exact stage sorts (one per lane)
+constexpr int kCapW = 256;    // ... when the levels run out (four per lane)
 constexpr int kLevels = 10;   // levels before a bucket falls back to the sort
 constexpr int kRow = kCols + 2;  // LDS words per bin row (padded)
 // values per thread: 32 (workgroups of 64 to 512 threads), 16 at d = 1024
@@ -661,7 +662,7 @@ void k_binopt_block(
       rq1 = nq1;
       rc1 = nc1;
       if (rc0 + rc1 <= kCap) state = 1;
-      else if (lev + 1 == kLevels) state = 2;
+      else if (lev + 1 == kLevels) state = rc0 + rc1 <= kCapW ? 3 : 2;
     }
     if (wl == 0) {
       sh.nlo[0] = rlo0;
@@ -716,127 +717,259 @@ void k_binopt_block(
     kthr = 0xffffffffu;  // every code 0 (keys of finite values are below
                          // 0xff800000)
   } else {
-    // one pass: the fp64 sums below each range start, and the survivors
-    // appended to this wave's list (offsets from the wave's ballot); with
-    // one range (nr is the same in every thread) the second range's sum and
-    // test are left out (p1 stays 0, no value lies in it)
-    double p0 = 0.0, p1 = 0.0;
-    int woff = 0;
-    // x times 1.0 or 0.0 (the selected constant has a zero low word)
-    auto gate = [](bool c) { return __hiloint2double(c ? 0x3ff00000 : 0, 0); };
-    auto pass = [&](auto two_tag) {
-      constexpr bool TWO = decltype(two_tag)::value;
+    if (state == 3) {
+      // The levels ran out with kCap < survivors <= kCapW (the bounds' slack
+      // for the fixed-point sums keeps near-maximal splits of flat objectives
+      // alive): the same exact stage with four survivors per lane.  One pass:
+      // the fp64 sums below each range start, and the survivors appended to
+      // one list in the histogram's LDS (no longer needed), at offsets from a
+      // per-wave reservation.
+      float* const list = reinterpret_cast<float*>(sh.h);
+      if (tid == 0) sh.wc[0] = 0;
+      __syncthreads();
+      double p0 = 0.0, p1 = 0.0;
 #pragma unroll
       for (int m = 0; m < E; ++m) {
         const bool v = valid(m);
         const uint32_t k = key(m);
         const float x = kval(k);
-        const double dx = (double)x;
-        p0 = __builtin_fma(dx, gate(v & (k < rlo0)), p0);
-        if constexpr (TWO) p1 = __builtin_fma(dx, gate(v & (k < rlo1)), p1);
-        const bool in0 = v & (k - rlo0 <= rhi0 - rlo0);
-        const bool in1 = TWO && (v & (k - rlo1 <= rhi1 - rlo1));
-        const uint64_t bal = TWO ? ((uint64_t)__ballot(in0) | (uint64_t)__ballot(in1))
-                                 : (uint64_t)__ballot(in0);
-        // most slots hold no survivor in any lane of the wave: the gather is
-        // skipped for them (a wave-uniform branch)
+        p0 = (v & (k < rlo0)) ? p0 + (double)x : p0;
+        p1 = (v & (k < rlo1)) ? p1 + (double)x : p1;
+        const bool in = v & ((k - rlo0 <= rhi0 - rlo0) | (k - rlo1 <= rhi1 - rlo1));
+        const uint64_t bal = (uint64_t)__ballot(in);
         if (bal != 0ull) {
-          const int pos = woff + (int)__builtin_amdgcn_mbcnt_hi(
-                                     (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-          // every lane stores (no branch per value): the others to a slot
-          // of their own above the list
-          sh.v[wv][((in0 | in1) & (pos < kCap)) ? pos : kCap + wl] = x;
-          woff += __popcll(bal);
+          int wbase = 0;
+          if (wl == 0) wbase = atomicAdd(&sh.wc[0], __popcll(bal));
+          wbase = __shfl(wbase, 0, 64);
+          const int pos = wbase + (int)__builtin_amdgcn_mbcnt_hi(
+                                      (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+          if (in && pos < kCapW) list[pos] = x;
         }
       }
-    };
-    if (nr == 2) pass(std::true_type{});
-    else pass(std::false_type{});
-    p0 = group_sum_d<64>(p0);
-    p1 = group_sum_d<64>(p1);
-    if (wl == 0) {
-      sh.rd[2][wv] = p0;
-      sh.rd[3][wv] = p1;
-      sh.wc[wv] = woff;
-    }
-    __syncthreads();
-    p0 = sh.rd[2][0];
-    p1 = sh.rd[3][0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      p0 = p0 + sh.rd[2][w];
-      p1 = p1 + sh.rd[3][w];
-    }
-    if (wv == 0) {
-      // one survivor per lane (the waves' lists in wave order), sorted
-      int cnt = 0;
-      float y[1] = {__builtin_inff()};
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const int cw = sh.wc[w];
-        const int at = wl - cnt;
-        if (at >= 0 && at < cw && at < kCap) y[0] = sh.v[w][at];
-        cnt += cw;
+      p0 = group_sum_d<64>(p0);
+      p1 = group_sum_d<64>(p1);
+      if (wl == 0) {
+        sh.rd[2][wv] = p0;
+        sh.rd[3][wv] = p1;
       }
-      sv_levels<1, kCap, 2>(y, wl);
-      const double own = wl < cnt ? (double)y[0] : 0.0;
-      const double pre0 = group_inclusive<64>(own) - own;  // sum before this position
-      const int off1 = rc0;                                  // start of range 1
-      const double pre_off1 = off1 < 64 ? __longlong_as_double(readlane64(__double_as_longlong(pre0), off1)) : 0.0;
-      const float y_prev = __shfl_up(y[0], 1, 64);
-      double bestF = -1.0;
-      int bestK = 0x7fffffff;
-      uint32_t bestT = 0u;
-      double bestP = 0.0;
-      // F to a few ulps: buckets whose best two splits are closer than
-      // that are ties, and either split is correct there
-      auto consider = [&](int k, double P, uint32_t kt) {
-        if (k <= 0 || k >= nj) return;
-        const double f = obj_fast(P, (double)k, S, dn);
-        if (f > bestF || (f == bestF && k < bestK)) {
-          bestF = f;
-          bestK = k;
-          bestT = kt;
-          bestP = P;
+      __syncthreads();
+      p0 = sh.rd[2][0];
+      p1 = sh.rd[3][0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) {
+        p0 = p0 + sh.rd[2][w];
+        p1 = p1 + sh.rd[3][w];
+      }
+      if (wv == 0) {
+        const int cnt = sh.wc[0];
+        // positions 4 wl .. 4 wl + 3 of the sorted survivors
+        float y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pos = 4 * wl + r;
+          y[r] = pos < cnt && pos < kCapW ? list[pos] : __builtin_inff();
+        }
+        sv_levels<4, kCapW, 2>(y, wl);
+        double own[4], tl = 0.0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          own[r] = 4 * wl + r < cnt ? (double)y[r] : 0.0;
+          tl = tl + own[r];
+        }
+        const double lane_pre = group_inclusive<64>(tl) - tl;  // sum before the lane
+        double pre[4];
+        {
+          double acc = lane_pre;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pre[r] = acc;  // sum before position 4 wl + r
+            acc = acc + own[r];
+          }
+        }
+        const int off1 = rc0;  // start of range 1
+        double pre_off1 = 0.0;
+        if (off1 < cnt) {
+          const int ro = off1 & 3;
+          const double mine = ro == 0 ? pre[0] : ro == 1 ? pre[1] : ro == 2 ? pre[2] : pre[3];
+          pre_off1 = __longlong_as_double(readlane64(__double_as_longlong(mine), off1 >> 2));
+        }
+        const float y_prev_lane = __shfl_up(y[3], 1, 64);
+        double bestF = -1.0;
+        int bestK = 0x7fffffff;
+        uint32_t bestT = 0u;
+        double bestP = 0.0;
+        auto consider = [&](int k, double P, uint32_t kt) {
+          if (k <= 0 || k >= nj) return;
+          const double f = obj_fast(P, (double)k, S, dn);
+          if (f > bestF || (f == bestF && k < bestK)) {
+            bestF = f;
+            bestK = k;
+            bestT = kt;
+            bestP = P;
+          }
+        };
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pos = 4 * wl + r;
+          if (pos < cnt) {
+            const bool r1 = pos >= off1;
+            const int start = r1 ? off1 : 0;
+            const float yp = r == 0 ? y_prev_lane : y[r > 0 ? r - 1 : 0];
+            const bool distinct = pos == start || yp < y[r];
+            const int k = (r1 ? rk1 : rk0) + (pos - start);
+            const double P = (r1 ? p1 : p0) + (pre[r] - (r1 ? pre_off1 : 0.0));
+            if (distinct) consider(k, P, fkey(y[r]));
+            if (pos + 1 == (r1 ? cnt : off1)) {  // after the range's last value
+              const int k2 = r1 ? rk1 + rc1 : rk0 + rc0;
+              const double P2 = (r1 ? p1 : p0) + ((pre[r] + own[r]) - (r1 ? pre_off1 : 0.0));
+              consider(k2, P2, (r1 ? rhi1 : rhi0) + 1u);
+            }
+          }
+        }
+        // lanes hold increasing splits: the first lane reaching the maximum
+        const double gF = group_max_d<64>(bestF);
+        const uint64_t at_max = (uint64_t)__ballot(bestF == gF);
+        const int win = __builtin_ctzll(at_max);
+        const int gK = __builtin_amdgcn_readlane(bestK, win);
+        const uint32_t kt = (uint32_t)__builtin_amdgcn_readlane((int)bestT, win);
+        const double Ps = __longlong_as_double(readlane64(__double_as_longlong(bestP), win));
+        if (wl == 0) {
+          if (gF < 0.0 || cnt > kCapW || cnt != rc0 + rc1) {
+            sh.flag = 2;
+          } else {
+            const double ks = (double)gK;
+            sh.kthr = kt;
+            sh.ks = ks;
+            sh.la = (float)(Ps / ks);
+            sh.lb = (float)((S - Ps) / (dn - ks));
+            const double tiny = 0x1p-20 * (double)amax * dn;
+            sh.flag = (fabs(Ps) < tiny || fabs(S - Ps) < tiny) ? 1 : 0;
+          }
+        }
+      }
+    } else {
+      // one pass: the fp64 sums below each range start, and the survivors
+      // appended to this wave's list (offsets from the wave's ballot); with
+      // one range (nr is the same in every thread) the second range's sum and
+      // test are left out (p1 stays 0, no value lies in it)
+      double p0 = 0.0, p1 = 0.0;
+      int woff = 0;
+      // x times 1.0 or 0.0 (the selected constant has a zero low word)
+      auto gate = [](bool c) { return __hiloint2double(c ? 0x3ff00000 : 0, 0); };
+      auto pass = [&](auto two_tag) {
+        constexpr bool TWO = decltype(two_tag)::value;
+  #pragma unroll
+        for (int m = 0; m < E; ++m) {
+          const bool v = valid(m);
+          const uint32_t k = key(m);
+          const float x = kval(k);
+          const double dx = (double)x;
+          p0 = __builtin_fma(dx, gate(v & (k < rlo0)), p0);
+          if constexpr (TWO) p1 = __builtin_fma(dx, gate(v & (k < rlo1)), p1);
+          const bool in0 = v & (k - rlo0 <= rhi0 - rlo0);
+          const bool in1 = TWO && (v & (k - rlo1 <= rhi1 - rlo1));
+          const uint64_t bal = TWO ? ((uint64_t)__ballot(in0) | (uint64_t)__ballot(in1))
+                                   : (uint64_t)__ballot(in0);
+          // most slots hold no survivor in any lane of the wave: the gather is
+          // skipped for them (a wave-uniform branch)
+          if (bal != 0ull) {
+            const int pos = woff + (int)__builtin_amdgcn_mbcnt_hi(
+                                       (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            // every lane stores (no branch per value): the others to a slot
+            // of their own above the list
+            sh.v[wv][((in0 | in1) & (pos < kCap)) ? pos : kCap + wl] = x;
+            woff += __popcll(bal);
+          }
         }
       };
-      if (wl < cnt) {
-        const bool r1 = wl >= off1;
-        const int start = r1 ? off1 : 0;
-        const bool distinct = wl == start || y_prev < y[0];
-        const int k = (r1 ? rk1 : rk0) + (wl - start);
-        const double P = (r1 ? p1 : p0) + (pre0 - (r1 ? pre_off1 : 0.0));
-        if (distinct) consider(k, P, fkey(y[0]));
-        // the split after the range's last value
-        const bool last = wl + 1 == (r1 ? cnt : off1);
-        if (last) {
-          const int k2 = r1 ? rk1 + rc1 : rk0 + rc0;
-          const double P2 = (r1 ? p1 : p0) + ((pre0 + own) - (r1 ? pre_off1 : 0.0));
-          consider(k2, P2, (r1 ? rhi1 : rhi0) + 1u);
-        }
-      }
-      // the largest F, then the smallest split: lanes hold increasing
-      // splits, so the first lane reaching the maximum
-      const double gF = group_max_d<64>(bestF);
-      const uint64_t at_max = (uint64_t)__ballot(bestF == gF);
-      const int win = __builtin_ctzll(at_max);
-      const int gK = __builtin_amdgcn_readlane(bestK, win);
-      const uint32_t kt = (uint32_t)__builtin_amdgcn_readlane((int)bestT, win);
-      const double Ps = __longlong_as_double(readlane64(__double_as_longlong(bestP), win));
+      if (nr == 2) pass(std::true_type{});
+      else pass(std::false_type{});
+      p0 = group_sum_d<64>(p0);
+      p1 = group_sum_d<64>(p1);
       if (wl == 0) {
-        if (gF < 0.0 || cnt > kCap) {
-          sh.flag = 2;  // no candidate (cannot happen when the bounds hold)
-        } else {
-          const double ks = (double)gK;
-          sh.kthr = kt;
-          sh.ks = ks;
-          sh.la = (float)(Ps / ks);
-          sh.lb = (float)((S - Ps) / (dn - ks));
-          // cluster sums with cancellation beyond the plain fp64 sums'
-          // accuracy (rare; the bucket's scale is max |p| times n): recompute
-          // both sides with compensated sums
-          const double tiny = 0x1p-20 * (double)amax * dn;
-          sh.flag = (fabs(Ps) < tiny || fabs(S - Ps) < tiny) ? 1 : 0;
+        sh.rd[2][wv] = p0;
+        sh.rd[3][wv] = p1;
+        sh.wc[wv] = woff;
+      }
+      __syncthreads();
+      p0 = sh.rd[2][0];
+      p1 = sh.rd[3][0];
+  #pragma unroll
+      for (int w = 1; w < NW; ++w) {
+        p0 = p0 + sh.rd[2][w];
+        p1 = p1 + sh.rd[3][w];
+      }
+      if (wv == 0) {
+        // one survivor per lane (the waves' lists in wave order), sorted
+        int cnt = 0;
+        float y[1] = {__builtin_inff()};
+  #pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const int cw = sh.wc[w];
+          const int at = wl - cnt;
+          if (at >= 0 && at < cw && at < kCap) y[0] = sh.v[w][at];
+          cnt += cw;
+        }
+        sv_levels<1, kCap, 2>(y, wl);
+        const double own = wl < cnt ? (double)y[0] : 0.0;
+        const double pre0 = group_inclusive<64>(own) - own;  // sum before this position
+        const int off1 = rc0;                                  // start of range 1
+        const double pre_off1 = off1 < 64 ? __longlong_as_double(readlane64(__double_as_longlong(pre0), off1)) : 0.0;
+        const float y_prev = __shfl_up(y[0], 1, 64);
+        double bestF = -1.0;
+        int bestK = 0x7fffffff;
+        uint32_t bestT = 0u;
+        double bestP = 0.0;
+        // F to a few ulps: buckets whose best two splits are closer than
+        // that are ties, and either split is correct there
+        auto consider = [&](int k, double P, uint32_t kt) {
+          if (k <= 0 || k >= nj) return;
+          const double f = obj_fast(P, (double)k, S, dn);
+          if (f > bestF || (f == bestF && k < bestK)) {
+            bestF = f;
+            bestK = k;
+            bestT = kt;
+            bestP = P;
+          }
+        };
+        if (wl < cnt) {
+          const bool r1 = wl >= off1;
+          const int start = r1 ? off1 : 0;
+          const bool distinct = wl == start || y_prev < y[0];
+          const int k = (r1 ? rk1 : rk0) + (wl - start);
+          const double P = (r1 ? p1 : p0) + (pre0 - (r1 ? pre_off1 : 0.0));
+          if (distinct) consider(k, P, fkey(y[0]));
+          // the split after the range's last value
+          const bool last = wl + 1 == (r1 ? cnt : off1);
+          if (last) {
+            const int k2 = r1 ? rk1 + rc1 : rk0 + rc0;
+            const double P2 = (r1 ? p1 : p0) + ((pre0 + own) - (r1 ? pre_off1 : 0.0));
+            consider(k2, P2, (r1 ? rhi1 : rhi0) + 1u);
+          }
+        }
+        // the largest F, then the smallest split: lanes hold increasing
+        // splits, so the first lane reaching the maximum
+        const double gF = group_max_d<64>(bestF);
+        const uint64_t at_max = (uint64_t)__ballot(bestF == gF);
+        const int win = __builtin_ctzll(at_max);
+        const int gK = __builtin_amdgcn_readlane(bestK, win);
+        const uint32_t kt = (uint32_t)__builtin_amdgcn_readlane((int)bestT, win);
+        const double Ps = __longlong_as_double(readlane64(__double_as_longlong(bestP), win));
+        if (wl == 0) {
+          if (gF < 0.0 || cnt > kCap) {
+            sh.flag = 2;  // no candidate (cannot happen when the bounds hold)
+          } else {
+            const double ks = (double)gK;
+            sh.kthr = kt;
+            sh.ks = ks;
+            sh.la = (float)(Ps / ks);
+            sh.lb = (float)((S - Ps) / (dn - ks));
+            // cluster sums with cancellation beyond the plain fp64 sums'
+            // accuracy (rare; the bucket's scale is max |p| times n): recompute
+            // both sides with compensated sums
+            const double tiny = 0x1p-20 * (double)amax * dn;
+            sh.flag = (fabs(Ps) < tiny || fabs(S - Ps) < tiny) ? 1 : 0;
+          }
         }
       }
     }

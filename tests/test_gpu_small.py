@@ -308,3 +308,28 @@ def test_deterministic_repeat(dev):
         b = run_gpu(dev, d, g, e, 7, 2)
         for x, y in zip(a, b):
             assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
+def _bingrad_after_ef_steps(d: int, buckets, steps: int):
+    """Buckets `buckets` of the 1B bingrad gradient (bucket indices counted
+    from element 2^24 on, inside its second and third chunks of 2^24 values)
+    and the residuals the oracle's own BinGrad-b + error-feedback steps
+    leave on them: (g, [e_0 = 0, e_1, ..., e_steps])."""
+    chunk = WL.bingrad_gradient(2 * WL.CHUNK, start=WL.CHUNK)
+    g = np.concatenate([chunk[b * d:(b + 1) * d] for b in buckets])
+    es = [np.zeros_like(g)]
+    for t in range(steps):
+        _, _, e_next, _ = O.quantize(O.Desc(O.BIN_OPT, d), g, es[-1], seed=0, step=t)
+        es.append(e_next)
+    return g, es
+
+
+def test_binopt_after_ef_steps(dev):
+    """BinGrad-b on buckets that a few error-feedback steps have shaped so
+    that near-maximal splits stay many (on the GPU's own trajectory the
+    split search's levels ran out there with 65 to 208 values left): each
+    step's quantize against the oracle, the residuals being the oracle's."""
+    d = 32768
+    g, es = _bingrad_after_ef_steps(d, [436, 437, 438, 564, 662, 663], 4)
+    for t, e in enumerate(es):
+        check_quantize(dev, O.Desc(O.BIN_OPT, d), g, e, step=t)
