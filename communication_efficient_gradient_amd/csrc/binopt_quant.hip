@@ -483,6 +483,7 @@ void k_binopt_block(
   };
 
   for (int lev = 0; lev < kLevels && state == 0; ++lev) {
+    const int cnt_prev = rc0 + rc1;
     const int lgb = nr == 2 ? 5 : 6;  // log2 of the bins per range
     const int nbr = 1 << lgb;
     // shift of each range: (hi - lo) >> sh < nbr
@@ -661,7 +662,10 @@ void k_binopt_block(
       rk1 = nk1;
       rq1 = nq1;
       rc1 = nc1;
+      // Large buckets stop refining once a level has not halved the
+      // candidates: the rest are near-equal splits the bounds cannot part.
       if (rc0 + rc1 <= kCap) state = 1;
+      else if (D >= 16384 && rc0 + rc1 <= kCapW && 2 * (rc0 + rc1) > cnt_prev) state = 3;
       else if (lev + 1 == kLevels) state = rc0 + rc1 <= kCapW ? 3 : 2;
     }
     if (wl == 0) {
@@ -718,9 +722,10 @@ void k_binopt_block(
                          // 0xff800000)
   } else {
     if (state == 3) {
-      // The levels ran out with kCap < survivors <= kCapW (the bounds' slack
-      // for the fixed-point sums keeps near-maximal splits of flat objectives
-      // alive): the same exact stage with four survivors per lane.  One pass:
+      // The levels ran out, or at d >= 16384 stopped halving, with
+      // kCap < survivors <= kCapW (the bounds' slack for the fixed-point
+      // sums keeps near-maximal splits of flat objectives alive): the same
+      // exact stage with four survivors per lane.  One pass:
       // the fp64 sums below each range start, and the survivors appended to
       // one list in the histogram's LDS (no longer needed), at offsets from a
       // per-wave reservation.
